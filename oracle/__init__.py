@@ -1,0 +1,191 @@
+"""CPU oracle for hierarchical sparse attention (HSA) and DHSA.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product path.  A thin ctypes
+wrapper over hsa_oracle.c (plain C, double precision); see that file for the
+step-by-step definitions and the pages each one follows.
+
+Arrays are numpy: float32, or uint16 holding bfloat16 bits.  Results are
+float64 (outputs, weights, margins) and int32 (indices).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+_F32, _BF16 = 0, 1
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        L.oracle_landmarks.argtypes = [_P, ctypes.c_int, _I, _I, _I, _I, _I, _P]
+        L.oracle_hsa_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _I, _I, _I,
+                                         _P, _I, ctypes.c_int, _P, _P, _P, _P]
+        L.oracle_hsa_decode_select.argtypes = [_P, ctypes.c_int, _P, _I, _I, _I, _I, _I, _I,
+                                               _I, _I, _P, _P]
+        L.oracle_hsa_decode_attend.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _I, _I, _I,
+                                               _I, _I, _I, _P, _P]
+        L.oracle_dhsa_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _P, _I, _I,
+                                          _P, _I, _P, _P, _P, _P, _P]
+        for f in (L.oracle_landmarks, L.oracle_hsa_prefill, L.oracle_hsa_decode_select,
+                  L.oracle_hsa_decode_attend, L.oracle_dhsa_prefill):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _dt(*arrays):
+    kinds = {a.dtype for a in arrays}
+    if kinds == {np.dtype(np.float32)}:
+        return _F32
+    if kinds == {np.dtype(np.uint16)}:
+        return _BF16
+    raise TypeError(f"inputs must all be float32 or all bf16 bits (uint16), got {kinds}")
+
+
+def _c(a):
+    return np.ascontiguousarray(a)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def landmarks(K, S):
+    """K [B,H,L,d] -> landmarks [B,H,L//S,d] float64: chunk key sums / sqrt(S)."""
+    K = _c(K)
+    B, H, L, d = K.shape
+    out = np.zeros((B, H, L // S, d), np.float64)
+    _check(lib().oracle_landmarks(K.ctypes.data, _dt(K), B, H, L, d, S, _ptr(out)), "landmarks")
+    return out
+
+
+def hsa_prefill(Q, K, V, S, topk, rows=None, include_current_chunk=False, want_out=True):
+    """HSA prefill for query positions `rows` (default: all).
+
+    Returns dict(out [B,Hq,R,d], sel [B,Hkv,R,K], w [B,Hq,R,K], margin [B,Hkv,R])."""
+    Q, K, V = _c(Q), _c(K), _c(V)
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    dt = _dt(Q, K, V)
+    if rows is None:
+        R = L
+        rows_a = None
+    else:
+        rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+        R = len(rows_a)
+    out = np.zeros((B, Hq, R, d), np.float64) if want_out else None
+    sel = np.zeros((B, Hkv, R, topk), np.int32)
+    w = np.zeros((B, Hq, R, topk), np.float64)
+    margin = np.zeros((B, Hkv, R), np.float64)
+    rc = lib().oracle_hsa_prefill(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dt, B, L, Hq,
+                                  Hkv, d, S, topk, _ptr(rows_a), R, int(include_current_chunk),
+                                  _ptr(out), _ptr(sel), _ptr(w), _ptr(margin))
+    _check(rc, "hsa_prefill")
+    return dict(out=out, sel=sel, w=w, margin=margin)
+
+
+def hsa_decode_select(q, lmk, S, n_ctx, topk, Hkv):
+    """q [B,Hq,d]; lmk float32 [B,Hkv,n_lmk,d].  Returns (sel [B,Hkv,K], margin [B,Hkv])."""
+    q = _c(q)
+    lmk = np.ascontiguousarray(lmk, dtype=np.float32)
+    B, Hq, d = q.shape
+    n_lmk = lmk.shape[2]
+    sel = np.zeros((B, Hkv, topk), np.int32)
+    margin = np.zeros((B, Hkv), np.float64)
+    rc = lib().oracle_hsa_decode_select(q.ctypes.data, _dt(q), lmk.ctypes.data, B, Hq, Hkv, d,
+                                        S, n_ctx, n_lmk, topk, sel.ctypes.data,
+                                        margin.ctypes.data)
+    _check(rc, "hsa_decode_select")
+    return sel, margin
+
+
+def hsa_decode_attend(q, Ksel, Vsel, lmk_sel, sel, S):
+    """Ksel, Vsel [B,Hkv,K,S,d] selected chunks in selection order, lmk_sel
+    float32 [B,Hkv,K,d], sel [B,Hkv,K].  Returns (out [B,Hq,d], w [B,Hq,K])."""
+    q, Ksel, Vsel = _c(q), _c(Ksel), _c(Vsel)
+    lmk_sel = np.ascontiguousarray(lmk_sel, dtype=np.float32)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    B, Hq, d = q.shape
+    Hkv, topk = sel.shape[1], sel.shape[2]
+    out = np.zeros((B, Hq, d), np.float64)
+    w = np.zeros((B, Hq, topk), np.float64)
+    rc = lib().oracle_hsa_decode_attend(q.ctypes.data, Ksel.ctypes.data, Vsel.ctypes.data,
+                                        _dt(q, Ksel, Vsel), lmk_sel.ctypes.data, sel.ctypes.data,
+                                        B, Hq, Hkv, d, S, topk, out.ctypes.data, w.ctypes.data)
+    _check(rc, "hsa_decode_attend")
+    return out, w
+
+
+def pack_selected(Kc, sel, S):
+    """Gather the selected chunks of a full cache Kc [B,Hkv,N,d] into
+    [B,Hkv,K,S,d] (zeros for -1 slots)."""
+    B, Hkv, N, d = Kc.shape
+    topk = sel.shape[2]
+    out = np.zeros((B, Hkv, topk, S, d), Kc.dtype)
+    for b in range(B):
+        for g in range(Hkv):
+            for k in range(topk):
+                c = sel[b, g, k]
+                if c >= 0:
+                    out[b, g, k] = Kc[b, g, c * S:(c + 1) * S]
+    return out
+
+
+def hsa_decode(q, Kc, Vc, lmk, S, n_ctx, topk):
+    """Full decode on caches small enough to hold on the host."""
+    Hkv = Kc.shape[1]
+    sel, margin = hsa_decode_select(q, lmk, S, n_ctx, topk, Hkv)
+    Ks, Vs = pack_selected(Kc, sel, S), pack_selected(Vc, sel, S)
+    lmk = np.asarray(lmk, np.float32)
+    B, _, _, d = lmk.shape
+    lsel = np.zeros((B, Hkv, topk, d), np.float32)
+    for b in range(B):
+        for g in range(Hkv):
+            for k in range(topk):
+                if sel[b, g, k] >= 0:
+                    lsel[b, g, k] = lmk[b, g, sel[b, g, k]]
+    out, w = hsa_decode_attend(q, Ks, Vs, lsel, sel, S)
+    return dict(out=out, w=w, sel=sel, margin=margin)
+
+
+def dhsa_prefill(Q, K, V, offsets, budget, rows=None, want_sc=False, want_kept=False):
+    """DHSA prefill for query positions `rows` (default: all).
+
+    Returns dict(out [B,H,R,d], sc [B,H,nc,nc] or None, n_kept [B,H,R],
+    kept [B,H,R,L] uint8 or None, margin [B,H,R])."""
+    Q, K, V = _c(Q), _c(K), _c(V)
+    B, H, L, d = Q.shape
+    offs = np.ascontiguousarray(offsets, dtype=np.int32)
+    nc = len(offs) - 1
+    if rows is None:
+        R, rows_a = L, None
+    else:
+        rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+        R = len(rows_a)
+    out = np.zeros((B, H, R, d), np.float64)
+    sc = np.zeros((B, H, nc, nc), np.float64) if want_sc else None
+    n_kept = np.zeros((B, H, R), np.int32)
+    kept = np.zeros((B, H, R, L), np.uint8) if want_kept else None
+    margin = np.zeros((B, H, R), np.float64)
+    rc = lib().oracle_dhsa_prefill(Q.ctypes.data, K.ctypes.data, V.ctypes.data, _dt(Q, K, V), B,
+                                   L, H, d, offs.ctypes.data, nc, budget, _ptr(rows_a), R,
+                                   out.ctypes.data, _ptr(sc), n_kept.ctypes.data, _ptr(kept),
+                                   margin.ctypes.data)
+    _check(rc, "dhsa_prefill")
+    return dict(out=out, sc=sc, n_kept=n_kept, kept=kept, margin=margin)

@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test checks the oracle against something other than itself: a closed
+form, a textbook routine the method reduces to in a special case (dense causal
+attention, top-k token attention), brute force on tiny exact inputs, or an
+invariant.  A plausible mistake in the oracle (dropped term, wrong sign, wrong
+index, off-by-one in the causal rule, transposed operand, wrong tie order)
+fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+def f32(shape, seed, tid, scale=1.0):
+    return synth.normal(shape, synth.F32, seed, tid, scale)
+
+
+def softmax(x):
+    m = x.max()
+    e = np.exp(x - m)
+    return e / e.sum()
+
+
+# ---------------------------------------------------------------- landmarks
+
+
+def test_landmark_closed_forms():
+    K = f32((2, 3, 37, 8), 1, synth.TID_K)
+    # S = 1: each landmark is its key
+    assert np.array_equal(oracle.landmarks(K, 1), K.astype(np.float64))
+    # constant keys u: landmark = sqrt(S) * u
+    u = f32((8,), 2, synth.TID_K)
+    Kc = np.broadcast_to(u, (1, 1, 64, 8)).copy()
+    lm = oracle.landmarks(Kc, 16)
+    assert lm.shape == (1, 1, 4, 8)
+    np.testing.assert_allclose(lm, np.broadcast_to(4.0 * u.astype(np.float64), lm.shape),
+                               rtol=1e-14, atol=0)
+    # trailing partial chunk has no landmark
+    assert oracle.landmarks(K, 16).shape == (2, 3, 2, 8)
+    np.testing.assert_array_equal(oracle.landmarks(K, 16), oracle.landmarks(K[:, :, :32], 16))
+
+
+def test_landmark_linearity_and_chunk_locality():
+    rng = np.random.default_rng(0)
+    K1 = rng.integers(-8, 8, (1, 2, 64, 4)).astype(np.float32)
+    K2 = rng.integers(-8, 8, (1, 2, 64, 4)).astype(np.float32)
+    l1, l2 = oracle.landmarks(K1, 16), oracle.landmarks(K2, 16)
+    l3 = oracle.landmarks((2 * K1 - 3 * K2).astype(np.float32), 16)
+    np.testing.assert_allclose(l3, 2 * l1 - 3 * l2, rtol=0, atol=1e-12)
+    # changing one key moves exactly one landmark, by (delta / sqrt(S))
+    K3 = K1.copy()
+    K3[0, 1, 37, 2] += 5
+    diff = oracle.landmarks(K3, 16) - l1
+    nz = np.argwhere(diff != 0)
+    assert nz.tolist() == [[0, 1, 2, 2]] and diff[0, 1, 2, 2] == pytest.approx(5 / 4)
+
+
+# ------------------------------------------------ HSA prefill special cases
+
+
+def dense_attention(q, K, V, causal_strict):
+    """Textbook masked softmax attention of one head, float64, numpy."""
+    L, d = q.shape
+    out = np.zeros((L, d))
+    for t in range(L):
+        hi = t if causal_strict else t + 1
+        if hi == 0:
+            continue
+        logits = (K[:hi].astype(np.float64) @ q[t].astype(np.float64)) / math.sqrt(d)
+        out[t] = softmax(logits) @ V[:hi].astype(np.float64)
+    return out
+
+
+def test_S1_all_chunks_is_dense_strict_causal_attention():
+    # With S = 1 each chunk is one token and its landmark is that key, so
+    # keeping every available chunk fuses softmax(q.k_j/sqrt d) over j < t:
+    # dense attention with a strict causal mask; row 0 has nothing.
+    B, Hq, Hkv, L, d = 1, 4, 2, 40, 16
+    Q = f32((B, Hq, L, d), 3, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 3, synth.TID_K)
+    V = f32((B, Hkv, L, d), 3, synth.TID_V)
+    r = oracle.hsa_prefill(Q, K, V, S=1, topk=L)
+    for h in range(Hq):
+        ref = dense_attention(Q[0, h], K[0, h // 2], V[0, h // 2], causal_strict=True)
+        np.testing.assert_allclose(r["out"][0, h], ref, rtol=0, atol=1e-12)
+    assert not r["out"][:, :, 0].any()
+
+
+def test_S1_topk_is_topk_token_attention():
+    # S = 1, K < L, one head per group: the K keys with the largest logits
+    # q.k_j/sqrt d among j < t (ties: lower j), then softmax over those.
+    L, d, K_ = 48, 8, 5
+    Q = f32((1, 1, L, d), 4, synth.TID_Q)
+    K = f32((1, 1, L, d), 4, synth.TID_K)
+    V = f32((1, 1, L, d), 4, synth.TID_V)
+    r = oracle.hsa_prefill(Q, K, V, S=1, topk=K_)
+    q, k, v = (a[0, 0].astype(np.float64) for a in (Q, K, V))
+    for t in range(L):
+        if t == 0:
+            assert not r["out"][0, 0, 0].any() and (r["sel"][0, 0, 0] == -1).all()
+            continue
+        lg = k[:t] @ q[t] / math.sqrt(d)
+        order = np.lexsort((np.arange(t), -lg))[:K_]
+        assert list(r["sel"][0, 0, t][: len(order)]) == list(order)
+        assert (r["sel"][0, 0, t][len(order):] == -1).all()
+        ref = softmax(lg[order]) @ v[order]
+        np.testing.assert_allclose(r["out"][0, 0, t], ref, rtol=0, atol=1e-12)
+
+
+def test_S_equals_L_current_chunk_is_dense_causal():
+    # With S = L there is one chunk.  The oracle-only switch that makes the
+    # chunk holding t available (keys j <= t) turns every row into dense
+    # causal attention; without it no chunk is ever fully before t.
+    L, d = 32, 8
+    Q = f32((1, 2, L, d), 5, synth.TID_Q)
+    K = f32((1, 1, L, d), 5, synth.TID_K)
+    V = f32((1, 1, L, d), 5, synth.TID_V)
+    r = oracle.hsa_prefill(Q, K, V, S=L, topk=1, include_current_chunk=True)
+    for h in range(2):
+        ref = dense_attention(Q[0, h], K[0, 0], V[0, 0], causal_strict=False)
+        np.testing.assert_allclose(r["out"][0, h], ref, rtol=0, atol=1e-12)
+    r0 = oracle.hsa_prefill(Q, K, V, S=L, topk=1)
+    assert not r0["out"].any() and (r0["sel"] == -1).all()
+
+
+def test_decode_S_equals_L_is_dense_attention():
+    # A decode query at position L after an L-token context, S = L, K = 1:
+    # softmax attention over all L context keys.
+    L, d = 64, 16
+    q = f32((2, 4, d), 6, synth.TID_QDEC)
+    K = f32((2, 2, L, d), 6, synth.TID_K)
+    V = f32((2, 2, L, d), 6, synth.TID_V)
+    lmk = oracle.landmarks(K, L).astype(np.float32)
+    r = oracle.hsa_decode(q, K, V, lmk, S=L, n_ctx=L, topk=1)
+    for b in range(2):
+        for h in range(4):
+            lg = K[b, h // 2].astype(np.float64) @ q[b, h].astype(np.float64) / math.sqrt(d)
+            ref = softmax(lg) @ V[b, h // 2].astype(np.float64)
+            np.testing.assert_allclose(r["out"][b, h], ref, rtol=0, atol=1e-12)
+    assert (r["w"][..., 0] == 1.0).all()
+
+
+def test_topk_brute_force_with_planted_ties():
+    # Integer inputs and power-of-two S and d make every score exact in
+    # double, so ties are exact.  Brute force: rank of chunk c = number of
+    # chunks with a larger group score, or an equal score and lower index.
+    rng = np.random.default_rng(7)
+    for trial in range(30):
+        S = [1, 4, 16][trial % 3]
+        G = [1, 2, 4][(trial // 3) % 3]
+        d, n = 4, 12
+        L = n * S + (trial % 5)
+        Q = rng.integers(-2, 3, (1, G, L, d)).astype(np.float32)
+        K = rng.integers(-2, 3, (1, 1, L, d)).astype(np.float32)
+        # plant exact ties: copy some chunks onto others
+        for _ in range(4):
+            a, b = rng.integers(0, n, 2)
+            K[0, 0, a * S:(a + 1) * S] = K[0, 0, b * S:(b + 1) * S]
+        V = rng.standard_normal((1, 1, L, d)).astype(np.float32)
+        topk = int(rng.integers(1, 7))
+        r = oracle.hsa_prefill(Q, K, V, S=S, topk=topk)
+        nfull = L // S
+        ksum = K[0, 0, : nfull * S].reshape(nfull, S, d).sum(1).astype(np.int64)
+        for t in range(L):
+            avail = min(t // S, nfull)
+            u = Q[0, :, t].astype(np.int64).sum(0)
+            score = ksum[:avail] @ u
+            rank = np.array([np.sum(score > score[c]) + np.sum((score == score[c]) &
+                                                               (np.arange(avail) < c))
+                             for c in range(avail)], dtype=np.int64)
+            expect = [-1] * topk
+            for c in range(avail):
+                if rank[c] < topk:
+                    expect[rank[c]] = c
+            assert list(r["sel"][0, 0, t]) == expect, (trial, t)
+
+
+def test_fusion_weights_are_a_softmax_of_head_scores():
+    B, Hq, Hkv, L, d, S, K_ = 1, 4, 2, 256, 16, 16, 4
+    Q = f32((B, Hq, L, d), 8, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 8, synth.TID_K)
+    V = f32((B, Hkv, L, d), 8, synth.TID_V)
+    r = oracle.hsa_prefill(Q, K, V, S=S, topk=K_)
+    w, sel = r["w"], r["sel"]
+    # per-head scores from chunk means (sqrt(S)*mean == sum/sqrt(S))
+    lm = K.astype(np.float64)[:, :, :(L // S) * S].reshape(B, Hkv, L // S, S, d).mean(3) * 4.0
+    for h in range(Hq):
+        for t in range(L):
+            m = int((sel[0, h // 2, t] >= 0).sum())
+            assert m == min(K_, t // S)
+            if m == 0:
+                assert not w[0, h, t].any()
+                continue
+            ww = w[0, h, t, :m]
+            assert abs(ww.sum() - 1) < 1e-12 and (ww > 0).all() and not w[0, h, t, m:].any()
+            s = lm[0, h // 2, sel[0, h // 2, t, :m]] @ Q[0, h, t].astype(np.float64) / 4.0
+            # weights are exp(s)/sum exp(s): log-ratios equal score differences
+            np.testing.assert_allclose(np.log(ww) - np.log(ww[0]), s - s[0], atol=1e-9)
+
+
+def test_causality_and_unselected_chunks():
+    B, Hq, Hkv, L, d, S, K_ = 1, 2, 1, 192, 8, 16, 3
+    Q = f32((B, Hq, L, d), 9, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 9, synth.TID_K)
+    V = f32((B, Hkv, L, d), 9, synth.TID_V)
+    base = oracle.hsa_prefill(Q, K, V, S=S, topk=K_)
+    t = 150  # chunks 0..8 are fully before t=150 (9*16 = 144 <= 150)
+    K2, V2, Q2 = K.copy(), V.copy(), Q.copy()
+    K2[:, :, 144:] += 7.0
+    V2[:, :, 144:] -= 3.0
+    Q2[:, :, t + 1:] *= -1
+    Q2[:, :, :t] += 1
+    r = oracle.hsa_prefill(Q2, K2, V2, S=S, topk=K_, rows=[t])
+    np.testing.assert_array_equal(r["out"][:, :, 0], base["out"][:, :, t])
+    # values of chunks not selected for t do not matter
+    chosen = set(base["sel"][0, 0, t].tolist())
+    V3 = V.copy()
+    for c in range(9):
+        if c not in chosen:
+            V3[:, :, c * S:(c + 1) * S] = 100.0
+    r3 = oracle.hsa_prefill(Q, K, V3, S=S, topk=K_, rows=[t])
+    np.testing.assert_array_equal(r3["out"][:, :, 0], base["out"][:, :, t])
+    # but moving a selected chunk's values does
+    V3[:, :, min(chosen) * S] += 1.0
+    r4 = oracle.hsa_prefill(Q, K, V3, S=S, topk=K_, rows=[t])
+    assert not np.array_equal(r4["out"][:, :, 0], base["out"][:, :, t])
+
+
+def test_gqa_group_selection():
+    L, d, S, K_ = 256, 16, 16, 4
+    q0 = f32((1, 1, L, d), 10, synth.TID_Q)
+    K = f32((1, 1, L, d), 10, synth.TID_K)
+    V = f32((1, 1, L, d), 10, synth.TID_V)
+    single = oracle.hsa_prefill(q0, K, V, S=S, topk=K_)
+    rep = oracle.hsa_prefill(np.repeat(q0, 4, axis=1), K, V, S=S, topk=K_)
+    np.testing.assert_array_equal(rep["sel"], single["sel"])
+    for h in range(4):
+        np.testing.assert_array_equal(rep["out"][:, h], single["out"][:, 0])
+    # with distinct heads the group ranks the summed scores
+    Q = f32((1, 2, L, d), 11, synth.TID_Q)
+    both = oracle.hsa_prefill(Q, K, V, S=S, topk=K_)
+    lm = oracle.landmarks(K, S)[0, 0]
+    for t in (100, 200, 255):
+        u = Q[0, :, t].astype(np.float64).sum(0)
+        sc = lm[: t // S] @ u
+        order = np.lexsort((np.arange(len(sc)), -sc))[:K_]
+        assert list(both["sel"][0, 0, t]) == list(order)
+
+
+def test_sel_padding_and_short_sequences():
+    Q = f32((1, 1, 20, 4), 12, synth.TID_Q)
+    K = f32((1, 1, 20, 4), 12, synth.TID_K)
+    r = oracle.hsa_prefill(Q, K, K.copy(), S=64, topk=4)  # L < S: no chunk at all
+    assert not r["out"].any() and (r["sel"] == -1).all() and np.isinf(r["margin"]).all()
+
+
+# ---------------------------------------------------------------- decode
+
+
+def test_decode_matches_prefill_row():
+    # A decode query at position n_ctx equals the prefill row t = n_ctx with
+    # the same context (landmarks rounded to fp32 on the decode side).
+    B, Hq, Hkv, N, d, S, K_ = 1, 4, 2, 320, 16, 16, 4
+    Q = f32((B, Hq, N + 1, d), 13, synth.TID_Q)
+    K = f32((B, Hkv, N + 1, d), 13, synth.TID_K)
+    V = f32((B, Hkv, N + 1, d), 13, synth.TID_V)
+    pre = oracle.hsa_prefill(Q, K, V, S=S, topk=K_, rows=[N])
+    lmk = oracle.landmarks(K[:, :, :N], S).astype(np.float32)
+    dec = oracle.hsa_decode(Q[:, :, N], K[:, :, :N], V[:, :, :N], lmk, S=S, n_ctx=N, topk=K_)
+    np.testing.assert_array_equal(dec["sel"], pre["sel"][:, :, 0])
+    np.testing.assert_allclose(dec["out"], pre["out"][:, :, 0], rtol=0, atol=1e-6)
+
+
+def test_needle_retrieved_at_rank_one():
+    # Downscaled version of the 16M-token needle workload: the planted chunk
+    # (keys = 3 * group query direction) must rank first in every group.
+    B, Hq, Hkv, d, S, n = 1, 8, 2, 64, 64, 1024
+    q = synth.normal((B, Hq, d), synth.BF16, 4, synth.TID_QDEC)
+    K = synth.normal((B, Hkv, n * S, d), synth.BF16, 4, synth.TID_K)
+    cstar = synth.pick_index(n, 4)
+    for g in range(Hkv):
+        K[0, g, cstar * S:(cstar + 1) * S] = synth.needle_key(q[0, g * 4:(g + 1) * 4], True)
+    lmk = oracle.landmarks(K, S).astype(np.float32)
+    sel, margin = oracle.hsa_decode_select(q, lmk, S, n * S, 16, Hkv)
+    assert (sel[0, :, 0] == cstar).all()
+
+
+# ---------------------------------------------------------------- DHSA
+
+
+def test_dhsa_budget_covering_everything_is_dense_causal():
+    L, d, H = 96, 8, 2
+    Q, K, V = (f32((1, H, L, d), 14, t) for t in (synth.TID_Q, synth.TID_K, synth.TID_V))
+    offs = synth.chunk_offsets(L, 3, 17, seed=14)
+    r = oracle.dhsa_prefill(Q, K, V, offs, budget=L)
+    for h in range(H):
+        ref = dense_attention(Q[0, h], K[0, h], V[0, h], causal_strict=False)
+        np.testing.assert_allclose(r["out"][0, h], ref, rtol=0, atol=1e-12)
+    assert (r["n_kept"][0, 0] == np.arange(1, L + 1)).all()
+
+
+def test_dhsa_unit_chunks_is_topk_token_attention():
+    # With every chunk of length 1, q_hat = q and k_hat = k, so the token map
+    # is the exact q.k score: keep the N_b largest among j <= i (ties lower j).
+    L, d, Nb = 64, 8, 9
+    Q, K, V = (f32((1, 1, L, d), 15, t) for t in (synth.TID_Q, synth.TID_K, synth.TID_V))
+    offs = np.arange(L + 1, dtype=np.int32)
+    r = oracle.dhsa_prefill(Q, K, V, offs, budget=Nb, want_kept=True)
+    q, k, v = (a[0, 0].astype(np.float64) for a in (Q, K, V))
+    for i in range(L):
+        raw = k[: i + 1] @ q[i]
+        keep = np.lexsort((np.arange(i + 1), -raw))[: min(Nb, i + 1)]
+        mask = np.zeros(L, np.uint8)
+        mask[keep] = 1
+        np.testing.assert_array_equal(r["kept"][0, 0, i], mask)
+        ref = softmax(raw[keep] / math.sqrt(d)) @ v[keep]
+        np.testing.assert_allclose(r["out"][0, 0, i], ref, rtol=0, atol=1e-12)
+
+
+def test_dhsa_equal_chunks_brute_force_token_map():
+    # Brute force on a tiny input: materialise the L x L token map by tiling
+    # S_c over chunk pairs, mask j > i, order each row by (score desc, j asc).
+    L, d, C, Nb = 48, 4, 6, 13
+    Q, K, V = (f32((1, 1, L, d), 16, t) for t in (synth.TID_Q, synth.TID_K, synth.TID_V))
+    offs = np.arange(0, L + 1, C, dtype=np.int32)
+    r = oracle.dhsa_prefill(Q, K, V, offs, budget=Nb, want_kept=True, want_sc=True)
+    q, k, v = (a[0, 0].astype(np.float64) for a in (Q, K, V))
+    qh = q.reshape(-1, C, d).mean(1) * math.sqrt(C)
+    kh = k.reshape(-1, C, d).mean(1) * math.sqrt(C)
+    Sc = qh @ kh.T
+    np.testing.assert_allclose(r["sc"][0, 0], Sc, rtol=1e-13, atol=1e-13)
+    St = np.kron(Sc, np.ones((C, C)))
+    for i in range(L):
+        keep = np.lexsort((np.arange(i + 1), -St[i, : i + 1]))[: min(Nb, i + 1)]
+        mask = np.zeros(L, np.uint8)
+        mask[keep] = 1
+        np.testing.assert_array_equal(r["kept"][0, 0, i], mask)
+        ref = softmax(k[keep] @ q[i] / math.sqrt(d)) @ v[keep]
+        np.testing.assert_allclose(r["out"][0, 0, i], ref, rtol=0, atol=1e-12)
+
+
+def test_dhsa_eq4_identity_and_length_bias():
+    # (S_c)_{l,k} = sqrt(|C_l||C_k|) (mean q_l . mean k_k): the sqrt|C| scaling
+    # makes scores grow with chunk size for chunks of equal mean.
+    L, d = 200, 8
+    Q, K, V = (f32((1, 1, L, d), 17, t) for t in (synth.TID_Q, synth.TID_K, synth.TID_V))
+    offs = synth.chunk_offsets(L, 2, 30, seed=17)
+    r = oracle.dhsa_prefill(Q, K, V, offs, budget=20, want_sc=True, rows=[0])
+    lens = np.diff(offs)
+    qbar = np.stack([Q[0, 0, a:b].astype(np.float64).mean(0) for a, b in zip(offs, offs[1:])])
+    kbar = np.stack([K[0, 0, a:b].astype(np.float64).mean(0) for a, b in zip(offs, offs[1:])])
+    ident = np.sqrt(np.outer(lens, lens)) * (qbar @ kbar.T)
+    np.testing.assert_allclose(r["sc"][0, 0], ident, rtol=1e-12, atol=1e-12)
+    # equal-mean chunks of lengths 4 and 16: the longer one scores 2x higher
+    u = np.ones(d, np.float32)
+    Kb = np.concatenate([np.tile(u, (4, 1)), np.tile(u, (16, 1))])[None, None]
+    Qb = np.tile(u, (20, 1))[None, None]
+    rb = oracle.dhsa_prefill(Qb, Kb, Kb.copy(), np.array([0, 4, 20], np.int32), budget=20,
+                             want_sc=True, rows=[19])
+    assert rb["sc"][0, 0, 1, 1] == pytest.approx(2 * rb["sc"][0, 0, 1, 0])
+
+
+def test_dhsa_margin_and_cut_structure():
+    L, d, Nb = 300, 8, 64
+    Q, K, V = (f32((1, 1, L, d), 18, t) for t in (synth.TID_Q, synth.TID_K, synth.TID_V))
+    offs = synth.chunk_offsets(L, 16, 40, seed=18)
+    r = oracle.dhsa_prefill(Q, K, V, offs, budget=Nb, want_kept=True, want_sc=True)
+    chunk_of = np.repeat(np.arange(len(offs) - 1), np.diff(offs))
+    for i in range(L):
+        kept = np.flatnonzero(r["kept"][0, 0, i])
+        assert len(kept) == min(Nb, i + 1) and kept.max() <= i
+        if i + 1 <= Nb:
+            assert np.isinf(r["margin"][0, 0, i])
+            continue
+        # at most one chunk is partially kept, and it keeps its lowest tokens
+        partial = [c for c in np.unique(chunk_of[kept])
+                   if np.sum(chunk_of[kept] == c) < min(np.sum(chunk_of[: i + 1] == c), 1 << 30)]
+        assert len(partial) <= 1
+        for c in partial:
+            toks = kept[chunk_of[kept] == c]
+            assert toks[0] == offs[c] and (np.diff(toks) == 1).all()
+        assert r["margin"][0, 0, i] >= 0
