@@ -1,0 +1,254 @@
+"""Hierarchical sparse attention (HSA / DHSA) forward pass for MI355X (gfx950).
+
+A thin ctypes binding over libhsa_attn.so, whose C ABI is declared in
+include/hsa_attn.h.  Python only marshals arguments: it checks tensors,
+allocates outputs and workspaces with torch (device memory) and passes raw
+pointers plus torch's current HIP stream.  Every step of the computation runs
+in the library's HIP kernels; there is no other code path.  If the library is
+not built, every call raises.
+"""
+import ctypes
+import os
+
+import torch  # loaded first: the library binds to the HIP runtime torch has loaded
+
+from . import build as _build
+
+__all__ = [
+    "HsaError", "hsa_status_string", "hsa_build_landmarks", "hsa_prefill",
+    "hsa_prefill_workspace_size", "hsa_decode", "hsa_decode_workspace_size",
+    "dhsa_prefill", "dhsa_prefill_workspace_size", "lib_path", "load_library",
+]
+
+HSA_OK = 0
+HSA_ERR_INVALID_ARGUMENT = 1
+HSA_ERR_UNSUPPORTED = 2
+HSA_ERR_WORKSPACE_TOO_SMALL = 3
+HSA_ERR_HIP = 4
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_Z = ctypes.c_size_t
+
+_lib = None
+
+
+class HsaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{hsa_status_string(status)} ({message})")
+        self.status = status
+
+
+def lib_path():
+    return _build.LIB
+
+
+def load_library():
+    """Load libhsa_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        raise RuntimeError(f"{_build.LIB} is not built: run __graft_entry__.build() "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(_build.LIB)
+    sig = {
+        "hsa_status_string": ([_I], ctypes.c_char_p),
+        "hsa_last_error_message": ([], ctypes.c_char_p),
+        "hsa_build_landmarks": ([_P, _P, _I, _I, _L, _I, _I, _L, _L, _I, _P], _I),
+        "hsa_prefill_workspace_size": ([_I, _L, _I, _I, _I, _I, _I, _I], _Z),
+        "hsa_prefill": ([_P, _P, _P, _P, _P, _P, _P, _I, _L, _I, _I, _I, _I, _I, _I, _P, _Z,
+                         _P], _I),
+        "hsa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _L], _Z),
+        "hsa_decode": ([_P, _P, _P, _P, _L, _L, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _Z,
+                        _P], _I),
+        "dhsa_prefill_workspace_size": ([_I, _L, _I, _I, _I, _I], _Z),
+        "dhsa_prefill": ([_P, _P, _P, _P, _I, _L, _P, _P, _P, _I, _L, _I, _I, _I, _P, _Z, _P],
+                         _I),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def hsa_status_string(status):
+    return load_library().hsa_status_string(status).decode()
+
+
+def _check(status):
+    if status != HSA_OK:
+        msg = load_library().hsa_last_error_message().decode()
+        raise HsaError(status, msg)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _need(t, name, ndim, dtype=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def hsa_build_landmarks(K, S, chunk_begin=0, chunk_end=None, lmk=None):
+    """Landmarks of K [B,Hkv,L,d]: fp32 [B,Hkv,L//S,d], the sum of each
+    chunk's S keys / sqrt(S).  With `lmk` given, only chunks
+    chunk_begin..chunk_end-1 are (re)written in place."""
+    _need(K, "K", 4)
+    B, Hkv, L, d = K.shape
+    n = L // S
+    if chunk_end is None:
+        chunk_end = n
+    if lmk is None:
+        lmk = torch.empty((B, Hkv, n, d), dtype=torch.float32, device=K.device)
+    _need(lmk, "lmk", 4, torch.float32)
+    _check(load_library().hsa_build_landmarks(K.data_ptr(), lmk.data_ptr(), B, Hkv, L, d, S,
+                                              chunk_begin, chunk_end, _dtype_code(K),
+                                              _stream(K)))
+    return lmk
+
+
+def hsa_prefill_workspace_size(B, L, Hq, Hkv, d, S, topk, dtype):
+    code = _dtype_code(torch.empty(0, dtype=dtype))
+    return load_library().hsa_prefill_workspace_size(B, L, Hq, Hkv, d, S, topk, code)
+
+
+def hsa_prefill(Q, K, V, S, topk, lmk=None, out=None, return_selection=False, workspace=None):
+    """HSA prefill.  Q [B,Hq,L,d], K and V [B,Hkv,L,d] (same dtype).
+
+    Returns O [B,Hq,L,d]; with return_selection also sel_idx int32
+    [B,Hkv,L,topk] (-1 padded) and sel_w fp32 [B,Hq,L,topk]."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, Q.dtype)
+    _need(V, "V", 4, Q.dtype)
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (B, Hkv, L, d) or V.shape != K.shape:
+        raise ValueError("K and V must be [B,Hkv,L,d] matching Q")
+    if lmk is not None:
+        _need(lmk, "lmk", 4, torch.float32)
+    if out is None:
+        out = torch.empty_like(Q)
+    sel_idx = sel_w = None
+    if return_selection:
+        sel_idx = torch.empty((B, Hkv, L, topk), dtype=torch.int32, device=Q.device)
+        sel_w = torch.empty((B, Hq, L, topk), dtype=torch.float32, device=Q.device)
+    lib = load_library()
+    code = _dtype_code(Q)
+    nbytes = lib.hsa_prefill_workspace_size(B, L, Hq, Hkv, d, S, topk, code)
+    ws = _workspace(nbytes, Q.device, workspace) if nbytes else None
+    _check(lib.hsa_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr(lmk), out.data_ptr(),
+                           _ptr(sel_idx), _ptr(sel_w), B, L, Hq, Hkv, d, S, topk, code, _ptr(ws),
+                           nbytes, _stream(Q)))
+    if return_selection:
+        return out, sel_idx, sel_w
+    return out
+
+
+def hsa_decode_workspace_size(B, Hq, Hkv, d, S, topk, n_ctx):
+    return load_library().hsa_decode_workspace_size(B, Hq, Hkv, d, S, topk, n_ctx)
+
+
+def hsa_decode(q, Kc, Vc, lmk, n_ctx, S, topk, out=None, return_selection=False,
+               workspace=None):
+    """HSA decode.  q [B,Hq,d], caches Kc, Vc [B,Hkv,n_max,d], landmarks
+    fp32 [B,Hkv,n_max//S,d]; the query sits at position n_ctx."""
+    _need(q, "q", 3)
+    _need(Kc, "Kc", 4, q.dtype)
+    _need(Vc, "Vc", 4, q.dtype)
+    _need(lmk, "lmk", 4, torch.float32)
+    B, Hq, d = q.shape
+    Hkv, n_max = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, Hkv, n_max, d) or Vc.shape != Kc.shape:
+        raise ValueError("Kc and Vc must be [B,Hkv,n_max,d] matching q")
+    if lmk.shape != (B, Hkv, n_max // S, d):
+        raise ValueError("lmk must be [B,Hkv,n_max//S,d]")
+    if out is None:
+        out = torch.empty_like(q)
+    sel_idx = sel_w = None
+    if return_selection:
+        sel_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+        sel_w = torch.empty((B, Hq, topk), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    nbytes = lib.hsa_decode_workspace_size(B, Hq, Hkv, d, S, topk, n_ctx)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    _check(lib.hsa_decode(q.data_ptr(), Kc.data_ptr(), Vc.data_ptr(), lmk.data_ptr(), n_ctx,
+                          n_max, out.data_ptr(), _ptr(sel_idx), _ptr(sel_w), B, Hq, Hkv, d, S,
+                          topk, _dtype_code(q), _ptr(ws), nbytes, _stream(q)))
+    if return_selection:
+        return out, sel_idx, sel_w
+    return out
+
+
+def dhsa_prefill_workspace_size(B, L, H, d, n_chunks, dtype):
+    code = _dtype_code(torch.empty(0, dtype=dtype))
+    return load_library().dhsa_prefill_workspace_size(B, L, H, d, n_chunks, code)
+
+
+def dhsa_prefill(Q, K, V, offsets, budget, out=None, return_mask=False, return_order=False,
+                 workspace=None):
+    """DHSA prefill.  Q, K, V [B,H,L,d] bf16; offsets: host int32 chunk
+    boundaries [n+1] (0 .. L); budget N_b.
+
+    Returns O, plus the uint32 mask bits [B,H,L,ceil(L/32)] and/or the chunk
+    order int32 [B,H,n,n] when requested."""
+    import numpy as np
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, Q.dtype)
+    _need(V, "V", 4, Q.dtype)
+    B, H, L, d = Q.shape
+    if K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K and V must have the same shape")
+    offs = np.ascontiguousarray(offsets, dtype=np.int32)
+    nc = len(offs) - 1
+    if out is None:
+        out = torch.empty_like(Q)
+    mask = order = None
+    if return_mask:
+        mask = torch.empty((B, H, L, (L + 31) // 32), dtype=torch.int32, device=Q.device)
+    if return_order:
+        order = torch.empty((B, H, nc, nc), dtype=torch.int32, device=Q.device)
+    lib = load_library()
+    code = _dtype_code(Q)
+    nbytes = lib.dhsa_prefill_workspace_size(B, L, H, d, nc, code)
+    ws = _workspace(nbytes, Q.device, workspace) if nbytes else None
+    _check(lib.dhsa_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), offs.ctypes.data, nc,
+                            budget, out.data_ptr(), _ptr(mask), _ptr(order), B, L, H, d, code,
+                            _ptr(ws), nbytes, _stream(Q)))
+    res = [out]
+    if return_mask:
+        res.append(mask)
+    if return_order:
+        res.append(order)
+    return res[0] if len(res) == 1 else tuple(res)

@@ -1,0 +1,388 @@
+// api.cpp - the C ABI of libhsa_attn (declared in include/hsa_attn.h):
+// host-side argument validation, workspace carving, launch sequencing.
+// Nothing is enqueued until every argument has been checked.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "hsa_attn.h"
+#include "kernels.h"
+
+namespace hsa {
+int64_t decode_max_chunks(int topk);
+int dhsa_max_chunks();
+}  // namespace hsa
+
+namespace {
+
+thread_local std::string g_err;
+
+hsa_status_t fail(hsa_status_t s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+hsa_status_t hip_fail(hipError_t e, const char* where) {
+  g_err = std::string(where) + ": " + hipGetErrorString(e);
+  return HSA_ERR_HIP;
+}
+
+bool dtype_ok(hsa_dtype_t dt) { return dt == HSA_DTYPE_F32 || dt == HSA_DTYPE_BF16; }
+int elem_bytes(hsa_dtype_t dt) { return dt == HSA_DTYPE_F32 ? 4 : 2; }
+int dt_code(hsa_dtype_t dt) { return dt == HSA_DTYPE_F32 ? hsa::kF32 : hsa::kBF16; }
+
+constexpr size_t kAlign = 256;
+
+// Carves aligned sub-buffers out of a workspace; with base == nullptr it
+// only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+// Total (token, slot) selections of one (b, group) in prefill.
+int64_t prefill_entries(int64_t L, int S, int topk) {
+  const int64_t n = L / S;
+  int64_t e = 0;
+  for (int64_t c = 0; c < n; ++c) e += (int64_t)S * (c < topk ? c : topk);
+  e += (L - n * S) * (n < topk ? n : topk);
+  return e;
+}
+
+hsa_status_t check_prefill(int B, int64_t L, int Hq, int Hkv, int d, int S, int topk,
+                           hsa_dtype_t dt) {
+  if (!dtype_ok(dt)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (B < 0 || L < 0) return fail(HSA_ERR_INVALID_ARGUMENT, "B and L must be >= 0");
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "Hq and Hkv must be positive with Hq % Hkv == 0");
+  if (Hq / Hkv > 32) return fail(HSA_ERR_UNSUPPORTED, "Hq / Hkv must be <= 32");
+  if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (S < 1 || S > 1024) return fail(HSA_ERR_INVALID_ARGUMENT, "chunk size S must be in [1, 1024]");
+  if (topk < 1 || topk > 32) return fail(HSA_ERR_INVALID_ARGUMENT, "topk must be in [1, 32]");
+  if ((int64_t)B * Hkv * L * topk >= (int64_t)1 << 31 ||
+      (int64_t)B * Hq * L * topk >= (int64_t)1 << 31)
+    return fail(HSA_ERR_UNSUPPORTED, "B*H*L*topk must be < 2^31");
+  return HSA_OK;
+}
+
+struct PrefillLayout {
+  float* lmk;
+  int32_t* idx;
+  int32_t *counts, *cursor, *offs, *tile_off, *list;
+  void* partial;
+  float* part_score;
+  size_t bytes;
+};
+
+PrefillLayout prefill_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d, int S,
+                             int topk, hsa_dtype_t dt) {
+  Carver cv(ws);
+  PrefillLayout p;
+  const int64_t n = L / S;
+  const int64_t BG = (int64_t)B * Hkv;
+  p.lmk = cv.take<float>((size_t)(BG * n * d));
+  p.idx = cv.take<int32_t>((size_t)(BG * L * topk));
+  p.counts = cv.take<int32_t>((size_t)(BG * n));
+  p.cursor = cv.take<int32_t>((size_t)(BG * n));
+  p.offs = cv.take<int32_t>((size_t)(BG * (n + 1)));
+  p.tile_off = cv.take<int32_t>((size_t)(BG * (n + 1)));
+  p.list = cv.take<int32_t>((size_t)(BG * L * topk));
+  p.partial = cv.take<char>((size_t)((int64_t)B * Hq * L * topk * d * elem_bytes(dt)));
+  p.part_score = cv.take<float>((size_t)((int64_t)B * Hq * L * topk));
+  p.bytes = cv.off + kAlign;
+  return p;
+}
+
+hsa_status_t check_decode(int B, int Hq, int Hkv, int d, int S, int topk, int64_t n_ctx,
+                          int64_t n_max, hsa_dtype_t dt) {
+  hsa_status_t s = check_prefill(B, 1, Hq, Hkv, d, S, topk, dt);
+  if (s != HSA_OK) return s;
+  if (n_ctx < 0 || n_max < n_ctx)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "need 0 <= n_ctx <= n_max");
+  if (n_ctx / S > hsa::decode_max_chunks(topk))
+    return fail(HSA_ERR_UNSUPPORTED, "too many chunks in the context for this topk");
+  return HSA_OK;
+}
+
+struct DecodeLayout {
+  uint64_t* cand;
+  int32_t* sel;
+  float* part_o;
+  float* part_s;
+  int n_slices, slice;
+  size_t bytes;
+};
+
+DecodeLayout decode_layout(void* ws, int B, int Hq, int Hkv, int d, int S, int topk,
+                           int64_t n_ctx) {
+  DecodeLayout p;
+  hsa::decode_plan(n_ctx / S, topk, (int64_t)B * Hkv, &p.n_slices, &p.slice);
+  Carver cv(ws);
+  p.cand = cv.take<uint64_t>((size_t)B * Hkv * p.n_slices * topk);
+  p.sel = cv.take<int32_t>((size_t)B * Hkv * topk);
+  p.part_o = cv.take<float>((size_t)B * Hq * topk * d);
+  p.part_s = cv.take<float>((size_t)B * Hq * topk);
+  p.bytes = cv.off + kAlign;
+  return p;
+}
+
+struct DhsaLayout {
+  int32_t* offs;
+  float *qh, *kh, *sc;
+  int32_t *order, *cumlen, *diag_pos;
+  size_t bytes;
+};
+
+DhsaLayout dhsa_layout(void* ws, int B, int H, int d, int nc) {
+  Carver cv(ws);
+  DhsaLayout p;
+  const int64_t BH = (int64_t)B * H;
+  p.offs = cv.take<int32_t>((size_t)nc + 1);
+  p.qh = cv.take<float>((size_t)(BH * nc * d));
+  p.kh = cv.take<float>((size_t)(BH * nc * d));
+  p.sc = cv.take<float>((size_t)(BH * nc * nc));
+  p.order = cv.take<int32_t>((size_t)(BH * nc * nc));
+  p.cumlen = cv.take<int32_t>((size_t)(BH * nc * (nc + 1)));
+  p.diag_pos = cv.take<int32_t>((size_t)(BH * nc));
+  p.bytes = cv.off + kAlign;
+  return p;
+}
+
+void* align_ws(void* ws) {
+  return (void*)(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hsa_status_string(hsa_status_t status) {
+  switch (status) {
+    case HSA_OK: return "HSA_OK: success";
+    case HSA_ERR_INVALID_ARGUMENT: return "HSA_ERR_INVALID_ARGUMENT: invalid argument";
+    case HSA_ERR_UNSUPPORTED: return "HSA_ERR_UNSUPPORTED: request not supported by this build";
+    case HSA_ERR_WORKSPACE_TOO_SMALL: return "HSA_ERR_WORKSPACE_TOO_SMALL: workspace too small";
+    case HSA_ERR_HIP: return "HSA_ERR_HIP: a HIP call failed";
+  }
+  return "unknown hsa_status_t";
+}
+
+const char* hsa_last_error_message(void) { return g_err.c_str(); }
+
+hsa_status_t hsa_build_landmarks(const void* K, float* lmk, int B, int Hkv, int64_t L, int d,
+                                 int S, int64_t chunk_begin, int64_t chunk_end,
+                                 hsa_dtype_t dtype, hsa_stream_t stream) {
+  g_err.clear();
+  if (!dtype_ok(dtype)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (B < 0 || Hkv <= 0 || L < 0) return fail(HSA_ERR_INVALID_ARGUMENT, "bad B, Hkv or L");
+  if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (S < 1 || S > 1024) return fail(HSA_ERR_INVALID_ARGUMENT, "chunk size S must be in [1, 1024]");
+  const int64_t n = L / S;
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > n)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "need 0 <= chunk_begin <= chunk_end <= L/S");
+  if ((int64_t)B * Hkv * (chunk_end - chunk_begin) >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "too many chunks for one launch");
+  if (B == 0 || chunk_end == chunk_begin) return HSA_OK;
+  if (!K || !lmk) return fail(HSA_ERR_INVALID_ARGUMENT, "K and lmk must not be NULL");
+  hipError_t e = hsa::launch_landmarks(K, dt_code(dtype), lmk, (int64_t)B * Hkv, L, n, d, S,
+                                       chunk_begin, chunk_end, (hipStream_t)stream);
+  return e == hipSuccess ? HSA_OK : hip_fail(e, "hsa_build_landmarks launch");
+}
+
+size_t hsa_prefill_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S, int topk,
+                                  hsa_dtype_t dtype) {
+  if (check_prefill(B, L, Hq, Hkv, d, S, topk, dtype) != HSA_OK) return 0;
+  return prefill_layout(nullptr, B, L, Hq, Hkv, d, S, topk, dtype).bytes;
+}
+
+hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const float* lmk,
+                         void* O, int32_t* sel_idx, float* sel_w, int B, int64_t L, int Hq,
+                         int Hkv, int d, int S, int topk, hsa_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, hsa_stream_t stream) {
+  g_err.clear();
+  hsa_status_t s = check_prefill(B, L, Hq, Hkv, d, S, topk, dtype);
+  if (s != HSA_OK) return s;
+  if (B == 0 || L == 0) return HSA_OK;
+  if (!Q || !K || !V || !O) return fail(HSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must not be NULL");
+  const size_t need = prefill_layout(nullptr, B, L, Hq, Hkv, d, S, topk, dtype).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(need) + " bytes");
+  PrefillLayout lay = prefill_layout(align_ws(workspace), B, L, Hq, Hkv, d, S, topk, dtype);
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t n = L / S;
+  const int G = Hq / Hkv;
+  hsa::PrefillArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.lmk = lmk ? lmk : lay.lmk;
+  a.idx = sel_idx ? sel_idx : lay.idx;
+  a.sel_w = sel_w;
+  a.counts = lay.counts;
+  a.cursor = lay.cursor;
+  a.offs = lay.offs;
+  a.tile_off = lay.tile_off;
+  a.list = lay.list;
+  a.partial = lay.partial;
+  a.part_score = lay.part_score;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.S = S;
+  a.topk = topk;
+  a.dtype = dt_code(dtype);
+  a.L = L;
+  a.n = n;
+  a.entries_per_tile = hsa::prefill_entries_per_tile(a.dtype, G);
+  a.tiles_ub = prefill_entries(L, S, topk) / a.entries_per_tile + n + 1;
+  if ((int64_t)B * Hkv * a.tiles_ub >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
+  hipError_t e;
+  if (!lmk && n > 0) {
+    e = hsa::launch_landmarks(K, a.dtype, lay.lmk, (int64_t)B * Hkv, L, n, d, S, 0, n, st);
+    if (e != hipSuccess) return hip_fail(e, "landmarks");
+  }
+  if ((e = hsa::prefill_select(a, st)) != hipSuccess) return hip_fail(e, "select");
+  if ((e = hsa::prefill_invert(a, st)) != hipSuccess) return hip_fail(e, "invert");
+  if ((e = hsa::prefill_attend(a, st)) != hipSuccess) return hip_fail(e, "attend");
+  if ((e = hsa::prefill_fuse(a, st)) != hipSuccess) return hip_fail(e, "fuse");
+  return HSA_OK;
+}
+
+size_t hsa_decode_workspace_size(int B, int Hq, int Hkv, int d, int S, int topk,
+                                 int64_t n_ctx) {
+  if (check_decode(B, Hq, Hkv, d, S, topk, n_ctx, n_ctx, HSA_DTYPE_BF16) != HSA_OK) return 0;
+  return decode_layout(nullptr, B, Hq, Hkv, d, S, topk, n_ctx).bytes;
+}
+
+hsa_status_t hsa_decode(const void* q, const void* Kc, const void* Vc, const float* lmk,
+                        int64_t n_ctx, int64_t n_max, void* o, int32_t* sel_idx, float* sel_w,
+                        int B, int Hq, int Hkv, int d, int S, int topk, hsa_dtype_t dtype,
+                        void* workspace, size_t workspace_bytes, hsa_stream_t stream) {
+  g_err.clear();
+  hsa_status_t s = check_decode(B, Hq, Hkv, d, S, topk, n_ctx, n_max, dtype);
+  if (s != HSA_OK) return s;
+  if (B == 0) return HSA_OK;
+  if (!q || !o) return fail(HSA_ERR_INVALID_ARGUMENT, "q and o must not be NULL");
+  if (n_ctx / S > 0 && (!Kc || !Vc || !lmk))
+    return fail(HSA_ERR_INVALID_ARGUMENT, "Kc, Vc and lmk must not be NULL");
+  const size_t need = decode_layout(nullptr, B, Hq, Hkv, d, S, topk, n_ctx).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(need) + " bytes");
+  DecodeLayout lay = decode_layout(align_ws(workspace), B, Hq, Hkv, d, S, topk, n_ctx);
+  hsa::DecodeArgs a;
+  a.q = q;
+  a.Kc = Kc;
+  a.Vc = Vc;
+  a.lmk = lmk;
+  a.o = o;
+  a.sel = sel_idx ? sel_idx : lay.sel;
+  a.sel_w = sel_w;
+  a.cand = lay.cand;
+  a.part_o = lay.part_o;
+  a.part_s = lay.part_s;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.S = S;
+  a.topk = topk;
+  a.dtype = dt_code(dtype);
+  a.n_ctx = n_ctx;
+  a.n_max = n_max;
+  a.n_avail = n_ctx / S;
+  a.lmk_chunks = n_max / S;
+  a.n_slices = lay.n_slices;
+  a.slice = lay.slice;
+  hipError_t e = hsa::decode_run(a, (hipStream_t)stream);
+  return e == hipSuccess ? HSA_OK : hip_fail(e, "decode");
+}
+
+size_t dhsa_prefill_workspace_size(int B, int64_t L, int H, int d, int n_chunks,
+                                   hsa_dtype_t dtype) {
+  (void)L;
+  if (!dtype_ok(dtype) || B < 0 || H <= 0 || n_chunks < 1 || n_chunks > hsa::dhsa_max_chunks())
+    return 0;
+  if (d != 64 && d != 128) return 0;
+  return dhsa_layout(nullptr, B, H, d, n_chunks).bytes;
+}
+
+hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int32_t* offsets,
+                          int n_chunks, int64_t budget, void* O, uint32_t* mask_bits,
+                          int32_t* chunk_order, int B, int64_t L, int H, int d,
+                          hsa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                          hsa_stream_t stream) {
+  g_err.clear();
+  if (!dtype_ok(dtype)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (dtype != HSA_DTYPE_BF16) return fail(HSA_ERR_UNSUPPORTED, "dhsa_prefill runs bf16 only");
+  if (B < 0 || L < 1 || H <= 0) return fail(HSA_ERR_INVALID_ARGUMENT, "need B >= 0, L >= 1, H >= 1");
+  if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (budget < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "budget N_b must be >= 1");
+  if (!offsets) return fail(HSA_ERR_INVALID_ARGUMENT, "offsets must not be NULL");
+  if (n_chunks < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "n_chunks must be >= 1");
+  if (n_chunks > hsa::dhsa_max_chunks())
+    return fail(HSA_ERR_UNSUPPORTED, "n_chunks must be <= 4096");
+  if (L >= ((int64_t)1 << 31)) return fail(HSA_ERR_UNSUPPORTED, "L must be < 2^31");
+  if ((int64_t)B * H * n_chunks * (n_chunks + 1) >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "B*H*n_chunks^2 must be < 2^31");
+  if (offsets[0] != 0 || offsets[n_chunks] != L)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "offsets must start at 0 and end at L");
+  int max_len = 0;
+  for (int l = 0; l < n_chunks; ++l) {
+    const int len = offsets[l + 1] - offsets[l];
+    if (len <= 0) return fail(HSA_ERR_INVALID_ARGUMENT, "offsets must be strictly increasing");
+    if (len > max_len) max_len = len;
+  }
+  if (B == 0) return HSA_OK;
+  if (!Q || !K || !V || !O) return fail(HSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must not be NULL");
+  const size_t need = dhsa_layout(nullptr, B, H, d, n_chunks).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(need) + " bytes");
+  DhsaLayout lay = dhsa_layout(align_ws(workspace), B, H, d, n_chunks);
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(lay.offs, offsets, sizeof(int32_t) * (n_chunks + 1),
+                                hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "offsets upload");
+  hsa::DhsaArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.offs = lay.offs;
+  a.qh = lay.qh;
+  a.kh = lay.kh;
+  a.sc = lay.sc;
+  a.order = chunk_order ? chunk_order : lay.order;
+  a.cumlen = lay.cumlen;
+  a.diag_pos = lay.diag_pos;
+  a.mask_bits = mask_bits;
+  a.B = B;
+  a.H = H;
+  a.d = d;
+  a.dtype = dt_code(dtype);
+  a.nc = n_chunks;
+  a.tiles_per_chunk = (max_len + 127) / 128;
+  a.L = L;
+  a.budget = budget;
+  if ((int64_t)B * H * n_chunks * a.tiles_per_chunk >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
+  e = hsa::dhsa_run(a, st);
+  return e == hipSuccess ? HSA_OK : hip_fail(e, "dhsa");
+}
+
+}  // extern "C"

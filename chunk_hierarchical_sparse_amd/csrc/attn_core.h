@@ -1,0 +1,197 @@
+// attn_core.h - bf16 MFMA softmax attention of 32 query rows per wave over
+// key blocks of up to 64 keys staged in LDS, with an online softmax across
+// blocks.  Used by the HSA chunk attention (one chunk per row, [HiLS]
+// abstract: attention independently inside each retrieved chunk) and by the
+// DHSA masked attention (several key chunks per row).
+//
+// Layout (v_mfma_f32_32x32x16_bf16, lane l, half h = l/32, row i = l%32):
+//  * scores are computed transposed, S^T = K Q^T: A = 32 keys x 16 dims from
+//    LDS, B = Q^T with lane l holding query l%32 (dims 16s+8h..+7 of k-step
+//    s).  The accumulator gives lane l the query l%32 and keys
+//    8*(r/4) + 4h + r%4 (r = 0..15), so each lane owns one query's row
+//    statistics and only lanes l and l^32 share a query.
+//  * O^T = V^T P^T: B = P^T straight from the score registers (registers
+//    8s'..8s'+7 form k-step s'; the k-slot -> key map is the one the score
+//    layout gives, and A uses the same map), A = V^T read from LDS where V
+//    is stored as [key/4][dim][4 keys], so each lane reads 8 contiguous
+//    bytes per key quad.  The output accumulator again has lane l = query,
+//    so the online-softmax rescale is a per-lane scalar.
+#pragma once
+
+#include "hsa_common.h"
+
+namespace hsa {
+
+constexpr int kKeyBlock = 64;
+
+template <int D>
+struct KVSmem {
+  uint16_t k[kKeyBlock * (D + 8)];  // row-major, rows padded by 16 bytes
+  uint16_t v[(kKeyBlock / 4) * D * 4];
+};
+
+// Stage keys/values rows [0, nk) of a block (row stride D elements) into
+// LDS; rows nk..63 are zero so masked keys never meet non-finite data.
+// Called by all threads of a 256-thread block.
+template <int D>
+__device__ __forceinline__ void load_kv_block(KVSmem<D>& sm, const uint16_t* __restrict__ Kg,
+                                              const uint16_t* __restrict__ Vg, int nk) {
+  const int tid = threadIdx.x;
+  constexpr int KPR = D / 8;  // 16-byte pieces per key row
+#pragma unroll
+  for (int e = tid; e < kKeyBlock * KPR; e += 256) {
+    const int row = e / KPR, c8 = e % KPR;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row < nk) x = *(const u32x4*)(Kg + (int64_t)row * D + c8 * 8);
+    *(u32x4*)(&sm.k[row * (D + 8) + c8 * 8]) = x;
+  }
+  constexpr int VPR = D / 4;  // 8-byte pieces per value row
+#pragma unroll
+  for (int e = tid; e < (kKeyBlock / 4) * VPR; e += 256) {
+    const int grp = e / VPR, cq = e % VPR;
+    u32x2 r[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int key = grp * 4 + kk;
+      r[kk] = key < nk ? *(const u32x2*)(Vg + (int64_t)key * D + cq * 4) : u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int w = x >> 1;
+      uint32_t lo, hi;
+      if ((x & 1) == 0) {
+        lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
+        hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
+      } else {
+        lo = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
+        hi = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
+      }
+      *(u32x2*)(&sm.v[(grp * D + cq * 4 + x) * 4]) = u32x2{lo, hi};
+    }
+  }
+}
+
+template <int D>
+struct WaveAttn {
+  bf16x8 qf[D / 16];  // Q^T operand, k-step s: dims 16s + 8h .. 16s + 8h + 7
+  f32x16 o[D / 32];   // O^T accumulator, block b: dims 32b + 8(r/4) + 4h + r%4
+  float m;            // running max of log2-domain logits (this lane's query)
+  float l;            // running sum of exp2(logit - m)
+};
+
+template <int D>
+__device__ __forceinline__ void wave_attn_init(WaveAttn<D>& st, const uint16_t* qrow,
+                                               bool valid) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (valid) x = *(const u32x4*)(qrow + 16 * s + 8 * h);
+    st.qf[s] = __builtin_bit_cast(bf16x8, x);
+  }
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[b][r] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+__device__ __forceinline__ bf16x8 cvt_bf16x8(const f32x16& p, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(p[base + e]);
+  return r;
+}
+
+// One key block: keys with in-block index < nvalid are attended by this
+// lane's query (nvalid may differ per lane; 0 = none).  scale_log2 =
+// log2(e)/sqrt(d).  Must be called by every lane of the wave.
+template <int D>
+__device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>& sm, int nvalid,
+                                                float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int i32 = lane & 31;
+  f32x16 s0, s1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = 0.f;
+    s1[r] = 0.f;
+  }
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const bf16x8 a0 = *(const bf16x8*)(&sm.k[i32 * (D + 8) + 16 * s + 8 * h]);
+    const bf16x8 a1 = *(const bf16x8*)(&sm.k[(32 + i32) * (D + 8) + 16 * s + 8 * h]);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, st.qf[s], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, st.qf[s], s1, 0, 0, 0);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = 8 * (r >> 2) + 4 * h + (r & 3);
+    const float x0 = key < nvalid ? s0[r] * scale_log2 : -INFINITY;
+    const float x1 = key + 32 < nvalid ? s1[r] * scale_log2 : -INFINITY;
+    s0[r] = x0;
+    s1[r] = x1;
+    mx = fmaxf(mx, fmaxf(x0, x1));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+  float ps = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = fast_exp2(s0[r] - m_use);
+    s1[r] = fast_exp2(s1[r] - m_use);
+    ps += s0[r] + s1[r];
+  }
+  ps += __shfl_xor(ps, 32, kWave);
+  st.l = st.l * alpha + ps;
+  st.m = m_new;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[b][r] *= alpha;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const f32x16& p = kt == 0 ? s0 : s1;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 pb = cvt_bf16x8(p, 8 * s2);
+      const int g0 = 8 * kt + 4 * s2 + h;  // key quad of k-slots 0..3
+      const int g1 = g0 + 2;               // key quad of k-slots 4..7
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) {
+        const int dd = 32 * b + i32;
+        const u32x2 v0 = *(const u32x2*)(&sm.v[(g0 * D + dd) * 4]);
+        const u32x2 v1 = *(const u32x2*)(&sm.v[(g1 * D + dd) * 4]);
+        const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
+        st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
+                                                          st.o[b], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Dot product of this lane's query half with an fp32 vector (dims
+// 16s + 8h + 0..7); the caller adds the partner lane (l ^ 32).
+template <int D>
+__device__ __forceinline__ float wave_q_dot_half(const WaveAttn<D>& st, const float* vec) {
+  const int h = (threadIdx.x & 63) >> 5;
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const f32x4 a = *(const f32x4*)(vec + 16 * s + 8 * h);
+    const f32x4 b = *(const f32x4*)(vec + 16 * s + 8 * h + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc += (float)st.qf[s][e] * a[e];
+      acc += (float)st.qf[s][e + 4] * b[e];
+    }
+  }
+  return acc;
+}
+
+}  // namespace hsa

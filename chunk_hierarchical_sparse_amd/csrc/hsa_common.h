@@ -1,0 +1,99 @@
+// hsa_common.h - device helpers shared by the gfx950 kernels of libhsa_attn.
+//
+// Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace hsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// Two floats -> packed bf16 pair (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+// Element i of an fp32 or bf16 array as float.
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if (DT == kF32) return ((const float*)p)[i];
+  return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
+  if (DT == kF32)
+    ((float*)p)[i] = v;
+  else
+    ((uint16_t*)p)[i] = f32_to_bf16_bits(v);
+}
+
+// Order-preserving map of a float onto uint32 (larger float -> larger
+// integer).  -0 is folded onto +0 so that equal scores tie exactly.
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  f = f + 0.0f;
+  uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float ordered_to_float(uint32_t o) {
+  uint32_t b = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(b);
+}
+
+// 64-bit selection key: score first, then the lower index.  Distinct
+// indices give distinct keys; 0 is below every real key.
+__device__ __forceinline__ uint64_t select_key(float score, uint32_t idx) {
+  return ((uint64_t)ordered_bits(score) << 32) | (uint64_t)(0xffffffffu - idx);
+}
+
+__device__ __forceinline__ uint32_t key_index(uint64_t key) {
+  return 0xffffffffu - (uint32_t)key;
+}
+
+__device__ __forceinline__ float key_score(uint64_t key) {
+  return ordered_to_float((uint32_t)(key >> 32));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o, kWave);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace hsa

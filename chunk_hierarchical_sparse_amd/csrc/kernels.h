@@ -1,0 +1,92 @@
+// kernels.h - host-side launchers of the gfx950 kernels (internal to
+// libhsa_attn; the public interface is include/hsa_attn.h).
+//
+// Every launcher enqueues on `stream` and returns the hipError_t of the
+// launch; argument validation has already happened in api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hsa {
+
+// Input element types.
+enum : int { kF32 = 0, kBF16 = 1 };
+
+// ---- shared ----------------------------------------------------------------
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream);
+
+// ---- landmarks (landmarks.hip) ---------------------------------------------
+// lmk[bh, c, :] = sum of rows c*S .. c*S+S-1 of K[bh] / sqrt(S), for chunks
+// c0 <= c < c1.  K row stride is d; a (b,h) slab holds `slab_tokens` rows and
+// lmk holds `lmk_chunks` chunks per (b,h).
+hipError_t launch_landmarks(const void* K, int dtype, float* lmk, int64_t BH, int64_t slab_tokens,
+                            int64_t lmk_chunks, int d, int S, int64_t c0, int64_t c1,
+                            hipStream_t stream);
+
+// ---- HSA prefill (prefill.hip) ---------------------------------------------
+struct PrefillArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* lmk;   // [B,Hkv,n,d]
+  void* O;            // [B,Hq,L,d]
+  int32_t* idx;       // [B,Hkv,L,topk]
+  float* sel_w;       // [B,Hq,L,topk] or null
+  int32_t* counts;    // [B*Hkv, n]
+  int32_t* cursor;    // [B*Hkv, n]
+  int32_t* offs;      // [B*Hkv, n+1]
+  int32_t* tile_off;  // [B*Hkv, n+1]
+  int32_t* list;      // [B*Hkv, L*topk]
+  void* partial;      // [B,Hq,L,topk,d] (bf16 for bf16 inputs, fp32 for fp32)
+  float* part_score;  // [B,Hq,L,topk]
+  int B, Hq, Hkv, d, S, topk, dtype;
+  int64_t L, n;
+  int entries_per_tile;  // selection entries (token, slot) per attention tile
+  int64_t tiles_ub;      // upper bound of tiles per (b, group)
+};
+hipError_t prefill_select(const PrefillArgs& a, hipStream_t stream);
+hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream);
+hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream);
+hipError_t prefill_fuse(const PrefillArgs& a, hipStream_t stream);
+int prefill_entries_per_tile(int dtype, int G);
+
+// ---- HSA decode (decode.hip) -----------------------------------------------
+struct DecodeArgs {
+  const void* q;       // [B,Hq,d]
+  const void* Kc;      // [B,Hkv,n_max,d]
+  const void* Vc;
+  const float* lmk;    // [B,Hkv,n_max/S,d]
+  void* o;             // [B,Hq,d]
+  int32_t* sel;        // [B,Hkv,topk]
+  float* sel_w;        // [B,Hq,topk] or null
+  uint64_t* cand;      // [B*Hkv, n_slices, topk]
+  float* part_o;       // [B,Hq,topk,d]
+  float* part_s;       // [B,Hq,topk]
+  int B, Hq, Hkv, d, S, topk, dtype;
+  int64_t n_ctx, n_max, n_avail, lmk_chunks;
+  int n_slices, slice;
+};
+void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* slice);
+hipError_t decode_run(const DecodeArgs& a, hipStream_t stream);
+
+// ---- DHSA prefill (dhsa.hip) -----------------------------------------------
+struct DhsaArgs {
+  const void* Q;          // [B,H,L,d]
+  const void* K;
+  const void* V;
+  void* O;
+  const int32_t* offs;    // device [nc+1]
+  float* qh;              // [B,H,nc,d]
+  float* kh;              // [B,H,nc,d]
+  float* sc;              // [B,H,nc,nc]
+  int32_t* order;         // [B,H,nc,nc]
+  int32_t* cumlen;        // [B,H,nc,nc+1]
+  int32_t* diag_pos;      // [B,H,nc]
+  uint32_t* mask_bits;    // [B,H,L,ceil(L/32)] or null
+  int B, H, d, dtype, nc, tiles_per_chunk;
+  int64_t L, budget;
+};
+hipError_t dhsa_run(const DhsaArgs& a, hipStream_t stream);
+
+}  // namespace hsa

@@ -1,0 +1,162 @@
+/*
+ * hsa_attn.h - C ABI of the gfx950 (MI355X) hierarchical sparse attention
+ * forward library, libhsa_attn.so.
+ *
+ * The method (sources are web pages, cited by title and section):
+ *  [HSA]  "Understanding and Improving Length Generalization in Hierarchical
+ *         Sparse Attention Models" (ai.info summary of arXiv 2510.17196),
+ *         Methodology: the sequence is split into chunks of S tokens, each
+ *         chunk gets a landmark vector, and each query retrieves the top-K
+ *         chunks (S = 64, K = 8 by default).
+ *  [HiLS] mlsift "length extrapolation" page, HiLS abstract: the query
+ *         attends independently inside each retrieved chunk and the chunk
+ *         outputs are fused according to the chunk retrieval scores.
+ *  [DHSA] pith.science review of arXiv 2510.24606, "What carries the
+ *         argument" and Referee report (Eq. 4, tiling rule, Algorithm 1):
+ *         variable-length chunks, sqrt|C|-scaled mean pooling of queries and
+ *         keys, chunk similarity S_c, tiled to a token map S_t, top-N_b
+ *         preceding keys per query, masked softmax attention.
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers unless stated otherwise.  Tensors are contiguous and
+ *    head-major: Q [B,Hq,L,d], K and V [B,Hkv,L,d].  Query head h belongs to
+ *    KV group g = h / (Hq/Hkv); Hq must be a multiple of Hkv.
+ *  - dtype is HSA_DTYPE_BF16 or HSA_DTYPE_F32 for Q, K, V and the output;
+ *    landmarks are always fp32; indices are int32.  Head dim d is 64 or 128.
+ *  - A landmark is (sum of the chunk's S keys) / sqrt(S), the sqrt(S)-scaled
+ *    mean.  Retrieval scores and in-chunk logits both scale by 1/sqrt(d).
+ *  - Chunk c is available to query position t when (c+1)*S <= t (all of its
+ *    tokens precede t).  A trailing partial chunk is never available.  A
+ *    query with no available chunk outputs zeros.
+ *  - The selection of a KV group is shared by its query heads and ranks the
+ *    sum of their per-head scores; ties go to the lower chunk index.  Each
+ *    head fuses the chunk outputs with a softmax over its own per-head scores
+ *    of the selected chunks.
+ *  - Ownership: the caller allocates and frees every buffer, the workspace
+ *    included.  The library allocates no device memory and keeps no global
+ *    mutable state.  All work is enqueued asynchronously on `stream` (a
+ *    hipStream_t, NULL = default stream); the library never synchronises.
+ *  - Errors: arguments are validated on the host before anything is
+ *    enqueued, so any status other than HSA_OK / HSA_ERR_HIP means nothing
+ *    was launched.  HSA_ERR_HIP reports a failed launch; the HIP message is
+ *    kept for the calling thread (hsa_last_error_message).  No C++ exception
+ *    crosses this boundary.
+ */
+#ifndef HSA_ATTN_H
+#define HSA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hsa_stream_t; /* the same handle as hipStream_t */
+
+typedef enum {
+  HSA_OK = 0,
+  HSA_ERR_INVALID_ARGUMENT = 1,    /* bad size, null required pointer, ... */
+  HSA_ERR_UNSUPPORTED = 2,         /* valid request this build does not run */
+  HSA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the *_size value */
+  HSA_ERR_HIP = 4,                 /* a HIP call failed */
+} hsa_status_t;
+
+typedef enum {
+  HSA_DTYPE_F32 = 0,
+  HSA_DTYPE_BF16 = 1,
+} hsa_dtype_t;
+
+/* Static description of a status code. */
+const char* hsa_status_string(hsa_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* hsa_last_error_message(void);
+
+/*
+ * Landmark pooling ([HSA] Methodology; sqrt-scaled mean as in [DHSA] Eq. 4).
+ *   K    [B,Hkv,L,d] dtype, read only.
+ *   lmk  [B,Hkv,L/S,d] fp32, written for chunks chunk_begin .. chunk_end-1
+ *        only (0 <= chunk_begin <= chunk_end <= L/S), so a decode cache can
+ *        append landmarks as chunks complete.
+ * lmk[b,g,c,:] = sum_{j<S} K[b,g,c*S+j,:] / sqrt(S).
+ */
+hsa_status_t hsa_build_landmarks(const void* K, float* lmk, int B, int Hkv, int64_t L, int d,
+                                 int S, int64_t chunk_begin, int64_t chunk_end,
+                                 hsa_dtype_t dtype, hsa_stream_t stream);
+
+/*
+ * HSA prefill (every query position of the sequence).  [HSA] Methodology,
+ * [HiLS] abstract.
+ *   Q [B,Hq,L,d], K, V [B,Hkv,L,d]: dtype, read only.
+ *   lmk     fp32 [B,Hkv,L/S,d] landmarks, or NULL to build them in the
+ *           workspace from K.
+ *   O       [B,Hq,L,d] dtype, written.
+ *   sel_idx int32 [B,Hkv,L,topk] or NULL: selected chunks of each query in
+ *           rank order (score desc, index asc), -1 padded.
+ *   sel_w   fp32 [B,Hq,L,topk] or NULL: fusion weights in the same order,
+ *           0 padded.
+ *   workspace of at least hsa_prefill_workspace_size(...) bytes, 256-byte
+ *   aligned; its contents on entry do not matter.
+ * Limits: 1 <= S <= 1024, 1 <= topk <= 32, B*Hkv*L*topk < 2^31, Hq/Hkv <= 32.
+ */
+size_t hsa_prefill_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S, int topk,
+                                  hsa_dtype_t dtype);
+hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const float* lmk,
+                         void* O, int32_t* sel_idx, float* sel_w, int B, int64_t L, int Hq,
+                         int Hkv, int d, int S, int topk, hsa_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, hsa_stream_t stream);
+
+/*
+ * HSA decode: one new query per sequence at position n_ctx, attending a KV
+ * cache of capacity n_max tokens whose first n_ctx are valid.  All
+ * floor(n_ctx/S) complete chunks are available.
+ *   q      [B,Hq,d] dtype.
+ *   Kc, Vc [B,Hkv,n_max,d] dtype (64-bit addressing: a group's slab may
+ *          exceed 4 GiB).
+ *   lmk    fp32 [B,Hkv,n_max/S,d]; entries of the first floor(n_ctx/S)
+ *          chunks are read (see hsa_build_landmarks).
+ *   o      [B,Hq,d] dtype, written.
+ *   sel_idx int32 [B,Hkv,topk] or NULL, sel_w fp32 [B,Hq,topk] or NULL, as
+ *          in hsa_prefill.
+ * Limits: 1 <= S <= 1024, 1 <= topk <= 32, n_ctx <= n_max, Hq/Hkv <= 32.
+ */
+size_t hsa_decode_workspace_size(int B, int Hq, int Hkv, int d, int S, int topk,
+                                 int64_t n_ctx);
+hsa_status_t hsa_decode(const void* q, const void* Kc, const void* Vc, const float* lmk,
+                        int64_t n_ctx, int64_t n_max, void* o, int32_t* sel_idx, float* sel_w,
+                        int B, int Hq, int Hkv, int d, int S, int topk, hsa_dtype_t dtype,
+                        void* workspace, size_t workspace_bytes, hsa_stream_t stream);
+
+/*
+ * DHSA prefill ([DHSA] "What carries the argument", Eq. 4, tiling rule,
+ * Algorithm 1 top-N_b preceding keys).
+ *   Q, K, V  [B,H,L,d] dtype (bf16 only in this build).
+ *   offsets  HOST int32 [n_chunks+1], 0 = b_0 < b_1 < ... < b_n = L: chunk l
+ *            holds tokens b_l .. b_{l+1}-1; the same boundaries for every
+ *            batch entry and head.
+ *   budget   N_b >= 1 keys kept per query.
+ *   O        [B,H,L,d] dtype, written.
+ *   mask_bits  uint32 [B,H,L,ceil(L/32)] or NULL: bit j of row i set when
+ *            key j is kept for query i (debug output; L*L/8 bytes per head).
+ *   chunk_order int32 [B,H,n_chunks,n_chunks] or NULL: row l lists the key
+ *            chunks 0..l by (S_c[l,k] desc, k asc), -1 padded.
+ * Per query i in chunk l: q_hat_l = sum_{i in C_l} q_i / sqrt|C_l| (same for
+ * k_hat), S_c[l,k] = q_hat_l . k_hat_k, every key j <= i scores
+ * S_c[l, chunk(j)], the first min(N_b, i+1) keys in (score desc, j asc)
+ * order are kept, and softmax(q.k/sqrt d) attention runs over them.
+ * Limits: n_chunks <= 4096, B*H*n_chunks*n_chunks < 2^31.
+ */
+size_t dhsa_prefill_workspace_size(int B, int64_t L, int H, int d, int n_chunks,
+                                   hsa_dtype_t dtype);
+hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int32_t* offsets,
+                          int n_chunks, int64_t budget, void* O, uint32_t* mask_bits,
+                          int32_t* chunk_order, int B, int64_t L, int H, int d,
+                          hsa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                          hsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_ATTN_H */

@@ -30,9 +30,9 @@ def lib():
         L = ctypes.CDLL(_build.LIB)
         L.oracle_landmarks.argtypes = [_P, ctypes.c_int, _I, _I, _I, _I, _I, _P]
         L.oracle_hsa_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _I, _I, _I,
-                                         _P, _I, ctypes.c_int, _P, _P, _P, _P]
+                                         _P, _I, ctypes.c_int, _P, _P, _P, _P, _P]
         L.oracle_hsa_decode_select.argtypes = [_P, ctypes.c_int, _P, _I, _I, _I, _I, _I, _I,
-                                               _I, _I, _P, _P]
+                                               _I, _I, _P, _P, _P]
         L.oracle_hsa_decode_attend.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _I, _I, _I,
                                                _I, _I, _I, _P, _P]
         L.oracle_dhsa_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _P, _I, _I,
@@ -78,7 +78,8 @@ def landmarks(K, S):
 def hsa_prefill(Q, K, V, S, topk, rows=None, include_current_chunk=False, want_out=True):
     """HSA prefill for query positions `rows` (default: all).
 
-    Returns dict(out [B,Hq,R,d], sel [B,Hkv,R,K], w [B,Hq,R,K], margin [B,Hkv,R])."""
+    Returns dict(out [B,Hq,R,d], sel [B,Hkv,R,K], w [B,Hq,R,K], margin [B,Hkv,R],
+    sel_score [B,Hkv,R,K] group-summed score of each selected chunk)."""
     Q, K, V = _c(Q), _c(K), _c(V)
     B, Hq, L, d = Q.shape
     Hkv = K.shape[1]
@@ -93,26 +94,29 @@ def hsa_prefill(Q, K, V, S, topk, rows=None, include_current_chunk=False, want_o
     sel = np.zeros((B, Hkv, R, topk), np.int32)
     w = np.zeros((B, Hq, R, topk), np.float64)
     margin = np.zeros((B, Hkv, R), np.float64)
+    sel_score = np.zeros((B, Hkv, R, topk), np.float64)
     rc = lib().oracle_hsa_prefill(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dt, B, L, Hq,
                                   Hkv, d, S, topk, _ptr(rows_a), R, int(include_current_chunk),
-                                  _ptr(out), _ptr(sel), _ptr(w), _ptr(margin))
+                                  _ptr(out), _ptr(sel), _ptr(w), _ptr(margin), _ptr(sel_score))
     _check(rc, "hsa_prefill")
-    return dict(out=out, sel=sel, w=w, margin=margin)
+    return dict(out=out, sel=sel, w=w, margin=margin, sel_score=sel_score)
 
 
 def hsa_decode_select(q, lmk, S, n_ctx, topk, Hkv):
-    """q [B,Hq,d]; lmk float32 [B,Hkv,n_lmk,d].  Returns (sel [B,Hkv,K], margin [B,Hkv])."""
+    """q [B,Hq,d]; lmk float32 [B,Hkv,n_lmk,d].  Returns (sel [B,Hkv,K],
+    margin [B,Hkv], sel_score [B,Hkv,K])."""
     q = _c(q)
     lmk = np.ascontiguousarray(lmk, dtype=np.float32)
     B, Hq, d = q.shape
     n_lmk = lmk.shape[2]
     sel = np.zeros((B, Hkv, topk), np.int32)
     margin = np.zeros((B, Hkv), np.float64)
+    sel_score = np.zeros((B, Hkv, topk), np.float64)
     rc = lib().oracle_hsa_decode_select(q.ctypes.data, _dt(q), lmk.ctypes.data, B, Hq, Hkv, d,
                                         S, n_ctx, n_lmk, topk, sel.ctypes.data,
-                                        margin.ctypes.data)
+                                        margin.ctypes.data, sel_score.ctypes.data)
     _check(rc, "hsa_decode_select")
-    return sel, margin
+    return sel, margin, sel_score
 
 
 def hsa_decode_attend(q, Ksel, Vsel, lmk_sel, sel, S):
@@ -150,7 +154,7 @@ def pack_selected(Kc, sel, S):
 def hsa_decode(q, Kc, Vc, lmk, S, n_ctx, topk):
     """Full decode on caches small enough to hold on the host."""
     Hkv = Kc.shape[1]
-    sel, margin = hsa_decode_select(q, lmk, S, n_ctx, topk, Hkv)
+    sel, margin, sel_score = hsa_decode_select(q, lmk, S, n_ctx, topk, Hkv)
     Ks, Vs = pack_selected(Kc, sel, S), pack_selected(Vc, sel, S)
     lmk = np.asarray(lmk, np.float32)
     B, _, _, d = lmk.shape
@@ -161,7 +165,7 @@ def hsa_decode(q, Kc, Vc, lmk, S, n_ctx, topk):
                 if sel[b, g, k] >= 0:
                     lsel[b, g, k] = lmk[b, g, sel[b, g, k]]
     out, w = hsa_decode_attend(q, Ks, Vs, lsel, sel, S)
-    return dict(out=out, w=w, sel=sel, margin=margin)
+    return dict(out=out, w=w, sel=sel, margin=margin, sel_score=sel_score)
 
 
 def dhsa_prefill(Q, K, V, offsets, budget, rows=None, want_sc=False, want_kept=False):

@@ -145,6 +145,8 @@ static double attend_rows(const double* q, const void* K, const void* V, int dty
  *   w      [B,Hq,n_rows,topk]    fusion weights in the same order, 0 padded
  *   margin [B,Hkv,n_rows]        sigma_(K) - sigma_(K+1) of the group-summed
  *                                scores, +inf when at most K are available
+ *   sel_score [B,Hkv,n_rows,topk] group-summed score of each selected chunk,
+ *                                -inf padded
  * Any output pointer may be NULL.  include_current_chunk (oracle-only switch
  * used to pin the dense-causal reduction) also makes the chunk holding t
  * available, with its keys restricted to j <= t.
@@ -152,7 +154,7 @@ static double attend_rows(const double* q, const void* K, const void* V, int dty
 int oracle_hsa_prefill(const void* Q, const void* K, const void* V, int dtype, int64_t B,
                        int64_t L, int64_t Hq, int64_t Hkv, int64_t d, int64_t S, int64_t topk,
                        const int64_t* rows, int64_t n_rows, int include_current_chunk,
-                       double* out, int32_t* sel, double* w, double* margin) {
+                       double* out, int32_t* sel, double* w, double* margin, double* sel_score) {
   if (!Q || !K || !V || B < 0 || L < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 ||
       S <= 0 || topk <= 0)
     return OR_EINVAL;
@@ -215,6 +217,10 @@ int oracle_hsa_prefill(const void* Q, const void* K, const void* V, int dtype, i
             if (sel)
               for (int64_t k = 0; k < topk; ++k)
                 sel[((b * Hkv + g) * n_rows + r) * topk + k] = k < m ? (int32_t)cand[k].idx : -1;
+            if (sel_score)
+              for (int64_t k = 0; k < topk; ++k)
+                sel_score[((b * Hkv + g) * n_rows + r) * topk + k] =
+                    k < m ? cand[k].score : -INFINITY;
             for (int64_t hh = 0; hh < G; ++hh) {
               const int64_t h = g * G + hh;
               double* orow = out ? out + ((b * Hq + h) * n_rows + r) * d : NULL;
@@ -266,12 +272,14 @@ int oracle_hsa_prefill(const void* Q, const void* K, const void* V, int dtype, i
 
 /*
  * q [B,Hq,d] (dtype), lmk [B,Hkv,n_lmk,d] fp32 landmarks as handed to the GPU
- * (n_lmk >= floor(n_ctx/S)).  Outputs sel [B,Hkv,topk] (-1 padded) and
- * margin [B,Hkv] (either may be NULL; group-summed scores as in prefill).
+ * (n_lmk >= floor(n_ctx/S)).  Outputs sel [B,Hkv,topk] (-1 padded), margin
+ * [B,Hkv] and sel_score [B,Hkv,topk] (-inf padded); any may be NULL
+ * (group-summed scores as in prefill).
  */
 int oracle_hsa_decode_select(const void* q, int dtype, const float* lmk, int64_t B,
                              int64_t Hq, int64_t Hkv, int64_t d, int64_t S, int64_t n_ctx,
-                             int64_t n_lmk, int64_t topk, int32_t* sel, double* margin) {
+                             int64_t n_lmk, int64_t topk, int32_t* sel, double* margin,
+                             double* sel_score) {
   if (!q || !lmk || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 || S <= 0 ||
       topk <= 0 || n_ctx < 0 || n_lmk < n_ctx / S)
     return OR_EINVAL;
@@ -302,6 +310,9 @@ int oracle_hsa_decode_select(const void* q, int dtype, const float* lmk, int64_t
           sel[(b * Hkv + g) * topk + k] = k < m ? (int32_t)cand[k].idx : -1;
       if (margin)
         margin[b * Hkv + g] = navail > topk ? cand[topk - 1].score - cand[topk].score : INFINITY;
+      if (sel_score)
+        for (int64_t k = 0; k < topk; ++k)
+          sel_score[(b * Hkv + g) * topk + k] = k < m ? cand[k].score : -INFINITY;
       free(cand);
     }
   return err;

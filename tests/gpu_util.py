@@ -1,0 +1,96 @@
+"""Helpers of the GPU parity tests: seeded inputs, device transfer, and the
+comparison rules.
+
+Rules (the same everywhere):
+ - selected chunk/token sets must match the oracle exactly wherever the
+   oracle's selection margin exceeds 1e-4; rows below that margin are
+   exempt and counted;
+ - outputs: bf16 max |gpu - oracle| <= 2e-2; fp32 max |gpu - oracle| /
+   max |oracle| <= 1e-5; compared on rows whose selection matches.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import synth
+
+MARGIN = 1e-4
+TOL_BF16 = 2e-2
+TOL_F32_REL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gen(shape, dt, seed, tid, scale=1.0):
+    return synth.normal(shape, synth.BF16 if dt == "bf16" else synth.F32, seed, tid, scale)
+
+
+def qkv(B, Hq, Hkv, L, d, dt, seed, scale=1.0):
+    return (gen((B, Hq, L, d), dt, seed, synth.TID_Q, scale),
+            gen((B, Hkv, L, d), dt, seed, synth.TID_K, scale),
+            gen((B, Hkv, L, d), dt, seed, synth.TID_V, scale))
+
+
+def dev(arr):
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(
+            torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float32) else \
+        t.cpu().numpy()
+
+
+def check_out(got, ref, dt, what):
+    if got.size == 0:
+        return 0.0
+    err = float(np.abs(got.astype(np.float64) - ref).max())
+    if dt == "bf16":
+        assert err <= TOL_BF16, f"{what}: max abs error {err} > {TOL_BF16}"
+        return err
+    scale = float(np.abs(ref).max()) or 1.0
+    assert err / scale <= TOL_F32_REL, f"{what}: relative error {err / scale} > {TOL_F32_REL}"
+    return err / scale
+
+
+def compare_selection(sel_gpu, sel_ref, margin, what, sel_score=None):
+    """Selected sets must equal the oracle's wherever margin > MARGIN.  Where
+    the sets are equal, the GPU's rank order must agree with the oracle's
+    scores up to MARGIN (near-equal chunks inside the top-K may swap).
+    Returns (rows with equal sets, exempt fraction)."""
+    strict = margin > MARGIN
+    same = (np.sort(sel_gpu, -1) == np.sort(sel_ref, -1)).all(-1)
+    bad = ~same & strict
+    assert not bad.any(), f"{what}: {int(bad.sum())} selected sets differ above the margin, " \
+                          f"first at {np.argwhere(bad)[0].tolist()}"
+    if sel_score is not None:
+        og, orf = np.argsort(sel_gpu, -1), np.argsort(sel_ref, -1)
+        s_sorted = np.take_along_axis(sel_score, orf, -1)
+        s_at_gpu = np.empty_like(sel_score)
+        np.put_along_axis(s_at_gpu, og, s_sorted, -1)
+        with np.errstate(invalid="ignore"):
+            drop = s_at_gpu[..., :-1] - s_at_gpu[..., 1:]
+        valid = (sel_gpu[..., 1:] >= 0) & same[..., None]
+        worst = float(np.min(np.where(valid, drop, 0.0))) if valid.any() else 0.0
+        assert worst >= -MARGIN, f"{what}: rank order disagrees with oracle scores by {worst}"
+    return same, float((~strict).mean())
+
+
+def by_chunk(sel, arr, G):
+    """Reorder per-head slot values arr [B,Hq,...,K] by the chunk index of
+    the group's selection sel [B,Hkv,...,K], so lists with equal sets align."""
+    order = np.repeat(np.argsort(sel, -1), G, axis=1)
+    return np.take_along_axis(arr, order, -1)
+
+
+def unpack_mask(words, L):
+    """uint32 words [..., ceil(L/32)] -> uint8 bits [..., L]."""
+    w = np.ascontiguousarray(words).view(np.uint32)
+    bits = ((w[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(np.uint8)
+    return bits.reshape(*w.shape[:-1], -1)[..., :L]

@@ -1,0 +1,151 @@
+"""The C-ABI library loads, exports every entry point its header declares,
+and rejects invalid arguments on the host before touching the GPU (these
+calls return before any HIP call, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (the library binds to torch's HIP runtime)
+
+import chunk_hierarchical_sparse_amd as hsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hsa_attn.h")
+
+INV, UNS, WS = hsa.HSA_ERR_INVALID_ARGUMENT, hsa.HSA_ERR_UNSUPPORTED, hsa.HSA_ERR_WORKSPACE_TOO_SMALL
+F32, BF16 = hsa.DTYPE_F32, hsa.DTYPE_BF16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["hsa_build_landmarks", "hsa_prefill", "hsa_decode", "dhsa_prefill",
+              "hsa_prefill_workspace_size", "hsa_decode_workspace_size",
+              "dhsa_prefill_workspace_size", "hsa_status_string", "hsa_last_error_message"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(hsa.lib_path())
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert hsa.hsa_status_string(0).startswith("HSA_OK")
+    for code in range(1, 5):
+        assert hsa.hsa_status_string(code).startswith("HSA_ERR")
+    assert "unknown" in hsa.hsa_status_string(99)
+
+
+def lib():
+    return hsa.load_library()
+
+
+def msg():
+    return lib().hsa_last_error_message().decode()
+
+
+def prefill(**kw):
+    a = dict(Q=1, K=1, V=1, lmk=None, O=1, sel=None, w=None, B=1, L=256, Hq=4, Hkv=2, d=128,
+             S=64, topk=8, dt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib().hsa_prefill(a["Q"], a["K"], a["V"], a["lmk"], a["O"], a["sel"], a["w"], a["B"],
+                             a["L"], a["Hq"], a["Hkv"], a["d"], a["S"], a["topk"], a["dt"],
+                             a["ws"], a["wsb"], None)
+
+
+def test_prefill_validation():
+    assert prefill(Hq=3, Hkv=2) == INV
+    assert prefill(Hkv=0) == INV
+    assert prefill(d=96) == UNS
+    assert prefill(S=0) == INV
+    assert prefill(S=2048) == INV
+    assert prefill(topk=0) == INV
+    assert prefill(topk=33) == INV
+    assert prefill(dt=7) == UNS
+    assert prefill(Hq=128, Hkv=2) == UNS
+    assert prefill(B=-1) == INV
+    assert prefill(Q=None) == INV and "NULL" in msg()
+    assert prefill(L=1 << 30, topk=32) == UNS
+    # valid arguments, but no workspace
+    assert prefill() == WS and "workspace needs" in msg()
+    need = lib().hsa_prefill_workspace_size(1, 256, 4, 2, 128, 64, 8, BF16)
+    assert need > 0
+    assert prefill(ws=1 << 20, wsb=need - 1) == WS
+    # nothing to do is success without any launch
+    assert prefill(L=0) == hsa.HSA_OK and prefill(B=0) == hsa.HSA_OK
+
+
+def test_workspace_sizes_grow_with_the_problem():
+    a = lib().hsa_prefill_workspace_size(1, 4096, 16, 4, 128, 64, 8, BF16)
+    b = lib().hsa_prefill_workspace_size(1, 8192, 16, 4, 128, 64, 8, BF16)
+    c = lib().hsa_prefill_workspace_size(1, 4096, 16, 4, 128, 64, 8, F32)
+    assert 0 < a < b and c > a
+    assert lib().hsa_prefill_workspace_size(1, 4096, 16, 3, 128, 64, 8, BF16) == 0
+    assert lib().hsa_decode_workspace_size(32, 32, 8, 128, 64, 8, 131072) > 0
+    assert lib().dhsa_prefill_workspace_size(1, 16384, 8, 128, 228, BF16) > 0
+    assert lib().dhsa_prefill_workspace_size(1, 16384, 8, 128, 0, BF16) == 0
+
+
+def test_landmark_validation():
+    L = lib()
+    assert L.hsa_build_landmarks(1, 1, 1, 2, 256, 128, 64, 0, 5, BF16, None) == INV  # > L/S
+    assert L.hsa_build_landmarks(1, 1, 1, 2, 256, 128, 64, 3, 2, BF16, None) == INV
+    assert L.hsa_build_landmarks(1, 1, 1, 2, 256, 100, 64, 0, 4, BF16, None) == UNS
+    assert L.hsa_build_landmarks(None, 1, 1, 2, 256, 128, 64, 0, 4, BF16, None) == INV
+    assert L.hsa_build_landmarks(1, 1, 1, 2, 256, 128, 64, 2, 2, BF16, None) == hsa.HSA_OK
+
+
+def decode(**kw):
+    a = dict(q=1, K=1, V=1, lmk=1, n_ctx=4096, n_max=4096, o=1, sel=None, w=None, B=2, Hq=8,
+             Hkv=2, d=128, S=64, topk=8, dt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib().hsa_decode(a["q"], a["K"], a["V"], a["lmk"], a["n_ctx"], a["n_max"], a["o"],
+                            a["sel"], a["w"], a["B"], a["Hq"], a["Hkv"], a["d"], a["S"],
+                            a["topk"], a["dt"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation():
+    assert decode(n_ctx=5000) == INV  # beyond the cache
+    assert decode(n_ctx=-1) == INV
+    assert decode(Hq=6, Hkv=4) == INV
+    assert decode(K=None) == INV
+    assert decode(lmk=None) == INV
+    assert decode() == WS
+    assert decode(B=0) == hsa.HSA_OK
+
+
+def dhsa(offsets, **kw):
+    import numpy as np
+    offs = np.ascontiguousarray(offsets, dtype=np.int32)
+    a = dict(Q=1, K=1, V=1, nc=len(offs) - 1, budget=64, O=1, mask=None, order=None, B=1,
+             L=int(offs[-1]), H=2, d=128, dt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib().dhsa_prefill(a["Q"], a["K"], a["V"], offs.ctypes.data, a["nc"], a["budget"],
+                              a["O"], a["mask"], a["order"], a["B"], a["L"], a["H"], a["d"],
+                              a["dt"], a["ws"], a["wsb"], None)
+
+
+def test_dhsa_validation():
+    assert dhsa([0, 10, 10, 30]) == INV  # empty chunk
+    assert dhsa([0, 20, 10, 30]) == INV  # decreasing
+    assert dhsa([1, 10, 30]) == INV      # does not start at 0
+    assert dhsa([0, 10, 30], L=31) == INV  # does not end at L
+    assert dhsa([0, 10, 30], budget=0) == INV
+    assert dhsa([0, 10, 30], dt=F32) == UNS
+    assert dhsa([0, 10, 30], d=80) == UNS
+    assert dhsa([0, 10, 30], Q=None) == INV
+    assert dhsa([0, 10, 30]) == WS
+    assert dhsa([0, 10, 30], B=0) == hsa.HSA_OK
+
+
+def test_python_layer_rejects_host_tensors():
+    q = torch.zeros(1, 2, 64, 64)
+    with pytest.raises(ValueError):
+        hsa.hsa_prefill(q, q, q, 16, 2)

@@ -286,7 +286,7 @@ def test_needle_retrieved_at_rank_one():
     for g in range(Hkv):
         K[0, g, cstar * S:(cstar + 1) * S] = synth.needle_key(q[0, g * 4:(g + 1) * 4], True)
     lmk = oracle.landmarks(K, S).astype(np.float32)
-    sel, margin = oracle.hsa_decode_select(q, lmk, S, n * S, 16, Hkv)
+    sel, margin, _ = oracle.hsa_decode_select(q, lmk, S, n * S, 16, Hkv)
     assert (sel[0, :, 0] == cstar).all()
 
 
