@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Throughput of the hierarchical sparse attention forward path on one MI355X.
+
+One step = one call of the whole path on one batch of synthetic input that is
+already resident in HBM.  The headline workload is HSA prefill at B=1,
+L=32768, 16 query heads over 4 KV heads, d=128, S=64, top-8, bf16: landmark
+pooling, scoring + top-K, chunk attention and fusion, all inside the timed
+call.  By default the decode workload (batch 32, 131072-token caches) and the
+DHSA prefill workload (L=16384, N_b=2048) are measured too and reported under
+"also".
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+METRIC = "HSA queries/sec + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(arr, torch):
+    import numpy as np
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(
+            torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def time_steps(torch, hsa, step, steps, warmup, n_stages):
+    """Run warmup + timed steps; returns (ms per step, per-stage ms averages)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    hsa.hsa_profile_read()  # drop anything recorded earlier
+    hsa.hsa_profile_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    hsa.hsa_profile_enable(False)
+    calls, stage_ms = hsa.hsa_profile_read(n_stages)
+    ms = start.elapsed_time(end) / steps
+    return ms, [s / max(calls, 1) for s in stage_ms]
+
+
+def prefill_counts(L, S, topk):
+    """Per (b, group): selected (token, chunk) pairs and available chunks."""
+    n = L // S
+    sel = avail = 0
+    for t in range(L):
+        a = min(t // S, n)
+        avail += a
+        sel += min(topk, a)
+    return sel, avail
+
+
+# ---------------------------------------------------------------- workloads
+
+
+def bench_prefill(torch, hsa, args):
+    import synth
+    B, Hq, Hkv, L, d, S, topk = 1, 16, 4, 32768, 128, 64, 8
+    log("prefill: generating inputs")
+    Q = synth.normal((B, Hq, L, d), synth.BF16, 2, synth.TID_Q, 0.5)
+    K = synth.normal((B, Hkv, L, d), synth.BF16, 2, synth.TID_K, 0.5)
+    V = synth.normal((B, Hkv, L, d), synth.BF16, 2, synth.TID_V, 0.5)
+    q, k, v = to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch)
+    out = torch.empty_like(q)
+    ws = torch.empty(hsa.hsa_prefill_workspace_size(B, L, Hq, Hkv, d, S, topk, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        hsa.hsa_prefill(q, k, v, S, topk, out=out, workspace=ws)
+
+    log("prefill: timing")
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 5)
+    sel, avail = prefill_counts(L, S, topk)
+    attn_flop = B * Hq * sel * S * d * 4          # QK^T + PV over selected chunks
+    score_flop = B * Hkv * avail * d * 2          # group-summed retrieval scores
+    fuse_flop = B * Hq * sel * d * 2              # per-head scores of kept chunks
+    total_flop = attn_flop + score_flop + fuse_flop
+    attn_ms = stages[3]
+    achieved = attn_flop / (attn_ms * 1e-3) / 1e12
+    res = dict(
+        value=B * L / (ms * 1e-3), ms_per_step=ms,
+        config={"workload": "hsa_prefill", "B": B, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d,
+                "S": S, "topk": topk, "inputs": "0.5*N(0,1) bf16, seed 2"},
+        roofline={"bound": "mfma", "kernel": "attend (chunk attention, bf16 MFMA)",
+                  "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                  "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": attn_ms},
+        stages_ms=dict(zip(["landmarks", "select", "invert", "attend", "fuse"], stages)),
+        whole_path={"gflop": total_flop / 1e9,
+                    "tflops": total_flop / (ms * 1e-3) / 1e12,
+                    "mfma_frac": total_flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+    inputs = (Q, K, V, S, topk)
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res, inputs
+
+
+def bench_decode(torch, hsa, args, big=False):
+    import numpy as np
+    import synth
+    if big:
+        B, Hq, Hkv, N, d, S, topk, seed = 1, 16, 4, 16777216, 128, 64, 16, 4
+    else:
+        B, Hq, Hkv, N, d, S, topk, seed = 32, 32, 8, 131072, 128, 64, 8, 3
+    log(f"decode: filling caches on the device (B={B}, N={N})")
+    Kc = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device="cuda")
+    Vc = torch.empty_like(Kc)
+    synth.normal_device(Kc, seed, synth.TID_K)
+    synth.normal_device(Vc, seed, synth.TID_V)
+    qh = synth.normal((B, Hq, d), synth.BF16, seed, synth.TID_QDEC)
+    if big:
+        cstar = synth.pick_index(N // S, seed)
+        G = Hq // Hkv
+        for g in range(Hkv):
+            key = synth.needle_key(qh[0, g * G:(g + 1) * G], True)
+            rows = np.broadcast_to(key, (S, d)).copy()
+            Kc[0, g, cstar * S:(cstar + 1) * S] = to_dev(rows, torch)
+    q = to_dev(qh, torch)
+    lmk = hsa.hsa_build_landmarks(Kc, S)
+    out = torch.empty_like(q)
+    ws = torch.empty(hsa.hsa_decode_workspace_size(B, Hq, Hkv, d, S, topk, N),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        hsa.hsa_decode(q, Kc, Vc, lmk, N, S, topk, out=out, workspace=ws)
+
+    log("decode: timing")
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 4)
+    n = N // S
+    lmk_bytes = B * Hkv * n * d * 4
+    kv_bytes = B * Hkv * topk * S * d * 2 * 2
+    qo_bytes = B * Hq * d * 2 * 2
+    total = lmk_bytes + kv_bytes + qo_bytes
+    scan_ms = stages[0]
+    achieved = lmk_bytes / (scan_ms * 1e-3) / 1e9
+    res = dict(
+        value=B / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
+        config={"workload": "hsa_decode_16m" if big else "hsa_decode", "B": B, "n_ctx": N,
+                "Hq": Hq, "Hkv": Hkv, "d": d, "S": S, "topk": topk,
+                "inputs": f"N(0,1) bf16, seed {seed}" + (", planted needle" if big else "")},
+        roofline={"bound": "hbm", "kernel": "scan (landmark stream + top-K)",
+                  "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                  "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                  "algorithmic_bytes_per_launch": lmk_bytes, "avg_launch_ms": scan_ms},
+        stages_ms=dict(zip(["scan", "merge", "attend", "fuse"], stages)),
+        whole_path={"algorithmic_bytes": total, "gbps": total / (ms * 1e-3) / 1e9,
+                    "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+    del Kc, Vc, lmk, q, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_dhsa(torch, hsa, args):
+    import synth
+    B, H, L, d, budget, seed = 1, 8, 16384, 128, 2048, 5
+    offs = synth.chunk_offsets(L, 16, 128, seed=seed)
+    Q = synth.normal((B, H, L, d), synth.BF16, seed, synth.TID_Q)
+    K = synth.normal((B, H, L, d), synth.BF16, seed, synth.TID_K)
+    V = synth.normal((B, H, L, d), synth.BF16, seed, synth.TID_V)
+    q, k, v = to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch)
+    out = torch.empty_like(q)
+    ws = torch.empty(hsa.dhsa_prefill_workspace_size(B, L, H, d, len(offs) - 1, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        hsa.dhsa_prefill(q, k, v, offs, budget, out=out, workspace=ws)
+
+    log("dhsa: timing")
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 5)
+    pairs = sum(min(budget, i + 1) for i in range(L))
+    attn_flop = B * H * pairs * d * 4
+    achieved = attn_flop / (stages[3] * 1e-3) / 1e12
+    res = dict(
+        value=B * L / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
+        config={"workload": "dhsa_prefill", "B": B, "L": L, "H": H, "d": d, "budget": budget,
+                "chunks": len(offs) - 1, "inputs": "N(0,1) bf16, lengths U{16..128}, seed 5"},
+        roofline={"bound": "mfma", "kernel": "attend (block-sparse masked attention)",
+                  "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                  "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": stages[3]},
+        stages_ms=dict(zip(["pool", "sc", "rank", "attend", "mask"], stages)))
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(inputs, target_s):
+    """The oracle as it is, timed on this host's cores on evenly spaced query
+    positions of the prefill workload (every head), scaled to queries/s."""
+    import numpy as np
+    import oracle
+    Q, K, V, S, topk = inputs
+    L = Q.shape[2]
+    probe = np.arange(0, L, L // 64)
+    t0 = time.perf_counter()
+    oracle.hsa_prefill(Q, K, V, S, topk, rows=probe)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n_rows = int(min(L, max(64, target_s / max(per_row, 1e-9))))
+    rows = np.linspace(0, L - 1, n_rows).astype(np.int64)
+    log(f"cpu baseline: {n_rows} rows on {oracle.num_threads()} threads")
+    t0 = time.perf_counter()
+    oracle.hsa_prefill(Q, K, V, S, topk, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": n_rows / dt, "unit": "queries/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"{n_rows} of {L} query positions, evenly spaced, all 16 heads, "
+                      "double precision C oracle (OpenMP)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--extras", default="decode,dhsa",
+                    help="comma list of extra workloads: decode, decode16m, dhsa, or none")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunk_hierarchical_sparse_amd as hsa
+
+    torch.cuda.set_device(0)
+    res, inputs = bench_prefill(torch, hsa, args)
+    line = {"metric": METRIC, "value": res["value"], "unit": "queries/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": res["config"], "roofline": res["roofline"],
+            "stages_ms": res["stages_ms"], "whole_path": res["whole_path"]}
+    also = []
+    extras = [e for e in args.extras.split(",") if e and e != "none"]
+    for e in extras:
+        if e == "decode":
+            also.append(bench_decode(torch, hsa, args))
+        elif e == "decode16m":
+            also.append(bench_decode(torch, hsa, args, big=True))
+        elif e == "dhsa":
+            also.append(bench_dhsa(torch, hsa, args))
+        else:
+            raise SystemExit(f"unknown extra workload {e}")
+    if also:
+        line["also"] = also
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,8 @@ from . import build as _build
 __all__ = [
     "HsaError", "hsa_status_string", "hsa_build_landmarks", "hsa_prefill",
     "hsa_prefill_workspace_size", "hsa_decode", "hsa_decode_workspace_size",
-    "dhsa_prefill", "dhsa_prefill_workspace_size", "lib_path", "load_library",
+    "dhsa_prefill", "dhsa_prefill_workspace_size", "hsa_profile_enable", "hsa_profile_read",
+    "lib_path", "load_library",
 ]
 
 HSA_OK = 0
@@ -69,6 +70,8 @@ def load_library():
         "dhsa_prefill_workspace_size": ([_I, _L, _I, _I, _I, _I], _Z),
         "dhsa_prefill": ([_P, _P, _P, _P, _I, _L, _P, _P, _P, _I, _L, _I, _I, _I, _P, _Z, _P],
                          _I),
+        "hsa_profile_enable": ([_I], _I),
+        "hsa_profile_read": ([_P, _I, _P], _I),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -252,3 +255,16 @@ def dhsa_prefill(Q, K, V, offsets, budget, out=None, return_mask=False, return_o
     if return_order:
         res.append(order)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def hsa_profile_enable(enable=True):
+    """Record per-stage HIP events in every following call on this thread."""
+    _check(load_library().hsa_profile_enable(1 if enable else 0))
+
+
+def hsa_profile_read(max_stages=8):
+    """(number of recorded calls, list of summed per-stage milliseconds)."""
+    buf = (ctypes.c_double * max_stages)()
+    ns = ctypes.c_int(0)
+    calls = load_library().hsa_profile_read(buf, max_stages, ctypes.byref(ns))
+    return calls, [buf[i] for i in range(min(ns.value, max_stages))]

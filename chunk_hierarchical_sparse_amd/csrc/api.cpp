@@ -10,14 +10,33 @@
 #include "hsa_attn.h"
 #include "kernels.h"
 
-namespace hsa {
-int64_t decode_max_chunks(int topk);
-int dhsa_max_chunks();
-}  // namespace hsa
-
 namespace {
 
 thread_local std::string g_err;
+
+// Optional per-stage event timing of the calling thread (profiling aid).
+struct Profile {
+  bool on = false;
+  std::vector<std::vector<hipEvent_t>> calls;
+};
+thread_local Profile g_prof;
+
+// Records an event before each stage of one call and one after the last.
+struct StageMarks {
+  hipStream_t st;
+  std::vector<hipEvent_t> ev;
+  explicit StageMarks(hipStream_t s) : st(s) {}
+  void mark() {
+    if (!g_prof.on) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEventRecord(e, st);
+    ev.push_back(e);
+  }
+  ~StageMarks() {
+    if (!ev.empty()) g_prof.calls.push_back(std::move(ev));
+  }
+};
 
 hsa_status_t fail(hsa_status_t s, const std::string& msg) {
   g_err = msg;
@@ -251,14 +270,21 @@ hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const floa
   if ((int64_t)B * Hkv * a.tiles_ub >= ((int64_t)1 << 31))
     return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
   hipError_t e;
+  StageMarks pm(st);
+  pm.mark();
   if (!lmk && n > 0) {
     e = hsa::launch_landmarks(K, a.dtype, lay.lmk, (int64_t)B * Hkv, L, n, d, S, 0, n, st);
     if (e != hipSuccess) return hip_fail(e, "landmarks");
   }
+  pm.mark();
   if ((e = hsa::prefill_select(a, st)) != hipSuccess) return hip_fail(e, "select");
+  pm.mark();
   if ((e = hsa::prefill_invert(a, st)) != hipSuccess) return hip_fail(e, "invert");
+  pm.mark();
   if ((e = hsa::prefill_attend(a, st)) != hipSuccess) return hip_fail(e, "attend");
+  pm.mark();
   if ((e = hsa::prefill_fuse(a, st)) != hipSuccess) return hip_fail(e, "fuse");
+  pm.mark();
   return HSA_OK;
 }
 
@@ -308,8 +334,15 @@ hsa_status_t hsa_decode(const void* q, const void* Kc, const void* Vc, const flo
   a.lmk_chunks = n_max / S;
   a.n_slices = lay.n_slices;
   a.slice = lay.slice;
-  hipError_t e = hsa::decode_run(a, (hipStream_t)stream);
-  return e == hipSuccess ? HSA_OK : hip_fail(e, "decode");
+  const hipStream_t st = (hipStream_t)stream;
+  StageMarks pm(st);
+  for (int stage = 0; stage < hsa::kDecodeStages; ++stage) {
+    pm.mark();
+    hipError_t e = hsa::decode_stage(a, stage, st);
+    if (e != hipSuccess) return hip_fail(e, "decode");
+  }
+  pm.mark();
+  return HSA_OK;
 }
 
 size_t dhsa_prefill_workspace_size(int B, int64_t L, int H, int d, int n_chunks,
@@ -381,8 +414,41 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
   a.budget = budget;
   if ((int64_t)B * H * n_chunks * a.tiles_per_chunk >= ((int64_t)1 << 31))
     return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
-  e = hsa::dhsa_run(a, st);
-  return e == hipSuccess ? HSA_OK : hip_fail(e, "dhsa");
+  StageMarks pm(st);
+  for (int stage = 0; stage < hsa::kDhsaStages; ++stage) {
+    pm.mark();
+    e = hsa::dhsa_stage(a, stage, st);
+    if (e != hipSuccess) return hip_fail(e, "dhsa");
+  }
+  pm.mark();
+  return HSA_OK;
+}
+
+hsa_status_t hsa_profile_enable(int enable) {
+  g_err.clear();
+  g_prof.on = enable != 0;
+  return HSA_OK;
+}
+
+int hsa_profile_read(double* stage_ms, int max_stages, int* n_stages) {
+  g_err.clear();
+  int stages = 0;
+  for (auto& ev : g_prof.calls) {
+    if (ev.empty()) continue;
+    hipEventSynchronize(ev.back());
+    const int ns = (int)ev.size() - 1;
+    if (ns > stages) stages = ns;
+    for (int s = 0; s < ns && s < max_stages; ++s) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, ev[s], ev[s + 1]) == hipSuccess && stage_ms) stage_ms[s] += ms;
+    }
+  }
+  const int calls = (int)g_prof.calls.size();
+  for (auto& ev : g_prof.calls)
+    for (hipEvent_t e : ev) hipEventDestroy(e);
+  g_prof.calls.clear();
+  if (n_stages) *n_stages = stages;
+  return calls;
 }
 
 }  // extern "C"

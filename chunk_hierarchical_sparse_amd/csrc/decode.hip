@@ -288,21 +288,25 @@ __global__ void __launch_bounds__(64) fuse_kernel(DecodeArgs a) {
 }
 
 template <int D, int DT>
-hipError_t run_dt(const DecodeArgs& a, hipStream_t stream) {
+hipError_t stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
   const int64_t BG = (int64_t)a.B * a.Hkv;
   const float scale = 1.0f / sqrtf((float)D);
-  if (a.n_avail > 0) {
-    scan_kernel<D, DT><<<dim3((unsigned)(BG * a.n_slices)), dim3(kThreads), 0, stream>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  switch (stage) {
+    case 0:
+      if (a.n_avail > 0)
+        scan_kernel<D, DT><<<dim3((unsigned)(BG * a.n_slices)), dim3(kThreads), 0, stream>>>(a);
+      break;
+    case 1:
+      merge_kernel<<<dim3((unsigned)BG), dim3(kThreads), 0, stream>>>(a);
+      break;
+    case 2:
+      attend_kernel<D, DT><<<dim3((unsigned)(BG * a.topk)), dim3(kThreads), 0, stream>>>(a,
+                                                                                       scale);
+      break;
+    default:
+      fuse_kernel<D, DT><<<dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(64), 0, stream>>>(a);
+      break;
   }
-  merge_kernel<<<dim3((unsigned)BG), dim3(kThreads), 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  attend_kernel<D, DT><<<dim3((unsigned)(BG * a.topk)), dim3(kThreads), 0, stream>>>(a, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  fuse_kernel<D, DT><<<dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(64), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -329,9 +333,12 @@ void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* sl
 
 int64_t decode_max_chunks(int topk) { return (int64_t)kMaxSlice * (kMaxCand / topk); }
 
-hipError_t decode_run(const DecodeArgs& a, hipStream_t stream) {
-  if (a.d == 64) return a.dtype == kF32 ? run_dt<64, kF32>(a, stream) : run_dt<64, kBF16>(a, stream);
-  return a.dtype == kF32 ? run_dt<128, kF32>(a, stream) : run_dt<128, kBF16>(a, stream);
+hipError_t decode_stage(const DecodeArgs& a, int stage, hipStream_t stream) {
+  if (a.d == 64)
+    return a.dtype == kF32 ? stage_dt<64, kF32>(a, stage, stream)
+                           : stage_dt<64, kBF16>(a, stage, stream);
+  return a.dtype == kF32 ? stage_dt<128, kF32>(a, stage, stream)
+                         : stage_dt<128, kBF16>(a, stage, stream);
 }
 
 }  // namespace hsa

@@ -276,43 +276,52 @@ __global__ void mask_kernel(DhsaArgs a) {
 
 }  // namespace
 
-hipError_t dhsa_run(const DhsaArgs& a, hipStream_t stream) {
+hipError_t dhsa_stage(const DhsaArgs& a, int stage, hipStream_t stream) {
   const int64_t BH = (int64_t)a.B * a.H;
   const int64_t rows = BH * a.nc;
   if (rows == 0 || a.L == 0) return hipSuccess;
-  const int VEC = a.dtype == kF32 ? 4 : 8;
-  const size_t lds_pool = 2 * (size_t)(kThreads / (a.d / VEC)) * a.d * sizeof(float);
-  if (a.dtype == kF32)
-    pool_kernel<kF32><<<dim3((unsigned)rows), dim3(kThreads), lds_pool, stream>>>(a);
-  else
-    pool_kernel<kBF16><<<dim3((unsigned)rows), dim3(kThreads), lds_pool, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.d == 64)
-    sc_kernel<64><<<dim3((unsigned)rows), dim3(kThreads), 0, stream>>>(a);
-  else
-    sc_kernel<128><<<dim3((unsigned)rows), dim3(kThreads), 0, stream>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  int P = 1;
-  while (P < a.nc) P <<= 1;
-  rank_kernel<<<dim3((unsigned)rows), dim3(kThreads), (size_t)P * sizeof(uint64_t), stream>>>(a,
-                                                                                              P);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const float sl2 = 1.4426950408889634f / sqrtf((float)a.d);
-  const int64_t blocks = rows * a.tiles_per_chunk;
-  if (a.d == 64)
-    attend_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2);
-  else
-    attend_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.mask_bits) {
-    const int64_t total = BH * a.L * ((a.L + 31) / 32);
-    int64_t nb = (total + 255) / 256;
-    if (nb > 65536) nb = 65536;
-    mask_kernel<<<dim3((unsigned)nb), dim3(256), 0, stream>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  switch (stage) {
+    case 0: {
+      const int VEC = a.dtype == kF32 ? 4 : 8;
+      const size_t lds = 2 * (size_t)(kThreads / (a.d / VEC)) * a.d * sizeof(float);
+      if (a.dtype == kF32)
+        pool_kernel<kF32><<<dim3((unsigned)rows), dim3(kThreads), lds, stream>>>(a);
+      else
+        pool_kernel<kBF16><<<dim3((unsigned)rows), dim3(kThreads), lds, stream>>>(a);
+      break;
+    }
+    case 1:
+      if (a.d == 64)
+        sc_kernel<64><<<dim3((unsigned)rows), dim3(kThreads), 0, stream>>>(a);
+      else
+        sc_kernel<128><<<dim3((unsigned)rows), dim3(kThreads), 0, stream>>>(a);
+      break;
+    case 2: {
+      int P = 1;
+      while (P < a.nc) P <<= 1;
+      rank_kernel<<<dim3((unsigned)rows), dim3(kThreads), (size_t)P * sizeof(uint64_t),
+                    stream>>>(a, P);
+      break;
+    }
+    case 3: {
+      const float sl2 = 1.4426950408889634f / sqrtf((float)a.d);
+      const int64_t blocks = rows * a.tiles_per_chunk;
+      if (a.d == 64)
+        attend_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2);
+      else
+        attend_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2);
+      break;
+    }
+    default: {
+      if (!a.mask_bits) return hipSuccess;
+      const int64_t total = BH * a.L * ((a.L + 31) / 32);
+      int64_t nb = (total + 255) / 256;
+      if (nb > 65536) nb = 65536;
+      mask_kernel<<<dim3((unsigned)nb), dim3(256), 0, stream>>>(a);
+      break;
+    }
   }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 int dhsa_max_chunks() { return kMaxSort; }

@@ -68,7 +68,10 @@ struct DecodeArgs {
   int n_slices, slice;
 };
 void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* slice);
-hipError_t decode_run(const DecodeArgs& a, hipStream_t stream);
+// stages: 0 scan, 1 merge, 2 attend, 3 fuse
+constexpr int kDecodeStages = 4;
+hipError_t decode_stage(const DecodeArgs& a, int stage, hipStream_t stream);
+int64_t decode_max_chunks(int topk);
 
 // ---- DHSA prefill (dhsa.hip) -----------------------------------------------
 struct DhsaArgs {
@@ -87,6 +90,9 @@ struct DhsaArgs {
   int B, H, d, dtype, nc, tiles_per_chunk;
   int64_t L, budget;
 };
-hipError_t dhsa_run(const DhsaArgs& a, hipStream_t stream);
+// stages: 0 pool, 1 sc, 2 rank, 3 attend, 4 mask (only with mask_bits)
+constexpr int kDhsaStages = 5;
+hipError_t dhsa_stage(const DhsaArgs& a, int stage, hipStream_t stream);
+int dhsa_max_chunks();
 
 }  // namespace hsa

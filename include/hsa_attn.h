@@ -155,6 +155,22 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
                           hsa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                           hsa_stream_t stream);
 
+/*
+ * Profiling aid (not part of the method).  While enabled on the calling
+ * thread, each hsa_prefill, hsa_decode and dhsa_prefill call records a HIP
+ * event on its stream before each of its stages and one after the last:
+ *   hsa_prefill : 0 landmarks, 1 select, 2 invert, 3 attend, 4 fuse
+ *   hsa_decode  : 0 scan, 1 merge, 2 attend, 3 fuse
+ *   dhsa_prefill: 0 pool, 1 S_c, 2 rank, 3 attend, 4 mask
+ * hsa_profile_read waits for the recorded events, adds the elapsed
+ * milliseconds of stage s summed over all recorded calls into stage_ms[s]
+ * (s < max_stages; the caller zeroes the array), releases the events and
+ * returns the number of calls; *n_stages receives the stage count.  The
+ * events are host-side runtime objects; no device memory is allocated.
+ */
+hsa_status_t hsa_profile_enable(int enable);
+int hsa_profile_read(double* stage_ms, int max_stages, int* n_stages);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,8 @@ def lib():
                                                _I, _I, _I, _P, _P]
         L.oracle_dhsa_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _P, _I, _I,
                                           _P, _I, _P, _P, _P, _P, _P]
-        for f in (L.oracle_landmarks, L.oracle_hsa_prefill, L.oracle_hsa_decode_select,
+        L.oracle_num_threads.argtypes = []
+        for f in (L.oracle_num_threads, L.oracle_landmarks, L.oracle_hsa_prefill, L.oracle_hsa_decode_select,
                   L.oracle_hsa_decode_attend, L.oracle_dhsa_prefill):
             f.restype = ctypes.c_int
         _lib = L
@@ -64,6 +65,11 @@ def _ptr(a):
 def _check(rc, what):
     if rc != 0:
         raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def num_threads():
+    """Threads the oracle's OpenMP loops use."""
+    return int(lib().oracle_num_threads())
 
 
 def landmarks(K, S):

@@ -47,7 +47,20 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 enum { OR_F32 = 0, OR_BF16 = 1 };
+
+/* Number of threads the oracle's parallel loops use. */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 enum {
   OR_OK = 0,
