@@ -104,15 +104,19 @@ __device__ __forceinline__ bf16x8 cvt_bf16x8(const f32x16& p, int base) {
   return r;
 }
 
-// One key block: keys with in-block index < nvalid are attended by this
-// lane's query (nvalid may differ per lane; 0 = none).  scale_log2 =
+// One key block of nkeys (<= 64, the same for the whole block) staged keys:
+// keys with in-block index < nvalid are attended by this lane's query
+// (nvalid <= nkeys may differ per lane; 0 = none).  scale_log2 =
 // log2(e)/sqrt(d).  Must be called by every lane of the wave.
 template <int D>
-__device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>& sm, int nvalid,
-                                                float scale_log2) {
+__device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>& sm, int nkeys,
+                                                int nvalid, float scale_log2) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int i32 = lane & 31;
+  // keys 32..63 of the block exist only when the block holds more than 32
+  // (block-uniform, so the branch does not diverge)
+  const bool two = nkeys > 32;
   f32x16 s0, s1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -122,10 +126,13 @@ __device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     const bf16x8 a0 = *(const bf16x8*)(&sm.k[i32 * (D + 8) + 16 * s + 8 * h]);
-    const bf16x8 a1 = *(const bf16x8*)(&sm.k[(32 + i32) * (D + 8) + 16 * s + 8 * h]);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, st.qf[s], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, st.qf[s], s1, 0, 0, 0);
+    if (two) {
+      const bf16x8 a1 = *(const bf16x8*)(&sm.k[(32 + i32) * (D + 8) + 16 * s + 8 * h]);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, st.qf[s], s1, 0, 0, 0);
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -150,16 +157,22 @@ __device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>
   ps += __shfl_xor(ps, 32, kWave);
   st.l = st.l * alpha + ps;
   st.m = m_new;
+  bf16x8 pb4[4];
+  pb4[0] = cvt_bf16x8(s0, 0);
+  pb4[1] = cvt_bf16x8(s0, 8);
+  pb4[2] = cvt_bf16x8(s1, 0);
+  pb4[3] = cvt_bf16x8(s1, 8);
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.o[b][r] *= alpha;
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const f32x16& p = kt == 0 ? s0 : s1;
+    if (kt == 1 && !two) break;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8 pb = cvt_bf16x8(p, 8 * s2);
+      const bf16x8 pb = pb4[2 * kt + s2];
       const int g0 = 8 * kt + 4 * s2 + h;  // key quad of k-slots 0..3
       const int g1 = g0 + 2;               // key quad of k-slots 4..7
 #pragma unroll

@@ -98,7 +98,7 @@ __device__ int block_topk_u64(const uint64_t* keys, int M, int K, uint64_t* out,
 template <int D, int DT>
 __global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
   __shared__ float u[D];
-  __shared__ uint64_t keys[kMaxSlice];
+  extern __shared__ uint64_t keys[];  // [slice]
   __shared__ uint64_t sel[32];
   __shared__ int hist[256];
   __shared__ int sv[4];
@@ -181,16 +181,20 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(DecodeArgs a) {
   if (threadIdx.x < a.topk) sel[threadIdx.x] = threadIdx.x < got ? sorted[threadIdx.x] : -1;
 }
 
-// Per (b, group, selected chunk): wave = head (looping over the group's
-// heads), keys of the chunk in blocks staged in LDS.
+// Per (b, group, selected chunk): the chunk's keys/values are staged in LDS
+// 64 (bf16) or 32 (fp32) rows at a time with 16-byte loads; wave = head
+// (looping over the group's heads), lane = key for the logits and lane =
+// output column for the weighted sum.
 template <int D, int DT>
 __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float scale) {
-  constexpr int KB = DT == kF32 ? 32 : 64;  // keys per LDS block
+  constexpr int KB = DT == kF32 ? 32 : 64;   // keys per LDS block
+  constexpr int EB = DT == kF32 ? 4 : 2;     // bytes per element
+  constexpr int VE = 16 / EB;                // elements per 16-byte piece
+  constexpr int KSTR = D + VE;               // key row stride, padded by 16 bytes
   typedef typename std::conditional<DT == kF32, float, uint16_t>::type T;
-  constexpr int PAD = DT == kF32 ? 1 : 2;  // one dword of row padding
-  __shared__ T ks[KB * (D + PAD)];
-  __shared__ T vs[KB * D];
-  __shared__ float qs[32 * D];
+  __shared__ __attribute__((aligned(16))) T ks[KB * KSTR];
+  __shared__ __attribute__((aligned(16))) T vs[KB * D];
+  __shared__ __attribute__((aligned(16))) float qs[32 * D];
   const int64_t bg = blockIdx.x / a.topk;
   const int k = blockIdx.x % a.topk;
   const int c = a.sel[bg * a.topk + k];
@@ -200,9 +204,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float sc
   for (int e = threadIdx.x; e < G * D; e += kThreads)
     qs[e] = load_elem<DT>(a.q, ((int64_t)b * a.Hq + g * G) * D + e);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // per-head state: each wave handles heads w, w+4, ...; lanes hold D/64
-  // output columns.
-  constexpr int CPL = D / 64;
+  constexpr int CPL = D / 64;  // output columns per lane
   float m[8], l[8], o[8][CPL];
   for (int hi = 0; hi < 8; ++hi) {
     m[hi] = -INFINITY;
@@ -212,28 +214,39 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float sc
   const int64_t base = (bg * a.n_max + (int64_t)c * a.S) * D;
   const T* Kg = (const T*)a.Kc + base;
   const T* Vg = (const T*)a.Vc + base;
+  constexpr int PPR = D / VE;  // 16-byte pieces per row
   for (int kb = 0; kb < a.S; kb += KB) {
     const int nk = min(KB, a.S - kb);
     __syncthreads();
-    for (int e = threadIdx.x; e < KB * D; e += kThreads) {
-      const int row = e / D, col = e % D;
-      T kv = 0, vv = 0;
+    for (int e = threadIdx.x; e < KB * PPR; e += kThreads) {
+      const int row = e / PPR, pc = e % PPR;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (row < nk) {
-        kv = Kg[(int64_t)(kb + row) * D + col];
-        vv = Vg[(int64_t)(kb + row) * D + col];
+        kv = *(const u32x4*)(Kg + (int64_t)(kb + row) * D + pc * VE);
+        vv = *(const u32x4*)(Vg + (int64_t)(kb + row) * D + pc * VE);
       }
-      ks[row * (D + PAD) + col] = kv;
-      vs[row * D + col] = vv;
+      *(u32x4*)(&ks[row * KSTR + pc * VE]) = kv;
+      *(u32x4*)(&vs[row * D + pc * VE]) = vv;
     }
     __syncthreads();
     int hi = 0;
     for (int hh = w; hh < G; hh += 4, ++hi) {
-      // logits: lane j = key j of the block
       float dot = -INFINITY;
       if (lane < nk) {
         float acc = 0.f;
-        for (int x = 0; x < D; ++x)
-          acc += qs[hh * D + x] * load_elem<DT>(ks, (int64_t)lane * (D + PAD) + x);
+        for (int x = 0; x < D; x += VE) {
+          const u32x4 kx = *(const u32x4*)(&ks[lane * KSTR + x]);
+          if (DT == kF32) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc += qs[hh * D + x + v] * __uint_as_float(kx[v]);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              acc += qs[hh * D + x + 2 * v] * bf16_bits_to_f32(kx[v] & 0xffffu);
+              acc += qs[hh * D + x + 2 * v + 1] * bf16_bits_to_f32(kx[v] >> 16);
+            }
+          }
+        }
         dot = acc * scale;
       }
       const float bm = wave_max(dot);
@@ -294,7 +307,8 @@ hipError_t stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
   switch (stage) {
     case 0:
       if (a.n_avail > 0)
-        scan_kernel<D, DT><<<dim3((unsigned)(BG * a.n_slices)), dim3(kThreads), 0, stream>>>(a);
+        scan_kernel<D, DT><<<dim3((unsigned)(BG * a.n_slices)), dim3(kThreads),
+                             (size_t)a.slice * sizeof(uint64_t), stream>>>(a);
       break;
     case 1:
       merge_kernel<<<dim3((unsigned)BG), dim3(kThreads), 0, stream>>>(a);

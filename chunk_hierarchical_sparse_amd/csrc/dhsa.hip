@@ -185,7 +185,7 @@ __device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int
 }
 
 template <int D>
-__global__ void __launch_bounds__(kThreads) attend_kernel(DhsaArgs a, float scale_log2) {
+__global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float scale_log2) {
   __shared__ KVSmem<D> sm;
   __shared__ int pmax;
   const int64_t per_bh = (int64_t)a.nc * a.tiles_per_chunk;
@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DhsaArgs a, float scal
       load_kv_block<D>(sm, Kb + (int64_t)(bk + kb) * D, Vb + (int64_t)(bk + kb) * D, nk);
       __syncthreads();
       const int nv = max(0, min(hi - kb, nk));
-      if (wave_any && __ballot(nv > 0) != 0) wave_attn_block<D>(st, sm, nv, scale_log2);
+      if (wave_any && __ballot(nv > 0) != 0) wave_attn_block<D>(st, sm, nk, nv, scale_log2);
     }
   }
   if (!valid) return;

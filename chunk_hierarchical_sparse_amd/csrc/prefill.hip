@@ -30,40 +30,47 @@ constexpr int kThreads = 256;
 
 // Keep a descending top-KM list in registers.  Candidates of one lane
 // arrive in increasing index order, so a strict '>' places a later
-// equal-score candidate after the earlier one (lower index first).
+// equal-score candidate after the earlier one (lower index first).  The
+// list is sorted, so slot j becomes max(min(s, ls[j-1]), ls[j]) and its
+// index follows the same choice; both are written as min/max and bit
+// masks so the compiler emits straight-line code.
 template <int KM>
 __device__ __forceinline__ void topk_insert_ordered(float (&ls)[KM], int (&li)[KM], float s,
                                                     int c) {
+  int m[KM];
 #pragma unroll
-  for (int j = KM - 1; j >= 0; --j) {
-    const bool gt_prev = j > 0 ? (s > ls[j > 0 ? j - 1 : 0]) : false;
-    const bool gt_cur = s > ls[j];
-    const float ns = gt_prev ? ls[j > 0 ? j - 1 : 0] : (gt_cur ? s : ls[j]);
-    const int ni = gt_prev ? li[j > 0 ? j - 1 : 0] : (gt_cur ? c : li[j]);
-    ls[j] = ns;
-    li[j] = ni;
+  for (int j = 0; j < KM; ++j) m[j] = -(int)(s > ls[j]);  // all ones where s beats slot j
+#pragma unroll
+  for (int j = KM - 1; j > 0; --j) {
+    ls[j] = fmaxf(fminf(s, ls[j - 1]), ls[j]);
+    const int t = (c & m[j]) | (li[j] & ~m[j]);
+    li[j] = (li[j - 1] & m[j - 1]) | (t & ~m[j - 1]);
   }
+  ls[0] = fmaxf(s, ls[0]);
+  li[0] = (c & m[0]) | (li[0] & ~m[0]);
 }
 
 // Full (score desc, index asc) comparison for merging lists of different
-// lanes/waves.
+// lanes/waves (bitwise, so no short-circuit branches).
 __device__ __forceinline__ bool better(float s, int c, float t, int d) {
-  return s > t || (s == t && c < d);
+  return (s > t) | ((s == t) & (c < d));
 }
 
 template <int KM>
 __device__ __forceinline__ void topk_insert_any(float (&ls)[KM], int (&li)[KM], float s, int c) {
-  if (c < 0) return;
+  int m[KM];
 #pragma unroll
-  for (int j = KM - 1; j >= 0; --j) {
-    const bool gt_prev = j > 0 ? better(s, c, ls[j > 0 ? j - 1 : 0], li[j > 0 ? j - 1 : 0])
-                               : false;
-    const bool gt_cur = better(s, c, ls[j], li[j]);
-    const float ns = gt_prev ? ls[j > 0 ? j - 1 : 0] : (gt_cur ? s : ls[j]);
-    const int ni = gt_prev ? li[j > 0 ? j - 1 : 0] : (gt_cur ? c : li[j]);
-    ls[j] = ns;
-    li[j] = ni;
+  for (int j = 0; j < KM; ++j) m[j] = -(int)((c >= 0) & better(s, c, ls[j], li[j]));
+  const int sb = __float_as_int(s);
+#pragma unroll
+  for (int j = KM - 1; j > 0; --j) {
+    const int ts = (sb & m[j]) | (__float_as_int(ls[j]) & ~m[j]);
+    const int ti = (c & m[j]) | (li[j] & ~m[j]);
+    ls[j] = __int_as_float((__float_as_int(ls[j - 1]) & m[j - 1]) | (ts & ~m[j - 1]));
+    li[j] = (li[j - 1] & m[j - 1]) | (ti & ~m[j - 1]);
   }
+  ls[0] = __int_as_float((sb & m[0]) | (__float_as_int(ls[0]) & ~m[0]));
+  li[0] = (c & m[0]) | (li[0] & ~m[0]);
 }
 
 // One block = 64 consecutive queries of one (b, group); lane = query.  The
@@ -129,7 +136,7 @@ __global__ void __launch_bounds__(kThreads) select_valu_kernel(PrefillArgs a, in
         dot += u[x + 2] * l4[2];
         dot += u[x + 3] * l4[3];
       }
-      if (c < navail) topk_insert_ordered<KM>(ls, li, dot, (int)c);
+      topk_insert_ordered<KM>(ls, li, c < navail ? dot : -INFINITY, (int)c);
     }
   }
   __syncthreads();  // the landmark tile is dead; its LDS now holds the lists
@@ -146,14 +153,151 @@ __global__ void __launch_bounds__(kThreads) select_valu_kernel(PrefillArgs a, in
     for (int j = 0; j < KM; ++j)
       topk_insert_any<KM>(ls, li, ms[(ww * 64 + lane) * KM + j], mi[(ww * 64 + lane) * KM + j]);
   int32_t* out = a.idx + (bg * a.L + t) * a.topk;
-  int32_t* cnt = a.counts + bg * a.n;
 #pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    if (j < a.topk) {
-      out[j] = li[j];
-      if (li[j] >= 0) atomicAdd(&cnt[li[j]], 1);
+  for (int j = 0; j < KM; ++j)
+    if (j < a.topk) out[j] = li[j];
+}
+
+// bf16 inputs: scores on MFMA.  Each wave owns 32 consecutive queries; a
+// block owns 128 queries of one (b, group).  Landmark tiles of 32 chunks are
+// staged in LDS split into three bf16 parts (hi + lo + lo2 == the fp32 value
+// exactly), the group-summed query u likewise in registers, and
+// u.lmk = sum of the six part products whose order is at most 2^-16 of the
+// leading one, accumulated in fp32 by v_mfma_f32_32x32x16_bf16: the result
+// is as accurate as an fp32 dot product.  S^T = LMK U^T puts one query per
+// lane (lanes l and l^32 hold disjoint halves of each chunk tile), so each
+// lane keeps its own sorted top-KM list; the two halves merge at the end.
+__device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& lo, uint16_t& lo2) {
+  const __bf16 h = static_cast<__bf16>(x);  // round to nearest even
+  const float r1 = x - static_cast<float>(h);
+  const __bf16 l = static_cast<__bf16>(r1);
+  const float r2 = r1 - static_cast<float>(l);
+  const __bf16 m = static_cast<__bf16>(r2);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+  lo2 = __builtin_bit_cast(uint16_t, m);
+}
+
+template <int D, int KM>
+__global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a, int64_t nqt) {
+  constexpr int TILE = 32;
+  constexpr int RS = D + 8;  // padded LDS row (bf16 elements)
+  __shared__ __attribute__((aligned(16))) uint16_t lt[3][TILE * RS];
+  const int64_t bg = blockIdx.x / nqt;
+  const int64_t qt = blockIdx.x % nqt;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int G = a.Hq / a.Hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i32 = lane & 31, hf = lane >> 5;
+  const int64_t t = qt * 128 + w * 32 + i32;
+  const bool tvalid = t < a.L;
+  const int64_t navail = tvalid ? min(t / a.S, a.n) : 0;
+  const int64_t tlast_b = min(qt * 128 + 127, a.L - 1);
+  const int64_t bavail = min(tlast_b / a.S, a.n);
+  const int64_t tlast_w = min(qt * 128 + w * 32 + 31, a.L - 1);
+  const int64_t wavail = qt * 128 + w * 32 < a.L ? min(tlast_w / a.S, a.n) : 0;
+
+  // u = sum over the group's heads, dims 16s + 8hf + e, split in 3 parts
+  bf16x8 u0[D / 16], u1[D / 16], u2[D / 16];
+  {
+    const uint16_t* Q = (const uint16_t*)a.Q;
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      if (tvalid) {
+        for (int hh = 0; hh < G; ++hh) {
+          const u32x4 x = *(const u32x4*)(Q + (((int64_t)b * a.Hq + g * G + hh) * a.L + t) * D +
+                                          16 * s2 + 8 * hf);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            acc[2 * v] += bf16_bits_to_f32(x[v] & 0xffffu);
+            acc[2 * v + 1] += bf16_bits_to_f32(x[v] >> 16);
+          }
+        }
+      }
+      u32x4 p0, p1, p2;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        uint16_t h0, l0, m0, h1, l1, m1;
+        split3_bf16(acc[2 * v], h0, l0, m0);
+        split3_bf16(acc[2 * v + 1], h1, l1, m1);
+        p0[v] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        p1[v] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        p2[v] = (uint32_t)m0 | ((uint32_t)m1 << 16);
+      }
+      u0[s2] = __builtin_bit_cast(bf16x8, p0);
+      u1[s2] = __builtin_bit_cast(bf16x8, p1);
+      u2[s2] = __builtin_bit_cast(bf16x8, p2);
     }
   }
+  float ls[KM];
+  int li[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    ls[j] = -INFINITY;
+    li[j] = -1;
+  }
+  const float* lmk = a.lmk + bg * a.n * D;
+  for (int64_t c0 = 0; c0 < bavail; c0 += TILE) {
+    __syncthreads();
+    // stage 32 landmark rows as three bf16 planes
+    for (int e = threadIdx.x; e < TILE * D / 4; e += kThreads) {
+      const int row = (e * 4) / D, col = (e * 4) % D;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (c0 + row < bavail) v = *(const f32x4*)(lmk + (c0 + row) * D + col);
+      uint16_t h[4], l[4], m[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) split3_bf16(v[x], h[x], l[x], m[x]);
+      *(u32x2*)(&lt[0][row * RS + col]) = u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+      *(u32x2*)(&lt[1][row * RS + col]) = u32x2{(uint32_t)l[0] | ((uint32_t)l[1] << 16),
+                                                (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
+      *(u32x2*)(&lt[2][row * RS + col]) = u32x2{(uint32_t)m[0] | ((uint32_t)m[1] << 16),
+                                                (uint32_t)m[2] | ((uint32_t)m[3] << 16)};
+    }
+    __syncthreads();
+    if (c0 >= wavail) continue;  // wave-uniform: no query of this wave sees these chunks
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) {
+      const int off = i32 * RS + 16 * s2 + 8 * hf;
+      const bf16x8 l0 = *(const bf16x8*)(&lt[0][off]);
+      const bf16x8 l1 = *(const bf16x8*)(&lt[1][off]);
+      const bf16x8 l2 = *(const bf16x8*)(&lt[2][off]);
+      // smallest terms first
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l2, u0[s2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, u1[s2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, u2[s2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, u0[s2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, u1[s2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, u0[s2], acc, 0, 0, 0);
+    }
+    // lane's candidates come in increasing chunk order: r -> 8(r/4)+4hf+r%4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = (int)c0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      topk_insert_ordered<KM>(ls, li, c < navail ? acc[r] : -INFINITY, c);
+    }
+  }
+  // merge the two halves of each query (lane l and l ^ 32)
+  float os[KM];
+  int oi[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    os[j] = __shfl_xor(ls[j], 32, kWave);
+    oi[j] = __shfl_xor(li[j], 32, kWave);
+  }
+  if (hf != 0 || !tvalid) return;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) topk_insert_any<KM>(ls, li, os[j], oi[j]);
+  int32_t* out = a.idx + (bg * a.L + t) * a.topk;
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < a.topk) out[j] = li[j];
 }
 
 // ---------------------------------------------------------------- invert --
@@ -207,19 +351,76 @@ __global__ void __launch_bounds__(1024) scan_kernel(PrefillArgs a) {
   }
 }
 
-// One thread per (b, group, token, slot): append (token*topk + slot) to the
-// selected chunk's list.  The order inside a list does not affect results:
-// every row is computed independently of the others in its tile.
-__global__ void scatter_kernel(PrefillArgs a) {
-  const int64_t total = (int64_t)a.B * a.Hkv * a.L * a.topk;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t c = a.idx[i];
+constexpr int kInvertTokens = 1024;  // tokens per counting / scatter block
+constexpr int kInvertLdsBins = 8192;  // chunks whose counters fit in LDS (2 arrays)
+
+// Per-chunk selection counts.  Each block histograms the selections of
+// kInvertTokens tokens in LDS and adds one global atomic per touched chunk,
+// so hot chunks see a few hundred global atomics instead of one per
+// selection.
+__global__ void __launch_bounds__(256) count_kernel(PrefillArgs a, int64_t blocks_per_bg,
+                                                    int use_lds) {
+  extern __shared__ int32_t hist[];  // [n]
+  const int64_t bg = blockIdx.x / blocks_per_bg;
+  const int64_t t0 = (blockIdx.x % blocks_per_bg) * kInvertTokens;
+  const int64_t t1 = min(t0 + kInvertTokens, a.L);
+  const int32_t* idx = a.idx + bg * a.L * a.topk;
+  int32_t* cnt = a.counts + bg * a.n;
+  if (use_lds) {
+    for (int c = threadIdx.x; c < a.n; c += 256) hist[c] = 0;
+    __syncthreads();
+  }
+  for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
+    const int32_t c = idx[i];
     if (c < 0) continue;
-    const int64_t bg = i / (a.L * a.topk);
-    const int32_t e = (int32_t)(i % (a.L * a.topk));
-    const int32_t pos = a.offs[bg * (a.n + 1) + c] + atomicAdd(&a.cursor[bg * a.n + c], 1);
-    a.list[bg * a.L * a.topk + pos] = e;
+    if (use_lds)
+      atomicAdd(&hist[c], 1);
+    else
+      atomicAdd(&cnt[c], 1);
+  }
+  if (!use_lds) return;
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.n; c += 256)
+    if (hist[c] != 0) atomicAdd(&cnt[c], hist[c]);
+}
+
+// Append (token*topk + slot) entries to the selected chunks' lists.  With
+// LDS bins: count locally, reserve one range per touched chunk with a global
+// atomic, then place entries by LDS atomics inside the range.  The order
+// inside a list does not affect results: every row is computed
+// independently of the others that share its chunk.
+__global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blocks_per_bg,
+                                                      int use_lds) {
+  extern __shared__ int32_t bins[];  // [2][n]: local counts, then running positions
+  const int64_t bg = blockIdx.x / blocks_per_bg;
+  const int64_t t0 = (blockIdx.x % blocks_per_bg) * kInvertTokens;
+  const int64_t t1 = min(t0 + kInvertTokens, a.L);
+  const int32_t* idx = a.idx + bg * a.L * a.topk;
+  const int32_t* offs = a.offs + bg * (a.n + 1);
+  int32_t* cursor = a.cursor + bg * a.n;
+  int32_t* list = a.list + bg * a.L * a.topk;
+  if (!use_lds) {
+    for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
+      const int32_t c = idx[i];
+      if (c >= 0) list[offs[c] + atomicAdd(&cursor[c], 1)] = (int32_t)i;
+    }
+    return;
+  }
+  int32_t* local = bins;
+  int32_t* pos = bins + a.n;
+  for (int c = threadIdx.x; c < a.n; c += 256) local[c] = 0;
+  __syncthreads();
+  for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
+    const int32_t c = idx[i];
+    if (c >= 0) atomicAdd(&local[c], 1);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.n; c += 256)
+    pos[c] = local[c] != 0 ? offs[c] + atomicAdd(&cursor[c], local[c]) : 0;
+  __syncthreads();
+  for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
+    const int32_t c = idx[i];
+    if (c >= 0) list[atomicAdd(&pos[c], 1)] = (int32_t)i;
   }
 }
 
@@ -279,7 +480,7 @@ __global__ void __launch_bounds__(kThreads) attend_bf16_kernel(PrefillArgs a, fl
     load_kv_block<D>(sm, (const uint16_t*)a.K + kv0 + (int64_t)kb * D,
                      (const uint16_t*)a.V + kv0 + (int64_t)kb * D, nk);
     __syncthreads();
-    if (wave_any) wave_attn_block<D>(st, sm, valid ? nk : 0, scale_log2);
+    if (wave_any) wave_attn_block<D>(st, sm, nk, valid ? nk : 0, scale_log2);
   }
   if (!wave_any) return;
   float s = wave_q_dot_half<D>(st, a.lmk + (bg * a.n + c) * D);
@@ -299,6 +500,176 @@ __global__ void __launch_bounds__(kThreads) attend_bf16_kernel(PrefillArgs a, fl
                        pack_bf16x2(st.o[bb][4 * q4 + 2] * inv, st.o[bb][4 * q4 + 3] * inv)};
       *(u32x2*)(po + dd) = v;
     }
+}
+
+// bf16, S <= 64: one block per (b, group, chunk).  The chunk's K/V and
+// landmark are staged in LDS once; each wave then walks 32-row tiles of the
+// chunk's (token, head) rows.  A row sees exactly this chunk, so its softmax
+// is over at most 64 keys held in registers: no online rescaling.  The next
+// tile's list entry and Q row are fetched while the current tile computes.
+// Blocks are ordered chunk-major over all (b, group) so the most-selected
+// early chunks start first.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2)
+    attend_chunk_bf16_kernel(PrefillArgs a, float scale_log2, float score_scale) {
+  __shared__ KVSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) float lm[D];
+  const int64_t BG = (int64_t)a.B * a.Hkv;
+  const int c = (int)(blockIdx.x / BG);
+  const int64_t bg = blockIdx.x % BG;
+  const int32_t* offs = a.offs + bg * (a.n + 1);
+  const int e_begin = offs[c];
+  const int cnt = offs[c + 1] - e_begin;
+  if (cnt == 0) return;
+  const int G = a.Hq / a.Hkv;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int rows = cnt * G;
+  const int ntiles = (rows + 31) / 32;
+  const int64_t kv0 = (bg * a.L + (int64_t)c * a.S) * D;
+  load_kv_block<D>(sm, (const uint16_t*)a.K + kv0, (const uint16_t*)a.V + kv0, a.S);
+  for (int x = threadIdx.x; x < D; x += kThreads) lm[x] = a.lmk[(bg * a.n + c) * D + x];
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i32 = lane & 31, hf = lane >> 5;
+  const int32_t* list = a.list + bg * a.L * a.topk + e_begin;
+  const uint16_t* Q = (const uint16_t*)a.Q;
+  const int64_t qplane = (int64_t)a.L * D;  // stride between heads
+  const int64_t qbase = (int64_t)b * a.Hq * qplane + (int64_t)g * G * qplane;
+
+  // row r of the chunk -> (entry, head); entry = token * topk + slot
+  auto entry_of = [&](int tile) -> int32_t {
+    const int r = tile * 32 + i32;
+    return r < rows ? list[r / G] : -1;
+  };
+  auto load_q = [&](int tile, int32_t entry, u32x4 (&q)[D / 16]) {
+    const int r = tile * 32 + i32;
+    if (entry >= 0) {
+      const int64_t t = entry / a.topk;
+      const uint16_t* qrow = Q + qbase + (int64_t)(r % G) * qplane + t * D + 8 * hf;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = *(const u32x4*)(qrow + 16 * s2);
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  int tile = w;
+  int32_t ent = tile < ntiles ? entry_of(tile) : -1;
+  int32_t ent_next = tile + 4 < ntiles ? entry_of(tile + 4) : -1;
+  u32x4 q[D / 16];
+  load_q(tile, ent, q);
+  const bool two = a.S > 32;
+  for (; tile < ntiles; tile += 4) {
+    // scores S^T = K Q^T for up to 64 keys
+    f32x16 s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = 0.f;
+      s1[r] = 0.f;
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) {
+      const bf16x8 qb = __builtin_bit_cast(bf16x8, q[s2]);
+      const bf16x8 a0 = *(const bf16x8*)(&sm.k[i32 * (D + 8) + 16 * s2 + 8 * hf]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb, s0, 0, 0, 0);
+      if (two) {
+        const bf16x8 a1 = *(const bf16x8*)(&sm.k[(32 + i32) * (D + 8) + 16 * s2 + 8 * hf]);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb, s1, 0, 0, 0);
+      }
+    }
+    // per-head retrieval score s_h(t, c) = q . lmk_c / sqrt(d)
+    float sh = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) {
+      const bf16x8 qb = __builtin_bit_cast(bf16x8, q[s2]);
+      const f32x4 l0 = *(const f32x4*)(&lm[16 * s2 + 8 * hf]);
+      const f32x4 l1 = *(const f32x4*)(&lm[16 * s2 + 8 * hf + 4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sh += (float)qb[e] * l0[e];
+        sh += (float)qb[e + 4] * l1[e];
+      }
+    }
+    sh += __shfl_xor(sh, 32, kWave);
+    __builtin_amdgcn_sched_barrier(0);
+    const int32_t ent_cur = ent;
+    const int r_cur = tile * 32 + i32;
+    // next tile: its Q rows stream in while this one finishes
+    ent = ent_next;
+    if (tile + 4 < ntiles) load_q(tile + 4, ent, q);
+    ent_next = tile + 8 < ntiles ? entry_of(tile + 8) : -1;
+    __builtin_amdgcn_sched_barrier(0);
+
+    // softmax over the chunk's keys (log2 domain)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+      s0[r] = key < a.S ? s0[r] * scale_log2 : -INFINITY;
+      s1[r] = key + 32 < a.S ? s1[r] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = fast_exp2(s0[r] - mx);
+      s1[r] = fast_exp2(s1[r] - mx);
+      ps += s0[r] + s1[r];
+    }
+    ps += __shfl_xor(ps, 32, kWave);
+    // P^T as bf16 MFMA operands; the fp32 scores die here
+    bf16x8 pb4[4];
+    pb4[0] = cvt_bf16x8(s0, 0);
+    pb4[1] = cvt_bf16x8(s0, 8);
+    pb4[2] = cvt_bf16x8(s1, 0);
+    pb4[3] = cvt_bf16x8(s1, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T = V^T P^T
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int bb = 0; bb < D / 32; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[bb][r] = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if (kt == 1 && !two) break;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 pb = pb4[2 * kt + s2];
+        const int g0 = 8 * kt + 4 * s2 + hf, g1 = g0 + 2;
+#pragma unroll
+        for (int bb = 0; bb < D / 32; ++bb) {
+          const int dd = 32 * bb + i32;
+          const u32x2 v0 = *(const u32x2*)(&sm.v[(g0 * D + dd) * 4]);
+          const u32x2 v1 = *(const u32x2*)(&sm.v[(g1 * D + dd) * 4]);
+          const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
+          o[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
+                                                          o[bb], 0, 0, 0);
+        }
+      }
+    }
+    if (ent_cur >= 0) {
+      const int64_t t = ent_cur / a.topk;
+      const int slot = ent_cur % a.topk;
+      const int h = g * G + r_cur % G;
+      const int64_t row = (((int64_t)b * a.Hq + h) * a.L + t) * a.topk + slot;
+      if (hf == 0) a.part_score[row] = sh * score_scale;
+      const float inv = 1.f / ps;
+      uint16_t* po = (uint16_t*)a.partial + row * D;
+#pragma unroll
+      for (int bb = 0; bb < D / 32; ++bb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int dd = 32 * bb + 8 * q4 + 4 * hf;
+          const u32x2 v = {pack_bf16x2(o[bb][4 * q4] * inv, o[bb][4 * q4 + 1] * inv),
+                           pack_bf16x2(o[bb][4 * q4 + 2] * inv, o[bb][4 * q4 + 3] * inv)};
+          *(u32x2*)(po + dd) = v;
+        }
+    }
+  }
 }
 
 // fp32: one wave per tile, one row per lane, online softmax on VALU.
@@ -353,8 +724,9 @@ __global__ void __launch_bounds__(64) attend_f32_kernel(PrefillArgs a, float sca
 
 // ------------------------------------------------------------------ fuse --
 
-// One group of D/VEC threads per (b, head, token) row.
-template <int D, int DT>
+// One group of D/VEC threads per (b, head, token) row; the row's slot loads
+// are all issued before the weighted sum.
+template <int D, int DT, int KM>
 __global__ void __launch_bounds__(kThreads) fuse_kernel(PrefillArgs a) {
   constexpr int VEC = DT == kF32 ? 4 : 8;
   constexpr int TPR = D / VEC;
@@ -366,26 +738,44 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(PrefillArgs a) {
   const int64_t t = row % a.L;
   const int m = (int)min((int64_t)a.topk, min(t / a.S, a.n));
   const float* sc = a.part_score + row * a.topk;
+  u32x4 x[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    if (k < m)
+      x[k] = __builtin_nontemporal_load(
+          (const u32x4*)((const char*)a.partial + ((row * a.topk + k) * D + cg * VEC) *
+                                                      (DT == kF32 ? 4 : 2)));
+    else
+      x[k] = u32x4{0u, 0u, 0u, 0u};
+  }
+  float s[KM];
   float smax = -INFINITY;
-  for (int k = 0; k < m; ++k) smax = fmaxf(smax, sc[k]);
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    s[k] = k < m ? sc[k] : -INFINITY;
+    smax = fmaxf(smax, s[k]);
+  }
   float z = 0.f;
-  for (int k = 0; k < m; ++k) z += expf(sc[k] - smax);
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    s[k] = k < m ? expf(s[k] - smax) : 0.f;
+    z += s[k];
+  }
+  const float iz = m > 0 ? 1.f / z : 0.f;
   float acc[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-  for (int k = 0; k < m; ++k) {
-    const float wk = expf(sc[k] - smax) / z;
-    const int64_t base = (row * a.topk + k) * D + cg * VEC;
-    if (DT == kF32) {
-      const f32x4 x = *(const f32x4*)((const float*)a.partial + base);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += wk * x[v];
+  for (int k = 0; k < KM; ++k) {
+    const float wk = s[k] * iz;
+    if (DT == kF32) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += wk * __uint_as_float(x[k][v]);
     } else {
-      const u32x4 x = *(const u32x4*)((const uint16_t*)a.partial + base);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        acc[2 * v] += wk * bf16_bits_to_f32(x[v] & 0xffffu);
-        acc[2 * v + 1] += wk * bf16_bits_to_f32(x[v] >> 16);
+        acc[2 * v] += wk * bf16_bits_to_f32(x[k][v] & 0xffffu);
+        acc[2 * v + 1] += wk * bf16_bits_to_f32(x[k][v] >> 16);
       }
     }
   }
@@ -397,9 +787,14 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(PrefillArgs a) {
         u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
   }
-  if (a.sel_w && cg == 0) {
-    for (int k = 0; k < a.topk; ++k)
-      a.sel_w[row * a.topk + k] = k < m ? expf(sc[k] - smax) / z : 0.f;
+  if (a.sel_w && cg < a.topk) {
+    for (int k = cg; k < a.topk; k += TPR) {
+      float wk = 0.f;
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+        if (j == k) wk = s[j] * iz;
+      a.sel_w[row * a.topk + k] = wk;
+    }
   }
 }
 
@@ -415,8 +810,21 @@ hipError_t launch_select_dt(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int KM>
+hipError_t launch_select_mfma(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t nqt = (a.L + 127) / 128;
+  const int64_t blocks = (int64_t)a.B * a.Hkv * nqt;
+  select_mfma_kernel<D, KM><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, nqt);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_select_d(const PrefillArgs& a, hipStream_t stream) {
+  if (a.dtype == kBF16) {
+    if (a.topk <= 8) return launch_select_mfma<D, 8>(a, stream);
+    if (a.topk <= 16) return launch_select_mfma<D, 16>(a, stream);
+    return launch_select_mfma<D, 32>(a, stream);
+  }
   if (a.topk <= 8) return launch_select_dt<D, 8>(a, stream);
   if (a.topk <= 16) return launch_select_dt<D, 16>(a, stream);
   return launch_select_dt<D, 32>(a, stream);
@@ -427,23 +835,24 @@ hipError_t launch_select_d(const PrefillArgs& a, hipStream_t stream) {
 int prefill_entries_per_tile(int dtype, int G) { return dtype == kF32 ? 64 / G : 128 / G; }
 
 hipError_t prefill_select(const PrefillArgs& a, hipStream_t stream) {
-  hipError_t e = launch_fill_i32(a.counts, (int64_t)a.B * a.Hkv * a.n, 0, stream);
-  if (e != hipSuccess) return e;
   if (a.L == 0) return hipSuccess;
   return a.d == 64 ? launch_select_d<64>(a, stream) : launch_select_d<128>(a, stream);
 }
 
 hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
-  hipError_t e = launch_fill_i32(a.cursor, (int64_t)a.B * a.Hkv * a.n, 0, stream);
+  const int64_t BG = (int64_t)a.B * a.Hkv;
+  hipError_t e = launch_fill_i32(a.counts, BG * a.n, 0, stream);
   if (e != hipSuccess) return e;
-  scan_kernel<<<dim3((unsigned)(a.B * a.Hkv)), dim3(1024), 0, stream>>>(a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t total = (int64_t)a.B * a.Hkv * a.L * a.topk;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
-  if (blocks > 0) scatter_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a);
+  if ((e = launch_fill_i32(a.cursor, BG * a.n, 0, stream)) != hipSuccess) return e;
+  const int64_t bpb = (a.L + kInvertTokens - 1) / kInvertTokens;
+  const int use_lds = a.n <= kInvertLdsBins;
+  const size_t lds1 = use_lds ? (size_t)a.n * sizeof(int32_t) : 0;
+  count_kernel<<<dim3((unsigned)(BG * bpb)), dim3(256), lds1, stream>>>(a, bpb, use_lds);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  scan_kernel<<<dim3((unsigned)BG), dim3(1024), 0, stream>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  scatter_kernel<<<dim3((unsigned)(BG * bpb)), dim3(256), 2 * lds1, stream>>>(a, bpb, use_lds);
   return hipGetLastError();
 }
 
@@ -459,6 +868,15 @@ hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream) {
     else
       attend_f32_kernel<128><<<dim3((unsigned)blocks), dim3(64), 0, stream>>>(a, scale,
                                                                               score_scale);
+  } else if (a.S <= kKeyBlock) {
+    const float sl2 = scale * 1.4426950408889634f;
+    const int64_t cblocks = (int64_t)a.B * a.Hkv * a.n;
+    if (a.d == 64)
+      attend_chunk_bf16_kernel<64><<<dim3((unsigned)cblocks), dim3(kThreads), 0, stream>>>(
+          a, sl2, score_scale);
+    else
+      attend_chunk_bf16_kernel<128><<<dim3((unsigned)cblocks), dim3(kThreads), 0, stream>>>(
+          a, sl2, score_scale);
   } else {
     const float sl2 = scale * 1.4426950408889634f;
     if (a.d == 64)
@@ -471,24 +889,28 @@ hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int DT>
+hipError_t launch_fuse_dt(const PrefillArgs& a, int64_t blocks, hipStream_t stream) {
+  if (a.topk <= 8)
+    fuse_kernel<D, DT, 8><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
+  else if (a.topk <= 16)
+    fuse_kernel<D, DT, 16><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
+  else
+    fuse_kernel<D, DT, 32><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t prefill_fuse(const PrefillArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.L;
   if (rows == 0) return hipSuccess;
   const int VEC = a.dtype == kF32 ? 4 : 8;
   const int rpb = kThreads / (a.d / VEC);
   const int64_t blocks = (rows + rpb - 1) / rpb;
-  if (a.dtype == kF32) {
-    if (a.d == 64)
-      fuse_kernel<64, kF32><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
-    else
-      fuse_kernel<128, kF32><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
-  } else {
-    if (a.d == 64)
-      fuse_kernel<64, kBF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
-    else
-      fuse_kernel<128, kBF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
-  }
-  return hipGetLastError();
+  if (a.dtype == kF32)
+    return a.d == 64 ? launch_fuse_dt<64, kF32>(a, blocks, stream)
+                     : launch_fuse_dt<128, kF32>(a, blocks, stream);
+  return a.d == 64 ? launch_fuse_dt<64, kBF16>(a, blocks, stream)
+                   : launch_fuse_dt<128, kBF16>(a, blocks, stream);
 }
 
 }  // namespace hsa
