@@ -236,6 +236,9 @@ def main():
                     help="comma list of extra workloads: decode, decode16m, dhsa, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="after the workloads, copy GIB GiB device-to-device twice (a plain "
+                         "copy kernel of known size to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -265,6 +268,15 @@ def main():
             raise SystemExit(f"unknown extra workload {e}")
     if also:
         line["also"] = also
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * (1 << 30))
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)
     print(json.dumps(line), flush=True)

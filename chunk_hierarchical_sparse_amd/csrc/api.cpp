@@ -91,6 +91,7 @@ hsa_status_t check_prefill(int B, int64_t L, int Hq, int Hkv, int d, int S, int 
   if ((int64_t)B * Hkv * L * topk >= (int64_t)1 << 31 ||
       (int64_t)B * Hq * L * topk >= (int64_t)1 << 31)
     return fail(HSA_ERR_UNSUPPORTED, "B*H*L*topk must be < 2^31");
+  if (L >= ((int64_t)1 << 26)) return fail(HSA_ERR_UNSUPPORTED, "L must be < 2^26");
   return HSA_OK;
 }
 
@@ -266,6 +267,9 @@ hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const floa
   a.L = L;
   a.n = n;
   a.entries_per_tile = hsa::prefill_entries_per_tile(a.dtype, G);
+  a.log2G = -1;
+  for (int k = 0; k < 6; ++k)
+    if ((1 << k) == G) a.log2G = k;
   a.tiles_ub = prefill_entries(L, S, topk) / a.entries_per_tile + n + 1;
   if ((int64_t)B * Hkv * a.tiles_ub >= ((int64_t)1 << 31))
     return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");

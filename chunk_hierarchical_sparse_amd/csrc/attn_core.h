@@ -188,6 +188,145 @@ __device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>
   }
 }
 
+// ---------------------------------------------------------------------
+// Variable-length key blocks of up to 128 keys (DHSA: one chunk per block).
+
+constexpr int kWideBlock = 128;
+
+template <int D>
+struct KVSmemWide {
+  uint16_t k[kWideBlock * (D + 8)];
+  uint16_t v[(kWideBlock / 4) * D * 4];
+};
+
+// Stage rows [0, nk) (nk <= 128) of a key/value block; rows up to the next
+// multiple of 32 are zero-filled, rows beyond that are never read.
+template <int D>
+__device__ __forceinline__ void load_kv_wide(KVSmemWide<D>& sm, const uint16_t* __restrict__ Kg,
+                                             const uint16_t* __restrict__ Vg, int nk) {
+  const int tid = threadIdx.x;
+  const int rows = (nk + 31) & ~31;
+  constexpr int KPR = D / 8;
+  for (int e = tid; e < rows * KPR; e += 256) {
+    const int row = e / KPR, c8 = e % KPR;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row < nk) x = *(const u32x4*)(Kg + (int64_t)row * D + c8 * 8);
+    *(u32x4*)(&sm.k[row * (D + 8) + c8 * 8]) = x;
+  }
+  constexpr int VPR = D / 4;
+  for (int e = tid; e < (rows / 4) * VPR; e += 256) {
+    const int grp = e / VPR, cq = e % VPR;
+    u32x2 r[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int key = grp * 4 + kk;
+      r[kk] = key < nk ? *(const u32x2*)(Vg + (int64_t)key * D + cq * 4) : u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int w = x >> 1;
+      uint32_t lo, hi;
+      if ((x & 1) == 0) {
+        lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
+        hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
+      } else {
+        lo = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
+        hi = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
+      }
+      *(u32x2*)(&sm.v[(grp * D + cq * 4 + x) * 4]) = u32x2{lo, hi};
+    }
+  }
+}
+
+// One staged block of nkeys (<= 128, block-uniform) keys: this lane's query
+// attends keys with in-block index < nvalid (<= nkeys; may differ per lane).
+// One online-softmax update for the whole block; the accumulator is
+// rescaled only when some lane's running maximum grew.
+template <int D>
+__device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide<D>& sm,
+                                               int nkeys, int nvalid, float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int i32 = lane & 31;
+  const int nsub = (nkeys + 31) >> 5;  // 1..4
+  f32x16 sc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t >= nsub) break;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 a0 = *(const bf16x8*)(&sm.k[(32 * t + i32) * (D + 8) + 16 * s + 8 * h]);
+      sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, st.qf[s], sc[t], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // keys at or past nvalid (and padding past nkeys) take no weight
+  const bool need_mask = __ballot(nvalid < 32 * nsub) != 0;
+  if (need_mask) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= nvalid) sc[t][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t >= nsub) break;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * scale_log2;
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  float ps = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t >= nsub) break;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[t][r] = fast_exp2(__builtin_fmaf(sc[t][r], scale_log2, -m_use));
+      ps += sc[t][r];
+    }
+  }
+  ps += __shfl_xor(ps, 32, kWave);
+  if (__ballot(m_new > st.m) != 0) {
+    const float alpha = fast_exp2(st.m - m_use);
+    st.l *= alpha;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[b][r] *= alpha;
+  }
+  st.l += ps;
+  st.m = m_new;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t >= nsub) break;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 pb = cvt_bf16x8(sc[t], 8 * s2);
+      const int g0 = 8 * t + 4 * s2 + h, g1 = g0 + 2;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) {
+        const int dd = 32 * b + i32;
+        const u32x2 v0 = *(const u32x2*)(&sm.v[(g0 * D + dd) * 4]);
+        const u32x2 v1 = *(const u32x2*)(&sm.v[(g1 * D + dd) * 4]);
+        const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
+        st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
+                                                          st.o[b], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // Dot product of this lane's query half with an fp32 vector (dims
 // 16s + 8h + 0..7); the caller adds the partner lane (l ^ 32).
 template <int D>

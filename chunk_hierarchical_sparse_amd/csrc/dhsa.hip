@@ -186,12 +186,15 @@ __device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int
 
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float scale_log2) {
-  __shared__ KVSmem<D> sm;
+  __shared__ KVSmemWide<D> sm;
   __shared__ int pmax;
-  const int64_t per_bh = (int64_t)a.nc * a.tiles_per_chunk;
-  const int64_t bh = blockIdx.x / per_bh;
-  const int l = (int)((blockIdx.x % per_bh) / a.tiles_per_chunk);
-  const int tile = (int)(blockIdx.x % a.tiles_per_chunk);
+  // late query chunks attend the most keys: dispatch them first, with all
+  // (b, h) of one chunk next to each other
+  const int64_t BH = (int64_t)a.B * a.H;
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t rest = blockIdx.x / BH;
+  const int l = a.nc - 1 - (int)(rest / a.tiles_per_chunk);
+  const int tile = (int)(rest % a.tiles_per_chunk);
   const int bl = a.offs[l], bl1 = a.offs[l + 1];
   const int row0 = bl + tile * kRowsPerTile;
   if (row0 >= bl1) return;
@@ -218,13 +221,13 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
     const int bk = a.offs[k], lk = a.offs[k + 1] - bk;
     const int len_eff = k == l ? (int)(i - bl + 1) : lk;
     const int hi = !valid ? 0 : (p < cut.pw ? len_eff : (p == cut.pw ? cut.rem : 0));
-    for (int kb = 0; kb < lk; kb += kKeyBlock) {
-      const int nk = min(kKeyBlock, lk - kb);
+    for (int kb = 0; kb < lk; kb += kWideBlock) {
+      const int nk = min(kWideBlock, lk - kb);
       __syncthreads();
-      load_kv_block<D>(sm, Kb + (int64_t)(bk + kb) * D, Vb + (int64_t)(bk + kb) * D, nk);
+      load_kv_wide<D>(sm, Kb + (int64_t)(bk + kb) * D, Vb + (int64_t)(bk + kb) * D, nk);
       __syncthreads();
       const int nv = max(0, min(hi - kb, nk));
-      if (wave_any && __ballot(nv > 0) != 0) wave_attn_block<D>(st, sm, nk, nv, scale_log2);
+      if (wave_any && __ballot(nv > 0) != 0) wave_attn_wide<D>(st, sm, nk, nv, scale_log2);
     }
   }
   if (!valid) return;

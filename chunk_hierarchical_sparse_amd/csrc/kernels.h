@@ -44,7 +44,10 @@ struct PrefillArgs {
   int64_t L, n;
   int entries_per_tile;  // selection entries (token, slot) per attention tile
   int64_t tiles_ub;      // upper bound of tiles per (b, group)
+  int log2G;             // log2(Hq/Hkv) when it is a power of two, else -1
 };
+// A selection entry of the per-chunk lists: token << kSlotBits | slot.
+constexpr int kSlotBits = 5;  // topk <= 32
 hipError_t prefill_select(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream);

@@ -183,8 +183,10 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
   constexpr int TILE = 32;
   constexpr int RS = D + 8;  // padded LDS row (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t lt[3][TILE * RS];
-  const int64_t bg = blockIdx.x / nqt;
-  const int64_t qt = blockIdx.x % nqt;
+  // late query tiles see the most chunks: dispatch them first
+  const int64_t BG = (int64_t)a.B * a.Hkv;
+  const int64_t bg = blockIdx.x % BG;
+  const int64_t qt = nqt - 1 - blockIdx.x / BG;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int G = a.Hq / a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -384,7 +386,7 @@ __global__ void __launch_bounds__(256) count_kernel(PrefillArgs a, int64_t block
     if (hist[c] != 0) atomicAdd(&cnt[c], hist[c]);
 }
 
-// Append (token*topk + slot) entries to the selected chunks' lists.  With
+// Append (token << kSlotBits | slot) entries to the selected chunks' lists.  With
 // LDS bins: count locally, reserve one range per touched chunk with a global
 // atomic, then place entries by LDS atomics inside the range.  The order
 // inside a list does not affect results: every row is computed
@@ -402,7 +404,9 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
   if (!use_lds) {
     for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
       const int32_t c = idx[i];
-      if (c >= 0) list[offs[c] + atomicAdd(&cursor[c], 1)] = (int32_t)i;
+      if (c >= 0)
+        list[offs[c] + atomicAdd(&cursor[c], 1)] =
+            (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
     }
     return;
   }
@@ -420,7 +424,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
   __syncthreads();
   for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
     const int32_t c = idx[i];
-    if (c >= 0) list[atomicAdd(&pos[c], 1)] = (int32_t)i;
+    if (c >= 0) list[atomicAdd(&pos[c], 1)] = (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
   }
 }
 
@@ -466,8 +470,8 @@ __global__ void __launch_bounds__(kThreads) attend_bf16_kernel(PrefillArgs a, fl
   const bool valid = r < a.entries_per_tile * G && e < e1;
   int32_t entry = 0;
   if (valid) entry = a.list[bg * a.L * a.topk + e];
-  const int64_t t = entry / a.topk;
-  const int slot = entry % a.topk;
+  const int64_t t = entry >> kSlotBits;
+  const int slot = entry & ((1 << kSlotBits) - 1);
   const int h = g * G + hh;
   const uint16_t* Q = (const uint16_t*)a.Q;
   WaveAttn<D> st;
@@ -502,18 +506,21 @@ __global__ void __launch_bounds__(kThreads) attend_bf16_kernel(PrefillArgs a, fl
     }
 }
 
-// bf16, S <= 64: one block per (b, group, chunk).  The chunk's K/V and
-// landmark are staged in LDS once; each wave then walks 32-row tiles of the
-// chunk's (token, head) rows.  A row sees exactly this chunk, so its softmax
-// is over at most 64 keys held in registers: no online rescaling.  The next
-// tile's list entry and Q row are fetched while the current tile computes.
-// Blocks are ordered chunk-major over all (b, group) so the most-selected
-// early chunks start first.
+// bf16, S <= 64: one block per (b, group, chunk).  The chunk's K/V are
+// staged in LDS once; each wave then walks 32-row tiles of the chunk's
+// (token, head) rows.  A row sees exactly this chunk, so its softmax is over
+// at most 64 keys held in registers: no online rescaling.  The per-head
+// retrieval score s_h = q . lmk_c runs on MFMA too: the fp32 landmark is
+// split into three bf16 rows (hi + lo + lo2 == the fp32 value) that act as
+// extra "keys", so q (exact in bf16) meets an exact landmark and s_h keeps
+// fp32 accuracy.  Q rows are double-buffered: a tile's rows load during the
+// whole previous tile.  Blocks are ordered chunk-major over all (b, group) so
+// the most-selected early chunks start first.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2)
     attend_chunk_bf16_kernel(PrefillArgs a, float scale_log2, float score_scale) {
   __shared__ KVSmem<D> sm;
-  __shared__ __attribute__((aligned(16))) float lm[D];
+  __shared__ __attribute__((aligned(16))) uint16_t lsplit[3][D];
   const int64_t BG = (int64_t)a.B * a.Hkv;
   const int c = (int)(blockIdx.x / BG);
   const int64_t bg = blockIdx.x % BG;
@@ -527,7 +534,16 @@ __global__ void __launch_bounds__(kThreads, 2)
   const int ntiles = (rows + 31) / 32;
   const int64_t kv0 = (bg * a.L + (int64_t)c * a.S) * D;
   load_kv_block<D>(sm, (const uint16_t*)a.K + kv0, (const uint16_t*)a.V + kv0, a.S);
-  for (int x = threadIdx.x; x < D; x += kThreads) lm[x] = a.lmk[(bg * a.n + c) * D + x];
+  for (int x = threadIdx.x; x < D; x += kThreads) {
+    const float v = a.lmk[(bg * a.n + c) * D + x];
+    const __bf16 h = static_cast<__bf16>(v);
+    const float r1 = v - static_cast<float>(h);
+    const __bf16 l = static_cast<__bf16>(r1);
+    const __bf16 m = static_cast<__bf16>(r1 - static_cast<float>(l));
+    lsplit[0][x] = __builtin_bit_cast(uint16_t, h);
+    lsplit[1][x] = __builtin_bit_cast(uint16_t, l);
+    lsplit[2][x] = __builtin_bit_cast(uint16_t, m);
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -536,17 +552,31 @@ __global__ void __launch_bounds__(kThreads, 2)
   const uint16_t* Q = (const uint16_t*)a.Q;
   const int64_t qplane = (int64_t)a.L * D;  // stride between heads
   const int64_t qbase = (int64_t)b * a.Hq * qplane + (int64_t)g * G * qplane;
+  const int lg = a.log2G;
+  const int slot_mask = (1 << kSlotBits) - 1;
 
-  // row r of the chunk -> (entry, head); entry = token * topk + slot
+  // row r of the chunk -> (entry index r / G, head r % G)
+  auto split_row = [&](int r, int& ei, int& hh) {
+    if (lg >= 0) {
+      ei = r >> lg;
+      hh = r & ((1 << lg) - 1);
+    } else {
+      ei = r / G;
+      hh = r - ei * G;
+    }
+  };
   auto entry_of = [&](int tile) -> int32_t {
     const int r = tile * 32 + i32;
-    return r < rows ? list[r / G] : -1;
+    int ei, hh;
+    split_row(r, ei, hh);
+    return r < rows ? list[ei] : -1;
   };
   auto load_q = [&](int tile, int32_t entry, u32x4 (&q)[D / 16]) {
-    const int r = tile * 32 + i32;
     if (entry >= 0) {
-      const int64_t t = entry / a.topk;
-      const uint16_t* qrow = Q + qbase + (int64_t)(r % G) * qplane + t * D + 8 * hf;
+      int ei, hh;
+      split_row(tile * 32 + i32, ei, hh);
+      const int64_t t = entry >> kSlotBits;
+      const uint16_t* qrow = Q + qbase + (int64_t)hh * qplane + t * D + 8 * hf;
 #pragma unroll
       for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = *(const u32x4*)(qrow + 16 * s2);
     } else {
@@ -555,19 +585,16 @@ __global__ void __launch_bounds__(kThreads, 2)
     }
   };
 
-  int tile = w;
-  int32_t ent = tile < ntiles ? entry_of(tile) : -1;
-  int32_t ent_next = tile + 4 < ntiles ? entry_of(tile + 4) : -1;
-  u32x4 q[D / 16];
-  load_q(tile, ent, q);
   const bool two = a.S > 32;
-  for (; tile < ntiles; tile += 4) {
-    // scores S^T = K Q^T for up to 64 keys
-    f32x16 s0, s1;
+  const bool full = a.S == kKeyBlock;  // no key masking needed
+  auto compute_tile = [&](int tile, int32_t ent_cur, const u32x4 (&q)[D / 16]) {
+    // S^T = K Q^T (keys 0..63) and L^T = LMK3 Q^T (rows 0..2: landmark parts)
+    f32x16 s0, s1, sl;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       s0[r] = 0.f;
       s1[r] = 0.f;
+      sl[r] = 0.f;
     }
 #pragma unroll
     for (int s2 = 0; s2 < D / 16; ++s2) {
@@ -578,61 +605,50 @@ __global__ void __launch_bounds__(kThreads, 2)
         const bf16x8 a1 = *(const bf16x8*)(&sm.k[(32 + i32) * (D + 8) + 16 * s2 + 8 * hf]);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb, s1, 0, 0, 0);
       }
+      u32x4 la = {0u, 0u, 0u, 0u};
+      if (i32 < 3) la = *(const u32x4*)(&lsplit[i32][16 * s2 + 8 * hf]);
+      sl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, la), qb, sl, 0,
+                                                   0, 0);
     }
-    // per-head retrieval score s_h(t, c) = q . lmk_c / sqrt(d)
-    float sh = 0.f;
+    // rows 0..2 of L^T sit in registers 0..2 of the lanes of half 0
+    const float sh = (sl[2] + sl[1]) + sl[0];
+    __builtin_amdgcn_sched_barrier(0);
+    // softmax over the chunk's keys: p = exp2((s - max) * scale), normalised
+    float mx = -INFINITY;
+    if (!full) {
 #pragma unroll
-    for (int s2 = 0; s2 < D / 16; ++s2) {
-      const bf16x8 qb = __builtin_bit_cast(bf16x8, q[s2]);
-      const f32x4 l0 = *(const f32x4*)(&lm[16 * s2 + 8 * hf]);
-      const f32x4 l1 = *(const f32x4*)(&lm[16 * s2 + 8 * hf + 4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sh += (float)qb[e] * l0[e];
-        sh += (float)qb[e + 4] * l1[e];
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+        s0[r] = key < a.S ? s0[r] : -INFINITY;
+        s1[r] = key + 32 < a.S ? s1[r] : -INFINITY;
       }
     }
-    sh += __shfl_xor(sh, 32, kWave);
-    __builtin_amdgcn_sched_barrier(0);
-    const int32_t ent_cur = ent;
-    const int r_cur = tile * 32 + i32;
-    // next tile: its Q rows stream in while this one finishes
-    ent = ent_next;
-    if (tile + 4 < ntiles) load_q(tile + 4, ent, q);
-    ent_next = tile + 8 < ntiles ? entry_of(tile + 8) : -1;
-    __builtin_amdgcn_sched_barrier(0);
-
-    // softmax over the chunk's keys (log2 domain)
-    float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
-      s0[r] = key < a.S ? s0[r] * scale_log2 : -INFINITY;
-      s1[r] = key + 32 < a.S ? s1[r] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    }
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mxs = mx * scale_log2;
     float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = fast_exp2(s0[r] - mx);
-      s1[r] = fast_exp2(s1[r] - mx);
+      s0[r] = fast_exp2(__builtin_fmaf(s0[r], scale_log2, -mxs));
+      s1[r] = fast_exp2(__builtin_fmaf(s1[r], scale_log2, -mxs));
       ps += s0[r] + s1[r];
     }
     ps += __shfl_xor(ps, 32, kWave);
-    // P^T as bf16 MFMA operands; the fp32 scores die here
+    const float inv = 1.f / ps;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] *= inv;
+      s1[r] *= inv;
+    }
     bf16x8 pb4[4];
     pb4[0] = cvt_bf16x8(s0, 0);
     pb4[1] = cvt_bf16x8(s0, 8);
     pb4[2] = cvt_bf16x8(s1, 0);
     pb4[3] = cvt_bf16x8(s1, 8);
     __builtin_amdgcn_sched_barrier(0);
-    // O^T = V^T P^T
+    // O^T = V^T P^T (already normalised)
     f32x16 o[D / 32];
-#pragma unroll
-    for (int bb = 0; bb < D / 32; ++bb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[bb][r] = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       if (kt == 1 && !two) break;
@@ -646,29 +662,69 @@ __global__ void __launch_bounds__(kThreads, 2)
           const u32x2 v0 = *(const u32x2*)(&sm.v[(g0 * D + dd) * 4]);
           const u32x2 v1 = *(const u32x2*)(&sm.v[(g1 * D + dd) * 4]);
           const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
-          o[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
-                                                          o[bb], 0, 0, 0);
+          if (kt == 0 && s2 == 0) {
+            const f32x16 zero = {};
+            o[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
+                                                            zero, 0, 0, 0);
+          } else {
+            o[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
+                                                            o[bb], 0, 0, 0);
+          }
         }
       }
     }
+    // lane half hf holds columns 32bb + 8q4 + 4hf + 0..3; swapping half of
+    // the groups with the partner lane leaves each lane 16 contiguous bytes
+    // (columns 32bb + 8(2pr + hf) + 0..7) to store
+    u32x4 outv[D / 32][2];
+#pragma unroll
+    for (int bb = 0; bb < D / 32; ++bb)
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int q_even = 2 * pr, q_odd = 2 * pr + 1;
+        const uint32_t e0 = pack_bf16x2(o[bb][4 * q_even], o[bb][4 * q_even + 1]);
+        const uint32_t e1 = pack_bf16x2(o[bb][4 * q_even + 2], o[bb][4 * q_even + 3]);
+        const uint32_t d0 = pack_bf16x2(o[bb][4 * q_odd], o[bb][4 * q_odd + 1]);
+        const uint32_t d1 = pack_bf16x2(o[bb][4 * q_odd + 2], o[bb][4 * q_odd + 3]);
+        // half 0 keeps the even group and sends the odd one; half 1 the reverse
+        const uint32_t got0 = __shfl_xor(hf ? e0 : d0, 32, kWave);
+        const uint32_t got1 = __shfl_xor(hf ? e1 : d1, 32, kWave);
+        outv[bb][pr] = hf ? u32x4{got0, got1, d0, d1} : u32x4{e0, e1, got0, got1};
+      }
     if (ent_cur >= 0) {
-      const int64_t t = ent_cur / a.topk;
-      const int slot = ent_cur % a.topk;
-      const int h = g * G + r_cur % G;
+      int ei, hh;
+      split_row(tile * 32 + i32, ei, hh);
+      const int64_t t = ent_cur >> kSlotBits;
+      const int slot = ent_cur & slot_mask;
+      const int h = g * G + hh;
       const int64_t row = (((int64_t)b * a.Hq + h) * a.L + t) * a.topk + slot;
       if (hf == 0) a.part_score[row] = sh * score_scale;
-      const float inv = 1.f / ps;
       uint16_t* po = (uint16_t*)a.partial + row * D;
 #pragma unroll
       for (int bb = 0; bb < D / 32; ++bb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int dd = 32 * bb + 8 * q4 + 4 * hf;
-          const u32x2 v = {pack_bf16x2(o[bb][4 * q4] * inv, o[bb][4 * q4 + 1] * inv),
-                           pack_bf16x2(o[bb][4 * q4 + 2] * inv, o[bb][4 * q4 + 3] * inv)};
-          *(u32x2*)(po + dd) = v;
-        }
+        for (int pr = 0; pr < 2; ++pr)
+          *(u32x4*)(po + 32 * bb + 8 * (2 * pr + hf)) = outv[bb][pr];
     }
+  };
+
+  // Double-buffered Q: the next tile's rows load during the whole current
+  // tile.  List entries run one tile further ahead.
+  u32x4 qa[D / 16], qb[D / 16];
+  int tile = w;
+  int32_t ea = tile < ntiles ? entry_of(tile) : -1;
+  int32_t eb = tile + 4 < ntiles ? entry_of(tile + 4) : -1;
+  load_q(tile, ea, qa);
+  for (; tile < ntiles; tile += 8) {
+    int32_t ec = tile + 8 < ntiles ? entry_of(tile + 8) : -1;
+    if (tile + 4 < ntiles) load_q(tile + 4, eb, qb);
+    compute_tile(tile, ea, qa);
+    if (tile + 4 >= ntiles) break;
+    int32_t ed = tile + 12 < ntiles ? entry_of(tile + 12) : -1;
+    if (tile + 8 < ntiles) load_q(tile + 8, ec, qa);
+    compute_tile(tile + 4, eb, qb);
+    ea = ec;
+    eb = ed;
   }
 }
 
@@ -685,8 +741,8 @@ __global__ void __launch_bounds__(64) attend_f32_kernel(PrefillArgs a, float sca
   const int e = e0 + r / G;
   if (r >= a.entries_per_tile * G || e >= e1) return;
   const int32_t entry = a.list[bg * a.L * a.topk + e];
-  const int64_t t = entry / a.topk;
-  const int slot = entry % a.topk;
+  const int64_t t = entry >> kSlotBits;
+  const int slot = entry & ((1 << kSlotBits) - 1);
   const int h = g * G + r % G;
   const float* qrow = (const float*)a.Q + (((int64_t)b * a.Hq + h) * a.L + t) * D;
   float q[D], o[D];

@@ -98,7 +98,8 @@ hsa_status_t hsa_build_landmarks(const void* K, float* lmk, int B, int Hkv, int6
  *           0 padded.
  *   workspace of at least hsa_prefill_workspace_size(...) bytes, 256-byte
  *   aligned; its contents on entry do not matter.
- * Limits: 1 <= S <= 1024, 1 <= topk <= 32, B*Hkv*L*topk < 2^31, Hq/Hkv <= 32.
+ * Limits: 1 <= S <= 1024, 1 <= topk <= 32, B*Hq*L*topk < 2^31, L < 2^26,
+ * Hq/Hkv <= 32.
  */
 size_t hsa_prefill_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S, int topk,
                                   hsa_dtype_t dtype);
