@@ -30,7 +30,10 @@ struct StageMarks {
     if (!g_prof.on) return;
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return;
-    hipEventRecord(e, st);
+    if (hipEventRecord(e, st) != hipSuccess) {
+      (void)hipEventDestroy(e);
+      return;
+    }
     ev.push_back(e);
   }
   ~StageMarks() {
@@ -98,7 +101,9 @@ hsa_status_t check_prefill(int B, int64_t L, int Hq, int Hkv, int d, int S, int 
 struct PrefillLayout {
   float* lmk;
   int32_t* idx;
-  int32_t *counts, *cursor, *offs, *tile_off, *list;
+  int32_t *counts, *cursor, *offs, *tile_off, *tile_chunk, *list, *entry_pos;
+  int entries_per_tile;
+  int64_t tiles_ub;
   void* partial;
   float* part_score;
   size_t bytes;
@@ -116,7 +121,11 @@ PrefillLayout prefill_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d,
   p.cursor = cv.take<int32_t>((size_t)(BG * n));
   p.offs = cv.take<int32_t>((size_t)(BG * (n + 1)));
   p.tile_off = cv.take<int32_t>((size_t)(BG * (n + 1)));
+  p.entries_per_tile = hsa::prefill_entries_per_tile(dt_code(dt), Hq / Hkv, S);
+  p.tiles_ub = prefill_entries(L, S, topk) / p.entries_per_tile + n + 1;
+  p.tile_chunk = cv.take<int32_t>((size_t)(BG * p.tiles_ub));
   p.list = cv.take<int32_t>((size_t)(BG * L * topk));
+  p.entry_pos = cv.take<int32_t>((size_t)(BG * L * topk));
   p.partial = cv.take<char>((size_t)((int64_t)B * Hq * L * topk * d * elem_bytes(dt)));
   p.part_score = cv.take<float>((size_t)((int64_t)B * Hq * L * topk));
   p.bytes = cv.off + kAlign;
@@ -254,7 +263,9 @@ hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const floa
   a.cursor = lay.cursor;
   a.offs = lay.offs;
   a.tile_off = lay.tile_off;
+  a.tile_chunk = lay.tile_chunk;
   a.list = lay.list;
+  a.entry_pos = lay.entry_pos;
   a.partial = lay.partial;
   a.part_score = lay.part_score;
   a.B = B;
@@ -266,11 +277,11 @@ hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const floa
   a.dtype = dt_code(dtype);
   a.L = L;
   a.n = n;
-  a.entries_per_tile = hsa::prefill_entries_per_tile(a.dtype, G);
+  a.entries_per_tile = lay.entries_per_tile;
   a.log2G = -1;
   for (int k = 0; k < 6; ++k)
     if ((1 << k) == G) a.log2G = k;
-  a.tiles_ub = prefill_entries(L, S, topk) / a.entries_per_tile + n + 1;
+  a.tiles_ub = lay.tiles_ub;
   if ((int64_t)B * Hkv * a.tiles_ub >= ((int64_t)1 << 31))
     return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
   hipError_t e;
@@ -439,7 +450,7 @@ int hsa_profile_read(double* stage_ms, int max_stages, int* n_stages) {
   int stages = 0;
   for (auto& ev : g_prof.calls) {
     if (ev.empty()) continue;
-    hipEventSynchronize(ev.back());
+    if (hipEventSynchronize(ev.back()) != hipSuccess) continue;
     const int ns = (int)ev.size() - 1;
     if (ns > stages) stages = ns;
     for (int s = 0; s < ns && s < max_stages; ++s) {
@@ -449,7 +460,7 @@ int hsa_profile_read(double* stage_ms, int max_stages, int* n_stages) {
   }
   const int calls = (int)g_prof.calls.size();
   for (auto& ev : g_prof.calls)
-    for (hipEvent_t e : ev) hipEventDestroy(e);
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
   g_prof.calls.clear();
   if (n_stages) *n_stages = stages;
   return calls;

@@ -37,13 +37,15 @@ struct PrefillArgs {
   int32_t* cursor;    // [B*Hkv, n]
   int32_t* offs;      // [B*Hkv, n+1]
   int32_t* tile_off;  // [B*Hkv, n+1]
+  int32_t* tile_chunk;  // [B*Hkv, tiles_ub]: chunk of each attention work unit
   int32_t* list;      // [B*Hkv, L*topk]
-  void* partial;      // [B,Hq,L,topk,d] (bf16 for bf16 inputs, fp32 for fp32)
-  float* part_score;  // [B,Hq,L,topk]
+  int32_t* entry_pos; // [B*Hkv, L*topk]: list position of selection (token, slot)
+  void* partial;      // [B*Hkv, L*topk, G, d] in list order (bf16 or fp32 like the inputs)
+  float* part_score;  // [B*Hkv, L*topk, G] in list order
   int B, Hq, Hkv, d, S, topk, dtype;
   int64_t L, n;
-  int entries_per_tile;  // selection entries (token, slot) per attention tile
-  int64_t tiles_ub;      // upper bound of tiles per (b, group)
+  int entries_per_tile;  // selection entries (token, slot) per attention work unit
+  int64_t tiles_ub;      // upper bound of work units per (b, group)
   int log2G;             // log2(Hq/Hkv) when it is a power of two, else -1
 };
 // A selection entry of the per-chunk lists: token << kSlotBits | slot.
@@ -52,7 +54,7 @@ hipError_t prefill_select(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_fuse(const PrefillArgs& a, hipStream_t stream);
-int prefill_entries_per_tile(int dtype, int G);
+int prefill_entries_per_tile(int dtype, int G, int S);
 
 // ---- HSA decode (decode.hip) -----------------------------------------------
 struct DecodeArgs {

@@ -25,6 +25,9 @@ namespace hsa {
 namespace {
 
 constexpr int kThreads = 256;
+// (token, head) rows per block of the S <= 64 chunk attention: 32 tiles of
+// 32 rows, 8 per wave, enough to amortise staging the chunk's K/V.
+constexpr int kChunkUnitRows = 1024;
 
 // ---------------------------------------------------------------- select --
 
@@ -305,7 +308,8 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
 // ---------------------------------------------------------------- invert --
 
 // One block per (b, group): exclusive scans of the selection counts
-// (entry offsets) and of the per-chunk tile counts (tile offsets).
+// (entry offsets) and of the per-chunk work-unit counts (unit offsets), and
+// the unit -> chunk map the attention blocks read.
 __global__ void __launch_bounds__(1024) scan_kernel(PrefillArgs a) {
   __shared__ int32_t sa[1024], sb[1024];
   __shared__ int32_t carry_a, carry_b;
@@ -313,6 +317,7 @@ __global__ void __launch_bounds__(1024) scan_kernel(PrefillArgs a) {
   const int32_t* cnt = a.counts + bg * a.n;
   int32_t* offs = a.offs + bg * (a.n + 1);
   int32_t* toff = a.tile_off + bg * (a.n + 1);
+  int32_t* tmap = a.tile_chunk + bg * a.tiles_ub;
   const int E = a.entries_per_tile;
   if (threadIdx.x == 0) {
     carry_a = 0;
@@ -337,8 +342,11 @@ __global__ void __launch_bounds__(1024) scan_kernel(PrefillArgs a) {
       __syncthreads();
     }
     if (c < a.n) {
+      const int32_t nt = (v + E - 1) / E;
+      const int32_t t0 = carry_b + sb[threadIdx.x] - nt;
       offs[c] = carry_a + sa[threadIdx.x] - v;
-      toff[c] = carry_b + sb[threadIdx.x] - (v + E - 1) / E;
+      toff[c] = t0;
+      for (int32_t j = 0; j < nt; ++j) tmap[t0 + j] = (int32_t)c;
     }
     __syncthreads();
     if (threadIdx.x == 1023) {
@@ -386,7 +394,8 @@ __global__ void __launch_bounds__(256) count_kernel(PrefillArgs a, int64_t block
     if (hist[c] != 0) atomicAdd(&cnt[c], hist[c]);
 }
 
-// Append (token << kSlotBits | slot) entries to the selected chunks' lists.  With
+// Append (token << kSlotBits | slot) entries to the selected chunks' lists,
+// and record where each selection landed (entry_pos).  With
 // LDS bins: count locally, reserve one range per touched chunk with a global
 // atomic, then place entries by LDS atomics inside the range.  The order
 // inside a list does not affect results: every row is computed
@@ -401,12 +410,15 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
   const int32_t* offs = a.offs + bg * (a.n + 1);
   int32_t* cursor = a.cursor + bg * a.n;
   int32_t* list = a.list + bg * a.L * a.topk;
+  int32_t* epos = a.entry_pos + bg * a.L * a.topk;
   if (!use_lds) {
     for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
       const int32_t c = idx[i];
-      if (c >= 0)
-        list[offs[c] + atomicAdd(&cursor[c], 1)] =
-            (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
+      if (c >= 0) {
+        const int32_t p = offs[c] + atomicAdd(&cursor[c], 1);
+        list[p] = (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
+        epos[i] = p;
+      }
     }
     return;
   }
@@ -424,29 +436,39 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
   __syncthreads();
   for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
     const int32_t c = idx[i];
-    if (c >= 0) list[atomicAdd(&pos[c], 1)] = (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
+    if (c >= 0) {
+      const int32_t p = atomicAdd(&pos[c], 1);
+      list[p] = (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
+      epos[i] = p;
+    }
   }
 }
 
 // ---------------------------------------------------------------- attend --
 
-// Locate this block's chunk and entry range.  Returns false for blocks past
-// the last tile of their (b, group).
+// Partial outputs and their retrieval scores share one row index, in list
+// order: row (e * G + head of the group) for entry e of the (b, group)'s
+// chunk lists.  A tile's rows are consecutive entries of one list, so the
+// attention writes its partials as one contiguous run; the fusion finds a
+// token's entries through entry_pos.
+__device__ __forceinline__ int64_t partial_row(const PrefillArgs& a, int64_t bg, int64_t e,
+                                               int hh) {
+  const int G = a.Hq / a.Hkv;
+  return (bg * a.L * a.topk + e) * G + hh;
+}
+
+// Locate this block's chunk and entry range.  Blocks interleave the (b,
+// group) pairs (b, group = fastest index) and walk each pair's work units in
+// chunk order, so the early, most-selected chunks start first.  Returns false
+// for blocks past the last unit of their (b, group).
 __device__ __forceinline__ bool locate_tile(const PrefillArgs& a, int64_t& bg, int& c, int& e0,
                                             int& e1) {
-  bg = blockIdx.x / a.tiles_ub;
-  const int64_t tile = blockIdx.x % a.tiles_ub;
+  const int64_t BG = (int64_t)a.B * a.Hkv;
+  bg = blockIdx.x % BG;
+  const int64_t tile = blockIdx.x / BG;
   const int32_t* toff = a.tile_off + bg * (a.n + 1);
   if (tile >= toff[a.n]) return false;
-  int lo = 0, hi = (int)a.n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (toff[mid] <= tile)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  c = lo;
+  c = a.tile_chunk[bg * a.tiles_ub + tile];
   const int32_t* offs = a.offs + bg * (a.n + 1);
   e0 = offs[c] + (int)(tile - toff[c]) * a.entries_per_tile;
   e1 = min(e0 + a.entries_per_tile, offs[c + 1]);
@@ -471,7 +493,6 @@ __global__ void __launch_bounds__(kThreads) attend_bf16_kernel(PrefillArgs a, fl
   int32_t entry = 0;
   if (valid) entry = a.list[bg * a.L * a.topk + e];
   const int64_t t = entry >> kSlotBits;
-  const int slot = entry & ((1 << kSlotBits) - 1);
   const int h = g * G + hh;
   const uint16_t* Q = (const uint16_t*)a.Q;
   WaveAttn<D> st;
@@ -490,7 +511,7 @@ __global__ void __launch_bounds__(kThreads) attend_bf16_kernel(PrefillArgs a, fl
   float s = wave_q_dot_half<D>(st, a.lmk + (bg * a.n + c) * D);
   s += __shfl_xor(s, 32, kWave);
   if (!valid) return;
-  const int64_t row = (((int64_t)b * a.Hq + h) * a.L + t) * a.topk + slot;
+  const int64_t row = partial_row(a, bg, e, hh);
   a.part_score[row] = s * score_scale;
   const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
   uint16_t* po = (uint16_t*)a.partial + row * D;
@@ -506,28 +527,25 @@ __global__ void __launch_bounds__(kThreads) attend_bf16_kernel(PrefillArgs a, fl
     }
 }
 
-// bf16, S <= 64: one block per (b, group, chunk).  The chunk's K/V are
-// staged in LDS once; each wave then walks 32-row tiles of the chunk's
-// (token, head) rows.  A row sees exactly this chunk, so its softmax is over
+// bf16, S <= 64: one block per work unit, a run of at most
+// kChunkUnitRows (token, head) rows of one chunk's list, so hot chunks spread
+// over several blocks.  The chunk's K/V are staged in LDS once per block;
+// each wave then walks 32-row tiles of the unit's rows.  A row sees exactly this chunk, so its softmax is over
 // at most 64 keys held in registers: no online rescaling.  The per-head
 // retrieval score s_h = q . lmk_c runs on MFMA too: the fp32 landmark is
 // split into three bf16 rows (hi + lo + lo2 == the fp32 value) that act as
 // extra "keys", so q (exact in bf16) meets an exact landmark and s_h keeps
 // fp32 accuracy.  Q rows are double-buffered: a tile's rows load during the
-// whole previous tile.  Blocks are ordered chunk-major over all (b, group) so
-// the most-selected early chunks start first.
+// whole previous tile.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2)
     attend_chunk_bf16_kernel(PrefillArgs a, float scale_log2, float score_scale) {
   __shared__ KVSmem<D> sm;
   __shared__ __attribute__((aligned(16))) uint16_t lsplit[3][D];
-  const int64_t BG = (int64_t)a.B * a.Hkv;
-  const int c = (int)(blockIdx.x / BG);
-  const int64_t bg = blockIdx.x % BG;
-  const int32_t* offs = a.offs + bg * (a.n + 1);
-  const int e_begin = offs[c];
-  const int cnt = offs[c + 1] - e_begin;
-  if (cnt == 0) return;
+  int64_t bg;
+  int c, e_begin, e_end;
+  if (!locate_tile(a, bg, c, e_begin, e_end)) return;
+  const int cnt = e_end - e_begin;
   const int G = a.Hq / a.Hkv;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int rows = cnt * G;
@@ -553,7 +571,6 @@ __global__ void __launch_bounds__(kThreads, 2)
   const int64_t qplane = (int64_t)a.L * D;  // stride between heads
   const int64_t qbase = (int64_t)b * a.Hq * qplane + (int64_t)g * G * qplane;
   const int lg = a.log2G;
-  const int slot_mask = (1 << kSlotBits) - 1;
 
   // row r of the chunk -> (entry index r / G, head r % G)
   auto split_row = [&](int r, int& ei, int& hh) {
@@ -692,12 +709,8 @@ __global__ void __launch_bounds__(kThreads, 2)
         outv[bb][pr] = hf ? u32x4{got0, got1, d0, d1} : u32x4{e0, e1, got0, got1};
       }
     if (ent_cur >= 0) {
-      int ei, hh;
-      split_row(tile * 32 + i32, ei, hh);
-      const int64_t t = ent_cur >> kSlotBits;
-      const int slot = ent_cur & slot_mask;
-      const int h = g * G + hh;
-      const int64_t row = (((int64_t)b * a.Hq + h) * a.L + t) * a.topk + slot;
+      // rows of a tile are consecutive: (entry e_begin + r / G, head r % G)
+      const int64_t row = partial_row(a, bg, e_begin, 0) + tile * 32 + i32;
       if (hf == 0) a.part_score[row] = sh * score_scale;
       uint16_t* po = (uint16_t*)a.partial + row * D;
 #pragma unroll
@@ -742,7 +755,6 @@ __global__ void __launch_bounds__(64) attend_f32_kernel(PrefillArgs a, float sca
   if (r >= a.entries_per_tile * G || e >= e1) return;
   const int32_t entry = a.list[bg * a.L * a.topk + e];
   const int64_t t = entry >> kSlotBits;
-  const int slot = entry & ((1 << kSlotBits) - 1);
   const int h = g * G + r % G;
   const float* qrow = (const float*)a.Q + (((int64_t)b * a.Hq + h) * a.L + t) * D;
   float q[D], o[D];
@@ -771,7 +783,7 @@ __global__ void __launch_bounds__(64) attend_f32_kernel(PrefillArgs a, float sca
   float s = 0.f;
 #pragma unroll
   for (int x = 0; x < D; ++x) s += q[x] * lc[x];
-  const int64_t row = (((int64_t)b * a.Hq + h) * a.L + t) * a.topk + slot;
+  const int64_t row = partial_row(a, bg, e, r % G);
   a.part_score[row] = s * score_scale;
   float* po = (float*)a.partial + row * D;
 #pragma unroll
@@ -780,27 +792,38 @@ __global__ void __launch_bounds__(64) attend_f32_kernel(PrefillArgs a, float sca
 
 // ------------------------------------------------------------------ fuse --
 
-// One group of D/VEC threads per (b, head, token) row; the row's slot loads
-// are all issued before the weighted sum.
+// One group of D/VEC threads per (b, group, token, head of the group) row,
+// heads fastest: the G heads of one selection entry are adjacent partial
+// rows, so a token's gather reads runs of G * d elements.  The row's slot
+// loads are all issued before the weighted sum.
 template <int D, int DT, int KM>
 __global__ void __launch_bounds__(kThreads) fuse_kernel(PrefillArgs a) {
   constexpr int VEC = DT == kF32 ? 4 : 8;
   constexpr int TPR = D / VEC;
   constexpr int RPB = kThreads / TPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int cg = threadIdx.x % TPR;
   const int64_t total = (int64_t)a.B * a.Hq * a.L;
-  if (row >= total) return;
-  const int64_t t = row % a.L;
+  if (r >= total) return;
+  const int G = a.Hq / a.Hkv;
+  const int hh = (int)(r % G);
+  const int64_t bgt = r / G;  // (b, group, token)
+  const int64_t t = bgt % a.L;
+  const int64_t bg = bgt / a.L;
+  const int64_t b = bg / a.Hkv;
+  const int h = (int)(bg % a.Hkv) * G + hh;
+  const int64_t row = (b * a.Hq + h) * a.L + t;  // output row
   const int m = (int)min((int64_t)a.topk, min(t / a.S, a.n));
-  const float* sc = a.part_score + row * a.topk;
+  const int32_t* epos = a.entry_pos + (bg * a.L + t) * a.topk;
+  int64_t pr[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) pr[k] = k < m ? partial_row(a, bg, epos[k], hh) : 0;
   u32x4 x[KM];
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
     if (k < m)
       x[k] = __builtin_nontemporal_load(
-          (const u32x4*)((const char*)a.partial + ((row * a.topk + k) * D + cg * VEC) *
-                                                      (DT == kF32 ? 4 : 2)));
+          (const u32x4*)((const char*)a.partial + (pr[k] * D + cg * VEC) * (DT == kF32 ? 4 : 2)));
     else
       x[k] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -808,7 +831,7 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(PrefillArgs a) {
   float smax = -INFINITY;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    s[k] = k < m ? sc[k] : -INFINITY;
+    s[k] = k < m ? a.part_score[pr[k]] : -INFINITY;
     smax = fmaxf(smax, s[k]);
   }
   float z = 0.f;
@@ -888,7 +911,11 @@ hipError_t launch_select_d(const PrefillArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int prefill_entries_per_tile(int dtype, int G) { return dtype == kF32 ? 64 / G : 128 / G; }
+int prefill_entries_per_tile(int dtype, int G, int S) {
+  if (dtype == kF32) return 64 / G;
+  if (S <= kKeyBlock) return kChunkUnitRows / G;
+  return (kThreads / kWave) * 32 / G;  // one 32-row tile per wave
+}
 
 hipError_t prefill_select(const PrefillArgs& a, hipStream_t stream) {
   if (a.L == 0) return hipSuccess;
@@ -926,12 +953,11 @@ hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream) {
                                                                               score_scale);
   } else if (a.S <= kKeyBlock) {
     const float sl2 = scale * 1.4426950408889634f;
-    const int64_t cblocks = (int64_t)a.B * a.Hkv * a.n;
     if (a.d == 64)
-      attend_chunk_bf16_kernel<64><<<dim3((unsigned)cblocks), dim3(kThreads), 0, stream>>>(
+      attend_chunk_bf16_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(
           a, sl2, score_scale);
     else
-      attend_chunk_bf16_kernel<128><<<dim3((unsigned)cblocks), dim3(kThreads), 0, stream>>>(
+      attend_chunk_bf16_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(
           a, sl2, score_scale);
   } else {
     const float sl2 = scale * 1.4426950408889634f;
