@@ -199,131 +199,185 @@ struct KVSmemWide {
   uint16_t v[(kWideBlock / 4) * D * 4];
 };
 
-// Stage rows [0, nk) (nk <= 128) of a key/value block; rows up to the next
-// multiple of 32 are zero-filled, rows beyond that are never read.
+// One thread's share of a 128-key block held in registers between its
+// global load and its LDS store, so the next block's loads can be in flight
+// while the current block is computed.  256 threads; K as 16-byte row
+// pieces, V as 8-byte pieces of four consecutive keys.
 template <int D>
-__device__ __forceinline__ void load_kv_wide(KVSmemWide<D>& sm, const uint16_t* __restrict__ Kg,
-                                             const uint16_t* __restrict__ Vg, int nk) {
+struct KVRegsWide {
+  static constexpr int KPR = D / 8;  // 16-byte pieces per key row
+  static constexpr int VPR = D / 4;  // 8-byte pieces per value row
+  static constexpr int NK = kWideBlock * KPR / 256;
+  static constexpr int NV = (kWideBlock / 4) * VPR / 256;
+  u32x4 k[NK];
+  u32x2 v[NV][4];
+};
+
+// Raw buffer resource over [base, base + bytes): buffer loads at offsets
+// past the range return zero instead of touching memory.  Word 3 holds the
+// CDNA default (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Loads of rows [0, nk) (nk <= 128) of a key/value block into registers;
+// rows past nk read as zero (buffer range check, no branches).  Called by
+// all 256 threads of the block: thread tid takes K piece tid % KPR of rows
+// tid / KPR + i * (256 / KPR), and V piece tid % VPR of key quads
+// tid / VPR + i * (256 / VPR).
+template <int D>
+__device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* __restrict__ Kg,
+                                              const uint16_t* __restrict__ Vg, int nk) {
+  using R = KVRegsWide<D>;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t kr = buffer_range(Kg, nk * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = buffer_range(Vg, nk * D * 2);
+  const int koff = ((tid / R::KPR) * D + (tid % R::KPR) * 8) * 2;  // bytes
+#pragma unroll
+  for (int i = 0; i < R::NK; ++i)
+    r.k[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff, i * (256 / R::KPR) * D * 2, 0));
+  const int voff = ((tid / R::VPR) * 4 * D + (tid % R::VPR) * 4) * 2;
+#pragma unroll
+  for (int i = 0; i < R::NV; ++i)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      r.v[i][kk] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                     vr, voff, (i * (256 / R::VPR) * 4 + kk) * D * 2, 0));
+}
+
+// LDS store of a fetched block: rows up to the next multiple of 32 above nk
+// (zeros past nk) are written, rows beyond that are never read.  V goes to
+// the [key/4][dim][4 keys] layout.
+template <int D>
+__device__ __forceinline__ void store_kv_wide(KVSmemWide<D>& sm, const KVRegsWide<D>& r,
+                                              int nk) {
+  using R = KVRegsWide<D>;
   const int tid = threadIdx.x;
   const int rows = (nk + 31) & ~31;
-  constexpr int KPR = D / 8;
-  for (int e = tid; e < rows * KPR; e += 256) {
-    const int row = e / KPR, c8 = e % KPR;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < nk) x = *(const u32x4*)(Kg + (int64_t)row * D + c8 * 8);
-    *(u32x4*)(&sm.k[row * (D + 8) + c8 * 8]) = x;
-  }
-  constexpr int VPR = D / 4;
-  for (int e = tid; e < (rows / 4) * VPR; e += 256) {
-    const int grp = e / VPR, cq = e % VPR;
-    u32x2 r[4];
+  const int krow = tid / R::KPR;
+  uint16_t* ks = &sm.k[krow * (D + 8) + (tid % R::KPR) * 8];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int key = grp * 4 + kk;
-      r[kk] = key < nk ? *(const u32x2*)(Vg + (int64_t)key * D + cq * 4) : u32x2{0u, 0u};
-    }
+  for (int i = 0; i < R::NK; ++i)
+    if (krow + i * (256 / R::KPR) < rows) *(u32x4*)(ks + i * (256 / R::KPR) * (D + 8)) = r.k[i];
+  const int vgrp = tid / R::VPR;
+  uint16_t* vs = &sm.v[(vgrp * D + (tid % R::VPR) * 4) * 4];
+#pragma unroll
+  for (int i = 0; i < R::NV; ++i) {
+    if ((vgrp + i * (256 / R::VPR)) * 4 >= rows) continue;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int w = x >> 1;
       uint32_t lo, hi;
       if ((x & 1) == 0) {
-        lo = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-        hi = (r[2][w] & 0xffffu) | (r[3][w] << 16);
+        lo = (r.v[i][0][w] & 0xffffu) | (r.v[i][1][w] << 16);
+        hi = (r.v[i][2][w] & 0xffffu) | (r.v[i][3][w] << 16);
       } else {
-        lo = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-        hi = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
+        lo = (r.v[i][0][w] >> 16) | (r.v[i][1][w] & 0xffff0000u);
+        hi = (r.v[i][2][w] >> 16) | (r.v[i][3][w] & 0xffff0000u);
       }
-      *(u32x2*)(&sm.v[(grp * D + cq * 4 + x) * 4]) = u32x2{lo, hi};
+      *(u32x2*)(vs + (i * (256 / R::VPR) * D + x) * 4) = u32x2{lo, hi};
     }
   }
 }
 
 // One staged block of nkeys (<= 128, block-uniform) keys: this lane's query
 // attends keys with in-block index < nvalid (<= nkeys; may differ per lane).
-// One online-softmax update for the whole block; the accumulator is
-// rescaled only when some lane's running maximum grew.
-template <int D>
+// The block is taken SUB 32-key sub-tiles at a time (SUB = 4: one update
+// for the whole block; SUB = 2: two, with half the score registers), each
+// with one online-softmax update; the accumulator is rescaled only when
+// some lane's running maximum grew.
+template <int D, int SUB>
 __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide<D>& sm,
                                                int nkeys, int nvalid, float scale_log2) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int i32 = lane & 31;
-  const int nsub = (nkeys + 31) >> 5;  // 1..4
-  f32x16 sc[4];
+  const int nsub_all = (nkeys + 31) >> 5;  // 1..4
+#pragma nounroll
+  for (int t0 = 0; t0 < nsub_all; t0 += SUB) {
+    const int nsub = min(SUB, nsub_all - t0);
+    const int nv = nvalid - 32 * t0;  // valid keys of this lane from sub-tile t0 on
+    // the valid keys are a prefix, so once no lane has any left none follow
+    if (__ballot(nv > 0) == 0) break;
+    f32x16 sc[SUB];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < SUB; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t >= nsub) break;
+    for (int t = 0; t < SUB; ++t) {
+      if (t >= nsub) break;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 a0 = *(const bf16x8*)(&sm.k[(32 * t + i32) * (D + 8) + 16 * s + 8 * h]);
-      sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, st.qf[s], sc[t], 0, 0, 0);
+      for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 a0 =
+            *(const bf16x8*)(&sm.k[(32 * (t0 + t) + i32) * (D + 8) + 16 * s + 8 * h]);
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, st.qf[s], sc[t], 0, 0, 0);
+      }
     }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // keys at or past nvalid (and padding past nkeys) take no weight
-  const bool need_mask = __ballot(nvalid < 32 * nsub) != 0;
-  if (need_mask) {
+    __builtin_amdgcn_sched_barrier(0);
+    // keys at or past nvalid (and padding past nkeys) take no weight
+    if (__ballot(nv < 32 * nsub) != 0) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < SUB; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= nv) sc[t][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < SUB; ++t) {
+      if (t >= nsub) break;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * scale_log2;
+    const float m_new = fmaxf(st.m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < SUB; ++t) {
+      if (t >= nsub) break;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (key >= nvalid) sc[t][r] = -INFINITY;
-      }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t >= nsub) break;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * scale_log2;
-  const float m_new = fmaxf(st.m, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  float ps = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t >= nsub) break;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[t][r] = fast_exp2(__builtin_fmaf(sc[t][r], scale_log2, -m_use));
-      ps += sc[t][r];
-    }
-  }
-  ps += __shfl_xor(ps, 32, kWave);
-  if (__ballot(m_new > st.m) != 0) {
-    const float alpha = fast_exp2(st.m - m_use);
-    st.l *= alpha;
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[b][r] *= alpha;
-  }
-  st.l += ps;
-  st.m = m_new;
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t >= nsub) break;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8 pb = cvt_bf16x8(sc[t], 8 * s2);
-      const int g0 = 8 * t + 4 * s2 + h, g1 = g0 + 2;
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b) {
-        const int dd = 32 * b + i32;
-        const u32x2 v0 = *(const u32x2*)(&sm.v[(g0 * D + dd) * 4]);
-        const u32x2 v1 = *(const u32x2*)(&sm.v[(g1 * D + dd) * 4]);
-        const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
-        st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
-                                                          st.o[b], 0, 0, 0);
+        sc[t][r] = fast_exp2(__builtin_fmaf(sc[t][r], scale_log2, -m_use));
+        ps += sc[t][r];
       }
     }
+    ps += __shfl_xor(ps, 32, kWave);
+    if (__ballot(m_new > st.m) != 0) {
+      const float alpha = fast_exp2(st.m - m_use);
+      st.l *= alpha;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[b][r] *= alpha;
+    }
+    st.l += ps;
+    st.m = m_new;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < SUB; ++t) {
+      if (t >= nsub) break;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 pb = cvt_bf16x8(sc[t], 8 * s2);
+        const int g0 = 8 * (t0 + t) + 4 * s2 + h, g1 = g0 + 2;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) {
+          const int dd = 32 * b + i32;
+          const u32x2 v0 = *(const u32x2*)(&sm.v[(g0 * D + dd) * 4]);
+          const u32x2 v1 = *(const u32x2*)(&sm.v[(g1 * D + dd) * 4]);
+          const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
+          st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
+                                                            st.o[b], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -29,6 +29,9 @@ namespace hsa {
 namespace {
 
 constexpr int kThreads = 256;
+// 32-key sub-tiles per online-softmax update in the attention (see
+// wave_attn_wide): two keep the scores and the prefetched block in registers.
+constexpr int kDhsaSub = 4;
 constexpr int kRowsPerTile = 128;
 constexpr int kMaxSort = 4096;  // 32 KiB of 64-bit sort keys in LDS
 
@@ -216,19 +219,45 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   wave_attn_init<D>(st, Qb + i * D, valid);
   const bool wave_any = __ballot(valid) != 0;
   const int32_t* order = a.order + (bh * a.nc + l) * a.nc;
-  for (int p = 0; p <= p_end; ++p) {
-    const int k = order[p];
-    const int bk = a.offs[k], lk = a.offs[k + 1] - bk;
+  // Key blocks in rank order: chunk order[p], keys [kb, kb + 128).  Each
+  // step stores the block fetched during the previous step, starts the
+  // fetch of the next one, then computes.
+  int p = 0, kb = 0, k = 0, bk = 0, lk = 0;
+  KVRegsWide<D> rg;
+  if (p_end >= 0) {
+    k = order[0];
+    bk = a.offs[k];
+    lk = a.offs[k + 1] - bk;
+    fetch_kv_wide<D>(rg, Kb + (int64_t)bk * D, Vb + (int64_t)bk * D, min(kWideBlock, lk));
+  }
+  while (p <= p_end) {
+    const int nk = min(kWideBlock, lk - kb);
+    __syncthreads();
+    store_kv_wide<D>(sm, rg, nk);
+    __syncthreads();
+    int np = p, nkb = kb + kWideBlock, nkc = k, nbk = bk, nlk = lk;
+    if (nkb >= lk) {
+      np = p + 1;
+      nkb = 0;
+      if (np <= p_end) {
+        nkc = order[np];
+        nbk = a.offs[nkc];
+        nlk = a.offs[nkc + 1] - nbk;
+      }
+    }
+    if (np <= p_end)
+      fetch_kv_wide<D>(rg, Kb + (int64_t)(nbk + nkb) * D, Vb + (int64_t)(nbk + nkb) * D,
+                       min(kWideBlock, nlk - nkb));
+    __builtin_amdgcn_sched_barrier(0);
     const int len_eff = k == l ? (int)(i - bl + 1) : lk;
     const int hi = !valid ? 0 : (p < cut.pw ? len_eff : (p == cut.pw ? cut.rem : 0));
-    for (int kb = 0; kb < lk; kb += kWideBlock) {
-      const int nk = min(kWideBlock, lk - kb);
-      __syncthreads();
-      load_kv_wide<D>(sm, Kb + (int64_t)(bk + kb) * D, Vb + (int64_t)(bk + kb) * D, nk);
-      __syncthreads();
-      const int nv = max(0, min(hi - kb, nk));
-      if (wave_any && __ballot(nv > 0) != 0) wave_attn_wide<D>(st, sm, nk, nv, scale_log2);
-    }
+    const int nv = max(0, min(hi - kb, nk));
+    if (wave_any && __ballot(nv > 0) != 0) wave_attn_wide<D, kDhsaSub>(st, sm, nk, nv, scale_log2);
+    p = np;
+    kb = nkb;
+    k = nkc;
+    bk = nbk;
+    lk = nlk;
   }
   if (!valid) return;
   const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
