@@ -5,8 +5,9 @@ One step = one call of the whole path on one batch of synthetic input that is
 already resident in HBM.  The headline workload is HSA prefill at B=1,
 L=32768, 16 query heads over 4 KV heads, d=128, S=64, top-8, bf16: landmark
 pooling, scoring + top-K, chunk attention and fusion, all inside the timed
-call.  By default the decode workload (batch 32, 131072-token caches) and the
-DHSA prefill workload (L=16384, N_b=2048) are measured too and reported under
+call.  By default the decode workloads (batch 32 with 131072-token caches;
+batch 1 with a 16,777,216-token cache and a planted needle) and the DHSA
+prefill workload (L=16384, N_b=2048) are measured too and reported under
 "also".
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
@@ -24,6 +25,47 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 METRIC = "HSA queries/sec + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU"
+
+# The dominant kernel of each workload (a substring of its demangled name and
+# its argument struct) and the sources it is built from.  HBM traffic per
+# launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs summarised by
+# --summarize-counters into TRAFFIC_FILE; it is reported only while these
+# sources hash the same as when the counters were taken.
+CSRC = os.path.join(ROOT, "chunk_hierarchical_sparse_amd", "csrc")
+DOMINANT = {
+    "hsa_prefill": ("attend_chunk_bf16_kernel<128>", "PrefillArgs",
+                    ["prefill.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
+    "hsa_decode": ("scan_kernel<128, 1>", "DecodeArgs",
+                   ["decode.hip", "hsa_common.h", "kernels.h"]),
+    "hsa_decode_16m": ("scan_kernel<128, 1>", "DecodeArgs",
+                       ["decode.hip", "hsa_common.h", "kernels.h"]),
+    "dhsa_prefill": ("attend_kernel<128>", "DhsaArgs",
+                     ["dhsa.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_workloads.txt")
+
+
+def sources_sha1(workload):
+    import hashlib
+    h = hashlib.sha1()
+    for f in DOMINANT[workload][2]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(workload):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    counter summary, or None when absent or taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            body = "".join(l for l in fh if not l.lstrip().startswith("#"))
+        rec = json.loads(body)["workloads"][workload]
+    except (OSError, ValueError, KeyError):
+        return None
+    if rec.get("sources_sha1") != sources_sha1(workload):
+        return None
+    return rec["traffic_bytes"]
 
 
 def log(*a):
@@ -102,7 +144,7 @@ def bench_prefill(torch, hsa, args):
                 "S": S, "topk": topk, "inputs": "0.5*N(0,1) bf16, seed 2"},
         roofline={"bound": "mfma", "kernel": "attend (chunk attention, bf16 MFMA)",
                   "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("hsa_prefill"),
                   "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": attn_ms},
         stages_ms=dict(zip(["landmarks", "select", "invert", "attend", "fuse"], stages)),
         whole_path={"gflop": total_flop / 1e9,
@@ -145,7 +187,7 @@ def bench_decode(torch, hsa, args, big=False):
         hsa.hsa_decode(q, Kc, Vc, lmk, N, S, topk, out=out, workspace=ws)
 
     log("decode: timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 4)
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 3)
     n = N // S
     lmk_bytes = B * Hkv * n * d * 4
     kv_bytes = B * Hkv * topk * S * d * 2 * 2
@@ -153,16 +195,17 @@ def bench_decode(torch, hsa, args, big=False):
     total = lmk_bytes + kv_bytes + qo_bytes
     scan_ms = stages[0]
     achieved = lmk_bytes / (scan_ms * 1e-3) / 1e9
+    workload = "hsa_decode_16m" if big else "hsa_decode"
     res = dict(
         value=B / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
-        config={"workload": "hsa_decode_16m" if big else "hsa_decode", "B": B, "n_ctx": N,
+        config={"workload": workload, "B": B, "n_ctx": N,
                 "Hq": Hq, "Hkv": Hkv, "d": d, "S": S, "topk": topk,
                 "inputs": f"N(0,1) bf16, seed {seed}" + (", planted needle" if big else "")},
         roofline={"bound": "hbm", "kernel": "scan (landmark stream + top-K)",
                   "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                  "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                  "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_for(workload),
                   "algorithmic_bytes_per_launch": lmk_bytes, "avg_launch_ms": scan_ms},
-        stages_ms=dict(zip(["scan", "merge", "attend", "fuse"], stages)),
+        stages_ms=dict(zip(["scan", "attend", "fuse"], stages)),
         whole_path={"algorithmic_bytes": total, "gbps": total / (ms * 1e-3) / 1e9,
                     "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
     del Kc, Vc, lmk, q, out, ws
@@ -196,7 +239,7 @@ def bench_dhsa(torch, hsa, args):
                 "chunks": len(offs) - 1, "inputs": "N(0,1) bf16, lengths U{16..128}, seed 5"},
         roofline={"bound": "mfma", "kernel": "attend (block-sparse masked attention)",
                   "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("dhsa_prefill"),
                   "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": stages[3]},
         stages_ms=dict(zip(["pool", "sc", "rank", "attend", "mask"], stages)))
     del q, k, v, out, ws
@@ -227,19 +270,84 @@ def cpu_baseline(inputs, target_s):
                       "double precision C oracle (OpenMP)"}
 
 
+def _counter_rows(run_dir):
+    """(dispatch id, kernel name, value) of a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"{run_dir}: expected one *counter_collection.csv, found {len(files)}")
+    rows = []
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir, bench_json):
+    """Per-launch HBM bytes of each workload's dominant kernel from a
+    FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch) of the same bench
+    command, each scaled by what the counter reads for the trailing plain
+    copy of known size (--copy-calibration)."""
+    with open(bench_json) as fh:
+        line = json.loads(fh.read().strip().splitlines()[-1])
+    order = [line["config"]["workload"]] + [a["config"]["workload"]
+                                           for a in line.get("also", [])]
+    per = line["steps"] + line["warmup"]
+    cal = line.get("copy_calibration_bytes")
+    if not cal:
+        raise SystemExit("the bench run needs --copy-calibration")
+    out = {"calibration_copy_bytes": cal, "launches_per_workload": per, "workloads": {}}
+    vals = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d)
+        copies = [v for _, n, v in rows if "copy" in n.lower()][-2:]
+        scale = cal / (sum(copies) / len(copies) * 1024.0)
+        out[counter.lower() + "_scale"] = scale
+        used = {}
+        for w in order:
+            if w not in DOMINANT:
+                continue
+            name, args_t = DOMINANT[w][0], DOMINANT[w][1]
+            mine = [v for _, n, v in rows if name in n and args_t in n]
+            k0 = used.get((name, args_t), 0)
+            take = mine[k0:k0 + per]
+            used[(name, args_t)] = k0 + per
+            if len(take) != per:
+                raise SystemExit(f"{counter}: {w}: expected {per} launches of {name}")
+            vals.setdefault(w, {})[counter] = sum(take) / per
+    for w, v in vals.items():
+        f_b = v["FETCH_SIZE"] * 1024.0 * out["fetch_size_scale"]
+        w_b = v["WRITE_SIZE"] * 1024.0 * out["write_size_scale"]
+        out["workloads"][w] = {"kernel": DOMINANT[w][0], "fetch_kib_per_launch": v["FETCH_SIZE"],
+                               "write_kib_per_launch": v["WRITE_SIZE"], "fetch_bytes": f_b,
+                               "write_bytes": w_b, "traffic_bytes": f_b + w_b,
+                               "sources_sha1": sources_sha1(w)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--extras", default="decode,dhsa",
+    ap.add_argument("--extras", default="decode,decode16m,dhsa",
                     help="comma list of extra workloads: decode, decode16m, dhsa, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="after the workloads, copy GIB GiB device-to-device twice (a plain "
                          "copy kernel of known size to scale HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=3,
+                    metavar=("FETCH_RUN_DIR", "WRITE_RUN_DIR", "BENCH_JSON"),
+                    help="no GPU work: summarise two rocprofv3 --pmc runs (FETCH_SIZE, "
+                         "WRITE_SIZE) of one bench command with --copy-calibration, and print "
+                         "per-launch HBM traffic of each workload's dominant kernel")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)

@@ -73,8 +73,11 @@ struct DecodeArgs {
   int n_slices, slice;
 };
 void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* slice);
-// stages: 0 scan, 1 merge, 2 attend, 3 fuse
-constexpr int kDecodeStages = 4;
+// stages: 0 scan (landmark stream + per-slice top-K), 1 attend (merge of the
+// slices' candidates, per-chunk attention), 2 fuse
+constexpr int kDecodeStages = 3;
+// dynamic LDS bytes of the attention stage
+size_t decode_attend_lds(int Hq, int Hkv, int d, int n_slices, int topk);
 hipError_t decode_stage(const DecodeArgs& a, int stage, hipStream_t stream);
 int64_t decode_max_chunks(int topk);
 

@@ -161,7 +161,8 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
  * thread, each hsa_prefill, hsa_decode and dhsa_prefill call records a HIP
  * event on its stream before each of its stages and one after the last:
  *   hsa_prefill : 0 landmarks, 1 select, 2 invert, 3 attend, 4 fuse
- *   hsa_decode  : 0 scan, 1 merge, 2 attend, 3 fuse
+ *   hsa_decode  : 0 scan (landmark stream, per-slice top-K), 1 attend (merge
+ *                 of the slices' candidates, chunk attention), 2 fuse
  *   dhsa_prefill: 0 pool, 1 S_c, 2 rank, 3 attend, 4 mask
  * hsa_profile_read waits for the recorded events, adds the elapsed
  * milliseconds of stage s summed over all recorded calls into stage_ms[s]

@@ -73,3 +73,34 @@ def test_decode_equals_prefill_last_row():
     torch.cuda.synchronize()
     diff = (host(pre)[:, :, L] - host(dec))
     assert np.abs(diff).max() <= 1e-2
+
+
+def test_decode_merge_with_many_candidates_above_the_bound():
+    # One KV head, S = 1, top-32 over 32768 chunks: 128 slices of 256 chunks
+    # feed the merge.  Landmarks are given directly so that the scores are
+    # set per chunk: each slice's first 32 chunks take distinct values
+    # 10 + u/64 (u a permutation of 0..4095), the rest lie below 1.  The
+    # slices' top-32 lists then interleave, more than 64 candidates reach
+    # the merge's lower bound and the radix-select path runs.
+    B, Hq, Hkv, N, d, S, topk = 1, 1, 1, 32768, 64, 1, 32
+    rng = np.random.default_rng(91)
+    q = np.zeros((B, Hq, d), np.uint16)
+    q[0, 0, 0] = synth.f32_to_bf16(np.float32(1.0))
+    score = rng.uniform(0.0, 1.0, N)
+    perm = rng.permutation(128 * 32)
+    for j in range(128):
+        for r in range(32):
+            score[j * 256 + r] = 10.0 + perm[j * 32 + r] / 64.0
+    lmk = np.zeros((B, Hkv, N, d), np.float32)
+    lmk[0, 0, :, 0] = (score * np.sqrt(d)).astype(np.float32)
+    Kc = gen((B, Hkv, N, d), "bf16", 91, synth.TID_K)
+    Vc = gen((B, Hkv, N, d), "bf16", 91, synth.TID_V)
+    o, sel, w = hsa.hsa_decode(dev(q), dev(Kc), dev(Vc), dev(lmk), N, S, topk,
+                               return_selection=True)
+    torch.cuda.synchronize()
+    o, sel, w = host(o), host(sel), host(w)
+    ref = oracle.hsa_decode(q, Kc, Vc, lmk, S, N, topk)
+    assert ref["margin"].min() > 1e-4
+    assert np.array_equal(sel, ref["sel"])
+    check_out(o, ref["out"], "bf16", "decode output (many candidates)")
+    assert np.abs(w - ref["w"]).max() <= 1e-5
