@@ -145,6 +145,7 @@ hsa_status_t check_decode(int B, int Hq, int Hkv, int d, int S, int topk, int64_
 
 struct DecodeLayout {
   uint64_t* cand;
+  uint64_t* cand_mm;
   int32_t* sel;
   float* part_o;
   float* part_s;
@@ -158,6 +159,7 @@ DecodeLayout decode_layout(void* ws, int B, int Hq, int Hkv, int d, int S, int t
   hsa::decode_plan(n_ctx / S, topk, (int64_t)B * Hkv, &p.n_slices, &p.slice);
   Carver cv(ws);
   p.cand = cv.take<uint64_t>((size_t)B * Hkv * p.n_slices * topk);
+  p.cand_mm = cv.take<uint64_t>((size_t)B * Hkv * p.n_slices * 2);
   p.sel = cv.take<int32_t>((size_t)B * Hkv * topk);
   p.part_o = cv.take<float>((size_t)B * Hq * topk * d);
   p.part_s = cv.take<float>((size_t)B * Hq * topk);
@@ -334,6 +336,7 @@ hsa_status_t hsa_decode(const void* q, const void* Kc, const void* Vc, const flo
   a.sel = sel_idx ? sel_idx : lay.sel;
   a.sel_w = sel_w;
   a.cand = lay.cand;
+  a.cand_mm = lay.cand_mm;
   a.part_o = lay.part_o;
   a.part_s = lay.part_s;
   a.B = B;

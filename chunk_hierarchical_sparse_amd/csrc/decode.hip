@@ -187,6 +187,14 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
   const int got = block_topk_ge(keys, M, 0ull, a.topk, sel, hist, sv);
   uint64_t* out = a.cand + (bg * a.n_slices + sl) * a.topk;
   for (int k = threadIdx.x; k < a.topk; k += kThreads) out[k] = k < got ? sel[k] : 0ull;
+  if (threadIdx.x == 0) {
+    uint64_t mx = 0ull, mn = ~0ull;
+    for (int k = 0; k < got; ++k) {
+      mx = sel[k] > mx ? sel[k] : mx;
+      mn = sel[k] < mn ? sel[k] : mn;
+    }
+    *(u64x2*)(a.cand_mm + (bg * a.n_slices + sl) * 2) = u64x2{mx, got == a.topk ? mn : 0ull};
+  }
 }
 
 constexpr int kMergeLds = 1024;  // candidates above the bound kept in LDS
@@ -211,27 +219,15 @@ __device__ int merge_candidates(const DecodeArgs& a, int64_t bg, uint64_t* ck, u
   if (total > kWave) {
     // Lower bounds of the K-th largest key: a full slice's smallest kept
     // key, and the K-th largest of the maxima of any 64 slices (K distinct
-    // keys reach it).  Lane l of a wave takes slice 64 * grp + l; its loads
-    // have fixed trip counts (K <= 32 is uniform) so all are in flight.
+    // keys reach it).  Lane l of a wave takes slice 64 * grp + l.
+    const uint64_t* mm = a.cand_mm + bg * (int64_t)a.n_slices * 2;
     uint64_t m = 0;
     for (int grp = w; grp * kWave < a.n_slices; grp += kThreads / kWave) {
       const int j = grp * kWave + lane;
-      uint64_t mx = 0ull, mn = 0ull;
-      if (j < a.n_slices) {
-        const uint64_t* cs = cand + (int64_t)j * K;
-        uint64_t x[32];
-#pragma unroll
-        for (int kk = 0; kk < 32; ++kk) x[kk] = kk < K ? cs[kk] : 0ull;
-        mn = ~0ull;
-#pragma unroll
-        for (int kk = 0; kk < 32; ++kk) {
-          if (kk < K) mn = x[kk] < mn ? x[kk] : mn;
-          mx = x[kk] > mx ? x[kk] : mx;
-        }
-      }
-      m = mn > m ? mn : m;
-      const uint64_t srt = wave_sort_desc_u64(mx);
-      const uint64_t kth = __shfl(srt, K - 1, kWave);
+      u64x2 v = {0ull, 0ull};
+      if (j < a.n_slices) v = *(const u64x2*)(mm + 2 * j);
+      m = v[1] > m ? v[1] : m;
+      const uint64_t kth = __shfl(wave_sort_desc_u64(v[0]), K - 1, kWave);
       m = kth > m ? kth : m;
     }
     m = wave_max_u64(m);
@@ -239,16 +235,20 @@ __device__ int merge_candidates(const DecodeArgs& a, int64_t bg, uint64_t* ck, u
     if (tid == 0) sv[3] = 0;
     __syncthreads();
     for (int x = 0; x < kThreads / kWave; ++x) lb = red[x] > lb ? red[x] : lb;
-    constexpr int U = 8;
-    for (int i0 = tid; i0 < total; i0 += U * kThreads) {
-      uint64_t x[U];
+    // only slices whose largest key reaches the bound hold survivors; their
+    // loads have fixed trip counts (K <= 32 is uniform) so all are in flight
+    for (int grp = w; grp * kWave < a.n_slices; grp += kThreads / kWave) {
+      const int j = grp * kWave + lane;
+      if (j >= a.n_slices || mm[2 * j] < lb) continue;
+      const uint64_t* cs = cand + (int64_t)j * K;
+      uint64_t x[32];
 #pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = i0 + u * kThreads < total ? cand[i0 + u * kThreads] : 0ull;
+      for (int kk = 0; kk < 32; ++kk) x[kk] = kk < K ? cs[kk] : 0ull;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (x[u] >= lb) {
+      for (int kk = 0; kk < 32; ++kk)
+        if (x[kk] >= lb) {
           const int p = atomicAdd(&sv[3], 1);
-          if (p < kMergeLds) ck[p] = x[u];
+          if (p < kMergeLds) ck[p] = x[kk];
         }
     }
     __syncthreads();

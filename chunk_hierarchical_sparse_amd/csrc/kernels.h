@@ -66,6 +66,7 @@ struct DecodeArgs {
   int32_t* sel;        // [B,Hkv,topk]
   float* sel_w;        // [B,Hq,topk] or null
   uint64_t* cand;      // [B*Hkv, n_slices, topk]
+  uint64_t* cand_mm;   // [B*Hkv, n_slices, 2]: largest, smallest kept key (0 if not full)
   float* part_o;       // [B,Hq,topk,d]
   float* part_s;       // [B,Hq,topk]
   int B, Hq, Hkv, d, S, topk, dtype;
