@@ -37,9 +37,13 @@ def lib():
                                                _I, _I, _I, _P, _P]
         L.oracle_dhsa_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _P, _I, _I,
                                           _P, _I, _P, _P, _P, _P, _P]
+        L.oracle_dhsa_chunk_keys.argtypes = [_P, ctypes.c_int, _I, _I, _I, _I, _P, _I, _P]
+        L.oracle_dhsa_decode.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _I, _P, _I,
+                                         _I, _P, _P, _P, _P, _P]
         L.oracle_num_threads.argtypes = []
         for f in (L.oracle_num_threads, L.oracle_landmarks, L.oracle_hsa_prefill, L.oracle_hsa_decode_select,
-                  L.oracle_hsa_decode_attend, L.oracle_dhsa_prefill):
+                  L.oracle_hsa_decode_attend, L.oracle_dhsa_prefill, L.oracle_dhsa_chunk_keys,
+                  L.oracle_dhsa_decode):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -199,3 +203,42 @@ def dhsa_prefill(Q, K, V, offsets, budget, rows=None, want_sc=False, want_kept=F
                                    margin.ctypes.data)
     _check(rc, "dhsa_prefill")
     return dict(out=out, sc=sc, n_kept=n_kept, kept=kept, margin=margin)
+
+
+def dhsa_chunk_keys(K, offsets):
+    """k_hat [B,H,n,d] (float64) of the n complete chunks given by offsets[0..n]."""
+    K = _c(K)
+    B, H, N, d = K.shape
+    offs = np.ascontiguousarray(offsets, dtype=np.int32)
+    n = len(offs) - 1
+    khat = np.zeros((B, H, n, d), np.float64)
+    rc = lib().oracle_dhsa_chunk_keys(K.ctypes.data, _dt(K), B, H, N, d, offs.ctypes.data, n,
+                                      khat.ctypes.data)
+    _check(rc, "dhsa_chunk_keys")
+    return khat
+
+
+def dhsa_decode(Qcur, K, V, offsets, budget, want_kept=False):
+    """DHSA decode of the new query at pos = offsets[-1] + m - 1, where
+    Qcur [B,H,m,d] holds the current chunk's queries (the last row is the new
+    query), K/V [B,H,N,d] caches and offsets[0..n] the complete chunks.
+
+    Returns dict(out [B,H,d], sc [B,H,n+1], n_kept [B,H], kept [B,H,pos+1]
+    uint8 or None, margin [B,H], pos)."""
+    Qcur, K, V = _c(Qcur), _c(K), _c(V)
+    B, H, m, d = Qcur.shape
+    N = K.shape[2]
+    offs = np.ascontiguousarray(offsets, dtype=np.int32)
+    n = len(offs) - 1
+    pos = int(offs[-1]) + m - 1
+    out = np.zeros((B, H, d), np.float64)
+    sc = np.zeros((B, H, n + 1), np.float64)
+    n_kept = np.zeros((B, H), np.int32)
+    kept = np.zeros((B, H, pos + 1), np.uint8) if want_kept else None
+    margin = np.zeros((B, H), np.float64)
+    rc = lib().oracle_dhsa_decode(Qcur.ctypes.data, K.ctypes.data, V.ctypes.data,
+                                  _dt(Qcur, K, V), B, H, d, m, N, offs.ctypes.data, n, budget,
+                                  out.ctypes.data, sc.ctypes.data, n_kept.ctypes.data, _ptr(kept),
+                                  margin.ctypes.data)
+    _check(rc, "dhsa_decode")
+    return dict(out=out, sc=sc, n_kept=n_kept, kept=kept, margin=margin, pos=pos)

@@ -40,7 +40,14 @@
  *    never available;
  *  - DHSA: S_c = q_hat . k_hat with no 1/sqrt(d); query i may keep keys
  *    j <= i; it keeps the first min(N_b, i+1) of them in (score desc, j asc)
- *    order; attention logits use 1/sqrt(d).
+ *    order; attention logits use 1/sqrt(d);
+ *  - DHSA decode (the decode-time update of [DHSA] Referee report, minor
+ *    comment on Algorithm 2, where the last chunk holds the current query):
+ *    the new query i sits in the current chunk [b_n, i], which is pooled
+ *    like any chunk over the tokens it has so far (its queries and keys
+ *    b_n..i); the complete chunks 0..n-1 and the current one are scored,
+ *    tiled to tokens j <= i and cut at min(N_b, i+1) exactly as in prefill,
+ *    so a decode step equals prefill row i of the sequence cut at i+1.
  */
 #include <math.h>
 #include <stdint.h>
@@ -551,5 +558,167 @@ int oracle_dhsa_prefill(const void* Q, const void* K, const void* V, int dtype, 
   free(qh);
   free(kh);
   free(sc_m);
+  return err;
+}
+
+
+/*
+ * DHSA pooled chunk keys ([DHSA] "What carries the argument", Eq. 4):
+ * k_hat_k = (sum of the keys of chunk k) / sqrt|C_k| for chunks
+ * k = 0..n-1 with boundaries offsets[0..n] (0 = b_0 < ... < b_n <= N).
+ *   K     [B,H,N,d] dtype
+ *   khat  [B,H,n,d]
+ */
+int oracle_dhsa_chunk_keys(const void* K, int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                           const int32_t* offsets, int64_t n, double* khat) {
+  if (!K || !offsets || !khat || B < 0 || H <= 0 || N < 0 || d <= 0 || n < 0) return OR_EINVAL;
+  if (offsets[0] != 0 || offsets[n] > N) return OR_EINVAL;
+  for (int64_t k = 0; k < n; ++k)
+    if (offsets[k + 1] <= offsets[k]) return OR_EINVAL;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t bh = 0; bh < B * H; ++bh)
+    for (int64_t k = 0; k < n; ++k) {
+      const int64_t len = offsets[k + 1] - offsets[k];
+      for (int64_t x = 0; x < d; ++x) {
+        double a = 0.0;
+        for (int64_t j = offsets[k]; j < offsets[k + 1]; ++j) a += ld(K, dtype, (bh * N + j) * d + x);
+        khat[(bh * n + k) * d + x] = a / sqrt((double)len);
+      }
+    }
+  return OR_OK;
+}
+
+/*
+ * DHSA decode: one new query at position pos = b_n + m - 1 per (b, h).
+ *   Qcur   [B,H,m,d] dtype: the queries of the current chunk b_n..pos (the
+ *          last row is the new query)
+ *   K, V   [B,H,N,d] dtype caches; rows 0..pos are used
+ *   offsets[0..n] boundaries of the n complete chunks (b_n <= pos < N)
+ *   budget N_b >= 1
+ * Outputs (any may be NULL):
+ *   out    [B,H,d]
+ *   Sc     [B,H,n+1]  chunk scores q_hat . k_hat_k, k = n is the current chunk
+ *   n_kept [B,H]      number of kept keys, min(N_b, pos+1)
+ *   kept   [B,H,pos+1] 1 where key j is kept
+ *   margin [B,H]      as in oracle_dhsa_prefill
+ */
+int oracle_dhsa_decode(const void* Qcur, const void* K, const void* V, int dtype, int64_t B,
+                       int64_t H, int64_t d, int64_t m, int64_t N, const int32_t* offsets,
+                       int64_t n, int64_t budget, double* out, double* Sc, int32_t* n_kept,
+                       uint8_t* kept, double* margin) {
+  if (!Qcur || !K || !V || !offsets || B < 0 || H <= 0 || d <= 0 || m < 1 || n < 0 ||
+      budget <= 0)
+    return OR_EINVAL;
+  if (offsets[0] != 0) return OR_EINVAL;
+  for (int64_t k = 0; k < n; ++k)
+    if (offsets[k + 1] <= offsets[k]) return OR_EINVAL;
+  const int64_t pos = offsets[n] + m - 1;
+  if (pos >= N) return OR_EINVAL;
+  const int64_t nc = n + 1;  /* complete chunks plus the current one */
+  const double sc = 1.0 / sqrt((double)d);
+  int64_t* chunk_of = (int64_t*)malloc((size_t)(pos + 1) * sizeof(int64_t));
+  int64_t* bnd = (int64_t*)malloc((size_t)(nc + 1) * sizeof(int64_t));
+  if (!chunk_of || !bnd) {
+    free(chunk_of); free(bnd);
+    return OR_ENOMEM;
+  }
+  for (int64_t k = 0; k <= n; ++k) bnd[k] = offsets[k];
+  bnd[nc] = pos + 1;
+  for (int64_t k = 0; k < nc; ++k)
+    for (int64_t j = bnd[k]; j < bnd[k + 1]; ++j) chunk_of[j] = k;
+  int err = OR_OK;
+#pragma omp parallel
+  {
+    double* qh = (double*)malloc((size_t)d * sizeof(double));
+    double* kh = (double*)malloc((size_t)d * sizeof(double));
+    double* scv = (double*)malloc((size_t)nc * sizeof(double));
+    double* logit = (double*)malloc((size_t)(pos + 1) * sizeof(double));
+    tok_t* tok = (tok_t*)malloc((size_t)(pos + 1) * sizeof(tok_t));
+    if (!qh || !kh || !scv || !logit || !tok) {
+#pragma omp atomic write
+      err = OR_ENOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t bh = 0; bh < B * H; ++bh) {
+        const int64_t kvb = bh * N * d;
+        /* the current chunk's pooled query: its m queries / sqrt(m) */
+        for (int64_t x = 0; x < d; ++x) {
+          double a = 0.0;
+          for (int64_t r = 0; r < m; ++r) a += ld(Qcur, dtype, (bh * m + r) * d + x);
+          qh[x] = a / sqrt((double)m);
+        }
+        /* S_c over the complete chunks and the current one */
+        for (int64_t k = 0; k < nc; ++k) {
+          const int64_t len = bnd[k + 1] - bnd[k];
+          for (int64_t x = 0; x < d; ++x) {
+            double a = 0.0;
+            for (int64_t j = bnd[k]; j < bnd[k + 1]; ++j) a += ld(K, dtype, kvb + j * d + x);
+            kh[x] = a / sqrt((double)len);
+          }
+          double s = 0.0;
+          for (int64_t x = 0; x < d; ++x) s += qh[x] * kh[x];
+          scv[k] = s;
+        }
+        if (Sc) memcpy(Sc + bh * nc, scv, (size_t)nc * sizeof(double));
+        /* tiling to the tokens j <= pos and the top-N_b cut */
+        for (int64_t j = 0; j <= pos; ++j) {
+          tok[j].score = scv[chunk_of[j]];
+          tok[j].j = j;
+        }
+        qsort(tok, (size_t)(pos + 1), sizeof(tok_t), tok_cmp);
+        const int64_t keep = (pos + 1) < budget ? (pos + 1) : budget;
+        if (n_kept) n_kept[bh] = (int32_t)keep;
+        if (kept) {
+          uint8_t* krow = kept + bh * (pos + 1);
+          memset(krow, 0, (size_t)(pos + 1));
+          for (int64_t p = 0; p < keep; ++p) krow[tok[p].j] = 1;
+        }
+        if (margin) {
+          double mg = INFINITY;
+          if (keep < pos + 1) {
+            const int64_t ccut = chunk_of[tok[keep].j];
+            const double scut = tok[keep].score;
+            int64_t p = keep;
+            while (p > 0 && chunk_of[tok[p - 1].j] == ccut) --p;
+            if (p > 0) mg = fmin(mg, tok[p - 1].score - scut);
+            p = keep;
+            while (p <= pos && chunk_of[tok[p].j] == ccut) ++p;
+            if (p <= pos) mg = fmin(mg, scut - tok[p].score);
+          }
+          margin[bh] = mg;
+        }
+        /* softmax attention of the new query over the kept keys */
+        const int64_t qb = (bh * m + m - 1) * d;
+        double mx = -INFINITY;
+        for (int64_t p = 0; p < keep; ++p) {
+          double a = 0.0;
+          for (int64_t x = 0; x < d; ++x)
+            a += ld(Qcur, dtype, qb + x) * ld(K, dtype, kvb + tok[p].j * d + x);
+          logit[p] = a * sc;
+          if (logit[p] > mx) mx = logit[p];
+        }
+        double z = 0.0;
+        for (int64_t p = 0; p < keep; ++p) {
+          logit[p] = exp(logit[p] - mx);
+          z += logit[p];
+        }
+        if (out) {
+          double* orow = out + bh * d;
+          for (int64_t x = 0; x < d; ++x) orow[x] = 0.0;
+          for (int64_t p = 0; p < keep; ++p) {
+            const double pw = logit[p] / z;
+            for (int64_t x = 0; x < d; ++x) orow[x] += pw * ld(V, dtype, kvb + tok[p].j * d + x);
+          }
+        }
+      }
+    }
+    free(qh);
+    free(kh);
+    free(scv);
+    free(logit);
+    free(tok);
+  }
+  free(chunk_of);
+  free(bnd);
   return err;
 }

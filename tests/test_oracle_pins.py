@@ -385,3 +385,83 @@ def test_dhsa_margin_and_cut_structure():
             toks = kept[chunk_of[kept] == c]
             assert toks[0] == offs[c] and (np.diff(toks) == 1).all()
         assert r["margin"][0, 0, i] >= 0
+
+
+# ---------------------------------------------------------- DHSA decode
+
+
+def _dhsa_decode_case(seed, N, d, H, lo, hi, n_complete, m):
+    Q, K, V = (f32((1, H, N, d), seed, t) for t in (synth.TID_Q, synth.TID_K, synth.TID_V))
+    offs = synth.chunk_offsets(N, lo, hi, seed=seed)[: n_complete + 1]
+    pos = int(offs[-1]) + m - 1
+    return Q, K, V, offs, pos
+
+
+@pytest.mark.parametrize("m", [1, 5, 17])
+def test_dhsa_decode_is_prefill_row_of_the_cut_sequence(m):
+    # A decode step at position pos, whose current chunk holds b_n..pos, is
+    # prefill row pos of the sequence cut at pos + 1 with the current chunk as
+    # its last chunk: same pooled query/key, same scores, same kept set.
+    H, d, Nb = 2, 8, 57
+    Q, K, V, offs, pos = _dhsa_decode_case(19, 400, d, H, 4, 20, 14, m)
+    dec = oracle.dhsa_decode(Q[:, :, offs[-1]: pos + 1], K, V, offs, Nb, want_kept=True)
+    assert dec["pos"] == pos
+    cut = np.append(offs, pos + 1).astype(np.int32)
+    pre = oracle.dhsa_prefill(Q[:, :, : pos + 1], K[:, :, : pos + 1], V[:, :, : pos + 1], cut, Nb,
+                              rows=[pos], want_kept=True, want_sc=True)
+    np.testing.assert_array_equal(dec["out"], pre["out"][:, :, 0])
+    np.testing.assert_array_equal(dec["kept"], pre["kept"][:, :, 0])
+    np.testing.assert_array_equal(dec["sc"], pre["sc"][:, :, len(offs) - 1])
+    np.testing.assert_array_equal(dec["margin"], pre["margin"][:, :, 0])
+    assert (dec["n_kept"] == min(Nb, pos + 1)).all()
+
+
+def test_dhsa_decode_budget_covering_everything_is_dense():
+    H, d = 3, 8
+    Q, K, V, offs, pos = _dhsa_decode_case(20, 300, d, H, 3, 15, 11, 4)
+    dec = oracle.dhsa_decode(Q[:, :, offs[-1]: pos + 1], K, V, offs, budget=pos + 1)
+    for h in range(H):
+        q = Q[0, h, pos].astype(np.float64)
+        k = K[0, h, : pos + 1].astype(np.float64)
+        ref = softmax(k @ q / math.sqrt(d)) @ V[0, h, : pos + 1].astype(np.float64)
+        np.testing.assert_allclose(dec["out"][0, h], ref, rtol=0, atol=1e-12)
+    assert np.isinf(dec["margin"]).all()
+
+
+def test_dhsa_decode_unit_chunks_is_topk_token_attention():
+    # Complete chunks and the current chunk of one token each: q_hat is the
+    # new query and k_hat_j the key, so the kept set is the N_b largest q.k_j.
+    N, d, Nb, pos = 80, 8, 11, 61
+    Q, K, V = (f32((1, 1, N, d), 21, t) for t in (synth.TID_Q, synth.TID_K, synth.TID_V))
+    offs = np.arange(pos + 1, dtype=np.int32)
+    dec = oracle.dhsa_decode(Q[:, :, pos: pos + 1], K, V, offs, Nb, want_kept=True)
+    q, k, v = Q[0, 0, pos].astype(np.float64), K[0, 0].astype(np.float64), V[0, 0]
+    raw = k[: pos + 1] @ q
+    keep = np.lexsort((np.arange(pos + 1), -raw))[:Nb]
+    mask = np.zeros(pos + 1, np.uint8)
+    mask[keep] = 1
+    np.testing.assert_array_equal(dec["kept"][0, 0], mask)
+    ref = softmax(raw[keep] / math.sqrt(d)) @ v[keep].astype(np.float64)
+    np.testing.assert_allclose(dec["out"][0, 0], ref, rtol=0, atol=1e-12)
+
+
+def test_dhsa_chunk_keys_closed_forms():
+    # constant keys u in a chunk of length c pool to sqrt(c) * u; pooling is
+    # linear; a key outside every complete chunk changes nothing
+    d = 4
+    u = np.array([1.0, -2.0, 0.5, 3.0], np.float32)
+    offs = np.array([0, 4, 13, 29], np.int32)
+    K = np.broadcast_to(u, (1, 1, 40, d)).copy()
+    kh = oracle.dhsa_chunk_keys(K, offs)
+    for k, c in enumerate(np.diff(offs)):
+        np.testing.assert_allclose(kh[0, 0, k], math.sqrt(c) * u.astype(np.float64),
+                                   rtol=1e-15, atol=0)
+    rng = np.random.default_rng(3)
+    K1 = rng.integers(-8, 8, (2, 3, 40, d)).astype(np.float32)
+    K2 = rng.integers(-8, 8, (2, 3, 40, d)).astype(np.float32)
+    lhs = oracle.dhsa_chunk_keys((3 * K1 - K2).astype(np.float32), offs)
+    rhs = 3 * oracle.dhsa_chunk_keys(K1, offs) - oracle.dhsa_chunk_keys(K2, offs)
+    np.testing.assert_allclose(lhs, rhs, rtol=0, atol=1e-12)
+    K3 = K1.copy()
+    K3[:, :, 35] += 7
+    np.testing.assert_array_equal(oracle.dhsa_chunk_keys(K3, offs), oracle.dhsa_chunk_keys(K1, offs))
