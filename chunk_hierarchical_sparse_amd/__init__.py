@@ -70,6 +70,12 @@ def load_library():
         "dhsa_prefill_workspace_size": ([_I, _L, _I, _I, _I, _I], _Z),
         "dhsa_prefill": ([_P, _P, _P, _P, _I, _L, _P, _P, _P, _I, _L, _I, _I, _I, _P, _Z, _P],
                          _I),
+        "dhsa_chunk_keys_workspace_size": ([_I], _Z),
+        "dhsa_build_chunk_keys": ([_P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I, _I, _P, _Z, _P],
+                                  _I),
+        "dhsa_decode_workspace_size": ([_I, _I, _I, _I], _Z),
+        "dhsa_decode": ([_P, _I, _P, _P, _L, _P, _I, _P, _I, _L, _P, _P, _I, _I, _I, _I, _P, _Z,
+                         _P], _I),
         "hsa_profile_enable": ([_I], _I),
         "hsa_profile_read": ([_P, _I, _P], _I),
     }
@@ -255,6 +261,71 @@ def dhsa_prefill(Q, K, V, offsets, budget, out=None, return_mask=False, return_o
     if return_order:
         res.append(order)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def dhsa_build_chunk_keys(K, offsets, chunk_begin=0, chunk_end=None, khat=None, n_cap=None):
+    """Pooled keys of the complete chunks given by host offsets [n+1]:
+    fp32 [B,H,n_cap,d] (default n_cap = n), row k = (sum of chunk k's keys)
+    / sqrt|C_k|.  With `khat` given, only chunks chunk_begin..chunk_end-1
+    are (re)written in place."""
+    import numpy as np
+    _need(K, "K", 4)
+    B, H, n_max, d = K.shape
+    offs = np.ascontiguousarray(offsets, dtype=np.int32)
+    n = len(offs) - 1
+    if chunk_end is None:
+        chunk_end = n
+    if khat is None:
+        n_cap = n if n_cap is None else n_cap
+        khat = torch.zeros((B, H, max(n_cap, 1), d), dtype=torch.float32, device=K.device)
+    else:
+        _need(khat, "khat", 4, torch.float32)
+        n_cap = khat.shape[2]
+    lib = load_library()
+    nbytes = lib.dhsa_chunk_keys_workspace_size(chunk_end - chunk_begin)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    _check(lib.dhsa_build_chunk_keys(K.data_ptr(), khat.data_ptr(), offs.ctypes.data, n,
+                                     chunk_begin, chunk_end, B, H, n_max, d, n_cap,
+                                     _dtype_code(K), ws.data_ptr(), nbytes, _stream(K)))
+    return khat
+
+
+def dhsa_decode_workspace_size(B, H, d, n_chunks):
+    return load_library().dhsa_decode_workspace_size(B, H, d, n_chunks)
+
+
+def dhsa_decode(q_cur, Kc, Vc, khat, offsets, budget, out=None, return_order=False,
+                workspace=None):
+    """DHSA decode of the new query at position offsets[-1] + m - 1.
+    q_cur [B,H,m,d]: the current chunk's queries (new query last); Kc, Vc
+    [B,H,n_max,d] caches; khat fp32 [B,H,n_cap,d] (dhsa_build_chunk_keys);
+    offsets: host int32 boundaries [n+1] of the complete chunks; budget N_b.
+
+    Returns o [B,H,d], plus the chunk order int32 [B,H,n+1] when requested."""
+    import numpy as np
+    _need(q_cur, "q_cur", 4)
+    _need(Kc, "Kc", 4, q_cur.dtype)
+    _need(Vc, "Vc", 4, q_cur.dtype)
+    _need(khat, "khat", 4, torch.float32)
+    B, H, m, d = q_cur.shape
+    n_max = Kc.shape[2]
+    if Kc.shape != (B, H, n_max, d) or Vc.shape != Kc.shape:
+        raise ValueError("Kc and Vc must be [B,H,n_max,d] like q_cur")
+    offs = np.ascontiguousarray(offsets, dtype=np.int32)
+    n = len(offs) - 1
+    if out is None:
+        out = torch.empty((B, H, d), dtype=q_cur.dtype, device=q_cur.device)
+    order = None
+    if return_order:
+        order = torch.empty((B, H, n + 1), dtype=torch.int32, device=q_cur.device)
+    lib = load_library()
+    nbytes = lib.dhsa_decode_workspace_size(B, H, d, n)
+    ws = _workspace(nbytes, q_cur.device, workspace) if nbytes else None
+    _check(lib.dhsa_decode(q_cur.data_ptr(), m, Kc.data_ptr(), Vc.data_ptr(), n_max,
+                           khat.data_ptr(), khat.shape[2], offs.ctypes.data, n, budget,
+                           out.data_ptr(), _ptr(order), B, H, d, _dtype_code(q_cur), _ptr(ws),
+                           nbytes, _stream(q_cur)))
+    return (out, order) if return_order else out
 
 
 def hsa_profile_enable(enable=True):

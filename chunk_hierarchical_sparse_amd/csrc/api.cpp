@@ -189,6 +189,38 @@ DhsaLayout dhsa_layout(void* ws, int B, int H, int d, int nc) {
   return p;
 }
 
+struct DhsaDecodeLayout {
+  int32_t* offs;
+  int32_t* plan;
+  int32_t* n_plan;
+  float* part;
+  size_t bytes;
+};
+
+DhsaDecodeLayout dhsa_decode_layout(void* ws, int B, int H, int d, int n_chunks) {
+  Carver cv(ws);
+  DhsaDecodeLayout p;
+  const int64_t BH = (int64_t)B * H, nc = (int64_t)n_chunks + 1;
+  p.offs = cv.take<int32_t>((size_t)nc);
+  p.plan = cv.take<int32_t>((size_t)(BH * nc * 2));
+  p.n_plan = cv.take<int32_t>((size_t)BH);
+  p.part = cv.take<float>((size_t)(BH * nc * (d + 2)));
+  p.bytes = cv.off + kAlign;
+  return p;
+}
+
+// Complete chunks 0..n-1: offsets[0] = 0, strictly increasing, ending at or
+// before `limit`.
+hsa_status_t check_chunk_offsets(const int32_t* offsets, int n, int64_t limit) {
+  if (!offsets) return fail(HSA_ERR_INVALID_ARGUMENT, "offsets must not be NULL");
+  if (offsets[0] != 0) return fail(HSA_ERR_INVALID_ARGUMENT, "offsets must start at 0");
+  for (int k = 0; k < n; ++k)
+    if (offsets[k + 1] <= offsets[k])
+      return fail(HSA_ERR_INVALID_ARGUMENT, "offsets must be strictly increasing");
+  if (offsets[n] > limit) return fail(HSA_ERR_INVALID_ARGUMENT, "offsets run past the cache");
+  return HSA_OK;
+}
+
 void* align_ws(void* ws) {
   return (void*)(((uintptr_t)ws + kAlign - 1) / kAlign * kAlign);
 }
@@ -437,6 +469,116 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
     pm.mark();
     e = hsa::dhsa_stage(a, stage, st);
     if (e != hipSuccess) return hip_fail(e, "dhsa");
+  }
+  pm.mark();
+  return HSA_OK;
+}
+
+size_t dhsa_chunk_keys_workspace_size(int n_chunks) {
+  if (n_chunks < 0) return 0;
+  return ((size_t)n_chunks + 1) * sizeof(int32_t) + kAlign;
+}
+
+hsa_status_t dhsa_build_chunk_keys(const void* K, float* khat, const int32_t* offsets,
+                                   int n_chunks, int chunk_begin, int chunk_end, int B, int H,
+                                   int64_t n_max, int d, int n_cap, hsa_dtype_t dtype,
+                                   void* workspace, size_t workspace_bytes, hsa_stream_t stream) {
+  g_err.clear();
+  if (!dtype_ok(dtype)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (B < 0 || H <= 0 || n_max < 0 || n_chunks < 0 || n_cap < n_chunks)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "need B >= 0, H >= 1, 0 <= n_chunks <= n_cap");
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > n_chunks)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "need 0 <= chunk_begin <= chunk_end <= n_chunks");
+  hsa_status_t s = check_chunk_offsets(offsets, n_chunks, n_max);
+  if (s != HSA_OK) return s;
+  if ((int64_t)B * H * (chunk_end - chunk_begin) >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "too many chunks for one launch");
+  if (B == 0 || chunk_end == chunk_begin) return HSA_OK;
+  if (!K || !khat) return fail(HSA_ERR_INVALID_ARGUMENT, "K and khat must not be NULL");
+  const int cnt = chunk_end - chunk_begin;
+  if (!workspace || workspace_bytes < dhsa_chunk_keys_workspace_size(cnt))
+    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(dhsa_chunk_keys_workspace_size(cnt)) +
+                    " bytes");
+  int32_t* offs = (int32_t*)align_ws(workspace);
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(offs, offsets + chunk_begin, sizeof(int32_t) * (cnt + 1),
+                                hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "offsets upload");
+  e = hsa::launch_dhsa_chunk_keys(K, khat, offs, dt_code(dtype), (int64_t)B * H, n_max, d, n_cap,
+                                  chunk_begin, chunk_end, st);
+  return e == hipSuccess ? HSA_OK : hip_fail(e, "dhsa_build_chunk_keys launch");
+}
+
+size_t dhsa_decode_workspace_size(int B, int H, int d, int n_chunks) {
+  if (B < 0 || H <= 0 || n_chunks < 0 || n_chunks + 1 > hsa::dhsa_max_chunks()) return 0;
+  if (d != 64 && d != 128) return 0;
+  return dhsa_decode_layout(nullptr, B, H, d, n_chunks).bytes;
+}
+
+hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* Vc,
+                         int64_t n_max, const float* khat, int n_cap, const int32_t* offsets,
+                         int n_chunks, int64_t budget, void* o, int32_t* chunk_order, int B,
+                         int H, int d, hsa_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, hsa_stream_t stream) {
+  g_err.clear();
+  if (!dtype_ok(dtype)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (B < 0 || H <= 0) return fail(HSA_ERR_INVALID_ARGUMENT, "need B >= 0 and H >= 1");
+  if (m < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "the current chunk needs m >= 1 queries");
+  if (n_chunks < 0 || n_chunks > n_cap)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "need 0 <= n_chunks <= n_cap");
+  if (n_chunks + 1 > hsa::dhsa_max_chunks())
+    return fail(HSA_ERR_UNSUPPORTED, "n_chunks + 1 must be <= 4096");
+  if (budget < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "budget N_b must be >= 1");
+  if (n_max >= ((int64_t)1 << 31)) return fail(HSA_ERR_UNSUPPORTED, "n_max must be < 2^31");
+  hsa_status_t s = check_chunk_offsets(offsets, n_chunks, n_max);
+  if (s != HSA_OK) return s;
+  const int64_t pos = (int64_t)offsets[n_chunks] + m - 1;
+  if (pos >= n_max) return fail(HSA_ERR_INVALID_ARGUMENT, "the new query lies past the cache");
+  if ((int64_t)B * H * (n_chunks + 1) * (d + 2) >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "B*H*(n_chunks+1)*(d+2) must be < 2^31");
+  if (B == 0) return HSA_OK;
+  if (!q_cur || !Kc || !Vc || !o || (n_chunks > 0 && !khat))
+    return fail(HSA_ERR_INVALID_ARGUMENT, "q_cur, Kc, Vc, o (and khat) must not be NULL");
+  const size_t need = dhsa_decode_layout(nullptr, B, H, d, n_chunks).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(need) + " bytes");
+  DhsaDecodeLayout lay = dhsa_decode_layout(align_ws(workspace), B, H, d, n_chunks);
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(lay.offs, offsets, sizeof(int32_t) * (n_chunks + 1),
+                                hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "offsets upload");
+  hsa::DhsaDecodeArgs a;
+  a.qcur = q_cur;
+  a.Kc = Kc;
+  a.Vc = Vc;
+  a.khat = khat;
+  a.o = o;
+  a.chunk_order = chunk_order;
+  a.offs = lay.offs;
+  a.plan = lay.plan;
+  a.n_plan = lay.n_plan;
+  a.part = lay.part;
+  a.B = B;
+  a.H = H;
+  a.d = d;
+  a.dtype = dt_code(dtype);
+  a.n = n_chunks;
+  a.n_cap = n_cap;
+  a.m = m;
+  a.P = 1;
+  while (a.P < n_chunks + 1) a.P <<= 1;
+  a.n_max = n_max;
+  a.pos = pos;
+  a.budget = budget;
+  StageMarks pm(st);
+  for (int stage = 0; stage < hsa::kDhsaDecodeStages; ++stage) {
+    pm.mark();
+    e = hsa::dhsa_decode_stage(a, stage, st);
+    if (e != hipSuccess) return hip_fail(e, "dhsa_decode");
   }
   pm.mark();
   return HSA_OK;

@@ -104,4 +104,26 @@ constexpr int kDhsaStages = 5;
 hipError_t dhsa_stage(const DhsaArgs& a, int stage, hipStream_t stream);
 int dhsa_max_chunks();
 
+// ---- DHSA decode (dhsa_decode.hip) -----------------------------------------
+struct DhsaDecodeArgs {
+  const void* qcur;     // [B,H,m,d]: queries of the current chunk, last = new query
+  const void* Kc;       // [B,H,n_max,d]
+  const void* Vc;
+  const float* khat;    // [B,H,n_cap,d]: pooled keys of the complete chunks
+  void* o;              // [B,H,d]
+  int32_t* chunk_order; // [B,H,n+1] or null
+  const int32_t* offs;  // [n+1] device copy of the complete chunks' boundaries
+  int32_t* plan;        // [B*H, n+1, 2]: (first token, count) of each kept run
+  int32_t* n_plan;      // [B*H]
+  float* part;          // [B*H, n+1, d+2]: (max, sum, weighted values) per run
+  int B, H, d, dtype, n, n_cap, m, P;
+  int64_t n_max, pos, budget;
+};
+// stages: 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
+constexpr int kDhsaDecodeStages = 3;
+hipError_t dhsa_decode_stage(const DhsaDecodeArgs& a, int stage, hipStream_t stream);
+hipError_t launch_dhsa_chunk_keys(const void* K, float* khat, const int32_t* offs, int dtype,
+                                  int64_t BH, int64_t n_max, int d, int n_cap, int chunk_begin,
+                                  int chunk_end, hipStream_t stream);
+
 }  // namespace hsa

@@ -157,6 +157,51 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
                           hsa_stream_t stream);
 
 /*
+ * DHSA decode, pooled chunk keys ([DHSA] "What carries the argument", Eq. 4):
+ * khat[b,h,k] = (sum of the keys of chunk k) / sqrt|C_k| for the complete
+ * chunks k in [chunk_begin, chunk_end), the cache dhsa_decode scores the new
+ * query against.  Append a chunk when it completes.
+ *   K        [B,H,n_max,d] dtype key cache.
+ *   khat     fp32 [B,H,n_cap,d], rows chunk_begin..chunk_end-1 written.
+ *   offsets  HOST int32 [n_chunks+1]: 0 = b_0 < ... < b_n <= n_max.
+ * The workspace (dhsa_chunk_keys_workspace_size(chunk_end - chunk_begin)
+ * bytes) receives the boundaries of the range.
+ */
+size_t dhsa_chunk_keys_workspace_size(int n_chunks);
+hsa_status_t dhsa_build_chunk_keys(const void* K, float* khat, const int32_t* offsets,
+                                   int n_chunks, int chunk_begin, int chunk_end, int B, int H,
+                                   int64_t n_max, int d, int n_cap, hsa_dtype_t dtype,
+                                   void* workspace, size_t workspace_bytes, hsa_stream_t stream);
+
+/*
+ * DHSA decode ([DHSA] Referee report, minor comment on Algorithm 2: the
+ * decode-time update in which the last chunk holds the current query): the
+ * new query i = b_n + m - 1 sits in the current, partial chunk [b_n, i].
+ * That chunk is pooled like any chunk over the tokens it holds so far:
+ * q_hat = (sum of its m queries) / sqrt(m), k_hat likewise over keys b_n..i.
+ * The n complete chunks (pooled keys from khat) and the current one are
+ * scored by S_c = q_hat . k_hat, every key j <= i takes the score of its
+ * chunk, the first min(N_b, i+1) keys in (score desc, j asc) order are kept
+ * and softmax(q_i . k / sqrt d) attention runs over them; the result equals
+ * dhsa_prefill's row i on the sequence cut at i+1.
+ *   q_cur    [B,H,m,d] dtype: the current chunk's queries, the new one last.
+ *   Kc, Vc   [B,H,n_max,d] dtype caches holding tokens 0..i (the new key and
+ *            value included).
+ *   khat     fp32 [B,H,n_cap,d] from dhsa_build_chunk_keys (rows 0..n-1).
+ *   offsets  HOST int32 [n_chunks+1]: boundaries of the complete chunks.
+ *   o        [B,H,d] dtype, written.
+ *   chunk_order int32 [B,H,n_chunks+1] or NULL: the chunks by (S_c desc,
+ *            index asc); index n_chunks is the current chunk.
+ * Limits: n_chunks + 1 <= 4096, n_max < 2^31.
+ */
+size_t dhsa_decode_workspace_size(int B, int H, int d, int n_chunks);
+hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* Vc,
+                         int64_t n_max, const float* khat, int n_cap, const int32_t* offsets,
+                         int n_chunks, int64_t budget, void* o, int32_t* chunk_order, int B,
+                         int H, int d, hsa_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, hsa_stream_t stream);
+
+/*
  * Profiling aid (not part of the method).  While enabled on the calling
  * thread, each hsa_prefill, hsa_decode and dhsa_prefill call records a HIP
  * event on its stream before each of its stages and one after the last:
@@ -164,6 +209,7 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
  *   hsa_decode  : 0 scan (landmark stream, per-slice top-K), 1 attend (merge
  *                 of the slices' candidates, chunk attention), 2 fuse
  *   dhsa_prefill: 0 pool, 1 S_c, 2 rank, 3 attend, 4 mask
+ *   dhsa_decode : 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
  * hsa_profile_read waits for the recorded events, adds the elapsed
  * milliseconds of stage s summed over all recorded calls into stage_ms[s]
  * (s < max_stages; the caller zeroes the array), releases the events and

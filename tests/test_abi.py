@@ -149,3 +149,57 @@ def test_python_layer_rejects_host_tensors():
     q = torch.zeros(1, 2, 64, 64)
     with pytest.raises(ValueError):
         hsa.hsa_prefill(q, q, q, 16, 2)
+
+
+def _offs(vals):
+    import numpy as np
+    a = np.asarray(vals, dtype=np.int32)
+    return a, a.ctypes.data
+
+
+def dhsa_decode_call(**kw):
+    offs, optr = _offs(kw.pop("offsets", [0, 4, 9, 20]))
+    a = dict(q=1, m=3, K=1, V=1, n_max=64, khat=1, n_cap=8, n=len(offs) - 1, budget=16, o=1,
+             B=1, H=2, d=128, dt=BF16, ws=None, wsb=0, optr=optr)
+    a.update(kw)
+    return lib().dhsa_decode(a["q"], a["m"], a["K"], a["V"], a["n_max"], a["khat"], a["n_cap"],
+                             a["optr"], a["n"], a["budget"], a["o"], None, a["B"], a["H"], a["d"],
+                             a["dt"], a["ws"], a["wsb"], None)
+
+
+def test_dhsa_decode_validation():
+    assert dhsa_decode_call(m=0) == INV
+    assert dhsa_decode_call(d=96) == UNS
+    assert dhsa_decode_call(dt=7) == UNS
+    assert dhsa_decode_call(budget=0) == INV
+    assert dhsa_decode_call(n_cap=2) == INV
+    assert dhsa_decode_call(offsets=[1, 4, 9, 20]) == INV and "start at 0" in msg()
+    assert dhsa_decode_call(offsets=[0, 4, 4, 20]) == INV and "increasing" in msg()
+    assert dhsa_decode_call(m=50) == INV and "past the cache" in msg()
+    assert dhsa_decode_call(q=None) == INV and "NULL" in msg()
+    assert dhsa_decode_call(offsets=list(range(0, 5000)), n_cap=5000, n_max=1 << 20) == UNS
+    assert dhsa_decode_call() == WS and "workspace needs" in msg()
+    need = lib().dhsa_decode_workspace_size(1, 2, 128, 3)
+    assert need > 0
+    assert dhsa_decode_call(ws=1 << 20, wsb=need - 1) == WS
+
+
+def test_dhsa_build_chunk_keys_validation():
+    offs, optr = _offs([0, 4, 9, 20])
+
+    def call(**kw):
+        a = dict(K=1, khat=1, n=3, cb=0, ce=3, B=1, H=2, n_max=64, d=128, n_cap=3, dt=BF16,
+                 ws=None, wsb=0, optr=optr)
+        a.update(kw)
+        return lib().dhsa_build_chunk_keys(a["K"], a["khat"], a["optr"], a["n"], a["cb"],
+                                           a["ce"], a["B"], a["H"], a["n_max"], a["d"],
+                                           a["n_cap"], a["dt"], a["ws"], a["wsb"], None)
+
+    assert call(ce=4) == INV
+    assert call(cb=2, ce=1) == INV
+    assert call(n_cap=2) == INV
+    assert call(n_max=10) == INV and "past the cache" in msg()
+    assert call(d=64 + 1) == UNS
+    assert call(K=None) == INV
+    assert call() == WS
+    assert call(cb=1, ce=1) == 0  # empty range: nothing to do
