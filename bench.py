@@ -6,9 +6,9 @@ already resident in HBM.  The headline workload is HSA prefill at B=1,
 L=32768, 16 query heads over 4 KV heads, d=128, S=64, top-8, bf16: landmark
 pooling, scoring + top-K, chunk attention and fusion, all inside the timed
 call.  By default the decode workloads (batch 32 with 131072-token caches;
-batch 1 with a 16,777,216-token cache and a planted needle) and the DHSA
-prefill workload (L=16384, N_b=2048) are measured too and reported under
-"also".
+batch 1 with a 16,777,216-token cache and a planted needle), the DHSA
+prefill workload (L=16384, N_b=2048) and DHSA decode (that sequence decoding
+its last token, batch 32) are measured too and reported under "also".
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -41,6 +41,8 @@ DOMINANT = {
                        ["decode.hip", "hsa_common.h", "kernels.h"]),
     "dhsa_prefill": ("attend_kernel<128>", "DhsaArgs",
                      ["dhsa.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
+    "dhsa_decode": ("attend_kernel<128, 1>", "DhsaDecodeArgs",
+                    ["dhsa_decode.hip", "hsa_common.h", "kernels.h"]),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_workloads.txt")
 
@@ -247,6 +249,56 @@ def bench_dhsa(torch, hsa, args):
     return res
 
 
+def bench_dhsa_decode(torch, hsa, args):
+    """The 16K-token DHSA sequence decoding its last token (its last chunk is
+    the current one), batch 32, 8 heads, N_b = 2048."""
+    import synth
+    B, H, L, d, budget, seed = 32, 8, 16384, 128, 2048, 5
+    offs_all = synth.chunk_offsets(L, 16, 128, seed=seed)
+    offs = offs_all[:-1]
+    n = len(offs) - 1
+    m = int(offs_all[-1] - offs_all[-2])
+    log(f"dhsa decode: filling caches on the device (B={B}, L={L})")
+    Kc = torch.empty((B, H, L, d), dtype=torch.bfloat16, device="cuda")
+    Vc = torch.empty_like(Kc)
+    synth.normal_device(Kc, seed, synth.TID_K)
+    synth.normal_device(Vc, seed, synth.TID_V)
+    qcur = to_dev(synth.normal((B, H, m, d), synth.BF16, seed, synth.TID_QDEC), torch)
+    khat = hsa.dhsa_build_chunk_keys(Kc, offs)
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(hsa.dhsa_decode_workspace_size(B, H, d, n, budget, L), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        hsa.dhsa_decode(qcur, Kc, Vc, khat, offs, budget, out=out, workspace=ws)
+
+    log("dhsa decode: timing")
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 3)
+    pos = L - 1
+    kept = min(budget, pos + 1)
+    kv_bytes = B * H * kept * d * 2 * 2            # the kept keys and values
+    khat_bytes = B * H * n * d * 4                 # pooled keys of the complete chunks
+    cur_bytes = B * H * m * d * 2 * 2              # current chunk's queries and keys
+    total = kv_bytes + khat_bytes + cur_bytes + B * H * d * 2
+    achieved = kv_bytes / (stages[1] * 1e-3) / 1e9
+    res = dict(
+        value=B / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
+        config={"workload": "dhsa_decode", "B": B, "H": H, "d": d, "context": L,
+                "complete_chunks": n, "current_chunk": m, "budget": budget,
+                "inputs": "N(0,1) bf16, lengths U{16..128}, seed 5"},
+        roofline={"bound": "hbm", "kernel": "attend (gather of the kept keys and values)",
+                  "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                  "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_for("dhsa_decode"),
+                  "algorithmic_bytes_per_launch": kv_bytes, "avg_launch_ms": stages[1]},
+        stages_ms=dict(zip(["score", "attend", "combine"], stages)),
+        whole_path={"algorithmic_bytes": total, "gbps": total / (ms * 1e-3) / 1e9,
+                    "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+    del Kc, Vc, qcur, khat, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(inputs, target_s):
     """The oracle as it is, timed on this host's cores on evenly spaced query
     positions of the prefill workload (every head), scaled to queries/s."""
@@ -332,8 +384,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--extras", default="decode,decode16m,dhsa",
-                    help="comma list of extra workloads: decode, decode16m, dhsa, or none")
+    ap.add_argument("--extras", default="decode,decode16m,dhsa,dhsa_decode",
+                    help="comma list of extra workloads: decode, decode16m, dhsa, dhsa_decode, "
+                         "or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -372,6 +425,8 @@ def main():
             also.append(bench_decode(torch, hsa, args, big=True))
         elif e == "dhsa":
             also.append(bench_dhsa(torch, hsa, args))
+        elif e == "dhsa_decode":
+            also.append(bench_dhsa_decode(torch, hsa, args))
         else:
             raise SystemExit(f"unknown extra workload {e}")
     if also:

@@ -73,7 +73,7 @@ def load_library():
         "dhsa_chunk_keys_workspace_size": ([_I], _Z),
         "dhsa_build_chunk_keys": ([_P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I, _I, _P, _Z, _P],
                                   _I),
-        "dhsa_decode_workspace_size": ([_I, _I, _I, _I], _Z),
+        "dhsa_decode_workspace_size": ([_I, _I, _I, _I, _L, _L], _Z),
         "dhsa_decode": ([_P, _I, _P, _P, _L, _P, _I, _P, _I, _L, _P, _P, _I, _I, _I, _I, _P, _Z,
                          _P], _I),
         "hsa_profile_enable": ([_I], _I),
@@ -290,8 +290,8 @@ def dhsa_build_chunk_keys(K, offsets, chunk_begin=0, chunk_end=None, khat=None, 
     return khat
 
 
-def dhsa_decode_workspace_size(B, H, d, n_chunks):
-    return load_library().dhsa_decode_workspace_size(B, H, d, n_chunks)
+def dhsa_decode_workspace_size(B, H, d, n_chunks, budget, n_max):
+    return load_library().dhsa_decode_workspace_size(B, H, d, n_chunks, budget, n_max)
 
 
 def dhsa_decode(q_cur, Kc, Vc, khat, offsets, budget, out=None, return_order=False,
@@ -319,7 +319,7 @@ def dhsa_decode(q_cur, Kc, Vc, khat, offsets, budget, out=None, return_order=Fal
     if return_order:
         order = torch.empty((B, H, n + 1), dtype=torch.int32, device=q_cur.device)
     lib = load_library()
-    nbytes = lib.dhsa_decode_workspace_size(B, H, d, n)
+    nbytes = lib.dhsa_decode_workspace_size(B, H, d, n, budget, n_max)
     ws = _workspace(nbytes, q_cur.device, workspace) if nbytes else None
     _check(lib.dhsa_decode(q_cur.data_ptr(), m, Kc.data_ptr(), Vc.data_ptr(), n_max,
                            khat.data_ptr(), khat.shape[2], offs.ctypes.data, n, budget,

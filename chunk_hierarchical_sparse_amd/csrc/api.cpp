@@ -197,16 +197,21 @@ struct DhsaDecodeLayout {
   size_t bytes;
 };
 
-DhsaDecodeLayout dhsa_decode_layout(void* ws, int B, int H, int d, int n_chunks) {
+DhsaDecodeLayout dhsa_decode_layout(void* ws, int B, int H, int d, int n_chunks,
+                                    int64_t max_pieces) {
   Carver cv(ws);
   DhsaDecodeLayout p;
   const int64_t BH = (int64_t)B * H, nc = (int64_t)n_chunks + 1;
   p.offs = cv.take<int32_t>((size_t)nc);
-  p.plan = cv.take<int32_t>((size_t)(BH * nc * 2));
+  p.plan = cv.take<int32_t>((size_t)(BH * max_pieces * 2));
   p.n_plan = cv.take<int32_t>((size_t)BH);
-  p.part = cv.take<float>((size_t)(BH * nc * (d + 2)));
+  p.part = cv.take<float>((size_t)(BH * max_pieces * (d + 2)));
   p.bytes = cv.off + kAlign;
   return p;
+}
+
+int64_t dhsa_decode_pieces(int n_chunks, int64_t budget, int64_t n_max) {
+  return hsa::dhsa_decode_max_pieces(budget < n_max ? budget : n_max, n_chunks);
 }
 
 // Complete chunks 0..n-1: offsets[0] = 0, strictly increasing, ending at or
@@ -511,10 +516,13 @@ hsa_status_t dhsa_build_chunk_keys(const void* K, float* khat, const int32_t* of
   return e == hipSuccess ? HSA_OK : hip_fail(e, "dhsa_build_chunk_keys launch");
 }
 
-size_t dhsa_decode_workspace_size(int B, int H, int d, int n_chunks) {
+size_t dhsa_decode_workspace_size(int B, int H, int d, int n_chunks, int64_t budget,
+                                  int64_t n_max) {
   if (B < 0 || H <= 0 || n_chunks < 0 || n_chunks + 1 > hsa::dhsa_max_chunks()) return 0;
   if (d != 64 && d != 128) return 0;
-  return dhsa_decode_layout(nullptr, B, H, d, n_chunks).bytes;
+  if (budget < 1 || n_max < 1) return 0;
+  return dhsa_decode_layout(nullptr, B, H, d, n_chunks, dhsa_decode_pieces(n_chunks, budget, n_max))
+      .bytes;
 }
 
 hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* Vc,
@@ -537,16 +545,17 @@ hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* V
   if (s != HSA_OK) return s;
   const int64_t pos = (int64_t)offsets[n_chunks] + m - 1;
   if (pos >= n_max) return fail(HSA_ERR_INVALID_ARGUMENT, "the new query lies past the cache");
-  if ((int64_t)B * H * (n_chunks + 1) * (d + 2) >= ((int64_t)1 << 31))
-    return fail(HSA_ERR_UNSUPPORTED, "B*H*(n_chunks+1)*(d+2) must be < 2^31");
+  const int64_t pieces = dhsa_decode_pieces(n_chunks, budget, n_max);
+  if ((int64_t)B * H * pieces * (d + 2) >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "B*H*(min(budget, n_max)/64 + n_chunks + 2)*(d+2) must be < 2^31");
   if (B == 0) return HSA_OK;
   if (!q_cur || !Kc || !Vc || !o || (n_chunks > 0 && !khat))
     return fail(HSA_ERR_INVALID_ARGUMENT, "q_cur, Kc, Vc, o (and khat) must not be NULL");
-  const size_t need = dhsa_decode_layout(nullptr, B, H, d, n_chunks).bytes;
+  const size_t need = dhsa_decode_layout(nullptr, B, H, d, n_chunks, pieces).bytes;
   if (!workspace || workspace_bytes < need)
     return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
                 "workspace needs " + std::to_string(need) + " bytes");
-  DhsaDecodeLayout lay = dhsa_decode_layout(align_ws(workspace), B, H, d, n_chunks);
+  DhsaDecodeLayout lay = dhsa_decode_layout(align_ws(workspace), B, H, d, n_chunks, pieces);
   const hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(lay.offs, offsets, sizeof(int32_t) * (n_chunks + 1),
                                 hipMemcpyHostToDevice, st);
@@ -571,6 +580,7 @@ hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* V
   a.m = m;
   a.P = 1;
   while (a.P < n_chunks + 1) a.P <<= 1;
+  a.max_pieces = (int)pieces;
   a.n_max = n_max;
   a.pos = pos;
   a.budget = budget;

@@ -9,12 +9,15 @@
 //  1. score      : one block per (b, head): pooled query and key of the
 //                  current chunk, S_c = q_hat . k_hat over the complete chunks
 //                  and the current one, chunks ranked by (S_c desc, index asc)
-//                  in LDS, and the top-N_b cut as a plan of key runs (whole
-//                  chunks in rank order, then the lowest tokens of one).
-//  2. attend     : one block per (b, head, run): softmax partials (max, sum,
-//                  weighted values) of the new query over the run's keys.
-//  3. combine    : per (b, head): the runs' partials into the output.
+//                  in LDS, and the top-N_b cut as runs of keys (whole chunks
+//                  in rank order, then the lowest tokens of one), split into
+//                  pieces of at most 64 keys.
+//  2. attend     : one wave per (b, head, piece): softmax partials (max, sum,
+//                  weighted values) of the new query over the piece's keys.
+//  3. combine    : per (b, head): the pieces' partials into the output.
 #include <math.h>
+
+#include <type_traits>
 
 #include "hsa_common.h"
 #include "kernels.h"
@@ -23,6 +26,7 @@ namespace hsa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPiece = 64;  // keys per attention piece (one per lane)
 
 // out[x] = (sum of rows [0, nrows) of src, row stride D) / sqrt(nrows), in
 // LDS.  Thread t sums column piece t % (D / VE) over rows t / (D / VE),
@@ -82,27 +86,36 @@ __global__ void __launch_bounds__(kThreads) chunk_keys_kernel(const void* K, flo
 template <int D, int DT>
 __global__ void __launch_bounds__(kThreads) score_kernel(DhsaDecodeArgs a) {
   __shared__ float scratch[kThreads * (DT == kF32 ? 4 : 8)];
-  __shared__ float qh[D], kc[D];
+  __shared__ __attribute__((aligned(16))) float qh[D], kc[D];
   __shared__ int32_t part[kThreads];
   __shared__ int s_pw;
   extern __shared__ uint64_t dyn[];
   uint64_t* keys = dyn;                      // [P]
   int32_t* cum = (int32_t*)(dyn + a.P);      // [P + 1]
   const int64_t bh = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x;
   const int n = a.n, nc = a.n + 1;           // complete chunks, plus the current one
   const int cur0 = a.offs[n];                // first token of the current chunk
   pool_rows<D, DT>(a.qcur, bh * a.m, a.m, qh, scratch);
   pool_rows<D, DT>(a.Kc, bh * a.n_max + cur0, a.m, kc, scratch);
-  // S_c[k] = q_hat . k_hat_k: one wave per chunk, lanes split the columns
-  constexpr int CPL = D / 64;
-  for (int k = w; k < nc; k += kThreads / kWave) {
-    const float* kr = k < n ? a.khat + (bh * a.n_cap + k) * D : kc;
+  // S_c[k] = q_hat . k_hat_k: one thread per chunk, its row's loads all in
+  // flight at once (the pooled-key stream is this kernel's HBM traffic)
+  for (int k = tid; k < nc; k += kThreads) {
+    f32x4 r[D / 4];
+    if (k < n) {
+      const f32x4* kr = (const f32x4*)(a.khat + (bh * a.n_cap + k) * D);
+#pragma unroll
+      for (int x = 0; x < D / 4; ++x) r[x] = kr[x];
+    } else {
+#pragma unroll
+      for (int x = 0; x < D / 4; ++x) r[x] = *(const f32x4*)(&kc[4 * x]);
+    }
     float s = 0.f;
 #pragma unroll
-    for (int x = 0; x < CPL; ++x) s += qh[CPL * lane + x] * kr[CPL * lane + x];
-    s = wave_sum(s);
-    if (lane == 0) keys[k] = select_key(s, (uint32_t)k);
+    for (int x = 0; x < D / 4; ++x)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s += qh[4 * x + v] * r[x][v];
+    keys[k] = select_key(s, (uint32_t)k);
   }
   for (int i = nc + tid; i < a.P; i += kThreads) keys[i] = 0ull;
   __syncthreads();
@@ -166,135 +179,188 @@ __global__ void __launch_bounds__(kThreads) score_kernel(DhsaDecodeArgs a) {
   __syncthreads();
   const int pw = s_pw;
   const int rem = (int)(keep - cum[pw]);
-  int32_t* plan = a.plan + bh * nc * 2;
-  for (int p = tid; p < nc; p += kThreads) {
+  // runs: p < pw whole chunks, p == pw the first rem tokens; each run is
+  // cut into pieces of kPiece keys, numbered by an exclusive scan over runs
+  auto run_of = [&](int p, int& start, int& count) {
     const int k = (int)key_index(keys[p]);
-    const int start = a.offs[k];  // the current chunk starts at offs[n]
-    if (p < pw) {
-      plan[2 * p] = start;
-      plan[2 * p + 1] = k < n ? a.offs[k + 1] - start : a.m;
-    } else if (p == pw && rem > 0) {
-      plan[2 * p] = start;
-      plan[2 * p + 1] = rem;
-    }
-    if (a.chunk_order) a.chunk_order[bh * nc + p] = k;
+    start = a.offs[k];  // the current chunk starts at offs[n]
+    count = p < pw ? (k < n ? a.offs[k + 1] - start : a.m) : (p == pw ? rem : 0);
+  };
+  int32_t pieces = 0;
+  for (int p = p0; p < min(p0 + per, nc); ++p) {
+    int st, cnt;
+    run_of(p, st, cnt);
+    pieces += (cnt + kPiece - 1) / kPiece;
   }
-  if (tid == 0) a.n_plan[bh] = pw + (pw < nc && rem > 0 ? 1 : 0);
+  __syncthreads();
+  part[tid] = pieces;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t acc = 0;
+    for (int t = 0; t < kThreads; ++t) {
+      const int32_t v = part[t];
+      part[t] = acc;
+      acc += v;
+    }
+    a.n_plan[bh] = acc;
+  }
+  __syncthreads();
+  int32_t q = part[tid];
+  int32_t* plan = a.plan + bh * a.max_pieces * 2;
+  for (int p = p0; p < min(p0 + per, nc); ++p) {
+    int st, cnt;
+    run_of(p, st, cnt);
+    for (int c0 = 0; c0 < cnt; c0 += kPiece, ++q) {
+      plan[2 * q] = st + c0;
+      plan[2 * q + 1] = min(kPiece, cnt - c0);
+    }
+  }
+  if (a.chunk_order)
+    for (int p = tid; p < nc; p += kThreads) a.chunk_order[bh * nc + p] = (int)key_index(keys[p]);
 }
 
-// One block per (b, head, run of the plan): keys [start, start + count),
-// 64 per wave step; lane = key for the logit, lane = column pair for the
-// weighted value sum (weights broadcast from LDS).
+// One wave per (b, head, piece of at most 64 keys): every load of the piece
+// is issued at once, the key rows with lane = key and the value rows with
+// lane = column pair (values stay packed until used); the weights pass
+// through LDS.  Writes the piece's (max, sum, weighted values).
 template <int D, int DT>
-__global__ void __launch_bounds__(kThreads) attend_kernel(DhsaDecodeArgs a, float scale) {
+__global__ void __launch_bounds__(kWave) attend_kernel(DhsaDecodeArgs a, float scale) {
   __shared__ float qs[D];
-  __shared__ __attribute__((aligned(16))) float ps[kThreads / kWave][kWave];
-  __shared__ float wm[kThreads / kWave], wl[kThreads / kWave];
-  __shared__ float wo[kThreads / kWave][D];
-  const int nc = a.n + 1;
-  const int64_t bh = blockIdx.x / nc;
-  const int p = blockIdx.x % nc;
-  if (p >= a.n_plan[bh]) return;
-  const int start = a.plan[(bh * nc + p) * 2], count = a.plan[(bh * nc + p) * 2 + 1];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ __attribute__((aligned(16))) float ps[kPiece];
+  const int64_t bh = blockIdx.x / a.max_pieces;
+  const int q = (int)(blockIdx.x % a.max_pieces);
+  if (q >= a.n_plan[bh]) return;
+  const int start = a.plan[(bh * a.max_pieces + q) * 2];
+  const int nk = a.plan[(bh * a.max_pieces + q) * 2 + 1];
+  const int lane = threadIdx.x;
   constexpr int CPL = D / 64;
   constexpr int VE = DT == kF32 ? 4 : 8;
-  for (int x = tid; x < D; x += kThreads)
-    qs[x] = load_elem<DT>(a.qcur, (bh * a.m + a.m - 1) * D + x);
-  __syncthreads();
+  constexpr int EB = DT == kF32 ? 4 : 2;
   const int64_t kv0 = bh * a.n_max * D;
-  float m = -INFINITY, l = 0.f, o[CPL];
+  // keys past nk re-read the piece's last key (in bounds, weight zero)
+  const int64_t row = start + min(lane, nk - 1);
+  u32x4 kx[D / VE];
 #pragma unroll
-  for (int x = 0; x < CPL; ++x) o[x] = 0.f;
-  for (int j0 = kWave * w; j0 < count; j0 += kThreads) {
-    const int nk = min(kWave, count - j0);
-    const int64_t row = start + j0 + lane;
-    float dot = -INFINITY;
-    if (lane < nk) {
-      float acc = 0.f;
+  for (int x = 0; x < D / VE; ++x)
+    kx[x] = *(const u32x4*)((const char*)a.Kc + (kv0 + row * D + x * VE) * EB);
+  // value columns CPL*lane .. +CPL-1 of every key of the piece
+  typedef typename std::conditional<
+      DT == kF32, typename std::conditional<CPL == 2, f32x2, float>::type,
+      typename std::conditional<CPL == 2, uint32_t, uint16_t>::type>::type VT;
+  VT vv[kPiece];
 #pragma unroll
-      for (int x = 0; x < D; x += VE) {
-        if (DT == kF32) {
-          const f32x4 k4 = *(const f32x4*)((const float*)a.Kc + kv0 + row * D + x);
+  for (int jj = 0; jj < kPiece; ++jj)
+    vv[jj] = *(const VT*)((const char*)a.Vc +
+                          (kv0 + (int64_t)(start + min(jj, nk - 1)) * D + CPL * lane) * EB);
+  for (int x = lane; x < D; x += kWave)
+    qs[x] = load_elem<DT>(a.qcur, (bh * a.m + a.m - 1) * D + x);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float dot = -INFINITY;
+  if (lane < nk) {
+    float acc = 0.f;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc += qs[x + v] * k4[v];
-        } else {
-          const u32x4 k8 = *(const u32x4*)((const uint16_t*)a.Kc + kv0 + row * D + x);
+    for (int x = 0; x < D / VE; ++x) {
+      if constexpr (DT == kF32) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            acc += qs[x + 2 * v] * bf16_bits_to_f32(k8[v] & 0xffffu);
-            acc += qs[x + 2 * v + 1] * bf16_bits_to_f32(k8[v] >> 16);
-          }
+        for (int v = 0; v < 4; ++v) acc += qs[x * VE + v] * __uint_as_float(kx[x][v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          acc += qs[x * VE + 2 * v] * bf16_bits_to_f32(kx[x][v] & 0xffffu);
+          acc += qs[x * VE + 2 * v + 1] * bf16_bits_to_f32(kx[x][v] >> 16);
         }
       }
-      dot = acc * scale;
     }
-    const float mn = fmaxf(m, wave_max(dot));
-    const float al = expf(m - mn);
-    const float pj = lane < nk ? expf(dot - mn) : 0.f;
-    l = l * al + wave_sum(pj);
-    m = mn;
-#pragma unroll
-    for (int x = 0; x < CPL; ++x) o[x] *= al;
-    ps[w][lane] = pj;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int jj = 0; jj < nk; ++jj) {
-      const float pw = ps[w][jj];
-      const int64_t e = kv0 + (start + j0 + jj) * D + CPL * lane;
-#pragma unroll
-      for (int x = 0; x < CPL; ++x) o[x] += pw * load_elem<DT>(a.Vc, e + x);
-    }
-    __builtin_amdgcn_wave_barrier();
+    dot = acc * scale;
   }
+  const float m = wave_max(dot);
+  const float pj = lane < nk ? expf(dot - m) : 0.f;
+  const float l = wave_sum(pj);
+  ps[lane] = pj;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float o[CPL];
+#pragma unroll
+  for (int x = 0; x < CPL; ++x) o[x] = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < kPiece; ++jj) {
+    const float pw = ps[jj];  // zero past nk
+    if constexpr (DT == kF32 && CPL == 2) {
+      o[0] += pw * vv[jj][0];
+      o[1] += pw * vv[jj][1];
+    } else if constexpr (DT == kF32) {
+      o[0] += pw * vv[jj];
+    } else if constexpr (CPL == 2) {
+      o[0] += pw * bf16_bits_to_f32(vv[jj] & 0xffffu);
+      o[1] += pw * bf16_bits_to_f32(vv[jj] >> 16);
+    } else {
+      o[0] += pw * bf16_bits_to_f32(vv[jj]);
+    }
+  }
+  float* part = a.part + (bh * a.max_pieces + q) * (D + 2);
   if (lane == 0) {
-    wm[w] = m;
-    wl[w] = l;
+    part[0] = m;
+    part[1] = l;
   }
-#pragma unroll
-  for (int x = 0; x < CPL; ++x) wo[w][CPL * lane + x] = o[x];
-  __syncthreads();
-  float* part = a.part + (bh * nc + p) * (D + 2);
-  float M = -INFINITY;
-  for (int v = 0; v < kThreads / kWave; ++v) M = fmaxf(M, wm[v]);
-  for (int x = tid; x < D + 1; x += kThreads) {
-    float acc = 0.f;
-    for (int v = 0; v < kThreads / kWave; ++v) {
-      if (wm[v] == -INFINITY) continue;  // a wave without keys
-      acc += (x < D ? wo[v][x] : wl[v]) * expf(wm[v] - M);
-    }
-    if (x < D)
-      part[2 + x] = acc;
-    else
-      part[1] = acc;
-  }
-  if (tid == 0) part[0] = M;
+  if constexpr (CPL == 2)
+    *(f32x2*)(part + 2 + 2 * lane) = f32x2{o[0], o[1]};
+  else
+    part[2 + lane] = o[0];
 }
 
-// Per (b, head): out = sum_p o_p e^(m_p - M) / sum_p l_p e^(m_p - M).
+// Per (b, head): out = sum_q o_q e^(m_q - M) / sum_q l_q e^(m_q - M) over
+// the pieces q; each thread's loads are issued 8 at a time.
 template <int D, int DT>
 __global__ void __launch_bounds__(D) combine_kernel(DhsaDecodeArgs a) {
-  const int nc = a.n + 1;
+  __shared__ float red[D];
+  __shared__ float s_M, s_L;
   const int64_t bh = blockIdx.x;
   const int np = a.n_plan[bh];
-  const float* part = a.part + bh * nc * (D + 2);
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, part[p * (D + 2)]);
-  float L = 0.f, O = 0.f;
+  const float* part = a.part + bh * a.max_pieces * (D + 2);
   const int x = threadIdx.x;
-  for (int p = 0; p < np; ++p) {
-    const float f = expf(part[p * (D + 2)] - M);
-    L += part[p * (D + 2) + 1] * f;
-    O += part[p * (D + 2) + 2 + x] * f;
+  float M = -INFINITY;
+  for (int q = x; q < np; q += D) M = fmaxf(M, part[q * (D + 2)]);
+  red[x] = M;
+  __syncthreads();
+  if (x == 0) {
+    for (int t = 1; t < D; ++t) M = fmaxf(M, red[t]);
+    s_M = M;
   }
-  store_elem<DT>(a.o, bh * D + x, np > 0 ? O / L : 0.f);
+  __syncthreads();
+  M = s_M;
+  float L = 0.f;
+  for (int q = x; q < np; q += D) L += part[q * (D + 2) + 1] * expf(part[q * (D + 2)] - M);
+  __syncthreads();
+  red[x] = L;
+  __syncthreads();
+  if (x == 0) {
+    float t = 0.f;
+    for (int i = 0; i < D; ++i) t += red[i];
+    s_L = t;
+  }
+  float O = 0.f;
+  int q = 0;
+  for (; q + 8 <= np; q += 8) {
+    float v[8], f[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u] = part[(q + u) * (D + 2) + 2 + x];
+      f[u] = part[(q + u) * (D + 2)];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) O += v[u] * expf(f[u] - M);
+  }
+  for (; q < np; ++q) O += part[q * (D + 2) + 2 + x] * expf(part[q * (D + 2)] - M);
+  __syncthreads();
+  store_elem<DT>(a.o, bh * D + x, np > 0 ? O / s_L : 0.f);
 }
 
 template <int D, int DT>
 hipError_t decode_dt(const DhsaDecodeArgs& a, int stage, hipStream_t stream) {
   const int64_t BH = (int64_t)a.B * a.H;
-  const int nc = a.n + 1;
   switch (stage) {
     case 0:
       score_kernel<D, DT><<<dim3((unsigned)BH), dim3(kThreads),
@@ -302,7 +368,7 @@ hipError_t decode_dt(const DhsaDecodeArgs& a, int stage, hipStream_t stream) {
                             stream>>>(a);
       break;
     case 1:
-      attend_kernel<D, DT><<<dim3((unsigned)(BH * nc)), dim3(kThreads), 0, stream>>>(
+      attend_kernel<D, DT><<<dim3((unsigned)(BH * a.max_pieces)), dim3(kWave), 0, stream>>>(
           a, 1.0f / sqrtf((float)D));
       break;
     default:
@@ -313,6 +379,11 @@ hipError_t decode_dt(const DhsaDecodeArgs& a, int stage, hipStream_t stream) {
 }
 
 }  // namespace
+
+int64_t dhsa_decode_max_pieces(int64_t keep_max, int n_chunks) {
+  // each kept run (at most n_chunks + 1) adds at most one partial piece
+  return (keep_max + kPiece - 1) / kPiece + n_chunks + 1;
+}
 
 hipError_t dhsa_decode_stage(const DhsaDecodeArgs& a, int stage, hipStream_t stream) {
   if (a.d == 64)

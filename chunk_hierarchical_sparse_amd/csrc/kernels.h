@@ -113,14 +113,16 @@ struct DhsaDecodeArgs {
   void* o;              // [B,H,d]
   int32_t* chunk_order; // [B,H,n+1] or null
   const int32_t* offs;  // [n+1] device copy of the complete chunks' boundaries
-  int32_t* plan;        // [B*H, n+1, 2]: (first token, count) of each kept run
-  int32_t* n_plan;      // [B*H]
-  float* part;          // [B*H, n+1, d+2]: (max, sum, weighted values) per run
-  int B, H, d, dtype, n, n_cap, m, P;
+  int32_t* plan;        // [B*H, max_pieces, 2]: (first token, count <= 64) of each piece
+  int32_t* n_plan;      // [B*H]: pieces in use
+  float* part;          // [B*H, max_pieces, d+2]: (max, sum, weighted values) per piece
+  int B, H, d, dtype, n, n_cap, m, P, max_pieces;
   int64_t n_max, pos, budget;
 };
 // stages: 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
 constexpr int kDhsaDecodeStages = 3;
+// pieces of at most 64 keys the kept keys can need
+int64_t dhsa_decode_max_pieces(int64_t keep_max, int n_chunks);
 hipError_t dhsa_decode_stage(const DhsaDecodeArgs& a, int stage, hipStream_t stream);
 hipError_t launch_dhsa_chunk_keys(const void* K, float* khat, const int32_t* offs, int dtype,
                                   int64_t BH, int64_t n_max, int d, int n_cap, int chunk_begin,

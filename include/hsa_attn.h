@@ -192,9 +192,11 @@ hsa_status_t dhsa_build_chunk_keys(const void* K, float* khat, const int32_t* of
  *   o        [B,H,d] dtype, written.
  *   chunk_order int32 [B,H,n_chunks+1] or NULL: the chunks by (S_c desc,
  *            index asc); index n_chunks is the current chunk.
- * Limits: n_chunks + 1 <= 4096, n_max < 2^31.
+ * Limits: n_chunks + 1 <= 4096, n_max < 2^31.  The workspace size depends on
+ * the budget and the cache capacity n_max as passed to dhsa_decode.
  */
-size_t dhsa_decode_workspace_size(int B, int H, int d, int n_chunks);
+size_t dhsa_decode_workspace_size(int B, int H, int d, int n_chunks, int64_t budget,
+                                  int64_t n_max);
 hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* Vc,
                          int64_t n_max, const float* khat, int n_cap, const int32_t* offsets,
                          int n_chunks, int64_t budget, void* o, int32_t* chunk_order, int B,

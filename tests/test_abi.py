@@ -178,8 +178,9 @@ def test_dhsa_decode_validation():
     assert dhsa_decode_call(m=50) == INV and "past the cache" in msg()
     assert dhsa_decode_call(q=None) == INV and "NULL" in msg()
     assert dhsa_decode_call(offsets=list(range(0, 5000)), n_cap=5000, n_max=1 << 20) == UNS
+    assert dhsa_decode_call(B=1 << 20, H=64, budget=1 << 20, n_max=1 << 21) == UNS
     assert dhsa_decode_call() == WS and "workspace needs" in msg()
-    need = lib().dhsa_decode_workspace_size(1, 2, 128, 3)
+    need = lib().dhsa_decode_workspace_size(1, 2, 128, 3, 16, 64)
     assert need > 0
     assert dhsa_decode_call(ws=1 << 20, wsb=need - 1) == WS
 
