@@ -30,7 +30,7 @@ def lib():
         L = ctypes.CDLL(_build.LIB)
         L.oracle_landmarks.argtypes = [_P, ctypes.c_int, _I, _I, _I, _I, _I, _P]
         L.oracle_hsa_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _I, _I, _I,
-                                         _P, _I, ctypes.c_int, _P, _P, _P, _P, _P]
+                                         _P, _I, ctypes.c_int, _I, _P, _P, _P, _P, _P]
         L.oracle_hsa_decode_select.argtypes = [_P, ctypes.c_int, _P, _I, _I, _I, _I, _I, _I,
                                                _I, _I, _P, _P, _P]
         L.oracle_hsa_decode_attend.argtypes = [_P, _P, _P, ctypes.c_int, _P, _P, _I, _I, _I,
@@ -85,8 +85,11 @@ def landmarks(K, S):
     return out
 
 
-def hsa_prefill(Q, K, V, S, topk, rows=None, include_current_chunk=False, want_out=True):
-    """HSA prefill for query positions `rows` (default: all).
+def hsa_prefill(Q, K, V, S, topk, rows=None, include_current_chunk=False, want_out=True,
+                retrieval_interval=1):
+    """HSA prefill for query positions `rows` (default: all).  With
+    retrieval_interval R > 1, row t reuses the selection made at
+    t0 = (t // R) * R (sel, margin and sel_score describe that selection).
 
     Returns dict(out [B,Hq,R,d], sel [B,Hkv,R,K], w [B,Hq,R,K], margin [B,Hkv,R],
     sel_score [B,Hkv,R,K] group-summed score of each selected chunk)."""
@@ -107,7 +110,8 @@ def hsa_prefill(Q, K, V, S, topk, rows=None, include_current_chunk=False, want_o
     sel_score = np.zeros((B, Hkv, R, topk), np.float64)
     rc = lib().oracle_hsa_prefill(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dt, B, L, Hq,
                                   Hkv, d, S, topk, _ptr(rows_a), R, int(include_current_chunk),
-                                  _ptr(out), _ptr(sel), _ptr(w), _ptr(margin), _ptr(sel_score))
+                                  int(retrieval_interval), _ptr(out), _ptr(sel), _ptr(w),
+                                  _ptr(margin), _ptr(sel_score))
     _check(rc, "hsa_prefill")
     return dict(out=out, sel=sel, w=w, margin=margin, sel_score=sel_score)
 

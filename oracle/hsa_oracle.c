@@ -170,13 +170,23 @@ static double attend_rows(const double* q, const void* K, const void* V, int dty
  * Any output pointer may be NULL.  include_current_chunk (oracle-only switch
  * used to pin the dense-causal reduction) also makes the chunk holding t
  * available, with its keys restricted to j <= t.
+ *
+ * interval R >= 1 is the retrieval interval ([HSA] Key Contributions 4 and
+ * Main Findings: retrieval refreshed every R tokens, per-token vs per-8-token
+ * retrieval).  Row t reuses the selection made at the first token of its
+ * block, t0 = floor(t/R)*R: the chunks available at t0 ranked by the group
+ * sum of q_t0 . lambda_c / sqrt(d).  The row then attends inside those
+ * chunks with its own query and fuses with its own per-head scores.  R = 1
+ * is per-token retrieval.  sel, margin and sel_score describe t0's
+ * selection.
  */
 int oracle_hsa_prefill(const void* Q, const void* K, const void* V, int dtype, int64_t B,
                        int64_t L, int64_t Hq, int64_t Hkv, int64_t d, int64_t S, int64_t topk,
                        const int64_t* rows, int64_t n_rows, int include_current_chunk,
-                       double* out, int32_t* sel, double* w, double* margin, double* sel_score) {
+                       int64_t interval, double* out, int32_t* sel, double* w, double* margin,
+                       double* sel_score) {
   if (!Q || !K || !V || B < 0 || L < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 ||
-      S <= 0 || topk <= 0)
+      S <= 0 || topk <= 0 || interval <= 0)
     return OR_EINVAL;
   if (!rows) n_rows = L;
   const int64_t G = Hq / Hkv;
@@ -194,9 +204,10 @@ int oracle_hsa_prefill(const void* Q, const void* K, const void* V, int dtype, i
     cand_t* cand = (cand_t*)malloc((size_t)(n + 1) * sizeof(cand_t));
     double* sh = (double*)malloc((size_t)(G * (n + 1)) * sizeof(double));
     double* qv = (double*)malloc((size_t)(G * d) * sizeof(double));
+    double* qs = (double*)malloc((size_t)(G * d) * sizeof(double));
     double* oc = (double*)malloc((size_t)d * sizeof(double));
     double* work = (double*)malloc((size_t)(S + 1) * sizeof(double));
-    if (!cand || !sh || !qv || !oc || !work) {
+    if (!cand || !sh || !qv || !qs || !oc || !work) {
 #pragma omp atomic write
       err = OR_ENOMEM;
     } else {
@@ -205,25 +216,30 @@ int oracle_hsa_prefill(const void* Q, const void* K, const void* V, int dtype, i
         for (int64_t g = 0; g < Hkv; ++g)
           for (int64_t r = 0; r < n_rows; ++r) {
             const int64_t t = rows ? rows[r] : r;
+            const int64_t t0 = t / interval * interval;  /* where the selection is made */
             const int64_t kv_base = (b * Hkv + g) * L * d;
-            /* Step 2: available chunks A(t). */
-            int64_t navail = include_current_chunk ? (t / S + 1) : (t / S);
+            /* Step 2: available chunks A(t0). */
+            int64_t navail = include_current_chunk ? (t0 / S + 1) : (t0 / S);
             if (navail > n) navail = n;
             if (navail < 0) navail = 0;
-            /* Query rows of the group's heads. */
+            /* Query rows of the group's heads at t (attention, fusion) and
+             * at t0 (selection). */
             for (int64_t hh = 0; hh < G; ++hh)
-              for (int64_t x = 0; x < d; ++x)
+              for (int64_t x = 0; x < d; ++x) {
                 qv[hh * d + x] = ld(Q, dtype, ((b * Hq + g * G + hh) * L + t) * d + x);
-            /* Step 3: per-head scores s_h(t,c) and the group sum sigma. */
+                qs[hh * d + x] = ld(Q, dtype, ((b * Hq + g * G + hh) * L + t0) * d + x);
+              }
+            /* Step 3: per-head scores s_h(t,c) of the row and the group sum
+             * sigma at t0. */
             for (int64_t c = 0; c < navail; ++c) {
               const double* lc = lmk + ((b * Hkv + g) * n + c) * d;
               double sigma = 0.0;
               for (int64_t hh = 0; hh < G; ++hh) {
-                double s = 0.0;
+                double s = 0.0, s0 = 0.0;
                 for (int64_t x = 0; x < d; ++x) s += qv[hh * d + x] * lc[x];
-                s *= sc;
-                sh[hh * (n + 1) + c] = s;
-                sigma += s;
+                for (int64_t x = 0; x < d; ++x) s0 += qs[hh * d + x] * lc[x];
+                sh[hh * (n + 1) + c] = s * sc;
+                sigma += s0 * sc;
               }
               cand[c].score = sigma;
               cand[c].idx = c;
@@ -277,6 +293,7 @@ int oracle_hsa_prefill(const void* Q, const void* K, const void* V, int dtype, i
     free(cand);
     free(sh);
     free(qv);
+    free(qs);
     free(oc);
     free(work);
   }

@@ -465,3 +465,65 @@ def test_dhsa_chunk_keys_closed_forms():
     K3 = K1.copy()
     K3[:, :, 35] += 7
     np.testing.assert_array_equal(oracle.dhsa_chunk_keys(K3, offs), oracle.dhsa_chunk_keys(K1, offs))
+
+
+# ------------------------------------------- retrieval every R tokens
+
+
+def test_interval_S1_all_chunks_is_dense_attention_before_the_block():
+    # S = 1 and K >= L: row t keeps every token before its block start
+    # t0 = (t // R) * R and fuses softmax(q_t . k_j / sqrt d) over them:
+    # dense attention of q_t over j < t0 (rows of the first block output 0).
+    B, Hq, Hkv, L, d, R = 1, 4, 2, 40, 16, 8
+    Q = f32((B, Hq, L, d), 22, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 22, synth.TID_K)
+    V = f32((B, Hkv, L, d), 22, synth.TID_V)
+    r = oracle.hsa_prefill(Q, K, V, S=1, topk=L, retrieval_interval=R)
+    for h in range(Hq):
+        q, k, v = Q[0, h].astype(np.float64), K[0, h // 2].astype(np.float64), V[0, h // 2]
+        for t in range(L):
+            t0 = t // R * R
+            if t0 == 0:
+                assert not r["out"][0, h, t].any()
+                continue
+            ref = softmax(k[:t0] @ q[t] / math.sqrt(d)) @ v[:t0].astype(np.float64)
+            np.testing.assert_allclose(r["out"][0, h, t], ref, rtol=0, atol=1e-12)
+
+
+def test_interval_S1_topk_selects_with_the_block_start_query():
+    # S = 1, K < L, one head: the K tokens with the largest q_t0 . k_j among
+    # j < t0 (ties lower j) are kept for the whole block; each row attends
+    # over them with its own query.
+    L, d, K_, R = 48, 8, 5, 4
+    Q = f32((1, 1, L, d), 23, synth.TID_Q)
+    K = f32((1, 1, L, d), 23, synth.TID_K)
+    V = f32((1, 1, L, d), 23, synth.TID_V)
+    r = oracle.hsa_prefill(Q, K, V, S=1, topk=K_, retrieval_interval=R)
+    q, k, v = (a[0, 0].astype(np.float64) for a in (Q, K, V))
+    for t in range(L):
+        t0 = t // R * R
+        if t0 == 0:
+            assert not r["out"][0, 0, t].any()
+            continue
+        keep = np.lexsort((np.arange(t0), -(k[:t0] @ q[t0])))[:K_]
+        assert list(r["sel"][0, 0, t][: len(keep)]) == list(keep)
+        ref = softmax(k[keep] @ q[t] / math.sqrt(d)) @ v[keep]
+        np.testing.assert_allclose(r["out"][0, 0, t], ref, rtol=0, atol=1e-12)
+
+
+def test_interval_shares_the_selection_of_the_block_start():
+    # every row of a block carries the per-token selection of its first row,
+    # and at the first rows the output is the per-token output
+    B, Hq, Hkv, L, d, S, K_, R = 1, 4, 2, 640, 16, 16, 4, 8
+    Q = f32((B, Hq, L, d), 24, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 24, synth.TID_K)
+    V = f32((B, Hkv, L, d), 24, synth.TID_V)
+    r8 = oracle.hsa_prefill(Q, K, V, S=S, topk=K_, retrieval_interval=R)
+    r1 = oracle.hsa_prefill(Q, K, V, S=S, topk=K_)
+    for t in range(L):
+        t0 = t // R * R
+        np.testing.assert_array_equal(r8["sel"][:, :, t], r1["sel"][:, :, t0])
+        np.testing.assert_array_equal(r8["margin"][:, :, t], r1["margin"][:, :, t0])
+    starts = np.arange(0, L, R)
+    np.testing.assert_array_equal(r8["out"][:, :, starts], r1["out"][:, :, starts])
+    np.testing.assert_array_equal(r8["w"][:, :, starts], r1["w"][:, :, starts])
