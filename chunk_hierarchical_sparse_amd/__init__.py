@@ -64,6 +64,9 @@ def load_library():
         "hsa_prefill_workspace_size": ([_I, _L, _I, _I, _I, _I, _I, _I], _Z),
         "hsa_prefill": ([_P, _P, _P, _P, _P, _P, _P, _I, _L, _I, _I, _I, _I, _I, _I, _P, _Z,
                          _P], _I),
+        "hsa_prefill_interval_workspace_size": ([_I, _L, _I, _I, _I, _I, _I, _I, _I], _Z),
+        "hsa_prefill_interval": ([_P, _P, _P, _P, _P, _P, _P, _I, _L, _I, _I, _I, _I, _I, _I,
+                                  _I, _P, _Z, _P], _I),
         "hsa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _L], _Z),
         "hsa_decode": ([_P, _P, _P, _P, _L, _L, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _Z,
                         _P], _I),
@@ -180,6 +183,48 @@ def hsa_prefill(Q, K, V, S, topk, lmk=None, out=None, return_selection=False, wo
     _check(lib.hsa_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr(lmk), out.data_ptr(),
                            _ptr(sel_idx), _ptr(sel_w), B, L, Hq, Hkv, d, S, topk, code, _ptr(ws),
                            nbytes, _stream(Q)))
+    if return_selection:
+        return out, sel_idx, sel_w
+    return out
+
+
+def hsa_prefill_interval_workspace_size(B, L, Hq, Hkv, d, S, topk, interval, dtype):
+    code = _dtype_code(torch.empty(0, dtype=dtype))
+    return load_library().hsa_prefill_interval_workspace_size(B, L, Hq, Hkv, d, S, topk,
+                                                              interval, code)
+
+
+def hsa_prefill_interval(Q, K, V, S, topk, interval, lmk=None, out=None,
+                         return_selection=False, workspace=None):
+    """HSA prefill with retrieval every `interval` tokens (token t reuses the
+    selection made at (t // interval) * interval).
+
+    Returns O [B,Hq,L,d]; with return_selection also sel_idx int32
+    [B,Hkv,ceil(L/interval),topk] (one selection per block, -1 padded) and
+    sel_w fp32 [B,Hq,L,topk]."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, Q.dtype)
+    _need(V, "V", 4, Q.dtype)
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (B, Hkv, L, d) or V.shape != K.shape:
+        raise ValueError("K and V must be [B,Hkv,L,d] matching Q")
+    if lmk is not None:
+        _need(lmk, "lmk", 4, torch.float32)
+    if out is None:
+        out = torch.empty_like(Q)
+    sel_idx = sel_w = None
+    if return_selection:
+        nq = (L + interval - 1) // interval
+        sel_idx = torch.empty((B, Hkv, nq, topk), dtype=torch.int32, device=Q.device)
+        sel_w = torch.empty((B, Hq, L, topk), dtype=torch.float32, device=Q.device)
+    lib = load_library()
+    code = _dtype_code(Q)
+    nbytes = lib.hsa_prefill_interval_workspace_size(B, L, Hq, Hkv, d, S, topk, interval, code)
+    ws = _workspace(nbytes, Q.device, workspace) if nbytes else None
+    _check(lib.hsa_prefill_interval(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr(lmk),
+                                    out.data_ptr(), _ptr(sel_idx), _ptr(sel_w), B, L, Hq, Hkv, d,
+                                    S, topk, interval, code, _ptr(ws), nbytes, _stream(Q)))
     if return_selection:
         return out, sel_idx, sel_w
     return out

@@ -110,13 +110,14 @@ struct PrefillLayout {
 };
 
 PrefillLayout prefill_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d, int S,
-                             int topk, hsa_dtype_t dt) {
+                             int topk, hsa_dtype_t dt, int interval = 1) {
   Carver cv(ws);
   PrefillLayout p;
   const int64_t n = L / S;
   const int64_t BG = (int64_t)B * Hkv;
+  const int64_t nq = (L + interval - 1) / interval;
   p.lmk = cv.take<float>((size_t)(BG * n * d));
-  p.idx = cv.take<int32_t>((size_t)(BG * L * topk));
+  p.idx = cv.take<int32_t>((size_t)(BG * nq * topk));
   p.counts = cv.take<int32_t>((size_t)(BG * n));
   p.cursor = cv.take<int32_t>((size_t)(BG * n));
   p.offs = cv.take<int32_t>((size_t)(BG * (n + 1)));
@@ -273,20 +274,26 @@ size_t hsa_prefill_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int 
   return prefill_layout(nullptr, B, L, Hq, Hkv, d, S, topk, dtype).bytes;
 }
 
-hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const float* lmk,
-                         void* O, int32_t* sel_idx, float* sel_w, int B, int64_t L, int Hq,
-                         int Hkv, int d, int S, int topk, hsa_dtype_t dtype, void* workspace,
-                         size_t workspace_bytes, hsa_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+hsa_status_t prefill_impl(const void* Q, const void* K, const void* V, const float* lmk,
+                          void* O, int32_t* sel_idx, float* sel_w, int B, int64_t L, int Hq,
+                          int Hkv, int d, int S, int topk, int interval, hsa_dtype_t dtype,
+                          void* workspace, size_t workspace_bytes, hsa_stream_t stream) {
   g_err.clear();
   hsa_status_t s = check_prefill(B, L, Hq, Hkv, d, S, topk, dtype);
   if (s != HSA_OK) return s;
+  if (interval < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "the retrieval interval must be >= 1");
   if (B == 0 || L == 0) return HSA_OK;
   if (!Q || !K || !V || !O) return fail(HSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must not be NULL");
-  const size_t need = prefill_layout(nullptr, B, L, Hq, Hkv, d, S, topk, dtype).bytes;
+  const size_t need = prefill_layout(nullptr, B, L, Hq, Hkv, d, S, topk, dtype, interval).bytes;
   if (!workspace || workspace_bytes < need)
     return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
                 "workspace needs " + std::to_string(need) + " bytes");
-  PrefillLayout lay = prefill_layout(align_ws(workspace), B, L, Hq, Hkv, d, S, topk, dtype);
+  PrefillLayout lay =
+      prefill_layout(align_ws(workspace), B, L, Hq, Hkv, d, S, topk, dtype, interval);
   const hipStream_t st = (hipStream_t)stream;
   const int64_t n = L / S;
   const int G = Hq / Hkv;
@@ -320,6 +327,8 @@ hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const floa
   a.log2G = -1;
   for (int k = 0; k < 6; ++k)
     if ((1 << k) == G) a.log2G = k;
+  a.interval = interval;
+  a.nq = (L + interval - 1) / interval;
   a.tiles_ub = lay.tiles_ub;
   if ((int64_t)B * Hkv * a.tiles_ub >= ((int64_t)1 << 31))
     return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
@@ -340,6 +349,33 @@ hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const floa
   if ((e = hsa::prefill_fuse(a, st)) != hipSuccess) return hip_fail(e, "fuse");
   pm.mark();
   return HSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const float* lmk,
+                         void* O, int32_t* sel_idx, float* sel_w, int B, int64_t L, int Hq,
+                         int Hkv, int d, int S, int topk, hsa_dtype_t dtype, void* workspace,
+                         size_t workspace_bytes, hsa_stream_t stream) {
+  return prefill_impl(Q, K, V, lmk, O, sel_idx, sel_w, B, L, Hq, Hkv, d, S, topk, 1, dtype,
+                      workspace, workspace_bytes, stream);
+}
+
+size_t hsa_prefill_interval_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S,
+                                           int topk, int interval, hsa_dtype_t dtype) {
+  if (interval < 1 || check_prefill(B, L, Hq, Hkv, d, S, topk, dtype) != HSA_OK) return 0;
+  return prefill_layout(nullptr, B, L, Hq, Hkv, d, S, topk, dtype, interval).bytes;
+}
+
+hsa_status_t hsa_prefill_interval(const void* Q, const void* K, const void* V, const float* lmk,
+                                  void* O, int32_t* sel_idx, float* sel_w, int B, int64_t L,
+                                  int Hq, int Hkv, int d, int S, int topk, int interval,
+                                  hsa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                  hsa_stream_t stream) {
+  return prefill_impl(Q, K, V, lmk, O, sel_idx, sel_w, B, L, Hq, Hkv, d, S, topk, interval,
+                      dtype, workspace, workspace_bytes, stream);
 }
 
 size_t hsa_decode_workspace_size(int B, int Hq, int Hkv, int d, int S, int topk,

@@ -31,7 +31,7 @@ struct PrefillArgs {
   const void* V;
   const float* lmk;   // [B,Hkv,n,d]
   void* O;            // [B,Hq,L,d]
-  int32_t* idx;       // [B,Hkv,L,topk]
+  int32_t* idx;       // [B,Hkv,nq,topk]: selection of each selection row
   float* sel_w;       // [B,Hq,L,topk] or null
   int32_t* counts;    // [B*Hkv, n]
   int32_t* cursor;    // [B*Hkv, n]
@@ -47,6 +47,8 @@ struct PrefillArgs {
   int entries_per_tile;  // selection entries (token, slot) per attention work unit
   int64_t tiles_ub;      // upper bound of work units per (b, group)
   int log2G;             // log2(Hq/Hkv) when it is a power of two, else -1
+  int interval;          // retrieval interval R: token t uses selection row t / R
+  int64_t nq;            // selection rows, ceil(L / R)
 };
 // A selection entry of the per-chunk lists: token << kSlotBits | slot.
 constexpr int kSlotBits = 5;  // topk <= 32

@@ -94,10 +94,12 @@ __global__ void __launch_bounds__(kThreads) select_valu_kernel(PrefillArgs a, in
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int G = a.Hq / a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t t = qt * 64 + lane;
-  const bool tvalid = t < a.L;
+  // selection rows are the tokens t = row * interval (every token at 1)
+  const int64_t tq = qt * 64 + lane;
+  const int64_t t = tq * a.interval;
+  const bool tvalid = tq < a.nq;
   const int64_t navail = tvalid ? min(t / a.S, a.n) : 0;
-  const int64_t tlast = min(qt * 64 + 63, a.L - 1);
+  const int64_t tlast = min(qt * 64 + 63, a.nq - 1) * a.interval;
   const int64_t bavail = min(tlast / a.S, a.n);
 
   float u[D];
@@ -155,7 +157,7 @@ __global__ void __launch_bounds__(kThreads) select_valu_kernel(PrefillArgs a, in
   for (int ww = 0; ww < 3; ++ww)
     for (int j = 0; j < KM; ++j)
       topk_insert_any<KM>(ls, li, ms[(ww * 64 + lane) * KM + j], mi[(ww * 64 + lane) * KM + j]);
-  int32_t* out = a.idx + (bg * a.L + t) * a.topk;
+  int32_t* out = a.idx + (bg * a.nq + tq) * a.topk;
 #pragma unroll
   for (int j = 0; j < KM; ++j)
     if (j < a.topk) out[j] = li[j];
@@ -194,13 +196,15 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
   const int G = a.Hq / a.Hkv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i32 = lane & 31, hf = lane >> 5;
-  const int64_t t = qt * 128 + w * 32 + i32;
-  const bool tvalid = t < a.L;
+  // selection rows are the tokens t = row * interval (every token at 1)
+  const int64_t tq = qt * 128 + w * 32 + i32;
+  const int64_t t = tq * a.interval;
+  const bool tvalid = tq < a.nq;
   const int64_t navail = tvalid ? min(t / a.S, a.n) : 0;
-  const int64_t tlast_b = min(qt * 128 + 127, a.L - 1);
+  const int64_t tlast_b = min(qt * 128 + 127, a.nq - 1) * a.interval;
   const int64_t bavail = min(tlast_b / a.S, a.n);
-  const int64_t tlast_w = min(qt * 128 + w * 32 + 31, a.L - 1);
-  const int64_t wavail = qt * 128 + w * 32 < a.L ? min(tlast_w / a.S, a.n) : 0;
+  const int64_t tlast_w = min(qt * 128 + w * 32 + 31, a.nq - 1) * a.interval;
+  const int64_t wavail = qt * 128 + w * 32 < a.nq ? min(tlast_w / a.S, a.n) : 0;
 
   // u = sum over the group's heads, dims 16s + 8hf + e, split in 3 parts
   bf16x8 u0[D / 16], u1[D / 16], u2[D / 16];
@@ -299,7 +303,7 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
   if (hf != 0 || !tvalid) return;
 #pragma unroll
   for (int j = 0; j < KM; ++j) topk_insert_any<KM>(ls, li, os[j], oi[j]);
-  int32_t* out = a.idx + (bg * a.L + t) * a.topk;
+  int32_t* out = a.idx + (bg * a.nq + tq) * a.topk;
 #pragma unroll
   for (int j = 0; j < KM; ++j)
     if (j < a.topk) out[j] = li[j];
@@ -362,6 +366,13 @@ __global__ void __launch_bounds__(1024) scan_kernel(PrefillArgs a) {
 }
 
 constexpr int kInvertTokens = 1024;  // tokens per counting / scatter block
+
+// Selection slot of (token, slot) i = token * topk + slot: the row of the
+// token's block start (token / interval) in the selection buffer.
+__device__ __forceinline__ int64_t sel_of(const PrefillArgs& a, int64_t i) {
+  if (a.interval == 1) return i;
+  return (i / a.topk) / a.interval * a.topk + i % a.topk;
+}
 constexpr int kInvertLdsBins = 8192;  // chunks whose counters fit in LDS (2 arrays)
 
 // Per-chunk selection counts.  Each block histograms the selections of
@@ -374,14 +385,14 @@ __global__ void __launch_bounds__(256) count_kernel(PrefillArgs a, int64_t block
   const int64_t bg = blockIdx.x / blocks_per_bg;
   const int64_t t0 = (blockIdx.x % blocks_per_bg) * kInvertTokens;
   const int64_t t1 = min(t0 + kInvertTokens, a.L);
-  const int32_t* idx = a.idx + bg * a.L * a.topk;
+  const int32_t* idx = a.idx + bg * a.nq * a.topk;
   int32_t* cnt = a.counts + bg * a.n;
   if (use_lds) {
     for (int c = threadIdx.x; c < a.n; c += 256) hist[c] = 0;
     __syncthreads();
   }
   for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
-    const int32_t c = idx[i];
+    const int32_t c = idx[sel_of(a, i)];
     if (c < 0) continue;
     if (use_lds)
       atomicAdd(&hist[c], 1);
@@ -406,14 +417,14 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
   const int64_t bg = blockIdx.x / blocks_per_bg;
   const int64_t t0 = (blockIdx.x % blocks_per_bg) * kInvertTokens;
   const int64_t t1 = min(t0 + kInvertTokens, a.L);
-  const int32_t* idx = a.idx + bg * a.L * a.topk;
+  const int32_t* idx = a.idx + bg * a.nq * a.topk;
   const int32_t* offs = a.offs + bg * (a.n + 1);
   int32_t* cursor = a.cursor + bg * a.n;
   int32_t* list = a.list + bg * a.L * a.topk;
   int32_t* epos = a.entry_pos + bg * a.L * a.topk;
   if (!use_lds) {
     for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
-      const int32_t c = idx[i];
+      const int32_t c = idx[sel_of(a, i)];
       if (c >= 0) {
         const int32_t p = offs[c] + atomicAdd(&cursor[c], 1);
         list[p] = (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
@@ -427,7 +438,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
   for (int c = threadIdx.x; c < a.n; c += 256) local[c] = 0;
   __syncthreads();
   for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
-    const int32_t c = idx[i];
+    const int32_t c = idx[sel_of(a, i)];
     if (c >= 0) atomicAdd(&local[c], 1);
   }
   __syncthreads();
@@ -435,7 +446,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
     pos[c] = local[c] != 0 ? offs[c] + atomicAdd(&cursor[c], local[c]) : 0;
   __syncthreads();
   for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
-    const int32_t c = idx[i];
+    const int32_t c = idx[sel_of(a, i)];
     if (c >= 0) {
       const int32_t p = atomicAdd(&pos[c], 1);
       list[p] = (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
@@ -813,7 +824,8 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(PrefillArgs a) {
   const int64_t b = bg / a.Hkv;
   const int h = (int)(bg % a.Hkv) * G + hh;
   const int64_t row = (b * a.Hq + h) * a.L + t;  // output row
-  const int m = (int)min((int64_t)a.topk, min(t / a.S, a.n));
+  const int64_t t0 = t / a.interval * a.interval;  // where the row's selection was made
+  const int m = (int)min((int64_t)a.topk, min(t0 / a.S, a.n));
   const int32_t* epos = a.entry_pos + (bg * a.L + t) * a.topk;
   int64_t pr[KM];
 #pragma unroll
@@ -879,7 +891,7 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(PrefillArgs a) {
 
 template <int D, int KM>
 hipError_t launch_select_dt(const PrefillArgs& a, hipStream_t stream) {
-  const int64_t nqt = (a.L + 63) / 64;
+  const int64_t nqt = (a.nq + 63) / 64;
   const int64_t blocks = (int64_t)a.B * a.Hkv * nqt;
   if (a.dtype == kF32)
     select_valu_kernel<D, KM, kF32><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, nqt);
@@ -891,7 +903,7 @@ hipError_t launch_select_dt(const PrefillArgs& a, hipStream_t stream) {
 
 template <int D, int KM>
 hipError_t launch_select_mfma(const PrefillArgs& a, hipStream_t stream) {
-  const int64_t nqt = (a.L + 127) / 128;
+  const int64_t nqt = (a.nq + 127) / 128;
   const int64_t blocks = (int64_t)a.B * a.Hkv * nqt;
   select_mfma_kernel<D, KM><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, nqt);
   return hipGetLastError();

@@ -109,6 +109,27 @@ hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const floa
                          size_t workspace_bytes, hsa_stream_t stream);
 
 /*
+ * HSA prefill with retrieval every R tokens ([HSA] Key Contributions 4,
+ * Main Findings: per-token vs per-8-token retrieval).  Token t reuses the
+ * chunk selection made at the first token of its block, t0 = floor(t/R)*R:
+ * the chunks fully before t0, ranked by the group sum of q_t0 . lmk / sqrt(d)
+ * (ties: lower index).  Each token then attends inside those chunks with its
+ * own query and fuses the chunk outputs by a softmax over its own per-head
+ * scores, as in hsa_prefill; R = 1 is hsa_prefill.
+ *   sel_idx int32 [B,Hkv,ceil(L/R),topk] or NULL: the selection of each
+ *          block (rank order, -1 padded).
+ *   sel_w  fp32 [B,Hq,L,topk] or NULL: each token's fusion weights.
+ * Other arguments, limits and errors as hsa_prefill; interval >= 1.
+ */
+size_t hsa_prefill_interval_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S,
+                                           int topk, int interval, hsa_dtype_t dtype);
+hsa_status_t hsa_prefill_interval(const void* Q, const void* K, const void* V, const float* lmk,
+                                  void* O, int32_t* sel_idx, float* sel_w, int B, int64_t L,
+                                  int Hq, int Hkv, int d, int S, int topk, int interval,
+                                  hsa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                  hsa_stream_t stream);
+
+/*
  * HSA decode: one new query per sequence at position n_ctx, attending a KV
  * cache of capacity n_max tokens whose first n_ctx are valid.  All
  * floor(n_ctx/S) complete chunks are available.

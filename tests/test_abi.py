@@ -204,3 +204,18 @@ def test_dhsa_build_chunk_keys_validation():
     assert call(K=None) == INV
     assert call() == WS
     assert call(cb=1, ce=1) == 0  # empty range: nothing to do
+
+
+def test_prefill_interval_validation():
+    def call(**kw):
+        a = dict(R=8, B=1, L=256, ws=None, wsb=0)
+        a.update(kw)
+        return lib().hsa_prefill_interval(1, 1, 1, None, 1, None, None, a["B"], a["L"], 4, 2,
+                                          128, 64, 8, a["R"], BF16, a["ws"], a["wsb"], None)
+    assert call(R=0) == INV and "interval" in msg()
+    assert call() == WS
+    n8 = lib().hsa_prefill_interval_workspace_size(1, 256, 4, 2, 128, 64, 8, 8, BF16)
+    n1 = lib().hsa_prefill_interval_workspace_size(1, 256, 4, 2, 128, 64, 8, 1, BF16)
+    assert n1 == lib().hsa_prefill_workspace_size(1, 256, 4, 2, 128, 64, 8, BF16)
+    assert 0 < n8 < n1  # one selection row per block
+    assert lib().hsa_prefill_interval_workspace_size(1, 256, 4, 2, 128, 64, 8, 0, BF16) == 0
