@@ -7,8 +7,9 @@ L=32768, 16 query heads over 4 KV heads, d=128, S=64, top-8, bf16: landmark
 pooling, scoring + top-K, chunk attention and fusion, all inside the timed
 call.  By default the decode workloads (batch 32 with 131072-token caches;
 batch 1 with a 16,777,216-token cache and a planted needle), the DHSA
-prefill workload (L=16384, N_b=2048) and DHSA decode (that sequence decoding
-its last token, batch 32) are measured too and reported under "also".
+prefill workload (L=16384, N_b=2048), DHSA decode (that sequence decoding
+its last token, batch 32) and the 32K prefill with retrieval every 8 tokens
+are measured too and reported under "also".
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -35,6 +36,8 @@ CSRC = os.path.join(ROOT, "chunk_hierarchical_sparse_amd", "csrc")
 DOMINANT = {
     "hsa_prefill": ("attend_chunk_bf16_kernel<128>", "PrefillArgs",
                     ["prefill.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
+    "hsa_prefill_r8": ("attend_chunk_bf16_kernel<128>", "PrefillArgs",
+                       ["prefill.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
     "hsa_decode": ("scan_kernel<128, 1>", "DecodeArgs",
                    ["decode.hip", "hsa_common.h", "kernels.h"]),
     "hsa_decode_16m": ("scan_kernel<128, 1>", "DecodeArgs",
@@ -156,6 +159,43 @@ def bench_prefill(torch, hsa, args):
     del q, k, v, out, ws
     torch.cuda.empty_cache()
     return res, inputs
+
+
+def bench_prefill_interval(torch, hsa, args, inputs, R=8):
+    """The 32K prefill workload with retrieval every R tokens (one selection
+    per block of R tokens, per-token attention and fusion)."""
+    Q, K, V, S, topk = inputs
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    q, k, v = to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch)
+    out = torch.empty_like(q)
+    ws = torch.empty(hsa.hsa_prefill_interval_workspace_size(B, L, Hq, Hkv, d, S, topk, R,
+                                                             torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        hsa.hsa_prefill_interval(q, k, v, S, topk, R, out=out, workspace=ws)
+
+    log(f"prefill, retrieval every {R} tokens: timing")
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 5)
+    n = L // S
+    sel = sum(min(topk, min((t // R * R) // S, n)) for t in range(L))
+    attn_flop = B * Hq * sel * S * d * 4
+    attn_ms = stages[3]
+    achieved = attn_flop / (attn_ms * 1e-3) / 1e12
+    res = dict(
+        value=B * L / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
+        config={"workload": f"hsa_prefill_r{R}", "B": B, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d,
+                "S": S, "topk": topk, "retrieval_interval": R,
+                "inputs": "0.5*N(0,1) bf16, seed 2"},
+        roofline={"bound": "mfma", "kernel": "attend (chunk attention, bf16 MFMA)",
+                  "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("hsa_prefill_r8"),
+                  "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": attn_ms},
+        stages_ms=dict(zip(["landmarks", "select", "invert", "attend", "fuse"], stages)))
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(torch, hsa, args, big=False):
@@ -384,9 +424,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--extras", default="decode,decode16m,dhsa,dhsa_decode",
-                    help="comma list of extra workloads: decode, decode16m, dhsa, dhsa_decode, "
-                         "or none")
+    ap.add_argument("--extras", default="prefill_r8,decode,decode16m,dhsa,dhsa_decode",
+                    help="comma list of extra workloads: prefill_r8, decode, decode16m, dhsa, "
+                         "dhsa_decode, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -419,7 +459,9 @@ def main():
     also = []
     extras = [e for e in args.extras.split(",") if e and e != "none"]
     for e in extras:
-        if e == "decode":
+        if e == "prefill_r8":
+            also.append(bench_prefill_interval(torch, hsa, args, inputs))
+        elif e == "decode":
             also.append(bench_decode(torch, hsa, args))
         elif e == "decode16m":
             also.append(bench_decode(torch, hsa, args, big=True))

@@ -185,6 +185,7 @@ __device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& lo,
 
 template <int D, int KM>
 __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a, int64_t nqt) {
+  constexpr int QPB = 128;  // selection rows per block: 4 waves x 32
   constexpr int TILE = 32;
   constexpr int RS = D + 8;  // padded LDS row (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t lt[3][TILE * RS];
@@ -197,14 +198,14 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i32 = lane & 31, hf = lane >> 5;
   // selection rows are the tokens t = row * interval (every token at 1)
-  const int64_t tq = qt * 128 + w * 32 + i32;
+  const int64_t tq = qt * QPB + w * 32 + i32;
   const int64_t t = tq * a.interval;
   const bool tvalid = tq < a.nq;
   const int64_t navail = tvalid ? min(t / a.S, a.n) : 0;
-  const int64_t tlast_b = min(qt * 128 + 127, a.nq - 1) * a.interval;
+  const int64_t tlast_b = min(qt * QPB + QPB - 1, a.nq - 1) * a.interval;
   const int64_t bavail = min(tlast_b / a.S, a.n);
-  const int64_t tlast_w = min(qt * 128 + w * 32 + 31, a.nq - 1) * a.interval;
-  const int64_t wavail = qt * 128 + w * 32 < a.nq ? min(tlast_w / a.S, a.n) : 0;
+  const int64_t tlast_w = min(qt * QPB + w * 32 + 31, a.nq - 1) * a.interval;
+  const int64_t wavail = qt * QPB + w * 32 < a.nq ? min(tlast_w / a.S, a.n) : 0;
 
   // u = sum over the group's heads, dims 16s + 8hf + e, split in 3 parts
   bf16x8 u0[D / 16], u1[D / 16], u2[D / 16];
@@ -371,7 +372,10 @@ constexpr int kInvertTokens = 1024;  // tokens per counting / scatter block
 // token's block start (token / interval) in the selection buffer.
 __device__ __forceinline__ int64_t sel_of(const PrefillArgs& a, int64_t i) {
   if (a.interval == 1) return i;
-  return (i / a.topk) / a.interval * a.topk + i % a.topk;
+  // per-(b, group) indices stay below L * topk < 2^31: 32-bit division
+  const uint32_t u = (uint32_t)i, k = (uint32_t)a.topk;
+  const uint32_t tok = u / k;
+  return (int64_t)((tok / (uint32_t)a.interval) * k + (u - tok * k));
 }
 constexpr int kInvertLdsBins = 8192;  // chunks whose counters fit in LDS (2 arrays)
 
