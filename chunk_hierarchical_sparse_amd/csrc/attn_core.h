@@ -301,31 +301,34 @@ __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide
     const int nv = nvalid - 32 * t0;  // valid keys of this lane from sub-tile t0 on
     // the valid keys are a prefix, so once no lane has any left none follow
     if (__ballot(nv > 0) == 0) break;
+    // the first k-step takes a zero accumulator operand: no register fill
     f32x16 sc[SUB];
-#pragma unroll
-    for (int t = 0; t < SUB; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
 #pragma unroll
     for (int t = 0; t < SUB; ++t) {
       if (t >= nsub) break;
+      const f32x16 zero = {};
+      const bf16x8 a0 = *(const bf16x8*)(&sm.k[(32 * (t0 + t) + i32) * (D + 8) + 8 * h]);
+      sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, st.qf[0], zero, 0, 0, 0);
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 a0 =
+      for (int s = 1; s < D / 16; ++s) {
+        const bf16x8 a1 =
             *(const bf16x8*)(&sm.k[(32 * (t0 + t) + i32) * (D + 8) + 16 * s + 8 * h]);
-        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, st.qf[s], sc[t], 0, 0, 0);
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, st.qf[s], sc[t], 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // keys at or past nvalid (and padding past nkeys) take no weight
-    if (__ballot(nv < 32 * nsub) != 0) {
+    // keys at or past nvalid (and padding past nkeys) take no weight; only
+    // the sub-tiles some lane's valid keys end in or before need the mask
 #pragma unroll
-      for (int t = 0; t < SUB; ++t)
+    for (int t = 0; t < SUB; ++t) {
+      if (t >= nsub) break;
+      if (__ballot(nv < 32 * (t + 1)) != 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
           if (key >= nv) sc[t][r] = -INFINITY;
         }
+      }
     }
     float mx = -INFINITY;
 #pragma unroll

@@ -271,15 +271,14 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
     if (c0 >= wavail) continue;  // wave-uniform: no query of this wave sees these chunks
     f32x16 acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
     for (int s2 = 0; s2 < D / 16; ++s2) {
       const int off = i32 * RS + 16 * s2 + 8 * hf;
       const bf16x8 l0 = *(const bf16x8*)(&lt[0][off]);
       const bf16x8 l1 = *(const bf16x8*)(&lt[1][off]);
       const bf16x8 l2 = *(const bf16x8*)(&lt[2][off]);
-      // smallest terms first
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l2, u0[s2], acc, 0, 0, 0);
+      const f32x16 zero = {};
+      // smallest terms first; the first takes a zero accumulator operand
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l2, u0[s2], s2 == 0 ? zero : acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, u1[s2], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, u2[s2], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, u0[s2], acc, 0, 0, 0);
@@ -621,26 +620,24 @@ __global__ void __launch_bounds__(kThreads, 2)
   const bool full = a.S == kKeyBlock;  // no key masking needed
   auto compute_tile = [&](int tile, int32_t ent_cur, const u32x4 (&q)[D / 16]) {
     // S^T = K Q^T (keys 0..63) and L^T = LMK3 Q^T (rows 0..2: landmark parts)
+    // the first k-step takes a zero accumulator operand: no register fill
     f32x16 s0, s1, sl;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = 0.f;
-      s1[r] = 0.f;
-      sl[r] = 0.f;
-    }
-#pragma unroll
     for (int s2 = 0; s2 < D / 16; ++s2) {
+      const f32x16 zero = {};
       const bf16x8 qb = __builtin_bit_cast(bf16x8, q[s2]);
       const bf16x8 a0 = *(const bf16x8*)(&sm.k[i32 * (D + 8) + 16 * s2 + 8 * hf]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb, s0, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb, s2 == 0 ? zero : s0, 0, 0, 0);
       if (two) {
         const bf16x8 a1 = *(const bf16x8*)(&sm.k[(32 + i32) * (D + 8) + 16 * s2 + 8 * hf]);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb, s1, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb, s2 == 0 ? zero : s1, 0, 0, 0);
+      } else if (s2 == 0) {
+        s1 = zero;
       }
       u32x4 la = {0u, 0u, 0u, 0u};
       if (i32 < 3) la = *(const u32x4*)(&lsplit[i32][16 * s2 + 8 * hf]);
-      sl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, la), qb, sl, 0,
-                                                   0, 0);
+      sl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, la), qb,
+                                                   s2 == 0 ? zero : sl, 0, 0, 0);
     }
     // rows 0..2 of L^T sit in registers 0..2 of the lanes of half 0
     const float sh = (sl[2] + sl[1]) + sl[0];
