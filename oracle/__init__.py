@@ -40,10 +40,14 @@ def lib():
         L.oracle_dhsa_chunk_keys.argtypes = [_P, ctypes.c_int, _I, _I, _I, _I, _P, _I, _P]
         L.oracle_dhsa_decode.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _I, _P, _I,
                                          _I, _P, _P, _P, _P, _P]
+        L.oracle_swa_prefill.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _I, _I, _P,
+                                         _I, _P]
+        L.oracle_swa_decode.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _I, _I, _I,
+                                        _P]
         L.oracle_num_threads.argtypes = []
         for f in (L.oracle_num_threads, L.oracle_landmarks, L.oracle_hsa_prefill, L.oracle_hsa_decode_select,
                   L.oracle_hsa_decode_attend, L.oracle_dhsa_prefill, L.oracle_dhsa_chunk_keys,
-                  L.oracle_dhsa_decode):
+                  L.oracle_dhsa_decode, L.oracle_swa_prefill, L.oracle_swa_decode):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -246,3 +250,34 @@ def dhsa_decode(Qcur, K, V, offsets, budget, want_kept=False):
                                   margin.ctypes.data)
     _check(rc, "dhsa_decode")
     return dict(out=out, sc=sc, n_kept=n_kept, kept=kept, margin=margin, pos=pos)
+
+
+def swa_prefill(Q, K, V, window, rows=None):
+    """Sliding-window causal attention: row t attends keys
+    max(0, t-window+1) .. t.  Returns out [B,Hq,R,d] float64."""
+    Q, K, V = _c(Q), _c(K), _c(V)
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    if rows is None:
+        R, rows_a = L, None
+    else:
+        rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+        R = len(rows_a)
+    out = np.zeros((B, Hq, R, d), np.float64)
+    rc = lib().oracle_swa_prefill(Q.ctypes.data, K.ctypes.data, V.ctypes.data, _dt(Q, K, V), B,
+                                  L, Hq, Hkv, d, window, _ptr(rows_a), R, out.ctypes.data)
+    _check(rc, "swa_prefill")
+    return out
+
+
+def swa_decode(q, K, V, pos, window):
+    """The query at position pos over cache keys max(0, pos-window+1) .. pos.
+    q [B,Hq,d], K/V [B,Hkv,N,d].  Returns out [B,Hq,d] float64."""
+    q, K, V = _c(q), _c(K), _c(V)
+    B, Hq, d = q.shape
+    Hkv, N = K.shape[1], K.shape[2]
+    out = np.zeros((B, Hq, d), np.float64)
+    rc = lib().oracle_swa_decode(q.ctypes.data, K.ctypes.data, V.ctypes.data, _dt(q, K, V), B,
+                                 Hq, Hkv, d, N, pos, window, out.ctypes.data)
+    _check(rc, "swa_decode")
+    return out

@@ -739,3 +739,79 @@ int oracle_dhsa_decode(const void* Qcur, const void* K, const void* V, int dtype
   free(bnd);
   return err;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sliding-window attention, the local part of the upper layers ([HSA]       */
+/* Methodology: upper layers combine local self-attention with HSA; a 512-   */
+/* token window by default).                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Q [B,Hq,L,d], K and V [B,Hkv,L,d] (head h uses KV head h / (Hq/Hkv)).  Row t
+ * attends keys j in [max(0, t-W+1), t]: out_t = softmax(q_t . k_j / sqrt d) v.
+ *   out [B,Hq,n_rows,d] for the positions rows[0..n_rows) (NULL: all L).
+ */
+int oracle_swa_prefill(const void* Q, const void* K, const void* V, int dtype, int64_t B,
+                       int64_t L, int64_t Hq, int64_t Hkv, int64_t d, int64_t W,
+                       const int64_t* rows, int64_t n_rows, double* out) {
+  if (!Q || !K || !V || !out || B < 0 || L < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 ||
+      W <= 0)
+    return OR_EINVAL;
+  if (!rows) n_rows = L;
+  const int64_t G = Hq / Hkv;
+  int err = OR_OK;
+#pragma omp parallel
+  {
+    double* qv = (double*)malloc((size_t)d * sizeof(double));
+    double* work = (double*)malloc((size_t)(W + 1) * sizeof(double));
+    if (!qv || !work) {
+#pragma omp atomic write
+      err = OR_ENOMEM;
+    } else {
+#pragma omp for collapse(3) schedule(dynamic, 16)
+      for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hq; ++h)
+          for (int64_t r = 0; r < n_rows; ++r) {
+            const int64_t t = rows ? rows[r] : r;
+            for (int64_t x = 0; x < d; ++x) qv[x] = ld(Q, dtype, ((b * Hq + h) * L + t) * d + x);
+            const int64_t j0 = t - W + 1 > 0 ? t - W + 1 : 0;
+            attend_rows(qv, K, V, dtype, (b * Hkv + h / G) * L * d, j0, t + 1, d,
+                        out + ((b * Hq + h) * n_rows + r) * d, work);
+          }
+    }
+    free(qv);
+    free(work);
+  }
+  return err;
+}
+
+/*
+ * One new query per sequence at position pos: q [B,Hq,d], caches
+ * [B,Hkv,N,d] holding tokens 0..pos (pos < N); keys j in
+ * [max(0, pos-W+1), pos].  out [B,Hq,d].
+ */
+int oracle_swa_decode(const void* q, const void* K, const void* V, int dtype, int64_t B,
+                      int64_t Hq, int64_t Hkv, int64_t d, int64_t N, int64_t pos, int64_t W,
+                      double* out) {
+  if (!q || !K || !V || !out || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 || W <= 0 ||
+      pos < 0 || pos >= N)
+    return OR_EINVAL;
+  const int64_t G = Hq / Hkv;
+  double* qv = (double*)malloc((size_t)d * sizeof(double));
+  double* work = (double*)malloc((size_t)(W + 1) * sizeof(double));
+  if (!qv || !work) {
+    free(qv);
+    free(work);
+    return OR_ENOMEM;
+  }
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < Hq; ++h) {
+      for (int64_t x = 0; x < d; ++x) qv[x] = ld(q, dtype, (b * Hq + h) * d + x);
+      const int64_t j0 = pos - W + 1 > 0 ? pos - W + 1 : 0;
+      attend_rows(qv, K, V, dtype, (b * Hkv + h / G) * N * d, j0, pos + 1, d,
+                  out + (b * Hq + h) * d, work);
+    }
+  free(qv);
+  free(work);
+  return OR_OK;
+}

@@ -527,3 +527,52 @@ def test_interval_shares_the_selection_of_the_block_start():
     starts = np.arange(0, L, R)
     np.testing.assert_array_equal(r8["out"][:, :, starts], r1["out"][:, :, starts])
     np.testing.assert_array_equal(r8["w"][:, :, starts], r1["w"][:, :, starts])
+
+
+# -------------------------------------------- sliding-window attention
+
+
+def test_swa_window_covering_everything_is_dense_causal():
+    B, Hq, Hkv, L, d = 1, 4, 2, 50, 8
+    Q = f32((B, Hq, L, d), 25, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 25, synth.TID_K)
+    V = f32((B, Hkv, L, d), 25, synth.TID_V)
+    out = oracle.swa_prefill(Q, K, V, window=L)
+    for h in range(Hq):
+        ref = dense_attention(Q[0, h], K[0, h // 2], V[0, h // 2], causal_strict=False)
+        np.testing.assert_allclose(out[0, h], ref, rtol=0, atol=1e-12)
+
+
+def test_swa_window_of_one_is_the_own_value():
+    Q = f32((2, 2, 30, 8), 26, synth.TID_Q)
+    K = f32((2, 1, 30, 8), 26, synth.TID_K)
+    V = f32((2, 1, 30, 8), 26, synth.TID_V)
+    out = oracle.swa_prefill(Q, K, V, window=1)
+    np.testing.assert_allclose(out, np.repeat(V.astype(np.float64), 2, axis=1), rtol=0, atol=0)
+
+
+def test_swa_window_drops_keys_older_than_the_window():
+    # perturbing keys/values older than the window leaves the row unchanged,
+    # perturbing the oldest key inside it changes the row
+    L, d, W = 40, 8, 7
+    Q, K, V = (f32((1, 1, L, d), 27, t) for t in (synth.TID_Q, synth.TID_K, synth.TID_V))
+    base = oracle.swa_prefill(Q, K, V, window=W)
+    t = 30
+    K2, V2 = K.copy(), V.copy()
+    K2[0, 0, : t - W + 1] += 3.0
+    V2[0, 0, : t - W + 1] -= 2.0
+    assert np.array_equal(oracle.swa_prefill(Q, K2, V2, W, rows=[t]), base[:, :, [t]])
+    K3 = K.copy()
+    K3[0, 0, t - W + 1] += 3.0
+    assert not np.array_equal(oracle.swa_prefill(Q, K3, V, W, rows=[t]), base[:, :, [t]])
+
+
+def test_swa_decode_is_the_prefill_row():
+    B, Hq, Hkv, L, d, W = 2, 4, 2, 90, 8, 16
+    Q = f32((B, Hq, L, d), 28, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 28, synth.TID_K)
+    V = f32((B, Hkv, L, d), 28, synth.TID_V)
+    for pos in (0, 5, 60, 89):
+        dec = oracle.swa_decode(np.ascontiguousarray(Q[:, :, pos]), K, V, pos, W)
+        pre = oracle.swa_prefill(Q, K, V, W, rows=[pos])
+        np.testing.assert_array_equal(dec, pre[:, :, 0])
