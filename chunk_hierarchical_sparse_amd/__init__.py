@@ -17,8 +17,10 @@ from . import build as _build
 __all__ = [
     "HsaError", "hsa_status_string", "hsa_build_landmarks", "hsa_prefill",
     "hsa_prefill_workspace_size", "hsa_decode", "hsa_decode_workspace_size",
-    "dhsa_prefill", "dhsa_prefill_workspace_size", "hsa_profile_enable", "hsa_profile_read",
-    "lib_path", "load_library",
+    "hsa_prefill_interval", "hsa_prefill_interval_workspace_size", "dhsa_prefill",
+    "dhsa_prefill_workspace_size", "dhsa_build_chunk_keys", "dhsa_decode",
+    "dhsa_decode_workspace_size", "swa_prefill", "swa_decode", "hsa_profile_enable",
+    "hsa_profile_read", "lib_path", "load_library",
 ]
 
 HSA_OK = 0
@@ -79,6 +81,8 @@ def load_library():
         "dhsa_decode_workspace_size": ([_I, _I, _I, _I, _L, _L], _Z),
         "dhsa_decode": ([_P, _I, _P, _P, _L, _P, _I, _P, _I, _L, _P, _P, _I, _I, _I, _I, _P, _Z,
                          _P], _I),
+        "swa_prefill": ([_P, _P, _P, _P, _I, _L, _I, _I, _I, _L, _I, _P], _I),
+        "swa_decode": ([_P, _P, _P, _L, _L, _L, _P, _I, _I, _I, _I, _I, _P], _I),
         "hsa_profile_enable": ([_I], _I),
         "hsa_profile_read": ([_P, _I, _P], _I),
     }
@@ -371,6 +375,42 @@ def dhsa_decode(q_cur, Kc, Vc, khat, offsets, budget, out=None, return_order=Fal
                            out.data_ptr(), _ptr(order), B, H, d, _dtype_code(q_cur), _ptr(ws),
                            nbytes, _stream(q_cur)))
     return (out, order) if return_order else out
+
+
+def swa_prefill(Q, K, V, window, out=None):
+    """Sliding-window attention over a whole sequence: row t attends keys
+    max(0, t-window+1) .. t.  Q [B,Hq,L,d], K, V [B,Hkv,L,d]."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, Q.dtype)
+    _need(V, "V", 4, Q.dtype)
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (B, Hkv, L, d) or V.shape != K.shape:
+        raise ValueError("K and V must be [B,Hkv,L,d] matching Q")
+    if out is None:
+        out = torch.empty_like(Q)
+    _check(load_library().swa_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(),
+                                      B, L, Hq, Hkv, d, window, _dtype_code(Q), _stream(Q)))
+    return out
+
+
+def swa_decode(q, Kc, Vc, pos, window, out=None):
+    """Sliding-window decode: the query at position pos over cache keys
+    max(0, pos-window+1) .. pos.  q [B,Hq,d], Kc, Vc [B,Hkv,n_max,d] holding
+    tokens 0..pos."""
+    _need(q, "q", 3)
+    _need(Kc, "Kc", 4, q.dtype)
+    _need(Vc, "Vc", 4, q.dtype)
+    B, Hq, d = q.shape
+    Hkv, n_max = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, Hkv, n_max, d) or Vc.shape != Kc.shape:
+        raise ValueError("Kc and Vc must be [B,Hkv,n_max,d] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(load_library().swa_decode(q.data_ptr(), Kc.data_ptr(), Vc.data_ptr(), pos, n_max,
+                                     window, out.data_ptr(), B, Hq, Hkv, d, _dtype_code(q),
+                                     _stream(q)))
+    return out
 
 
 def hsa_profile_enable(enable=True):

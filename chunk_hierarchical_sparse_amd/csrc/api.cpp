@@ -630,6 +630,93 @@ hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* V
   return HSA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+hsa_status_t check_swa(int B, int Hq, int Hkv, int d, int64_t window, hsa_dtype_t dtype) {
+  if (!dtype_ok(dtype)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+  if (B < 0 || Hq <= 0 || Hkv <= 0)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "need B >= 0, Hq >= 1, Hkv >= 1");
+  if (Hq % Hkv != 0) return fail(HSA_ERR_INVALID_ARGUMENT, "Hq must be a multiple of Hkv");
+  if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+  if (window < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "window must be >= 1");
+  return HSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hsa_status_t swa_prefill(const void* Q, const void* K, const void* V, void* O, int B, int64_t L,
+                         int Hq, int Hkv, int d, int64_t window, hsa_dtype_t dtype,
+                         hsa_stream_t stream) {
+  g_err.clear();
+  hsa_status_t s = check_swa(B, Hq, Hkv, d, window, dtype);
+  if (s != HSA_OK) return s;
+  if (L < 0) return fail(HSA_ERR_INVALID_ARGUMENT, "need L >= 0");
+  if ((int64_t)B * Hq * L >= (int64_t(1) << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "B*Hq*L must be < 2^31");
+  if (B == 0 || L == 0) return HSA_OK;
+  if (!Q || !K || !V || !O)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must not be NULL");
+  hsa::SwaArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.dtype = dt_code(dtype);
+  a.L = L;
+  a.window = window;
+  a.n_ctx = 0;
+  const hipStream_t st = (hipStream_t)stream;
+  StageMarks pm(st);
+  pm.mark();
+  hipError_t e = hsa::launch_swa_prefill(a, st);
+  if (e != hipSuccess) return hip_fail(e, "swa_prefill");
+  pm.mark();
+  return HSA_OK;
+}
+
+hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t pos,
+                        int64_t n_max, int64_t window, void* o, int B, int Hq, int Hkv, int d,
+                        hsa_dtype_t dtype, hsa_stream_t stream) {
+  g_err.clear();
+  hsa_status_t s = check_swa(B, Hq, Hkv, d, window, dtype);
+  if (s != HSA_OK) return s;
+  if (pos < 0 || pos >= n_max)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "need 0 <= pos < n_max (the new token is cached)");
+  if (B == 0) return HSA_OK;
+  if ((int64_t)B * Hkv * n_max >= (int64_t(1) << 40))
+    return fail(HSA_ERR_UNSUPPORTED, "B*Hkv*n_max must be < 2^40");
+  if (!q || !Kc || !Vc || !o)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "q, Kc, Vc and o must not be NULL");
+  hsa::SwaArgs a;
+  a.Q = q;
+  a.K = Kc;
+  a.V = Vc;
+  a.O = o;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.dtype = dt_code(dtype);
+  a.L = n_max;
+  a.window = window;
+  a.n_ctx = pos + 1;
+  const hipStream_t st = (hipStream_t)stream;
+  StageMarks pm(st);
+  pm.mark();
+  hipError_t e = hsa::launch_swa_decode(a, st);
+  if (e != hipSuccess) return hip_fail(e, "swa_decode");
+  pm.mark();
+  return HSA_OK;
+}
+
 hsa_status_t hsa_profile_enable(int enable) {
   g_err.clear();
   g_prof.on = enable != 0;

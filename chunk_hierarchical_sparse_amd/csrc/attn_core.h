@@ -283,14 +283,16 @@ __device__ __forceinline__ void store_kv_wide(KVSmemWide<D>& sm, const KVRegsWid
 }
 
 // One staged block of nkeys (<= 128, block-uniform) keys: this lane's query
-// attends keys with in-block index < nvalid (<= nkeys; may differ per lane).
+// attends keys with in-block index < nvalid (<= nkeys; may differ per lane)
+// and, with BAND, also >= nlo (a sliding window's lower edge).
 // The block is taken SUB 32-key sub-tiles at a time (SUB = 4: one update
 // for the whole block; SUB = 2: two, with half the score registers), each
 // with one online-softmax update; the accumulator is rescaled only when
 // some lane's running maximum grew.
-template <int D, int SUB>
+template <int D, int SUB, bool BAND = false>
 __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide<D>& sm,
-                                               int nkeys, int nvalid, float scale_log2) {
+                                               int nkeys, int nvalid, float scale_log2,
+                                               int nlo = 0) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int i32 = lane & 31;
@@ -299,8 +301,11 @@ __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide
   for (int t0 = 0; t0 < nsub_all; t0 += SUB) {
     const int nsub = min(SUB, nsub_all - t0);
     const int nv = nvalid - 32 * t0;  // valid keys of this lane from sub-tile t0 on
-    // the valid keys are a prefix, so once no lane has any left none follow
+    const int nl = nlo - 32 * t0;     // first valid key relative to sub-tile t0
+    // the valid keys end before nvalid, so once no lane has any left none follow
     if (__ballot(nv > 0) == 0) break;
+    // sub-tiles wholly below every lane's window hold no valid key
+    if (BAND && __ballot(nl < 32 * nsub) == 0) continue;
     // the first k-step takes a zero accumulator operand: no register fill
     f32x16 sc[SUB];
 #pragma unroll
@@ -322,11 +327,11 @@ __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide
 #pragma unroll
     for (int t = 0; t < SUB; ++t) {
       if (t >= nsub) break;
-      if (__ballot(nv < 32 * (t + 1)) != 0) {
+      if (__ballot(nv < 32 * (t + 1) || (BAND && nl > 32 * t)) != 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= nv) sc[t][r] = -INFINITY;
+          if (key >= nv || (BAND && key < nl)) sc[t][r] = -INFINITY;
         }
       }
     }

@@ -130,4 +130,18 @@ hipError_t launch_dhsa_chunk_keys(const void* K, float* khat, const int32_t* off
                                   int64_t BH, int64_t n_max, int d, int n_cap, int chunk_begin,
                                   int chunk_end, hipStream_t stream);
 
+// ---- sliding-window attention (swa.hip) ------------------------------------
+struct SwaArgs {
+  const void* Q;   // prefill [B,Hq,L,d]; decode [B,Hq,d]
+  const void* K;   // [B,Hkv,L,d] (decode: the cache, L = its capacity)
+  const void* V;
+  void* O;         // like Q
+  int B, Hq, Hkv, d, dtype;
+  int64_t L;       // prefill: sequence length; decode: cache capacity n_max
+  int64_t window;  // W >= 1: a query at t attends keys max(0, t-W+1) .. t
+  int64_t n_ctx;   // decode: tokens in the cache, the new one at n_ctx - 1
+};
+hipError_t launch_swa_prefill(const SwaArgs& a, hipStream_t stream);
+hipError_t launch_swa_decode(const SwaArgs& a, hipStream_t stream);
+
 }  // namespace hsa

@@ -225,14 +225,44 @@ hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* V
                          size_t workspace_bytes, hsa_stream_t stream);
 
 /*
+ * Sliding-window attention, the local attention of the upper layers ([HSA]
+ * Methodology: upper layers pair local self-attention with the HSA module;
+ * 512-token sliding windows by default).  A query at position t attends the
+ * keys max(0, t-W+1) .. t of its KV head (query head h uses KV head
+ * h / (Hq/Hkv)): o_t = softmax(q_t . k_j / sqrt d) v_j over that window.
+ * The pages give no formula for how the layer merges this output with the
+ * HSA output, so the two come from separate calls and the model combines
+ * them (residual sum, the bypassing path, gating).
+ *
+ * swa_prefill: every position of the sequence.
+ *   Q [B,Hq,L,d], K, V [B,Hkv,L,d] dtype, read only; O [B,Hq,L,d] written.
+ *   W = window >= 1 (W >= L gives dense causal attention).
+ * swa_decode: one new query per sequence at position pos (the position
+ *   hsa_decode calls n_ctx).
+ *   q [B,Hq,d]; Kc, Vc [B,Hkv,n_max,d] caches holding tokens 0..pos (the new
+ *   key and value included); o [B,Hq,d] written.
+ * Device pointers, row-major, caller-owned; no workspace.  Limits: d in
+ * {64, 128}, Hq % Hkv == 0, B*Hq*L < 2^31 (prefill), 0 <= pos < n_max
+ * (decode).  Invalid arguments return an error before anything is enqueued.
+ * With profiling on, each call records one stage (0 attend).
+ */
+hsa_status_t swa_prefill(const void* Q, const void* K, const void* V, void* O, int B, int64_t L,
+                         int Hq, int Hkv, int d, int64_t window, hsa_dtype_t dtype,
+                         hsa_stream_t stream);
+hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t pos,
+                        int64_t n_max, int64_t window, void* o, int B, int Hq, int Hkv, int d,
+                        hsa_dtype_t dtype, hsa_stream_t stream);
+
+/*
  * Profiling aid (not part of the method).  While enabled on the calling
- * thread, each hsa_prefill, hsa_decode and dhsa_prefill call records a HIP
+ * thread, each call of the entry points below records a HIP
  * event on its stream before each of its stages and one after the last:
  *   hsa_prefill : 0 landmarks, 1 select, 2 invert, 3 attend, 4 fuse
  *   hsa_decode  : 0 scan (landmark stream, per-slice top-K), 1 attend (merge
  *                 of the slices' candidates, chunk attention), 2 fuse
  *   dhsa_prefill: 0 pool, 1 S_c, 2 rank, 3 attend, 4 mask
  *   dhsa_decode : 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
+ *   swa_prefill, swa_decode: 0 attend
  * hsa_profile_read waits for the recorded events, adds the elapsed
  * milliseconds of stage s summed over all recorded calls into stage_ms[s]
  * (s < max_stages; the caller zeroes the array), releases the events and

@@ -26,7 +26,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["hsa_build_landmarks", "hsa_prefill", "hsa_decode", "dhsa_prefill",
               "hsa_prefill_workspace_size", "hsa_decode_workspace_size",
-              "dhsa_prefill_workspace_size", "hsa_status_string", "hsa_last_error_message"]:
+              "dhsa_prefill_workspace_size", "hsa_status_string", "hsa_last_error_message",
+              "hsa_prefill_interval", "dhsa_build_chunk_keys", "dhsa_decode", "swa_prefill",
+              "swa_decode"]:
         assert n in names
 
 
@@ -219,3 +221,33 @@ def test_prefill_interval_validation():
     assert n1 == lib().hsa_prefill_workspace_size(1, 256, 4, 2, 128, 64, 8, BF16)
     assert 0 < n8 < n1  # one selection row per block
     assert lib().hsa_prefill_interval_workspace_size(1, 256, 4, 2, 128, 64, 8, 0, BF16) == 0
+
+
+def swa_call(which, **kw):
+    a = dict(Q=1, K=1, V=1, O=1, B=1, L=256, Hq=4, Hkv=2, d=128, W=512, dt=BF16, pos=10,
+             n_max=256)
+    a.update(kw)
+    if which == "prefill":
+        return lib().swa_prefill(a["Q"], a["K"], a["V"], a["O"], a["B"], a["L"], a["Hq"],
+                                 a["Hkv"], a["d"], a["W"], a["dt"], None)
+    return lib().swa_decode(a["Q"], a["K"], a["V"], a["pos"], a["n_max"], a["W"], a["O"],
+                            a["B"], a["Hq"], a["Hkv"], a["d"], a["dt"], None)
+
+
+@pytest.mark.parametrize("which", ["prefill", "decode"])
+def test_swa_validation(which):
+    assert swa_call(which, Hq=3, Hkv=2) == INV
+    assert swa_call(which, Hkv=0) == INV
+    assert swa_call(which, d=96) == UNS
+    assert swa_call(which, W=0) == INV
+    assert swa_call(which, dt=7) == UNS
+    assert swa_call(which, B=-1) == INV
+    assert swa_call(which, Q=None) == INV and "NULL" in msg()
+    assert swa_call(which, B=0) == hsa.HSA_OK  # nothing to do, nothing launched
+    if which == "prefill":
+        assert swa_call(which, L=-1) == INV
+        assert swa_call(which, L=0) == hsa.HSA_OK
+        assert swa_call(which, B=64, Hq=64, Hkv=8, L=1 << 20) == UNS
+    else:
+        assert swa_call(which, pos=-1) == INV
+        assert swa_call(which, pos=256) == INV and "pos" in msg()
