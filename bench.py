@@ -8,8 +8,10 @@ pooling, scoring + top-K, chunk attention and fusion, all inside the timed
 call.  By default the decode workloads (batch 32 with 131072-token caches;
 batch 1 with a 16,777,216-token cache and a planted needle), the DHSA
 prefill workload (L=16384, N_b=2048), DHSA decode (that sequence decoding
-its last token, batch 32) and the 32K prefill with retrieval every 8 tokens
-are measured too and reported under "also".
+its last token, batch 32), the 32K prefill with retrieval every 8 tokens and
+the sliding-window attention of the upper layers (512-token window, over the
+32K prefill inputs and at the end of the batch-32 decode caches) are measured
+too and reported under "also".
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -46,6 +48,10 @@ DOMINANT = {
                      ["dhsa.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
     "dhsa_decode": ("attend_kernel<128, 1>", "DhsaDecodeArgs",
                     ["dhsa_decode.hip", "hsa_common.h", "kernels.h"]),
+    "swa_prefill": ("prefill_bf16_kernel<128, 4>", "SwaArgs",
+                    ["swa.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
+    "swa_decode": ("decode_kernel<128, 1, 4>", "SwaArgs",
+                   ["swa.hip", "hsa_common.h", "kernels.h"]),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_workloads.txt")
 
@@ -339,6 +345,73 @@ def bench_dhsa_decode(torch, hsa, args):
     return res
 
 
+def bench_swa(torch, hsa, args, inputs, W=512):
+    """Sliding-window attention of the upper layers over the 32K prefill
+    workload's Q, K, V (512-token window)."""
+    Q, K, V, _, _ = inputs
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    q, k, v = to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch)
+    out = torch.empty_like(q)
+
+    def step():
+        hsa.swa_prefill(q, k, v, W, out=out)
+
+    log(f"swa prefill (W={W}): timing")
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 1)
+    pairs = sum(min(W, t + 1) for t in range(L))
+    flop = B * Hq * pairs * d * 4
+    achieved = flop / (stages[0] * 1e-3) / 1e12
+    res = dict(
+        value=B * L / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
+        config={"workload": "swa_prefill", "B": B, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d,
+                "window": W, "inputs": "0.5*N(0,1) bf16, seed 2"},
+        roofline={"bound": "mfma", "kernel": "sliding-window attention (bf16 MFMA)",
+                  "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("swa_prefill"),
+                  "algorithmic_gflop_per_launch": flop / 1e9, "avg_launch_ms": stages[0]},
+        stages_ms={"attend": stages[0]})
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_swa_decode(torch, hsa, args, W=512):
+    """Sliding-window decode at the end of 131072-token caches, batch 32,
+    32 query heads over 8 KV heads (the HSA decode workload's shapes)."""
+    import synth
+    B, Hq, Hkv, N, d, seed = 32, 32, 8, 131072, 128, 3
+    log(f"swa decode: filling caches on the device (B={B}, N={N})")
+    Kc = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device="cuda")
+    Vc = torch.empty_like(Kc)
+    synth.normal_device(Kc, seed, synth.TID_K)
+    synth.normal_device(Vc, seed, synth.TID_V)
+    q = to_dev(synth.normal((B, Hq, d), synth.BF16, seed, synth.TID_QDEC), torch)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    def step():
+        hsa.swa_decode(q, Kc, Vc, N - 1, W, out=out)
+
+    log("swa decode: timing")
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 1)
+    kv_bytes = B * Hkv * W * d * 2 * 2
+    total = kv_bytes + B * Hq * d * 2 * 2
+    achieved = total / (stages[0] * 1e-3) / 1e9
+    res = dict(
+        value=B / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
+        config={"workload": "swa_decode", "B": B, "n_ctx": N, "Hq": Hq, "Hkv": Hkv, "d": d,
+                "window": W, "inputs": f"N(0,1) bf16, seed {seed}"},
+        roofline={"bound": "hbm", "kernel": "sliding-window decode (window keys and values)",
+                  "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                  "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_for("swa_decode"),
+                  "algorithmic_bytes_per_launch": total, "avg_launch_ms": stages[0]},
+        stages_ms={"attend": stages[0]})
+    del Kc, Vc, q, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(inputs, target_s):
     """The oracle as it is, timed on this host's cores on evenly spaced query
     positions of the prefill workload (every head), scaled to queries/s."""
@@ -424,9 +497,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--extras", default="prefill_r8,decode,decode16m,dhsa,dhsa_decode",
+    ap.add_argument("--extras", default="prefill_r8,decode,decode16m,dhsa,dhsa_decode,swa,"
+                                        "swa_decode",
                     help="comma list of extra workloads: prefill_r8, decode, decode16m, dhsa, "
-                         "dhsa_decode, or none")
+                         "dhsa_decode, swa, swa_decode, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -469,6 +543,10 @@ def main():
             also.append(bench_dhsa(torch, hsa, args))
         elif e == "dhsa_decode":
             also.append(bench_dhsa_decode(torch, hsa, args))
+        elif e == "swa":
+            also.append(bench_swa(torch, hsa, args, inputs))
+        elif e == "swa_decode":
+            also.append(bench_swa_decode(torch, hsa, args))
         else:
             raise SystemExit(f"unknown extra workload {e}")
     if also:
