@@ -815,3 +815,188 @@ int oracle_swa_decode(const void* q, const void* K, const void* V, int dtype, in
   free(work);
   return OR_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* HSA prefill backward ([HiLS] abstract: retrieval learned end to end, the  */
+/* gradient reaching the retrieval scores through the fusion weights).       */
+/* ------------------------------------------------------------------------ */
+
+/* p_j = softmax_j(q . k_j / sqrt(d)) over keys rows [j0, j1) of a slab. */
+static void chunk_probs(const double* q, const void* K, int dtype, int64_t base, int64_t j0,
+                        int64_t j1, int64_t d, double* p) {
+  const double sc = 1.0 / sqrt((double)d);
+  double mx = -INFINITY;
+  for (int64_t j = j0; j < j1; ++j) {
+    double a = 0.0;
+    for (int64_t x = 0; x < d; ++x) a += q[x] * ld(K, dtype, base + j * d + x);
+    p[j - j0] = a * sc;
+    if (p[j - j0] > mx) mx = p[j - j0];
+  }
+  double z = 0.0;
+  for (int64_t j = j0; j < j1; ++j) {
+    p[j - j0] = exp(p[j - j0] - mx);
+    z += p[j - j0];
+  }
+  for (int64_t j = j0; j < j1; ++j) p[j - j0] /= z;
+}
+
+/*
+ * Gradients of sum over (b, h, t, x) of dO * out, out being HSA prefill with
+ * per-token retrieval (oracle_hsa_prefill, interval 1), with respect to Q, K
+ * and V.  The top-K selection is piecewise constant in the inputs and is
+ * held fixed (its derivative is zero wherever the ranking does not change).
+ * Per row t and head h with the selected chunks c_1..c_m:
+ *   s_k = q . lambda_ck / sqrt(d),  w = softmax(s),
+ *   o_k = sum_j p_kj v_j with p_k = softmax_j(q . k_j / sqrt(d)) over chunk c_k,
+ *   out = sum_k w_k o_k.
+ * Chain rule, in the forward's order reversed:
+ *   fusion     dw_k = dO . o_k,  ds_k = w_k (dw_k - sum_k' w_k' dw_k'),
+ *              the chunk outputs receive do_k = w_k dO;
+ *   chunk k    dp_j = do_k . v_j,  dz_j = p_kj (dp_j - do_k . o_k),
+ *              dq += dz_j k_j / sqrt(d),  dk_j += dz_j q / sqrt(d),
+ *              dv_j += p_kj do_k;
+ *   retrieval  dq += ds_k lambda_ck / sqrt(d),  dlambda_ck += ds_k q / sqrt(d);
+ *   landmarks  lambda_c = sum_{j in c} k_j / sqrt(S): dk_j += dlambda_c / sqrt(S).
+ * dO has Q's shape and dtype.  dQ [B,Hq,L,d], dK and dV [B,Hkv,L,d] (double)
+ * are overwritten.
+ */
+int oracle_hsa_prefill_backward(const void* Q, const void* K, const void* V, const void* dO,
+                                int dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv,
+                                int64_t d, int64_t S, int64_t topk, double* dQ, double* dK,
+                                double* dV) {
+  if (!Q || !K || !V || !dO || !dQ || !dK || !dV || B < 0 || L < 0 || Hq <= 0 || Hkv <= 0 ||
+      Hq % Hkv || d <= 0 || S <= 0 || topk <= 0)
+    return OR_EINVAL;
+  const int64_t G = Hq / Hkv;
+  const int64_t n = L / S;
+  const double sc = 1.0 / sqrt((double)d);
+  const double rs = 1.0 / sqrt((double)S);
+  memset(dQ, 0, (size_t)(B * Hq * L * d) * sizeof(double));
+  memset(dK, 0, (size_t)(B * Hkv * L * d) * sizeof(double));
+  memset(dV, 0, (size_t)(B * Hkv * L * d) * sizeof(double));
+  double* lmk = (double*)malloc((size_t)(B * Hkv * (n > 0 ? n : 1) * d) * sizeof(double));
+  if (!lmk) return OR_ENOMEM;
+  oracle_landmarks(K, dtype, B, Hkv, L, d, S, lmk);
+  const int64_t m_max = topk < n ? topk : n;
+  int err = OR_OK;
+  /* each (b, group) owns its slabs of dK, dV and its landmark gradients */
+#pragma omp parallel
+  {
+    cand_t* cand = (cand_t*)malloc((size_t)(n + 1) * sizeof(cand_t));
+    double* qv = (double*)malloc((size_t)(G * d) * sizeof(double));
+    double* dov = (double*)malloc((size_t)d * sizeof(double));
+    double* s = (double*)malloc((size_t)(m_max + 1) * sizeof(double));
+    double* w = (double*)malloc((size_t)(m_max + 1) * sizeof(double));
+    double* dw = (double*)malloc((size_t)(m_max + 1) * sizeof(double));
+    double* o = (double*)malloc((size_t)((m_max + 1) * d) * sizeof(double));
+    double* p = (double*)malloc((size_t)((m_max + 1) * S) * sizeof(double));
+    double* dlmk = (double*)malloc((size_t)((n > 0 ? n : 1) * d) * sizeof(double));
+    if (!cand || !qv || !dov || !s || !w || !dw || !o || !p || !dlmk) {
+#pragma omp atomic write
+      err = OR_ENOMEM;
+    } else {
+#pragma omp for collapse(2) schedule(dynamic, 1)
+      for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < Hkv; ++g) {
+          const int64_t kv_base = (b * Hkv + g) * L * d;
+          const double* lg = lmk + (b * Hkv + g) * n * d;
+          for (int64_t x = 0; x < n * d; ++x) dlmk[x] = 0.0;
+          for (int64_t t = 0; t < L; ++t) {
+            const int64_t navail = t / S < n ? t / S : n;
+            for (int64_t hh = 0; hh < G; ++hh)
+              for (int64_t x = 0; x < d; ++x)
+                qv[hh * d + x] = ld(Q, dtype, ((b * Hq + g * G + hh) * L + t) * d + x);
+            /* the forward's selection: group-summed scores, top-K */
+            for (int64_t c = 0; c < navail; ++c) {
+              double sigma = 0.0;
+              for (int64_t hh = 0; hh < G; ++hh) {
+                double a = 0.0;
+                for (int64_t x = 0; x < d; ++x) a += qv[hh * d + x] * lg[c * d + x];
+                sigma += a * sc;
+              }
+              cand[c].score = sigma;
+              cand[c].idx = c;
+            }
+            qsort(cand, (size_t)navail, sizeof(cand_t), cand_cmp);
+            const int64_t m = navail < topk ? navail : topk;
+            if (m == 0) continue;
+            for (int64_t hh = 0; hh < G; ++hh) {
+              const int64_t h = g * G + hh;
+              const double* q = qv + hh * d;
+              double* dq = dQ + ((b * Hq + h) * L + t) * d;
+              for (int64_t x = 0; x < d; ++x) dov[x] = ld(dO, dtype, ((b * Hq + h) * L + t) * d + x);
+              /* forward quantities of the row */
+              double smax = -INFINITY;
+              for (int64_t k = 0; k < m; ++k) {
+                const int64_t c = cand[k].idx;
+                double a = 0.0;
+                for (int64_t x = 0; x < d; ++x) a += q[x] * lg[c * d + x];
+                s[k] = a * sc;
+                if (s[k] > smax) smax = s[k];
+              }
+              double zs = 0.0;
+              for (int64_t k = 0; k < m; ++k) zs += exp(s[k] - smax);
+              for (int64_t k = 0; k < m; ++k) {
+                const int64_t c = cand[k].idx;
+                w[k] = exp(s[k] - smax) / zs;
+                chunk_probs(q, K, dtype, kv_base, c * S, (c + 1) * S, d, p + k * S);
+                for (int64_t x = 0; x < d; ++x) {
+                  double a = 0.0;
+                  for (int64_t j = 0; j < S; ++j)
+                    a += p[k * S + j] * ld(V, dtype, kv_base + (c * S + j) * d + x);
+                  o[k * d + x] = a;
+                }
+              }
+              /* fusion */
+              double wdw = 0.0;
+              for (int64_t k = 0; k < m; ++k) {
+                double a = 0.0;
+                for (int64_t x = 0; x < d; ++x) a += dov[x] * o[k * d + x];
+                dw[k] = a;
+                wdw += w[k] * a;
+              }
+              for (int64_t k = 0; k < m; ++k) {
+                const int64_t c = cand[k].idx;
+                const double ds = w[k] * (dw[k] - wdw);
+                /* retrieval scores */
+                for (int64_t x = 0; x < d; ++x) {
+                  dq[x] += ds * sc * lg[c * d + x];
+                  dlmk[c * d + x] += ds * sc * q[x];
+                }
+                /* attention inside chunk c with do = w_k dO; do . o_k = w_k dw_k */
+                const double D = w[k] * dw[k];
+                for (int64_t j = 0; j < S; ++j) {
+                  const int64_t row = kv_base + (c * S + j) * d;
+                  double dp = 0.0;
+                  for (int64_t x = 0; x < d; ++x) dp += w[k] * dov[x] * ld(V, dtype, row + x);
+                  const double pj = p[k * S + j];
+                  const double dz = pj * (dp - D);
+                  for (int64_t x = 0; x < d; ++x) {
+                    dq[x] += dz * sc * ld(K, dtype, row + x);
+                    dK[row + x] += dz * sc * q[x];
+                    dV[row + x] += pj * w[k] * dov[x];
+                  }
+                }
+              }
+            }
+          }
+          /* landmark pooling */
+          for (int64_t c = 0; c < n; ++c)
+            for (int64_t j = 0; j < S; ++j)
+              for (int64_t x = 0; x < d; ++x)
+                dK[kv_base + (c * S + j) * d + x] += dlmk[c * d + x] * rs;
+        }
+    }
+    free(cand);
+    free(qv);
+    free(dov);
+    free(s);
+    free(w);
+    free(dw);
+    free(o);
+    free(p);
+    free(dlmk);
+  }
+  free(lmk);
+  return err;
+}

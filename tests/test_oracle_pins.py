@@ -576,3 +576,125 @@ def test_swa_decode_is_the_prefill_row():
         dec = oracle.swa_decode(np.ascontiguousarray(Q[:, :, pos]), K, V, pos, W)
         pre = oracle.swa_prefill(Q, K, V, W, rows=[pos])
         np.testing.assert_array_equal(dec, pre[:, :, 0])
+
+
+# -------------------------------------------------------- HSA backward
+
+
+def _hsa_loss(Q, K, V, dO, S, topk):
+    r = oracle.hsa_prefill(Q, K, V, S, topk)
+    return float((r["out"] * dO.astype(np.float64)).sum()), r["sel"]
+
+
+def test_hsa_backward_matches_finite_differences():
+    # central differences of sum(dO * out) on sampled coordinates of Q, K and
+    # V, with a step that is exact in fp32 (2^-12, |x| < 2^11); coordinates
+    # whose perturbation changes the top-K selection are skipped (the
+    # selection is held fixed by the backward).  L = 50 leaves a trailing
+    # partial chunk whose keys reach nothing.
+    B, Hq, Hkv, L, d, S, topk = 1, 4, 2, 50, 8, 4, 3
+    Q = f32((B, Hq, L, d), 60, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 60, synth.TID_K)
+    V = f32((B, Hkv, L, d), 60, synth.TID_V)
+    dO = f32((B, Hq, L, d), 60, synth.TID_QDEC)
+    grads = oracle.hsa_prefill_backward(Q, K, V, dO, S, topk)
+    base_sel = oracle.hsa_prefill(Q, K, V, S, topk, want_out=False)["sel"]
+    h = 2.0 ** -12
+    rng = np.random.default_rng(61)
+    checked = 0
+    for name, X, G in (("Q", Q, grads["dQ"]), ("K", K, grads["dK"]), ("V", V, grads["dV"])):
+        idx = [tuple(rng.integers(0, s) for s in X.shape) for _ in range(24)]
+        if name == "K":
+            idx += [(0, 0, 48, 3), (0, 1, 49, 0)]  # the partial chunk
+        for i in idx:
+            Xp, Xm = X.copy(), X.copy()
+            Xp[i] += np.float32(h)
+            Xm[i] -= np.float32(h)
+            assert Xp[i] - X[i] == np.float32(h) and X[i] - Xm[i] == np.float32(h)
+            args_p = [Q, K, V]
+            args_m = [Q, K, V]
+            k = "QKV".index(name)
+            args_p[k], args_m[k] = Xp, Xm
+            lp, sp = _hsa_loss(*args_p, dO, S, topk)
+            lm, sm = _hsa_loss(*args_m, dO, S, topk)
+            if not (np.array_equal(sp, base_sel) and np.array_equal(sm, base_sel)):
+                continue
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - G[i]) <= 1e-6 + 1e-5 * abs(G[i]), (name, i, fd, G[i])
+            checked += 1
+    assert checked >= 60
+    assert np.all(grads["dK"][:, :, 48:] == 0)
+
+
+def _dense_attention_grads(Q, K, V, dO, causal_strict):
+    """Textbook gradients of masked softmax attention (per head; grouped
+    heads summed into their KV head): dV = P^T dO, dP = dO V^T,
+    dS = P * (dP - rowsum(P * dP)), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d)."""
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    Q, K, V, dO = (x.astype(np.float64) for x in (Q, K, V, dO))
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    mask = np.tril(np.ones((L, L), bool), -1 if causal_strict else 0)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            logits = np.where(mask, Q[b, h] @ K[b, g].T / math.sqrt(d), -np.inf)
+            mx = np.max(logits, axis=1, keepdims=True)
+            mx[~np.isfinite(mx)] = 0.0
+            e = np.exp(logits - mx)
+            z = e.sum(axis=1, keepdims=True)
+            P = np.divide(e, z, out=np.zeros_like(e), where=z > 0)
+            dV[b, g] += P.T @ dO[b, h]
+            dP = dO[b, h] @ V[b, g].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dQ[b, h] = dS @ K[b, g] / math.sqrt(d)
+            dK[b, g] += dS.T @ Q[b, h] / math.sqrt(d)
+    return dQ, dK, dV
+
+
+def test_hsa_backward_unit_chunks_all_kept_is_dense_attention_backward():
+    # S = 1 with every available chunk kept: the landmarks are the keys, each
+    # chunk's attention is its own value (constant weight 1), and the fusion
+    # is softmax attention over tokens j < t; the gradients are the textbook
+    # ones of strictly causal attention
+    B, Hq, Hkv, L, d = 1, 4, 2, 24, 8
+    Q = f32((B, Hq, L, d), 62, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 62, synth.TID_K)
+    V = f32((B, Hkv, L, d), 62, synth.TID_V)
+    dO = f32((B, Hq, L, d), 62, synth.TID_QDEC)
+    got = oracle.hsa_prefill_backward(Q, K, V, dO, 1, L)
+    dQ, dK, dV = _dense_attention_grads(Q, K, V, dO, causal_strict=True)
+    np.testing.assert_allclose(got["dQ"], dQ, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["dK"], dK, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["dV"], dV, rtol=0, atol=1e-12)
+
+
+def test_hsa_backward_top1_is_attention_backward_inside_the_chunk():
+    # K = 1: the single weight is 1 and carries no gradient; each row's
+    # gradient is the textbook attention gradient over the keys of its
+    # selected chunk
+    B, Hq, Hkv, L, d, S = 1, 2, 1, 40, 8, 5
+    Q = f32((B, Hq, L, d), 63, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 63, synth.TID_K)
+    V = f32((B, Hkv, L, d), 63, synth.TID_V)
+    dO = f32((B, Hq, L, d), 63, synth.TID_QDEC)
+    got = oracle.hsa_prefill_backward(Q, K, V, dO, S, 1)
+    sel = oracle.hsa_prefill(Q, K, V, S, 1, want_out=False)["sel"]
+    Qd, Kd, Vd, dOd = (x.astype(np.float64) for x in (Q, K, V, dO))
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    for h in range(Hq):
+        for t in range(L):
+            c = sel[0, 0, t, 0]
+            if c < 0:
+                continue
+            ks, vs = Kd[0, 0, c * S:(c + 1) * S], Vd[0, 0, c * S:(c + 1) * S]
+            p = softmax(ks @ Qd[0, h, t] / math.sqrt(d))
+            dp = vs @ dOd[0, h, t]
+            dz = p * (dp - p @ dp)
+            dQ[0, h, t] = dz @ ks / math.sqrt(d)
+            dK[0, 0, c * S:(c + 1) * S] += np.outer(dz, Qd[0, h, t]) / math.sqrt(d)
+            dV[0, 0, c * S:(c + 1) * S] += np.outer(p, dOd[0, h, t])
+    np.testing.assert_allclose(got["dQ"], dQ, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["dK"], dK, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got["dV"], dV, rtol=0, atol=1e-12)
