@@ -17,7 +17,8 @@ from . import build as _build
 __all__ = [
     "HsaError", "hsa_status_string", "hsa_build_landmarks", "hsa_prefill",
     "hsa_prefill_workspace_size", "hsa_decode", "hsa_decode_workspace_size",
-    "hsa_prefill_interval", "hsa_prefill_interval_workspace_size", "dhsa_prefill",
+    "hsa_prefill_interval", "hsa_prefill_interval_workspace_size", "hsa_prefill_backward",
+    "hsa_prefill_backward_workspace_size", "dhsa_prefill",
     "dhsa_prefill_workspace_size", "dhsa_build_chunk_keys", "dhsa_decode",
     "dhsa_decode_workspace_size", "swa_prefill", "swa_decode", "hsa_profile_enable",
     "hsa_profile_read", "lib_path", "load_library",
@@ -81,6 +82,9 @@ def load_library():
         "dhsa_decode_workspace_size": ([_I, _I, _I, _I, _L, _L], _Z),
         "dhsa_decode": ([_P, _I, _P, _P, _L, _P, _I, _P, _I, _L, _P, _P, _I, _I, _I, _I, _P, _Z,
                          _P], _I),
+        "hsa_prefill_backward_workspace_size": ([_I, _L, _I, _I, _I, _I, _I, _I], _Z),
+        "hsa_prefill_backward": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _L, _I, _I, _I, _I, _I, _I,
+                                  _P, _Z, _P], _I),
         "swa_prefill": ([_P, _P, _P, _P, _I, _L, _I, _I, _I, _L, _I, _P], _I),
         "swa_decode": ([_P, _P, _P, _L, _L, _L, _P, _I, _I, _I, _I, _I, _P], _I),
         "hsa_profile_enable": ([_I], _I),
@@ -375,6 +379,37 @@ def dhsa_decode(q_cur, Kc, Vc, khat, offsets, budget, out=None, return_order=Fal
                            out.data_ptr(), _ptr(order), B, H, d, _dtype_code(q_cur), _ptr(ws),
                            nbytes, _stream(q_cur)))
     return (out, order) if return_order else out
+
+
+def hsa_prefill_backward_workspace_size(B, L, Hq, Hkv, d, S, topk, dtype):
+    code = _dtype_code(torch.empty(0, dtype=dtype))
+    return load_library().hsa_prefill_backward_workspace_size(B, L, Hq, Hkv, d, S, topk, code)
+
+
+def hsa_prefill_backward(Q, K, V, dO, S, topk, lmk=None, workspace=None, grads=None):
+    """Gradients (dQ, dK, dV) of sum(dO * hsa_prefill(Q, K, V, S, topk)), the
+    top-K selection held fixed.  bf16, S <= 64."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, Q.dtype)
+    _need(V, "V", 4, Q.dtype)
+    _need(dO, "dO", 4, Q.dtype)
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (B, Hkv, L, d) or V.shape != K.shape or dO.shape != Q.shape:
+        raise ValueError("K, V must be [B,Hkv,L,d] and dO [B,Hq,L,d] matching Q")
+    if lmk is not None:
+        _need(lmk, "lmk", 4, torch.float32)
+    if grads is None:
+        grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    dQ, dK, dV = grads
+    lib = load_library()
+    nbytes = lib.hsa_prefill_backward_workspace_size(B, L, Hq, Hkv, d, S, topk, _dtype_code(Q))
+    ws = _workspace(nbytes, Q.device, workspace) if nbytes else None
+    _check(lib.hsa_prefill_backward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dO.data_ptr(),
+                                    _ptr(lmk), dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), B, L,
+                                    Hq, Hkv, d, S, topk, _dtype_code(Q), _ptr(ws), nbytes,
+                                    _stream(Q)))
+    return dQ, dK, dV
 
 
 def swa_prefill(Q, K, V, window, out=None):

@@ -133,6 +133,31 @@ PrefillLayout prefill_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d,
   return p;
 }
 
+// The backward's workspace: the forward's work list, per-row values in list
+// order and fp32 dK / dV accumulators.
+struct BackwardLayout {
+  PrefillLayout fwd;
+  float *lse2, *dw, *wk, *ds, *dk_acc, *dv_acc;
+  size_t bytes;
+};
+
+BackwardLayout backward_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d, int S,
+                               int topk) {
+  BackwardLayout p;
+  p.fwd = prefill_layout(ws, B, L, Hq, Hkv, d, S, topk, HSA_DTYPE_BF16);
+  Carver cv(ws);
+  cv.off = p.fwd.bytes;
+  const size_t rows = (size_t)B * Hq * L * topk;
+  p.lse2 = cv.take<float>(rows);
+  p.dw = cv.take<float>(rows);
+  p.wk = cv.take<float>(rows);
+  p.ds = cv.take<float>(rows);
+  p.dk_acc = cv.take<float>((size_t)B * Hkv * L * d);
+  p.dv_acc = cv.take<float>((size_t)B * Hkv * L * d);
+  p.bytes = cv.off + kAlign;
+  return p;
+}
+
 hsa_status_t check_decode(int B, int Hq, int Hkv, int d, int S, int topk, int64_t n_ctx,
                           int64_t n_max, hsa_dtype_t dt) {
   hsa_status_t s = check_prefill(B, 1, Hq, Hkv, d, S, topk, dt);
@@ -278,24 +303,11 @@ size_t hsa_prefill_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int 
 
 namespace {
 
-hsa_status_t prefill_impl(const void* Q, const void* K, const void* V, const float* lmk,
-                          void* O, int32_t* sel_idx, float* sel_w, int B, int64_t L, int Hq,
-                          int Hkv, int d, int S, int topk, int interval, hsa_dtype_t dtype,
-                          void* workspace, size_t workspace_bytes, hsa_stream_t stream) {
-  g_err.clear();
-  hsa_status_t s = check_prefill(B, L, Hq, Hkv, d, S, topk, dtype);
-  if (s != HSA_OK) return s;
-  if (interval < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "the retrieval interval must be >= 1");
-  if (B == 0 || L == 0) return HSA_OK;
-  if (!Q || !K || !V || !O) return fail(HSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must not be NULL");
-  const size_t need = prefill_layout(nullptr, B, L, Hq, Hkv, d, S, topk, dtype, interval).bytes;
-  if (!workspace || workspace_bytes < need)
-    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
-                "workspace needs " + std::to_string(need) + " bytes");
-  PrefillLayout lay =
-      prefill_layout(align_ws(workspace), B, L, Hq, Hkv, d, S, topk, dtype, interval);
-  const hipStream_t st = (hipStream_t)stream;
-  const int64_t n = L / S;
+// The forward's kernel arguments over a carved workspace.
+hsa::PrefillArgs prefill_args(const PrefillLayout& lay, const void* Q, const void* K,
+                              const void* V, const float* lmk, void* O, int32_t* sel_idx,
+                              float* sel_w, int B, int64_t L, int Hq, int Hkv, int d, int S,
+                              int topk, int interval, hsa_dtype_t dtype) {
   const int G = Hq / Hkv;
   hsa::PrefillArgs a;
   a.Q = Q;
@@ -322,7 +334,7 @@ hsa_status_t prefill_impl(const void* Q, const void* K, const void* V, const flo
   a.topk = topk;
   a.dtype = dt_code(dtype);
   a.L = L;
-  a.n = n;
+  a.n = L / S;
   a.entries_per_tile = lay.entries_per_tile;
   a.log2G = -1;
   for (int k = 0; k < 6; ++k)
@@ -330,6 +342,29 @@ hsa_status_t prefill_impl(const void* Q, const void* K, const void* V, const flo
   a.interval = interval;
   a.nq = (L + interval - 1) / interval;
   a.tiles_ub = lay.tiles_ub;
+  return a;
+}
+
+hsa_status_t prefill_impl(const void* Q, const void* K, const void* V, const float* lmk,
+                          void* O, int32_t* sel_idx, float* sel_w, int B, int64_t L, int Hq,
+                          int Hkv, int d, int S, int topk, int interval, hsa_dtype_t dtype,
+                          void* workspace, size_t workspace_bytes, hsa_stream_t stream) {
+  g_err.clear();
+  hsa_status_t s = check_prefill(B, L, Hq, Hkv, d, S, topk, dtype);
+  if (s != HSA_OK) return s;
+  if (interval < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "the retrieval interval must be >= 1");
+  if (B == 0 || L == 0) return HSA_OK;
+  if (!Q || !K || !V || !O) return fail(HSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must not be NULL");
+  const size_t need = prefill_layout(nullptr, B, L, Hq, Hkv, d, S, topk, dtype, interval).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(need) + " bytes");
+  PrefillLayout lay =
+      prefill_layout(align_ws(workspace), B, L, Hq, Hkv, d, S, topk, dtype, interval);
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t n = L / S;
+  hsa::PrefillArgs a = prefill_args(lay, Q, K, V, lmk, O, sel_idx, sel_w, B, L, Hq, Hkv, d, S,
+                                    topk, interval, dtype);
   if ((int64_t)B * Hkv * a.tiles_ub >= ((int64_t)1 << 31))
     return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
   hipError_t e;
@@ -361,6 +396,71 @@ hsa_status_t hsa_prefill(const void* Q, const void* K, const void* V, const floa
                          size_t workspace_bytes, hsa_stream_t stream) {
   return prefill_impl(Q, K, V, lmk, O, sel_idx, sel_w, B, L, Hq, Hkv, d, S, topk, 1, dtype,
                       workspace, workspace_bytes, stream);
+}
+
+size_t hsa_prefill_backward_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S,
+                                           int topk, hsa_dtype_t dtype) {
+  if (dtype != HSA_DTYPE_BF16 || S > 64 || check_prefill(B, L, Hq, Hkv, d, S, topk, dtype) != HSA_OK)
+    return 0;
+  return backward_layout(nullptr, B, L, Hq, Hkv, d, S, topk).bytes;
+}
+
+hsa_status_t hsa_prefill_backward(const void* Q, const void* K, const void* V, const void* dO,
+                                  const float* lmk, void* dQ, void* dK, void* dV, int B,
+                                  int64_t L, int Hq, int Hkv, int d, int S, int topk,
+                                  hsa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                  hsa_stream_t stream) {
+  g_err.clear();
+  hsa_status_t s = check_prefill(B, L, Hq, Hkv, d, S, topk, dtype);
+  if (s != HSA_OK) return s;
+  if (dtype != HSA_DTYPE_BF16) return fail(HSA_ERR_UNSUPPORTED, "the backward runs bf16 only");
+  if (S > 64) return fail(HSA_ERR_UNSUPPORTED, "the backward needs chunk size S <= 64");
+  if (B == 0 || L == 0) return HSA_OK;
+  if (!Q || !K || !V || !dO || !dQ || !dK || !dV)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "Q, K, V, dO, dQ, dK and dV must not be NULL");
+  const size_t need = backward_layout(nullptr, B, L, Hq, Hkv, d, S, topk).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(need) + " bytes");
+  BackwardLayout lay = backward_layout(align_ws(workspace), B, L, Hq, Hkv, d, S, topk);
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t n = L / S;
+  hsa::PrefillBwdArgs ba;
+  ba.p = prefill_args(lay.fwd, Q, K, V, lmk, nullptr, nullptr, nullptr, B, L, Hq, Hkv, d, S,
+                      topk, 1, dtype);
+  if ((int64_t)B * Hkv * ba.p.tiles_ub >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
+  ba.dO = dO;
+  ba.lse2 = lay.lse2;
+  ba.dw = lay.dw;
+  ba.wk = lay.wk;
+  ba.ds = lay.ds;
+  ba.dk_acc = lay.dk_acc;
+  ba.dv_acc = lay.dv_acc;
+  ba.dQ = dQ;
+  ba.dK = dK;
+  ba.dV = dV;
+  hipError_t e;
+  StageMarks pm(st);
+  pm.mark();
+  if (!lmk && n > 0) {
+    e = hsa::launch_landmarks(K, ba.p.dtype, lay.fwd.lmk, (int64_t)B * Hkv, L, n, d, S, 0, n, st);
+    if (e != hipSuccess) return hip_fail(e, "landmarks");
+  }
+  pm.mark();
+  if ((e = hsa::prefill_select(ba.p, st)) != hipSuccess) return hip_fail(e, "select");
+  pm.mark();
+  if ((e = hsa::prefill_invert(ba.p, st)) != hipSuccess) return hip_fail(e, "invert");
+  pm.mark();
+  if ((e = hsa::prefill_bwd_score(ba, st)) != hipSuccess) return hip_fail(e, "backward score");
+  pm.mark();
+  if ((e = hsa::prefill_bwd_rows(ba, st)) != hipSuccess) return hip_fail(e, "backward rows");
+  pm.mark();
+  if ((e = hsa::prefill_bwd_chunk(ba, st)) != hipSuccess) return hip_fail(e, "backward chunk");
+  pm.mark();
+  if ((e = hsa::prefill_bwd_finish(ba, st)) != hipSuccess) return hip_fail(e, "backward finish");
+  pm.mark();
+  return HSA_OK;
 }
 
 size_t hsa_prefill_interval_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S,

@@ -130,6 +130,31 @@ hsa_status_t hsa_prefill_interval(const void* Q, const void* K, const void* V, c
                                   hsa_stream_t stream);
 
 /*
+ * HSA prefill backward ([HiLS] abstract: retrieval learned end to end, the
+ * gradient reaching the retrieval scores through the fusion weights).
+ * Gradients of sum(dO * O), O the output of hsa_prefill on the same inputs,
+ * with respect to Q, K and V.  The top-K selection is piecewise constant in
+ * the inputs and is held fixed; every other step is differentiated: the
+ * fusion softmax, the attention inside each chunk, the retrieval scores
+ * q . lambda_c / sqrt(d) and the landmark pooling lambda_c = sum_j k_j /
+ * sqrt(S).
+ *   Q, dO [B,Hq,L,d], K, V [B,Hkv,L,d] bf16, read only.
+ *   lmk   fp32 [B,Hkv,L/S,d] landmarks of K, or NULL to build them.
+ *   dQ [B,Hq,L,d], dK, dV [B,Hkv,L,d] bf16, written.
+ *   workspace of at least hsa_prefill_backward_workspace_size(...) bytes.
+ * Limits: as hsa_prefill, plus bf16 only and S <= 64 (HSA_ERR_UNSUPPORTED
+ * otherwise).  Gradients are accumulated in fp32; dK and dV sum with global
+ * atomics, so their last bits may differ from run to run.
+ */
+size_t hsa_prefill_backward_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S,
+                                           int topk, hsa_dtype_t dtype);
+hsa_status_t hsa_prefill_backward(const void* Q, const void* K, const void* V, const void* dO,
+                                  const float* lmk, void* dQ, void* dK, void* dV, int B,
+                                  int64_t L, int Hq, int Hkv, int d, int S, int topk,
+                                  hsa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                  hsa_stream_t stream);
+
+/*
  * HSA decode: one new query per sequence at position n_ctx, attending a KV
  * cache of capacity n_max tokens whose first n_ctx are valid.  All
  * floor(n_ctx/S) complete chunks are available.
@@ -263,6 +288,9 @@ hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t p
  *   dhsa_prefill: 0 pool, 1 S_c, 2 rank, 3 attend, 4 mask
  *   dhsa_decode : 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
  *   swa_prefill, swa_decode: 0 attend
+ *   hsa_prefill_backward: 0 landmarks, 1 select, 2 invert, 3 score (log-sum-
+ *                 exp, dO . o_k), 4 rows (w, ds), 5 chunk (dK, dV, dQ pieces),
+ *                 6 finish (dQ gather, dK / dV to bf16)
  * hsa_profile_read waits for the recorded events, adds the elapsed
  * milliseconds of stage s summed over all recorded calls into stage_ms[s]
  * (s < max_stages; the caller zeroes the array), releases the events and

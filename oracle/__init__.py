@@ -45,7 +45,7 @@ def lib():
         L.oracle_swa_decode.argtypes = [_P, _P, _P, ctypes.c_int, _I, _I, _I, _I, _I, _I, _I,
                                         _P]
         L.oracle_hsa_prefill_backward.argtypes = [_P, _P, _P, _P, ctypes.c_int, _I, _I, _I, _I,
-                                                  _I, _I, _I, _P, _P, _P]
+                                                  _I, _I, _I, _P, _I, _P, _P, _P]
         L.oracle_num_threads.argtypes = []
         for f in (L.oracle_num_threads, L.oracle_landmarks, L.oracle_hsa_prefill, L.oracle_hsa_decode_select,
                   L.oracle_hsa_decode_attend, L.oracle_dhsa_prefill, L.oracle_dhsa_chunk_keys,
@@ -286,11 +286,12 @@ def swa_decode(q, K, V, pos, window):
     return out
 
 
-def hsa_prefill_backward(Q, K, V, dO, S, topk):
+def hsa_prefill_backward(Q, K, V, dO, S, topk, rows=None):
     """Gradients of sum(dO * out) for HSA prefill (per-token retrieval) with
     respect to Q, K, V, the top-K selection held fixed.  dO has Q's shape and
-    dtype.  Returns dict(dQ [B,Hq,L,d], dK [B,Hkv,L,d], dV [B,Hkv,L,d])
-    float64."""
+    dtype.  With `rows`, only those query positions' terms are taken (the
+    gradient with dO zero elsewhere).  Returns dict(dQ [B,Hq,L,d],
+    dK [B,Hkv,L,d], dV [B,Hkv,L,d]) float64."""
     Q, K, V, dO = _c(Q), _c(K), _c(V), _c(dO)
     B, Hq, L, d = Q.shape
     Hkv = K.shape[1]
@@ -299,9 +300,11 @@ def hsa_prefill_backward(Q, K, V, dO, S, topk):
     dQ = np.zeros(Q.shape, np.float64)
     dK = np.zeros(K.shape, np.float64)
     dV = np.zeros(V.shape, np.float64)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     rc = lib().oracle_hsa_prefill_backward(Q.ctypes.data, K.ctypes.data, V.ctypes.data,
                                            dO.ctypes.data, _dt(Q, K, V, dO), B, L, Hq, Hkv, d,
-                                           S, topk, dQ.ctypes.data, dK.ctypes.data,
-                                           dV.ctypes.data)
+                                           S, topk, _ptr(rows_a),
+                                           0 if rows_a is None else len(rows_a),
+                                           dQ.ctypes.data, dK.ctypes.data, dV.ctypes.data)
     _check(rc, "hsa_prefill_backward")
     return dict(dQ=dQ, dK=dK, dV=dV)

@@ -858,15 +858,20 @@ static void chunk_probs(const double* q, const void* K, int dtype, int64_t base,
  *   retrieval  dq += ds_k lambda_ck / sqrt(d),  dlambda_ck += ds_k q / sqrt(d);
  *   landmarks  lambda_c = sum_{j in c} k_j / sqrt(S): dk_j += dlambda_c / sqrt(S).
  * dO has Q's shape and dtype.  dQ [B,Hq,L,d], dK and dV [B,Hkv,L,d] (double)
- * are overwritten.
+ * are overwritten.  rows[0..n_rows) (NULL: every position) lists the query
+ * positions whose terms are taken: the result is then the gradient of the
+ * same sum with dO set to zero at every other position (dQ is zero there).
  */
 int oracle_hsa_prefill_backward(const void* Q, const void* K, const void* V, const void* dO,
                                 int dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv,
-                                int64_t d, int64_t S, int64_t topk, double* dQ, double* dK,
-                                double* dV) {
+                                int64_t d, int64_t S, int64_t topk, const int64_t* rows,
+                                int64_t n_rows, double* dQ, double* dK, double* dV) {
   if (!Q || !K || !V || !dO || !dQ || !dK || !dV || B < 0 || L < 0 || Hq <= 0 || Hkv <= 0 ||
-      Hq % Hkv || d <= 0 || S <= 0 || topk <= 0)
+      Hq % Hkv || d <= 0 || S <= 0 || topk <= 0 || (rows && n_rows < 0))
     return OR_EINVAL;
+  if (rows)
+    for (int64_t r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= L) return OR_EINVAL;
   const int64_t G = Hq / Hkv;
   const int64_t n = L / S;
   const double sc = 1.0 / sqrt((double)d);
@@ -901,7 +906,9 @@ int oracle_hsa_prefill_backward(const void* Q, const void* K, const void* V, con
           const int64_t kv_base = (b * Hkv + g) * L * d;
           const double* lg = lmk + (b * Hkv + g) * n * d;
           for (int64_t x = 0; x < n * d; ++x) dlmk[x] = 0.0;
-          for (int64_t t = 0; t < L; ++t) {
+          const int64_t nr = rows ? n_rows : L;
+          for (int64_t ri = 0; ri < nr; ++ri) {
+            const int64_t t = rows ? rows[ri] : ri;
             const int64_t navail = t / S < n ? t / S : n;
             for (int64_t hh = 0; hh < G; ++hh)
               for (int64_t x = 0; x < d; ++x)

@@ -20,6 +20,7 @@ TID_V = 3
 TID_QDEC = 4
 TID_LENGTHS = 5
 TID_NEEDLE = 6
+TID_DO = 7      # output gradients of the backward
 
 F32, BF16, F64 = 0, 1, 2
 

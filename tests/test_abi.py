@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
               "hsa_prefill_workspace_size", "hsa_decode_workspace_size",
               "dhsa_prefill_workspace_size", "hsa_status_string", "hsa_last_error_message",
               "hsa_prefill_interval", "dhsa_build_chunk_keys", "dhsa_decode", "swa_prefill",
-              "swa_decode"]:
+              "swa_decode", "hsa_prefill_backward", "hsa_prefill_backward_workspace_size"]:
         assert n in names
 
 
@@ -251,3 +251,26 @@ def test_swa_validation(which):
     else:
         assert swa_call(which, pos=-1) == INV
         assert swa_call(which, pos=256) == INV and "pos" in msg()
+
+
+def backward_call(**kw):
+    a = dict(Q=1, K=1, V=1, dO=1, lmk=None, dQ=1, dK=1, dV=1, B=1, L=256, Hq=4, Hkv=2, d=128,
+             S=64, topk=8, dt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib().hsa_prefill_backward(a["Q"], a["K"], a["V"], a["dO"], a["lmk"], a["dQ"], a["dK"],
+                                      a["dV"], a["B"], a["L"], a["Hq"], a["Hkv"], a["d"], a["S"],
+                                      a["topk"], a["dt"], a["ws"], a["wsb"], None)
+
+
+def test_backward_validation():
+    assert backward_call(dt=F32) == UNS and "bf16" in msg()
+    assert backward_call(S=128) == UNS and "S <= 64" in msg()
+    assert backward_call(Hq=3) == INV
+    assert backward_call(dO=None) == INV and "NULL" in msg()
+    assert backward_call() == WS
+    need = lib().hsa_prefill_backward_workspace_size(1, 256, 4, 2, 128, 64, 8, BF16)
+    assert need > lib().hsa_prefill_workspace_size(1, 256, 4, 2, 128, 64, 8, BF16)
+    assert backward_call(ws=1 << 20, wsb=need - 1) == WS
+    assert lib().hsa_prefill_backward_workspace_size(1, 256, 4, 2, 128, 64, 8, F32) == 0
+    assert lib().hsa_prefill_backward_workspace_size(1, 256, 4, 2, 128, 128, 8, BF16) == 0
+    assert backward_call(B=0) == hsa.HSA_OK

@@ -698,3 +698,20 @@ def test_hsa_backward_top1_is_attention_backward_inside_the_chunk():
     np.testing.assert_allclose(got["dQ"], dQ, rtol=0, atol=1e-12)
     np.testing.assert_allclose(got["dK"], dK, rtol=0, atol=1e-12)
     np.testing.assert_allclose(got["dV"], dV, rtol=0, atol=1e-12)
+
+
+def test_hsa_backward_rows_equals_masked_output_gradient():
+    # taking only some rows' terms equals the full backward with dO zeroed
+    # at every other position
+    B, Hq, Hkv, L, d, S, topk = 1, 4, 2, 60, 8, 4, 3
+    Q = f32((B, Hq, L, d), 64, synth.TID_Q)
+    K = f32((B, Hkv, L, d), 64, synth.TID_K)
+    V = f32((B, Hkv, L, d), 64, synth.TID_V)
+    dO = f32((B, Hq, L, d), 64, synth.TID_DO)
+    rows = [3, 17, 18, 40, 59]
+    part = oracle.hsa_prefill_backward(Q, K, V, dO, S, topk, rows=rows)
+    masked = np.zeros_like(dO)
+    masked[:, :, rows] = dO[:, :, rows]
+    full = oracle.hsa_prefill_backward(Q, K, V, masked, S, topk)
+    for k in ("dQ", "dK", "dV"):
+        np.testing.assert_allclose(part[k], full[k], rtol=0, atol=1e-13)
