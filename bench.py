@@ -10,8 +10,9 @@ batch 1 with a 16,777,216-token cache and a planted needle), the DHSA
 prefill workload (L=16384, N_b=2048), DHSA decode (that sequence decoding
 its last token, batch 32), the 32K prefill with retrieval every 8 tokens and
 the sliding-window attention of the upper layers (512-token window, over the
-32K prefill inputs and at the end of the batch-32 decode caches) are measured
-too and reported under "also".
+32K prefill inputs and at the end of the batch-32 decode caches) and the
+prefill backward (gradients of the 32K prefill for an N(0,1) output
+gradient) are measured too and reported under "also".
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -48,6 +49,9 @@ DOMINANT = {
                      ["dhsa.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
     "dhsa_decode": ("attend_kernel<128, 1>", "DhsaDecodeArgs",
                     ["dhsa_decode.hip", "hsa_common.h", "kernels.h"]),
+    "hsa_prefill_backward": ("bwd_chunk_kernel<128>", "PrefillBwdArgs",
+                             ["prefill_bwd.hip", "prefill_common.h", "attn_core.h",
+                              "hsa_common.h", "kernels.h"]),
     "swa_prefill": ("prefill_bf16_kernel<128, 4>", "SwaArgs",
                     ["swa.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
     "swa_decode": ("decode_kernel<128, 1, 4>", "SwaArgs",
@@ -345,6 +349,46 @@ def bench_dhsa_decode(torch, hsa, args):
     return res
 
 
+def bench_backward(torch, hsa, args, inputs):
+    """HSA prefill backward on the 32K prefill workload: gradients of
+    sum(dO * O) for an N(0,1) bf16 output gradient."""
+    import synth
+    Q, K, V, S, topk = inputs
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    q, k, v = to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch)
+    dO = to_dev(synth.normal((B, Hq, L, d), synth.BF16, 2, synth.TID_DO), torch)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws = torch.empty(hsa.hsa_prefill_backward_workspace_size(B, L, Hq, Hkv, d, S, topk,
+                                                             torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        hsa.hsa_prefill_backward(q, k, v, dO, S, topk, workspace=ws, grads=grads)
+
+    log("backward: timing")
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 7)
+    sel, _ = prefill_counts(L, S, topk)
+    rows = B * Hq * sel  # (token, head, selected chunk) rows
+    # chunk stage per row: S = Q K^T, dP = dO V^T, dV, dK and dQ products
+    chunk_flop = rows * S * d * 2 * 5
+    achieved = chunk_flop / (stages[5] * 1e-3) / 1e12
+    res = dict(
+        value=B * L / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
+        config={"workload": "hsa_prefill_backward", "B": B, "L": L, "Hq": Hq, "Hkv": Hkv,
+                "d": d, "S": S, "topk": topk, "inputs": "0.5*N(0,1) bf16 Q/K/V, N(0,1) dO, seed 2"},
+        roofline={"bound": "mfma", "kernel": "chunk (dK, dV, dQ pieces; bf16 MFMA)",
+                  "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                  "frac": achieved / PEAK_BF16_TFLOPS,
+                  "traffic": traffic_for("hsa_prefill_backward"),
+                  "algorithmic_gflop_per_launch": chunk_flop / 1e9, "avg_launch_ms": stages[5]},
+        stages_ms=dict(zip(["landmarks", "select", "invert", "score", "rows", "chunk", "finish"],
+                           stages)))
+    del q, k, v, dO, grads, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_swa(torch, hsa, args, inputs, W=512):
     """Sliding-window attention of the upper layers over the 32K prefill
     workload's Q, K, V (512-token window)."""
@@ -497,10 +541,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--extras", default="prefill_r8,decode,decode16m,dhsa,dhsa_decode,swa,"
-                                        "swa_decode",
-                    help="comma list of extra workloads: prefill_r8, decode, decode16m, dhsa, "
-                         "dhsa_decode, swa, swa_decode, or none")
+    ap.add_argument("--extras", default="prefill_r8,backward,decode,decode16m,dhsa,dhsa_decode,"
+                                        "swa,swa_decode",
+                    help="comma list of extra workloads: prefill_r8, backward, decode, "
+                         "decode16m, dhsa, dhsa_decode, swa, swa_decode, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -543,6 +587,8 @@ def main():
             also.append(bench_dhsa(torch, hsa, args))
         elif e == "dhsa_decode":
             also.append(bench_dhsa_decode(torch, hsa, args))
+        elif e == "backward":
+            also.append(bench_backward(torch, hsa, args, inputs))
         elif e == "swa":
             also.append(bench_swa(torch, hsa, args, inputs))
         elif e == "swa_decode":

@@ -109,8 +109,11 @@ struct PrefillLayout {
   size_t bytes;
 };
 
+// entries_per_unit > 0 overrides the attention work-unit size (selection
+// entries per unit).
 PrefillLayout prefill_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d, int S,
-                             int topk, hsa_dtype_t dt, int interval = 1) {
+                             int topk, hsa_dtype_t dt, int interval = 1,
+                             int entries_per_unit = 0) {
   Carver cv(ws);
   PrefillLayout p;
   const int64_t n = L / S;
@@ -122,7 +125,9 @@ PrefillLayout prefill_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d,
   p.cursor = cv.take<int32_t>((size_t)(BG * n));
   p.offs = cv.take<int32_t>((size_t)(BG * (n + 1)));
   p.tile_off = cv.take<int32_t>((size_t)(BG * (n + 1)));
-  p.entries_per_tile = hsa::prefill_entries_per_tile(dt_code(dt), Hq / Hkv, S);
+  p.entries_per_tile = entries_per_unit > 0
+                           ? entries_per_unit
+                           : hsa::prefill_entries_per_tile(dt_code(dt), Hq / Hkv, S);
   p.tiles_ub = prefill_entries(L, S, topk) / p.entries_per_tile + n + 1;
   p.tile_chunk = cv.take<int32_t>((size_t)(BG * p.tiles_ub));
   p.list = cv.take<int32_t>((size_t)(BG * L * topk));
@@ -133,18 +138,20 @@ PrefillLayout prefill_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d,
   return p;
 }
 
-// The backward's workspace: the forward's work list, per-row values in list
-// order and fp32 dK / dV accumulators.
+// The backward's workspace: the forward's work list with one work unit per
+// chunk (so a chunk's dK and dV are summed inside one block) and per-row
+// values in list order.
 struct BackwardLayout {
   PrefillLayout fwd;
-  float *lse2, *dw, *wk, *ds, *dk_acc, *dv_acc;
+  float *lse2, *dw, *wk, *ds;
   size_t bytes;
 };
 
 BackwardLayout backward_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d, int S,
                                int topk) {
   BackwardLayout p;
-  p.fwd = prefill_layout(ws, B, L, Hq, Hkv, d, S, topk, HSA_DTYPE_BF16);
+  // a token selects a chunk at most once: a chunk's list has at most L entries
+  p.fwd = prefill_layout(ws, B, L, Hq, Hkv, d, S, topk, HSA_DTYPE_BF16, 1, (int)(L > 0 ? L : 1));
   Carver cv(ws);
   cv.off = p.fwd.bytes;
   const size_t rows = (size_t)B * Hq * L * topk;
@@ -152,8 +159,6 @@ BackwardLayout backward_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int 
   p.dw = cv.take<float>(rows);
   p.wk = cv.take<float>(rows);
   p.ds = cv.take<float>(rows);
-  p.dk_acc = cv.take<float>((size_t)B * Hkv * L * d);
-  p.dv_acc = cv.take<float>((size_t)B * Hkv * L * d);
   p.bytes = cv.off + kAlign;
   return p;
 }
@@ -435,8 +440,6 @@ hsa_status_t hsa_prefill_backward(const void* Q, const void* K, const void* V, c
   ba.dw = lay.dw;
   ba.wk = lay.wk;
   ba.ds = lay.ds;
-  ba.dk_acc = lay.dk_acc;
-  ba.dv_acc = lay.dv_acc;
   ba.dQ = dQ;
   ba.dK = dK;
   ba.dV = dV;

@@ -101,4 +101,12 @@ __device__ __forceinline__ T wave_sum(T v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Block barrier ordering LDS accesses only: unlike __syncthreads(), global
+// loads issued before it (prefetches) stay in flight across it.
+__device__ __forceinline__ void block_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace hsa

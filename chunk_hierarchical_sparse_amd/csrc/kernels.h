@@ -131,9 +131,9 @@ hipError_t launch_dhsa_chunk_keys(const void* K, float* khat, const int32_t* off
                                   int chunk_end, hipStream_t stream);
 
 // ---- HSA prefill backward (prefill_bwd.hip) ---------------------------------
-// Reuses the forward's work list (select + invert outputs in p).  Per-row
-// values live in list order at partial_row(); p.partial (bf16) receives each
-// (row, slot)'s dQ piece.
+// Reuses the forward's work list (select + invert outputs in p), built with
+// one work unit per chunk.  Per-row values live in list order at
+// partial_row(); p.partial (bf16) receives each (row, slot)'s dQ piece.
 struct PrefillBwdArgs {
   PrefillArgs p;
   const void* dO;   // [B,Hq,L,d]
@@ -141,15 +141,13 @@ struct PrefillBwdArgs {
   float* dw;        // list order: dO . o_k, the gradient of the row's fusion weight
   float* wk;        // list order: fusion weight w_k
   float* ds;        // list order: gradient of the row's retrieval score
-  float* dk_acc;    // [B,Hkv,L,d] fp32 accumulators (zeroed by prefill_bwd_chunk)
-  float* dv_acc;
   void* dQ;         // [B,Hq,L,d] outputs, dtype of the inputs
   void* dK;         // [B,Hkv,L,d]
   void* dV;
 };
 // stages after landmarks / select / invert: score (part_score, lse2, dw), rows
-// (wk, ds), chunk (dK, dV accumulators, dQ pieces), finish (dQ gather, dK/dV
-// conversion)
+// (wk, ds), chunk (dK, dV of every selected chunk, zero elsewhere; dQ
+// pieces), finish (dQ gather)
 hipError_t prefill_bwd_score(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t prefill_bwd_rows(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t prefill_bwd_chunk(const PrefillBwdArgs& a, hipStream_t stream);

@@ -11,18 +11,19 @@
 //          (dO . v_j) from dP^T = V dO^T.  Nothing of size d is written.
 //  rows  : per (token, head): w = softmax(s) over the kept slots and
 //          ds_k = w_k (dw_k - sum_k' w_k' dw_k').
-//  chunk : per work unit, the chunk's K and V stay in LDS and each wave walks
-//          32-row tiles with the key on the lane: S = Q K^T and dP = dO V^T
-//          (MFMA), P = exp2(S - lse), dS = w P (dP - dw); then
+//  chunk : per chunk, its K and V stay in LDS and wave pairs walk 32-row
+//          tiles with the key on the lane (one wave per 32-key half):
+//          S = Q K^T and dP = dO V^T (MFMA), P = exp2(S - lse),
+//          dS = w P (dP - dw); then
 //             dV^T += dO^T (w P)                 (MFMA, registers)
 //             dK^T += Q^T (dS + ds / sqrt(S))   (MFMA; the landmark term:
 //                     lambda_c = sum_j k_j / sqrt(S) gives every key of the
 //                     chunk ds q / sqrt(d) / sqrt(S))
 //             dQ^T piece = K^T dS^T              (MFMA, dS through LDS)
-//          The unit's dK/dV sums meet in LDS and are added to fp32
-//          accumulators with global atomics (several units share hot chunks).
+//          A work unit holds a chunk's whole list, so the waves' dK/dV sums
+//          meet in LDS and are written once, as bf16.
 //  finish: per (token, head): dQ = sum of its slots' pieces + sum_k ds_k
-//          lambda_ck / sqrt(d); dK and dV accumulators converted to bf16.
+//          lambda_ck / sqrt(d).
 #include <math.h>
 
 #include "attn_core.h"
@@ -79,6 +80,11 @@ __device__ __forceinline__ void load_quads(uint16_t* dst, const uint16_t* __rest
       *(u32x2*)(&dst[(grp * D + cq * 4 + x) * 4]) = u32x2{lo, hi};
     }
   }
+}
+
+// The value of the neighbouring lane (lane ^ 1), by a DPP quad permute.
+__device__ __forceinline__ uint32_t swap_adjacent_lanes(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
 }
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -266,12 +272,19 @@ __global__ void __launch_bounds__(kThreads) bwd_rows_kernel(PrefillBwdArgs ba) {
 
 // ----------------------------------------------------------------- chunk --
 
+constexpr int kTPitch = 36;  // [dim][row] tiles: 32 rows + 4 pad (18 dwords: rows of
+                             // dims 8 apart fall 16 banks apart)
+constexpr int kRedPitch = 1;  // pad of the [key][dim] fp32 sums (lanes = keys)
+
+// A wave pair's tile buffers: the tile's Q and dO transposed as [dim][row]
+// (the A operand of dV^T and dK^T reads 4 consecutive rows of one dim), dS
+// as [row][key] (the B operand of dQ^T) and the rows' statistics.
 template <int D>
-struct WaveTiles {
-  uint16_t qq[8 * D * 4];  // the tile's Q rows, quad layout [row/4][dim][4]
-  uint16_t oq[8 * D * 4];  // the tile's dO rows, same layout
-  uint16_t dsl[32 * kDsPitch];  // dS, row-major [row][key]
-  float st[4][32];         // per row: lse2, dw, w, ds
+struct PairTiles {
+  uint16_t qt[D * kTPitch];
+  uint16_t ot[D * kTPitch];
+  uint16_t dsl[32 * kDsPitch];
+  float st[4][32];  // per row: lse2, dw, w, ds
 };
 
 template <int D>
@@ -280,13 +293,19 @@ struct ChunkSmem {
   uint16_t v[64 * (D + kRowPad)];
   uint16_t kq[16 * D * 4];
   union {
-    WaveTiles<D> w[kThreads / kWave];
-    float red[2][64 * D];  // the unit's dK, dV sums
+    PairTiles<D> t[2][2];                // [pair][iteration parity]
+    float red[2][64 * (D + kRedPitch)];  // the chunk's dK, dV sums
   } u;
 };
 
-// Lane = key: S = Q K^T, dP = dO V^T; accumulator register r of lane (j, h)
-// holds row 8(r/4) + 4h + r%4 of the tile and key 32 kt + j.
+// Waves form two pairs; pair p takes row tiles p, p + 2, ...  Within a
+// pair, the wave of key half kt computes S = Q K^T and dP = dO V^T for keys
+// 32 kt .. 32 kt + 31 (key on the lane: accumulator register r of lane
+// (j, h) holds row 8(r/4) + 4h + r%4 of the tile and key 32 kt + j), keeps
+// that half's dK^T and dV^T in registers, and produces dQ^T for dims
+// 64 kt .. 64 kt + 63 from the pair's whole dS tile.  The pair's tile
+// buffers alternate with the iteration parity, so a buffer is rewritten
+// only after the barrier that follows its last read.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) bwd_chunk_kernel(PrefillBwdArgs ba, float sl2,
                                                                 float sc, float rs) {
@@ -303,170 +322,211 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_chunk_kernel(PrefillBwdArgs b
   load_rows<D>(sm.k, (const uint16_t*)a.K + kv0, a.S);
   load_rows<D>(sm.v, (const uint16_t*)a.V + kv0, a.S);
   load_quads<D>(sm.kq, (const uint16_t*)a.K + kv0, a.S);
-  __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i32 = lane & 31, hf = lane >> 5;
+  const int pair = w >> 1, kt = w & 1;
+  const bool keys = 32 * kt < a.S;         // this wave's key half holds keys
+  const bool kval = 32 * kt + i32 < a.S;  // this lane's key exists
+  const int nks = a.S > 32 ? 4 : 2;       // 16-key steps of dQ
   const int32_t* list = a.list + bg * a.L * a.topk + e_begin;
   const int64_t qplane = a.L * D;
   const int64_t qbase = ((int64_t)b * a.Hq + (int64_t)g * G) * qplane;
-  const bool two = a.S > 32;
-  const int nks = two ? 4 : 2;  // 16-key steps of dQ
-  WaveTiles<D>& wt = sm.u.w[w];
-  const f32x16 zero = {};
-  f32x16 dk[D / 32][2], dv[D / 32][2];
-#pragma unroll
-  for (int bb = 0; bb < D / 32; ++bb)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      dk[bb][kt] = zero;
-      dv[bb][kt] = zero;
-    }
   const int64_t row0 = partial_row(a, bg, e_begin, 0);
-  for (int tile = w; tile < ntiles; tile += kThreads / kWave) {
-    const int r = tile * 32 + i32;
+  const f32x16 zero = {};
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int bb = 0; bb < D / 32; ++bb) {
+    dk[bb] = zero;
+    dv[bb] = zero;
+  }
+  const int iters = (ntiles + 1) / 2;
+  // rows of iteration i: list entries run two iterations ahead, Q / dO rows
+  // and the row statistics one iteration ahead of their use
+  auto entry_of = [&](int i) -> int32_t {
+    const int r = (2 * i + pair) * 32 + i32;
+    if (i >= iters || r >= rows) return -1;
     int ei, hh;
     split_row(r, G, a.log2G, ei, hh);
-    const int32_t entry = r < rows ? list[ei] : -1;
-    u32x4 q[D / 16], o[D / 16];
-    load_row_pair<D>(ba, qbase, qplane, entry, hh, hf, q, o);
-    // the tile's Q and dO rows into the quad layout (row i32, dims 16s+8hf+e)
+    return list[ei];
+  };
+  auto head_of = [&](int i) -> int {
+    int ei, hh;
+    split_row((2 * i + pair) * 32 + i32, G, a.log2G, ei, hh);
+    return hh;
+  };
+  const bool stat_lane = kt == 1 && hf == 0;
+  auto load_stats = [&](int i, int32_t e, f32x4& st4) {
+    const int64_t pr = row0 + (2 * i + pair) * 32 + i32;
+    st4 = f32x4{INFINITY, 0.f, 0.f, 0.f};
+    if (stat_lane && e >= 0) st4 = f32x4{ba.lse2[pr], ba.dw[pr], ba.wk[pr], ba.ds[pr]};
+  };
+  // one tile of the pair: rows of iteration it with their Q / dO rows and
+  // statistics already in registers
+  auto body = [&](int it, int32_t entry, const u32x4 (&q)[D / 16], const u32x4 (&o)[D / 16],
+                  const f32x4& st4) {
+    PairTiles<D>& pt = sm.u.t[pair][it & 1];
+    const int r = (2 * it + pair) * 32 + i32;
+    // the pair's tile buffers: Q rows from the kt = 0 wave, dO rows and the
+    // row statistics from the kt = 1 wave.  Lanes i32 and i32 ^ 1 hold
+    // adjacent rows: per pair of dims (2x, 2x+1) they swap one value so the
+    // even lane writes dim 2x of both rows and the odd lane dim 2x+1, one
+    // dword each.
+    uint16_t* tt = kt == 0 ? pt.qt : pt.ot;
+    const int odd = i32 & 1;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dim = 16 * s + 8 * hf + e;
-        const int at = ((i32 >> 2) * D + dim) * 4 + (i32 & 3);
-        const uint32_t qw = q[s][e >> 1], ow = o[s][e >> 1];
-        wt.qq[at] = (uint16_t)((e & 1) ? (qw >> 16) : (qw & 0xffffu));
-        wt.oq[at] = (uint16_t)((e & 1) ? (ow >> 16) : (ow & 0xffffu));
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t wv = kt == 0 ? q[s][x] : o[s][x];  // dims 2x, 2x+1 of this row
+        const uint32_t got = swap_adjacent_lanes(odd ? (wv & 0xffffu) : (wv >> 16));
+        const uint32_t word = odd ? (got | (wv & 0xffff0000u)) : ((wv & 0xffffu) | (got << 16));
+        const int dim = 16 * s + 8 * hf + 2 * x + odd;
+        *(uint32_t*)&tt[dim * kTPitch + (i32 & ~1)] = word;
       }
-    if (hf == 0) {
-      const bool ok = entry >= 0;
-      wt.st[0][i32] = ok ? ba.lse2[row0 + r] : INFINITY;
-      wt.st[1][i32] = ok ? ba.dw[row0 + r] : 0.f;
-      wt.st[2][i32] = ok ? ba.wk[row0 + r] : 0.f;
-      wt.st[3][i32] = ok ? ba.ds[row0 + r] : 0.f;
-    }
-    // S = Q K^T, dP = dO V^T (keys on lanes)
-    f32x16 sa[2], pa[2];
+    if (stat_lane) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sa[kt] = zero;
-      pa[kt] = zero;
-      if (kt == 1 && !two) break;
+      for (int f = 0; f < 4; ++f) pt.st[f][i32] = st4[f];
+    }
+    // S = Q K^T and dP = dO V^T for this wave's 32 keys
+    f32x16 sa = zero, pa = zero;
+    if (keys) {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         const int ko = (32 * kt + i32) * (D + kRowPad) + 16 * s + 8 * hf;
-        sa[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[s]),
-                                                         *(const bf16x8*)&sm.k[ko], sa[kt], 0, 0,
-                                                         0);
-        pa[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o[s]),
-                                                         *(const bf16x8*)&sm.v[ko], pa[kt], 0, 0,
-                                                         0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[s]),
+                                                     *(const bf16x8*)&sm.k[ko], sa, 0, 0, 0);
+        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o[s]),
+                                                     *(const bf16x8*)&sm.v[ko], pa, 0, 0, 0);
       }
     }
-    wave_sync_lds();
-    // Per key sub-tile: P = exp2(S - lse), w P, dS = w P (dP - dw) and
-    // dS' = dS + ds / sqrt(S) (keys past S are 0), packed to bf16 at once;
-    // then dV^T += dO^T (w P) and dK^T += Q^T dS' (the tile's rows are the
-    // contraction), and dS to LDS as [row][key] for dQ.  Row statistics of
-    // rows 8u + 4hf + 0..3 are read per u.
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      if (kt == 1 && !two) break;
-      const bool kval = 32 * kt + i32 < a.S;
+    block_sync_lds();  // the pair's Q/dO tiles and statistics are in LDS
+    if (keys) {
+      // P = exp2(S - lse), w P, dS = w P (dP - dw), dS' = dS + ds / sqrt(S)
+      // (keys past S are 0), packed to bf16 at once; dS to LDS for dQ
       bf16x8 bp[2], bs[2];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const f32x4 l4 = *(const f32x4*)&wt.st[0][8 * u + 4 * hf];
-        const f32x4 d4 = *(const f32x4*)&wt.st[1][8 * u + 4 * hf];
-        const f32x4 w4 = *(const f32x4*)&wt.st[2][8 * u + 4 * hf];
-        const f32x4 s4 = *(const f32x4*)&wt.st[3][8 * u + 4 * hf];
+        const f32x4 l4 = *(const f32x4*)&pt.st[0][8 * u + 4 * hf];
+        const f32x4 d4 = *(const f32x4*)&pt.st[1][8 * u + 4 * hf];
+        const f32x4 w4 = *(const f32x4*)&pt.st[2][8 * u + 4 * hf];
+        const f32x4 s4 = *(const f32x4*)&pt.st[3][8 * u + 4 * hf];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int rr = 4 * u + v;
-          const float p = kval ? fast_exp2(__builtin_fmaf(sa[kt][rr], sl2, -l4[v])) : 0.f;
+          const float p = kval ? fast_exp2(__builtin_fmaf(sa[rr], sl2, -l4[v])) : 0.f;
           const float wpv = w4[v] * p;
-          const float dsv = wpv * (pa[kt][rr] - d4[v]);
+          const float dsv = wpv * (pa[rr] - d4[v]);
           const float dsk = kval ? dsv + s4[v] * rs : 0.f;
           bp[u >> 1][4 * (u & 1) + v] = static_cast<__bf16>(wpv);
           bs[u >> 1][4 * (u & 1) + v] = static_cast<__bf16>(dsk);
-          wt.dsl[(8 * u + 4 * hf + v) * kDsPitch + 32 * kt + i32] =
+          pt.dsl[(8 * u + 4 * hf + v) * kDsPitch + 32 * kt + i32] =
               __builtin_bit_cast(uint16_t, static_cast<__bf16>(dsv));
         }
       }
+      // dV^T += dO^T (w P), dK^T += Q^T dS' (the tile's rows are the
+      // contraction, in the k-slot order of the score registers)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int g0 = 4 * s2 + hf, g1 = g0 + 2;
+        // k-slots 0..3 are rows 16 s2 + 4 hf + 0..3, k-slots 4..7 rows + 8
+        const int r0 = 16 * s2 + 4 * hf;
 #pragma unroll
         for (int bb = 0; bb < D / 32; ++bb) {
           const int dd = 32 * bb + i32;
-          const u32x2 o0 = *(const u32x2*)&wt.oq[(g0 * D + dd) * 4];
-          const u32x2 o1 = *(const u32x2*)&wt.oq[(g1 * D + dd) * 4];
-          const u32x2 q0 = *(const u32x2*)&wt.qq[(g0 * D + dd) * 4];
-          const u32x2 q1 = *(const u32x2*)&wt.qq[(g1 * D + dd) * 4];
-          dv[bb][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o1[0], o1[1]}), bp[s2], dv[bb][kt],
-              0, 0, 0);
-          dk[bb][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), bs[s2], dk[bb][kt],
-              0, 0, 0);
+          const u32x2 o0 = *(const u32x2*)&pt.ot[dd * kTPitch + r0];
+          const u32x2 o1 = *(const u32x2*)&pt.ot[dd * kTPitch + r0 + 8];
+          const u32x2 q0 = *(const u32x2*)&pt.qt[dd * kTPitch + r0];
+          const u32x2 q1 = *(const u32x2*)&pt.qt[dd * kTPitch + r0 + 8];
+          dv[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o1[0], o1[1]}), bp[s2], dv[bb], 0, 0,
+              0);
+          dk[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), bs[s2], dk[bb], 0, 0,
+              0);
         }
       }
     }
-    wave_sync_lds();
-    f32x16 dq[D / 32];
+    block_sync_lds();  // the pair's dS tile is complete
+    // dQ^T = K^T dS^T for dims 64 kt .. 64 kt + 63 over all keys
+    f32x16 dq[D / 64];
 #pragma unroll
-    for (int bb = 0; bb < D / 32; ++bb) {
-      dq[bb] = zero;
+    for (int b2 = 0; b2 < D / 64; ++b2) {
+      const int bb = (D / 64) * kt + b2;
+      dq[b2] = zero;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if (s >= nks) break;
-        const bf16x8 bsv = *(const bf16x8*)&wt.dsl[i32 * kDsPitch + 16 * s + 8 * hf];
+        const bf16x8 bsv = *(const bf16x8*)&pt.dsl[i32 * kDsPitch + 16 * s + 8 * hf];
         const int g0 = 4 * s + 2 * hf, g1 = g0 + 1;
         const int dd = 32 * bb + i32;
         const u32x2 k0 = *(const u32x2*)&sm.kq[(g0 * D + dd) * 4];
         const u32x2 k1 = *(const u32x2*)&sm.kq[(g1 * D + dd) * 4];
-        dq[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), bsv, dq[bb], 0, 0, 0);
+        dq[b2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), bsv, dq[b2], 0, 0, 0);
       }
     }
     if (entry >= 0) {
       uint16_t* po = (uint16_t*)a.partial + (row0 + r) * D;
 #pragma unroll
-      for (int bb = 0; bb < D / 32; ++bb)
+      for (int b2 = 0; b2 < D / 64; ++b2)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int dd = 32 * bb + 8 * q4 + 4 * hf;
-          const u32x2 v = {pack_bf16x2(dq[bb][4 * q4] * sc, dq[bb][4 * q4 + 1] * sc),
-                           pack_bf16x2(dq[bb][4 * q4 + 2] * sc, dq[bb][4 * q4 + 3] * sc)};
+          const int dd = 32 * ((D / 64) * kt + b2) + 8 * q4 + 4 * hf;
+          const u32x2 v = {pack_bf16x2(dq[b2][4 * q4] * sc, dq[b2][4 * q4 + 1] * sc),
+                           pack_bf16x2(dq[b2][4 * q4 + 2] * sc, dq[b2][4 * q4 + 3] * sc)};
           *(u32x2*)(po + dd) = v;
         }
     }
-    // the next tile rewrites this wave's LDS tiles only after every lane read them
-    wave_sync_lds();
+  };
+  // two register sets: the next tile's rows load during the current tile,
+  // list entries run one tile further ahead
+  int32_t ea = entry_of(0), eb = entry_of(1);
+  u32x4 qa[D / 16], oa[D / 16], qb[D / 16], ob[D / 16];
+  f32x4 sta, stb;
+  load_row_pair<D>(ba, qbase, qplane, ea, head_of(0), hf, qa, oa);
+  load_stats(0, ea, sta);
+  for (int it = 0; it < iters; it += 2) {
+    const int32_t ec = entry_of(it + 2);
+    load_row_pair<D>(ba, qbase, qplane, eb, head_of(it + 1), hf, qb, ob);
+    load_stats(it + 1, eb, stb);
+    body(it, ea, qa, oa, sta);
+    if (it + 1 >= iters) break;
+    const int32_t ed = entry_of(it + 3);
+    load_row_pair<D>(ba, qbase, qplane, ec, head_of(it + 2), hf, qa, oa);
+    load_stats(it + 2, ec, sta);
+    body(it + 1, eb, qb, ob, stb);
+    ea = ec;
+    eb = ed;
   }
-  // the unit's dK / dV: sum the waves in LDS, then one global atomic each
+  // the chunk's dK / dV: the two pairs' halves summed in LDS
+  constexpr int RP = D + kRedPitch;
   __syncthreads();
-  for (int x = threadIdx.x; x < 2 * 64 * D; x += kThreads) (&sm.u.red[0][0])[x] = 0.f;
+  for (int x = threadIdx.x; x < 2 * 64 * RP; x += kThreads) (&sm.u.red[0][0])[x] = 0.f;
   __syncthreads();
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  if (kval) {
     const int key = 32 * kt + i32;
-    if (key >= a.S) continue;
 #pragma unroll
     for (int bb = 0; bb < D / 32; ++bb)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int dim = 32 * bb + 8 * (rr >> 2) + 4 * hf + (rr & 3);
-        atomicAdd(&sm.u.red[0][key * D + dim], dk[bb][kt][rr]);
-        atomicAdd(&sm.u.red[1][key * D + dim], dv[bb][kt][rr]);
+        atomicAdd(&sm.u.red[0][key * RP + dim], dk[bb][rr]);
+        atomicAdd(&sm.u.red[1][key * RP + dim], dv[bb][rr]);
       }
   }
   __syncthreads();
-  for (int x = threadIdx.x; x < a.S * D; x += kThreads) {
-    atomicAdd(&ba.dk_acc[kv0 + x], sm.u.red[0][x] * sc);
-    atomicAdd(&ba.dv_acc[kv0 + x], sm.u.red[1][x]);
+  // the block holds the chunk's whole list: its rows of dK and dV are final
+  for (int x = threadIdx.x; x < a.S * D / 8; x += kThreads) {
+    const int key = x / (D / 8), d0 = 8 * (x % (D / 8));
+    const float* kr = &sm.u.red[0][key * RP + d0];
+    const float* vr = &sm.u.red[1][key * RP + d0];
+    u32x4 ko, vo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ko[j] = pack_bf16x2(kr[2 * j] * sc, kr[2 * j + 1] * sc);
+      vo[j] = pack_bf16x2(vr[2 * j], vr[2 * j + 1]);
+    }
+    *(u32x4*)((uint16_t*)ba.dK + kv0 + 8 * x) = ko;
+    *(u32x4*)((uint16_t*)ba.dV + kv0 + 8 * x) = vo;
   }
 }
 
@@ -526,17 +586,6 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(PrefillBwdArgs ba, flo
             pack_bf16x2(acc[6], acc[7])};
 }
 
-// fp32 accumulators -> bf16 outputs, 8 elements per thread.
-__global__ void __launch_bounds__(kThreads) bwd_convert_kernel(const float* __restrict__ src,
-                                                               uint16_t* __restrict__ dst,
-                                                               int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a0 = *(const f32x4*)(src + 8 * i), a1 = *(const f32x4*)(src + 8 * i + 4);
-  *(u32x4*)(dst + 8 * i) = u32x4{pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
-                                 pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3])};
-}
-
 template <int D>
 hipError_t finish_d(const PrefillBwdArgs& ba, hipStream_t stream) {
   const PrefillArgs& a = ba.p;
@@ -550,13 +599,6 @@ hipError_t finish_d(const PrefillBwdArgs& ba, hipStream_t stream) {
     bwd_dq_kernel<D, 16><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
   else
     bwd_dq_kernel<D, 32><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n8 = (int64_t)a.B * a.Hkv * a.L * D / 8;
-  const unsigned cb = (unsigned)((n8 + kThreads - 1) / kThreads);
-  bwd_convert_kernel<<<dim3(cb), dim3(kThreads), 0, stream>>>(ba.dk_acc, (uint16_t*)ba.dK, n8);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  bwd_convert_kernel<<<dim3(cb), dim3(kThreads), 0, stream>>>(ba.dv_acc, (uint16_t*)ba.dV, n8);
   return hipGetLastError();
 }
 
@@ -591,10 +633,11 @@ hipError_t prefill_bwd_rows(const PrefillBwdArgs& ba, hipStream_t stream) {
 
 hipError_t prefill_bwd_chunk(const PrefillBwdArgs& ba, hipStream_t stream) {
   const PrefillArgs& a = ba.p;
-  const int64_t n_acc = (int64_t)a.B * a.Hkv * a.L * a.d;
-  hipError_t e = launch_fill_i32((int32_t*)ba.dk_acc, n_acc, 0, stream);
+  // keys of chunks no row selected (and of a trailing partial chunk) get zero
+  const int64_t words = (int64_t)a.B * a.Hkv * a.L * a.d / 2;  // bf16 pairs
+  hipError_t e = launch_fill_i32((int32_t*)ba.dK, words, 0, stream);
   if (e != hipSuccess) return e;
-  if ((e = launch_fill_i32((int32_t*)ba.dv_acc, n_acc, 0, stream)) != hipSuccess) return e;
+  if ((e = launch_fill_i32((int32_t*)ba.dV, words, 0, stream)) != hipSuccess) return e;
   if (a.n == 0) return hipSuccess;
   const int64_t blocks = (int64_t)a.B * a.Hkv * a.tiles_ub;
   const float sc = 1.0f / sqrtf((float)a.d);

@@ -143,8 +143,9 @@ hsa_status_t hsa_prefill_interval(const void* Q, const void* K, const void* V, c
  *   dQ [B,Hq,L,d], dK, dV [B,Hkv,L,d] bf16, written.
  *   workspace of at least hsa_prefill_backward_workspace_size(...) bytes.
  * Limits: as hsa_prefill, plus bf16 only and S <= 64 (HSA_ERR_UNSUPPORTED
- * otherwise).  Gradients are accumulated in fp32; dK and dV sum with global
- * atomics, so their last bits may differ from run to run.
+ * otherwise).  Gradients are accumulated in fp32; a chunk's dK and dV rows
+ * sum the waves of one block with LDS atomics, so their last bits may differ
+ * from run to run.
  */
 size_t hsa_prefill_backward_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S,
                                            int topk, hsa_dtype_t dtype);
