@@ -251,13 +251,28 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
     li[j] = -1;
   }
   const float* lmk = a.lmk + bg * a.n * D;
+  // the next landmark tile is loaded into registers while the current one is
+  // scored: thread e takes float4 pieces e, e + 256, ... of the 32 x D tile
+  constexpr int NPT = TILE * D / 4 / kThreads;
+  f32x4 nxt[NPT];
+  auto fetch = [&](int64_t cb) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int row = (e * 4) / D, col = (e * 4) % D;
+      nxt[i] = cb + row < bavail ? *(const f32x4*)(lmk + (cb + row) * D + col)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (bavail > 0) fetch(0);
   for (int64_t c0 = 0; c0 < bavail; c0 += TILE) {
     __syncthreads();
-    // stage 32 landmark rows as three bf16 planes
-    for (int e = threadIdx.x; e < TILE * D / 4; e += kThreads) {
+    // stage the 32 landmark rows as three bf16 planes
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int e = threadIdx.x + i * kThreads;
       const int row = (e * 4) / D, col = (e * 4) % D;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (c0 + row < bavail) v = *(const f32x4*)(lmk + (c0 + row) * D + col);
+      const f32x4 v = nxt[i];
       uint16_t h[4], l[4], m[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) split3_bf16(v[x], h[x], l[x], m[x]);
@@ -269,6 +284,7 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
                                                 (uint32_t)m[2] | ((uint32_t)m[3] << 16)};
     }
     __syncthreads();
+    if (c0 + TILE < bavail) fetch(c0 + TILE);
     if (c0 >= wavail) continue;  // wave-uniform: no query of this wave sees these chunks
     f32x16 acc;
 #pragma unroll
