@@ -19,7 +19,7 @@
 //             dK^T += Q^T (dS + ds / sqrt(S))   (MFMA; the landmark term:
 //                     lambda_c = sum_j k_j / sqrt(S) gives every key of the
 //                     chunk ds q / sqrt(d) / sqrt(S))
-//             dQ^T piece = K^T dS^T              (MFMA, dS through LDS)
+//             dQ^T piece = K^T dS^T / sqrt(d)    (MFMA, dS through LDS)
 //          A work unit holds a chunk's whole list, so the waves' dK/dV sums
 //          meet in LDS and are written once, as bf16.
 //  finish: per (token, head): dQ = sum of its slots' pieces + sum_k ds_k
@@ -373,13 +373,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_chunk_kernel(PrefillBwdArgs b
     // dword each.
     uint16_t* tt = kt == 0 ? pt.qt : pt.ot;
     const int odd = i32 & 1;
+    // v_perm_b32 picks bytes of {got, own}: the even lane keeps the low
+    // halves (own, then the partner's), the odd lane the high halves
+    const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const uint32_t wv = kt == 0 ? q[s][x] : o[s][x];  // dims 2x, 2x+1 of this row
-        const uint32_t got = swap_adjacent_lanes(odd ? (wv & 0xffffu) : (wv >> 16));
-        const uint32_t word = odd ? (got | (wv & 0xffff0000u)) : ((wv & 0xffffu) | (got << 16));
+        const uint32_t word = __builtin_amdgcn_perm(swap_adjacent_lanes(wv), wv, psel);
         const int dim = 16 * s + 8 * hf + 2 * x + odd;
         *(uint32_t*)&tt[dim * kTPitch + (i32 & ~1)] = word;
       }
@@ -402,7 +404,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_chunk_kernel(PrefillBwdArgs b
     block_sync_lds();  // the pair's Q/dO tiles and statistics are in LDS
     if (keys) {
       // P = exp2(S - lse), w P, dS = w P (dP - dw), dS' = dS + ds / sqrt(S)
-      // (keys past S are 0), packed to bf16 at once; dS to LDS for dQ
+      // (keys past S are 0; no masking when the wave's 32 keys all exist),
+      // packed to bf16 at once; dS / sqrt(d) to LDS for dQ
+      const bool kfull = 32 * kt + 32 <= a.S;
+      const float kon = kval ? 1.f : 0.f;
       bf16x8 bp[2], bs[2];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -413,14 +418,16 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_chunk_kernel(PrefillBwdArgs b
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int rr = 4 * u + v;
-          const float p = kval ? fast_exp2(__builtin_fmaf(sa[rr], sl2, -l4[v])) : 0.f;
+          float p = fast_exp2(__builtin_fmaf(sa[rr], sl2, -l4[v]));
+          if (!kfull) p *= kon;
           const float wpv = w4[v] * p;
           const float dsv = wpv * (pa[rr] - d4[v]);
-          const float dsk = kval ? dsv + s4[v] * rs : 0.f;
+          float dsk = __builtin_fmaf(s4[v], rs, dsv);
+          if (!kfull) dsk *= kon;
           bp[u >> 1][4 * (u & 1) + v] = static_cast<__bf16>(wpv);
           bs[u >> 1][4 * (u & 1) + v] = static_cast<__bf16>(dsk);
           pt.dsl[(8 * u + 4 * hf + v) * kDsPitch + 32 * kt + i32] =
-              __builtin_bit_cast(uint16_t, static_cast<__bf16>(dsv));
+              __builtin_bit_cast(uint16_t, static_cast<__bf16>(dsv * sc));
         }
       }
       // dV^T += dO^T (w P), dK^T += Q^T dS' (the tile's rows are the
@@ -471,8 +478,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_chunk_kernel(PrefillBwdArgs b
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int dd = 32 * ((D / 64) * kt + b2) + 8 * q4 + 4 * hf;
-          const u32x2 v = {pack_bf16x2(dq[b2][4 * q4] * sc, dq[b2][4 * q4 + 1] * sc),
-                           pack_bf16x2(dq[b2][4 * q4 + 2] * sc, dq[b2][4 * q4 + 3] * sc)};
+          const u32x2 v = {pack_bf16x2(dq[b2][4 * q4], dq[b2][4 * q4 + 1]),
+                           pack_bf16x2(dq[b2][4 * q4 + 2], dq[b2][4 * q4 + 3])};
           *(u32x2*)(po + dd) = v;
         }
     }
