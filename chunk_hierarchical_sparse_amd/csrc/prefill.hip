@@ -709,7 +709,8 @@ __global__ void __launch_bounds__(kThreads, 2)
         outv[bb][pr] = hf ? u32x4{got0, got1, d0, d1} : u32x4{e0, e1, got0, got1};
       }
     if (ent_cur >= 0) {
-      // rows of a tile are consecutive: (entry e_begin + r / G, head r % G)
+      // rows of a tile are consecutive: (entry e_begin + r / G, head r % G).
+      // The partials are read once, by the fusion: streaming stores.
       const int64_t row = partial_row(a, bg, e_begin, 0) + tile * 32 + i32;
       if (hf == 0) a.part_score[row] = sh * score_scale;
       uint16_t* po = (uint16_t*)a.partial + row * D;
@@ -717,7 +718,7 @@ __global__ void __launch_bounds__(kThreads, 2)
       for (int bb = 0; bb < D / 32; ++bb)
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr)
-          *(u32x4*)(po + 32 * bb + 8 * (2 * pr + hf)) = outv[bb][pr];
+          __builtin_nontemporal_store(outv[bb][pr], (u32x4*)(po + 32 * bb + 8 * (2 * pr + hf)));
     }
   };
 
