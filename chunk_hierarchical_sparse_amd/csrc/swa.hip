@@ -153,8 +153,7 @@ __global__ void __launch_bounds__(kDecWaves * kWave) decode_kernel(SwaArgs a, fl
     qs[x / D][x % D] = load_elem<DT>(a.Q, ((int64_t)b * a.Hq + h0 + x / D) * D + x % D);
   __syncthreads();
   const int64_t k0 = max((int64_t)0, a.n_ctx - a.window);
-  const int n = (int)(a.n_ctx - k0);
-  const int np = (n + kPiece - 1) / kPiece;
+  const int64_t np = (a.n_ctx - k0 + kPiece - 1) / kPiece;  // 64-key pieces of the window
   const int64_t kv0 = bg * a.L * D;
   float m[GT], l[GT], o[GT][CPL];
 #pragma unroll
@@ -167,7 +166,7 @@ __global__ void __launch_bounds__(kDecWaves * kWave) decode_kernel(SwaArgs a, fl
   typedef typename std::conditional<
       DT == kF32, typename std::conditional<CPL == 2, f32x2, float>::type,
       typename std::conditional<CPL == 2, uint32_t, uint16_t>::type>::type VT;
-  for (int pc = w; pc < np; pc += kDecWaves) {
+  for (int64_t pc = w; pc < np; pc += kDecWaves) {
     const int64_t start = k0 + (int64_t)pc * kPiece;
     const int nk = (int)min((int64_t)kPiece, a.n_ctx - start);
     // keys past nk re-read the piece's last key (in bounds, weight zero)
@@ -254,7 +253,7 @@ __global__ void __launch_bounds__(kDecWaves * kWave) decode_kernel(SwaArgs a, fl
   }
   __syncthreads();
   // merge the waves' partials: waves without a piece hold m = -inf, l = 0
-  const int nw = min(np, kDecWaves);
+  const int nw = (int)min(np, (int64_t)kDecWaves);
   for (int x = threadIdx.x; x < GT * D; x += kDecWaves * kWave) {
     const int hh = x / D, dx = x % D;
     float M = -INFINITY;
