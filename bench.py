@@ -83,6 +83,17 @@ def traffic_for(workload):
     return rec["traffic_bytes"]
 
 
+def hbm_view(traffic, ms):
+    """The kernel's counter-measured HBM bytes per launch over its measured
+    duration, against the HBM peak: how close the schedule's own traffic
+    runs to the memory roofline (null without counter data)."""
+    if traffic is None or not ms:
+        return None
+    gbps = traffic / (ms * 1e-3) / 1e9
+    return {"bytes_per_launch": traffic, "achieved": gbps, "unit": "GB/s",
+            "peak": PEAK_HBM_GBPS, "frac": gbps / PEAK_HBM_GBPS}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -160,7 +171,8 @@ def bench_prefill(torch, hsa, args):
         roofline={"bound": "mfma", "kernel": "attend (chunk attention, bf16 MFMA)",
                   "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                   "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("hsa_prefill"),
-                  "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": attn_ms},
+                  "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": attn_ms,
+                  "hbm_view": hbm_view(traffic_for("hsa_prefill"), attn_ms)},
         stages_ms=dict(zip(["landmarks", "select", "invert", "attend", "fuse"], stages)),
         whole_path={"gflop": total_flop / 1e9,
                     "tflops": total_flop / (ms * 1e-3) / 1e12,
@@ -201,7 +213,8 @@ def bench_prefill_interval(torch, hsa, args, inputs, R=8):
         roofline={"bound": "mfma", "kernel": "attend (chunk attention, bf16 MFMA)",
                   "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                   "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("hsa_prefill_r8"),
-                  "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": attn_ms},
+                  "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": attn_ms,
+                  "hbm_view": hbm_view(traffic_for("hsa_prefill_r8"), attn_ms)},
         stages_ms=dict(zip(["landmarks", "select", "invert", "attend", "fuse"], stages)))
     del q, k, v, out, ws
     torch.cuda.empty_cache()
@@ -292,7 +305,8 @@ def bench_dhsa(torch, hsa, args):
         roofline={"bound": "mfma", "kernel": "attend (block-sparse masked attention)",
                   "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                   "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("dhsa_prefill"),
-                  "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": stages[3]},
+                  "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": stages[3],
+                  "hbm_view": hbm_view(traffic_for("dhsa_prefill"), stages[3])},
         stages_ms=dict(zip(["pool", "sc", "rank", "attend", "mask"], stages)))
     del q, k, v, out, ws
     torch.cuda.empty_cache()
@@ -381,7 +395,8 @@ def bench_backward(torch, hsa, args, inputs):
                   "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                   "frac": achieved / PEAK_BF16_TFLOPS,
                   "traffic": traffic_for("hsa_prefill_backward"),
-                  "algorithmic_gflop_per_launch": chunk_flop / 1e9, "avg_launch_ms": stages[5]},
+                  "algorithmic_gflop_per_launch": chunk_flop / 1e9, "avg_launch_ms": stages[5],
+                  "hbm_view": hbm_view(traffic_for("hsa_prefill_backward"), stages[5])},
         stages_ms=dict(zip(["landmarks", "select", "invert", "score", "rows", "chunk", "finish"],
                            stages)))
     del q, k, v, dO, grads, ws
@@ -413,7 +428,8 @@ def bench_swa(torch, hsa, args, inputs, W=512):
         roofline={"bound": "mfma", "kernel": "sliding-window attention (bf16 MFMA)",
                   "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                   "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("swa_prefill"),
-                  "algorithmic_gflop_per_launch": flop / 1e9, "avg_launch_ms": stages[0]},
+                  "algorithmic_gflop_per_launch": flop / 1e9, "avg_launch_ms": stages[0],
+                  "hbm_view": hbm_view(traffic_for("swa_prefill"), stages[0])},
         stages_ms={"attend": stages[0]})
     del q, k, v, out
     torch.cuda.empty_cache()
