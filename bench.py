@@ -49,7 +49,7 @@ DOMINANT = {
                      ["dhsa.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
     "dhsa_decode": ("attend_kernel<128, 1>", "DhsaDecodeArgs",
                     ["dhsa_decode.hip", "hsa_common.h", "kernels.h"]),
-    "hsa_prefill_backward": ("bwd_chunk_kernel<128>", "PrefillBwdArgs",
+    "hsa_prefill_backward": ("bwd_kv_kernel<128>", "PrefillBwdArgs",
                              ["prefill_bwd.hip", "prefill_common.h", "attn_core.h",
                               "hsa_common.h", "kernels.h"]),
     "swa_prefill": ("prefill_bf16_kernel<128, 4>", "SwaArgs",
@@ -381,24 +381,24 @@ def bench_backward(torch, hsa, args, inputs):
         hsa.hsa_prefill_backward(q, k, v, dO, S, topk, workspace=ws, grads=grads)
 
     log("backward: timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 7)
+    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 8)
     sel, _ = prefill_counts(L, S, topk)
     rows = B * Hq * sel  # (token, head, selected chunk) rows
-    # chunk stage per row: S = Q K^T, dP = dO V^T, dV, dK and dQ products
-    chunk_flop = rows * S * d * 2 * 5
-    achieved = chunk_flop / (stages[5] * 1e-3) / 1e12
+    # kv stage per row: S = Q K^T, dP = dO V^T, dV and dK products
+    kv_flop = rows * S * d * 2 * 4
+    achieved = kv_flop / (stages[6] * 1e-3) / 1e12
     res = dict(
         value=B * L / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
         config={"workload": "hsa_prefill_backward", "B": B, "L": L, "Hq": Hq, "Hkv": Hkv,
                 "d": d, "S": S, "topk": topk, "inputs": "0.5*N(0,1) bf16 Q/K/V, N(0,1) dO, seed 2"},
-        roofline={"bound": "mfma", "kernel": "chunk (dK, dV, dQ pieces; bf16 MFMA)",
+        roofline={"bound": "mfma", "kernel": "kv (dK, dV; bf16 MFMA)",
                   "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                   "frac": achieved / PEAK_BF16_TFLOPS,
                   "traffic": traffic_for("hsa_prefill_backward"),
-                  "algorithmic_gflop_per_launch": chunk_flop / 1e9, "avg_launch_ms": stages[5],
-                  "hbm_view": hbm_view(traffic_for("hsa_prefill_backward"), stages[5])},
-        stages_ms=dict(zip(["landmarks", "select", "invert", "score", "rows", "chunk", "finish"],
-                           stages)))
+                  "algorithmic_gflop_per_launch": kv_flop / 1e9, "avg_launch_ms": stages[6],
+                  "hbm_view": hbm_view(traffic_for("hsa_prefill_backward"), stages[6])},
+        stages_ms=dict(zip(["landmarks", "select", "invert", "weights", "score", "rows", "kv",
+                            "finish"], stages)))
     del q, k, v, dO, grads, ws
     torch.cuda.empty_cache()
     return res

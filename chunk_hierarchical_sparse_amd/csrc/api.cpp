@@ -455,11 +455,14 @@ hsa_status_t hsa_prefill_backward(const void* Q, const void* K, const void* V, c
   pm.mark();
   if ((e = hsa::prefill_invert(ba.p, st)) != hipSuccess) return hip_fail(e, "invert");
   pm.mark();
+  if ((e = hsa::prefill_bwd_weights(ba, st)) != hipSuccess)
+    return hip_fail(e, "backward weights");
+  pm.mark();
   if ((e = hsa::prefill_bwd_score(ba, st)) != hipSuccess) return hip_fail(e, "backward score");
   pm.mark();
   if ((e = hsa::prefill_bwd_rows(ba, st)) != hipSuccess) return hip_fail(e, "backward rows");
   pm.mark();
-  if ((e = hsa::prefill_bwd_chunk(ba, st)) != hipSuccess) return hip_fail(e, "backward chunk");
+  if ((e = hsa::prefill_bwd_kv(ba, st)) != hipSuccess) return hip_fail(e, "backward kv");
   pm.mark();
   if ((e = hsa::prefill_bwd_finish(ba, st)) != hipSuccess) return hip_fail(e, "backward finish");
   pm.mark();

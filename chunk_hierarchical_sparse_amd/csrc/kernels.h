@@ -145,12 +145,13 @@ struct PrefillBwdArgs {
   void* dK;         // [B,Hkv,L,d]
   void* dV;
 };
-// stages after landmarks / select / invert: score (part_score, lse2, dw), rows
-// (wk, ds), chunk (dK, dV of every selected chunk, zero elsewhere; dQ
-// pieces), finish (dQ gather)
+// stages after landmarks / select / invert: weights (wk), score (lse2, dw, dQ
+// pieces), rows (ds), kv (dK, dV of every selected chunk, zero elsewhere),
+// finish (dQ gather)
+hipError_t prefill_bwd_weights(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t prefill_bwd_score(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t prefill_bwd_rows(const PrefillBwdArgs& a, hipStream_t stream);
-hipError_t prefill_bwd_chunk(const PrefillBwdArgs& a, hipStream_t stream);
+hipError_t prefill_bwd_kv(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t prefill_bwd_finish(const PrefillBwdArgs& a, hipStream_t stream);
 
 // ---- sliding-window attention (swa.hip) ------------------------------------

@@ -4,24 +4,26 @@
 // top-K selection itself is piecewise constant and held fixed).
 //
 // With the forward's selection and chunk-major work list already built:
-//  score : one block per work unit (a run of one chunk's (token, head) rows)
-//          recomputes, on MFMA, each row's in-chunk logits S^T = K Q^T, its
-//          log-sum-exp, its retrieval score s = q . lambda_c (split-bf16
-//          landmark rows, fp32 accurate) and dw = dO . o_k = sum_j p_j
-//          (dO . v_j) from dP^T = V dO^T.  Nothing of size d is written.
-//  rows  : per (token, head): w = softmax(s) over the kept slots and
-//          ds_k = w_k (dw_k - sum_k' w_k' dw_k').
-//  chunk : per chunk, its K and V stay in LDS and wave pairs walk 32-row
-//          tiles with the key on the lane (one wave per 32-key half):
-//          S = Q K^T and dP = dO V^T (MFMA), P = exp2(S - lse),
-//          dS = w P (dP - dw); then
+//  weights: per (token, group), each head: the retrieval scores s_k =
+//          q . lambda_ck / sqrt(d) of the kept chunks and the fusion weights
+//          w = softmax(s).
+//  score : one block per chunk (its whole list of (token, head) rows), the
+//          chunk's K and V in LDS, lane = row as in the forward's chunk
+//          attention: S^T = K Q^T and dP^T = V dO^T (MFMA), the row's
+//          log-sum-exp and dw = dO . o_k = sum_j p_j dP_j, then
+//          dS^T = w P^T (dP^T - dw) and the row's dQ piece
+//          K^T dS^T / sqrt(d) (MFMA, K^T in the key-quad layout).
+//  rows  : per (token, head): ds_k = w_k (dw_k - sum_k' w_k' dw_k').
+//  kv    : one block per chunk again, lane = key: each wave owns one 32-key
+//          half and walks its own row tiles with no barrier: S = Q K^T,
+//          dP = dO V^T, P = exp2(S - lse); Q^T and dO^T come from products
+//          with a 0/1 selector; then
 //             dV^T += dO^T (w P)                 (MFMA, registers)
 //             dK^T += Q^T (dS + ds / sqrt(S))   (MFMA; the landmark term:
 //                     lambda_c = sum_j k_j / sqrt(S) gives every key of the
 //                     chunk ds q / sqrt(d) / sqrt(S))
-//             dQ^T piece = K^T dS^T / sqrt(d)    (MFMA, dS through LDS)
-//          A work unit holds a chunk's whole list, so the waves' dK/dV sums
-//          meet in LDS and are written once, as bf16.
+//          The block holds the chunk's whole list, so its waves' sums meet
+//          in LDS and are written once, as bf16.
 //  finish: per (token, head): dQ = sum of its slots' pieces + sum_k ds_k
 //          lambda_ck / sqrt(d).
 #include <math.h>
@@ -36,7 +38,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowPad = 8;    // LDS row padding (elements) of row-major tiles
-constexpr int kDsPitch = 72;  // LDS row pitch of a wave's dS tile (64 keys + pad)
 
 // Rows [0, nk) of a [rows, D] bf16 block into LDS, row-major with rows
 // padded by kRowPad elements; rows nk..63 are zero.  All threads call.
@@ -82,11 +83,6 @@ __device__ __forceinline__ void load_quads(uint16_t* dst, const uint16_t* __rest
   }
 }
 
-// The value of the neighbouring lane (lane ^ 1), by a DPP quad permute.
-__device__ __forceinline__ uint32_t swap_adjacent_lanes(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-}
-
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -128,19 +124,90 @@ __device__ __forceinline__ void load_row_pair(const PrefillBwdArgs& ba, int64_t 
   }
 }
 
+
+// ---------------------------------------------------------------- weights --
+
+// One group of D/8 threads per (b, group, token), 8 dims each: the kept
+// chunks' landmark segments stay in registers while each head of the group
+// takes s_k = q . lambda_ck / sqrt(d) and w = softmax(s), written at the
+// slots' list positions.
+template <int D, int KM>
+__global__ void __launch_bounds__(kThreads) bwd_weights_kernel(PrefillBwdArgs ba, float sc) {
+  const PrefillArgs& a = ba.p;
+  constexpr int TPR = D / 8;
+  constexpr int RPB = kThreads / TPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int cg = threadIdx.x % TPR;
+  if (r >= (int64_t)a.B * a.Hkv * a.L) return;  // whole groups of TPR threads leave together
+  const int G = a.Hq / a.Hkv;
+  const int64_t t = r % a.L;
+  const int64_t bg = r / a.L;
+  const int64_t b = bg / a.Hkv;
+  const int g = (int)(bg % a.Hkv);
+  const int m = (int)min((int64_t)a.topk, min(t / a.S, a.n));
+  const int32_t* sel = a.idx + (bg * a.nq + t) * a.topk;
+  const int32_t* epos = a.entry_pos + (bg * a.L + t) * a.topk;
+  f32x4 lam[KM][2];
+  int32_t ep[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    lam[k][0] = lam[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ep[k] = k < m ? epos[k] : 0;
+    if (k < m) {
+      const float* lc = a.lmk + (bg * a.n + sel[k]) * D + cg * 8;
+      lam[k][0] = *(const f32x4*)lc;
+      lam[k][1] = *(const f32x4*)(lc + 4);
+    }
+  }
+  for (int hh = 0; hh < G; ++hh) {
+    const u32x4 qv = *(const u32x4*)((const uint16_t*)a.Q +
+                                     ((b * a.Hq + g * G + hh) * a.L + t) * D + cg * 8);
+    float qf[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      qf[2 * v] = bf16_bits_to_f32(qv[v] & 0xffffu);
+      qf[2 * v + 1] = bf16_bits_to_f32(qv[v] >> 16);
+    }
+    float s[KM];
+    float smax = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      float acc = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc += qf[v] * lam[k][0][v] + qf[4 + v] * lam[k][1][v];
+#pragma unroll
+      for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+      s[k] = k < m ? acc * sc : -INFINITY;
+      smax = fmaxf(smax, s[k]);
+    }
+    float z = 0.f;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      s[k] = k < m ? expf(s[k] - smax) : 0.f;
+      z += s[k];
+    }
+    if (cg == 0) {
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+        if (k < m) ba.wk[partial_row(a, bg, ep[k], hh)] = s[k] / z;
+    }
+  }
+}
+
 // ----------------------------------------------------------------- score --
 
 template <int D>
 struct ScoreSmem {
-  uint16_t k[64 * (D + kRowPad)];
-  uint16_t v[64 * (D + kRowPad)];
-  uint16_t lsplit[3][D];
+  uint16_t k[64 * (D + kRowPad)];  // K rows: A operand of S^T = K Q^T
+  uint16_t v[64 * (D + kRowPad)];  // V rows: A operand of dP^T = V dO^T
+  uint16_t kq[16 * D * 4];         // K, key-quad layout: A operand of K^T dS^T
 };
 
-// Lane = query row (S^T = K Q^T as in the forward's chunk attention).
+// Lane = row (S^T = K Q^T as in the forward's chunk attention): register r
+// of lane (i, h) holds the row i's key 8(r/4) + 4h + r%4 (+32 in s1/p1).
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs ba, float sl2,
-                                                                float score_scale) {
+                                                                float sc) {
   const PrefillArgs& a = ba.p;
   __shared__ __attribute__((aligned(16))) ScoreSmem<D> sm;
   int64_t bg;
@@ -153,24 +220,16 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
   const int64_t kv0 = (bg * a.L + (int64_t)c * a.S) * D;
   load_rows<D>(sm.k, (const uint16_t*)a.K + kv0, a.S);
   load_rows<D>(sm.v, (const uint16_t*)a.V + kv0, a.S);
-  for (int x = threadIdx.x; x < D; x += kThreads) {
-    // the fp32 landmark as three bf16 parts hi + lo + lo2 (exact)
-    const float v = a.lmk[(bg * a.n + c) * D + x];
-    const __bf16 h = static_cast<__bf16>(v);
-    const float r1 = v - static_cast<float>(h);
-    const __bf16 l = static_cast<__bf16>(r1);
-    const __bf16 m = static_cast<__bf16>(r1 - static_cast<float>(l));
-    sm.lsplit[0][x] = __builtin_bit_cast(uint16_t, h);
-    sm.lsplit[1][x] = __builtin_bit_cast(uint16_t, l);
-    sm.lsplit[2][x] = __builtin_bit_cast(uint16_t, m);
-  }
+  load_quads<D>(sm.kq, (const uint16_t*)a.K + kv0, a.S);
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i32 = lane & 31, hf = lane >> 5;
   const int32_t* list = a.list + bg * a.L * a.topk + e_begin;
   const int64_t qplane = a.L * D;
   const int64_t qbase = ((int64_t)b * a.Hq + (int64_t)g * G) * qplane;
+  const int64_t row0 = partial_row(a, bg, e_begin, 0);
   const bool two = a.S > 32;
+  const f32x16 zero = {};
   for (int tile = w; tile < ntiles; tile += kThreads / kWave) {
     const int r = tile * 32 + i32;
     int ei, hh;
@@ -178,8 +237,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
     const int32_t entry = r < rows ? list[ei] : -1;
     u32x4 q[D / 16], o[D / 16];
     load_row_pair<D>(ba, qbase, qplane, entry, hh, hf, q, o);
-    const f32x16 zero = {};
-    f32x16 s0 = zero, s1 = zero, p0 = zero, p1 = zero, sl = zero;
+    const float wr = entry >= 0 ? ba.wk[row0 + r] : 0.f;
+    f32x16 s0 = zero, s1 = zero, p0 = zero, p1 = zero;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       const bf16x8 qb = __builtin_bit_cast(bf16x8, q[s]);
@@ -192,12 +251,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&sm.k[k1], qb, s1, 0, 0, 0);
         p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&sm.v[k1], ob, p1, 0, 0, 0);
       }
-      u32x4 la = {0u, 0u, 0u, 0u};
-      if (i32 < 3) la = *(const u32x4*)(&sm.lsplit[i32][16 * s + 8 * hf]);
-      sl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, la), qb, sl, 0, 0,
-                                                   0);
     }
-    const float sh = (sl[2] + sl[1]) + sl[0];
+    __builtin_amdgcn_sched_barrier(0);
     float mx = -INFINITY;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -211,19 +266,68 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
     float ps = 0.f, pd = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const float e0 = fast_exp2(__builtin_fmaf(s0[rr], sl2, -mxs));
-      const float e1 = fast_exp2(__builtin_fmaf(s1[rr], sl2, -mxs));
-      ps += e0 + e1;
-      pd += e0 * p0[rr] + e1 * p1[rr];
+      s0[rr] = fast_exp2(__builtin_fmaf(s0[rr], sl2, -mxs));
+      s1[rr] = fast_exp2(__builtin_fmaf(s1[rr], sl2, -mxs));
+      ps += s0[rr] + s1[rr];
+      pd += s0[rr] * p0[rr] + s1[rr] * p1[rr];
     }
     ps += __shfl_xor(ps, 32, kWave);
     pd += __shfl_xor(pd, 32, kWave);
-    if (entry >= 0 && hf == 0) {
-      const int64_t row = partial_row(a, bg, e_begin, 0) + r;
-      a.part_score[row] = sh * score_scale;
-      ba.lse2[row] = mxs + log2f(ps);
-      ba.dw[row] = pd / ps;
+    const float dw = pd / ps;
+    // dS^T = w P^T (dP^T - dw), P = exp2(...) / ps; the / sqrt(d) of dQ too
+    const float f = wr * sc / ps;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      s0[rr] = f * s0[rr] * (p0[rr] - dw);
+      s1[rr] = f * s1[rr] * (p1[rr] - dw);
     }
+    bf16x8 db4[4];
+    db4[0] = cvt_bf16x8(s0, 0);
+    db4[1] = cvt_bf16x8(s0, 8);
+    db4[2] = cvt_bf16x8(s1, 0);
+    db4[3] = cvt_bf16x8(s1, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    // dQ^T = K^T dS^T: B = dS^T straight from the score registers, A = K^T
+    // from the key quads in the same k-slot order
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if (kt == 1 && !two) break;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int g0 = 8 * kt + 4 * s2 + hf, g1 = g0 + 2;
+#pragma unroll
+        for (int bb = 0; bb < D / 32; ++bb) {
+          const int dd = 32 * bb + i32;
+          const u32x2 k0 = *(const u32x2*)&sm.kq[(g0 * D + dd) * 4];
+          const u32x2 k1 = *(const u32x2*)&sm.kq[(g1 * D + dd) * 4];
+          dq[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), db4[2 * kt + s2],
+              kt == 0 && s2 == 0 ? zero : dq[bb], 0, 0, 0);
+        }
+      }
+    }
+    if (entry < 0) continue;
+    if (hf == 0) {
+      ba.lse2[row0 + r] = mxs + log2f(ps);
+      ba.dw[row0 + r] = dw;
+    }
+    // lane half hf holds dims 32bb + 8q4 + 4hf + 0..3; swapping half of the
+    // groups with the partner lane leaves each lane 16 contiguous bytes
+    uint16_t* po = (uint16_t*)a.partial + (row0 + r) * D;
+#pragma unroll
+    for (int bb = 0; bb < D / 32; ++bb)
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const uint32_t e0 = pack_bf16x2(dq[bb][8 * pr], dq[bb][8 * pr + 1]);
+        const uint32_t e1 = pack_bf16x2(dq[bb][8 * pr + 2], dq[bb][8 * pr + 3]);
+        const uint32_t d0 = pack_bf16x2(dq[bb][8 * pr + 4], dq[bb][8 * pr + 5]);
+        const uint32_t d1 = pack_bf16x2(dq[bb][8 * pr + 6], dq[bb][8 * pr + 7]);
+        const uint32_t got0 = __shfl_xor(hf ? e0 : d0, 32, kWave);
+        const uint32_t got1 = __shfl_xor(hf ? e1 : d1, 32, kWave);
+        *(u32x4*)(po + 32 * bb + 8 * (2 * pr + hf)) =
+            hf ? u32x4{got0, got1, d0, d1} : u32x4{e0, e1, got0, got1};
+      }
   }
 }
 
@@ -242,75 +346,60 @@ __global__ void __launch_bounds__(kThreads) bwd_rows_kernel(PrefillBwdArgs ba) {
   const int m = (int)min((int64_t)a.topk, min(t / a.S, a.n));
   const int32_t* epos = a.entry_pos + (bg * a.L + t) * a.topk;
   int64_t pr[KM];
-  float s[KM], dw[KM];
-  float smax = -INFINITY;
+  float wk[KM], dw[KM];
+  float wdw = 0.f;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
     pr[k] = k < m ? partial_row(a, bg, epos[k], hh) : 0;
-    s[k] = k < m ? a.part_score[pr[k]] : -INFINITY;
+    wk[k] = k < m ? ba.wk[pr[k]] : 0.f;
     dw[k] = k < m ? ba.dw[pr[k]] : 0.f;
-    smax = fmaxf(smax, s[k]);
+    wdw += wk[k] * dw[k];
   }
-  float z = 0.f;
-#pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    s[k] = k < m ? expf(s[k] - smax) : 0.f;
-    z += s[k];
-  }
-  const float iz = m > 0 ? 1.f / z : 0.f;
-  float wdw = 0.f;
-#pragma unroll
-  for (int k = 0; k < KM; ++k) wdw += s[k] * iz * dw[k];
 #pragma unroll
   for (int k = 0; k < KM; ++k)
-    if (k < m) {
-      const float wk = s[k] * iz;
-      ba.wk[pr[k]] = wk;
-      ba.ds[pr[k]] = wk * (dw[k] - wdw);
-    }
+    if (k < m) ba.ds[pr[k]] = wk[k] * (dw[k] - wdw);
 }
 
-// ----------------------------------------------------------------- chunk --
+// -------------------------------------------------------------------- kv --
 
-constexpr int kTPitch = 36;  // [dim][row] tiles: 32 rows + 4 pad (18 dwords: rows of
-                             // dims 8 apart fall 16 banks apart)
 constexpr int kRedPitch = 1;  // pad of the [key][dim] fp32 sums (lanes = keys)
 
-// A wave pair's tile buffers: the tile's Q and dO transposed as [dim][row]
-// (the A operand of dV^T and dK^T reads 4 consecutive rows of one dim), dS
-// as [row][key] (the B operand of dQ^T) and the rows' statistics.
 template <int D>
-struct PairTiles {
-  uint16_t qt[D * kTPitch];
-  uint16_t ot[D * kTPitch];
-  uint16_t dsl[32 * kDsPitch];
-  float st[4][32];  // per row: lse2, dw, w, ds
-};
-
-template <int D>
-struct ChunkSmem {
-  uint16_t k[64 * (D + kRowPad)];
-  uint16_t v[64 * (D + kRowPad)];
-  uint16_t kq[16 * D * 4];
+struct KvSmem {
   union {
-    PairTiles<D> t[2][2];                // [pair][iteration parity]
-    float red[2][64 * (D + kRedPitch)];  // the chunk's dK, dV sums
+    struct {
+      uint16_t k[64 * (D + kRowPad)];
+      uint16_t v[64 * (D + kRowPad)];
+    } kv;
+    float red[64 * (D + kRedPitch)];  // the chunk's dK, then dV sums
   } u;
+  float st[kThreads / kWave][4][32];  // per wave, per row: lse2, dw, w, ds
 };
 
-// Waves form two pairs; pair p takes row tiles p, p + 2, ...  Within a
-// pair, the wave of key half kt computes S = Q K^T and dP = dO V^T for keys
-// 32 kt .. 32 kt + 31 (key on the lane: accumulator register r of lane
-// (j, h) holds row 8(r/4) + 4h + r%4 of the tile and key 32 kt + j), keeps
-// that half's dK^T and dV^T in registers, and produces dQ^T for dims
-// 64 kt .. 64 kt + 63 from the pair's whole dS tile.  The pair's tile
-// buffers alternate with the iteration parity, so a buffer is rewritten
-// only after the barrier that follows its last read.
+// The 0/1 operand that turns a row-major A operand into its transpose: the
+// product Q E (E selecting dims 32 bb .. 32 bb + 31 over the k-steps 2 bb and
+// 2 bb + 1) leaves Q[row][32 bb + j] in lane j, register r holding row
+// 8(r/4) + 4h + r%4 -- the k-slot order of the score registers -- so its
+// bf16 packing is the A operand of a product contracted over the tile's
+// rows.  Lane (j, h) holds k-slots 8h .. 8h+7 of k-step 2 bb + t: a one
+// where 16 t + 8 h + e == j.
+__device__ __forceinline__ bf16x8 selector(int t, int j, int h) {
+  bf16x8 e8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    e8[e] = static_cast<__bf16>(16 * t + 8 * h + e == j ? 1.f : 0.f);
+  return e8;
+}
+
+// Wave w owns keys 32 kt .. 32 kt + 31 (kt = w % 2) and the row tiles
+// w / 2, w / 2 + 2, ...; lane = key: register r of lane (j, h) holds row
+// 8(r/4) + 4h + r%4 of the tile and key 32 kt + j.  The waves never wait
+// for each other inside the loop.
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) bwd_chunk_kernel(PrefillBwdArgs ba, float sl2,
-                                                                float sc, float rs) {
+__global__ void __launch_bounds__(kThreads, 2) bwd_kv_kernel(PrefillBwdArgs ba, float sl2,
+                                                             float sc, float rs) {
   const PrefillArgs& a = ba.p;
-  __shared__ __attribute__((aligned(16))) ChunkSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) KvSmem<D> sm;
   int64_t bg;
   int c, e_begin, e_end;
   if (!locate_tile(a, bg, c, e_begin, e_end)) return;
@@ -319,19 +408,20 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_chunk_kernel(PrefillBwdArgs b
   const int rows = (e_end - e_begin) * G;
   const int ntiles = (rows + 31) / 32;
   const int64_t kv0 = (bg * a.L + (int64_t)c * a.S) * D;
-  load_rows<D>(sm.k, (const uint16_t*)a.K + kv0, a.S);
-  load_rows<D>(sm.v, (const uint16_t*)a.V + kv0, a.S);
-  load_quads<D>(sm.kq, (const uint16_t*)a.K + kv0, a.S);
+  load_rows<D>(sm.u.kv.k, (const uint16_t*)a.K + kv0, a.S);
+  load_rows<D>(sm.u.kv.v, (const uint16_t*)a.V + kv0, a.S);
+  __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i32 = lane & 31, hf = lane >> 5;
-  const int pair = w >> 1, kt = w & 1;
+  const int kt = w & 1, stream = w >> 1;
   const bool keys = 32 * kt < a.S;         // this wave's key half holds keys
-  const bool kval = 32 * kt + i32 < a.S;  // this lane's key exists
-  const int nks = a.S > 32 ? 4 : 2;       // 16-key steps of dQ
+  const bool kfull = 32 * kt + 32 <= a.S;  // ... and all 32 of them
+  const float kon = 32 * kt + i32 < a.S ? 1.f : 0.f;
   const int32_t* list = a.list + bg * a.L * a.topk + e_begin;
   const int64_t qplane = a.L * D;
   const int64_t qbase = ((int64_t)b * a.Hq + (int64_t)g * G) * qplane;
   const int64_t row0 = partial_row(a, bg, e_begin, 0);
+  const bf16x8 sel0 = selector(0, i32, hf), sel1 = selector(1, i32, hf);
   const f32x16 zero = {};
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -339,201 +429,108 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_chunk_kernel(PrefillBwdArgs b
     dk[bb] = zero;
     dv[bb] = zero;
   }
-  const int iters = (ntiles + 1) / 2;
-  // rows of iteration i: list entries run two iterations ahead, Q / dO rows
-  // and the row statistics one iteration ahead of their use
-  auto entry_of = [&](int i) -> int32_t {
-    const int r = (2 * i + pair) * 32 + i32;
-    if (i >= iters || r >= rows) return -1;
+  float(&st)[4][32] = sm.st[w];
+  for (int tile = stream; keys && tile < ntiles; tile += 2) {
+    const int r = tile * 32 + i32;
     int ei, hh;
     split_row(r, G, a.log2G, ei, hh);
-    return list[ei];
-  };
-  auto head_of = [&](int i) -> int {
-    int ei, hh;
-    split_row((2 * i + pair) * 32 + i32, G, a.log2G, ei, hh);
-    return hh;
-  };
-  const bool stat_lane = kt == 1 && hf == 0;
-  auto load_stats = [&](int i, int32_t e, f32x4& st4) {
-    const int64_t pr = row0 + (2 * i + pair) * 32 + i32;
-    st4 = f32x4{INFINITY, 0.f, 0.f, 0.f};
-    if (stat_lane && e >= 0) st4 = f32x4{ba.lse2[pr], ba.dw[pr], ba.wk[pr], ba.ds[pr]};
-  };
-  // one tile of the pair: rows of iteration it with their Q / dO rows and
-  // statistics already in registers
-  auto body = [&](int it, int32_t entry, const u32x4 (&q)[D / 16], const u32x4 (&o)[D / 16],
-                  const f32x4& st4) {
-    PairTiles<D>& pt = sm.u.t[pair][it & 1];
-    const int r = (2 * it + pair) * 32 + i32;
-    // the pair's tile buffers: Q rows from the kt = 0 wave, dO rows and the
-    // row statistics from the kt = 1 wave.  Lanes i32 and i32 ^ 1 hold
-    // adjacent rows: per pair of dims (2x, 2x+1) they swap one value so the
-    // even lane writes dim 2x of both rows and the odd lane dim 2x+1, one
-    // dword each.
-    uint16_t* tt = kt == 0 ? pt.qt : pt.ot;
-    const int odd = i32 & 1;
-    // v_perm_b32 picks bytes of {got, own}: the even lane keeps the low
-    // halves (own, then the partner's), the odd lane the high halves
-    const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const uint32_t wv = kt == 0 ? q[s][x] : o[s][x];  // dims 2x, 2x+1 of this row
-        const uint32_t word = __builtin_amdgcn_perm(swap_adjacent_lanes(wv), wv, psel);
-        const int dim = 16 * s + 8 * hf + 2 * x + odd;
-        *(uint32_t*)&tt[dim * kTPitch + (i32 & ~1)] = word;
-      }
-    if (stat_lane) {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) pt.st[f][i32] = st4[f];
+    const int32_t entry = r < rows ? list[ei] : -1;
+    u32x4 q[D / 16], o[D / 16];
+    load_row_pair<D>(ba, qbase, qplane, entry, hh, hf, q, o);
+    if (hf == 0) {
+      const bool ok = entry >= 0;
+      st[0][i32] = ok ? ba.lse2[row0 + r] : INFINITY;
+      st[1][i32] = ok ? ba.dw[row0 + r] : 0.f;
+      st[2][i32] = ok ? ba.wk[row0 + r] : 0.f;
+      st[3][i32] = ok ? ba.ds[row0 + r] : 0.f;
     }
-    // S = Q K^T and dP = dO V^T for this wave's 32 keys
     f32x16 sa = zero, pa = zero;
-    if (keys) {
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int ko = (32 * kt + i32) * (D + kRowPad) + 16 * s + 8 * hf;
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[s]),
-                                                     *(const bf16x8*)&sm.k[ko], sa, 0, 0, 0);
-        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o[s]),
-                                                     *(const bf16x8*)&sm.v[ko], pa, 0, 0, 0);
+    for (int s = 0; s < D / 16; ++s) {
+      const int ko = (32 * kt + i32) * (D + kRowPad) + 16 * s + 8 * hf;
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q[s]),
+                                                   *(const bf16x8*)&sm.u.kv.k[ko], sa, 0, 0, 0);
+      pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o[s]),
+                                                   *(const bf16x8*)&sm.u.kv.v[ko], pa, 0, 0, 0);
+    }
+    wave_sync_lds();
+    // P = exp2(S - lse), w P, dS' = w P (dP - dw) + ds / sqrt(S) (keys past S
+    // are 0), packed to bf16 at once
+    bf16x8 bp[2], bs[2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 l4 = *(const f32x4*)&st[0][8 * u + 4 * hf];
+      const f32x4 d4 = *(const f32x4*)&st[1][8 * u + 4 * hf];
+      const f32x4 w4 = *(const f32x4*)&st[2][8 * u + 4 * hf];
+      const f32x4 s4 = *(const f32x4*)&st[3][8 * u + 4 * hf];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = 4 * u + v;
+        float p = fast_exp2(__builtin_fmaf(sa[rr], sl2, -l4[v]));
+        if (!kfull) p *= kon;
+        const float wpv = w4[v] * p;
+        float dsk = __builtin_fmaf(s4[v], rs, wpv * (pa[rr] - d4[v]));
+        if (!kfull) dsk *= kon;
+        bp[u >> 1][4 * (u & 1) + v] = static_cast<__bf16>(wpv);
+        bs[u >> 1][4 * (u & 1) + v] = static_cast<__bf16>(dsk);
       }
     }
-    block_sync_lds();  // the pair's Q/dO tiles and statistics are in LDS
-    if (keys) {
-      // P = exp2(S - lse), w P, dS = w P (dP - dw), dS' = dS + ds / sqrt(S)
-      // (keys past S are 0; no masking when the wave's 32 keys all exist),
-      // packed to bf16 at once; dS / sqrt(d) to LDS for dQ
-      const bool kfull = 32 * kt + 32 <= a.S;
-      const float kon = kval ? 1.f : 0.f;
-      bf16x8 bp[2], bs[2];
+    // the row statistics of the next tile overwrite st only after every lane
+    // has read them
+    wave_sync_lds();
+    // per dims block: Q^T (then dO^T) from the selector products, and
+    // dK^T += Q^T dS' (then dV^T += dO^T (w P)) over the tile's rows; all of
+    // dK first, so Q's registers are free during dV's pass
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f32x4 l4 = *(const f32x4*)&pt.st[0][8 * u + 4 * hf];
-        const f32x4 d4 = *(const f32x4*)&pt.st[1][8 * u + 4 * hf];
-        const f32x4 w4 = *(const f32x4*)&pt.st[2][8 * u + 4 * hf];
-        const f32x4 s4 = *(const f32x4*)&pt.st[3][8 * u + 4 * hf];
+    for (int m = 0; m < 2; ++m) {
+      const u32x4(&x)[D / 16] = m == 0 ? q : o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int rr = 4 * u + v;
-          float p = fast_exp2(__builtin_fmaf(sa[rr], sl2, -l4[v]));
-          if (!kfull) p *= kon;
-          const float wpv = w4[v] * p;
-          const float dsv = wpv * (pa[rr] - d4[v]);
-          float dsk = __builtin_fmaf(s4[v], rs, dsv);
-          if (!kfull) dsk *= kon;
-          bp[u >> 1][4 * (u & 1) + v] = static_cast<__bf16>(wpv);
-          bs[u >> 1][4 * (u & 1) + v] = static_cast<__bf16>(dsk);
-          pt.dsl[(8 * u + 4 * hf + v) * kDsPitch + 32 * kt + i32] =
-              __builtin_bit_cast(uint16_t, static_cast<__bf16>(dsv * sc));
-        }
-      }
-      // dV^T += dO^T (w P), dK^T += Q^T dS' (the tile's rows are the
-      // contraction, in the k-slot order of the score registers)
+      for (int bb = 0; bb < D / 32; ++bb) {
+        f32x16 xt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, x[2 * bb]), sel0, zero, 0, 0, 0);
+        xt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[2 * bb + 1]),
+                                                     sel1, xt, 0, 0, 0);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        // k-slots 0..3 are rows 16 s2 + 4 hf + 0..3, k-slots 4..7 rows + 8
-        const int r0 = 16 * s2 + 4 * hf;
-#pragma unroll
-        for (int bb = 0; bb < D / 32; ++bb) {
-          const int dd = 32 * bb + i32;
-          const u32x2 o0 = *(const u32x2*)&pt.ot[dd * kTPitch + r0];
-          const u32x2 o1 = *(const u32x2*)&pt.ot[dd * kTPitch + r0 + 8];
-          const u32x2 q0 = *(const u32x2*)&pt.qt[dd * kTPitch + r0];
-          const u32x2 q1 = *(const u32x2*)&pt.qt[dd * kTPitch + r0 + 8];
-          dv[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o1[0], o1[1]}), bp[s2], dv[bb], 0, 0,
-              0);
-          dk[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), bs[s2], dk[bb], 0, 0,
-              0);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (m == 0)
+            dk[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt_bf16x8(xt, 8 * s2), bs[s2],
+                                                             dk[bb], 0, 0, 0);
+          else
+            dv[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt_bf16x8(xt, 8 * s2), bp[s2],
+                                                             dv[bb], 0, 0, 0);
         }
       }
     }
-    block_sync_lds();  // the pair's dS tile is complete
-    // dQ^T = K^T dS^T for dims 64 kt .. 64 kt + 63 over all keys
-    f32x16 dq[D / 64];
-#pragma unroll
-    for (int b2 = 0; b2 < D / 64; ++b2) {
-      const int bb = (D / 64) * kt + b2;
-      dq[b2] = zero;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s >= nks) break;
-        const bf16x8 bsv = *(const bf16x8*)&pt.dsl[i32 * kDsPitch + 16 * s + 8 * hf];
-        const int g0 = 4 * s + 2 * hf, g1 = g0 + 1;
-        const int dd = 32 * bb + i32;
-        const u32x2 k0 = *(const u32x2*)&sm.kq[(g0 * D + dd) * 4];
-        const u32x2 k1 = *(const u32x2*)&sm.kq[(g1 * D + dd) * 4];
-        dq[b2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), bsv, dq[b2], 0, 0, 0);
-      }
-    }
-    if (entry >= 0) {
-      uint16_t* po = (uint16_t*)a.partial + (row0 + r) * D;
-#pragma unroll
-      for (int b2 = 0; b2 < D / 64; ++b2)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int dd = 32 * ((D / 64) * kt + b2) + 8 * q4 + 4 * hf;
-          const u32x2 v = {pack_bf16x2(dq[b2][4 * q4], dq[b2][4 * q4 + 1]),
-                           pack_bf16x2(dq[b2][4 * q4 + 2], dq[b2][4 * q4 + 3])};
-          *(u32x2*)(po + dd) = v;
-        }
-    }
-  };
-  // two register sets: the next tile's rows load during the current tile,
-  // list entries run one tile further ahead
-  int32_t ea = entry_of(0), eb = entry_of(1);
-  u32x4 qa[D / 16], oa[D / 16], qb[D / 16], ob[D / 16];
-  f32x4 sta, stb;
-  load_row_pair<D>(ba, qbase, qplane, ea, head_of(0), hf, qa, oa);
-  load_stats(0, ea, sta);
-  for (int it = 0; it < iters; it += 2) {
-    const int32_t ec = entry_of(it + 2);
-    load_row_pair<D>(ba, qbase, qplane, eb, head_of(it + 1), hf, qb, ob);
-    load_stats(it + 1, eb, stb);
-    body(it, ea, qa, oa, sta);
-    if (it + 1 >= iters) break;
-    const int32_t ed = entry_of(it + 3);
-    load_row_pair<D>(ba, qbase, qplane, ec, head_of(it + 2), hf, qa, oa);
-    load_stats(it + 2, ec, sta);
-    body(it + 1, eb, qb, ob, stb);
-    ea = ec;
-    eb = ed;
   }
-  // the chunk's dK / dV: the two pairs' halves summed in LDS
+  // the chunk's dK, then dV: the two streams of each key half summed in LDS
+  // over the K/V area (no longer read), then written once as bf16
   constexpr int RP = D + kRedPitch;
-  __syncthreads();
-  for (int x = threadIdx.x; x < 2 * 64 * RP; x += kThreads) (&sm.u.red[0][0])[x] = 0.f;
-  __syncthreads();
-  if (kval) {
-    const int key = 32 * kt + i32;
+  const int key = 32 * kt + i32;
 #pragma unroll
-    for (int bb = 0; bb < D / 32; ++bb)
+  for (int m = 0; m < 2; ++m) {
+    __syncthreads();
+    for (int x = threadIdx.x; x < 64 * RP; x += kThreads) sm.u.red[x] = 0.f;
+    __syncthreads();
+    if (key < a.S) {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int dim = 32 * bb + 8 * (rr >> 2) + 4 * hf + (rr & 3);
-        atomicAdd(&sm.u.red[0][key * RP + dim], dk[bb][rr]);
-        atomicAdd(&sm.u.red[1][key * RP + dim], dv[bb][rr]);
-      }
-  }
-  __syncthreads();
-  // the block holds the chunk's whole list: its rows of dK and dV are final
-  for (int x = threadIdx.x; x < a.S * D / 8; x += kThreads) {
-    const int key = x / (D / 8), d0 = 8 * (x % (D / 8));
-    const float* kr = &sm.u.red[0][key * RP + d0];
-    const float* vr = &sm.u.red[1][key * RP + d0];
-    u32x4 ko, vo;
+      for (int bb = 0; bb < D / 32; ++bb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ko[j] = pack_bf16x2(kr[2 * j] * sc, kr[2 * j + 1] * sc);
-      vo[j] = pack_bf16x2(vr[2 * j], vr[2 * j + 1]);
+        for (int rr = 0; rr < 16; ++rr) {
+          const int dim = 32 * bb + 8 * (rr >> 2) + 4 * hf + (rr & 3);
+          atomicAdd(&sm.u.red[key * RP + dim], m == 0 ? dk[bb][rr] : dv[bb][rr]);
+        }
     }
-    *(u32x4*)((uint16_t*)ba.dK + kv0 + 8 * x) = ko;
-    *(u32x4*)((uint16_t*)ba.dV + kv0 + 8 * x) = vo;
+    __syncthreads();
+    const float scale = m == 0 ? sc : 1.f;
+    uint16_t* dst = (uint16_t*)(m == 0 ? ba.dK : ba.dV) + kv0;
+    for (int x = threadIdx.x; x < a.S * D / 8; x += kThreads) {
+      const int kr = x / (D / 8), d0 = 8 * (x % (D / 8));
+      const float* src = &sm.u.red[kr * RP + d0];
+      u32x4 out;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = pack_bf16x2(src[2 * j] * scale, src[2 * j + 1] * scale);
+      *(u32x4*)(dst + 8 * x) = out;
+    }
   }
 }
 
@@ -609,7 +606,33 @@ hipError_t finish_d(const PrefillBwdArgs& ba, hipStream_t stream) {
   return hipGetLastError();
 }
 
+
 }  // namespace
+
+hipError_t prefill_bwd_weights(const PrefillBwdArgs& ba, hipStream_t stream) {
+  const PrefillArgs& a = ba.p;
+  if (a.n == 0) return hipSuccess;
+  const int64_t groups = (int64_t)a.B * a.Hkv * a.L;  // (b, group, token)
+  const int rpb = kThreads / (a.d / 8);
+  const unsigned nb = (unsigned)((groups + rpb - 1) / rpb);
+  const float sc = 1.0f / sqrtf((float)a.d);
+  if (a.d == 64) {
+    if (a.topk <= 8)
+      bwd_weights_kernel<64, 8><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+    else if (a.topk <= 16)
+      bwd_weights_kernel<64, 16><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+    else
+      bwd_weights_kernel<64, 32><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+  } else {
+    if (a.topk <= 8)
+      bwd_weights_kernel<128, 8><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+    else if (a.topk <= 16)
+      bwd_weights_kernel<128, 16><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+    else
+      bwd_weights_kernel<128, 32><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+  }
+  return hipGetLastError();
+}
 
 hipError_t prefill_bwd_score(const PrefillBwdArgs& ba, hipStream_t stream) {
   const PrefillArgs& a = ba.p;
@@ -638,7 +661,7 @@ hipError_t prefill_bwd_rows(const PrefillBwdArgs& ba, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t prefill_bwd_chunk(const PrefillBwdArgs& ba, hipStream_t stream) {
+hipError_t prefill_bwd_kv(const PrefillBwdArgs& ba, hipStream_t stream) {
   const PrefillArgs& a = ba.p;
   // keys of chunks no row selected (and of a trailing partial chunk) get zero
   const int64_t words = (int64_t)a.B * a.Hkv * a.L * a.d / 2;  // bf16 pairs
@@ -651,10 +674,9 @@ hipError_t prefill_bwd_chunk(const PrefillBwdArgs& ba, hipStream_t stream) {
   const float sl2 = sc * 1.4426950408889634f;
   const float rs = 1.0f / sqrtf((float)a.S);
   if (a.d == 64)
-    bwd_chunk_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(ba, sl2, sc, rs);
+    bwd_kv_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(ba, sl2, sc, rs);
   else
-    bwd_chunk_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(ba, sl2, sc,
-                                                                                 rs);
+    bwd_kv_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(ba, sl2, sc, rs);
   return hipGetLastError();
 }
 

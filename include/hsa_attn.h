@@ -289,9 +289,9 @@ hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t p
  *   dhsa_prefill: 0 pool, 1 S_c, 2 rank, 3 attend, 4 mask
  *   dhsa_decode : 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
  *   swa_prefill, swa_decode: 0 attend
- *   hsa_prefill_backward: 0 landmarks, 1 select, 2 invert, 3 score (log-sum-
- *                 exp, dO . o_k), 4 rows (w, ds), 5 chunk (dK, dV, dQ pieces),
- *                 6 finish (dQ gather, dK / dV to bf16)
+ *   hsa_prefill_backward: 0 landmarks, 1 select, 2 invert, 3 weights (fusion
+ *                 weights), 4 score (log-sum-exp, dO . o_k, dQ pieces), 5 rows
+ *                 (retrieval-score gradients), 6 kv (dK, dV), 7 finish (dQ)
  * hsa_profile_read waits for the recorded events, adds the elapsed
  * milliseconds of stage s summed over all recorded calls into stage_ms[s]
  * (s < max_stages; the caller zeroes the array), releases the events and
