@@ -544,6 +544,8 @@ __global__ void __launch_bounds__(kThreads, 2)
     attend_chunk_bf16_kernel(PrefillArgs a, float scale_log2, float score_scale) {
   __shared__ KVSmem<D> sm;
   __shared__ __attribute__((aligned(16))) uint16_t lsplit[3][D];
+  // each wave's tile of partial rows, rows padded by 16 bytes (conflict-free)
+  __shared__ __attribute__((aligned(16))) uint16_t ostage[kThreads / kWave][32 * (D + 8)];
   int64_t bg;
   int c, e_begin, e_end;
   if (!locate_tile(a, bg, c, e_begin, e_end)) return;
@@ -708,17 +710,34 @@ __global__ void __launch_bounds__(kThreads, 2)
         const uint32_t got1 = __shfl_xor(hf ? e1 : d1, 32, kWave);
         outv[bb][pr] = hf ? u32x4{got0, got1, d0, d1} : u32x4{e0, e1, got0, got1};
       }
-    if (ent_cur >= 0) {
-      // rows of a tile are consecutive: (entry e_begin + r / G, head r % G).
-      // The partials are read once, by the fusion: streaming stores.
-      const int64_t row = partial_row(a, bg, e_begin, 0) + tile * 32 + i32;
-      if (hf == 0) a.part_score[row] = sh * score_scale;
-      uint16_t* po = (uint16_t*)a.partial + row * D;
+    // rows of a tile are consecutive: (entry e_begin + r / G, head r % G),
+    // so the tile's partials are one contiguous run of up to 32 rows.  They
+    // go through LDS and leave as 1 KB stores; rows past the unit's end
+    // belong to the next unit and are not written.
+    const int64_t row0 = partial_row(a, bg, e_begin, 0) + tile * 32;
+    if (ent_cur >= 0 && hf == 0) a.part_score[row0 + i32] = sh * score_scale;
+    uint16_t* stg = ostage[w];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int bb = 0; bb < D / 32; ++bb)
+    for (int bb = 0; bb < D / 32; ++bb)
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr)
-          __builtin_nontemporal_store(outv[bb][pr], (u32x4*)(po + 32 * bb + 8 * (2 * pr + hf)));
+      for (int pr = 0; pr < 2; ++pr)
+        *(u32x4*)(stg + i32 * (D + 8) + 32 * bb + 8 * (2 * pr + hf)) = outv[bb][pr];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int nrow = min(32, rows - tile * 32);
+    constexpr int LPR = D / 8;        // lanes per row (16 bytes each)
+    constexpr int RPI = kWave / LPR;  // rows per store instruction
+    uint16_t* base = (uint16_t*)a.partial + row0 * D;
+    const int piece = lane % LPR;
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int row = k * RPI + lane / LPR;
+      const u32x4 v = *(const u32x4*)(stg + row * (D + 8) + 8 * piece);
+      if (row < nrow) __builtin_nontemporal_store(v, (u32x4*)(base + (int64_t)row * D + 8 * piece));
     }
   };
 
