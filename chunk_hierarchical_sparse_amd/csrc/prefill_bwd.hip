@@ -201,6 +201,7 @@ struct ScoreSmem {
   uint16_t k[64 * (D + kRowPad)];  // K rows: A operand of S^T = K Q^T
   uint16_t v[64 * (D + kRowPad)];  // V rows: A operand of dP^T = V dO^T
   uint16_t kq[16 * D * 4];         // K, key-quad layout: A operand of K^T dS^T
+  uint16_t ostage[kThreads / kWave][16 * (D + 8)];  // each wave's dQ rows, padded
 };
 
 // Lane = row (S^T = K Q^T as in the forward's chunk attention): register r
@@ -307,14 +308,15 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
         }
       }
     }
-    if (entry < 0) continue;
-    if (hf == 0) {
+    if (entry >= 0 && hf == 0) {
       ba.lse2[row0 + r] = mxs + log2f(ps);
       ba.dw[row0 + r] = dw;
     }
     // lane half hf holds dims 32bb + 8q4 + 4hf + 0..3; swapping half of the
-    // groups with the partner lane leaves each lane 16 contiguous bytes
-    uint16_t* po = (uint16_t*)a.partial + (row0 + r) * D;
+    // groups with the partner lane leaves each lane 16 contiguous bytes.
+    // The tile's rows are one contiguous run: they go through LDS and leave
+    // as 1 KB stores; rows past the unit's end are not written.
+    u32x4 outv[D / 32][2];
 #pragma unroll
     for (int bb = 0; bb < D / 32; ++bb)
 #pragma unroll
@@ -325,9 +327,32 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
         const uint32_t d1 = pack_bf16x2(dq[bb][8 * pr + 6], dq[bb][8 * pr + 7]);
         const uint32_t got0 = __shfl_xor(hf ? e0 : d0, 32, kWave);
         const uint32_t got1 = __shfl_xor(hf ? e1 : d1, 32, kWave);
-        *(u32x4*)(po + 32 * bb + 8 * (2 * pr + hf)) =
-            hf ? u32x4{got0, got1, d0, d1} : u32x4{e0, e1, got0, got1};
+        outv[bb][pr] = hf ? u32x4{got0, got1, d0, d1} : u32x4{e0, e1, got0, got1};
       }
+    uint16_t* stg = sm.ostage[w];
+    const int nrow = min(32, rows - tile * 32);
+    constexpr int LPR = D / 8;        // lanes per row (16 bytes each)
+    constexpr int RPI = kWave / LPR;  // rows per store instruction
+    const int piece = lane % LPR;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      wave_sync_lds();
+      if (i32 / 16 == h2) {
+#pragma unroll
+        for (int bb = 0; bb < D / 32; ++bb)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr)
+            *(u32x4*)(stg + (i32 % 16) * (D + 8) + 32 * bb + 8 * (2 * pr + hf)) = outv[bb][pr];
+      }
+      wave_sync_lds();
+      uint16_t* base = (uint16_t*)a.partial + (row0 + tile * 32 + h2 * 16) * D;
+#pragma unroll
+      for (int k = 0; k < 16 / RPI; ++k) {
+        const int row = k * RPI + lane / LPR;
+        const u32x4 v = *(const u32x4*)(stg + row * (D + 8) + 8 * piece);
+        if (h2 * 16 + row < nrow) __builtin_nontemporal_store(v, (u32x4*)(base + (int64_t)row * D + 8 * piece));
+      }
+    }
   }
 }
 
