@@ -107,22 +107,28 @@ def to_dev(arr, torch):
 
 
 def time_steps(torch, hsa, step, steps, warmup, n_stages):
-    """Run warmup + timed steps; returns (ms per step, per-stage ms averages)."""
+    """Run warmup steps, then `steps` timed steps with nothing else on the
+    stream (ms per step), then `steps` more with the library's per-stage HIP
+    events on (per-stage ms averages).  The events sit between the kernels of
+    every call and cost a few microseconds each, so they stay out of the
+    throughput figure."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    hsa.hsa_profile_read()  # drop anything recorded earlier
-    hsa.hsa_profile_enable(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
     for _ in range(steps):
         step()
     end.record()
     torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    hsa.hsa_profile_read()  # drop anything recorded earlier
+    hsa.hsa_profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     hsa.hsa_profile_enable(False)
     calls, stage_ms = hsa.hsa_profile_read(n_stages)
-    ms = start.elapsed_time(end) / steps
     return ms, [s / max(calls, 1) for s in stage_ms]
 
 

@@ -3,16 +3,20 @@
 // [HiLS] abstract: per-chunk attention fused by the retrieval scores).
 //
 //  1. scan   : grid (b, group, slice).  Streams the slice's fp32 landmarks
-//              once (the bandwidth-bound step), scores them against the
+//              once (the bandwidth-bound step; the next batch of rows loads
+//              while the current one is scored), scores them against the
 //              group-summed query and keeps the slice's top-K as 64-bit keys
-//              (score, then lower index) via an LDS radix select.
-//  2. attend : one block per (b, group, rank k).  Every block of a (b, group)
-//              merges the slices' candidates into the same ordered top-K
-//              (score desc, index asc), stages the chunk of rank k in LDS,
-//              lets every head of the group attend to it and scores it
-//              against its own query (s_h).
+//              (score, then lower index): per-wave bitonic sorts merged into
+//              one sorted list.
+//  2. attend : chunks of at most 64 keys: R = ceil(K/8) blocks of 8 waves per
+//              (b, group), one wave per selected chunk (keys and values in
+//              registers); every block merges the slices' candidates into
+//              the same ordered top-K; with K <= 8 the block also fuses.
+//              Longer chunks: one block per (b, group, rank k) staging the
+//              chunk in LDS, every head of the group attending to it.
 //  3. fuse   : one block per (b, group): per head, a softmax over the
-//              selected chunks' s_h weights the chunk outputs.
+//              selected chunks' s_h weights the chunk outputs (when the
+//              attention blocks did not fuse).
 #include <math.h>
 
 #include <type_traits>
@@ -30,15 +34,16 @@ constexpr int kMaxSlice = 4096;
 // The K largest of the distinct keys >= lo among keys[0..M) (LDS or
 // global), written unordered to out[0..min(K, count)); returns that count.
 // Radix select, 8 bits at a time from the top, until the bin holding the
-// K-th largest key is needed whole.  Called by all 256 threads; `hist` is
-// 256 ints of LDS, `sv` 4 ints.
+// K-th largest key is needed whole.  Called by all NT (>= 256) threads of
+// the block; `hist` is 256 ints of LDS, `sv` 4 ints.
+template <int NT>
 __device__ int block_topk_ge(const uint64_t* keys, int M, uint64_t lo, int K, uint64_t* out,
                              int* hist, int* sv) {
   const int tid = threadIdx.x;
   if (tid == 0) sv[3] = 0;
   __syncthreads();
   int mine = 0;
-  for (int i = tid; i < M; i += kThreads) mine += keys[i] >= lo;
+  for (int i = tid; i < M; i += NT) mine += keys[i] >= lo;
   if (mine) atomicAdd(&sv[3], mine);
   __syncthreads();
   const int n = sv[3];
@@ -46,7 +51,7 @@ __device__ int block_topk_ge(const uint64_t* keys, int M, uint64_t lo, int K, ui
   if (n <= K) {
     if (tid == 0) sv[3] = 0;
     __syncthreads();
-    for (int i = tid; i < M; i += kThreads) {
+    for (int i = tid; i < M; i += NT) {
       const uint64_t k = keys[i];
       if (k >= lo) out[atomicAdd(&sv[3], 1)] = k;
     }
@@ -56,9 +61,9 @@ __device__ int block_topk_ge(const uint64_t* keys, int M, uint64_t lo, int K, ui
   uint64_t prefix = 0, mask = 0;
   int need = K;
   for (int shift = 56; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < M; i += kThreads) {
+    for (int i = tid; i < M; i += NT) {
       const uint64_t k = keys[i];
       if (k >= lo && (k & mask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 255u)], 1);
     }
@@ -101,12 +106,60 @@ __device__ int block_topk_ge(const uint64_t* keys, int M, uint64_t lo, int K, ui
   }
   if (tid == 0) sv[3] = 0;
   __syncthreads();
-  for (int i = tid; i < M; i += kThreads) {
+  for (int i = tid; i < M; i += NT) {
     const uint64_t k = keys[i];
     if (k >= lo && (k & mask) >= prefix) out[atomicAdd(&sv[3], 1)] = k;
   }
   __syncthreads();
   return K;
+}
+
+// The value of lane (this lane ^ j), j a power of two below 64 known at
+// compile time after unrolling.  j <= 8 stays in the lane's 16-lane row and
+// goes through DPP moves: the quad permutations give j = 1, 2, and j = 4, 8
+// compose two mirrors (lane ^ 3 then ^ 7, lane ^ 7 then ^ 15).  j = 16, 32
+// cross rows and use the LDS permute.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int j) {
+  const int x = (int)v;
+  if (j == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
+  if (j == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
+  if (j == 4)
+    return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false),
+                                              0x141, 0xF, 0xF, false);
+  if (j == 8)
+    return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false),
+                                              0x140, 0xF, 0xF, false);
+  return (uint32_t)__shfl_xor(x, j, kWave);
+}
+
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int j) {
+  return (uint64_t)lane_xor((uint32_t)v, j) | ((uint64_t)lane_xor((uint32_t)(v >> 32), j) << 32);
+}
+
+__device__ __forceinline__ float lane_xor_f32(float v, int j) {
+  return __builtin_bit_cast(float, lane_xor(__builtin_bit_cast(uint32_t, v), j));
+}
+
+// Wave-wide maximum and sum: butterflies inside each 16-lane row, then the
+// four row results read out of lanes 0, 16, 32, 48.
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int j = 1; j < 16; j <<= 1) v = fmaxf(v, lane_xor_f32(v, j));
+  const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int j = 1; j < 16; j <<= 1) v += lane_xor_f32(v, j);
+  const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (a0 + a1) + (a2 + a3);
 }
 
 // Bitonic sort of one 64-bit key per lane across the wave, descending
@@ -117,7 +170,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t x) {
   for (int k = 2; k <= kWave; k <<= 1)
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t y = __shfl_xor(x, j, kWave);
+      const uint64_t y = lane_xor_u64(x, j);
       // in a block of k lanes that ends ascending (lane & k set) the lower
       // lane of each pair keeps the smaller key, otherwise the larger
       const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
@@ -136,36 +189,104 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// The value of the partner lane whose index differs in bit log2(M) within
+// a group of 2M lanes (M = 16: across the two 16-lane rows of a 32-lane
+// group; M = 8, 4: the mirrored lane of the 16- or 8-lane half row, which
+// differs in that bit and in all lower ones; M = 2, 1: the quad partner).
+template <int M>
+__device__ __forceinline__ float partner(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int y;
+  if constexpr (M == 16) y = __shfl_xor(x, 16, kWave);
+  else if constexpr (M == 8) y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);
+  else if constexpr (M == 4) y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+  else if constexpr (M == 2) y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
+  else y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
+  return __builtin_bit_cast(float, y);
+}
+
+// p[0..8) are a lane's partial dot products for 8 rows, each row spread over
+// the LPR lanes of its lane group.  Three halving exchanges leave each lane
+// one row's partial (row index from bits LPR/2, LPR/4, LPR/8 of the lane),
+// the remaining steps finish the sum over the group: 8 rows cost
+// 4 + 2 + 1 + log2(LPR/8) exchanges instead of 8 log2(LPR).
+template <int LPR>
+__device__ __forceinline__ float reduce8_rows(const float (&p)[8], int li, int& row) {
+  constexpr int M1 = LPR / 2, M2 = LPR / 4, M3 = LPR / 8;
+  const bool h1 = li & M1, h2 = li & M2, h3 = li & M3;
+  float q[4], r[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = (h1 ? p[j + 4] : p[j]) + partner<M1>(h1 ? p[j] : p[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) r[j] = (h2 ? q[j + 2] : q[j]) + partner<M2>(h2 ? q[j] : q[j + 2]);
+  float s = (h3 ? r[1] : r[0]) + partner<M3>(h3 ? r[0] : r[1]);
+  if constexpr (M3 >= 4) s += partner<2>(s);
+  if constexpr (M3 >= 2) s += partner<1>(s);
+  row = (h3 ? 1 : 0) + (h2 ? 2 : 0) + (h1 ? 4 : 0);
+  return s;
+}
+
+// Descending bitonic merge of a bitonic sequence of 64 keys, one per lane.
+__device__ __forceinline__ uint64_t wave_merge_desc_u64(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = kWave / 2; j > 0; j >>= 1) {
+    const uint64_t y = lane_xor_u64(x, j);
+    x = ((lane & j) == 0) == (x > y) ? x : y;
+  }
+  return x;
+}
+
+// The K (<= 32) largest of keys[0..M) in LDS, descending in lanes 0..K-1 of
+// wave 0 (zeros past the M-th).  Each wave sorts its 64-key pieces and
+// merges them into a running top list; wave 0 then merges the four lists.
+// `lists` is 4 * 32 keys of LDS.  Called by all threads.
+__device__ uint64_t block_topk_sorted(const uint64_t* keys, int M, int K, uint64_t* lists) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint64_t run = 0ull;
+  for (int c = w; c * kWave < M; c += kThreads / kWave) {
+    const int i = c * kWave + lane;
+    uint64_t x = wave_sort_desc_u64(i < M ? keys[i] : 0ull);
+    // lanes 0..31: the piece's 32 largest, descending; lanes 32..63: the
+    // running list reversed (ascending): a bitonic sequence
+    const uint64_t rr = __shfl(run, kWave - 1 - lane, kWave);
+    x = wave_merge_desc_u64(lane < 32 ? x : rr);
+    run = lane < K ? x : 0ull;
+  }
+  if (lane < 32) lists[w * 32 + lane] = run;
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll 1
+    for (int v = 1; v < kThreads / kWave; ++v) {
+      const uint64_t x = lane < 32 ? lists[v * 32 + lane] : 0ull;
+      const uint64_t rr = __shfl(run, kWave - 1 - lane, kWave);
+      run = wave_merge_desc_u64(lane < 32 ? x : rr);
+      run = lane < K ? run : 0ull;
+    }
+  }
+  return run;
+}
+
 template <int D, int DT>
 __global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
   __shared__ float u[D];
   extern __shared__ uint64_t keys[];  // [slice]
-  __shared__ uint64_t sel[32];
-  __shared__ int hist[256];
-  __shared__ int sv[4];
+  __shared__ uint64_t lists[4 * 32];
   const int64_t bg = blockIdx.x / a.n_slices;
   const int sl = blockIdx.x % a.n_slices;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int G = a.Hq / a.Hkv;
   const int64_t c_begin = (int64_t)sl * a.slice;
   const int M = (int)max((int64_t)0, min((int64_t)a.slice, a.n_avail - c_begin));
-  for (int x = threadIdx.x; x < D; x += kThreads) {
-    float acc = 0.f;
-    for (int hh = 0; hh < G; ++hh)
-      acc += load_elem<DT>(a.q, ((int64_t)b * a.Hq + g * G + hh) * D + x);
-    u[x] = acc;
-  }
-  __syncthreads();
-  constexpr int LPR = D / 4;        // lanes per landmark row
+  constexpr int LPR = D / 4;        // lanes per landmark row (16 bytes each)
   constexpr int RPW = kWave / LPR;  // rows per wave step
-  constexpr int U = 8;              // row steps in flight per wave
+  constexpr int U = 8;              // row steps per batch (the reduction takes 8)
+  constexpr int STEP = kThreads / kWave * RPW;  // rows per block step
+  constexpr int CH = STEP * U;                  // rows per batch
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane % LPR, sub = lane / LPR;
-  const f32x4 u4 = *(const f32x4*)(&u[4 * li]);
   const float* lm = a.lmk + (bg * a.lmk_chunks + c_begin) * D + 4 * li;
-  constexpr int STEP = 4 * RPW;  // rows per block step
-  for (int r0 = 0; r0 < M; r0 += STEP * U) {
-    f32x4 x[U];
+  auto load = [&](int r0, f32x4 (&x)[U]) {
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
       const int row = r0 + uu * STEP + w * RPW + sub;
@@ -174,26 +295,54 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
       else
         x[uu] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+  // the first batch is in flight while the group's query sum forms
+  f32x4 xa[U], xb[U];
+  load(0, xa);
+  if (threadIdx.x < D) {
+    const int x = threadIdx.x;
+    const int64_t q0 = ((int64_t)b * a.Hq + g * G) * D + x;
+    float acc = 0.f;
+    for (int h0 = 0; h0 < G; h0 += 8) {
+      float v[8];
 #pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      const int row = r0 + uu * STEP + w * RPW + sub;
-      float p = u4[0] * x[uu][0] + u4[1] * x[uu][1] + u4[2] * x[uu][2] + u4[3] * x[uu][3];
+      for (int j = 0; j < 8; ++j) v[j] = h0 + j < G ? load_elem<DT>(a.q, q0 + (h0 + j) * D) : 0.f;
 #pragma unroll
-      for (int o = LPR / 2; o > 0; o >>= 1) p += __shfl_xor(p, o, kWave);
-      if (li == 0 && row < M) keys[row] = select_key(p, (uint32_t)(c_begin + row));
+      for (int j = 0; j < 8; ++j)
+        if (h0 + j < G) acc += v[j];
     }
+    u[x] = acc;
+  }
+  block_sync_lds();
+  const f32x4 u4 = *(const f32x4*)(&u[4 * li]);
+  auto score = [&](int r0, const f32x4 (&x)[U]) {
+    float p[U];
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu)
+      p[uu] = u4[0] * x[uu][0] + u4[1] * x[uu][1] + u4[2] * x[uu][2] + u4[3] * x[uu][3];
+    int uu;
+    const float s = reduce8_rows<LPR>(p, li, uu);
+    const int row = r0 + uu * STEP + w * RPW + sub;
+    if (li % (LPR / 8) == 0 && row < M) keys[row] = select_key(s, (uint32_t)(c_begin + row));
+  };
+  // double-buffered: the next batch loads while the current one is scored
+  for (int r0 = 0; r0 < M; r0 += 2 * CH) {
+    if (r0 + CH < M) load(r0 + CH, xb);
+    score(r0, xa);
+    if (r0 + CH >= M) break;
+    if (r0 + 2 * CH < M) load(r0 + 2 * CH, xa);
+    score(r0 + CH, xb);
   }
   __syncthreads();
-  const int got = block_topk_ge(keys, M, 0ull, a.topk, sel, hist, sv);
-  uint64_t* out = a.cand + (bg * a.n_slices + sl) * a.topk;
-  for (int k = threadIdx.x; k < a.topk; k += kThreads) out[k] = k < got ? sel[k] : 0ull;
-  if (threadIdx.x == 0) {
-    uint64_t mx = 0ull, mn = ~0ull;
-    for (int k = 0; k < got; ++k) {
-      mx = sel[k] > mx ? sel[k] : mx;
-      mn = sel[k] < mn ? sel[k] : mn;
-    }
-    *(u64x2*)(a.cand_mm + (bg * a.n_slices + sl) * 2) = u64x2{mx, got == a.topk ? mn : 0ull};
+  const uint64_t top = block_topk_sorted(keys, M, a.topk, lists);
+  if (w == 0) {
+    const int got = min(M, a.topk);
+    uint64_t* out = a.cand + (bg * a.n_slices + sl) * a.topk;
+    if (lane < a.topk) out[lane] = lane < got ? top : 0ull;
+    const uint64_t mn = __shfl(top, max(got - 1, 0), kWave);
+    if (lane == 0)
+      *(u64x2*)(a.cand_mm + (bg * a.n_slices + sl) * 2) =
+          u64x2{got > 0 ? top : 0ull, got == a.topk ? mn : 0ull};
   }
 }
 
@@ -206,7 +355,8 @@ constexpr int kMergeLds = 1024;  // candidates above the bound kept in LDS
 // are first cut at a lower bound of the K-th largest key (the largest
 // smallest-kept key of a full slice) and the survivors sorted the same way,
 // or, past 64 survivors, radix-selected.  Deterministic: every block of the
-// (b, group) gets the same list.  Called by all 256 threads.
+// (b, group) gets the same list.  Called by all NT threads of the block.
+template <int NT>
 __device__ int merge_candidates(const DecodeArgs& a, int64_t bg, uint64_t* ck, uint64_t* top,
                                 int32_t* order, int* hist, int* sv, uint64_t* red) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -222,7 +372,7 @@ __device__ int merge_candidates(const DecodeArgs& a, int64_t bg, uint64_t* ck, u
     // keys reach it).  Lane l of a wave takes slice 64 * grp + l.
     const uint64_t* mm = a.cand_mm + bg * (int64_t)a.n_slices * 2;
     uint64_t m = 0;
-    for (int grp = w; grp * kWave < a.n_slices; grp += kThreads / kWave) {
+    for (int grp = w; grp * kWave < a.n_slices; grp += NT / kWave) {
       const int j = grp * kWave + lane;
       u64x2 v = {0ull, 0ull};
       if (j < a.n_slices) v = *(const u64x2*)(mm + 2 * j);
@@ -234,10 +384,10 @@ __device__ int merge_candidates(const DecodeArgs& a, int64_t bg, uint64_t* ck, u
     if (lane == 0) red[w] = m;
     if (tid == 0) sv[3] = 0;
     __syncthreads();
-    for (int x = 0; x < kThreads / kWave; ++x) lb = red[x] > lb ? red[x] : lb;
+    for (int x = 0; x < NT / kWave; ++x) lb = red[x] > lb ? red[x] : lb;
     // only slices whose largest key reaches the bound hold survivors; their
     // loads have fixed trip counts (K <= 32 is uniform) so all are in flight
-    for (int grp = w; grp * kWave < a.n_slices; grp += kThreads / kWave) {
+    for (int grp = w; grp * kWave < a.n_slices; grp += NT / kWave) {
       const int j = grp * kWave + lane;
       if (j >= a.n_slices || mm[2 * j] < lb) continue;
       const uint64_t* cs = cand + (int64_t)j * K;
@@ -270,7 +420,7 @@ __device__ int merge_candidates(const DecodeArgs& a, int64_t bg, uint64_t* ck, u
     __syncthreads();
     return got;
   }
-  const int got = block_topk_ge(src, n <= kMergeLds ? n : total, lb, K, top, hist, sv);
+  const int got = block_topk_ge<NT>(src, n <= kMergeLds ? n : total, lb, K, top, hist, sv);
   if (tid < K) {
     int32_t idx = -1;
     if (tid < got) {
@@ -323,7 +473,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float sc
       for (int e = tid; e < a.topk; e += kThreads) a.sel[bg * a.topk + e] = -1;
     return;
   }
-  const int got = merge_candidates(a, bg, ck, top, order, hist, sv, red);
+  const int got = merge_candidates<kThreads>(a, bg, ck, top, order, hist, sv, red);
   if (k == 0)
     for (int e = tid; e < a.topk; e += kThreads) a.sel[bg * a.topk + e] = order[e];
   const int c = k < got ? order[k] : -1;
@@ -474,6 +624,283 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
   }
 }
 
+// Chunks of at most 64 keys: R = ceil(K / 8) blocks of 8 waves per (b,
+// group), wave w of block rb taking rank 8 rb + w.  Each block runs the
+// merge itself; lane = key for the logits (the key row in registers, packed
+// bf16 dot products) and lane = output columns for the weighted value sum
+// (the values in registers, the weights broadcast from LDS).  With R = 1 the
+// chunk outputs of a round of `fused_heads` heads stay in LDS and the block
+// fuses them (the softmax over the ranks' s_h) itself; with R > 1 they go to
+// the partial buffers for fuse_kernel.
+constexpr int kFusedWaves = 8;
+constexpr int kFusedThreads = kFusedWaves * kWave;
+constexpr int kFusedPartBytes = 32768;  // LDS for one round's chunk outputs
+constexpr int kFusedMaxLds = 61440;  // dynamic LDS bytes (static arrays take ~1.5 KB)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__host__ __device__ inline int fused_heads(int G, int K, int D) {
+  int hg = kFusedPartBytes / (K * D * 4);
+  hg = hg < 1 ? 1 : hg;
+  hg = hg > 8 ? 8 : hg;
+  return hg < G ? hg : G;
+}
+
+__host__ __device__ inline int round4(int x) { return (x + 3) & ~3; }
+
+
+// LDS floats before the merge's candidate buffer
+__host__ __device__ inline int fused_lds_floats(int G, int K, int D, int dt) {
+  const int hg = fused_heads(G, K, D);
+  return G * D + (dt == kBF16 ? G * D / 2 : 0) + hg * K * D + 2 * round4(hg * K) +
+         kFusedWaves * hg * kWave;
+}
+
+// dynamic LDS bytes of the fused kernel, 0 if it does not apply
+size_t fused_lds_bytes(const DecodeArgs& a) {
+  const int G = a.Hq / a.Hkv;
+  if (a.S > kWave) return 0;
+  size_t bytes = (size_t)fused_lds_floats(G, a.topk, a.d, a.dtype) * sizeof(float);
+  if ((int64_t)a.n_slices * a.topk > kWave) bytes += (size_t)kMergeLds * sizeof(uint64_t);
+  return bytes <= (size_t)kFusedMaxLds ? bytes : 0;
+}
+
+template <int D, int DT>
+__global__ void __launch_bounds__(kFusedThreads) attend_fused_kernel(DecodeArgs a, float scale) {
+  constexpr int NW = kFusedWaves, NT = kFusedThreads;
+  constexpr int CPL = D / 64;                  // output columns per lane
+  constexpr int KV4 = D * (DT == kF32 ? 4 : 2) / 16;  // 16-byte pieces per key row
+  __shared__ uint64_t top[32];
+  __shared__ uint64_t red[NW];
+  __shared__ int32_t order[32];
+  __shared__ int hist[256];
+  __shared__ int sv[4];
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  const int G = a.Hq / a.Hkv;
+  const int K = a.topk;
+  const int HG = fused_heads(G, K, D);
+  float* qf = dyn;                                             // [G][D] fp32
+  uint32_t* qb = (uint32_t*)(qf + G * D);                      // [G][D/2] bf16 pairs
+  float* part = (float*)(qb + (DT == kBF16 ? G * D / 2 : 0));  // [HG][K][D]
+  float* psc = part + HG * K * D;                              // [HG][K] s_h
+  float* wts = psc + round4(HG * K);                           // [HG][K] fusion weights
+  float* pbuf = wts + round4(HG * K);                          // [NW][HG][64] key weights
+  uint64_t* ck = (uint64_t*)(pbuf + NW * HG * kWave);
+  const int R = (K + NW - 1) / NW;  // blocks per (b, group)
+  const int64_t bg = blockIdx.x / R;
+  const int rb = blockIdx.x % R;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t qrow0 = (int64_t)b * a.Hq + g * G;  // first head row of the group
+
+  // the group's queries load during the merge
+  constexpr int QP = 2;  // query element pairs per thread in flight
+  const int npairs = G * D / 2;
+  uint32_t qraw[QP];
+  f32x2 qpair[QP];
+#pragma unroll
+  for (int i = 0; i < QP; ++i) {
+    const int e2 = tid + i * NT;
+    if (e2 < npairs) {
+      if (DT == kF32) qpair[i] = ((const f32x2*)a.q)[qrow0 * D / 2 + e2];
+      else qraw[i] = ((const uint32_t*)a.q)[qrow0 * D / 2 + e2];
+    }
+  }
+  int got = 0;
+  if (a.n_avail > 0) got = merge_candidates<NT>(a, bg, ck, top, order, hist, sv, red);
+  for (int i = 0; i < QP; ++i) {
+    const int e2 = tid + i * NT;
+    if (e2 < npairs) {
+      if (DT == kF32) {
+        *(f32x2*)(qf + 2 * e2) = qpair[i];
+      } else {
+        qb[e2] = qraw[i];
+        *(f32x2*)(qf + 2 * e2) =
+            f32x2{bf16_bits_to_f32(qraw[i] & 0xffffu), bf16_bits_to_f32(qraw[i] >> 16)};
+      }
+    }
+  }
+  for (int e2 = tid + QP * NT; e2 < npairs; e2 += NT) {
+    if (DT == kF32) {
+      *(f32x2*)(qf + 2 * e2) = ((const f32x2*)a.q)[qrow0 * D / 2 + e2];
+    } else {
+      const uint32_t r = ((const uint32_t*)a.q)[qrow0 * D / 2 + e2];
+      qb[e2] = r;
+      *(f32x2*)(qf + 2 * e2) = f32x2{bf16_bits_to_f32(r & 0xffffu), bf16_bits_to_f32(r >> 16)};
+    }
+  }
+  if (rb == 0 && tid < K) a.sel[bg * K + tid] = tid < got ? order[tid] : -1;
+  __syncthreads();
+
+  const bool key_ok = lane < a.S;
+  const int r = rb * NW + w;  // this wave's rank
+  float* pw = pbuf + w * HG * kWave;
+  for (int h0 = 0; h0 < G; h0 += HG) {
+    const int nh = min(HG, G - h0);
+    if (r < got) {
+      const int c = order[r];
+      const int64_t base = (bg * a.n_max + (int64_t)c * a.S) * D;
+      // the chunk's rows load again in each round of heads (one round unless
+      // the group has more than 8 heads or K * D is large): keeping them
+      // across rounds would not fit in registers beside the next loads
+      u32x4 kr[KV4];                // this lane's key row
+      float lam[CPL];               // this lane's landmark columns
+      uint32_t vr[kWave];           // bf16: value columns of key j as loaded
+      uint32_t vp[kWave / 2][CPL];  // bf16: values of keys 2m, 2m + 1 in one column
+      float vf[kWave][CPL];         // fp32: values of key j
+      {
+#pragma unroll
+        for (int i = 0; i < KV4; ++i)
+          kr[i] = key_ok ? *(const u32x4*)((const char*)a.Kc + (base + (int64_t)lane * D) *
+                                                                    (DT == kF32 ? 4 : 2) + 16 * i)
+                         : u32x4{0u, 0u, 0u, 0u};
+        const float* lc = a.lmk + (bg * a.lmk_chunks + c) * D + CPL * lane;
+#pragma unroll
+        for (int x = 0; x < CPL; ++x) lam[x] = lc[x];
+        if (DT == kBF16) {
+          // values: lane = output columns, one 2- or 4-byte load per key,
+          // in flight with the keys
+#pragma unroll
+          for (int j = 0; j < kWave; ++j) {
+            const int64_t off = base + (int64_t)j * D + CPL * lane;
+            vr[j] = 0u;
+            if (j < a.S)
+              vr[j] = CPL == 2 ? *(const uint32_t*)((const uint16_t*)a.Vc + off)
+                               : (uint32_t)((const uint16_t*)a.Vc)[off];
+          }
+        }
+      }
+      // logits, softmax over the chunk's keys, s_h: one head at a time; the
+      // normalised weights go to this wave's LDS rows (bf16 pairs of
+      // consecutive keys, or fp32)
+      for (int hh = 0; hh < nh; ++hh) {
+        const int h = h0 + hh;
+        float acc = 0.f;
+        if (DT == kF32) {
+          const f32x4* qv = (const f32x4*)(qf + h * D);
+#pragma unroll
+          for (int i = 0; i < KV4; ++i) {
+            const f32x4 q4 = qv[i];
+            const f32x4 k4 = __builtin_bit_cast(f32x4, kr[i]);
+            acc += q4[0] * k4[0] + q4[1] * k4[1] + q4[2] * k4[2] + q4[3] * k4[3];
+          }
+        } else {
+          const u32x4* qv = (const u32x4*)(qb + h * D / 2);
+#pragma unroll
+          for (int i = 0; i < KV4; ++i) {
+            const u32x4 q4 = qv[i];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              // copy the elements out first: bit casts of vector-element
+              // operands read element 0
+              const uint32_t kw = kr[i][v], qw = q4[v];
+              acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw),
+                                                    __builtin_bit_cast(bf16x2, qw), acc, false);
+            }
+          }
+        }
+        const float sc = key_ok ? acc * scale : -INFINITY;
+        const float mx = wave_max_f32(sc);
+        const float p = key_ok ? expf(sc - mx) : 0.f;
+        const float pn = p / wave_sum_f32(p);
+        if (DT == kF32) {
+          pw[hh * kWave + lane] = pn;
+        } else {
+          const float next = partner<1>(pn);  // the weight of key lane + 1
+          if ((lane & 1) == 0) ((uint32_t*)pw)[hh * kWave + lane / 2] = pack_bf16x2(pn, next);
+        }
+        float sl = 0.f;
+#pragma unroll
+        for (int x = 0; x < CPL; ++x) sl += qf[h * D + CPL * lane + x] * lam[x];
+        sl = wave_sum_f32(sl);
+        if (lane == 0) {
+          if (R == 1) psc[hh * K + r] = sl * scale;
+          else a.part_s[(qrow0 + h) * K + r] = sl * scale;
+        }
+      }
+      {
+        if (DT == kBF16) {
+          // pair consecutive keys per column for the packed dot products
+#pragma unroll
+          for (int m = 0; m < kWave / 2; ++m) {
+            vp[m][0] = __builtin_amdgcn_perm(vr[2 * m + 1], vr[2 * m], 0x05040100u);
+            if (CPL == 2) vp[m][CPL - 1] = __builtin_amdgcn_perm(vr[2 * m + 1], vr[2 * m], 0x07060302u);
+          }
+        } else {
+          // values: lane = output columns, one 4- or 8-byte load per key
+#pragma unroll
+          for (int j = 0; j < kWave; ++j) {
+            const int64_t off = base + (int64_t)j * D + CPL * lane;
+#pragma unroll
+            for (int x = 0; x < CPL; ++x) vf[j][x] = j < a.S ? ((const float*)a.Vc)[off + x] : 0.f;
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int hh = 0; hh < nh; ++hh) {
+        float o[CPL];
+#pragma unroll
+        for (int x = 0; x < CPL; ++x) o[x] = 0.f;
+        if (DT == kF32) {
+#pragma unroll
+          for (int j = 0; j < kWave; j += 4) {
+            const f32x4 p4 = *(const f32x4*)(pw + hh * kWave + j);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+              for (int x = 0; x < CPL; ++x) o[x] += p4[jj] * vf[j + jj][x];
+          }
+        } else {
+          const uint32_t* pp = (const uint32_t*)pw + hh * kWave;
+#pragma unroll
+          for (int m = 0; m < kWave / 2; m += 4) {
+            const u32x4 p4 = *(const u32x4*)(pp + m);
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm) {
+              const uint32_t pq = p4[mm];
+#pragma unroll
+              for (int x = 0; x < CPL; ++x) {
+                const uint32_t vq = vp[m + mm][x];
+                o[x] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vq),
+                                                       __builtin_bit_cast(bf16x2, pq), o[x], false);
+              }
+            }
+          }
+        }
+        float* po = (R == 1 ? part + ((int64_t)hh * K + r) * D
+                            : a.part_o + ((qrow0 + h0 + hh) * K + r) * D) + CPL * lane;
+#pragma unroll
+        for (int x = 0; x < CPL; ++x) po[x] = o[x];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (R > 1) continue;  // fuse_kernel combines the blocks' outputs
+    __syncthreads();
+    // fusion weights: per head, a softmax over the ranks' s_h
+    for (int e = tid; e < nh * K; e += NT) {
+      const int hh = e / K, kk = e % K;
+      const float* sc = psc + hh * K;
+      float smax = -INFINITY, z = 0.f;
+      for (int j = 0; j < got; ++j) smax = fmaxf(smax, sc[j]);
+      for (int j = 0; j < got; ++j) z += expf(sc[j] - smax);
+      const float wk = kk < got ? expf(sc[kk] - smax) / z : 0.f;
+      wts[e] = wk;
+      if (a.sel_w) a.sel_w[(qrow0 + h0 + hh) * K + kk] = wk;
+    }
+    __syncthreads();
+    for (int e = tid; e < nh * D; e += NT) {
+      const int hh = e / D, x = e % D;
+      float acc = 0.f;
+      for (int kk = 0; kk < got; ++kk) acc += wts[hh * K + kk] * part[(hh * K + kk) * D + x];
+      store_elem<DT>(a.o, (qrow0 + h0 + hh) * D + x, acc);
+    }
+    __syncthreads();
+  }
+}
+
 template <int D, int DT>
 hipError_t stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
   const int64_t BG = (int64_t)a.B * a.Hkv;
@@ -482,6 +909,15 @@ hipError_t stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
     if (a.n_avail > 0)
       scan_kernel<D, DT><<<dim3((unsigned)(BG * a.n_slices)), dim3(kThreads),
                            (size_t)a.slice * sizeof(uint64_t), stream>>>(a);
+  } else if (const size_t lds = fused_lds_bytes(a)) {
+    // chunks of at most 64 keys: one wave per selected chunk; with K <= 8
+    // the attention block also fuses
+    const int R = (a.topk + kFusedWaves - 1) / kFusedWaves;
+    if (stage == 1)
+      attend_fused_kernel<D, DT><<<dim3((unsigned)(BG * R)), dim3(kFusedThreads), lds, stream>>>(
+          a, scale);
+    else if (R > 1)
+      fuse_kernel<D, DT><<<dim3((unsigned)BG), dim3(kThreads), 0, stream>>>(a);
   } else if (stage == 1) {
     attend_kernel<D, DT><<<dim3((unsigned)(BG * a.topk)), dim3(kThreads),
                            decode_attend_lds(a.Hq, a.Hkv, D, a.n_slices, a.topk), stream>>>(a, scale);

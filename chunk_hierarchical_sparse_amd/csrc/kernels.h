@@ -77,7 +77,8 @@ struct DecodeArgs {
 };
 void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* slice);
 // stages: 0 scan (landmark stream + per-slice top-K), 1 attend (merge of the
-// slices' candidates, per-chunk attention), 2 fuse
+// slices' candidates, per-chunk attention; with chunks of <= 64 keys and
+// K <= 8 also the fusion), 2 fuse (empty when stage 1 fused)
 constexpr int kDecodeStages = 3;
 // dynamic LDS bytes of the attention stage
 size_t decode_attend_lds(int Hq, int Hkv, int d, int n_slices, int topk);

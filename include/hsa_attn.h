@@ -285,7 +285,8 @@ hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t p
  * event on its stream before each of its stages and one after the last:
  *   hsa_prefill : 0 landmarks, 1 select, 2 invert, 3 attend, 4 fuse
  *   hsa_decode  : 0 scan (landmark stream, per-slice top-K), 1 attend (merge
- *                 of the slices' candidates, chunk attention), 2 fuse
+ *                 of the slices' candidates, chunk attention; also the
+ *                 fusion when S <= 64 and topk <= 8), 2 fuse (then empty)
  *   dhsa_prefill: 0 pool, 1 S_c, 2 rank, 3 attend, 4 mask
  *   dhsa_decode : 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
  *   swa_prefill, swa_decode: 0 attend

@@ -43,6 +43,12 @@ CASES = [
     (2, 4, 1, 1000, 999, 128, 16, 32, "bf16"),
     (1, 2, 2, 300, 300, 64, 1, 8, "f32"),
     (1, 8, 1, 5000, 4500, 128, 200, 3, "bf16"),
+    # chunks of <= 64 keys take one wave per chunk; these cover fp32 rows of
+    # 128, groups of 16 heads handled in rounds of 8 and of 4, R = 2 blocks
+    # per group, and groups of 3 heads with d = 64 in bf16
+    (2, 16, 1, 3000, 2900, 128, 64, 8, "f32"),
+    (1, 32, 2, 2048, 2047, 128, 32, 16, "bf16"),
+    (2, 6, 2, 1500, 1400, 64, 64, 8, "bf16"),
 ]
 
 
