@@ -114,54 +114,6 @@ __device__ int block_topk_ge(const uint64_t* keys, int M, uint64_t lo, int K, ui
   return K;
 }
 
-// The value of lane (this lane ^ j), j a power of two below 64 known at
-// compile time after unrolling.  j <= 8 stays in the lane's 16-lane row and
-// goes through DPP moves: the quad permutations give j = 1, 2, and j = 4, 8
-// compose two mirrors (lane ^ 3 then ^ 7, lane ^ 7 then ^ 15).  j = 16, 32
-// cross rows and use the LDS permute.
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int j) {
-  const int x = (int)v;
-  if (j == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
-  if (j == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
-  if (j == 4)
-    return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false),
-                                              0x141, 0xF, 0xF, false);
-  if (j == 8)
-    return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false),
-                                              0x140, 0xF, 0xF, false);
-  return (uint32_t)__shfl_xor(x, j, kWave);
-}
-
-__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int j) {
-  return (uint64_t)lane_xor((uint32_t)v, j) | ((uint64_t)lane_xor((uint32_t)(v >> 32), j) << 32);
-}
-
-__device__ __forceinline__ float lane_xor_f32(float v, int j) {
-  return __builtin_bit_cast(float, lane_xor(__builtin_bit_cast(uint32_t, v), j));
-}
-
-// Wave-wide maximum and sum: butterflies inside each 16-lane row, then the
-// four row results read out of lanes 0, 16, 32, 48.
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int j = 1; j < 16; j <<= 1) v = fmaxf(v, lane_xor_f32(v, j));
-  const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
-}
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int j = 1; j < 16; j <<= 1) v += lane_xor_f32(v, j);
-  const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return (a0 + a1) + (a2 + a3);
-}
-
 // Bitonic sort of one 64-bit key per lane across the wave, descending
 // (lane 0 ends with the largest).
 __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t x) {
@@ -636,7 +588,6 @@ constexpr int kFusedWaves = 8;
 constexpr int kFusedThreads = kFusedWaves * kWave;
 constexpr int kFusedPartBytes = 32768;  // LDS for one round's chunk outputs
 constexpr int kFusedMaxLds = 61440;  // dynamic LDS bytes (static arrays take ~1.5 KB)
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __host__ __device__ inline int fused_heads(int G, int K, int D) {
   int hg = kFusedPartBytes / (K * D * 4);
