@@ -68,6 +68,88 @@ __device__ void pool_rows(const void* src, int64_t row0, int nrows, float* out, 
   __syncthreads();
 }
 
+// pool_rows over two sources at once (the current chunk's queries and
+// keys), their loads in flight together; barriers order LDS only, so
+// global loads issued before the call stay in flight.  `scratch` holds
+// 2 * kThreads * VE floats.
+template <int D, int DT>
+__device__ void pool_rows2(const void* srcA, int64_t rowA, const void* srcB, int64_t rowB,
+                           int nrows, float* outA, float* outB, float* scratch) {
+  constexpr int VE = DT == kF32 ? 4 : 8;  // elements per 16-byte piece
+  constexpr int CG = D / VE;              // pieces per row
+  constexpr int RG = kThreads / CG;       // row groups
+  const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
+  float accA[VE], accB[VE];
+#pragma unroll
+  for (int v = 0; v < VE; ++v) accA[v] = accB[v] = 0.f;
+  for (int r = rg; r < nrows; r += RG) {
+    const int64_t ea = (rowA + r) * D + cg * VE, eb = (rowB + r) * D + cg * VE;
+    if (DT == kF32) {
+      const f32x4 x = *(const f32x4*)((const float*)srcA + ea);
+      const f32x4 y = *(const f32x4*)((const float*)srcB + eb);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        accA[v] += x[v];
+        accB[v] += y[v];
+      }
+    } else {
+      const u32x4 x = *(const u32x4*)((const uint16_t*)srcA + ea);
+      const u32x4 y = *(const u32x4*)((const uint16_t*)srcB + eb);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        accA[2 * v] += bf16_bits_to_f32(x[v] & 0xffffu);
+        accA[2 * v + 1] += bf16_bits_to_f32(x[v] >> 16);
+        accB[2 * v] += bf16_bits_to_f32(y[v] & 0xffffu);
+        accB[2 * v + 1] += bf16_bits_to_f32(y[v] >> 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < VE; ++v) {
+    scratch[rg * D + cg * VE + v] = accA[v];
+    scratch[(RG + rg) * D + cg * VE + v] = accB[v];
+  }
+  block_sync_lds();
+  const float rs = __fsqrt_rn((float)nrows);
+  for (int x = threadIdx.x; x < D; x += kThreads) {
+    float sa = 0.f, sb = 0.f;
+    for (int g = 0; g < RG; ++g) {
+      sa += scratch[g * D + x];
+      sb += scratch[(RG + g) * D + x];
+    }
+    outA[x] = __fdiv_rn(sa, rs);
+    outB[x] = __fdiv_rn(sb, rs);
+  }
+  block_sync_lds();
+}
+
+// Exclusive prefix sum of one int per thread over the block's kThreads
+// threads (wave scans, then the four wave totals); *total receives the sum.
+// `wsum` is kThreads / 64 ints of LDS.  Called by all threads; contains
+// barriers.
+__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) wsum[w] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i) {
+    base += i < w ? wsum[i] : 0;
+    all += wsum[i];
+  }
+  __syncthreads();
+  *total = all;
+  return base + incl - v;
+}
+
+constexpr int kRankSortMax = 1024;  // chunks ranked by counting (else bitonic)
+
 // One block per (b, head, complete chunk in [chunk_begin, chunk_end)).
 template <int D, int DT>
 __global__ void __launch_bounds__(kThreads) chunk_keys_kernel(const void* K, float* khat,
@@ -83,11 +165,19 @@ __global__ void __launch_bounds__(kThreads) chunk_keys_kernel(const void* K, flo
   for (int x = threadIdx.x; x < D; x += kThreads) khat[(bh * n_cap + k) * D + x] = kh[x];
 }
 
+// dynamic LDS of the score kernel: keys [P], cum [P + 1], and with the
+// counting rank a second key buffer [P] (8-byte aligned)
+size_t dhsa_score_lds(int P) {
+  const size_t cum_bytes = ((size_t)(P + 1) * sizeof(int32_t) + 7) / 8 * 8;
+  return (size_t)P * sizeof(uint64_t) + cum_bytes +
+         (P <= kRankSortMax ? (size_t)P * sizeof(uint64_t) : 0);
+}
+
 template <int D, int DT>
 __global__ void __launch_bounds__(kThreads) score_kernel(DhsaDecodeArgs a) {
-  __shared__ float scratch[kThreads * (DT == kF32 ? 4 : 8)];
+  __shared__ float scratch[2 * kThreads * (DT == kF32 ? 4 : 8)];
   __shared__ __attribute__((aligned(16))) float qh[D], kc[D];
-  __shared__ int32_t part[kThreads];
+  __shared__ int32_t part[kThreads / kWave];
   __shared__ int s_pw;
   extern __shared__ uint64_t dyn[];
   uint64_t* keys = dyn;                      // [P]
@@ -96,16 +186,20 @@ __global__ void __launch_bounds__(kThreads) score_kernel(DhsaDecodeArgs a) {
   const int tid = threadIdx.x;
   const int n = a.n, nc = a.n + 1;           // complete chunks, plus the current one
   const int cur0 = a.offs[n];                // first token of the current chunk
-  pool_rows<D, DT>(a.qcur, bh * a.m, a.m, qh, scratch);
-  pool_rows<D, DT>(a.Kc, bh * a.n_max + cur0, a.m, kc, scratch);
   // S_c[k] = q_hat . k_hat_k: one thread per chunk, its row's loads all in
-  // flight at once (the pooled-key stream is this kernel's HBM traffic)
-  for (int k = tid; k < nc; k += kThreads) {
-    f32x4 r[D / 4];
-    if (k < n) {
-      const f32x4* kr = (const f32x4*)(a.khat + (bh * a.n_cap + k) * D);
+  // flight at once (the pooled-key stream is this kernel's HBM traffic);
+  // the first row of each thread loads while the current chunk is pooled
+  f32x4 r[D / 4];
+  auto load_khat = [&](int k) {
+    const f32x4* kr = (const f32x4*)(a.khat + (bh * a.n_cap + k) * D);
 #pragma unroll
-      for (int x = 0; x < D / 4; ++x) r[x] = kr[x];
+    for (int x = 0; x < D / 4; ++x) r[x] = kr[x];
+  };
+  if (tid < n) load_khat(tid);
+  pool_rows2<D, DT>(a.qcur, bh * a.m, a.Kc, bh * a.n_max + cur0, a.m, qh, kc, scratch);
+  for (int k = tid; k < nc; k += kThreads) {
+    if (k < n) {
+      if (k != tid) load_khat(k);
     } else {
 #pragma unroll
       for (int x = 0; x < D / 4; ++x) r[x] = *(const f32x4*)(&kc[4 * x]);
@@ -119,21 +213,36 @@ __global__ void __launch_bounds__(kThreads) score_kernel(DhsaDecodeArgs a) {
   }
   for (int i = nc + tid; i < a.P; i += kThreads) keys[i] = 0ull;
   __syncthreads();
-  // bitonic sort, descending: (S_c desc, chunk index asc); padding last
-  for (int k = 2; k <= a.P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < a.P; i += kThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t x = keys[i], y = keys[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            keys[i] = y;
-            keys[ixj] = x;
+  if (a.P <= kRankSortMax) {
+    // rank by counting: each key's position is the number of larger keys
+    // (keys are distinct); the ranked keys go to the second buffer
+    uint64_t* ranked = (uint64_t*)((char*)cum + ((size_t)(a.P + 1) * sizeof(int32_t) + 7) / 8 * 8);
+    for (int i = tid; i < nc; i += kThreads) {
+      const uint64_t x = keys[i];
+      int r = 0;
+      for (int j = 0; j < nc; ++j) r += keys[j] > x;
+      ranked[r] = x;
+    }
+    __syncthreads();
+    for (int i = tid; i < nc; i += kThreads) keys[i] = ranked[i];
+    __syncthreads();
+  } else {
+    // bitonic sort, descending: (S_c desc, chunk index asc); padding last
+    for (int k = 2; k <= a.P; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < a.P; i += kThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const uint64_t x = keys[i], y = keys[ixj];
+            const bool desc = (i & k) == 0;
+            if (desc ? (x < y) : (x > y)) {
+              keys[i] = y;
+              keys[ixj] = x;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
   // cum[p] = tokens of the chunks ranked before p, p = 0..nc
@@ -144,18 +253,8 @@ __global__ void __launch_bounds__(kThreads) score_kernel(DhsaDecodeArgs a) {
     const int k = (int)key_index(keys[p]);
     s += k < n ? a.offs[k + 1] - a.offs[k] : a.m;
   }
-  part[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    int32_t acc = 0;
-    for (int t = 0; t < kThreads; ++t) {
-      const int32_t v = part[t];
-      part[t] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  int32_t run = part[tid];
+  int32_t tokens_all;  // cum[nc], written below by the thread holding the last rank
+  int32_t run = block_exclusive_scan(s, part, &tokens_all);
   for (int p = p0; p < min(p0 + per, nc); ++p) {
     cum[p] = run;
     const int k = (int)key_index(keys[p]);
@@ -192,20 +291,9 @@ __global__ void __launch_bounds__(kThreads) score_kernel(DhsaDecodeArgs a) {
     run_of(p, st, cnt);
     pieces += (cnt + kPiece - 1) / kPiece;
   }
-  __syncthreads();
-  part[tid] = pieces;
-  __syncthreads();
-  if (tid == 0) {
-    int32_t acc = 0;
-    for (int t = 0; t < kThreads; ++t) {
-      const int32_t v = part[t];
-      part[t] = acc;
-      acc += v;
-    }
-    a.n_plan[bh] = acc;
-  }
-  __syncthreads();
-  int32_t q = part[tid];
+  int32_t pieces_all;
+  int32_t q = block_exclusive_scan(pieces, part, &pieces_all);
+  if (tid == 0) a.n_plan[bh] = pieces_all;
   int32_t* plan = a.plan + bh * a.max_pieces * 2;
   for (int p = p0; p < min(p0 + per, nc); ++p) {
     int st, cnt;
@@ -312,50 +400,59 @@ __global__ void __launch_bounds__(kWave) attend_kernel(DhsaDecodeArgs a, float s
 }
 
 // Per (b, head): out = sum_q o_q e^(m_q - M) / sum_q l_q e^(m_q - M) over
-// the pieces q; each thread's loads are issued 8 at a time.
+// the pieces q.  The pieces' (max, sum) pairs are read once into LDS by one
+// thread each and reduced by waves; then thread t adds column t % D over
+// every kThreads / D-th piece with 8 loads in flight, and the column's
+// partial sums meet in LDS.
 template <int D, int DT>
-__global__ void __launch_bounds__(D) combine_kernel(DhsaDecodeArgs a) {
-  __shared__ float red[D];
-  __shared__ float s_M, s_L;
+__global__ void __launch_bounds__(kThreads) combine_kernel(DhsaDecodeArgs a) {
+  constexpr int PS = kThreads / D;  // piece subsets
+  extern __shared__ float cw[];     // [max_pieces]: e^(m_q - M)
+  __shared__ float red[kThreads / kWave];
+  __shared__ float acc_s[PS][D];
   const int64_t bh = blockIdx.x;
   const int np = a.n_plan[bh];
   const float* part = a.part + bh * a.max_pieces * (D + 2);
-  const int x = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float M = -INFINITY;
-  for (int q = x; q < np; q += D) M = fmaxf(M, part[q * (D + 2)]);
-  red[x] = M;
+  for (int q = tid; q < np; q += kThreads) M = fmaxf(M, part[q * (D + 2)]);
+  M = wave_max_f32(M);
+  if (lane == 0) red[w] = M;
   __syncthreads();
-  if (x == 0) {
-    for (int t = 1; t < D; ++t) M = fmaxf(M, red[t]);
-    s_M = M;
-  }
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i) M = fmaxf(M, red[i]);
   __syncthreads();
-  M = s_M;
   float L = 0.f;
-  for (int q = x; q < np; q += D) L += part[q * (D + 2) + 1] * expf(part[q * (D + 2)] - M);
-  __syncthreads();
-  red[x] = L;
-  __syncthreads();
-  if (x == 0) {
-    float t = 0.f;
-    for (int i = 0; i < D; ++i) t += red[i];
-    s_L = t;
+  for (int q = tid; q < np; q += kThreads) {
+    const float f = expf(part[q * (D + 2)] - M);
+    cw[q] = f;
+    L += part[q * (D + 2) + 1] * f;
   }
+  L = wave_sum_f32(L);
+  if (lane == 0) red[w] = L;
+  __syncthreads();
+  L = 0.f;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i) L += red[i];
+  const int x = tid % D, sub = tid / D;
   float O = 0.f;
-  int q = 0;
-  for (; q + 8 <= np; q += 8) {
-    float v[8], f[8];
+  int q = sub;
+  for (; q + 7 * PS < np; q += 8 * PS) {
+    float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      v[u] = part[(q + u) * (D + 2) + 2 + x];
-      f[u] = part[(q + u) * (D + 2)];
-    }
+    for (int u = 0; u < 8; ++u) v[u] = part[(q + u * PS) * (D + 2) + 2 + x];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) O += v[u] * expf(f[u] - M);
+    for (int u = 0; u < 8; ++u) O += v[u] * cw[q + u * PS];
   }
-  for (; q < np; ++q) O += part[q * (D + 2) + 2 + x] * expf(part[q * (D + 2)] - M);
+  for (; q < np; q += PS) O += part[q * (D + 2) + 2 + x] * cw[q];
+  acc_s[sub][x] = O;
   __syncthreads();
-  store_elem<DT>(a.o, bh * D + x, np > 0 ? O / s_L : 0.f);
+  if (sub == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < PS; ++i) t += acc_s[i][x];
+    store_elem<DT>(a.o, bh * D + x, np > 0 ? t / L : 0.f);
+  }
 }
 
 template <int D, int DT>
@@ -363,16 +460,15 @@ hipError_t decode_dt(const DhsaDecodeArgs& a, int stage, hipStream_t stream) {
   const int64_t BH = (int64_t)a.B * a.H;
   switch (stage) {
     case 0:
-      score_kernel<D, DT><<<dim3((unsigned)BH), dim3(kThreads),
-                            (size_t)a.P * sizeof(uint64_t) + (size_t)(a.P + 1) * sizeof(int32_t),
-                            stream>>>(a);
+      score_kernel<D, DT><<<dim3((unsigned)BH), dim3(kThreads), dhsa_score_lds(a.P), stream>>>(a);
       break;
     case 1:
       attend_kernel<D, DT><<<dim3((unsigned)(BH * a.max_pieces)), dim3(kWave), 0, stream>>>(
           a, 1.0f / sqrtf((float)D));
       break;
     default:
-      combine_kernel<D, DT><<<dim3((unsigned)BH), dim3(D), 0, stream>>>(a);
+      combine_kernel<D, DT><<<dim3((unsigned)BH), dim3(kThreads),
+                              (size_t)a.max_pieces * sizeof(float), stream>>>(a);
       break;
   }
   return hipGetLastError();
