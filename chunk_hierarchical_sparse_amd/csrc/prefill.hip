@@ -836,23 +836,30 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(PrefillArgs a) {
   const int64_t t0 = t / a.interval * a.interval;  // where the row's selection was made
   const int m = (int)min((int64_t)a.topk, min(t0 / a.S, a.n));
   const int32_t* epos = a.entry_pos + (bg * a.L + t) * a.topk;
+  // every load is issued unconditionally (slots past m read row 0 and are
+  // dropped afterwards): guarding them per lane would make each wait for
+  // the one before
+  int32_t ep[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) ep[k] = epos[min(k, a.topk - 1)];  // in bounds; unused past m
   int64_t pr[KM];
 #pragma unroll
-  for (int k = 0; k < KM; ++k) pr[k] = k < m ? partial_row(a, bg, epos[k], hh) : 0;
+  for (int k = 0; k < KM; ++k) pr[k] = k < m ? partial_row(a, bg, ep[k], hh) : 0;
   u32x4 x[KM];
+  float s[KM];
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    if (k < m)
-      x[k] = __builtin_nontemporal_load(
-          (const u32x4*)((const char*)a.partial + (pr[k] * D + cg * VEC) * (DT == kF32 ? 4 : 2)));
-    else
-      x[k] = u32x4{0u, 0u, 0u, 0u};
+    x[k] = __builtin_nontemporal_load(
+        (const u32x4*)((const char*)a.partial + (pr[k] * D + cg * VEC) * (DT == kF32 ? 4 : 2)));
+    s[k] = a.part_score[pr[k]];
   }
-  float s[KM];
   float smax = -INFINITY;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    s[k] = k < m ? a.part_score[pr[k]] : -INFINITY;
+    if (k >= m) {
+      x[k] = u32x4{0u, 0u, 0u, 0u};
+      s[k] = -INFINITY;
+    }
     smax = fmaxf(smax, s[k]);
   }
   float z = 0.f;

@@ -147,17 +147,21 @@ __global__ void __launch_bounds__(kThreads) bwd_weights_kernel(PrefillBwdArgs ba
   const int m = (int)min((int64_t)a.topk, min(t / a.S, a.n));
   const int32_t* sel = a.idx + (bg * a.nq + t) * a.topk;
   const int32_t* epos = a.entry_pos + (bg * a.L + t) * a.topk;
+  // loads issued unconditionally (slots past m read in-bounds entries,
+  // dropped below): per-lane guards would make each wait for the one before
   f32x4 lam[KM][2];
-  int32_t ep[KM];
+  int32_t ep[KM], ck[KM];
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    lam[k][0] = lam[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    ep[k] = k < m ? epos[k] : 0;
-    if (k < m) {
-      const float* lc = a.lmk + (bg * a.n + sel[k]) * D + cg * 8;
-      lam[k][0] = *(const f32x4*)lc;
-      lam[k][1] = *(const f32x4*)(lc + 4);
-    }
+    const int kk = min(k, a.topk - 1);
+    ep[k] = epos[kk];
+    ck[k] = sel[kk];
+  }
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const float* lc = a.lmk + (bg * a.n + (k < m ? ck[k] : 0)) * D + cg * 8;
+    lam[k][0] = *(const f32x4*)lc;
+    lam[k][1] = *(const f32x4*)(lc + 4);
   }
   for (int hh = 0; hh < G; ++hh) {
     const u32x4 qv = *(const u32x4*)((const uint16_t*)a.Q +
@@ -370,14 +374,22 @@ __global__ void __launch_bounds__(kThreads) bwd_rows_kernel(PrefillBwdArgs ba) {
   const int64_t bg = r / G / a.L;
   const int m = (int)min((int64_t)a.topk, min(t / a.S, a.n));
   const int32_t* epos = a.entry_pos + (bg * a.L + t) * a.topk;
+  // two rounds of loads, none guarded per lane (slots past m read row 0)
+  int32_t ep[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) ep[k] = epos[min(k, a.topk - 1)];
   int64_t pr[KM];
   float wk[KM], dw[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    pr[k] = k < m ? partial_row(a, bg, ep[k], hh) : 0;
+    wk[k] = ba.wk[pr[k]];
+    dw[k] = ba.dw[pr[k]];
+  }
   float wdw = 0.f;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    pr[k] = k < m ? partial_row(a, bg, epos[k], hh) : 0;
-    wk[k] = k < m ? ba.wk[pr[k]] : 0.f;
-    dw[k] = k < m ? ba.dw[pr[k]] : 0.f;
+    if (k >= m) wk[k] = dw[k] = 0.f;
     wdw += wk[k] * dw[k];
   }
 #pragma unroll
@@ -582,22 +594,31 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(PrefillBwdArgs ba, flo
   float acc[8];
 #pragma unroll
   for (int v = 0; v < 8; ++v) acc[v] = 0.f;
-  u32x4 x[KM];
-  float dsk[KM];
-  int32_t ck[KM];
+  // every load is issued unconditionally (slots past m read in-bounds
+  // entries and are dropped): per-lane guards would make each wait for the
+  // one before.  Round 1: list positions and chunks; round 2: the rest.
+  int32_t ep[KM], ck[KM];
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    const int64_t pr = k < m ? partial_row(a, bg, epos[k], hh) : 0;
-    x[k] = k < m ? *(const u32x4*)((const uint16_t*)a.partial + pr * D + cg * 8)
-                 : u32x4{0u, 0u, 0u, 0u};
-    dsk[k] = k < m ? ba.ds[pr] * sc : 0.f;
-    ck[k] = k < m ? sel[k] : 0;
+    const int kk = min(k, a.topk - 1);
+    ep[k] = epos[kk];
+    ck[k] = sel[kk];
+  }
+  u32x4 x[KM];
+  float dsk[KM];
+  f32x4 l0[KM], l1[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int64_t pr = k < m ? partial_row(a, bg, ep[k], hh) : 0;
+    x[k] = *(const u32x4*)((const uint16_t*)a.partial + pr * D + cg * 8);
+    dsk[k] = ba.ds[pr] * sc;
+    const float* lc = a.lmk + (bg * a.n + (k < m ? ck[k] : 0)) * D + cg * 8;
+    l0[k] = *(const f32x4*)lc;
+    l1[k] = *(const f32x4*)(lc + 4);
   }
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
     if (k >= m) break;
-    const float* lc = a.lmk + (bg * a.n + ck[k]) * D + cg * 8;
-    const f32x4 l0 = *(const f32x4*)lc, l1 = *(const f32x4*)(lc + 4);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       acc[2 * v] += bf16_bits_to_f32(x[k][v] & 0xffffu);
@@ -605,8 +626,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(PrefillBwdArgs ba, flo
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      acc[v] += dsk[k] * l0[v];
-      acc[4 + v] += dsk[k] * l1[v];
+      acc[v] += dsk[k] * l0[k][v];
+      acc[4 + v] += dsk[k] * l1[k][v];
     }
   }
   const int64_t ob = ((b * a.Hq + h) * a.L + t) * D + cg * 8;
