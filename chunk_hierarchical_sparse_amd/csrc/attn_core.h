@@ -30,31 +30,44 @@ struct KVSmem {
   uint16_t v[(kKeyBlock / 4) * D * 4];
 };
 
-// Stage keys/values rows [0, nk) of a block (row stride D elements) into
-// LDS; rows nk..63 are zero so masked keys never meet non-finite data.
-// Called by all threads of a 256-thread block.
+// Stage keys/values rows [0, nk) (1 <= nk <= 64) of a block (row stride D
+// elements) into LDS; rows nk..63 are zero so masked keys never meet
+// non-finite data.  Every load is issued before any store (rows past nk
+// re-read row nk - 1 and are zeroed): guarded loads would each wait for
+// the one before.  Called by all threads of a 256-thread block.
 template <int D>
 __device__ __forceinline__ void load_kv_block(KVSmem<D>& sm, const uint16_t* __restrict__ Kg,
                                               const uint16_t* __restrict__ Vg, int nk) {
   const int tid = threadIdx.x;
-  constexpr int KPR = D / 8;  // 16-byte pieces per key row
+  constexpr int KPR = D / 8;                        // 16-byte pieces per key row
+  constexpr int NKL = kKeyBlock * KPR / 256;        // key loads per thread
+  constexpr int VPR = D / 4;                        // 8-byte pieces per value row
+  constexpr int NVL = (kKeyBlock / 4) * VPR / 256;  // value quads per thread
+  u32x4 kx[NKL];
 #pragma unroll
-  for (int e = tid; e < kKeyBlock * KPR; e += 256) {
-    const int row = e / KPR, c8 = e % KPR;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < nk) x = *(const u32x4*)(Kg + (int64_t)row * D + c8 * 8);
-    *(u32x4*)(&sm.k[row * (D + 8) + c8 * 8]) = x;
+  for (int i = 0; i < NKL; ++i) {
+    const int e = tid + i * 256, row = e / KPR, c8 = e % KPR;
+    kx[i] = *(const u32x4*)(Kg + (int64_t)min(row, nk - 1) * D + c8 * 8);
   }
-  constexpr int VPR = D / 4;  // 8-byte pieces per value row
+  u32x2 vr[NVL][4];
 #pragma unroll
-  for (int e = tid; e < (kKeyBlock / 4) * VPR; e += 256) {
-    const int grp = e / VPR, cq = e % VPR;
+  for (int i = 0; i < NVL; ++i) {
+    const int e = tid + i * 256, grp = e / VPR, cq = e % VPR;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      vr[i][kk] = *(const u32x2*)(Vg + (int64_t)min(grp * 4 + kk, nk - 1) * D + cq * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < NKL; ++i) {
+    const int e = tid + i * 256, row = e / KPR, c8 = e % KPR;
+    *(u32x4*)(&sm.k[row * (D + 8) + c8 * 8]) = row < nk ? kx[i] : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < NVL; ++i) {
+    const int e = tid + i * 256, grp = e / VPR, cq = e % VPR;
     u32x2 r[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int key = grp * 4 + kk;
-      r[kk] = key < nk ? *(const u32x2*)(Vg + (int64_t)key * D + cq * 4) : u32x2{0u, 0u};
-    }
+    for (int kk = 0; kk < 4; ++kk) r[kk] = grp * 4 + kk < nk ? vr[i][kk] : u32x2{0u, 0u};
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int w = x >> 1;
