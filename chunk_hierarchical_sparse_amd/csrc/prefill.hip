@@ -208,32 +208,40 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
   const int64_t tlast_w = min(qt * QPB + w * 32 + 31, a.nq - 1) * a.interval;
   const int64_t wavail = qt * QPB + w * 32 < a.nq ? min(tlast_w / a.S, a.n) : 0;
 
-  // u = sum over the group's heads, dims 16s + 8hf + e, split in 3 parts
+  // u = sum over the group's heads, dims 16s + 8hf + e, split in 3 parts;
+  // one head's row pieces are all in flight at once (heads in order, so
+  // the sum is the same as adding one head at a time)
   bf16x8 u0[D / 16], u1[D / 16], u2[D / 16];
   {
     const uint16_t* Q = (const uint16_t*)a.Q;
+    float acc[D / 16][8];
 #pragma unroll
-    for (int s2 = 0; s2 < D / 16; ++s2) {
-      float acc[8];
+    for (int s2 = 0; s2 < D / 16; ++s2)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-      if (tvalid) {
-        for (int hh = 0; hh < G; ++hh) {
-          const u32x4 x = *(const u32x4*)(Q + (((int64_t)b * a.Hq + g * G + hh) * a.L + t) * D +
-                                          16 * s2 + 8 * hf);
+      for (int e = 0; e < 8; ++e) acc[s2][e] = 0.f;
+    if (tvalid) {
+      for (int hh = 0; hh < G; ++hh) {
+        const uint16_t* qrow = Q + (((int64_t)b * a.Hq + g * G + hh) * a.L + t) * D + 8 * hf;
+        u32x4 x[D / 16];
+#pragma unroll
+        for (int s2 = 0; s2 < D / 16; ++s2) x[s2] = *(const u32x4*)(qrow + 16 * s2);
+#pragma unroll
+        for (int s2 = 0; s2 < D / 16; ++s2)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            acc[2 * v] += bf16_bits_to_f32(x[v] & 0xffffu);
-            acc[2 * v + 1] += bf16_bits_to_f32(x[v] >> 16);
+            acc[s2][2 * v] += bf16_bits_to_f32(x[s2][v] & 0xffffu);
+            acc[s2][2 * v + 1] += bf16_bits_to_f32(x[s2][v] >> 16);
           }
-        }
       }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2) {
       u32x4 p0, p1, p2;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         uint16_t h0, l0, m0, h1, l1, m1;
-        split3_bf16(acc[2 * v], h0, l0, m0);
-        split3_bf16(acc[2 * v + 1], h1, l1, m1);
+        split3_bf16(acc[s2][2 * v], h0, l0, m0);
+        split3_bf16(acc[s2][2 * v + 1], h1, l1, m1);
         p0[v] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         p1[v] = (uint32_t)l0 | ((uint32_t)l1 << 16);
         p2[v] = (uint32_t)m0 | ((uint32_t)m1 << 16);
