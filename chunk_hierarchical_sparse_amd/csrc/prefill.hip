@@ -401,6 +401,16 @@ __device__ __forceinline__ int64_t sel_of(const PrefillArgs& a, int64_t i) {
   const uint32_t tok = u / k;
   return (int64_t)((tok / (uint32_t)a.interval) * k + (u - tok * k));
 }
+// Selection chunk of entries i = i0 + 256 u (u < 8) of [.., e1): all eight
+// loads go out together (past e1: -1, reading the last entry instead).
+__device__ __forceinline__ void load_sel8(const PrefillArgs& a, const int32_t* idx, int64_t i0,
+                                          int64_t e1, int32_t (&c)[8]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) c[u] = idx[sel_of(a, min(i0 + 256 * u, e1 - 1))];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (i0 + 256 * u >= e1) c[u] = -1;
+}
 constexpr int kInvertLdsBins = 8192;  // chunks whose counters fit in LDS (2 arrays)
 
 // Per-chunk selection counts.  Each block histograms the selections of
@@ -419,13 +429,18 @@ __global__ void __launch_bounds__(256) count_kernel(PrefillArgs a, int64_t block
     for (int c = threadIdx.x; c < a.n; c += 256) hist[c] = 0;
     __syncthreads();
   }
-  for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
-    const int32_t c = idx[sel_of(a, i)];
-    if (c < 0) continue;
-    if (use_lds)
-      atomicAdd(&hist[c], 1);
-    else
-      atomicAdd(&cnt[c], 1);
+  const int64_t e1 = t1 * a.topk;
+  for (int64_t i0 = t0 * a.topk + threadIdx.x; i0 < e1; i0 += 8 * 256) {
+    int32_t c[8];
+    load_sel8(a, idx, i0, e1, c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c[u] < 0) continue;
+      if (use_lds)
+        atomicAdd(&hist[c[u]], 1);
+      else
+        atomicAdd(&cnt[c[u]], 1);
+    }
   }
   if (!use_lds) return;
   __syncthreads();
@@ -465,18 +480,26 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
   int32_t* pos = bins + a.n;
   for (int c = threadIdx.x; c < a.n; c += 256) local[c] = 0;
   __syncthreads();
-  for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
-    const int32_t c = idx[sel_of(a, i)];
-    if (c >= 0) atomicAdd(&local[c], 1);
+  const int64_t e1 = t1 * a.topk;
+  for (int64_t i0 = t0 * a.topk + threadIdx.x; i0 < e1; i0 += 8 * 256) {
+    int32_t c[8];
+    load_sel8(a, idx, i0, e1, c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c[u] >= 0) atomicAdd(&local[c[u]], 1);
   }
   __syncthreads();
   for (int c = threadIdx.x; c < a.n; c += 256)
     pos[c] = local[c] != 0 ? offs[c] + atomicAdd(&cursor[c], local[c]) : 0;
   __syncthreads();
-  for (int64_t i = t0 * a.topk + threadIdx.x; i < t1 * a.topk; i += 256) {
-    const int32_t c = idx[sel_of(a, i)];
-    if (c >= 0) {
-      const int32_t p = atomicAdd(&pos[c], 1);
+  for (int64_t i0 = t0 * a.topk + threadIdx.x; i0 < e1; i0 += 8 * 256) {
+    int32_t c[8];
+    load_sel8(a, idx, i0, e1, c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c[u] < 0) continue;
+      const int64_t i = i0 + 256 * u;
+      const int32_t p = atomicAdd(&pos[c[u]], 1);
       list[p] = (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
       epos[i] = p;
     }
