@@ -257,8 +257,10 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
     float acc = 0.f;
     for (int h0 = 0; h0 < G; h0 += 8) {
       float v[8];
+      // unguarded loads (heads past G re-read head G - 1 and are not added):
+      // guarded ones would each wait for the one before
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = h0 + j < G ? load_elem<DT>(a.q, q0 + (h0 + j) * D) : 0.f;
+      for (int j = 0; j < 8; ++j) v[j] = load_elem<DT>(a.q, q0 + min(h0 + j, G - 1) * D);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (h0 + j < G) acc += v[j];
