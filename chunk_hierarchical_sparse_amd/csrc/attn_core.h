@@ -92,16 +92,18 @@ struct WaveAttn {
   float l;            // running sum of exp2(logit - m)
 };
 
+// qrow must point at a readable row even when !valid (the row is loaded and
+// then zeroed: loads guarded per lane would each wait for the one before).
 template <int D>
 __device__ __forceinline__ void wave_attn_init(WaveAttn<D>& st, const uint16_t* qrow,
                                                bool valid) {
   const int h = (threadIdx.x & 63) >> 5;
+  u32x4 x[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (valid) x = *(const u32x4*)(qrow + 16 * s + 8 * h);
-    st.qf[s] = __builtin_bit_cast(bf16x8, x);
-  }
+  for (int s = 0; s < D / 16; ++s) x[s] = *(const u32x4*)(qrow + 16 * s + 8 * h);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    st.qf[s] = __builtin_bit_cast(bf16x8, valid ? x[s] : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll

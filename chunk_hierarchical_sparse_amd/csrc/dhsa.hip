@@ -216,7 +216,7 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   const uint16_t* Kb = (const uint16_t*)a.K + bh * a.L * D;
   const uint16_t* Vb = (const uint16_t*)a.V + bh * a.L * D;
   WaveAttn<D> st;
-  wave_attn_init<D>(st, Qb + i * D, valid);
+  wave_attn_init<D>(st, Qb + min(i, a.L - 1) * D, valid);
   const bool wave_any = __ballot(valid) != 0;
   const int32_t* order = a.order + (bh * a.nc + l) * a.nc;
   // Key blocks in rank order: chunk order[p], keys [kb, kb + 128).  Each

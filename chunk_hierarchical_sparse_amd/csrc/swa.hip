@@ -57,7 +57,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(SwaArgs a, fl
   const uint16_t* Kb = (const uint16_t*)a.K + bg * a.L * D;
   const uint16_t* Vb = (const uint16_t*)a.V + bg * a.L * D;
   WaveAttn<D> st;
-  wave_attn_init<D>(st, (const uint16_t*)a.Q + (((int64_t)b * a.Hq + h) * a.L + t) * D, valid);
+  wave_attn_init<D>(st, (const uint16_t*)a.Q + (((int64_t)b * a.Hq + h) * a.L + min(t, a.L - 1)) * D,
+                    valid);
   const int64_t t_end = min(a.L, t0 + MQ);
   const int64_t k_lo = max((int64_t)0, t0 - a.window + 1);
   KVRegsWide<D> rg;
