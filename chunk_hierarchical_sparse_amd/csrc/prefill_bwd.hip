@@ -100,6 +100,24 @@ __device__ __forceinline__ void split_row(int r, int G, int lg, int& ei, int& hh
   }
 }
 
+// One row's Q and dO as load_row_pair gives them, loaded unconditionally
+// (a missing row, entry < 0, reads token 0 and is zeroed by the caller):
+// loads guarded per lane would each be waited for before the next.
+template <int D>
+__device__ __forceinline__ void load_row_pair_nb(const PrefillBwdArgs& ba, int64_t qbase,
+                                                 int64_t qplane, int32_t entry, int hh, int hf,
+                                                 u32x4 (&q)[D / 16], u32x4 (&o)[D / 16]) {
+  const int64_t tok = entry >= 0 ? (int64_t)(entry >> kSlotBits) : 0;
+  const int64_t off = qbase + (int64_t)hh * qplane + tok * D + 8 * hf;
+  const uint16_t* qr = (const uint16_t*)ba.p.Q + off;
+  const uint16_t* orow = (const uint16_t*)ba.dO + off;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    q[s] = *(const u32x4*)(qr + 16 * s);
+    o[s] = *(const u32x4*)(orow + 16 * s);
+  }
+}
+
 // One row's Q and dO (dims 16s + 8h .. +7 for s = 0 .. D/16-1), zero when
 // the row does not exist.
 template <int D>
@@ -235,14 +253,22 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
   const int64_t row0 = partial_row(a, bg, e_begin, 0);
   const bool two = a.S > 32;
   const f32x16 zero = {};
+  const int last_ei = rows > 0 ? (rows - 1) / G : 0;
   for (int tile = w; tile < ntiles; tile += kThreads / kWave) {
     const int r = tile * 32 + i32;
     int ei, hh;
     split_row(r, G, a.log2G, ei, hh);
-    const int32_t entry = r < rows ? list[ei] : -1;
+    // unguarded loads (past the unit: clamped, then dropped)
+    const int32_t e_raw = list[min(ei, last_ei)];
+    const int32_t entry = r < rows ? e_raw : -1;
     u32x4 q[D / 16], o[D / 16];
-    load_row_pair<D>(ba, qbase, qplane, entry, hh, hf, q, o);
-    const float wr = entry >= 0 ? ba.wk[row0 + r] : 0.f;
+    load_row_pair_nb<D>(ba, qbase, qplane, entry, hh, hf, q, o);
+    const float wr_raw = ba.wk[row0 + min(r, rows - 1)];
+    const float wr = entry >= 0 ? wr_raw : 0.f;
+    if (entry < 0) {
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = o[s2] = u32x4{0u, 0u, 0u, 0u};
+    }
     f32x16 s0 = zero, s1 = zero, p0 = zero, p1 = zero;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
@@ -467,19 +493,28 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_kv_kernel(PrefillBwdArgs ba, 
     dv[bb] = zero;
   }
   float(&st)[4][32] = sm.st[w];
+  const int last_ei = rows > 0 ? (rows - 1) / G : 0;
   for (int tile = stream; keys && tile < ntiles; tile += 2) {
     const int r = tile * 32 + i32;
     int ei, hh;
     split_row(r, G, a.log2G, ei, hh);
-    const int32_t entry = r < rows ? list[ei] : -1;
+    // unguarded loads (past the unit: clamped, then dropped)
+    const int32_t e_raw = list[min(ei, last_ei)];
+    const int32_t entry = r < rows ? e_raw : -1;
     u32x4 q[D / 16], o[D / 16];
-    load_row_pair<D>(ba, qbase, qplane, entry, hh, hf, q, o);
+    load_row_pair_nb<D>(ba, qbase, qplane, entry, hh, hf, q, o);
+    if (entry < 0) {
+#pragma unroll
+      for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = o[s2] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (hf == 0) {
       const bool ok = entry >= 0;
-      st[0][i32] = ok ? ba.lse2[row0 + r] : INFINITY;
-      st[1][i32] = ok ? ba.dw[row0 + r] : 0.f;
-      st[2][i32] = ok ? ba.wk[row0 + r] : 0.f;
-      st[3][i32] = ok ? ba.ds[row0 + r] : 0.f;
+      const int64_t rr = row0 + min(r, rows - 1);
+      const float v0 = ba.lse2[rr], v1 = ba.dw[rr], v2 = ba.wk[rr], v3 = ba.ds[rr];
+      st[0][i32] = ok ? v0 : INFINITY;
+      st[1][i32] = ok ? v1 : 0.f;
+      st[2][i32] = ok ? v2 : 0.f;
+      st[3][i32] = ok ? v3 : 0.f;
     }
     f32x16 sa = zero, pa = zero;
 #pragma unroll
