@@ -617,24 +617,27 @@ __global__ void __launch_bounds__(kThreads, 2)
       hh = r - ei * G;
     }
   };
-  auto entry_of = [&](int tile) -> int32_t {
-    const int r = tile * 32 + i32;
+  // Loads are issued unconditionally (indices clamped in bounds, values
+  // dropped afterwards): a load under a per-lane guard makes the compiler
+  // count outstanding loads for the path without it, so the next wait would
+  // also cover the prefetch it was meant to overlap.
+  // A tile's row exists when row_ok; entry_raw and load_q read clamped,
+  // always-valid indices for the others (values unused), also for tiles
+  // past the last, so no load is issued conditionally.
+  const int last_e = max(cnt - 1, 0);
+  auto row_ok = [&](int tile) { return tile * 32 + i32 < rows; };
+  auto entry_raw = [&](int tile) -> int32_t {
     int ei, hh;
-    split_row(r, ei, hh);
-    return r < rows ? list[ei] : -1;
+    split_row(tile * 32 + i32, ei, hh);
+    return list[min(ei, last_e)];
   };
   auto load_q = [&](int tile, int32_t entry, u32x4 (&q)[D / 16]) {
-    if (entry >= 0) {
-      int ei, hh;
-      split_row(tile * 32 + i32, ei, hh);
-      const int64_t t = entry >> kSlotBits;
-      const uint16_t* qrow = Q + qbase + (int64_t)hh * qplane + t * D + 8 * hf;
+    int ei, hh;
+    split_row(tile * 32 + i32, ei, hh);
+    const int64_t t = row_ok(tile) ? (int64_t)(entry >> kSlotBits) : 0;
+    const uint16_t* qrow = Q + qbase + (int64_t)hh * qplane + t * D + 8 * hf;
 #pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = *(const u32x4*)(qrow + 16 * s2);
-    } else {
-#pragma unroll
-      for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = *(const u32x4*)(qrow + 16 * s2);
   };
 
   const bool two = a.S > 32;
@@ -774,19 +777,22 @@ __global__ void __launch_bounds__(kThreads, 2)
 
   // Double-buffered Q: the next tile's rows load during the whole current
   // tile.  List entries run one tile further ahead.
+  // Every load is unconditional: a load issued on one path only makes the
+  // compiler count outstanding loads for the other path, and the next wait
+  // would then cover the prefetch too.
   u32x4 qa[D / 16], qb[D / 16];
   int tile = w;
-  int32_t ea = tile < ntiles ? entry_of(tile) : -1;
-  int32_t eb = tile + 4 < ntiles ? entry_of(tile + 4) : -1;
+  int32_t ea = entry_raw(tile);
+  int32_t eb = entry_raw(tile + 4);
   load_q(tile, ea, qa);
   for (; tile < ntiles; tile += 8) {
-    int32_t ec = tile + 8 < ntiles ? entry_of(tile + 8) : -1;
-    if (tile + 4 < ntiles) load_q(tile + 4, eb, qb);
-    compute_tile(tile, ea, qa);
+    const int32_t ec = entry_raw(tile + 8);
+    load_q(tile + 4, eb, qb);
+    compute_tile(tile, row_ok(tile) ? ea : -1, qa);
     if (tile + 4 >= ntiles) break;
-    int32_t ed = tile + 12 < ntiles ? entry_of(tile + 12) : -1;
-    if (tile + 8 < ntiles) load_q(tile + 8, ec, qa);
-    compute_tile(tile + 4, eb, qb);
+    const int32_t ed = entry_raw(tile + 12);
+    load_q(tile + 8, ec, qa);
+    compute_tile(tile + 4, row_ok(tile + 4) ? eb : -1, qb);
     ea = ec;
     eb = ed;
   }
