@@ -65,6 +65,10 @@ SWEEP = [
     (1, 2, 128, "bf16", 200, 700, 9, 300, 1500),  # chunks longer than 256 keys
     (2, 2, 64, "bf16", 5, 9, 0, 6, 4),          # no complete chunk yet
     (1, 1, 128, "bf16", 5, 9, 0, 1, 1),         # the very first token
+    # the chunk ranking counts larger keys up to 1024 chunks (+ the current
+    # one) and sorts bitonically beyond: both sides of the switch
+    (1, 2, 64, "bf16", 1, 1, 1023, 1, 700),
+    (1, 2, 64, "bf16", 1, 1, 1500, 1, 700),
 ]
 
 
