@@ -990,9 +990,16 @@ hipError_t prefill_select(const PrefillArgs& a, hipStream_t stream) {
 hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
   const int64_t BG = (int64_t)a.B * a.Hkv;
-  hipError_t e = launch_fill_i32(a.counts, BG * a.n, 0, stream);
-  if (e != hipSuccess) return e;
-  if ((e = launch_fill_i32(a.cursor, BG * a.n, 0, stream)) != hipSuccess) return e;
+  // the workspace places cursor right after counts (alignment padding
+  // between): one fill clears both, one launch fewer
+  hipError_t e;
+  const int64_t span = (int64_t)(a.cursor - a.counts) + BG * a.n;
+  if (a.cursor > a.counts && a.cursor - a.counts <= BG * a.n + 64) {
+    if ((e = launch_fill_i32(a.counts, span, 0, stream)) != hipSuccess) return e;
+  } else {
+    if ((e = launch_fill_i32(a.counts, BG * a.n, 0, stream)) != hipSuccess) return e;
+    if ((e = launch_fill_i32(a.cursor, BG * a.n, 0, stream)) != hipSuccess) return e;
+  }
   const int64_t bpb = (a.L + kInvertTokens - 1) / kInvertTokens;
   const int use_lds = a.n <= kInvertLdsBins;
   const size_t lds1 = use_lds ? (size_t)a.n * sizeof(int32_t) : 0;
