@@ -205,28 +205,46 @@ __device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>
 
 // ---------------------------------------------------------------------
 // Variable-length key blocks of up to 128 keys (DHSA: one chunk per block).
+//
+// V layout of these blocks: 16-byte units of 8 keys per value column, one
+// unit per A operand of O^T = V^T P^T.  Lane half h of k-step s' of 32-key
+// sub-tile u takes keys 32u + 16s' + 4h + 0..3 and the same + 8, so unit
+// "oct" o = 4u + 2s' + h holds keys 16(o/2) + 4(o%2) + {0..3, 8..11}, and
+// the operand is one 16-byte LDS read (two 8-byte reads would have to be
+// re-paired in registers).  Columns are swizzled by vcol_wide.
 
 constexpr int kWideBlock = 128;
 
 template <int D>
 struct KVSmemWide {
   uint16_t k[kWideBlock * (D + 8)];
-  uint16_t v[(kWideBlock / 4) * D * 4];
+  uint16_t v[(kWideBlock / 8) * D * 8];  // [oct][column (swizzled)][8 keys]
 };
+
+// Unit position of value column dd in an oct row: bits 0..1 are XORed with
+// bits 3..4.  A staging store has lane c writing columns 4c..4c+3, so every
+// 8 lanes of a 16-byte store land on distinct banks; a read of 32
+// consecutive columns is 8-unit runs permuted in place (also conflict-free),
+// and since only bits below 5 enter, column 32b + i keeps the lane's
+// offset for every b.
+__device__ __forceinline__ int vcol_wide(int dd) { return dd ^ ((dd >> 3) & 3); }
 
 // One thread's share of a 128-key block held in registers between its
 // global load and its LDS store, so the next block's loads can be in flight
 // while the current block is computed.  256 threads; K as 16-byte row
-// pieces, V as 8-byte pieces of four consecutive keys.
+// pieces, V as 8-byte pieces (four columns) of the eight keys of an oct.
 template <int D>
 struct KVRegsWide {
   static constexpr int KPR = D / 8;  // 16-byte pieces per key row
   static constexpr int VPR = D / 4;  // 8-byte pieces per value row
   static constexpr int NK = kWideBlock * KPR / 256;
-  static constexpr int NV = (kWideBlock / 4) * VPR / 256;
+  static constexpr int NO = (kWideBlock / 8) * VPR / 256;  // octs per thread
   u32x4 k[NK];
-  u32x2 v[NV][4];
+  u32x2 v[NO][8];
 };
+
+// In-oct key of slot kk (0..7): the oct's first quad, then the quad 8 keys on.
+__device__ __forceinline__ constexpr int oct_key(int kk) { return (kk & 3) + 8 * (kk >> 2); }
 
 // Raw buffer resource over [base, base + bytes): buffer loads at offsets
 // past the range return zero instead of touching memory.  Word 3 holds the
@@ -238,7 +256,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void* base,
 // Loads of rows [0, nk) (nk <= 128) of a key/value block into registers;
 // rows past nk read as zero (buffer range check, no branches).  Called by
 // all 256 threads of the block: thread tid takes K piece tid % KPR of rows
-// tid / KPR + i * (256 / KPR), and V piece tid % VPR of key quads
+// tid / KPR + i * (256 / KPR), and V piece tid % VPR of the keys of octs
 // tid / VPR + i * (256 / VPR).
 template <int D>
 __device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* __restrict__ Kg,
@@ -252,19 +270,22 @@ __device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* 
   for (int i = 0; i < R::NK; ++i)
     r.k[i] = __builtin_bit_cast(
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff, i * (256 / R::KPR) * D * 2, 0));
-  const int voff = ((tid / R::VPR) * 4 * D + (tid % R::VPR) * 4) * 2;
+  // oct o starts at key 16 (o / 2) + 4 (o % 2); octs o0 + i (256 / VPR)
+  // (an even step) start 8 i (256 / VPR) keys further on
+  const int o0 = tid / R::VPR;
+  const int voff = ((16 * (o0 >> 1) + 4 * (o0 & 1)) * D + (tid % R::VPR) * 4) * 2;
 #pragma unroll
-  for (int i = 0; i < R::NV; ++i)
+  for (int i = 0; i < R::NO; ++i)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 8; ++kk)
       r.v[i][kk] = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                     vr, voff, (i * (256 / R::VPR) * 4 + kk) * D * 2, 0));
+                     vr, voff, (i * (256 / R::VPR) * 8 + oct_key(kk)) * D * 2, 0));
 }
 
 // LDS store of a fetched block: rows up to the next multiple of 32 above nk
 // (zeros past nk) are written, rows beyond that are never read.  V goes to
-// the [key/4][dim][4 keys] layout.
+// the [oct][column][8 keys] layout, one 16-byte unit per column.
 template <int D>
 __device__ __forceinline__ void store_kv_wide(KVSmemWide<D>& sm, const KVRegsWide<D>& r,
                                               int nk) {
@@ -276,23 +297,22 @@ __device__ __forceinline__ void store_kv_wide(KVSmemWide<D>& sm, const KVRegsWid
 #pragma unroll
   for (int i = 0; i < R::NK; ++i)
     if (krow + i * (256 / R::KPR) < rows) *(u32x4*)(ks + i * (256 / R::KPR) * (D + 8)) = r.k[i];
-  const int vgrp = tid / R::VPR;
-  uint16_t* vs = &sm.v[(vgrp * D + (tid % R::VPR) * 4) * 4];
+  const int o0 = tid / R::VPR, cq = tid % R::VPR;
 #pragma unroll
-  for (int i = 0; i < R::NV; ++i) {
-    if ((vgrp + i * (256 / R::VPR)) * 4 >= rows) continue;
+  for (int i = 0; i < R::NO; ++i) {
+    const int o = o0 + i * (256 / R::VPR);
+    if (16 * (o >> 1) >= rows) continue;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
+      // column 4 cq + x: keys (slot order) as bf16 pairs
       const int w = x >> 1;
-      uint32_t lo, hi;
-      if ((x & 1) == 0) {
-        lo = (r.v[i][0][w] & 0xffffu) | (r.v[i][1][w] << 16);
-        hi = (r.v[i][2][w] & 0xffffu) | (r.v[i][3][w] << 16);
-      } else {
-        lo = (r.v[i][0][w] >> 16) | (r.v[i][1][w] & 0xffff0000u);
-        hi = (r.v[i][2][w] >> 16) | (r.v[i][3][w] & 0xffff0000u);
+      uint32_t p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = r.v[i][2 * j][w], b = r.v[i][2 * j + 1][w];
+        p[j] = (x & 1) == 0 ? (a & 0xffffu) | (b << 16) : (a >> 16) | (b & 0xffff0000u);
       }
-      *(u32x2*)(vs + (i * (256 / R::VPR) * D + x) * 4) = u32x2{lo, hi};
+      *(u32x4*)(&sm.v[(o * D + vcol_wide(4 * cq + x)) * 8]) = u32x4{p[0], p[1], p[2], p[3]};
     }
   }
 }
@@ -382,21 +402,18 @@ __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide
     st.l += ps;
     st.m = m_new;
     __builtin_amdgcn_sched_barrier(0);
+    const int vc = vcol_wide(i32);  // = vcol_wide(32 b + i32) - 32 b for every b
 #pragma unroll
     for (int t = 0; t < SUB; ++t) {
       if (t >= nsub) break;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const bf16x8 pb = cvt_bf16x8(sc[t], 8 * s2);
-        const int g0 = 8 * (t0 + t) + 4 * s2 + h, g1 = g0 + 2;
+        const int o = 4 * (t0 + t) + 2 * s2 + h;
 #pragma unroll
         for (int b = 0; b < D / 32; ++b) {
-          const int dd = 32 * b + i32;
-          const u32x2 v0 = *(const u32x2*)(&sm.v[(g0 * D + dd) * 4]);
-          const u32x2 v1 = *(const u32x2*)(&sm.v[(g1 * D + dd) * 4]);
-          const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
-          st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
-                                                            st.o[b], 0, 0, 0);
+          const bf16x8 av = *(const bf16x8*)(&sm.v[(o * D + 32 * b + vc) * 8]);
+          st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, st.o[b], 0, 0, 0);
         }
       }
     }

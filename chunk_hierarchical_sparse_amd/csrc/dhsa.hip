@@ -164,10 +164,10 @@ struct Cut {
   int rem;
 };
 
-__device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int64_t i) {
+__device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int i) {
   const int bl = a.offs[l], ll = a.offs[l + 1] - bl;
-  const int64_t B = min(a.budget, i + 1);
-  const int tail = ll - (int)(i - bl + 1);  // tokens of chunk l after i
+  const int B = (int)min(a.budget, (int64_t)i + 1);
+  const int tail = ll - (i - bl + 1);  // tokens of chunk l after i
   const int dp = a.diag_pos[bh * a.nc + l];
   const int32_t* cum = a.cumlen + (bh * a.nc + l) * (a.nc + 1);
   // E(p) = cum[p] - (p > dp ? tail : 0) is non-decreasing; find the largest
@@ -175,7 +175,7 @@ __device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int
   int lo = 0, hi = l + 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    const int64_t e = cum[mid] - (mid > dp ? tail : 0);
+    const int e = cum[mid] - (mid > dp ? tail : 0);
     if (e <= B)
       lo = mid;
     else
@@ -202,7 +202,7 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   const int row0 = bl + tile * kRowsPerTile;
   if (row0 >= bl1) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t i = row0 + w * 32 + (lane & 31);
+  const int i = row0 + w * 32 + (lane & 31);  // L < 2^31 is checked on the host
   const bool valid = i < bl1;
   Cut cut = {0, 0};
   if (valid) cut = row_cut(a, bh, l, i);
@@ -216,7 +216,7 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   const uint16_t* Kb = (const uint16_t*)a.K + bh * a.L * D;
   const uint16_t* Vb = (const uint16_t*)a.V + bh * a.L * D;
   WaveAttn<D> st;
-  wave_attn_init<D>(st, Qb + min(i, a.L - 1) * D, valid);
+  wave_attn_init<D>(st, Qb + (int64_t)min(i, (int)a.L - 1) * D, valid);
   const bool wave_any = __ballot(valid) != 0;
   const int32_t* order = a.order + (bh * a.nc + l) * a.nc;
   // Key blocks in rank order: chunk order[p], keys [kb, kb + 128).  Each
@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
       fetch_kv_wide<D>(rg, Kb + (int64_t)(nbk + nkb) * D, Vb + (int64_t)(nbk + nkb) * D,
                        min(kWideBlock, nlk - nkb));
     __builtin_amdgcn_sched_barrier(0);
-    const int len_eff = k == l ? (int)(i - bl + 1) : lk;
+    const int len_eff = k == l ? i - bl + 1 : lk;
     const int hi = !valid ? 0 : (p < cut.pw ? len_eff : (p == cut.pw ? cut.rem : 0));
     const int nv = max(0, min(hi - kb, nk));
     if (wave_any && __ballot(nv > 0) != 0) wave_attn_wide<D, kDhsaSub>(st, sm, nk, nv, scale_log2);
@@ -290,7 +290,7 @@ __global__ void mask_kernel(DhsaArgs a) {
       if (a.offs[mid] <= i) lo = mid; else hi = mid - 1;
     }
     const int l = lo;
-    const Cut cut = row_cut(a, bh, l, i);
+    const Cut cut = row_cut(a, bh, l, (int)i);
     const int32_t* order = a.order + (bh * a.nc + l) * a.nc;
     uint32_t bits = 0;
     // rank position of a chunk: scan the (short) kept prefix of the order

@@ -52,29 +52,38 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(SwaArgs a, fl
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = g * G + hb * GT + w % GT;
-  const int64_t t = t0 + (w / GT) * 32 + (lane & 31);
-  const bool valid = t < a.L;
+  // positions in 32 bits (B * Hq * L < 2^31 is checked on the host); a
+  // window reaching past the sequence start is the whole prefix
+  const int Li = (int)a.L, W = (int)min(a.window, a.L);
+  const int tb = (int)t0;
+  const int t = tb + (w / GT) * 32 + (lane & 31);
+  const bool valid = t < Li;
   const uint16_t* Kb = (const uint16_t*)a.K + bg * a.L * D;
   const uint16_t* Vb = (const uint16_t*)a.V + bg * a.L * D;
   WaveAttn<D> st;
-  wave_attn_init<D>(st, (const uint16_t*)a.Q + (((int64_t)b * a.Hq + h) * a.L + min(t, a.L - 1)) * D,
+  wave_attn_init<D>(st, (const uint16_t*)a.Q + (((int64_t)b * a.Hq + h) * a.L + min(t, Li - 1)) * D,
                     valid);
-  const int64_t t_end = min(a.L, t0 + MQ);
-  const int64_t k_lo = max((int64_t)0, t0 - a.window + 1);
+  const int t_end = min(Li, tb + MQ);
+  const int k_lo = max(0, tb - W + 1);
   KVRegsWide<D> rg;
-  fetch_kv_wide<D>(rg, Kb + k_lo * D, Vb + k_lo * D, (int)min((int64_t)kWideBlock, t_end - k_lo));
-  for (int64_t kb = k_lo; kb < t_end; kb += kWideBlock) {
-    const int nk = (int)min((int64_t)kWideBlock, t_end - kb);
+  fetch_kv_wide<D>(rg, Kb + (int64_t)k_lo * D, Vb + (int64_t)k_lo * D,
+                   min(kWideBlock, t_end - k_lo));
+  for (int kb = k_lo; kb < t_end; kb += kWideBlock) {
+    const int nk = min(kWideBlock, t_end - kb);
     __syncthreads();
     store_kv_wide<D>(sm, rg, nk);
     __syncthreads();
-    const int64_t nkb = kb + kWideBlock;
+    const int nkb = kb + kWideBlock;
     if (nkb < t_end)
-      fetch_kv_wide<D>(rg, Kb + nkb * D, Vb + nkb * D, (int)min((int64_t)kWideBlock, t_end - nkb));
+      fetch_kv_wide<D>(rg, Kb + (int64_t)nkb * D, Vb + (int64_t)nkb * D,
+                       min(kWideBlock, t_end - nkb));
     __builtin_amdgcn_sched_barrier(0);
-    // this lane's keys in the block: [lo, hi) in-block indices
-    const int hi = valid ? (int)min((int64_t)nk, t - kb + 1) : 0;
-    const int lo = (int)max((int64_t)-1, min((int64_t)kWideBlock + 1, t - a.window + 1 - kb));
+    // this lane's keys in the block: [lo, hi) in-block indices.  t - kb lies
+    // in (-128, 2^31); lo = t - kb - (W - 1) clamped to [-1, 129], the
+    // difference taken unsigned so the branch not chosen cannot overflow
+    const int dk = t - kb;
+    const int hi = valid ? min(nk, dk + 1) : 0;
+    const int lo = dk >= W - 1 ? min(kWideBlock + 1, (int)((unsigned)dk - (unsigned)(W - 1))) : -1;
     if (__ballot(hi > 0 && hi > lo) != 0)
       wave_attn_wide<D, 4, true>(st, sm, nk, max(hi, 0), scale_log2, lo);
   }
