@@ -37,9 +37,9 @@ METRIC = "HSA queries/sec + achieved HBM GB/s (decode) / MFMA util (prefill), 1 
 # sources hash the same as when the counters were taken.
 CSRC = os.path.join(ROOT, "chunk_hierarchical_sparse_amd", "csrc")
 DOMINANT = {
-    "hsa_prefill": ("attend_chunk_bf16_kernel<128>", "PrefillArgs",
+    "hsa_prefill": ("attend_chunk_bf16_kernel<128, true>", "PrefillArgs",
                     ["prefill.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
-    "hsa_prefill_r8": ("attend_chunk_bf16_kernel<128>", "PrefillArgs",
+    "hsa_prefill_r8": ("attend_chunk_bf16_kernel<128, true>", "PrefillArgs",
                        ["prefill.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
     "hsa_decode": ("scan_kernel<128, 1>", "DecodeArgs",
                    ["decode.hip", "hsa_common.h", "kernels.h"]),

@@ -569,12 +569,14 @@ __global__ void __launch_bounds__(kThreads) attend_bf16_kernel(PrefillArgs a, fl
 // split into three bf16 rows (hi + lo + lo2 == the fp32 value) that act as
 // extra "keys", so q (exact in bf16) meets an exact landmark and s_h keeps
 // fp32 accuracy.  Q rows are double-buffered: a tile's rows load during the
-// whole previous tile.
-template <int D>
+// whole previous tile.  S64: chunks of exactly 64 keys (both key halves, no
+// masking), fixed at compile time.
+template <int D, bool S64>
 __global__ void __launch_bounds__(kThreads, 2)
     attend_chunk_bf16_kernel(PrefillArgs a, float scale_log2, float score_scale) {
   __shared__ KVSmem<D> sm;
-  __shared__ __attribute__((aligned(16))) uint16_t lsplit[3][D];
+  // the landmark's three bf16 parts, then a zero row that lanes 3..31 read
+  __shared__ __attribute__((aligned(16))) uint16_t lsplit[4][D];
   // each wave's tile of partial rows, rows padded by 16 bytes (conflict-free)
   __shared__ __attribute__((aligned(16))) uint16_t ostage[kThreads / kWave][32 * (D + 8)];
   int64_t bg;
@@ -596,6 +598,7 @@ __global__ void __launch_bounds__(kThreads, 2)
     lsplit[0][x] = __builtin_bit_cast(uint16_t, h);
     lsplit[1][x] = __builtin_bit_cast(uint16_t, l);
     lsplit[2][x] = __builtin_bit_cast(uint16_t, m);
+    lsplit[3][x] = 0;
   }
   __syncthreads();
 
@@ -640,8 +643,8 @@ __global__ void __launch_bounds__(kThreads, 2)
     for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = *(const u32x4*)(qrow + 16 * s2);
   };
 
-  const bool two = a.S > 32;
-  const bool full = a.S == kKeyBlock;  // no key masking needed
+  const bool two = S64 || a.S > 32;
+  const bool full = S64 || a.S == kKeyBlock;  // no key masking needed
   auto compute_tile = [&](int tile, int32_t ent_cur, const u32x4 (&q)[D / 16]) {
     // S^T = K Q^T (keys 0..63) and L^T = LMK3 Q^T (rows 0..2: landmark parts)
     // the first k-step takes a zero accumulator operand: no register fill
@@ -658,10 +661,8 @@ __global__ void __launch_bounds__(kThreads, 2)
       } else if (s2 == 0) {
         s1 = zero;
       }
-      u32x4 la = {0u, 0u, 0u, 0u};
-      if (i32 < 3) la = *(const u32x4*)(&lsplit[i32][16 * s2 + 8 * hf]);
-      sl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, la), qb,
-                                                   s2 == 0 ? zero : sl, 0, 0, 0);
+      const bf16x8 la = *(const bf16x8*)(&lsplit[min(i32, 3)][16 * s2 + 8 * hf]);
+      sl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la, qb, s2 == 0 ? zero : sl, 0, 0, 0);
     }
     // rows 0..2 of L^T sit in registers 0..2 of the lanes of half 0
     const float sh = (sl[2] + sl[1]) + sl[0];
@@ -1025,12 +1026,18 @@ hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream) {
                                                                               score_scale);
   } else if (a.S <= kKeyBlock) {
     const float sl2 = scale * 1.4426950408889634f;
-    if (a.d == 64)
-      attend_chunk_bf16_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(
-          a, sl2, score_scale);
-    else
-      attend_chunk_bf16_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(
-          a, sl2, score_scale);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (a.d == 64) {
+      if (a.S == kKeyBlock)
+        attend_chunk_bf16_kernel<64, true><<<grid, block, 0, stream>>>(a, sl2, score_scale);
+      else
+        attend_chunk_bf16_kernel<64, false><<<grid, block, 0, stream>>>(a, sl2, score_scale);
+    } else {
+      if (a.S == kKeyBlock)
+        attend_chunk_bf16_kernel<128, true><<<grid, block, 0, stream>>>(a, sl2, score_scale);
+      else
+        attend_chunk_bf16_kernel<128, false><<<grid, block, 0, stream>>>(a, sl2, score_scale);
+    }
   } else {
     const float sl2 = scale * 1.4426950408889634f;
     if (a.d == 64)
