@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kThreads = 256;
 // 32-key sub-tiles per online-softmax update in the attention (see
-// wave_attn_wide): two keep the scores and the prefetched block in registers.
+// wave_attn_wide): four, one update per key block of up to 128 keys.
 constexpr int kDhsaSub = 4;
 constexpr int kRowsPerTile = 128;
 constexpr int kMaxSort = 4096;  // 32 KiB of 64-bit sort keys in LDS

@@ -52,6 +52,8 @@ struct PrefillArgs {
 };
 // A selection entry of the per-chunk lists: token << kSlotBits | slot.
 constexpr int kSlotBits = 5;  // topk <= 32
+// prefill_select also clears counts and cursor; prefill_invert relies on
+// that, so it runs right after prefill_select on the same stream.
 hipError_t prefill_select(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream);

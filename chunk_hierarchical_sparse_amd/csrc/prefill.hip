@@ -32,6 +32,18 @@ constexpr int kChunkUnitRows = 1024;
 
 // ---------------------------------------------------------------- select --
 
+// The invert's per-chunk counters (counts, cursor) must start at zero.  The
+// select launch, which always runs right before the invert, clears them on
+// the way: one launch fewer than a separate fill.
+__device__ __forceinline__ void clear_invert_counters(const PrefillArgs& a) {
+  const int64_t m = (int64_t)a.B * a.Hkv * a.n;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < m; i += step) {
+    a.counts[i] = 0;
+    a.cursor[i] = 0;
+  }
+}
+
 // Keep a descending top-KM list in registers.  Candidates of one lane
 // arrive in increasing index order, so a strict '>' places a later
 // equal-score candidate after the earlier one (lower index first).  The
@@ -83,6 +95,7 @@ __device__ __forceinline__ void topk_insert_any(float (&ls)[KM], int (&li)[KM], 
 // positive factor 1/sqrt(d) does not change the order.
 template <int D, int KM, int DT>
 __global__ void __launch_bounds__(kThreads) select_valu_kernel(PrefillArgs a, int64_t nqt) {
+  clear_invert_counters(a);
   constexpr int TILE = 32;
   constexpr int LT_BYTES = TILE * D * 4;
   constexpr int MERGE_BYTES = 3 * 64 * KM * 8;
@@ -186,6 +199,7 @@ __device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& lo,
 
 template <int D, int KM>
 __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a, int64_t nqt) {
+  clear_invert_counters(a);
   constexpr int QPB = 128;  // selection rows per block: 4 waves x 32
   constexpr int TILE = 32;
   constexpr int RS = D + 8;  // padded LDS row (bf16 elements)
@@ -991,16 +1005,8 @@ hipError_t prefill_select(const PrefillArgs& a, hipStream_t stream) {
 hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
   const int64_t BG = (int64_t)a.B * a.Hkv;
-  // the workspace places cursor right after counts (alignment padding
-  // between): one fill clears both, one launch fewer
+  // counts and cursor were cleared by the select launch
   hipError_t e;
-  const int64_t span = (int64_t)(a.cursor - a.counts) + BG * a.n;
-  if (a.cursor > a.counts && a.cursor - a.counts <= BG * a.n + 64) {
-    if ((e = launch_fill_i32(a.counts, span, 0, stream)) != hipSuccess) return e;
-  } else {
-    if ((e = launch_fill_i32(a.counts, BG * a.n, 0, stream)) != hipSuccess) return e;
-    if ((e = launch_fill_i32(a.cursor, BG * a.n, 0, stream)) != hipSuccess) return e;
-  }
   const int64_t bpb = (a.L + kInvertTokens - 1) / kInvertTokens;
   const int use_lds = a.n <= kInvertLdsBins;
   const size_t lds1 = use_lds ? (size_t)a.n * sizeof(int32_t) : 0;
