@@ -101,7 +101,7 @@ hsa_status_t check_prefill(int B, int64_t L, int Hq, int Hkv, int d, int S, int 
 struct PrefillLayout {
   float* lmk;
   int32_t* idx;
-  int32_t *counts, *cursor, *offs, *tile_off, *tile_chunk, *list, *entry_pos;
+  int32_t *counts, *cursor, *blockbase, *offs, *tile_off, *tile_chunk, *list, *entry_pos;
   int entries_per_tile;
   int64_t tiles_ub;
   void* partial;
@@ -123,6 +123,8 @@ PrefillLayout prefill_layout(void* ws, int B, int64_t L, int Hq, int Hkv, int d,
   p.idx = cv.take<int32_t>((size_t)(BG * nq * topk));
   p.counts = cv.take<int32_t>((size_t)(BG * n));
   p.cursor = cv.take<int32_t>((size_t)(BG * n));
+  const int64_t inv_blocks = (L + hsa::kInvertTokens - 1) / hsa::kInvertTokens;
+  p.blockbase = cv.take<int32_t>(n <= hsa::kInvertDetBins ? (size_t)(BG * inv_blocks * n) : 1);
   p.offs = cv.take<int32_t>((size_t)(BG * (n + 1)));
   p.tile_off = cv.take<int32_t>((size_t)(BG * (n + 1)));
   p.entries_per_tile = entries_per_unit > 0
@@ -324,6 +326,8 @@ hsa::PrefillArgs prefill_args(const PrefillLayout& lay, const void* Q, const voi
   a.sel_w = sel_w;
   a.counts = lay.counts;
   a.cursor = lay.cursor;
+  a.blockbase = lay.blockbase;
+  a.ordered = 0;
   a.offs = lay.offs;
   a.tile_off = lay.tile_off;
   a.tile_chunk = lay.tile_chunk;
@@ -435,6 +439,7 @@ hsa_status_t hsa_prefill_backward(const void* Q, const void* K, const void* V, c
                       topk, 1, dtype);
   if ((int64_t)B * Hkv * ba.p.tiles_ub >= ((int64_t)1 << 31))
     return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
+  ba.p.ordered = 1;  // dK and dV sum over each chunk's list: keep it in token order
   ba.dO = dO;
   ba.lse2 = lay.lse2;
   ba.dw = lay.dw;

@@ -35,6 +35,8 @@ struct PrefillArgs {
   float* sel_w;       // [B,Hq,L,topk] or null
   int32_t* counts;    // [B*Hkv, n]
   int32_t* cursor;    // [B*Hkv, n]
+  int32_t* blockbase; // [B*Hkv, ceil(L/kInvertTokens), n] when n <= kInvertDetBins: each
+                      // counting block's per-chunk counts (ordered lists only)
   int32_t* offs;      // [B*Hkv, n+1]
   int32_t* tile_off;  // [B*Hkv, n+1]
   int32_t* tile_chunk;  // [B*Hkv, tiles_ub]: chunk of each attention work unit
@@ -49,9 +51,18 @@ struct PrefillArgs {
   int log2G;             // log2(Hq/Hkv) when it is a power of two, else -1
   int interval;          // retrieval interval R: token t uses selection row t / R
   int64_t nq;            // selection rows, ceil(L / R)
+  int ordered;           // build each chunk's list in token order (when n <= kInvertDetBins)
 };
 // A selection entry of the per-chunk lists: token << kSlotBits | slot.
 constexpr int kSlotBits = 5;  // topk <= 32
+// The per-chunk lists are built over blocks of kInvertTokens tokens.  The
+// order inside a list follows atomic arrival, which no forward result
+// depends on (every row is computed on its own).  With `ordered` set (the
+// backward, whose dK and dV sum over a chunk's list) and up to
+// kInvertDetBins chunks, the lists are in token order instead, so those
+// sums run in a fixed order.
+constexpr int kInvertTokens = 1024;
+constexpr int kInvertDetBins = 4096;
 // prefill_select also clears counts and cursor; prefill_invert relies on
 // that, so it runs right after prefill_select on the same stream.
 hipError_t prefill_select(const PrefillArgs& a, hipStream_t stream);

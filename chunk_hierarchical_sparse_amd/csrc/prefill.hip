@@ -404,8 +404,6 @@ __global__ void __launch_bounds__(1024) scan_kernel(PrefillArgs a) {
   }
 }
 
-constexpr int kInvertTokens = 1024;  // tokens per counting / scatter block
-
 // Selection slot of (token, slot) i = token * topk + slot: the row of the
 // token's block start (token / interval) in the selection buffer.
 __device__ __forceinline__ int64_t sel_of(const PrefillArgs& a, int64_t i) {
@@ -430,7 +428,8 @@ constexpr int kInvertLdsBins = 8192;  // chunks whose counters fit in LDS (2 arr
 // Per-chunk selection counts.  Each block histograms the selections of
 // kInvertTokens tokens in LDS and adds one global atomic per touched chunk,
 // so hot chunks see a few hundred global atomics instead of one per
-// selection.
+// selection (integer sums: the totals do not depend on the order).  For
+// ordered lists it also keeps the histogram as its row of blockbase.
 __global__ void __launch_bounds__(256) count_kernel(PrefillArgs a, int64_t blocks_per_bg,
                                                     int use_lds) {
   extern __shared__ int32_t hist[];  // [n]
@@ -458,8 +457,96 @@ __global__ void __launch_bounds__(256) count_kernel(PrefillArgs a, int64_t block
   }
   if (!use_lds) return;
   __syncthreads();
+  if (a.ordered && a.n <= kInvertDetBins) {
+    int32_t* row = a.blockbase + blockIdx.x * a.n;  // blocks of one (b, group) are consecutive
+    for (int c = threadIdx.x; c < a.n; c += 256) row[c] = hist[c];
+  }
   for (int c = threadIdx.x; c < a.n; c += 256)
     if (hist[c] != 0) atomicAdd(&cnt[c], hist[c]);
+}
+
+// Lists in token order (ordered lists, up to kInvertDetBins chunks).  A
+// block's first position in chunk c's list is offs[c] plus the counts of
+// the (b, group)'s earlier blocks (their blockbase rows).  Its tokens then
+// go in rounds of 64: every selection sets its token's bit in its chunk's
+// 64-bit round mask, and its list position is the block's running position
+// for the chunk plus the number of earlier tokens in the mask.  The first
+// token of each chunk in the round then advances the running position and
+// clears the mask.  A token selects a chunk at most once.
+__global__ void __launch_bounds__(256) scatter_ordered_kernel(PrefillArgs a,
+                                                              int64_t blocks_per_bg) {
+  extern __shared__ int32_t sh[];  // running position [n], then round masks [n][2]
+  constexpr int kRound = 64;
+  const int64_t bg = blockIdx.x / blocks_per_bg;
+  const int64_t t0 = (blockIdx.x % blocks_per_bg) * kInvertTokens;
+  const int64_t t1 = min(t0 + kInvertTokens, a.L);
+  const int32_t* idx = a.idx + bg * a.nq * a.topk;
+  const int32_t* rows0 = a.blockbase + bg * blocks_per_bg * a.n;  // this (b, group)'s rows
+  const int nprev = (int)(blockIdx.x % blocks_per_bg);
+  const int32_t* offs = a.offs + bg * (a.n + 1);
+  int32_t* list = a.list + bg * a.L * a.topk;
+  int32_t* epos = a.entry_pos + bg * a.L * a.topk;
+  int32_t* run = sh;
+  uint32_t* mask = (uint32_t*)(sh + a.n);
+  for (int c = threadIdx.x; c < a.n; c += 256) {
+    // four rows in flight at a time (rows past nprev read row 0, add 0)
+    int32_t acc = offs[c];
+    for (int k = 0; k < nprev; k += 4) {
+      int32_t h[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = rows0[(int64_t)(k + j < nprev ? k + j : 0) * a.n + c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc += k + j < nprev ? h[j] : 0;
+    }
+    run[c] = acc;
+    mask[2 * c] = 0u;
+    mask[2 * c + 1] = 0u;
+  }
+  __syncthreads();
+  const int K = a.topk;
+  // the next round's selections load while the current round is placed
+  int32_t cn[8];
+  load_sel8(a, idx, t0 * K + threadIdx.x, min(t0 + kRound, t1) * K, cn);
+  for (int64_t r0 = t0; r0 < t1; r0 += kRound) {
+    const int64_t e0 = r0 * K;  // this round's entries: e0 + threadIdx.x + 256 u
+    int32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = cn[u];
+    const int64_t r1 = r0 + kRound;
+    if (r1 < t1) load_sel8(a, idx, r1 * K + threadIdx.x, min(r1 + kRound, t1) * K, cn);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c[u] < 0) continue;
+      const int tl = (int)((threadIdx.x + 256 * u) / K);  // token within the round
+      atomicOr(&mask[2 * c[u] + (tl >> 5)], 1u << (tl & 31));
+    }
+    __syncthreads();
+    int rank[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      rank[u] = -1;
+      if (c[u] < 0) continue;
+      const int e = threadIdx.x + 256 * u;
+      const int tl = e / K;
+      const uint32_t lo = mask[2 * c[u]], hi = mask[2 * c[u] + 1];
+      const uint32_t below = (1u << (tl & 31)) - 1u;
+      rank[u] = tl < 32 ? __popc(lo & below) : __popc(lo) + __popc(hi & below);
+      const int32_t p = run[c[u]] + rank[u];
+      const int64_t i = e0 + e;
+      list[p] = (int32_t)(((i / K) << kSlotBits) | (i % K));
+      epos[i] = p;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (rank[u] != 0) continue;
+      const int cc = c[u];
+      run[cc] += __popc(mask[2 * cc]) + __popc(mask[2 * cc + 1]);
+      mask[2 * cc] = 0u;
+      mask[2 * cc + 1] = 0u;
+    }
+    __syncthreads();
+  }
 }
 
 // Append (token << kSlotBits | slot) entries to the selected chunks' lists,
@@ -1009,12 +1096,16 @@ hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream) {
   hipError_t e;
   const int64_t bpb = (a.L + kInvertTokens - 1) / kInvertTokens;
   const int use_lds = a.n <= kInvertLdsBins;
+  const bool ordered = a.ordered && a.n <= kInvertDetBins;
   const size_t lds1 = use_lds ? (size_t)a.n * sizeof(int32_t) : 0;
   count_kernel<<<dim3((unsigned)(BG * bpb)), dim3(256), lds1, stream>>>(a, bpb, use_lds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   scan_kernel<<<dim3((unsigned)BG), dim3(1024), 0, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  scatter_kernel<<<dim3((unsigned)(BG * bpb)), dim3(256), 2 * lds1, stream>>>(a, bpb, use_lds);
+  if (ordered)
+    scatter_ordered_kernel<<<dim3((unsigned)(BG * bpb)), dim3(256), 3 * lds1, stream>>>(a, bpb);
+  else
+    scatter_kernel<<<dim3((unsigned)(BG * bpb)), dim3(256), 2 * lds1, stream>>>(a, bpb, use_lds);
   return hipGetLastError();
 }
 
