@@ -63,6 +63,8 @@ SWEEP = [
     (1, 4, 1, 400, 128, 64, 32),   # top-K past the available chunks
     (1, 4, 2, 200, 64, 1, 8),      # unit chunks
     (1, 2, 2, 300, 128, 48, 3),    # a chunk size that is not a power of two
+    (1, 2, 1, 4096, 64, 1, 4),     # 4096 unit chunks: the largest count with token-ordered lists
+    (1, 2, 1, 4400, 64, 1, 4),     # 4400 chunks: lists in atomic order
 ]
 
 
