@@ -78,6 +78,7 @@ SWEEP = [
     (1, 4, 4, 640, 128, 16, 32, "f32"),
     (1, 6, 3, 1300, 128, 128, 5, "bf16"),
     (1, 32, 1, 256, 64, 32, 2, "bf16"),
+    (1, 2, 1, 9000, 64, 1, 4, "bf16"),  # 9000 chunks: past the LDS histograms of the invert
 ]
 
 
