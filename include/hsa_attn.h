@@ -34,7 +34,9 @@
  *    of the selected chunks.
  *  - Ownership: the caller allocates and frees every buffer, the workspace
  *    included.  The library allocates no device memory and keeps no global
- *    mutable state.  All work is enqueued asynchronously on `stream` (a
+ *    mutable state.  A workspace's contents on entry do not matter: each
+ *    call clears, in its own launches, whatever it accumulates into, and
+ *    results repeat bit for bit from call to call.  All work is enqueued asynchronously on `stream` (a
  *    hipStream_t, NULL = default stream); the library never synchronises.
  *  - Errors: arguments are validated on the host before anything is
  *    enqueued, so any status other than HSA_OK / HSA_ERR_HIP means nothing
@@ -143,9 +145,10 @@ hsa_status_t hsa_prefill_interval(const void* Q, const void* K, const void* V, c
  *   dQ [B,Hq,L,d], dK, dV [B,Hkv,L,d] bf16, written.
  *   workspace of at least hsa_prefill_backward_workspace_size(...) bytes.
  * Limits: as hsa_prefill, plus bf16 only and S <= 64 (HSA_ERR_UNSUPPORTED
- * otherwise).  Gradients are accumulated in fp32; a chunk's dK and dV rows
- * sum the waves of one block with LDS atomics, so their last bits may differ
- * from run to run.
+ * otherwise).  Gradients are accumulated in fp32 in a fixed order (each
+ * chunk's rows in token order), so they repeat bit for bit; above 4096
+ * chunks (L / S > 4096) a chunk's rows follow atomic arrival instead, and
+ * dK, dV may then differ from run to run in their last bits.
  */
 size_t hsa_prefill_backward_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S,
                                            int topk, hsa_dtype_t dtype);
