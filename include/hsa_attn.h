@@ -36,7 +36,8 @@
  *    included.  The library allocates no device memory and keeps no global
  *    mutable state.  A workspace's contents on entry do not matter: each
  *    call clears, in its own launches, whatever it accumulates into, and
- *    results repeat bit for bit from call to call.  All work is enqueued asynchronously on `stream` (a
+ *    results repeat bit for bit from call to call (the backward above 4096
+ *    chunks excepted; see there).  All work is enqueued asynchronously on `stream` (a
  *    hipStream_t, NULL = default stream); the library never synchronises.
  *  - Errors: arguments are validated on the host before anything is
  *    enqueued, so any status other than HSA_OK / HSA_ERR_HIP means nothing
