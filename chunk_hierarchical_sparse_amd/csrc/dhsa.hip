@@ -202,7 +202,10 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   const int row0 = bl + tile * kRowsPerTile;
   if (row0 >= bl1) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int i = row0 + w * 32 + (lane & 31);  // L < 2^31 is checked on the host
+  // the tile's 32-row groups go to the waves rotated by block, so the groups
+  // past a short chunk's end (idle waves) fall on different SIMDs
+  const int wr = (w + (int)(blockIdx.x & 3)) & 3;
+  const int i = row0 + wr * 32 + (lane & 31);  // L < 2^31 is checked on the host
   const bool valid = i < bl1;
   Cut cut = {0, 0};
   if (valid) cut = row_cut(a, bh, l, i);
