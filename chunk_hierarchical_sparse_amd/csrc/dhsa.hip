@@ -82,16 +82,25 @@ __global__ void __launch_bounds__(kThreads) sc_kernel(DhsaArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane % LPR, sub = lane / LPR;
   const f32x4 q4 = *(const f32x4*)(a.qh + (bh * a.nc + l) * D + 4 * li);
-  for (int k0 = 0; k0 <= l; k0 += 4 * RPW) {
-    const int k = k0 + w * RPW + sub;
-    float p = 0.f;
-    if (k <= l) {
-      const f32x4 x = *(const f32x4*)(a.kh + (bh * a.nc + k) * D + 4 * li);
-      p = q4[0] * x[0] + q4[1] * x[1] + q4[2] * x[2] + q4[3] * x[3];
+  // U steps of keys per round, every load issued unconditionally (keys past
+  // l read key l and are not stored): loads under a per-lane guard would
+  // each be waited for before the next
+  constexpr int U = 4;
+  for (int k0 = 0; k0 <= l; k0 += U * 4 * RPW) {
+    f32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = min(k0 + u * 4 * RPW + w * RPW + sub, l);
+      x[u] = *(const f32x4*)(a.kh + (bh * a.nc + k) * D + 4 * li);
     }
 #pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) p += __shfl_xor(p, o, kWave);
-    if (li == 0 && k <= l) a.sc[(bh * a.nc + l) * a.nc + k] = p;
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + u * 4 * RPW + w * RPW + sub;
+      float p = q4[0] * x[u][0] + q4[1] * x[u][1] + q4[2] * x[u][2] + q4[3] * x[u][3];
+#pragma unroll
+      for (int o = LPR / 2; o > 0; o >>= 1) p += __shfl_xor(p, o, kWave);
+      if (li == 0 && k <= l) a.sc[(bh * a.nc + l) * a.nc + k] = p;
+    }
   }
 }
 
@@ -137,18 +146,19 @@ __global__ void __launch_bounds__(kThreads) rank_kernel(DhsaArgs a, int P) {
     const int k = (int)key_index(keys[p]);
     s += a.offs[k + 1] - a.offs[k];
   }
-  part[threadIdx.x] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int t = 0; t < kThreads; ++t) {
-      const int32_t v = part[t];
-      part[t] = acc;
-      acc += v;
-    }
+  // exclusive scan of the threads' sums: inclusive within each wave by lane
+  // shifts, then the totals of the waves before
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t inc = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += y;
   }
+  if (lane == 63) part[w] = inc;
   __syncthreads();
-  int32_t run = part[threadIdx.x];
+  int32_t run = inc - s;
+  for (int v = 0; v < w; ++v) run += part[v];
   for (int p = p0; p < min(p0 + per, n); ++p) {
     cum[p] = run;
     const int k = (int)key_index(keys[p]);
