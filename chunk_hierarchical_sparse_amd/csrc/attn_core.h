@@ -257,7 +257,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void* base,
 // rows past nk read as zero (buffer range check, no branches).  Called by
 // all 256 threads of the block: thread tid takes K piece tid % KPR of rows
 // tid / KPR + i * (256 / KPR), and V piece tid % VPR of the keys of octs
-// tid / VPR + i * (256 / VPR).
+// tid / VPR + i * (256 / VPR).  The whole byte offset of every load goes
+// in the per-lane offset operand with a zero scalar offset: the range check
+// of a raw buffer load covers the lane offset (and the instruction's
+// immediate) but not the scalar offset, so a row step passed there would
+// read past nk, past the end of the tensor for its last chunk.
 template <int D>
 __device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* __restrict__ Kg,
                                               const uint16_t* __restrict__ Vg, int nk) {
@@ -269,7 +273,7 @@ __device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* 
 #pragma unroll
   for (int i = 0; i < R::NK; ++i)
     r.k[i] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff, i * (256 / R::KPR) * D * 2, 0));
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + i * (256 / R::KPR) * D * 2, 0, 0));
   // oct o starts at key 16 (o / 2) + 4 (o % 2); octs o0 + i (256 / VPR)
   // (an even step) start 8 i (256 / VPR) keys further on
   const int o0 = tid / R::VPR;
@@ -280,7 +284,7 @@ __device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* 
     for (int kk = 0; kk < 8; ++kk)
       r.v[i][kk] = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                     vr, voff, (i * (256 / R::VPR) * 8 + oct_key(kk)) * D * 2, 0));
+                     vr, voff + (i * (256 / R::VPR) * 8 + oct_key(kk)) * D * 2, 0, 0));
 }
 
 // LDS store of a fetched block: rows up to the next multiple of 32 above nk
