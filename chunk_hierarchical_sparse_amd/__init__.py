@@ -17,6 +17,7 @@ from . import build as _build
 __all__ = [
     "HsaError", "hsa_status_string", "hsa_build_landmarks", "hsa_prefill",
     "hsa_prefill_workspace_size", "hsa_decode", "hsa_decode_workspace_size",
+    "hsa_decode_noalloc", "HSA_DECODE_NOALLOC_SCRATCH_BYTES",
     "hsa_prefill_interval", "hsa_prefill_interval_workspace_size", "hsa_prefill_backward",
     "hsa_prefill_backward_workspace_size", "dhsa_prefill",
     "dhsa_prefill_workspace_size", "dhsa_build_chunk_keys", "dhsa_decode",
@@ -32,6 +33,9 @@ HSA_ERR_HIP = 4
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+
+# fixed device scratch of hsa_decode_noalloc (include/hsa_attn.h)
+HSA_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -73,6 +77,8 @@ def load_library():
         "hsa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _L], _Z),
         "hsa_decode": ([_P, _P, _P, _P, _L, _L, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _Z,
                         _P], _I),
+        "hsa_decode_noalloc": ([_P, _P, _P, _P, _L, _L, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                _P], _I),
         "dhsa_prefill_workspace_size": ([_I, _L, _I, _I, _I, _I], _Z),
         "dhsa_prefill": ([_P, _P, _P, _P, _I, _L, _P, _P, _P, _I, _L, _I, _I, _I, _P, _Z, _P],
                          _I),
@@ -270,6 +276,40 @@ def hsa_decode(q, Kc, Vc, lmk, n_ctx, S, topk, out=None, return_selection=False,
                           topk, _dtype_code(q), _ptr(ws), nbytes, _stream(q)))
     if return_selection:
         return out, sel_idx, sel_w
+    return out
+
+
+def hsa_decode_noalloc(q, Kc, Vc, lmk, n_ctx, S, topk, out, sel_idx=None, sel_w=None):
+    """hsa_decode without a workspace: the library's fixed per-device scratch
+    array stands in for it, so the call allocates nothing.  The outputs are
+    the caller's: out [B,Hq,d] like q, and optionally sel_idx int32
+    [B,Hkv,topk] and sel_w fp32 [B,Hq,topk].  Calls that overlap on one GPU
+    race on the scratch."""
+    _need(q, "q", 3)
+    _need(Kc, "Kc", 4, q.dtype)
+    _need(Vc, "Vc", 4, q.dtype)
+    _need(lmk, "lmk", 4, torch.float32)
+    B, Hq, d = q.shape
+    Hkv, n_max = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, Hkv, n_max, d) or Vc.shape != Kc.shape:
+        raise ValueError("Kc and Vc must be [B,Hkv,n_max,d] matching q")
+    if lmk.shape != (B, Hkv, n_max // S, d):
+        raise ValueError("lmk must be [B,Hkv,n_max//S,d]")
+    _need(out, "out", 3, q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must be [B,Hq,d] like q")
+    if sel_idx is not None:
+        _need(sel_idx, "sel_idx", 3, torch.int32)
+        if sel_idx.shape != (B, Hkv, topk):
+            raise ValueError("sel_idx must be [B,Hkv,topk]")
+    if sel_w is not None:
+        _need(sel_w, "sel_w", 3, torch.float32)
+        if sel_w.shape != (B, Hq, topk):
+            raise ValueError("sel_w must be [B,Hq,topk]")
+    _check(load_library().hsa_decode_noalloc(q.data_ptr(), Kc.data_ptr(), Vc.data_ptr(),
+                                             lmk.data_ptr(), n_ctx, n_max, out.data_ptr(),
+                                             _ptr(sel_idx), _ptr(sel_w), B, Hq, Hkv, d, S, topk,
+                                             _dtype_code(q), _stream(q)))
     return out
 
 

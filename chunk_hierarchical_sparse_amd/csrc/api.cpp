@@ -265,6 +265,15 @@ void* align_ws(void* ws) {
 
 }  // namespace
 
+namespace hsa {
+
+int api_error(int status, const char* message) {
+  g_err = message;
+  return status;
+}
+
+}  // namespace hsa
+
 extern "C" {
 
 const char* hsa_status_string(hsa_status_t status) {

@@ -16,6 +16,10 @@ enum : int { kF32 = 0, kBF16 = 1 };
 // ---- shared ----------------------------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream);
 
+// Records `message` as the calling thread's last error (hsa_last_error_message)
+// and returns `status` (an hsa_status_t value).
+int api_error(int status, const char* message);
+
 // ---- landmarks (landmarks.hip) ---------------------------------------------
 // lmk[bh, c, :] = sum of rows c*S .. c*S+S-1 of K[bh] / sqrt(S), for chunks
 // c0 <= c < c1.  K row stride is d; a (b,h) slab holds `slab_tokens` rows and

@@ -34,7 +34,7 @@
  *    of the selected chunks.
  *  - Ownership: the caller allocates and frees every buffer, the workspace
  *    included.  The library allocates no device memory and keeps no global
- *    mutable state.  A workspace's contents on entry do not matter: each
+ *    mutable state, except the fixed scratch array of hsa_decode_noalloc.  A workspace's contents on entry do not matter: each
  *    call clears, in its own launches, whatever it accumulates into, and
  *    results repeat bit for bit from call to call (the backward above 4096
  *    chunks excepted; see there).  All work is enqueued asynchronously on `stream` (a
@@ -179,6 +179,30 @@ hsa_status_t hsa_decode(const void* q, const void* Kc, const void* Vc, const flo
                         int64_t n_ctx, int64_t n_max, void* o, int32_t* sel_idx, float* sel_w,
                         int B, int Hq, int Hkv, int d, int S, int topk, hsa_dtype_t dtype,
                         void* workspace, size_t workspace_bytes, hsa_stream_t stream);
+
+/*
+ * hsa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * arguments and results are hsa_decode's (the same kernels run); instead of
+ * a caller workspace the call uses a fixed scratch array of
+ * HSA_DECODE_NOALLOC_SCRATCH_BYTES in device memory that each GPU holds
+ * from the first call on it until the process ends.  The scratch of the
+ * current device is used, so `stream` must belong to the current device.
+ * The call allocates and frees nothing (no hipMalloc, no library
+ * allocation); the first call on a device looks up the array's address.
+ *  - A shape whose hsa_decode_workspace_size exceeds the scratch size is
+ *    rejected with HSA_ERR_UNSUPPORTED before anything is enqueued (16 MiB
+ *    covers, e.g., batch 32 x 32/8 heads x 131,072 tokens at topk 8, which
+ *    needs 4.4 MB, and batch 1 x 16/4 heads x 16M tokens at topk 16).
+ *  - Every call on a GPU shares that GPU's array, and the array keeps the
+ *    last call's contents (which no result depends on).  Calls that overlap
+ *    on one GPU (two streams, two threads) race on it: serialise them.
+ */
+#define HSA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+hsa_status_t hsa_decode_noalloc(const void* q, const void* Kc, const void* Vc, const float* lmk,
+                                int64_t n_ctx, int64_t n_max, void* o, int32_t* sel_idx,
+                                float* sel_w, int B, int Hq, int Hkv, int d, int S, int topk,
+                                hsa_dtype_t dtype, hsa_stream_t stream);
 
 /*
  * DHSA prefill ([DHSA] "What carries the argument", Eq. 4, tiling rule,
