@@ -230,7 +230,10 @@ int oracle_hsa_prefill(const void* Q, const void* K, const void* V, int dtype, i
                 qs[hh * d + x] = ld(Q, dtype, ((b * Hq + g * G + hh) * L + t0) * d + x);
               }
             /* Step 3: per-head scores s_h(t,c) of the row and the group sum
-             * sigma at t0. */
+             * sigma at t0.  sigma = (sum over heads of q . lambda) / sqrt(d):
+             * the positive factor is applied once to the summed dot products,
+             * so scores that are exactly equal stay equal for the tie rule
+             * (rounding each head's scaled term first could split them). */
             for (int64_t c = 0; c < navail; ++c) {
               const double* lc = lmk + ((b * Hkv + g) * n + c) * d;
               double sigma = 0.0;
@@ -239,9 +242,9 @@ int oracle_hsa_prefill(const void* Q, const void* K, const void* V, int dtype, i
                 for (int64_t x = 0; x < d; ++x) s += qv[hh * d + x] * lc[x];
                 for (int64_t x = 0; x < d; ++x) s0 += qs[hh * d + x] * lc[x];
                 sh[hh * (n + 1) + c] = s * sc;
-                sigma += s0 * sc;
+                sigma += s0;
               }
-              cand[c].score = sigma;
+              cand[c].score = sigma * sc;
               cand[c].idx = c;
             }
             /* Step 4: top-min(K, |A|) by (sigma desc, c asc). */
@@ -331,13 +334,14 @@ int oracle_hsa_decode_select(const void* q, int dtype, const float* lmk, int64_t
 #pragma omp parallel for schedule(static)
       for (int64_t c = 0; c < navail; ++c) {
         const float* lc = lmk + ((b * Hkv + g) * n_lmk + c) * d;
+        /* group sum of the dot products, scaled once (as in prefill) */
         double sigma = 0.0;
         for (int64_t hh = 0; hh < G; ++hh) {
           double s = 0.0;
           for (int64_t x = 0; x < d; ++x) s += ld(q, dtype, (b * Hq + g * G + hh) * d + x) * (double)lc[x];
-          sigma += s * sc;
+          sigma += s;
         }
-        cand[c].score = sigma;
+        cand[c].score = sigma * sc;
         cand[c].idx = c;
       }
       qsort(cand, (size_t)navail, sizeof(cand_t), cand_cmp);
@@ -913,15 +917,16 @@ int oracle_hsa_prefill_backward(const void* Q, const void* K, const void* V, con
             for (int64_t hh = 0; hh < G; ++hh)
               for (int64_t x = 0; x < d; ++x)
                 qv[hh * d + x] = ld(Q, dtype, ((b * Hq + g * G + hh) * L + t) * d + x);
-            /* the forward's selection: group-summed scores, top-K */
+            /* the forward's selection: group-summed scores (the summed dot
+             * products scaled once, as in the forward), top-K */
             for (int64_t c = 0; c < navail; ++c) {
               double sigma = 0.0;
               for (int64_t hh = 0; hh < G; ++hh) {
                 double a = 0.0;
                 for (int64_t x = 0; x < d; ++x) a += qv[hh * d + x] * lg[c * d + x];
-                sigma += a * sc;
+                sigma += a;
               }
-              cand[c].score = sigma;
+              cand[c].score = sigma * sc;
               cand[c].idx = c;
             }
             qsort(cand, (size_t)navail, sizeof(cand_t), cand_cmp);
