@@ -18,6 +18,12 @@ import synth
 MARGIN = 1e-4
 TOL_BF16 = 2e-2
 TOL_F32_REL = 1e-5
+# Upper bound on the rows a test may exempt for a margin <= MARGIN.  With
+# the seeded random inputs here the K-th/(K+1)-th gap falls below 1e-4 on
+# well under 1% of rows (about 0.4% at the 32K prefill workload), so a
+# margin computation that read small would trip this bound instead of
+# making the exact-set checks vacuous.
+MAX_EXEMPT = 0.02
 
 
 def say(*a):
@@ -59,12 +65,25 @@ def check_out(got, ref, dt, what):
     return err / scale
 
 
-def compare_selection(sel_gpu, sel_ref, margin, what, sel_score=None):
-    """Selected sets must equal the oracle's wherever margin > MARGIN.  Where
+def check_exempt(strict, what, limit=MAX_EXEMPT):
+    """At most a fraction `limit` of the rows (and never more than 2 when
+    there are few rows) may be exempt from the exact checks.  Returns the
+    exempt fraction."""
+    n = int(np.size(strict))
+    ex = int(np.size(strict) - np.count_nonzero(strict))
+    assert ex <= max(2, limit * n), f"{what}: {ex} of {n} rows exempt (margin <= {MARGIN}), " \
+                                    f"above the bound {limit}"
+    return ex / max(n, 1)
+
+
+def compare_selection(sel_gpu, sel_ref, margin, what, sel_score=None, max_exempt=MAX_EXEMPT):
+    """Selected sets must equal the oracle's wherever margin > MARGIN, and at
+    most `max_exempt` of the rows may fall at or below that margin.  Where
     the sets are equal, the GPU's rank order must agree with the oracle's
     scores up to MARGIN (near-equal chunks inside the top-K may swap).
     Returns (rows with equal sets, exempt fraction)."""
     strict = margin > MARGIN
+    check_exempt(strict, what, max_exempt)
     same = (np.sort(sel_gpu, -1) == np.sort(sel_ref, -1)).all(-1)
     bad = ~same & strict
     assert not bad.any(), f"{what}: {int(bad.sum())} selected sets differ above the margin, " \

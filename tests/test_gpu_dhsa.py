@@ -8,33 +8,43 @@ import torch
 import chunk_hierarchical_sparse_amd as hsa
 import oracle
 import synth
-from gpu_util import MARGIN, check_out, dev, host, qkv, say, unpack_mask
+from gpu_util import MARGIN, check_exempt, check_out, dev, host, qkv, say, unpack_mask
 
 pytestmark = pytest.mark.gpu
 
 
-def run_case(B, H, L, d, offs, budget, seed, rows=None, check_order=True):
+def run_case(B, H, L, d, offs, budget, seed, rows=None, check_order=True, block=2048):
     say(f"dhsa case B={B} H={H} L={L} d={d} chunks={len(offs) - 1} budget={budget} seed={seed}")
     Q, K, V = qkv(B, H, H, L, d, "bf16", seed)
     out, mask, order = hsa.dhsa_prefill(dev(Q), dev(K), dev(V), offs, budget, return_mask=True,
                                         return_order=True)
     torch.cuda.synchronize()
     out, mask, order = host(out), host(mask), host(order)
-    ref = oracle.dhsa_prefill(Q, K, V, offs, budget, rows=rows, want_kept=True,
-                              want_sc=check_order)
-    r = np.arange(L) if rows is None else np.asarray(rows)
-    bits = unpack_mask(mask[:, :, r], L)
     # every row keeps exactly min(N_b, i+1) keys, all causal
-    counts = unpack_mask(mask, L).sum(-1)
+    counts = np.bitwise_count(np.ascontiguousarray(mask).view(np.uint32)).sum(-1)
     assert (counts == np.minimum(budget, np.arange(L) + 1)).all(), "kept count != min(N_b, i+1)"
-    strict = ref["margin"] > MARGIN
-    bad = (bits != ref["kept"]).any(-1) & strict
-    assert not bad.any(), f"kept sets differ above the margin at {np.argwhere(bad)[0].tolist()}"
-    same = (bits == ref["kept"]).all(-1)
-    err = check_out(out[:, :, r][same], ref["out"][same], "bf16", "dhsa output")
+    r_all = np.arange(L) if rows is None else np.asarray(rows)
+    err, n_strict, n_rows = 0.0, 0, 0
+    sc = None
+    # the oracle runs on blocks of rows so its kept-set arrays stay small
+    for k0 in range(0, len(r_all), block):
+        r = r_all[k0:k0 + block]
+        ref = oracle.dhsa_prefill(Q, K, V, offs, budget, rows=r, want_kept=True,
+                                  want_sc=check_order and sc is None)
+        if ref["sc"] is not None:
+            sc = ref["sc"]
+        bits = unpack_mask(mask[:, :, r], L)
+        strict = ref["margin"] > MARGIN
+        bad = (bits != ref["kept"]).any(-1) & strict
+        assert not bad.any(), \
+            f"kept sets differ above the margin at {np.argwhere(bad)[0].tolist()} (block {k0})"
+        same = (bits == ref["kept"]).all(-1)
+        err = max(err, check_out(out[:, :, r][same], ref["out"][same], "bf16", "dhsa output"))
+        n_strict += int(strict.sum())
+        n_rows += strict.size
+    exempt = check_exempt(np.arange(n_rows) < n_strict, "dhsa kept sets")
     if check_order:
         nc = len(offs) - 1
-        sc = ref["sc"]
         for b in range(B):
             for h in range(H):
                 for l in range(nc):
@@ -44,18 +54,15 @@ def run_case(B, H, L, d, offs, budget, seed, rows=None, check_order=True):
                     if gaps.size == 0 or gaps.min() > MARGIN:
                         assert (order[b, h, l, : l + 1] == exp).all()
                     assert (order[b, h, l, l + 1:] == -1).all()
-    say(f"  ok: max err {err:.3g}, exempt {float((~strict).mean()):.4f}")
+    say(f"  ok: {len(r_all)} rows, max err {err:.3g}, exempt {exempt:.4f}")
 
 
 def test_dhsa_16k_workload():
-    # B=1, L=16384, H=8, d=128, chunk lengths U{16..128} (seed 5), N_b=2048
+    # B=1, L=16384, H=8, d=128, chunk lengths U{16..128} (seed 5), N_b=2048:
+    # every row's kept set and output, and the chunk ranking of every chunk
     L = 16384
     offs = synth.chunk_offsets(L, 16, 128, seed=5)
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([[0, 1, 15, 16, 2046, 2047, 2048, 2049, L - 1],
-                                     offs[:-1][:40], offs[1:-1][:40] - 1,
-                                     rng.integers(0, L, 300)]))
-    run_case(1, 8, L, 128, offs, 2048, seed=5, rows=rows, check_order=False)
+    run_case(1, 8, L, 128, offs, 2048, seed=5)
 
 
 SWEEP = [
