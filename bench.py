@@ -106,30 +106,73 @@ def to_dev(arr, torch):
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
-def time_steps(torch, hsa, step, steps, warmup, n_stages):
-    """Run warmup steps, then `steps` timed steps with nothing else on the
-    stream (ms per step), then `steps` more with the library's per-stage HIP
-    events on (per-stage ms averages).  The events sit between the kernels of
-    every call and cost a few microseconds each, so they stay out of the
-    throughput figure."""
+class Flush:
+    """Writes a 1 GiB scratch buffer on the current stream: run before every
+    timed call, outside its events, so that no call finds data the previous
+    one left in the L2 or the 256 MB Infinity Cache."""
+
+    def __init__(self, torch, gib=1.0):
+        self.buf = torch.empty(int(gib * (1 << 30)), dtype=torch.uint8, device="cuda")
+        self.k = 0
+
+    def __call__(self):
+        self.k ^= 1
+        self.buf.fill_(self.k)
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return 0.0 if n == 0 else (xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2]))
+
+
+def time_steps(torch, hsa, step, steps, warmup, n_stages, flush):
+    """Warm-up calls, then `steps` timed calls, each after a cache flush and
+    between its own pair of HIP events on the library's stream (torch's
+    current stream): the step time is their median.  Then `steps` more
+    calls, again each after a flush, with the library's per-stage HIP events
+    on: the events between the kernels cost a few microseconds each, so they
+    stay out of the step time.  Every workload therefore launches its
+    kernels warmup + 2 * steps times.
+
+    Returns dict(ms = median step, ms_mean, stage_mean = per-stage mean ms,
+    stage_median = per-stage median ms)."""
     for _ in range(warmup):
+        flush()
         step()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        flush()
+        a.record()
         step()
-    end.record()
+        b.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    times = [a.elapsed_time(b) for a, b in ev]
     hsa.hsa_profile_read()  # drop anything recorded earlier
-    hsa.hsa_profile_enable(True)
+    per_call = []
     for _ in range(steps):
+        flush()
+        hsa.hsa_profile_enable(True)
         step()
+        hsa.hsa_profile_enable(False)
+        calls, st = hsa.hsa_profile_read(n_stages)
+        per_call.append(st if calls == 1 else [0.0] * n_stages)
     torch.cuda.synchronize()
-    hsa.hsa_profile_enable(False)
-    calls, stage_ms = hsa.hsa_profile_read(n_stages)
-    return ms, [s / max(calls, 1) for s in stage_ms]
+    cols = list(zip(*per_call)) if per_call else [()] * n_stages
+    return {"ms": _median(times), "ms_mean": sum(times) / len(times),
+            "stage_mean": [sum(c) / max(len(c), 1) for c in cols],
+            "stage_median": [_median(list(c)) for c in cols]}
+
+
+def add_timing(res, t, stage):
+    """Adds the mean step time and the dominant kernel's median launch time
+    (stage `stage`) beside the median step time and mean launch time the
+    record already holds."""
+    res["ms_per_step_mean"] = t["ms_mean"]
+    res["roofline"]["median_launch_ms"] = t["stage_median"][stage]
+    return res
 
 
 def prefill_counts(L, S, topk):
@@ -162,7 +205,8 @@ def bench_prefill(torch, hsa, args):
         hsa.hsa_prefill(q, k, v, S, topk, out=out, workspace=ws)
 
     log("prefill: timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 5)
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 5, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
     sel, avail = prefill_counts(L, S, topk)
     attn_flop = B * Hq * sel * S * d * 4          # QK^T + PV over selected chunks
     score_flop = B * Hkv * avail * d * 2          # group-summed retrieval scores
@@ -186,6 +230,7 @@ def bench_prefill(torch, hsa, args):
     inputs = (Q, K, V, S, topk)
     del q, k, v, out, ws
     torch.cuda.empty_cache()
+    add_timing(res, t, 3)
     return res, inputs
 
 
@@ -205,7 +250,8 @@ def bench_prefill_interval(torch, hsa, args, inputs, R=8):
         hsa.hsa_prefill_interval(q, k, v, S, topk, R, out=out, workspace=ws)
 
     log(f"prefill, retrieval every {R} tokens: timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 5)
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 5, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
     n = L // S
     sel = sum(min(topk, min((t // R * R) // S, n)) for t in range(L))
     attn_flop = B * Hq * sel * S * d * 4
@@ -224,6 +270,7 @@ def bench_prefill_interval(torch, hsa, args, inputs, R=8):
         stages_ms=dict(zip(["landmarks", "select", "invert", "attend", "fuse"], stages)))
     del q, k, v, out, ws
     torch.cuda.empty_cache()
+    add_timing(res, t, 3)
     return res
 
 
@@ -258,7 +305,8 @@ def bench_decode(torch, hsa, args, big=False):
         hsa.hsa_decode(q, Kc, Vc, lmk, N, S, topk, out=out, workspace=ws)
 
     log("decode: timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 3)
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 3, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
     n = N // S
     lmk_bytes = B * Hkv * n * d * 4
     kv_bytes = B * Hkv * topk * S * d * 2 * 2
@@ -281,6 +329,7 @@ def bench_decode(torch, hsa, args, big=False):
                     "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
     del Kc, Vc, lmk, q, out, ws
     torch.cuda.empty_cache()
+    add_timing(res, t, 0)
     return res
 
 
@@ -300,7 +349,8 @@ def bench_dhsa(torch, hsa, args):
         hsa.dhsa_prefill(q, k, v, offs, budget, out=out, workspace=ws)
 
     log("dhsa: timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 5)
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 5, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
     pairs = sum(min(budget, i + 1) for i in range(L))
     attn_flop = B * H * pairs * d * 4
     achieved = attn_flop / (stages[3] * 1e-3) / 1e12
@@ -316,6 +366,7 @@ def bench_dhsa(torch, hsa, args):
         stages_ms=dict(zip(["pool", "sc", "rank", "attend", "mask"], stages)))
     del q, k, v, out, ws
     torch.cuda.empty_cache()
+    add_timing(res, t, 3)
     return res
 
 
@@ -344,7 +395,8 @@ def bench_dhsa_decode(torch, hsa, args):
         hsa.dhsa_decode(qcur, Kc, Vc, khat, offs, budget, out=out, workspace=ws)
 
     log("dhsa decode: timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 3)
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 3, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
     pos = L - 1
     kept = min(budget, pos + 1)
     kv_bytes = B * H * kept * d * 2 * 2            # the kept keys and values
@@ -366,6 +418,7 @@ def bench_dhsa_decode(torch, hsa, args):
                     "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
     del Kc, Vc, qcur, khat, out, ws
     torch.cuda.empty_cache()
+    add_timing(res, t, 1)
     return res
 
 
@@ -387,7 +440,8 @@ def bench_backward(torch, hsa, args, inputs):
         hsa.hsa_prefill_backward(q, k, v, dO, S, topk, workspace=ws, grads=grads)
 
     log("backward: timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 8)
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 8, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
     sel, _ = prefill_counts(L, S, topk)
     rows = B * Hq * sel  # (token, head, selected chunk) rows
     # kv stage per row: S = Q K^T, dP = dO V^T, dV and dK products
@@ -407,6 +461,7 @@ def bench_backward(torch, hsa, args, inputs):
                             "finish"], stages)))
     del q, k, v, dO, grads, ws
     torch.cuda.empty_cache()
+    add_timing(res, t, 6)
     return res
 
 
@@ -423,7 +478,8 @@ def bench_swa(torch, hsa, args, inputs, W=512):
         hsa.swa_prefill(q, k, v, W, out=out)
 
     log(f"swa prefill (W={W}): timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 1)
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 1, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
     pairs = sum(min(W, t + 1) for t in range(L))
     flop = B * Hq * pairs * d * 4
     achieved = flop / (stages[0] * 1e-3) / 1e12
@@ -439,6 +495,7 @@ def bench_swa(torch, hsa, args, inputs, W=512):
         stages_ms={"attend": stages[0]})
     del q, k, v, out
     torch.cuda.empty_cache()
+    add_timing(res, t, 0)
     return res
 
 
@@ -460,7 +517,8 @@ def bench_swa_decode(torch, hsa, args, W=512):
         hsa.swa_decode(q, Kc, Vc, N - 1, W, out=out)
 
     log("swa decode: timing")
-    ms, stages = time_steps(torch, hsa, step, args.steps, args.warmup, 1)
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 1, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
     kv_bytes = B * Hkv * W * d * 2 * 2
     total = kv_bytes + B * Hq * d * 2 * 2
     achieved = total / (stages[0] * 1e-3) / 1e9
@@ -475,6 +533,7 @@ def bench_swa_decode(torch, hsa, args, W=512):
         stages_ms={"attend": stages[0]})
     del Kc, Vc, q, out
     torch.cuda.empty_cache()
+    add_timing(res, t, 0)
     return res
 
 
@@ -525,7 +584,7 @@ def summarize_counters(fetch_dir, write_dir, bench_json):
         line = json.loads(fh.read().strip().splitlines()[-1])
     order = [line["config"]["workload"]] + [a["config"]["workload"]
                                            for a in line.get("also", [])]
-    per = line["steps"] + line["warmup"]
+    per = line["warmup"] + 2 * line["steps"]  # warm-up, timed and per-stage passes
     cal = line.get("copy_calibration_bytes")
     if not cal:
         raise SystemExit("the bench run needs --copy-calibration")
@@ -558,6 +617,104 @@ def summarize_counters(fetch_dir, write_dir, bench_json):
     return out
 
 
+def _trace_rows(run_dir):
+    """(start ns, end ns, kernel name) of every dispatch of a rocprofv3
+    --kernel-trace csv run, in dispatch order."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"{run_dir}: expected one *kernel_trace.csv, found {len(files)}")
+    rows = []
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((int(r["Dispatch_Id"]), int(r["Start_Timestamp"]),
+                         int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    return [(a, b, n) for _, a, b, n in rows]
+
+
+def summarize_trace(trace_dir, bench_json):
+    """Per-workload launch durations of each dominant kernel from a rocprofv3
+    --kernel-trace run of one bench command, beside the HIP-event average the
+    same run reported: workloads run in order and each launches its dominant
+    kernel warmup + 2 * steps times (warm-up, timed and per-stage passes), so
+    the trace's launches are attributed in that order.  The last `steps`
+    launches of each workload are the per-stage pass the events timed."""
+    with open(bench_json) as fh:
+        line = json.loads(fh.read().strip().splitlines()[-1])
+    recs = [line] + line.get("also", [])
+    per = line["warmup"] + 2 * line["steps"]
+    rows = _trace_rows(trace_dir)
+    used, out = {}, []
+    for rec in recs:
+        w = rec["config"]["workload"]
+        if w not in DOMINANT:
+            continue
+        name, args_t = DOMINANT[w][0], DOMINANT[w][1]
+        mine = [(b - a) / 1e3 for a, b, n in rows if name in n and args_t in n]
+        k0 = used.get((name, args_t), 0)
+        take = mine[k0:k0 + per]
+        used[(name, args_t)] = k0 + per
+        if len(take) != per:
+            raise SystemExit(f"{w}: expected {per} launches of {name}, found {len(take)}")
+        staged = take[-line["steps"]:]
+        ev_us = rec["roofline"]["avg_launch_ms"] * 1e3
+        out.append({"workload": w, "kernel": name, "launches": per,
+                    "trace_avg_us_all": sum(take) / per,
+                    "trace_avg_us_stage_pass": sum(staged) / len(staged),
+                    "trace_median_us_stage_pass": _median(staged),
+                    "event_avg_us": ev_us,
+                    "event_vs_trace": ev_us / (sum(staged) / len(staged))})
+    return out
+
+
+def summarize_sq(run_dir, bench_json):
+    """Per-workload SQ counters of each dominant kernel from a rocprofv3 --pmc
+    run (MfmaUtil, VALUBusy, SQ_INSTS_VALU_MFMA_MOPS_BF16) of one bench
+    command: MFMA-busy and VALU-busy percentages averaged over the workload's
+    launches, and the bf16 MFMA flops the kernel executed (MOPS * 512)
+    against the algorithmic flops of the record."""
+    import csv
+    import glob
+    with open(bench_json) as fh:
+        line = json.loads(fh.read().strip().splitlines()[-1])
+    recs = [line] + line.get("also", [])
+    per = line["warmup"] + 2 * line["steps"]
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"{run_dir}: expected one *counter_collection.csv, found {len(files)}")
+    by_disp = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            d = by_disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [by_disp[k] for k in sorted(by_disp)]
+    used, out = {}, []
+    for rec in recs:
+        w = rec["config"]["workload"]
+        if w not in DOMINANT or rec["roofline"]["bound"] != "mfma":
+            continue
+        name, args_t = DOMINANT[w][0], DOMINANT[w][1]
+        mine = [d for d in disp if name in d["name"] and args_t in d["name"]]
+        k0 = used.get((name, args_t), 0)
+        take = mine[k0:k0 + per]
+        used[(name, args_t)] = k0 + per
+        if len(take) != per:
+            raise SystemExit(f"{w}: expected {per} launches of {name}, found {len(take)}")
+        avg = {c: sum(d.get(c, 0.0) for d in take) / per
+               for c in ("MfmaUtil", "VALUBusy", "SQ_INSTS_VALU_MFMA_MOPS_BF16")}
+        alg = rec["roofline"]["algorithmic_gflop_per_launch"] * 1e9
+        executed = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        out.append({"workload": w, "kernel": name, "launches": per,
+                    "mfma_busy_pct": avg["MfmaUtil"], "valu_busy_pct": avg["VALUBusy"],
+                    "executed_mfma_gflop": executed / 1e9, "algorithmic_gflop": alg / 1e9,
+                    "executed_over_algorithmic": executed / alg if alg else None,
+                    "algorithmic_mfma_frac": rec["roofline"]["frac"],
+                    "sources_sha1": sources_sha1(w)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -572,6 +729,13 @@ def main():
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="after the workloads, copy GIB GiB device-to-device twice (a plain "
                          "copy kernel of known size to scale HBM byte counters)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_RUN_DIR", "BENCH_JSON"),
+                    help="no GPU work: per-workload launch durations of the dominant kernels "
+                         "from a rocprofv3 --kernel-trace run of one bench command")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("PMC_RUN_DIR", "BENCH_JSON"),
+                    help="no GPU work: per-workload MFMA/VALU busy and executed MFMA flops of "
+                         "the dominant kernels from a rocprofv3 --pmc MfmaUtil VALUBusy "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16 run of one bench command")
     ap.add_argument("--summarize-counters", nargs=3,
                     metavar=("FETCH_RUN_DIR", "WRITE_RUN_DIR", "BENCH_JSON"),
                     help="no GPU work: summarise two rocprofv3 --pmc runs (FETCH_SIZE, "
@@ -580,6 +744,12 @@ def main():
     args = ap.parse_args()
     if args.summarize_counters:
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(*args.summarize_trace), indent=1))
+        return
+    if args.summarize_sq:
+        print(json.dumps(summarize_sq(*args.summarize_sq), indent=1))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -590,12 +760,16 @@ def main():
     import chunk_hierarchical_sparse_amd as hsa
 
     torch.cuda.set_device(0)
+    args.flush = Flush(torch)
     res, inputs = bench_prefill(torch, hsa, args)
     line = {"metric": METRIC, "value": res["value"], "unit": "queries/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic", "config": res["config"], "roofline": res["roofline"],
-            "stages_ms": res["stages_ms"], "whole_path": res["whole_path"]}
+            "stages_ms": res["stages_ms"], "whole_path": res["whole_path"],
+            "ms_per_step_mean": res["ms_per_step_mean"],
+            "timing": "median of K steps, each between its own HIP events on the library's "
+                      "stream after a 1 GiB cache-flush write outside the events"}
     also = []
     extras = [e for e in args.extras.split(",") if e and e != "none"]
     for e in extras:
