@@ -31,89 +31,6 @@ constexpr int kThreads = 256;
 constexpr int kMaxCand = 8192;  // candidates per (b, group) the merge reads
 constexpr int kMaxSlice = 4096;
 
-// The K largest of the distinct keys >= lo among keys[0..M) (LDS or
-// global), written unordered to out[0..min(K, count)); returns that count.
-// Radix select, 8 bits at a time from the top, until the bin holding the
-// K-th largest key is needed whole.  Called by all NT (>= 256) threads of
-// the block; `hist` is 256 ints of LDS, `sv` 4 ints.
-template <int NT>
-__device__ int block_topk_ge(const uint64_t* keys, int M, uint64_t lo, int K, uint64_t* out,
-                             int* hist, int* sv) {
-  const int tid = threadIdx.x;
-  if (tid == 0) sv[3] = 0;
-  __syncthreads();
-  int mine = 0;
-  for (int i = tid; i < M; i += NT) mine += keys[i] >= lo;
-  if (mine) atomicAdd(&sv[3], mine);
-  __syncthreads();
-  const int n = sv[3];
-  __syncthreads();
-  if (n <= K) {
-    if (tid == 0) sv[3] = 0;
-    __syncthreads();
-    for (int i = tid; i < M; i += NT) {
-      const uint64_t k = keys[i];
-      if (k >= lo) out[atomicAdd(&sv[3], 1)] = k;
-    }
-    __syncthreads();
-    return n;
-  }
-  uint64_t prefix = 0, mask = 0;
-  int need = K;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < M; i += NT) {
-      const uint64_t k = keys[i];
-      if (k >= lo && (k & mask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 255u)], 1);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      int c[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) c[q] = hist[255 - 4 * tid - q];
-      const int s = c[0] + c[1] + c[2] + c[3];
-      int incl = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, kWave);
-        if (tid >= o) incl += y;
-      }
-      const int excl = incl - s;
-      if (excl < need && need <= incl) {
-        int cum = excl;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (cum + c[q] >= need) {
-            sv[0] = 255 - 4 * tid - q;
-            sv[1] = need - cum;
-            sv[2] = c[q];
-            break;
-          }
-          cum += c[q];
-        }
-      }
-    }
-    __syncthreads();
-    const int digit = sv[0];
-    need = sv[1];
-    const int bin = sv[2];
-    prefix |= (uint64_t)digit << shift;
-    mask |= (uint64_t)0xff << shift;
-    __syncthreads();
-    if (bin == need) break;
-  }
-  if (tid == 0) sv[3] = 0;
-  __syncthreads();
-  for (int i = tid; i < M; i += NT) {
-    const uint64_t k = keys[i];
-    if (k >= lo && (k & mask) >= prefix) out[atomicAdd(&sv[3], 1)] = k;
-  }
-  __syncthreads();
-  return K;
-}
-
 // Bitonic sort of one 64-bit key per lane across the wave, descending
 // (lane 0 ends with the largest).
 __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t x) {
@@ -189,16 +106,17 @@ __device__ __forceinline__ uint64_t wave_merge_desc_u64(uint64_t x) {
   return x;
 }
 
-// The K (<= 32) largest of keys[0..M) in LDS, descending in lanes 0..K-1 of
-// wave 0 (zeros past the M-th).  Each wave sorts its 64-key pieces and
-// merges them into a running top list; wave 0 then merges the four lists.
-// `lists` is 4 * 32 keys of LDS.  Called by all threads.
-__device__ uint64_t block_topk_sorted(const uint64_t* keys, int M, int K, uint64_t* lists) {
+// The K (<= 32) largest of the keys get(0..M) (zeros past the M-th),
+// descending in lanes 0..K-1 of wave 0.  Each wave sorts its 64-key pieces
+// and merges them into a running top list; wave 0 then merges the four
+// lists.  `lists` is 4 * 32 keys of LDS.  Called by all threads.
+template <typename Get>
+__device__ uint64_t block_topk_sorted(Get get, int M, int K, uint64_t* lists) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint64_t run = 0ull;
   for (int c = w; c * kWave < M; c += kThreads / kWave) {
     const int i = c * kWave + lane;
-    uint64_t x = wave_sort_desc_u64(i < M ? keys[i] : 0ull);
+    uint64_t x = wave_sort_desc_u64(i < M ? get(i) : 0ull);
     // lanes 0..31: the piece's 32 largest, descending; lanes 32..63: the
     // running list reversed (ascending): a bitonic sequence
     const uint64_t rr = __shfl(run, kWave - 1 - lane, kWave);
@@ -288,7 +206,7 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
     score(r0 + CH, xb);
   }
   __syncthreads();
-  const uint64_t top = block_topk_sorted(keys, M, a.topk, lists);
+  const uint64_t top = block_topk_sorted([&](int i) { return keys[i]; }, M, a.topk, lists);
   if (w == 0) {
     const int got = min(M, a.topk);
     uint64_t* out = a.cand + (bg * a.n_slices + sl) * a.topk;
@@ -300,94 +218,65 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
   }
 }
 
-constexpr int kMergeLds = 1024;  // candidates above the bound kept in LDS
+// LDS of the candidate merge.
+struct MergeLds {
+  uint64_t ck[32 * 32];   // candidates at or above the bound (at most K * K)
+  uint64_t lists[4 * 32];
+  int32_t order[32];
+  int sv[4];
+};
 
 // The ordered top-K chunks of one (b, group) from its slices' candidate
-// lists (n_slices lists of K keys, 0 = empty): order[0..K) = chunk indices
-// by (score desc, index asc), -1 past the available ones; returns their
-// count.  Up to 64 candidates are sorted by one wave in registers.  More
-// are first cut at a lower bound of the K-th largest key (the largest
-// smallest-kept key of a full slice) and the survivors sorted the same way,
-// or, past 64 survivors, radix-selected.  Deterministic: every block of the
-// (b, group) gets the same list.  Called by all NT threads of the block.
-template <int NT>
-__device__ int merge_candidates(const DecodeArgs& a, int64_t bg, uint64_t* ck, uint64_t* top,
-                                int32_t* order, int* hist, int* sv, uint64_t* red) {
+// lists (n_slices lists of K keys, each the slice's K largest, 0 = empty):
+// ml.order[0..K) = chunk indices by (score desc, index asc), -1 past the
+// available ones; returns their count.  Up to 64 candidates are sorted by
+// one wave.  More are cut first at lb, the K-th largest slice maximum: the
+// K largest maxima are K distinct keys at or above it, so every key of the
+// global top K is >= lb and lies in a slice whose maximum reaches lb --
+// one of those K slices -- and in that slice's list.  At most K * K
+// candidates survive; the block takes the K largest.  Deterministic: every
+// block of the (b, group) computes the same list.  Called by all threads.
+__device__ int merge_sorted(const DecodeArgs& a, int64_t bg, MergeLds& ml) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int K = a.topk;
-  const int total = a.n_slices * K;
+  const int K = a.topk, ns = a.n_slices;
+  const int total = ns * K;
   const uint64_t* cand = a.cand + bg * (int64_t)total;
-  const uint64_t* src = cand;
-  int n = total;
-  uint64_t lb = 1;  // keys are nonzero
-  if (total > kWave) {
-    // Lower bounds of the K-th largest key: a full slice's smallest kept
-    // key, and the K-th largest of the maxima of any 64 slices (K distinct
-    // keys reach it).  Lane l of a wave takes slice 64 * grp + l.
-    const uint64_t* mm = a.cand_mm + bg * (int64_t)a.n_slices * 2;
-    uint64_t m = 0;
-    for (int grp = w; grp * kWave < a.n_slices; grp += NT / kWave) {
-      const int j = grp * kWave + lane;
-      u64x2 v = {0ull, 0ull};
-      if (j < a.n_slices) v = *(const u64x2*)(mm + 2 * j);
-      m = v[1] > m ? v[1] : m;
-      const uint64_t kth = __shfl(wave_sort_desc_u64(v[0]), K - 1, kWave);
-      m = kth > m ? kth : m;
-    }
-    m = wave_max_u64(m);
-    if (lane == 0) red[w] = m;
-    if (tid == 0) sv[3] = 0;
-    __syncthreads();
-    for (int x = 0; x < NT / kWave; ++x) lb = red[x] > lb ? red[x] : lb;
-    // only slices whose largest key reaches the bound hold survivors; their
-    // loads have fixed trip counts (K <= 32 is uniform) so all are in flight
-    for (int grp = w; grp * kWave < a.n_slices; grp += NT / kWave) {
-      const int j = grp * kWave + lane;
-      if (j >= a.n_slices || mm[2 * j] < lb) continue;
-      const uint64_t* cs = cand + (int64_t)j * K;
-      uint64_t x[32];
-#pragma unroll
-      for (int kk = 0; kk < 32; ++kk) x[kk] = kk < K ? cs[kk] : 0ull;
-#pragma unroll
-      for (int kk = 0; kk < 32; ++kk)
-        if (x[kk] >= lb) {
-          const int p = atomicAdd(&sv[3], 1);
-          if (p < kMergeLds) ck[p] = x[kk];
-        }
-    }
-    __syncthreads();
-    n = sv[3];
-    __syncthreads();
-    if (n <= kMergeLds) src = ck;
-  }
-  if (n <= kWave) {
+  uint64_t top = 0ull;  // wave 0, lanes 0..K-1: the result, descending
+  if (total <= kWave) {
+    if (w == 0) top = wave_sort_desc_u64(lane < total ? cand[lane] : 0ull);
+  } else {
+    const uint64_t* mm = a.cand_mm + bg * (int64_t)ns * 2;
+    const uint64_t tm =
+        block_topk_sorted([&](int i) { return mm[2 * i]; }, ns, K, ml.lists);  // the K largest maxima
     if (w == 0) {
-      uint64_t x = lane < n ? src[lane] : 0ull;
-      if (x < lb) x = 0ull;
-      x = wave_sort_desc_u64(x);
-      if (lane < K) order[lane] = x != 0ull ? (int32_t)key_index(x) : -1;
-      const uint64_t live = __ballot(lane < K && x != 0ull);
-      if (lane == 0) sv[0] = __popcll(live);
+      const uint64_t kth = __shfl(tm, K - 1, kWave);
+      // slice of each of the K largest maxima (0: fewer nonempty slices)
+      if (lane < K) ml.order[lane] = tm != 0ull ? (int)(key_index(tm) / a.slice) : -1;
+      if (lane == 0) {
+        ml.sv[0] = 0;
+        *(uint64_t*)&ml.sv[2] = kth > 1ull ? kth : 1ull;
+      }
     }
     __syncthreads();
-    const int got = sv[0];
+    const uint64_t lb = *(const uint64_t*)&ml.sv[2];
+    for (int e = tid; e < K * K; e += kThreads) {
+      const int j = ml.order[e / K];
+      if (j < 0) continue;
+      const uint64_t x = cand[(int64_t)j * K + e % K];
+      if (x >= lb) ml.ck[atomicAdd(&ml.sv[0], 1)] = x;
+    }
     __syncthreads();
-    return got;
+    const int n = ml.sv[0];
+    top = block_topk_sorted([&](int i) { return ml.ck[i]; }, n, K, ml.lists);
   }
-  const int got = block_topk_ge<NT>(src, n <= kMergeLds ? n : total, lb, K, top, hist, sv);
-  if (tid < K) {
-    int32_t idx = -1;
-    if (tid < got) {
-      const uint64_t k = top[tid];
-      int rank = 0;
-      for (int j = 0; j < got; ++j) rank += top[j] > k;
-      order[rank] = (int32_t)key_index(k);
-    } else {
-      order[tid] = idx;
-    }
+  __syncthreads();  // order[] is rewritten below
+  if (w == 0) {
+    if (lane < K) ml.order[lane] = top != 0ull ? (int32_t)key_index(top) : -1;
+    const uint64_t live = __ballot(lane < K && top != 0ull);
+    if (lane == 0) ml.sv[1] = __popcll(live);
   }
   __syncthreads();
-  return got;
+  return ml.sv[1];
 }
 
 // Per (b, group, rank k): the chunk's keys/values are staged in LDS
@@ -405,16 +294,11 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float sc
   __shared__ __attribute__((aligned(16))) T ks[KB * KSTR];
   __shared__ __attribute__((aligned(16))) T vs[KB * D];
   __shared__ __attribute__((aligned(16))) float ps[kThreads / kWave][KB];
-  __shared__ uint64_t top[32];
-  __shared__ uint64_t red[kThreads / kWave];
-  __shared__ int32_t order[32];
-  __shared__ int hist[256];
-  __shared__ int sv[4];
-  // qs [G * D] fp32, then the merge's candidate buffer when it needs one
+  __shared__ MergeLds ml;
+  // qs [G * D] fp32
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   const int G = a.Hq / a.Hkv;
   float* qs = dyn;
-  uint64_t* ck = (uint64_t*)(dyn + ((G * D + 1) & ~1));
   const int64_t bg = blockIdx.x / a.topk;
   const int k = blockIdx.x % a.topk;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
@@ -427,10 +311,10 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float sc
       for (int e = tid; e < a.topk; e += kThreads) a.sel[bg * a.topk + e] = -1;
     return;
   }
-  const int got = merge_candidates<kThreads>(a, bg, ck, top, order, hist, sv, red);
+  const int got = merge_sorted(a, bg, ml);
   if (k == 0)
-    for (int e = tid; e < a.topk; e += kThreads) a.sel[bg * a.topk + e] = order[e];
-  const int c = k < got ? order[k] : -1;
+    for (int e = tid; e < a.topk; e += kThreads) a.sel[bg * a.topk + e] = ml.order[e];
+  const int c = k < got ? ml.order[k] : -1;
   if (c < 0 || c >= a.n_avail) return;
   // this lane's landmark columns (for s_h)
   const float* lc = a.lmk + (bg * a.lmk_chunks + c) * D;
@@ -537,320 +421,212 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float sc
   }
 }
 
-// Per (b, group): softmax over the selected chunks' per-head scores and the
-// weighted sum of the chunk outputs; no selected chunk gives zeros.
+// Chunks of at most 64 keys: one block per (b, group, rank r).  Every block
+// runs the merge, then loads its chunk's keys and values into registers with
+// coalesced 16-byte loads (each wave instruction reads 1 KB of consecutive
+// bytes: the gather is bandwidth-bound and cold in cache, so the loads must
+// be whole lines) and the chunk's landmark row.  The keys go to LDS first
+// (16-byte pieces XOR-swizzled by row, so lane = key reads spread over the
+// banks): wave w takes heads w, w + 4, ...: lane = key for the logits and a
+// softmax over the chunk's keys, whose weights go to LDS, and the head's
+// retrieval score s_h = q . lambda / sqrt(d).  Then the values replace the
+// keys in the same LDS buffer and lane = output columns for the weighted
+// value sum.  One 16 KB buffer (bf16, d = 128) keeps the block at about
+// 19 KB of LDS, so 8 blocks fit on a CU and every block of a batch-32
+// decode is resident at once.  The normalised chunk output and s_h go to
+// the partial buffers; fuse_kernel weights and sums the ranks.
+template <int D, int DT>
+__global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, float scale) {
+  constexpr int EB = DT == kF32 ? 4 : 2;  // bytes per element
+  constexpr int ROWB = D * EB;            // bytes per key row
+  constexpr int PPR = ROWB / 16;          // 16-byte pieces per row
+  constexpr int NL = kWave * PPR / kThreads;  // 16-byte loads per thread per tensor
+  constexpr int CPL = D / 64;             // output columns per lane
+  typedef typename std::conditional<DT == kF32, float, uint16_t>::type T;
+  union Stage {
+    MergeLds m;
+    unsigned char kv[kWave * ROWB];  // keys (swizzled pieces), then values
+  };
+  __shared__ __attribute__((aligned(16))) Stage st;
+  __shared__ __attribute__((aligned(16))) float lam[D];
+  __shared__ int32_t s_c;
+  // [G][D] queries as loaded (bf16 or fp32), then [G][64] key weights
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  const int G = a.Hq / a.Hkv;
+  const int K = a.topk;
+  uint32_t* qs = (uint32_t*)dyn;
+  float* ps = dyn + G * D * EB / 4;
+  const int64_t bg = blockIdx.x / K;
+  const int r = blockIdx.x % K;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t qrow0 = (int64_t)((bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G);
+  // the group's queries load during the merge (G * D elements, 16 bytes at a time)
+  const int nq = G * D * EB / 16;
+  const u32x4* qg = (const u32x4*)((const char*)a.q + qrow0 * ROWB);
+  u32x4 qx[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) qx[i] = qg[min(tid + i * kThreads, nq - 1)];
+  if (a.n_avail > 0) {
+    const int got = merge_sorted(a, bg, st.m);
+    if (tid == 0) s_c = r < got ? st.m.order[r] : -1;
+    if (r == 0 && tid < K) a.sel[bg * K + tid] = st.m.order[tid];
+  } else {
+    if (tid == 0) s_c = -1;
+    if (r == 0 && tid < K) a.sel[bg * K + tid] = -1;
+  }
+  __syncthreads();
+  const int c = s_c;
+  if (c < 0) return;  // uniform: rank past the selected chunks
+  const int64_t base = (bg * a.n_max + (int64_t)c * a.S) * ROWB;
+  const char* Kg = (const char*)a.Kc + base;
+  const char* Vg = (const char*)a.Vc + base;
+  // rows past the chunk (S < 64) re-read row S - 1; their weights are zero
+  u32x4 kx[NL], vx[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int e = tid + i * kThreads, row = e / PPR, pc = e % PPR;
+    const int64_t off = (int64_t)min(row, a.S - 1) * ROWB + pc * 16;
+    kx[i] = *(const u32x4*)(Kg + off);
+    vx[i] = *(const u32x4*)(Vg + off);
+  }
+  f32x4 lx = {0.f, 0.f, 0.f, 0.f};
+  if (tid < D / 4) lx = *(const f32x4*)(a.lmk + (bg * a.lmk_chunks + c) * D + 4 * tid);
+  {
+    int m = 0;
+    for (int i = tid; i < nq; i += kThreads, ++m)
+      *(u32x4*)(&qs[4 * i]) = m == 0 ? qx[0] : (m == 1 ? qx[1] : qg[i]);
+  }
+  // piece pc of key row j sits at piece pc ^ (j % PPR) of the row
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int e = tid + i * kThreads, row = e / PPR, pc = e % PPR;
+    *(u32x4*)(&st.kv[row * ROWB + ((pc ^ (row % PPR)) * 16)]) = kx[i];
+  }
+  if (tid < D / 4) *(f32x4*)(&lam[4 * tid]) = lx;
+  __syncthreads();
+  const bool key_ok = lane < a.S;
+  for (int h = w; h < G; h += kThreads / kWave) {
+    // logit of key `lane`
+    float acc = 0.f;
+    const unsigned char* kr = &st.kv[lane * ROWB];
+    const uint32_t* qh = qs + h * D * EB / 4;
+#pragma unroll 4
+    for (int pc = 0; pc < PPR; ++pc) {
+      const u32x4 k4 = *(const u32x4*)(kr + ((pc ^ (lane % PPR)) * 16));
+      const u32x4 q4 = *(const u32x4*)(qh + 4 * pc);
+      if (DT == kF32) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc += __uint_as_float(q4[v]) * __uint_as_float(k4[v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t kw = k4[v], qw = q4[v];
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw),
+                                                __builtin_bit_cast(bf16x2, qw), acc, false);
+        }
+      }
+    }
+    const float lg = key_ok ? acc * scale : -INFINITY;
+    const float mx = wave_max_f32(lg);
+    const float pe = key_ok ? expf(lg - mx) : 0.f;
+    ps[h * kWave + lane] = pe / wave_sum_f32(pe);
+    // s_h: this lane's landmark columns
+    float sl = 0.f;
+#pragma unroll
+    for (int x = 0; x < CPL; ++x) {
+      const int col = CPL * lane + x;
+      const float qv = DT == kF32 ? __uint_as_float(qh[col])
+                                  : bf16_bits_to_f32(((const uint16_t*)qh)[col]);
+      sl += qv * lam[col];
+    }
+    sl = wave_sum_f32(sl);
+    if (lane == 0) a.part_s[(qrow0 + h) * K + r] = sl * scale;
+  }
+  __syncthreads();
+  // the values replace the keys
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int e = tid + i * kThreads, row = e / PPR, pc = e % PPR;
+    *(u32x4*)(&st.kv[row * ROWB + pc * 16]) = vx[i];
+  }
+  __syncthreads();
+  for (int h = w; h < G; h += kThreads / kWave) {
+    float o[CPL];
+#pragma unroll
+    for (int x = 0; x < CPL; ++x) o[x] = 0.f;
+    const float* ph = ps + h * kWave;
+#pragma unroll 4
+    for (int j = 0; j < kWave; j += 4) {
+      const f32x4 p4 = *(const f32x4*)(&ph[j]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const T* vr = (const T*)&st.kv[(j + jj) * ROWB] + CPL * lane;
+        if (DT == kF32) {
+#pragma unroll
+          for (int x = 0; x < CPL; ++x) o[x] += p4[jj] * ((const float*)vr)[x];
+        } else if (CPL == 2) {
+          const uint32_t v2 = *(const uint32_t*)vr;
+          o[0] += p4[jj] * bf16_bits_to_f32(v2 & 0xffffu);
+          o[CPL - 1] += p4[jj] * bf16_bits_to_f32(v2 >> 16);
+        } else {
+          o[0] += p4[jj] * bf16_bits_to_f32(*(const uint16_t*)vr);
+        }
+      }
+    }
+    float* po = a.part_o + ((qrow0 + h) * K + r) * D + CPL * lane;
+    if (CPL == 2)
+      *(f32x2*)po = f32x2{o[0], o[CPL - 1]};
+    else
+      po[0] = o[0];
+  }
+}
+
+// Per (b, group): per head, a softmax over the selected chunks' s_h (one
+// wave per head, lane = rank) and the weighted sum of the normalised chunk
+// outputs (16 bytes of columns per thread, all ranks' loads in flight); no
+// selected chunk gives zeros.
 template <int D, int DT>
 __global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
   __shared__ float wts[32 * 32];  // [head of the group][rank]
   __shared__ int s_got;
   const int64_t bg = blockIdx.x;
-  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int G = a.Hq / a.Hkv;
-  const int tid = threadIdx.x;
-  const int64_t qrow0 = (int64_t)b * a.Hq + g * G;
-  if (tid == 0) {
-    const int32_t* sel = a.sel + bg * a.topk;
-    int m = 0;
-    while (m < a.topk && sel[m] >= 0) ++m;
-    s_got = m;
+  const int K = a.topk;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t qrow0 = (int64_t)((bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G);
+  if (w == 0) {
+    const int32_t sv = lane < K ? a.sel[bg * K + lane] : -1;
+    const uint64_t live = __ballot(sv >= 0);
+    if (lane == 0) s_got = __popcll(live);
   }
   __syncthreads();
   const int got = s_got;
-  for (int e = tid; e < G * a.topk; e += kThreads) {
-    const int64_t row = qrow0 + e / a.topk;
-    const int kk = e % a.topk;
-    const float* sc = a.part_s + row * a.topk;
-    float smax = -INFINITY, z = 0.f;
-    for (int j = 0; j < got; ++j) smax = fmaxf(smax, sc[j]);
-    for (int j = 0; j < got; ++j) z += expf(sc[j] - smax);
-    const float wk = kk < got ? expf(sc[kk] - smax) / z : 0.f;
-    wts[e] = wk;
-    if (a.sel_w) a.sel_w[row * a.topk + kk] = wk;
+  for (int h = w; h < G; h += kThreads / kWave) {
+    const int64_t row = qrow0 + h;
+    const float sc = lane < got ? a.part_s[row * K + lane] : -INFINITY;
+    const float mx = wave_max_f32(sc);
+    const float e = lane < got ? expf(sc - mx) : 0.f;
+    const float wk = e / wave_sum_f32(e);
+    if (lane < K) {
+      wts[h * K + lane] = lane < got ? wk : 0.f;
+      if (a.sel_w) a.sel_w[row * K + lane] = lane < got ? wk : 0.f;
+    }
   }
   __syncthreads();
-  for (int e = tid; e < G * D; e += kThreads) {
-    const int hh = e / D, x = e % D;
-    const int64_t row = qrow0 + hh;
-    float acc = 0.f;
-    for (int kk = 0; kk < got; ++kk)
-      acc += wts[hh * a.topk + kk] * a.part_o[(row * a.topk + kk) * D + x];
-    store_elem<DT>(a.o, row * D + x, acc);
-  }
-}
-
-// Chunks of at most 64 keys: R = ceil(K / 8) blocks of 8 waves per (b,
-// group), wave w of block rb taking rank 8 rb + w.  Each block runs the
-// merge itself; lane = key for the logits (the key row in registers, packed
-// bf16 dot products) and lane = output columns for the weighted value sum
-// (the values in registers, the weights broadcast from LDS).  With R = 1 the
-// chunk outputs of a round of `fused_heads` heads stay in LDS and the block
-// fuses them (the softmax over the ranks' s_h) itself; with R > 1 they go to
-// the partial buffers for fuse_kernel.
-constexpr int kFusedWaves = 8;
-constexpr int kFusedThreads = kFusedWaves * kWave;
-constexpr int kFusedPartBytes = 32768;  // LDS for one round's chunk outputs
-constexpr int kFusedMaxLds = 61440;  // dynamic LDS bytes (static arrays take ~1.5 KB)
-
-__host__ __device__ inline int fused_heads(int G, int K, int D) {
-  int hg = kFusedPartBytes / (K * D * 4);
-  hg = hg < 1 ? 1 : hg;
-  hg = hg > 8 ? 8 : hg;
-  return hg < G ? hg : G;
-}
-
-__host__ __device__ inline int round4(int x) { return (x + 3) & ~3; }
-
-
-// LDS floats before the merge's candidate buffer
-__host__ __device__ inline int fused_lds_floats(int G, int K, int D, int dt) {
-  const int hg = fused_heads(G, K, D);
-  return G * D + (dt == kBF16 ? G * D / 2 : 0) + hg * K * D + 2 * round4(hg * K) +
-         kFusedWaves * hg * kWave;
-}
-
-// dynamic LDS bytes of the fused kernel, 0 if it does not apply
-size_t fused_lds_bytes(const DecodeArgs& a) {
-  const int G = a.Hq / a.Hkv;
-  if (a.S > kWave) return 0;
-  size_t bytes = (size_t)fused_lds_floats(G, a.topk, a.d, a.dtype) * sizeof(float);
-  if ((int64_t)a.n_slices * a.topk > kWave) bytes += (size_t)kMergeLds * sizeof(uint64_t);
-  return bytes <= (size_t)kFusedMaxLds ? bytes : 0;
-}
-
-template <int D, int DT>
-__global__ void __launch_bounds__(kFusedThreads) attend_fused_kernel(DecodeArgs a, float scale) {
-  constexpr int NW = kFusedWaves, NT = kFusedThreads;
-  constexpr int CPL = D / 64;                  // output columns per lane
-  constexpr int KV4 = D * (DT == kF32 ? 4 : 2) / 16;  // 16-byte pieces per key row
-  __shared__ uint64_t top[32];
-  __shared__ uint64_t red[NW];
-  __shared__ int32_t order[32];
-  __shared__ int hist[256];
-  __shared__ int sv[4];
-  extern __shared__ __attribute__((aligned(16))) float dyn[];
-  const int G = a.Hq / a.Hkv;
-  const int K = a.topk;
-  const int HG = fused_heads(G, K, D);
-  float* qf = dyn;                                             // [G][D] fp32
-  uint32_t* qb = (uint32_t*)(qf + G * D);                      // [G][D/2] bf16 pairs
-  float* part = (float*)(qb + (DT == kBF16 ? G * D / 2 : 0));  // [HG][K][D]
-  float* psc = part + HG * K * D;                              // [HG][K] s_h
-  float* wts = psc + round4(HG * K);                           // [HG][K] fusion weights
-  float* pbuf = wts + round4(HG * K);                          // [NW][HG][64] key weights
-  uint64_t* ck = (uint64_t*)(pbuf + NW * HG * kWave);
-  const int R = (K + NW - 1) / NW;  // blocks per (b, group)
-  const int64_t bg = blockIdx.x / R;
-  const int rb = blockIdx.x % R;
-  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t qrow0 = (int64_t)b * a.Hq + g * G;  // first head row of the group
-
-  // the group's queries load during the merge
-  constexpr int QP = 2;  // query element pairs per thread in flight
-  const int npairs = G * D / 2;
-  uint32_t qraw[QP];
-  f32x2 qpair[QP];
+  for (int e = tid; e < G * D / 4; e += kThreads) {
+    const int h = e / (D / 4), x4 = e % (D / 4);
+    const int64_t row = qrow0 + h;
+    const float* po = a.part_o + row * K * D + 4 * x4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int kk = 0; kk < got; ++kk) {
+      const f32x4 v = *(const f32x4*)(po + (int64_t)kk * D);
+      const float wk = wts[h * K + kk];
 #pragma unroll
-  for (int i = 0; i < QP; ++i) {
-    const int e2 = tid + i * NT;
-    if (e2 < npairs) {
-      if (DT == kF32) qpair[i] = ((const f32x2*)a.q)[qrow0 * D / 2 + e2];
-      else qraw[i] = ((const uint32_t*)a.q)[qrow0 * D / 2 + e2];
+      for (int x = 0; x < 4; ++x) acc[x] += wk * v[x];
     }
-  }
-  int got = 0;
-  if (a.n_avail > 0) got = merge_candidates<NT>(a, bg, ck, top, order, hist, sv, red);
-  for (int i = 0; i < QP; ++i) {
-    const int e2 = tid + i * NT;
-    if (e2 < npairs) {
-      if (DT == kF32) {
-        *(f32x2*)(qf + 2 * e2) = qpair[i];
-      } else {
-        qb[e2] = qraw[i];
-        *(f32x2*)(qf + 2 * e2) =
-            f32x2{bf16_bits_to_f32(qraw[i] & 0xffffu), bf16_bits_to_f32(qraw[i] >> 16)};
-      }
-    }
-  }
-  for (int e2 = tid + QP * NT; e2 < npairs; e2 += NT) {
-    if (DT == kF32) {
-      *(f32x2*)(qf + 2 * e2) = ((const f32x2*)a.q)[qrow0 * D / 2 + e2];
-    } else {
-      const uint32_t r = ((const uint32_t*)a.q)[qrow0 * D / 2 + e2];
-      qb[e2] = r;
-      *(f32x2*)(qf + 2 * e2) = f32x2{bf16_bits_to_f32(r & 0xffffu), bf16_bits_to_f32(r >> 16)};
-    }
-  }
-  if (rb == 0 && tid < K) a.sel[bg * K + tid] = tid < got ? order[tid] : -1;
-  __syncthreads();
-
-  const bool key_ok = lane < a.S;
-  const int r = rb * NW + w;  // this wave's rank
-  float* pw = pbuf + w * HG * kWave;
-  for (int h0 = 0; h0 < G; h0 += HG) {
-    const int nh = min(HG, G - h0);
-    if (r < got) {
-      const int c = order[r];
-      const int64_t base = (bg * a.n_max + (int64_t)c * a.S) * D;
-      // the chunk's rows load again in each round of heads (one round unless
-      // the group has more than 8 heads or K * D is large): keeping them
-      // across rounds would not fit in registers beside the next loads
-      u32x4 kr[KV4];                // this lane's key row
-      float lam[CPL];               // this lane's landmark columns
-      uint32_t vr[kWave];           // bf16: value columns of key j as loaded
-      uint32_t vp[kWave / 2][CPL];  // bf16: values of keys 2m, 2m + 1 in one column
-      float vf[kWave][CPL];         // fp32: values of key j
-      {
 #pragma unroll
-        for (int i = 0; i < KV4; ++i)
-          kr[i] = key_ok ? *(const u32x4*)((const char*)a.Kc + (base + (int64_t)lane * D) *
-                                                                    (DT == kF32 ? 4 : 2) + 16 * i)
-                         : u32x4{0u, 0u, 0u, 0u};
-        const float* lc = a.lmk + (bg * a.lmk_chunks + c) * D + CPL * lane;
-#pragma unroll
-        for (int x = 0; x < CPL; ++x) lam[x] = lc[x];
-        if (DT == kBF16) {
-          // values: lane = output columns, one 2- or 4-byte load per key,
-          // in flight with the keys
-#pragma unroll
-          for (int j = 0; j < kWave; ++j) {
-            const int64_t off = base + (int64_t)j * D + CPL * lane;
-            vr[j] = 0u;
-            if (j < a.S)
-              vr[j] = CPL == 2 ? *(const uint32_t*)((const uint16_t*)a.Vc + off)
-                               : (uint32_t)((const uint16_t*)a.Vc)[off];
-          }
-        }
-      }
-      // logits, softmax over the chunk's keys, s_h: one head at a time; the
-      // normalised weights go to this wave's LDS rows (bf16 pairs of
-      // consecutive keys, or fp32)
-      for (int hh = 0; hh < nh; ++hh) {
-        const int h = h0 + hh;
-        float acc = 0.f;
-        if (DT == kF32) {
-          const f32x4* qv = (const f32x4*)(qf + h * D);
-#pragma unroll
-          for (int i = 0; i < KV4; ++i) {
-            const f32x4 q4 = qv[i];
-            const f32x4 k4 = __builtin_bit_cast(f32x4, kr[i]);
-            acc += q4[0] * k4[0] + q4[1] * k4[1] + q4[2] * k4[2] + q4[3] * k4[3];
-          }
-        } else {
-          const u32x4* qv = (const u32x4*)(qb + h * D / 2);
-#pragma unroll
-          for (int i = 0; i < KV4; ++i) {
-            const u32x4 q4 = qv[i];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              // copy the elements out first: bit casts of vector-element
-              // operands read element 0
-              const uint32_t kw = kr[i][v], qw = q4[v];
-              acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw),
-                                                    __builtin_bit_cast(bf16x2, qw), acc, false);
-            }
-          }
-        }
-        const float sc = key_ok ? acc * scale : -INFINITY;
-        const float mx = wave_max_f32(sc);
-        const float p = key_ok ? expf(sc - mx) : 0.f;
-        const float pn = p / wave_sum_f32(p);
-        if (DT == kF32) {
-          pw[hh * kWave + lane] = pn;
-        } else {
-          const float next = partner<1>(pn);  // the weight of key lane + 1
-          if ((lane & 1) == 0) ((uint32_t*)pw)[hh * kWave + lane / 2] = pack_bf16x2(pn, next);
-        }
-        float sl = 0.f;
-#pragma unroll
-        for (int x = 0; x < CPL; ++x) sl += qf[h * D + CPL * lane + x] * lam[x];
-        sl = wave_sum_f32(sl);
-        if (lane == 0) {
-          if (R == 1) psc[hh * K + r] = sl * scale;
-          else a.part_s[(qrow0 + h) * K + r] = sl * scale;
-        }
-      }
-      {
-        if (DT == kBF16) {
-          // pair consecutive keys per column for the packed dot products
-#pragma unroll
-          for (int m = 0; m < kWave / 2; ++m) {
-            vp[m][0] = __builtin_amdgcn_perm(vr[2 * m + 1], vr[2 * m], 0x05040100u);
-            if (CPL == 2) vp[m][CPL - 1] = __builtin_amdgcn_perm(vr[2 * m + 1], vr[2 * m], 0x07060302u);
-          }
-        } else {
-          // values: lane = output columns, one 4- or 8-byte load per key
-#pragma unroll
-          for (int j = 0; j < kWave; ++j) {
-            const int64_t off = base + (int64_t)j * D + CPL * lane;
-#pragma unroll
-            for (int x = 0; x < CPL; ++x) vf[j][x] = j < a.S ? ((const float*)a.Vc)[off + x] : 0.f;
-          }
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int hh = 0; hh < nh; ++hh) {
-        float o[CPL];
-#pragma unroll
-        for (int x = 0; x < CPL; ++x) o[x] = 0.f;
-        if (DT == kF32) {
-#pragma unroll
-          for (int j = 0; j < kWave; j += 4) {
-            const f32x4 p4 = *(const f32x4*)(pw + hh * kWave + j);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-              for (int x = 0; x < CPL; ++x) o[x] += p4[jj] * vf[j + jj][x];
-          }
-        } else {
-          const uint32_t* pp = (const uint32_t*)pw + hh * kWave;
-#pragma unroll
-          for (int m = 0; m < kWave / 2; m += 4) {
-            const u32x4 p4 = *(const u32x4*)(pp + m);
-#pragma unroll
-            for (int mm = 0; mm < 4; ++mm) {
-              const uint32_t pq = p4[mm];
-#pragma unroll
-              for (int x = 0; x < CPL; ++x) {
-                const uint32_t vq = vp[m + mm][x];
-                o[x] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vq),
-                                                       __builtin_bit_cast(bf16x2, pq), o[x], false);
-              }
-            }
-          }
-        }
-        float* po = (R == 1 ? part + ((int64_t)hh * K + r) * D
-                            : a.part_o + ((qrow0 + h0 + hh) * K + r) * D) + CPL * lane;
-#pragma unroll
-        for (int x = 0; x < CPL; ++x) po[x] = o[x];
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    if (R > 1) continue;  // fuse_kernel combines the blocks' outputs
-    __syncthreads();
-    // fusion weights: per head, a softmax over the ranks' s_h
-    for (int e = tid; e < nh * K; e += NT) {
-      const int hh = e / K, kk = e % K;
-      const float* sc = psc + hh * K;
-      float smax = -INFINITY, z = 0.f;
-      for (int j = 0; j < got; ++j) smax = fmaxf(smax, sc[j]);
-      for (int j = 0; j < got; ++j) z += expf(sc[j] - smax);
-      const float wk = kk < got ? expf(sc[kk] - smax) / z : 0.f;
-      wts[e] = wk;
-      if (a.sel_w) a.sel_w[(qrow0 + h0 + hh) * K + kk] = wk;
-    }
-    __syncthreads();
-    for (int e = tid; e < nh * D; e += NT) {
-      const int hh = e / D, x = e % D;
-      float acc = 0.f;
-      for (int kk = 0; kk < got; ++kk) acc += wts[hh * K + kk] * part[(hh * K + kk) * D + x];
-      store_elem<DT>(a.o, (qrow0 + h0 + hh) * D + x, acc);
-    }
-    __syncthreads();
+    for (int x = 0; x < 4; ++x) store_elem<DT>(a.o, row * D + 4 * x4 + x, acc[x]);
   }
 }
 
@@ -858,22 +634,20 @@ template <int D, int DT>
 hipError_t stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
   const int64_t BG = (int64_t)a.B * a.Hkv;
   const float scale = 1.0f / sqrtf((float)D);
+  const int G = a.Hq / a.Hkv;
   if (stage == 0) {
     if (a.n_avail > 0)
       scan_kernel<D, DT><<<dim3((unsigned)(BG * a.n_slices)), dim3(kThreads),
                            (size_t)a.slice * sizeof(uint64_t), stream>>>(a);
-  } else if (const size_t lds = fused_lds_bytes(a)) {
-    // chunks of at most 64 keys: one wave per selected chunk; with K <= 8
-    // the attention block also fuses
-    const int R = (a.topk + kFusedWaves - 1) / kFusedWaves;
-    if (stage == 1)
-      attend_fused_kernel<D, DT><<<dim3((unsigned)(BG * R)), dim3(kFusedThreads), lds, stream>>>(
-          a, scale);
-    else if (R > 1)
-      fuse_kernel<D, DT><<<dim3((unsigned)BG), dim3(kThreads), 0, stream>>>(a);
   } else if (stage == 1) {
-    attend_kernel<D, DT><<<dim3((unsigned)(BG * a.topk)), dim3(kThreads),
-                           decode_attend_lds(a.Hq, a.Hkv, D, a.n_slices, a.topk), stream>>>(a, scale);
+    // one block per (b, group, rank)
+    const size_t q_lds = (size_t)G * D * (DT == kF32 ? 4 : 2) + (size_t)G * kWave * sizeof(float);
+    if (a.S <= kWave)
+      attend_rank_kernel<D, DT><<<dim3((unsigned)(BG * a.topk)), dim3(kThreads), q_lds, stream>>>(
+          a, scale);
+    else
+      attend_kernel<D, DT><<<dim3((unsigned)(BG * a.topk)), dim3(kThreads),
+                             (size_t)G * D * sizeof(float), stream>>>(a, scale);
   } else {
     fuse_kernel<D, DT><<<dim3((unsigned)BG), dim3(kThreads), 0, stream>>>(a);
   }
@@ -902,12 +676,6 @@ void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* sl
 }
 
 int64_t decode_max_chunks(int topk) { return (int64_t)kMaxSlice * (kMaxCand / topk); }
-
-size_t decode_attend_lds(int Hq, int Hkv, int d, int n_slices, int topk) {
-  const size_t q = (size_t)(((Hq / Hkv) * d + 1) & ~1) * sizeof(float);
-  // the merge stages candidates in LDS only past one wave's worth
-  return q + ((int64_t)n_slices * topk > kWave ? (size_t)kMergeLds * sizeof(uint64_t) : 0);
-}
 
 hipError_t decode_stage(const DecodeArgs& a, int stage, hipStream_t stream) {
   if (a.d == 64)

@@ -94,11 +94,9 @@ struct DecodeArgs {
 };
 void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* slice);
 // stages: 0 scan (landmark stream + per-slice top-K), 1 attend (merge of the
-// slices' candidates, per-chunk attention; with chunks of <= 64 keys and
-// K <= 8 also the fusion), 2 fuse (empty when stage 1 fused)
+// slices' candidates, then one block per selected chunk), 2 fuse (softmax
+// over the chunks' retrieval scores, weighted sum of the chunk outputs)
 constexpr int kDecodeStages = 3;
-// dynamic LDS bytes of the attention stage
-size_t decode_attend_lds(int Hq, int Hkv, int d, int n_slices, int topk);
 hipError_t decode_stage(const DecodeArgs& a, int stage, hipStream_t stream);
 int64_t decode_max_chunks(int topk);
 
