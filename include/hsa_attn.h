@@ -222,6 +222,9 @@ hsa_status_t hsa_decode_noalloc(const void* q, const void* Kc, const void* Vc, c
  * S_c[l, chunk(j)], the first min(N_b, i+1) keys in (score desc, j asc)
  * order are kept, and softmax(q.k/sqrt d) attention runs over them.
  * Limits: n_chunks <= 4096, B*H*n_chunks*n_chunks < 2^31.
+ * The offsets are validated on the host and copied into the workspace on
+ * `stream` from pageable memory: the call cannot be captured in a HIP graph
+ * (dhsa_decode and dhsa_build_chunk_keys likewise).
  */
 size_t dhsa_prefill_workspace_size(int B, int64_t L, int H, int d, int n_chunks,
                                    hsa_dtype_t dtype);
