@@ -537,6 +537,62 @@ def bench_swa_decode(torch, hsa, args, W=512):
     return res
 
 
+def bench_upper_decode(torch, hsa, args, W=512):
+    """The upper layers' two attentions of one new query in one pass
+    (hsa_swa_decode): HSA decode and 512-token sliding-window decode at the
+    end of 131072-token caches, batch 32, 32 query heads over 8 KV heads,
+    S = 64, top-8.  The same two outputs from separate hsa_decode and
+    swa_decode calls are timed beside it."""
+    import synth
+    B, Hq, Hkv, N, d, S, topk, seed = 32, 32, 8, 131072, 128, 64, 8, 3
+    n_ctx = N - 1  # the new token's key and value are the cache's last row
+    log(f"upper-layer decode: filling caches on the device (B={B}, N={N})")
+    Kc = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device="cuda")
+    Vc = torch.empty_like(Kc)
+    synth.normal_device(Kc, seed, synth.TID_K)
+    synth.normal_device(Vc, seed, synth.TID_V)
+    q = to_dev(synth.normal((B, Hq, d), synth.BF16, seed, synth.TID_QDEC), torch)
+    lmk = hsa.hsa_build_landmarks(Kc, S)
+    oh, osw = torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(hsa.hsa_swa_decode_workspace_size(B, Hq, Hkv, d, S, topk, n_ctx, W),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        hsa.hsa_swa_decode(q, Kc, Vc, lmk, n_ctx, S, topk, W, out_hsa=oh, out_swa=osw,
+                           workspace=ws)
+
+    def separate():
+        hsa.hsa_decode(q, Kc, Vc, lmk, n_ctx, S, topk, out=oh, workspace=ws)
+        hsa.swa_decode(q, Kc, Vc, n_ctx, W, out=osw)
+
+    log(f"upper-layer decode (W={W}): timing")
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 3, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
+    t_sep = time_steps(torch, hsa, separate, args.steps, args.warmup, 4, args.flush)
+    n = n_ctx // S
+    lmk_bytes = B * Hkv * n * d * 4
+    kv_bytes = B * Hkv * topk * S * d * 2 * 2
+    win_bytes = B * Hkv * W * d * 2 * 2
+    qo_bytes = B * Hq * d * 2 * 3
+    total = lmk_bytes + kv_bytes + win_bytes + qo_bytes
+    res = dict(
+        value=B / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
+        config={"workload": "hsa_swa_decode", "B": B, "n_ctx": n_ctx, "Hq": Hq, "Hkv": Hkv,
+                "d": d, "S": S, "topk": topk, "window": W, "inputs": f"N(0,1) bf16, seed {seed}"},
+        roofline={"bound": "hbm", "kernel": "whole step (landmark stream, chunk and window "
+                                            "gathers)",
+                  "achieved": total / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                  "frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
+                  "algorithmic_bytes_per_launch": total, "avg_launch_ms": ms},
+        stages_ms=dict(zip(["scan", "attend", "fuse"], stages)),
+        separate_calls_ms=t_sep["ms"])
+    res["ms_per_step_mean"] = t["ms_mean"]
+    del Kc, Vc, q, lmk, oh, osw, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(inputs, target_s):
     """The oracle as it is, timed on this host's cores on evenly spaced query
     positions of the prefill workload (every head), scaled to queries/s."""
@@ -721,9 +777,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extras", default="prefill_r8,backward,decode,decode16m,dhsa,dhsa_decode,"
-                                        "swa,swa_decode",
+                                        "swa,swa_decode,upper_decode",
                     help="comma list of extra workloads: prefill_r8, backward, decode, "
-                         "decode16m, dhsa, dhsa_decode, swa, swa_decode, or none")
+                         "decode16m, dhsa, dhsa_decode, swa, swa_decode, upper_decode, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -789,6 +845,8 @@ def main():
             also.append(bench_swa(torch, hsa, args, inputs))
         elif e == "swa_decode":
             also.append(bench_swa_decode(torch, hsa, args))
+        elif e == "upper_decode":
+            also.append(bench_upper_decode(torch, hsa, args))
         else:
             raise SystemExit(f"unknown extra workload {e}")
     if also:

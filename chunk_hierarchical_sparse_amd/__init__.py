@@ -17,7 +17,8 @@ from . import build as _build
 __all__ = [
     "HsaError", "hsa_status_string", "hsa_build_landmarks", "hsa_prefill",
     "hsa_prefill_workspace_size", "hsa_decode", "hsa_decode_workspace_size",
-    "hsa_decode_noalloc", "HSA_DECODE_NOALLOC_SCRATCH_BYTES",
+    "hsa_decode_noalloc", "HSA_DECODE_NOALLOC_SCRATCH_BYTES", "hsa_swa_decode",
+    "hsa_swa_decode_workspace_size",
     "hsa_prefill_interval", "hsa_prefill_interval_workspace_size", "hsa_prefill_backward",
     "hsa_prefill_backward_workspace_size", "dhsa_prefill",
     "dhsa_prefill_workspace_size", "dhsa_build_chunk_keys", "dhsa_decode",
@@ -79,6 +80,9 @@ def load_library():
                         _P], _I),
         "hsa_decode_noalloc": ([_P, _P, _P, _P, _L, _L, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                 _P], _I),
+        "hsa_swa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _L, _L], _Z),
+        "hsa_swa_decode": ([_P, _P, _P, _P, _L, _L, _L, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                            _I, _P, _Z, _P], _I),
         "dhsa_prefill_workspace_size": ([_I, _L, _I, _I, _I, _I], _Z),
         "dhsa_prefill": ([_P, _P, _P, _P, _I, _L, _P, _P, _P, _I, _L, _I, _I, _I, _P, _Z, _P],
                          _I),
@@ -311,6 +315,44 @@ def hsa_decode_noalloc(q, Kc, Vc, lmk, n_ctx, S, topk, out, sel_idx=None, sel_w=
                                              _ptr(sel_idx), _ptr(sel_w), B, Hq, Hkv, d, S, topk,
                                              _dtype_code(q), _stream(q)))
     return out
+
+
+def hsa_swa_decode_workspace_size(B, Hq, Hkv, d, S, topk, n_ctx, window):
+    return load_library().hsa_swa_decode_workspace_size(B, Hq, Hkv, d, S, topk, n_ctx, window)
+
+
+def hsa_swa_decode(q, Kc, Vc, lmk, n_ctx, S, topk, window, out_hsa=None, out_swa=None,
+                   return_selection=False, workspace=None):
+    """HSA decode and sliding-window decode of the same query in one pass.
+    q [B,Hq,d] at position n_ctx; caches Kc, Vc [B,Hkv,n_max,d] holding
+    tokens 0..n_ctx; landmarks fp32 [B,Hkv,n_max//S,d].  Returns (o_hsa,
+    o_swa), plus sel_idx, sel_w with return_selection."""
+    _need(q, "q", 3)
+    _need(Kc, "Kc", 4, q.dtype)
+    _need(Vc, "Vc", 4, q.dtype)
+    _need(lmk, "lmk", 4, torch.float32)
+    B, Hq, d = q.shape
+    Hkv, n_max = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, Hkv, n_max, d) or Vc.shape != Kc.shape:
+        raise ValueError("Kc and Vc must be [B,Hkv,n_max,d] matching q")
+    if lmk.shape != (B, Hkv, n_max // S, d):
+        raise ValueError("lmk must be [B,Hkv,n_max//S,d]")
+    out_hsa = torch.empty_like(q) if out_hsa is None else out_hsa
+    out_swa = torch.empty_like(q) if out_swa is None else out_swa
+    sel_idx = sel_w = None
+    if return_selection:
+        sel_idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+        sel_w = torch.empty((B, Hq, topk), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    nbytes = lib.hsa_swa_decode_workspace_size(B, Hq, Hkv, d, S, topk, n_ctx, window)
+    ws = _workspace(nbytes, q.device, workspace) if nbytes else None
+    _check(lib.hsa_swa_decode(q.data_ptr(), Kc.data_ptr(), Vc.data_ptr(), lmk.data_ptr(), n_ctx,
+                              n_max, window, out_hsa.data_ptr(), out_swa.data_ptr(),
+                              _ptr(sel_idx), _ptr(sel_w), B, Hq, Hkv, d, S, topk,
+                              _dtype_code(q), _ptr(ws), nbytes, _stream(q)))
+    if return_selection:
+        return out_hsa, out_swa, sel_idx, sel_w
+    return out_hsa, out_swa
 
 
 def dhsa_prefill_workspace_size(B, L, H, d, n_chunks, dtype):

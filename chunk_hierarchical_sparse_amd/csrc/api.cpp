@@ -182,12 +182,15 @@ struct DecodeLayout {
   int32_t* sel;
   float* part_o;
   float* part_s;
+  float* sw_o;
+  float* sw_lse;
   int n_slices, slice;
   size_t bytes;
 };
 
+// swa_pieces > 0: room for the window pieces of hsa_swa_decode as well.
 DecodeLayout decode_layout(void* ws, int B, int Hq, int Hkv, int d, int S, int topk,
-                           int64_t n_ctx) {
+                           int64_t n_ctx, int swa_pieces = 0) {
   DecodeLayout p;
   hsa::decode_plan(n_ctx / S, topk, (int64_t)B * Hkv, &p.n_slices, &p.slice);
   Carver cv(ws);
@@ -196,8 +199,18 @@ DecodeLayout decode_layout(void* ws, int B, int Hq, int Hkv, int d, int S, int t
   p.sel = cv.take<int32_t>((size_t)B * Hkv * topk);
   p.part_o = cv.take<float>((size_t)B * Hq * topk * d);
   p.part_s = cv.take<float>((size_t)B * Hq * topk);
+  p.sw_o = swa_pieces ? cv.take<float>((size_t)B * Hq * swa_pieces * d) : nullptr;
+  p.sw_lse = swa_pieces ? cv.take<float>((size_t)B * Hq * swa_pieces) : nullptr;
   p.bytes = cv.off + kAlign;
   return p;
+}
+
+constexpr int kSwaPieceKeys = 64;
+constexpr int kSwaMaxPieces = 64;  // window of at most 4096 keys in the fused decode
+
+int swa_decode_pieces(int64_t n_ctx, int64_t window) {
+  const int64_t w = window < n_ctx + 1 ? window : n_ctx + 1;
+  return (int)((w + kSwaPieceKeys - 1) / kSwaPieceKeys);
 }
 
 struct DhsaLayout {
@@ -545,12 +558,93 @@ hsa_status_t hsa_decode(const void* q, const void* Kc, const void* Vc, const flo
   a.lmk_chunks = n_max / S;
   a.n_slices = lay.n_slices;
   a.slice = lay.slice;
+  a.swa_pieces = 0;
+  a.swa_lo = a.swa_hi = 0;
+  a.o_swa = nullptr;
+  a.sw_o = a.sw_lse = nullptr;
   const hipStream_t st = (hipStream_t)stream;
   StageMarks pm(st);
   for (int stage = 0; stage < hsa::kDecodeStages; ++stage) {
     pm.mark();
     hipError_t e = hsa::decode_stage(a, stage, st);
     if (e != hipSuccess) return hip_fail(e, "decode");
+  }
+  pm.mark();
+  return HSA_OK;
+}
+
+size_t hsa_swa_decode_workspace_size(int B, int Hq, int Hkv, int d, int S, int topk,
+                                     int64_t n_ctx, int64_t window) {
+  if (check_decode(B, Hq, Hkv, d, S, topk, n_ctx, n_ctx, HSA_DTYPE_BF16) != HSA_OK) return 0;
+  if (window < 1) return 0;
+  return decode_layout(nullptr, B, Hq, Hkv, d, S, topk, n_ctx, swa_decode_pieces(n_ctx, window))
+      .bytes;
+}
+
+hsa_status_t hsa_swa_decode(const void* q, const void* Kc, const void* Vc, const float* lmk,
+                            int64_t n_ctx, int64_t n_max, int64_t window, void* o_hsa,
+                            void* o_swa, int32_t* sel_idx, float* sel_w, int B, int Hq, int Hkv,
+                            int d, int S, int topk, hsa_dtype_t dtype, void* workspace,
+                            size_t workspace_bytes, hsa_stream_t stream) {
+  g_err.clear();
+  hsa_status_t s = check_decode(B, Hq, Hkv, d, S, topk, n_ctx, n_max, dtype);
+  if (s != HSA_OK) return s;
+  if (n_ctx >= n_max)
+    return fail(HSA_ERR_INVALID_ARGUMENT,
+                "need n_ctx < n_max: the new token (position n_ctx) is in the cache");
+  if (window < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "window must be >= 1");
+  if (S > kSwaPieceKeys) return fail(HSA_ERR_UNSUPPORTED, "hsa_swa_decode needs S <= 64");
+  const int pieces = swa_decode_pieces(n_ctx, window);
+  if (pieces > kSwaMaxPieces)
+    return fail(HSA_ERR_UNSUPPORTED, "hsa_swa_decode needs min(window, n_ctx + 1) <= 4096");
+  if (B == 0) return HSA_OK;
+  if (!q || !Kc || !Vc || !o_hsa || !o_swa)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "q, Kc, Vc, o_hsa and o_swa must not be NULL");
+  if (n_ctx / S > 0 && !lmk) return fail(HSA_ERR_INVALID_ARGUMENT, "lmk must not be NULL");
+  if ((int64_t)B * Hkv * n_max >= (int64_t(1) << 40))
+    return fail(HSA_ERR_UNSUPPORTED, "B*Hkv*n_max must be < 2^40");
+  const size_t need = decode_layout(nullptr, B, Hq, Hkv, d, S, topk, n_ctx, pieces).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(need) + " bytes");
+  DecodeLayout lay = decode_layout(align_ws(workspace), B, Hq, Hkv, d, S, topk, n_ctx, pieces);
+  hsa::DecodeArgs a;
+  a.q = q;
+  a.Kc = Kc;
+  a.Vc = Vc;
+  a.lmk = lmk;
+  a.o = o_hsa;
+  a.sel = sel_idx ? sel_idx : lay.sel;
+  a.sel_w = sel_w;
+  a.cand = lay.cand;
+  a.cand_mm = lay.cand_mm;
+  a.part_o = lay.part_o;
+  a.part_s = lay.part_s;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.S = S;
+  a.topk = topk;
+  a.dtype = dt_code(dtype);
+  a.n_ctx = n_ctx;
+  a.n_max = n_max;
+  a.n_avail = n_ctx / S;
+  a.lmk_chunks = n_max / S;
+  a.n_slices = lay.n_slices;
+  a.slice = lay.slice;
+  a.swa_pieces = pieces;
+  a.swa_hi = n_ctx + 1;
+  a.swa_lo = a.swa_hi - (window < n_ctx + 1 ? window : n_ctx + 1);
+  a.o_swa = o_swa;
+  a.sw_o = lay.sw_o;
+  a.sw_lse = lay.sw_lse;
+  const hipStream_t st = (hipStream_t)stream;
+  StageMarks pm(st);
+  for (int stage = 0; stage < hsa::kDecodeStages; ++stage) {
+    pm.mark();
+    hipError_t e = hsa::decode_stage(a, stage, st);
+    if (e != hipSuccess) return hip_fail(e, "hsa_swa_decode");
   }
   pm.mark();
   return HSA_OK;

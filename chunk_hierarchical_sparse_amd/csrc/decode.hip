@@ -8,15 +8,15 @@
 //              group-summed query and keeps the slice's top-K as 64-bit keys
 //              (score, then lower index): per-wave bitonic sorts merged into
 //              one sorted list.
-//  2. attend : chunks of at most 64 keys: R = ceil(K/8) blocks of 8 waves per
-//              (b, group), one wave per selected chunk (keys and values in
-//              registers); every block merges the slices' candidates into
-//              the same ordered top-K; with K <= 8 the block also fuses.
-//              Longer chunks: one block per (b, group, rank k) staging the
-//              chunk in LDS, every head of the group attending to it.
+//  2. attend : one block per (b, group, rank k); every block merges the
+//              slices' candidates into the same ordered top-K, then attends
+//              to the chunk of its rank (coalesced loads, every head of the
+//              group); the sliding-window attention of the upper layers can
+//              ride in the same launch as extra blocks, one per 64-key piece
+//              of the window.
 //  3. fuse   : one block per (b, group): per head, a softmax over the
-//              selected chunks' s_h weights the chunk outputs (when the
-//              attention blocks did not fuse).
+//              selected chunks' s_h weights the chunk outputs; the window's
+//              pieces are merged by their log-sum-exp.
 #include <math.h>
 
 #include <type_traits>
@@ -421,20 +421,24 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float sc
   }
 }
 
-// Chunks of at most 64 keys: one block per (b, group, rank r).  Every block
-// runs the merge, then loads its chunk's keys and values into registers with
-// coalesced 16-byte loads (each wave instruction reads 1 KB of consecutive
-// bytes: the gather is bandwidth-bound and cold in cache, so the loads must
-// be whole lines) and the chunk's landmark row.  The keys go to LDS first
-// (16-byte pieces XOR-swizzled by row, so lane = key reads spread over the
-// banks): wave w takes heads w, w + 4, ...: lane = key for the logits and a
-// softmax over the chunk's keys, whose weights go to LDS, and the head's
-// retrieval score s_h = q . lambda / sqrt(d).  Then the values replace the
-// keys in the same LDS buffer and lane = output columns for the weighted
-// value sum.  One 16 KB buffer (bf16, d = 128) keeps the block at about
-// 19 KB of LDS, so 8 blocks fit on a CU and every block of a batch-32
-// decode is resident at once.  The normalised chunk output and s_h go to
-// the partial buffers; fuse_kernel weights and sums the ranks.
+// Chunks of at most 64 keys: one block per (b, group, unit r).  Units r < K
+// are the selected chunks: every such block runs the merge and takes the
+// chunk of rank r.  Units r >= K (sliding-window attention in the same
+// launch) are 64-key pieces of the window [swa_lo, swa_hi): they need no
+// merge and start at once.  A block loads its keys and values into
+// registers with coalesced 16-byte loads (each wave instruction reads 1 KB
+// of consecutive bytes: the gather is bandwidth-bound and cold in cache, so
+// the loads must be whole lines), and a chunk block its landmark row.  The
+// keys go to LDS first (16-byte pieces XOR-swizzled by row, so lane = key
+// reads spread over the banks): wave w takes heads w, w + 4, ...: lane =
+// key for the logits and a softmax over the block's keys, whose weights go
+// to LDS, and for a chunk the head's retrieval score s_h = q . lambda /
+// sqrt(d), for a window piece the log-sum-exp of its logits.  Then the
+// values replace the keys in the same LDS buffer and lane = output columns
+// for the weighted value sum.  One 16 KB buffer (bf16, d = 128) keeps the
+// block at about 19 KB of LDS, so 8 blocks fit on a CU and every block of a
+// batch-32 decode is resident at once.  The normalised outputs go to the
+// partial buffers; fuse_kernel combines them.
 template <int D, int DT>
 __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, float scale) {
   constexpr int EB = DT == kF32 ? 4 : 2;  // bytes per element
@@ -456,8 +460,10 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
   const int K = a.topk;
   uint32_t* qs = (uint32_t*)dyn;
   float* ps = dyn + G * D * EB / 4;
-  const int64_t bg = blockIdx.x / K;
-  const int r = blockIdx.x % K;
+  const int units = K + a.swa_pieces;
+  const int64_t bg = blockIdx.x / units;
+  const int r = blockIdx.x % units;
+  const bool win = r >= K;  // block-uniform
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t qrow0 = (int64_t)((bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G);
   // the group's queries load during the merge (G * D elements, 16 bytes at a time)
@@ -466,31 +472,41 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
   u32x4 qx[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) qx[i] = qg[min(tid + i * kThreads, nq - 1)];
-  if (a.n_avail > 0) {
-    const int got = merge_sorted(a, bg, st.m);
-    if (tid == 0) s_c = r < got ? st.m.order[r] : -1;
-    if (r == 0 && tid < K) a.sel[bg * K + tid] = st.m.order[tid];
+  int64_t row0;  // the block's first key row in the (b, group) cache
+  int nk;        // its keys (1..64)
+  int c = -1;    // chunk blocks: the chunk
+  if (win) {
+    row0 = a.swa_lo + (int64_t)(r - K) * kWave;
+    nk = (int)min((int64_t)kWave, a.swa_hi - row0);
   } else {
-    if (tid == 0) s_c = -1;
-    if (r == 0 && tid < K) a.sel[bg * K + tid] = -1;
+    if (a.n_avail > 0) {
+      const int got = merge_sorted(a, bg, st.m);
+      if (tid == 0) s_c = r < got ? st.m.order[r] : -1;
+      if (r == 0 && tid < K) a.sel[bg * K + tid] = st.m.order[tid];
+    } else {
+      if (tid == 0) s_c = -1;
+      if (r == 0 && tid < K) a.sel[bg * K + tid] = -1;
+    }
+    __syncthreads();
+    c = s_c;
+    if (c < 0) return;  // uniform: rank past the selected chunks
+    row0 = (int64_t)c * a.S;
+    nk = a.S;
   }
-  __syncthreads();
-  const int c = s_c;
-  if (c < 0) return;  // uniform: rank past the selected chunks
-  const int64_t base = (bg * a.n_max + (int64_t)c * a.S) * ROWB;
+  const int64_t base = (bg * a.n_max + row0) * ROWB;
   const char* Kg = (const char*)a.Kc + base;
   const char* Vg = (const char*)a.Vc + base;
-  // rows past the chunk (S < 64) re-read row S - 1; their weights are zero
+  // rows past the block's keys (nk < 64) re-read row nk - 1; their weights are zero
   u32x4 kx[NL], vx[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int e = tid + i * kThreads, row = e / PPR, pc = e % PPR;
-    const int64_t off = (int64_t)min(row, a.S - 1) * ROWB + pc * 16;
+    const int64_t off = (int64_t)min(row, nk - 1) * ROWB + pc * 16;
     kx[i] = *(const u32x4*)(Kg + off);
     vx[i] = *(const u32x4*)(Vg + off);
   }
   f32x4 lx = {0.f, 0.f, 0.f, 0.f};
-  if (tid < D / 4) lx = *(const f32x4*)(a.lmk + (bg * a.lmk_chunks + c) * D + 4 * tid);
+  if (!win && tid < D / 4) lx = *(const f32x4*)(a.lmk + (bg * a.lmk_chunks + c) * D + 4 * tid);
   {
     int m = 0;
     for (int i = tid; i < nq; i += kThreads, ++m)
@@ -504,7 +520,7 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
   }
   if (tid < D / 4) *(f32x4*)(&lam[4 * tid]) = lx;
   __syncthreads();
-  const bool key_ok = lane < a.S;
+  const bool key_ok = lane < nk;
   for (int h = w; h < G; h += kThreads / kWave) {
     // logit of key `lane`
     float acc = 0.f;
@@ -529,18 +545,23 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
     const float lg = key_ok ? acc * scale : -INFINITY;
     const float mx = wave_max_f32(lg);
     const float pe = key_ok ? expf(lg - mx) : 0.f;
-    ps[h * kWave + lane] = pe / wave_sum_f32(pe);
-    // s_h: this lane's landmark columns
-    float sl = 0.f;
+    const float z = wave_sum_f32(pe);
+    ps[h * kWave + lane] = pe / z;
+    if (win) {
+      if (lane == 0) a.sw_lse[(qrow0 + h) * a.swa_pieces + (r - K)] = mx + logf(z);
+    } else {
+      // s_h: this lane's landmark columns
+      float sl = 0.f;
 #pragma unroll
-    for (int x = 0; x < CPL; ++x) {
-      const int col = CPL * lane + x;
-      const float qv = DT == kF32 ? __uint_as_float(qh[col])
-                                  : bf16_bits_to_f32(((const uint16_t*)qh)[col]);
-      sl += qv * lam[col];
+      for (int x = 0; x < CPL; ++x) {
+        const int col = CPL * lane + x;
+        const float qv = DT == kF32 ? __uint_as_float(qh[col])
+                                    : bf16_bits_to_f32(((const uint16_t*)qh)[col]);
+        sl += qv * lam[col];
+      }
+      sl = wave_sum_f32(sl);
+      if (lane == 0) a.part_s[(qrow0 + h) * K + r] = sl * scale;
     }
-    sl = wave_sum_f32(sl);
-    if (lane == 0) a.part_s[(qrow0 + h) * K + r] = sl * scale;
   }
   __syncthreads();
   // the values replace the keys
@@ -573,7 +594,8 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
         }
       }
     }
-    float* po = a.part_o + ((qrow0 + h) * K + r) * D + CPL * lane;
+    float* po = (win ? a.sw_o + ((qrow0 + h) * a.swa_pieces + (r - K)) * D
+                     : a.part_o + ((qrow0 + h) * K + r) * D) + CPL * lane;
     if (CPL == 2)
       *(f32x2*)po = f32x2{o[0], o[CPL - 1]};
     else
@@ -587,7 +609,7 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
 // selected chunk gives zeros.
 template <int D, int DT>
 __global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
-  __shared__ float wts[32 * 32];  // [head of the group][rank]
+  __shared__ float wts[32 * kWave];  // [head of the group][rank or window piece]
   __shared__ int s_got;
   const int64_t bg = blockIdx.x;
   const int G = a.Hq / a.Hkv;
@@ -628,6 +650,34 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) store_elem<DT>(a.o, row * D + 4 * x4 + x, acc[x]);
   }
+  if (a.swa_pieces == 0) return;
+  // the window: a softmax merge of the pieces by their log-sum-exp
+  const int P = a.swa_pieces;  // <= 64
+  __syncthreads();
+  for (int h = w; h < G; h += kThreads / kWave) {
+    const int64_t row = qrow0 + h;
+    const float ls = lane < P ? a.sw_lse[row * P + lane] : -INFINITY;
+    const float mx = wave_max_f32(ls);
+    const float e = lane < P ? expf(ls - mx) : 0.f;
+    const float wk = e / wave_sum_f32(e);
+    if (lane < P) wts[h * kWave + lane] = wk;
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D / 4; e += kThreads) {
+    const int h = e / (D / 4), x4 = e % (D / 4);
+    const int64_t row = qrow0 + h;
+    const float* po = a.sw_o + row * P * D + 4 * x4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int pp = 0; pp < P; ++pp) {
+      const f32x4 v = *(const f32x4*)(po + (int64_t)pp * D);
+      const float wk = wts[h * kWave + pp];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) acc[x] += wk * v[x];
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) store_elem<DT>(a.o_swa, row * D + 4 * x4 + x, acc[x]);
+  }
 }
 
 template <int D, int DT>
@@ -643,8 +693,8 @@ hipError_t stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
     // one block per (b, group, rank)
     const size_t q_lds = (size_t)G * D * (DT == kF32 ? 4 : 2) + (size_t)G * kWave * sizeof(float);
     if (a.S <= kWave)
-      attend_rank_kernel<D, DT><<<dim3((unsigned)(BG * a.topk)), dim3(kThreads), q_lds, stream>>>(
-          a, scale);
+      attend_rank_kernel<D, DT><<<dim3((unsigned)(BG * (a.topk + a.swa_pieces))), dim3(kThreads),
+                                  q_lds, stream>>>(a, scale);
     else
       attend_kernel<D, DT><<<dim3((unsigned)(BG * a.topk)), dim3(kThreads),
                              (size_t)G * D * sizeof(float), stream>>>(a, scale);

@@ -91,11 +91,20 @@ struct DecodeArgs {
   int B, Hq, Hkv, d, S, topk, dtype;
   int64_t n_ctx, n_max, n_avail, lmk_chunks;
   int n_slices, slice;
+  // sliding-window attention of the same query in the same launches (0
+  // pieces: none): keys [swa_lo, swa_hi) of the cache in pieces of 64
+  int swa_pieces;
+  int64_t swa_lo, swa_hi;
+  void* o_swa;         // [B,Hq,d]
+  float* sw_o;         // [B,Hq,swa_pieces,d]: each piece's normalised output
+  float* sw_lse;       // [B,Hq,swa_pieces]: natural log-sum-exp of its logits
 };
 void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* slice);
 // stages: 0 scan (landmark stream + per-slice top-K), 1 attend (merge of the
-// slices' candidates, then one block per selected chunk), 2 fuse (softmax
-// over the chunks' retrieval scores, weighted sum of the chunk outputs)
+// slices' candidates, then one block per selected chunk; with swa_pieces
+// also one block per window piece), 2 fuse (softmax over the chunks'
+// retrieval scores, weighted sum of the chunk outputs; the window pieces'
+// softmax merge)
 constexpr int kDecodeStages = 3;
 hipError_t decode_stage(const DecodeArgs& a, int stage, hipStream_t stream);
 int64_t decode_max_chunks(int topk);

@@ -311,13 +311,39 @@ hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t p
                         hsa_dtype_t dtype, hsa_stream_t stream);
 
 /*
+ * The upper layers' two attentions of one new query in one pass ([HSA]
+ * Methodology: upper layers pair local sliding-window self-attention with
+ * the HSA module): HSA decode (as hsa_decode: the query at position n_ctx
+ * retrieves among the floor(n_ctx/S) complete chunks) and sliding-window
+ * attention over the cache keys max(0, n_ctx-W+1) .. n_ctx (as swa_decode
+ * with pos = n_ctx), written to two outputs.  The window's 64-key pieces
+ * run as blocks of the same attention launch as the selected chunks (they
+ * need no selection, so they start at once), and the fusion launch also
+ * merges the pieces; the combination of the two outputs is the caller's
+ * (the pages give no formula for it).
+ *   q [B,Hq,d]; Kc, Vc [B,Hkv,n_max,d] holding tokens 0..n_ctx (n_ctx <
+ *   n_max); lmk fp32 [B,Hkv,n_max/S,d]; o_hsa, o_swa [B,Hq,d] written;
+ *   sel_idx, sel_w as in hsa_decode.
+ * Limits: as hsa_decode, plus S <= 64 and min(window, n_ctx+1) <= 4096
+ * (HSA_ERR_UNSUPPORTED otherwise).  Profiling stages: 0 scan, 1 attend
+ * (chunks and window pieces), 2 fuse (both outputs).
+ */
+size_t hsa_swa_decode_workspace_size(int B, int Hq, int Hkv, int d, int S, int topk,
+                                     int64_t n_ctx, int64_t window);
+hsa_status_t hsa_swa_decode(const void* q, const void* Kc, const void* Vc, const float* lmk,
+                            int64_t n_ctx, int64_t n_max, int64_t window, void* o_hsa,
+                            void* o_swa, int32_t* sel_idx, float* sel_w, int B, int Hq, int Hkv,
+                            int d, int S, int topk, hsa_dtype_t dtype, void* workspace,
+                            size_t workspace_bytes, hsa_stream_t stream);
+
+/*
  * Profiling aid (not part of the method).  While enabled on the calling
  * thread, each call of the entry points below records a HIP
  * event on its stream before each of its stages and one after the last:
  *   hsa_prefill : 0 landmarks, 1 select, 2 invert, 3 attend, 4 fuse
  *   hsa_decode  : 0 scan (landmark stream, per-slice top-K), 1 attend (merge
- *                 of the slices' candidates, chunk attention; also the
- *                 fusion when S <= 64 and topk <= 8), 2 fuse (then empty)
+ *                 of the slices' candidates, one block per selected chunk),
+ *                 2 fuse (softmax over the retrieval scores, weighted sum)
  *   dhsa_prefill: 0 pool, 1 S_c, 2 rank, 3 attend, 4 mask
  *   dhsa_decode : 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
  *   swa_prefill, swa_decode: 0 attend

@@ -274,3 +274,22 @@ def test_backward_validation():
     assert lib().hsa_prefill_backward_workspace_size(1, 256, 4, 2, 128, 64, 8, F32) == 0
     assert lib().hsa_prefill_backward_workspace_size(1, 256, 4, 2, 128, 128, 8, BF16) == 0
     assert backward_call(B=0) == hsa.HSA_OK
+
+
+def test_hsa_swa_decode_validation():
+    def call(**kw):
+        a = dict(n_ctx=1000, n_max=2000, W=512, B=1, Hq=4, Hkv=2, d=128, S=64, K=8, dt=BF16,
+                 ws=None, wsb=0, o=1)
+        a.update(kw)
+        return lib().hsa_swa_decode(1, 1, 1, 1, a["n_ctx"], a["n_max"], a["W"], a["o"], a["o"],
+                                    None, None, a["B"], a["Hq"], a["Hkv"], a["d"], a["S"], a["K"],
+                                    a["dt"], a["ws"], a["wsb"], None)
+    assert call(S=128) == UNS
+    assert call(W=5000, n_ctx=8000, n_max=9000) == UNS
+    assert call(W=0) == INV
+    assert call(n_ctx=2000) == INV
+    assert call(Hq=3) == INV
+    assert call(o=None) == INV
+    assert call() == WS and "workspace needs" in msg()
+    assert lib().hsa_swa_decode_workspace_size(1, 4, 2, 128, 64, 8, 1000, 512) > \
+        lib().hsa_decode_workspace_size(1, 4, 2, 128, 64, 8, 1000)
