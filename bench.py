@@ -537,6 +537,53 @@ def bench_swa_decode(torch, hsa, args, W=512):
     return res
 
 
+def bench_upper_prefill(torch, hsa, args, inputs, W=512):
+    """The upper layers' two attentions over the 32K prefill workload in one
+    pass (hsa_swa_prefill): HSA prefill and 512-token sliding-window
+    attention of the same Q, K, V, their attention blocks in one launch.  The
+    same two outputs from separate hsa_prefill and swa_prefill calls are
+    timed beside it."""
+    Q, K, V, S, topk = inputs
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    q, k, v = to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch)
+    oh, osw = torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(hsa.hsa_prefill_workspace_size(B, L, Hq, Hkv, d, S, topk, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        hsa.hsa_swa_prefill(q, k, v, S, topk, W, out_hsa=oh, out_swa=osw, workspace=ws)
+
+    def separate():
+        hsa.hsa_prefill(q, k, v, S, topk, out=oh, workspace=ws)
+        hsa.swa_prefill(q, k, v, W, out=osw)
+
+    log(f"upper-layer prefill (W={W}): timing")
+    t = time_steps(torch, hsa, step, args.steps, args.warmup, 5, args.flush)
+    ms, stages = t["ms"], t["stage_mean"]
+    t_sep = time_steps(torch, hsa, separate, args.steps, args.warmup, 6, args.flush)
+    sel, _ = prefill_counts(L, S, topk)
+    hsa_flop = B * Hq * sel * S * d * 4
+    swa_flop = B * Hq * sum(min(W, t_ + 1) for t_ in range(L)) * d * 4
+    flop = hsa_flop + swa_flop
+    achieved = flop / (stages[3] * 1e-3) / 1e12
+    res = dict(
+        value=B * L / (ms * 1e-3), unit="queries/s", ms_per_step=ms,
+        config={"workload": "hsa_swa_prefill", "B": B, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d,
+                "S": S, "topk": topk, "window": W, "inputs": "0.5*N(0,1) bf16, seed 2"},
+        roofline={"bound": "mfma", "kernel": "attend (HSA chunk attention and sliding-window "
+                                             "attention in one launch, bf16 MFMA)",
+                  "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                  "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                  "algorithmic_gflop_per_launch": flop / 1e9, "avg_launch_ms": stages[3]},
+        stages_ms=dict(zip(["landmarks", "select", "invert", "attend", "fuse"], stages)),
+        separate_calls_ms=t_sep["ms"])
+    add_timing(res, t, 3)
+    del q, k, v, oh, osw, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_upper_decode(torch, hsa, args, W=512):
     """The upper layers' two attentions of one new query in one pass
     (hsa_swa_decode): HSA decode and 512-token sliding-window decode at the
@@ -777,9 +824,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extras", default="prefill_r8,backward,decode,decode16m,dhsa,dhsa_decode,"
-                                        "swa,swa_decode,upper_decode",
+                                        "swa,swa_decode,upper_prefill,upper_decode",
                     help="comma list of extra workloads: prefill_r8, backward, decode, "
-                         "decode16m, dhsa, dhsa_decode, swa, swa_decode, upper_decode, or none")
+                         "decode16m, dhsa, dhsa_decode, swa, swa_decode, upper_prefill, "
+                         "upper_decode, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -845,6 +893,8 @@ def main():
             also.append(bench_swa(torch, hsa, args, inputs))
         elif e == "swa_decode":
             also.append(bench_swa_decode(torch, hsa, args))
+        elif e == "upper_prefill":
+            also.append(bench_upper_prefill(torch, hsa, args, inputs))
         elif e == "upper_decode":
             also.append(bench_upper_decode(torch, hsa, args))
         else:

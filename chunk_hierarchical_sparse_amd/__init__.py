@@ -17,7 +17,7 @@ from . import build as _build
 __all__ = [
     "HsaError", "hsa_status_string", "hsa_build_landmarks", "hsa_prefill",
     "hsa_prefill_workspace_size", "hsa_decode", "hsa_decode_workspace_size",
-    "hsa_decode_noalloc", "HSA_DECODE_NOALLOC_SCRATCH_BYTES", "hsa_swa_decode",
+    "hsa_decode_noalloc", "HSA_DECODE_NOALLOC_SCRATCH_BYTES", "hsa_swa_decode", "hsa_swa_prefill",
     "hsa_swa_decode_workspace_size",
     "hsa_prefill_interval", "hsa_prefill_interval_workspace_size", "hsa_prefill_backward",
     "hsa_prefill_backward_workspace_size", "dhsa_prefill",
@@ -81,6 +81,8 @@ def load_library():
         "hsa_decode_noalloc": ([_P, _P, _P, _P, _L, _L, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                 _P], _I),
         "hsa_swa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _L, _L], _Z),
+        "hsa_swa_prefill": ([_P, _P, _P, _P, _L, _P, _P, _P, _P, _I, _L, _I, _I, _I, _I, _I, _I,
+                             _P, _Z, _P], _I),
         "hsa_swa_decode": ([_P, _P, _P, _P, _L, _L, _L, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                             _I, _P, _Z, _P], _I),
         "dhsa_prefill_workspace_size": ([_I, _L, _I, _I, _I, _I], _Z),
@@ -315,6 +317,40 @@ def hsa_decode_noalloc(q, Kc, Vc, lmk, n_ctx, S, topk, out, sel_idx=None, sel_w=
                                              _ptr(sel_idx), _ptr(sel_w), B, Hq, Hkv, d, S, topk,
                                              _dtype_code(q), _stream(q)))
     return out
+
+
+def hsa_swa_prefill(Q, K, V, S, topk, window, lmk=None, out_hsa=None, out_swa=None,
+                    return_selection=False, workspace=None):
+    """HSA prefill and sliding-window prefill of the same Q [B,Hq,L,d], K, V
+    [B,Hkv,L,d] in one pass (one attention launch for both when bf16 and
+    S <= 64).  Returns (O_hsa, O_swa), plus sel_idx, sel_w with
+    return_selection.  The workspace is hsa_prefill's."""
+    _need(Q, "Q", 4)
+    _need(K, "K", 4, Q.dtype)
+    _need(V, "V", 4, Q.dtype)
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    if K.shape != (B, Hkv, L, d) or V.shape != K.shape:
+        raise ValueError("K and V must be [B,Hkv,L,d] matching Q")
+    if lmk is not None:
+        _need(lmk, "lmk", 4, torch.float32)
+    out_hsa = torch.empty_like(Q) if out_hsa is None else out_hsa
+    out_swa = torch.empty_like(Q) if out_swa is None else out_swa
+    sel_idx = sel_w = None
+    if return_selection:
+        sel_idx = torch.empty((B, Hkv, L, topk), dtype=torch.int32, device=Q.device)
+        sel_w = torch.empty((B, Hq, L, topk), dtype=torch.float32, device=Q.device)
+    lib = load_library()
+    code = _dtype_code(Q)
+    nbytes = lib.hsa_prefill_workspace_size(B, L, Hq, Hkv, d, S, topk, code)
+    ws = _workspace(nbytes, Q.device, workspace) if nbytes else None
+    _check(lib.hsa_swa_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _ptr(lmk), window,
+                               out_hsa.data_ptr(), out_swa.data_ptr(), _ptr(sel_idx),
+                               _ptr(sel_w), B, L, Hq, Hkv, d, S, topk, code, _ptr(ws), nbytes,
+                               _stream(Q)))
+    if return_selection:
+        return out_hsa, out_swa, sel_idx, sel_w
+    return out_hsa, out_swa
 
 
 def hsa_swa_decode_workspace_size(B, Hq, Hkv, d, S, topk, n_ctx, window):

@@ -16,7 +16,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "landmarks.hip", "prefill.hip", "decode.hip", "dhsa.hip", "dhsa_decode.hip",
-           "swa.hip", "prefill_bwd.hip", "decode_noalloc.hip"]
+           "swa.hip", "prefill_bwd.hip", "decode_noalloc.hip",
+           "upper.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,

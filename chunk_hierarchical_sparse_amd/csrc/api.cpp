@@ -896,6 +896,71 @@ hsa_status_t swa_prefill(const void* Q, const void* K, const void* V, void* O, i
   return HSA_OK;
 }
 
+hsa_status_t hsa_swa_prefill(const void* Q, const void* K, const void* V, const float* lmk,
+                             int64_t window, void* O_hsa, void* O_swa, int32_t* sel_idx,
+                             float* sel_w, int B, int64_t L, int Hq, int Hkv, int d, int S,
+                             int topk, hsa_dtype_t dtype, void* workspace,
+                             size_t workspace_bytes, hsa_stream_t stream) {
+  g_err.clear();
+  hsa_status_t s = check_prefill(B, L, Hq, Hkv, d, S, topk, dtype);
+  if (s != HSA_OK) return s;
+  if ((s = check_swa(B, Hq, Hkv, d, window, dtype)) != HSA_OK) return s;
+  if ((int64_t)B * Hq * L >= (int64_t(1) << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "B*Hq*L must be < 2^31");
+  if (B == 0 || L == 0) return HSA_OK;
+  if (!Q || !K || !V || !O_hsa || !O_swa)
+    return fail(HSA_ERR_INVALID_ARGUMENT, "Q, K, V, O_hsa and O_swa must not be NULL");
+  const size_t need = prefill_layout(nullptr, B, L, Hq, Hkv, d, S, topk, dtype).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(HSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(need) + " bytes");
+  PrefillLayout lay = prefill_layout(align_ws(workspace), B, L, Hq, Hkv, d, S, topk, dtype);
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t n = L / S;
+  hsa::PrefillArgs a = prefill_args(lay, Q, K, V, lmk, O_hsa, sel_idx, sel_w, B, L, Hq, Hkv, d,
+                                    S, topk, 1, dtype);
+  if ((int64_t)B * Hkv * a.tiles_ub >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
+  hsa::SwaArgs w;
+  w.Q = Q;
+  w.K = K;
+  w.V = V;
+  w.O = O_swa;
+  w.B = B;
+  w.Hq = Hq;
+  w.Hkv = Hkv;
+  w.d = d;
+  w.dtype = dt_code(dtype);
+  w.L = L;
+  w.window = window;
+  w.n_ctx = 0;
+  // one launch for both attentions: bf16 with chunks of at most 64 keys;
+  // otherwise the two run as consecutive launches
+  const bool fused = dtype == HSA_DTYPE_BF16 && S <= 64;
+  hipError_t e;
+  StageMarks pm(st);
+  pm.mark();
+  if (!lmk && n > 0) {
+    e = hsa::launch_landmarks(K, a.dtype, lay.lmk, (int64_t)B * Hkv, L, n, d, S, 0, n, st);
+    if (e != hipSuccess) return hip_fail(e, "landmarks");
+  }
+  pm.mark();
+  if ((e = hsa::prefill_select(a, st)) != hipSuccess) return hip_fail(e, "select");
+  pm.mark();
+  if ((e = hsa::prefill_invert(a, st)) != hipSuccess) return hip_fail(e, "invert");
+  pm.mark();
+  if (fused) {
+    if ((e = hsa::launch_upper_attend(a, w, st)) != hipSuccess) return hip_fail(e, "attend");
+  } else {
+    if ((e = hsa::prefill_attend(a, st)) != hipSuccess) return hip_fail(e, "attend");
+    if ((e = hsa::launch_swa_prefill(w, st)) != hipSuccess) return hip_fail(e, "swa");
+  }
+  pm.mark();
+  if ((e = hsa::prefill_fuse(a, st)) != hipSuccess) return hip_fail(e, "fuse");
+  pm.mark();
+  return HSA_OK;
+}
+
 hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t pos,
                         int64_t n_max, int64_t window, void* o, int B, int Hq, int Hkv, int d,
                         hsa_dtype_t dtype, hsa_stream_t stream) {

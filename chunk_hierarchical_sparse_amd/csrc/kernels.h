@@ -193,4 +193,8 @@ struct SwaArgs {
 hipError_t launch_swa_prefill(const SwaArgs& a, hipStream_t stream);
 hipError_t launch_swa_decode(const SwaArgs& a, hipStream_t stream);
 
+// ---- upper layers: HSA chunk attention and sliding-window prefill in one
+// launch (upper.hip); bf16, chunks of at most 64 keys, the same Q/K/V -------
+hipError_t launch_upper_attend(const PrefillArgs& pa, const SwaArgs& sa, hipStream_t stream);
+
 }  // namespace hsa

@@ -24,11 +24,11 @@ __device__ __forceinline__ int64_t partial_row(const PrefillArgs& a, int64_t bg,
 // group) pairs (b, group = fastest index) and walk each pair's work units in
 // chunk order, so the early, most-selected chunks start first.  Returns false
 // for blocks past the last unit of their (b, group).
-__device__ __forceinline__ bool locate_tile(const PrefillArgs& a, int64_t& bg, int& c, int& e0,
-                                            int& e1) {
+__device__ __forceinline__ bool locate_tile(const PrefillArgs& a, int64_t blk, int64_t& bg,
+                                            int& c, int& e0, int& e1) {
   const int64_t BG = (int64_t)a.B * a.Hkv;
-  bg = blockIdx.x % BG;
-  const int64_t tile = blockIdx.x / BG;
+  bg = blk % BG;
+  const int64_t tile = blk / BG;
   const int32_t* toff = a.tile_off + bg * (a.n + 1);
   if (tile >= toff[a.n]) return false;
   c = a.tile_chunk[bg * a.tiles_ub + tile];
@@ -36,6 +36,11 @@ __device__ __forceinline__ bool locate_tile(const PrefillArgs& a, int64_t& bg, i
   e0 = offs[c] + (int)(tile - toff[c]) * a.entries_per_tile;
   e1 = min(e0 + a.entries_per_tile, offs[c + 1]);
   return true;
+}
+
+__device__ __forceinline__ bool locate_tile(const PrefillArgs& a, int64_t& bg, int& c, int& e0,
+                                            int& e1) {
+  return locate_tile(a, (int64_t)blockIdx.x, bg, c, e0, e1);
 }
 
 }  // namespace hsa

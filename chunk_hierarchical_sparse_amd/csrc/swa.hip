@@ -22,6 +22,7 @@
 #include "attn_core.h"
 #include "hsa_common.h"
 #include "kernels.h"
+#include "swa_core.h"
 
 namespace hsa {
 namespace {
@@ -36,70 +37,8 @@ int heads_per_block(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 template <int D, int GT>
 __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(SwaArgs a, float scale_log2,
                                                                    int64_t n_units) {
-  constexpr int MQ = 32 * 4 / GT;  // positions per block
   __shared__ KVSmemWide<D> sm;
-  // block i runs on XCD i % 8; XCD x takes units [x * per, (x + 1) * per)
-  const int64_t per = (n_units + kXcds - 1) / kXcds;
-  const int64_t unit = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  if (unit >= n_units) return;
-  const int G = a.Hq / a.Hkv;
-  const int64_t P = (a.L + MQ - 1) / MQ;
-  const int64_t grp = unit / P;  // (b, g, head block)
-  const int64_t t0 = (unit % P) * MQ;
-  const int nhb = G / GT;
-  const int64_t bg = grp / nhb;
-  const int hb = (int)(grp % nhb);
-  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = g * G + hb * GT + w % GT;
-  // positions in 32 bits (B * Hq * L < 2^31 is checked on the host); a
-  // window reaching past the sequence start is the whole prefix
-  const int Li = (int)a.L, W = (int)min(a.window, a.L);
-  const int tb = (int)t0;
-  const int t = tb + (w / GT) * 32 + (lane & 31);
-  const bool valid = t < Li;
-  const uint16_t* Kb = (const uint16_t*)a.K + bg * a.L * D;
-  const uint16_t* Vb = (const uint16_t*)a.V + bg * a.L * D;
-  WaveAttn<D> st;
-  wave_attn_init<D>(st, (const uint16_t*)a.Q + (((int64_t)b * a.Hq + h) * a.L + min(t, Li - 1)) * D,
-                    valid);
-  const int t_end = min(Li, tb + MQ);
-  const int k_lo = max(0, tb - W + 1);
-  KVRegsWide<D> rg;
-  fetch_kv_wide<D>(rg, Kb + (int64_t)k_lo * D, Vb + (int64_t)k_lo * D,
-                   min(kWideBlock, t_end - k_lo));
-  for (int kb = k_lo; kb < t_end; kb += kWideBlock) {
-    const int nk = min(kWideBlock, t_end - kb);
-    __syncthreads();
-    store_kv_wide<D>(sm, rg, nk);
-    __syncthreads();
-    const int nkb = kb + kWideBlock;
-    if (nkb < t_end)
-      fetch_kv_wide<D>(rg, Kb + (int64_t)nkb * D, Vb + (int64_t)nkb * D,
-                       min(kWideBlock, t_end - nkb));
-    __builtin_amdgcn_sched_barrier(0);
-    // this lane's keys in the block: [lo, hi) in-block indices.  t - kb lies
-    // in (-128, 2^31); lo = t - kb - (W - 1) clamped to [-1, 129], the
-    // difference taken unsigned so the branch not chosen cannot overflow
-    const int dk = t - kb;
-    const int hi = valid ? min(nk, dk + 1) : 0;
-    const int lo = dk >= W - 1 ? min(kWideBlock + 1, (int)((unsigned)dk - (unsigned)(W - 1))) : -1;
-    if (__ballot(hi > 0 && hi > lo) != 0)
-      wave_attn_wide<D, 4, true>(st, sm, nk, max(hi, 0), scale_log2, lo);
-  }
-  if (!valid) return;
-  const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-  uint16_t* orow = (uint16_t*)a.O + (((int64_t)b * a.Hq + h) * a.L + t) * D;
-  const int hf = lane >> 5;
-#pragma unroll
-  for (int bb = 0; bb < D / 32; ++bb)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int dd = 32 * bb + 8 * q4 + 4 * hf;
-      const u32x2 v = {pack_bf16x2(st.o[bb][4 * q4] * inv, st.o[bb][4 * q4 + 1] * inv),
-                       pack_bf16x2(st.o[bb][4 * q4 + 2] * inv, st.o[bb][4 * q4 + 3] * inv)};
-      *(u32x2*)(orow + dd) = v;
-    }
+  swa_prefill_body<D, GT>(a, scale_log2, n_units, blockIdx.x, sm);
 }
 
 // fp32: lane = (b, head, position), positions fastest.

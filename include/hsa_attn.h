@@ -311,6 +311,28 @@ hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t p
                         hsa_dtype_t dtype, hsa_stream_t stream);
 
 /*
+ * The upper layers' two attentions over a whole sequence ([HSA]
+ * Methodology: upper layers pair local sliding-window self-attention, 512
+ * tokens by default, with the HSA module): hsa_prefill's output O_hsa and
+ * swa_prefill's output O_swa of the same Q, K, V.  After HSA's landmark,
+ * selection and list stages, one launch runs both HSA's chunk attention and
+ * the sliding-window attention (the HSA blocks move partial outputs and
+ * gathered query rows; the window blocks are bound by MFMA issue and softmax
+ * arithmetic; sharing the launch overlaps the two); then HSA's fusion.  The
+ * combination of the two outputs is the caller's (the pages give no formula).
+ *   Arguments as hsa_prefill plus window (>= 1) and O_swa [B,Hq,L,d];
+ *   workspace of hsa_prefill_workspace_size(...) bytes.
+ * The single launch needs bf16 and S <= 64; otherwise the two attentions run
+ * as consecutive launches (same results).  Profiling stages: 0 landmarks,
+ * 1 select, 2 invert, 3 attend (both), 4 fuse.
+ */
+hsa_status_t hsa_swa_prefill(const void* Q, const void* K, const void* V, const float* lmk,
+                             int64_t window, void* O_hsa, void* O_swa, int32_t* sel_idx,
+                             float* sel_w, int B, int64_t L, int Hq, int Hkv, int d, int S,
+                             int topk, hsa_dtype_t dtype, void* workspace,
+                             size_t workspace_bytes, hsa_stream_t stream);
+
+/*
  * The upper layers' two attentions of one new query in one pass ([HSA]
  * Methodology: upper layers pair local sliding-window self-attention with
  * the HSA module): HSA decode (as hsa_decode: the query at position n_ctx

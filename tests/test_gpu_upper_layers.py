@@ -70,3 +70,60 @@ def test_hsa_swa_decode_rejects_what_it_cannot_run():
         hsa.hsa_swa_decode(q, Kc, Kc, lmk64, 8000, 64, 8, 5000)
     with pytest.raises(hsa.HsaError):  # the new token must be in the cache
         hsa.hsa_swa_decode(q, Kc, Kc, lmk64, 9000, 64, 8, 512)
+
+
+def run_prefill_case(B, Hq, Hkv, L, d, S, K, W, dt, seed, scale=1.0):
+    say(f"hsa+swa prefill B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} S={S} K={K} W={W} {dt}")
+    Q, Kx, V = (gen((B, H, L, d), dt, seed, t, scale)
+                for H, t in ((Hq, synth.TID_Q), (Hkv, synth.TID_K), (Hkv, synth.TID_V)))
+    qd, kd, vd = dev(Q), dev(Kx), dev(V)
+    oh, osw, sel, w = hsa.hsa_swa_prefill(qd, kd, vd, S, K, W, return_selection=True)
+    ref_h, ref_sel, ref_w = hsa.hsa_prefill(qd, kd, vd, S, K, return_selection=True)
+    ref_s = hsa.swa_prefill(qd, kd, vd, W)
+    torch.cuda.synchronize()
+    # the same kernels as the separate calls: the same bits
+    view = (lambda t: t.view(torch.int16)) if dt == "bf16" else (lambda t: t)
+    assert torch.equal(view(oh), view(ref_h)), "HSA output differs from hsa_prefill"
+    assert torch.equal(view(osw), view(ref_s)), "window output differs from swa_prefill"
+    assert torch.equal(sel, ref_sel) and torch.equal(w, ref_w)
+    r = oracle.hsa_prefill(Q, Kx, V, S, K)
+    ok = r["margin"] > MARGIN
+    check_exempt(ok, "hsa+swa prefill rows")
+    same = (np.sort(host(sel), -1) == np.sort(r["sel"], -1)).all(-1) | ~ok
+    assert same.all(), "selection differs above the margin"
+    okh = np.repeat(ok, Hq // Hkv, axis=1)
+    err_h = check_out(host(oh)[okh], r["out"][okh], dt, "hsa output")
+    err_s = check_out(host(osw), oracle.swa_prefill(Q, Kx, V, W), dt, "swa output")
+    say(f"  ok: hsa err {err_h:.3g}, swa err {err_s:.3g}")
+
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, L, d, S, K, W, dtype
+    (1, 16, 4, 2000, 128, 64, 8, 512, "bf16"),  # the upper-layer shapes (one launch)
+    (2, 8, 8, 777, 64, 32, 4, 100, "bf16"),     # 32-key chunks, no grouping
+    (1, 6, 2, 513, 128, 16, 8, 33, "bf16"),     # groups of 3 heads: one head per window block
+    (1, 4, 1, 300, 128, 64, 4, 1, "bf16"),      # a window of one key
+    (1, 4, 2, 50, 128, 64, 4, 512, "bf16"),     # shorter than a chunk: window blocks only
+    (1, 4, 2, 600, 128, 100, 4, 200, "bf16"),   # 100-key chunks: two launches
+    (2, 4, 2, 400, 64, 64, 4, 64, "f32"),       # fp32: two launches
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[str(i) for i in range(len(PREFILL_CASES))])
+def test_hsa_swa_prefill(case):
+    run_prefill_case(*case, seed=640 + PREFILL_CASES.index(case))
+
+
+def test_hsa_swa_prefill_32k_workload_equals_separate_calls():
+    # the 32K GQA bf16 sequence, 512-token window: bit for bit the separate calls
+    B, Hq, Hkv, L, d, S, K, W = 1, 16, 4, 32768, 128, 64, 8, 512
+    say("hsa+swa prefill 32K")
+    Q, Kx, V = (gen((B, H, L, d), "bf16", 2, t, 0.5)
+                for H, t in ((Hq, synth.TID_Q), (Hkv, synth.TID_K), (Hkv, synth.TID_V)))
+    qd, kd, vd = dev(Q), dev(Kx), dev(V)
+    oh, osw = hsa.hsa_swa_prefill(qd, kd, vd, S, K, W)
+    ref_h = hsa.hsa_prefill(qd, kd, vd, S, K)
+    ref_s = hsa.swa_prefill(qd, kd, vd, W)
+    torch.cuda.synchronize()
+    assert torch.equal(oh.view(torch.int16), ref_h.view(torch.int16))
+    assert torch.equal(osw.view(torch.int16), ref_s.view(torch.int16))
