@@ -36,11 +36,11 @@ METRIC = "HSA queries/sec + achieved HBM GB/s (decode) / MFMA util (prefill), 1 
 # --summarize-counters into TRAFFIC_FILE; it is reported only while these
 # sources hash the same as when the counters were taken.
 CSRC = os.path.join(ROOT, "chunk_hierarchical_sparse_amd", "csrc")
+PREFILL_SRC = ["prefill.hip", "chunk_attend.h", "prefill_common.h", "attn_core.h", "hsa_common.h",
+               "kernels.h"]
 DOMINANT = {
-    "hsa_prefill": ("attend_chunk_bf16_kernel<128, true>", "PrefillArgs",
-                    ["prefill.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
-    "hsa_prefill_r8": ("attend_chunk_bf16_kernel<128, true>", "PrefillArgs",
-                       ["prefill.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
+    "hsa_prefill": ("attend_chunk_bf16_kernel<128, true>", "PrefillArgs", PREFILL_SRC),
+    "hsa_prefill_r8": ("attend_chunk_bf16_kernel<128, true>", "PrefillArgs", PREFILL_SRC),
     "hsa_decode": ("scan_kernel<128, 1>", "DecodeArgs",
                    ["decode.hip", "hsa_common.h", "kernels.h"]),
     "hsa_decode_16m": ("scan_kernel<128, 1>", "DecodeArgs",
@@ -53,32 +53,74 @@ DOMINANT = {
                              ["prefill_bwd.hip", "prefill_common.h", "attn_core.h",
                               "hsa_common.h", "kernels.h"]),
     "swa_prefill": ("prefill_bf16_kernel<128, 4>", "SwaArgs",
-                    ["swa.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
+                    ["swa.hip", "swa_core.h", "attn_core.h", "hsa_common.h", "kernels.h"]),
     "swa_decode": ("decode_kernel<128, 1, 4>", "SwaArgs",
                    ["swa.hip", "hsa_common.h", "kernels.h"]),
+    "hsa_swa_prefill": ("upper_attend_kernel<128, true, 4>", "PrefillArgs",
+                        ["upper.hip", "chunk_attend.h", "swa_core.h", "prefill_common.h",
+                         "attn_core.h", "hsa_common.h", "kernels.h"]),
+}
+# Other kernels whose HBM traffic the counter summary records per workload
+# (name, argument struct, sources): the prefill fusion, for the traffic floor
+# of the chunk-major schedule.
+SECONDARY = {
+    "hsa_prefill": ("fuse_kernel<128, 1, 8>", "PrefillArgs", PREFILL_SRC),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_workloads.txt")
 
 
-def sources_sha1(workload):
+SQ_FILE = os.path.join(ROOT, "profiles", "sq_counters_bench_workloads.txt")
+
+
+def sources_sha1(workload, table=None):
     import hashlib
     h = hashlib.sha1()
-    for f in DOMINANT[workload][2]:
+    for f in (table or DOMINANT)[workload][2]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
+def _profile_record(path, key, workload):
+    """The record of `workload` under `key` in a committed profile summary
+    (JSON after '#' comment lines), or None when absent or taken on other
+    sources."""
+    try:
+        with open(path) as fh:
+            body = "".join(l for l in fh if not l.lstrip().startswith("#"))
+        rec = json.loads(body)[key][workload]
+    except (OSError, ValueError, KeyError, TypeError):
+        return None
+    return rec if rec.get("sources_sha1") == sources_sha1(workload) else None
+
+
+def mfma_busy_for(workload):
+    """MFMA-busy and VALU-busy percentages and executed / algorithmic MFMA
+    flops of the workload's dominant kernel from the SQ counter summary, or
+    None when absent or taken on other sources."""
+    rec = _profile_record(SQ_FILE, "workloads", workload)
+    if rec is None:
+        return None
+    return {k: rec[k] for k in ("mfma_busy_pct", "valu_busy_pct", "executed_over_algorithmic")}
+
+
 def traffic_for(workload):
     """HBM bytes per launch of the workload's dominant kernel from the
     counter summary, or None when absent or taken on other sources."""
+    rec = _profile_record(TRAFFIC_FILE, "workloads", workload)
+    return None if rec is None else rec["traffic_bytes"]
+
+
+def secondary_traffic_for(workload):
+    """HBM bytes per launch of the workload's secondary kernel (SECONDARY),
+    or None."""
     try:
         with open(TRAFFIC_FILE) as fh:
             body = "".join(l for l in fh if not l.lstrip().startswith("#"))
-        rec = json.loads(body)["workloads"][workload]
-    except (OSError, ValueError, KeyError):
+        rec = json.loads(body)["secondary"][workload]
+    except (OSError, ValueError, KeyError, TypeError):
         return None
-    if rec.get("sources_sha1") != sources_sha1(workload):
+    if rec.get("sources_sha1") != sources_sha1(workload, SECONDARY):
         return None
     return rec["traffic_bytes"]
 
@@ -169,10 +211,35 @@ def time_steps(torch, hsa, step, steps, warmup, n_stages, flush):
 def add_timing(res, t, stage):
     """Adds the mean step time and the dominant kernel's median launch time
     (stage `stage`) beside the median step time and mean launch time the
-    record already holds."""
+    record already holds, and for MFMA-bound kernels the SQ counters'
+    MFMA-busy corroboration."""
     res["ms_per_step_mean"] = t["ms_mean"]
     res["roofline"]["median_launch_ms"] = t["stage_median"][stage]
+    if res["roofline"]["bound"] == "mfma":
+        res["roofline"]["mfma_busy"] = mfma_busy_for(res["config"]["workload"])
     return res
+
+
+def measure_copy_rate(torch, flush, reps=5):
+    """Bytes moved per second (read + write) by a plain 1 GiB device copy,
+    median of `reps`, each after a cache flush: the rate the traffic floor is
+    priced at."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / (_median(ts) * 1e-3)
 
 
 def prefill_counts(L, S, topk):
@@ -184,6 +251,61 @@ def prefill_counts(L, S, topk):
         avail += a
         sel += min(topk, a)
     return sel, avail
+
+
+def gather_probe(torch, Kc, Vc, S, n, flush, reps=5):
+    """The decode gather at the memory-system level: torch's row gather of n
+    random S-key chunks (16 KB each at d = 128, bf16) from each of the two
+    caches, after a cache flush (median of reps), beside a contiguous copy
+    of the same number of bytes.  Random chunks spread over 8 GiB caches
+    touch a new memory page each, which the contiguous copy does not."""
+    rk, rv = Kc.view(-1, S * Kc.shape[-1]), Vc.view(-1, S * Vc.shape[-1])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    idx = torch.randint(0, rk.shape[0], (n,), device="cuda", generator=gen)
+    gk = torch.empty((n, rk.shape[1]), dtype=rk.dtype, device="cuda")
+    gv = torch.empty_like(gk)
+    src = rk[:n]
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return _median(ts)
+
+    def g():
+        torch.index_select(rk, 0, idx, out=gk)
+        torch.index_select(rv, 0, idx, out=gv)
+
+    def c():
+        gk.copy_(src)
+        gv.copy_(rv[:n])
+
+    g()
+    c()
+    tg, tc = timed(g), timed(c)
+    nbytes = 2 * gk.numel() * gk.element_size()
+    del gk, gv, idx
+    return {"chunks": 2 * n, "bytes_read": nbytes, "random_gather_ms": tg,
+            "random_gather_GBps": nbytes / (tg * 1e-3) / 1e9, "contiguous_copy_ms": tc,
+            "contiguous_copy_GBps": nbytes / (tc * 1e-3) / 1e9}
+
+
+def prefill_traffic_floor(copy_rate, attend_fuse_ms):
+    """The chunk-major schedule's traffic floor: the HBM bytes its attention
+    and fusion kernels move per call (counter summary) priced at the plain
+    copy rate measured in this run, beside their measured time."""
+    ta, tf = traffic_for("hsa_prefill"), secondary_traffic_for("hsa_prefill")
+    if ta is None or tf is None:
+        return None
+    return {"attend_bytes": ta, "fuse_bytes": tf, "copy_GBps": copy_rate / 1e9,
+            "floor_ms": (ta + tf) / copy_rate * 1e3, "attend_plus_fuse_ms": attend_fuse_ms}
 
 
 # ---------------------------------------------------------------- workloads
@@ -224,6 +346,7 @@ def bench_prefill(torch, hsa, args):
                   "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": attn_ms,
                   "hbm_view": hbm_view(traffic_for("hsa_prefill"), attn_ms)},
         stages_ms=dict(zip(["landmarks", "select", "invert", "attend", "fuse"], stages)),
+        traffic_floor=prefill_traffic_floor(args.copy_rate, stages[3] + stages[4]),
         whole_path={"gflop": total_flop / 1e9,
                     "tflops": total_flop / (ms * 1e-3) / 1e12,
                     "mfma_frac": total_flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
@@ -307,6 +430,7 @@ def bench_decode(torch, hsa, args, big=False):
     log("decode: timing")
     t = time_steps(torch, hsa, step, args.steps, args.warmup, 3, args.flush)
     ms, stages = t["ms"], t["stage_mean"]
+    gather = None if big else gather_probe(torch, Kc, Vc, S, B * Hkv * topk, args.flush)
     n = N // S
     lmk_bytes = B * Hkv * n * d * 4
     kv_bytes = B * Hkv * topk * S * d * 2 * 2
@@ -327,6 +451,8 @@ def bench_decode(torch, hsa, args, big=False):
         stages_ms=dict(zip(["scan", "attend", "fuse"], stages)),
         whole_path={"algorithmic_bytes": total, "gbps": total / (ms * 1e-3) / 1e9,
                     "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+    if gather is not None:
+        res["gather_probe"] = gather
     del Kc, Vc, lmk, q, out, ws
     torch.cuda.empty_cache()
     add_timing(res, t, 0)
@@ -717,6 +843,24 @@ def summarize_counters(fetch_dir, write_dir, bench_json):
                                "write_kib_per_launch": v["WRITE_SIZE"], "fetch_bytes": f_b,
                                "write_bytes": w_b, "traffic_bytes": f_b + w_b,
                                "sources_sha1": sources_sha1(w)}
+    # secondary kernels: each launches once per call of its workload too
+    out["secondary"] = {}
+    for w, (name, args_t, _) in SECONDARY.items():
+        if w not in order:
+            continue
+        rec = {"kernel": name, "sources_sha1": sources_sha1(w, SECONDARY)}
+        for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            rows = _counter_rows(d)
+            mine = [val for _, n, val in rows if name in n and args_t in n]
+            k0 = sum(per for x in order[:order.index(w)]
+                     if x in SECONDARY and SECONDARY[x][:2] == (name, args_t))
+            take = mine[k0:k0 + per]
+            if len(take) != per:
+                raise SystemExit(f"{counter}: {w}: expected {per} launches of {name}")
+            scale = out[counter.lower() + "_scale"]
+            rec[counter.lower() + "_bytes"] = sum(take) / per * 1024.0 * scale
+        rec["traffic_bytes"] = rec["fetch_size_bytes"] + rec["write_size_bytes"]
+        out["secondary"][w] = rec
     return out
 
 
@@ -865,12 +1009,14 @@ def main():
 
     torch.cuda.set_device(0)
     args.flush = Flush(torch)
+    args.copy_rate = measure_copy_rate(torch, args.flush)
     res, inputs = bench_prefill(torch, hsa, args)
     line = {"metric": METRIC, "value": res["value"], "unit": "queries/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic", "config": res["config"], "roofline": res["roofline"],
             "stages_ms": res["stages_ms"], "whole_path": res["whole_path"],
+            "traffic_floor": res["traffic_floor"],
             "ms_per_step_mean": res["ms_per_step_mean"],
             "timing": "median of K steps, each between its own HIP events on the library's "
                       "stream after a 1 GiB cache-flush write outside the events"}
