@@ -253,50 +253,6 @@ def prefill_counts(L, S, topk):
     return sel, avail
 
 
-def gather_probe(torch, Kc, Vc, S, n, flush, reps=5):
-    """The decode gather at the memory-system level: torch's row gather of n
-    random S-key chunks (16 KB each at d = 128, bf16) from each of the two
-    caches, after a cache flush (median of reps), beside a contiguous copy
-    of the same number of bytes.  Random chunks spread over 8 GiB caches
-    touch a new memory page each, which the contiguous copy does not."""
-    rk, rv = Kc.view(-1, S * Kc.shape[-1]), Vc.view(-1, S * Vc.shape[-1])
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(7)
-    idx = torch.randint(0, rk.shape[0], (n,), device="cuda", generator=gen)
-    gk = torch.empty((n, rk.shape[1]), dtype=rk.dtype, device="cuda")
-    gv = torch.empty_like(gk)
-    src = rk[:n]
-
-    def timed(fn):
-        ts = []
-        for _ in range(reps):
-            flush()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        return _median(ts)
-
-    def g():
-        torch.index_select(rk, 0, idx, out=gk)
-        torch.index_select(rv, 0, idx, out=gv)
-
-    def c():
-        gk.copy_(src)
-        gv.copy_(rv[:n])
-
-    g()
-    c()
-    tg, tc = timed(g), timed(c)
-    nbytes = 2 * gk.numel() * gk.element_size()
-    del gk, gv, idx
-    return {"chunks": 2 * n, "bytes_read": nbytes, "random_gather_ms": tg,
-            "random_gather_GBps": nbytes / (tg * 1e-3) / 1e9, "contiguous_copy_ms": tc,
-            "contiguous_copy_GBps": nbytes / (tc * 1e-3) / 1e9}
-
-
 def prefill_traffic_floor(copy_rate, attend_fuse_ms):
     """The chunk-major schedule's traffic floor: the HBM bytes its attention
     and fusion kernels move per call (counter summary) priced at the plain
@@ -430,7 +386,6 @@ def bench_decode(torch, hsa, args, big=False):
     log("decode: timing")
     t = time_steps(torch, hsa, step, args.steps, args.warmup, 3, args.flush)
     ms, stages = t["ms"], t["stage_mean"]
-    gather = None if big else gather_probe(torch, Kc, Vc, S, B * Hkv * topk, args.flush)
     n = N // S
     lmk_bytes = B * Hkv * n * d * 4
     kv_bytes = B * Hkv * topk * S * d * 2 * 2
@@ -451,8 +406,6 @@ def bench_decode(torch, hsa, args, big=False):
         stages_ms=dict(zip(["scan", "attend", "fuse"], stages)),
         whole_path={"algorithmic_bytes": total, "gbps": total / (ms * 1e-3) / 1e9,
                     "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
-    if gather is not None:
-        res["gather_probe"] = gather
     del Kc, Vc, lmk, q, out, ws
     torch.cuda.empty_cache()
     add_timing(res, t, 0)
