@@ -23,7 +23,8 @@ __all__ = [
     "hsa_prefill_backward_workspace_size", "dhsa_prefill",
     "dhsa_prefill_workspace_size", "dhsa_build_chunk_keys", "dhsa_decode",
     "dhsa_decode_workspace_size", "swa_prefill", "swa_decode", "hsa_profile_enable",
-    "hsa_profile_read", "lib_path", "load_library",
+    "hsa_profile_read", "lib_path", "load_library", "hsa_device_checks_enabled",
+    "hsa_device_checks_selftest",
 ]
 
 HSA_OK = 0
@@ -53,18 +54,21 @@ class HsaError(RuntimeError):
 
 
 def lib_path():
-    return _build.LIB
+    """The library this process loads: libhsa_attn.so, or the debug library
+    with device checks (libhsa_attn_debug.so) when HSA_ATTN_DEBUG=1."""
+    return _build.LIB_DEBUG if os.environ.get("HSA_ATTN_DEBUG", "0") == "1" else _build.LIB
 
 
 def load_library():
-    """Load libhsa_attn.so (raises if it has not been built)."""
+    """Load the library (raises if it has not been built)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
-        raise RuntimeError(f"{_build.LIB} is not built: run __graft_entry__.build() "
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() "
                            "(there is no fallback implementation)")
-    lib = ctypes.CDLL(_build.LIB)
+    lib = ctypes.CDLL(path)
     sig = {
         "hsa_status_string": ([_I], ctypes.c_char_p),
         "hsa_last_error_message": ([], ctypes.c_char_p),
@@ -101,6 +105,8 @@ def load_library():
         "swa_decode": ([_P, _P, _P, _L, _L, _L, _P, _I, _I, _I, _I, _I, _P], _I),
         "hsa_profile_enable": ([_I], _I),
         "hsa_profile_read": ([_P, _I, _P], _I),
+        "hsa_device_checks_enabled": ([], _I),
+        "hsa_device_checks_selftest": ([_I, _P], _I),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -398,7 +404,7 @@ def dhsa_prefill_workspace_size(B, L, H, d, n_chunks, dtype):
 
 def dhsa_prefill(Q, K, V, offsets, budget, out=None, return_mask=False, return_order=False,
                  workspace=None):
-    """DHSA prefill.  Q, K, V [B,H,L,d] bf16; offsets: host int32 chunk
+    """DHSA prefill.  Q, K, V [B,H,L,d] fp32 or bf16; offsets: host int32 chunk
     boundaries [n+1] (0 .. L); budget N_b.
 
     Returns O, plus the uint32 mask bits [B,H,L,ceil(L/32)] and/or the chunk
@@ -577,3 +583,16 @@ def hsa_profile_read(max_stages=8):
     ns = ctypes.c_int(0)
     calls = load_library().hsa_profile_read(buf, max_stages, ctypes.byref(ns))
     return calls, [buf[i] for i in range(min(ns.value, max_stages))]
+
+
+def hsa_device_checks_enabled():
+    """True when the loaded library is the debug build with device checks."""
+    return bool(load_library().hsa_device_checks_enabled())
+
+
+def hsa_device_checks_selftest(fail_check, stream=None):
+    """Run the debug library's one-check self-test kernel; returns the status
+    (HSA_ERR_HIP when the check was made to fail, HSA_ERR_UNSUPPORTED in the
+    release library)."""
+    st = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    return load_library().hsa_device_checks_selftest(1 if fail_check else 0, st)

@@ -12,6 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhsa_attn.so")
+# the same sources with device checks compiled in (HSA_ATTN_DEBUG=1 loads it)
+LIB_DEBUG = os.path.join(HERE, "libhsa_attn_debug.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -25,28 +27,39 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD_DIR, src + ".o")
+def _compile(src, debug):
+    out_dir = os.path.join(BUILD_DIR, "debug") if debug else BUILD_DIR
+    obj = os.path.join(out_dir, src + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    defs = ["-DHSA_DEVICE_CHECKS=1"] if debug else []
+    cmd = [HIPCC] + FLAGS + defs + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{out}")
-    if out.strip():
+    if out.strip() and not debug:
         print(out, flush=True)
     return obj
 
 
-def build(verbose=True):
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB] + objs
-    subprocess.run(cmd, check=True)
-    if verbose:
-        print("built", LIB, flush=True)
+def build(verbose=True, debug=True):
+    """Compile every source for gfx950 and link libhsa_attn.so; with `debug`
+    also the device-checked libhsa_attn_debug.so from the same sources."""
+    variants = [False, True] if debug else [False]
+    for v in variants:
+        os.makedirs(os.path.join(BUILD_DIR, "debug") if v else BUILD_DIR, exist_ok=True)
+    jobs = [(src, v) for v in variants for src in SOURCES]
+    workers = min(len(jobs), max(1, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    for v in variants:
+        lib = LIB_DEBUG if v else LIB
+        mine = [o for o, (_, jv) in zip(objs, jobs) if jv == v]
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib] + mine
+        subprocess.run(cmd, check=True)
+        if verbose:
+            print("built", lib, flush=True)
     return LIB
 
 

@@ -2,13 +2,61 @@
 // host-side argument validation, workspace carving, launch sequencing.
 // Nothing is enqueued until every argument has been checked.
 #include <hip/hip_runtime.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <cxxabi.h>
 
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "hsa_attn.h"
 #include "kernels.h"
+
+namespace hsa {
+
+// Translation units of the debug library register their check counters,
+// and source files with checks their tags, during static initialisation
+// (hsa_common.h).
+struct CheckSource {
+  CheckRead read;
+  CheckClear clear;
+};
+
+std::vector<CheckSource>& check_sources() {
+  static std::vector<CheckSource> v;
+  return v;
+}
+
+std::vector<std::pair<uint32_t, std::string>>& check_paths() {
+  static std::vector<std::pair<uint32_t, std::string>> v;
+  return v;
+}
+
+bool register_device_checks(CheckRead read, CheckClear clear) {
+  check_sources().push_back({read, clear});
+  return true;
+}
+
+bool register_check_source(uint32_t tag, const char* path) {
+  check_paths().emplace_back(tag, path);
+  return true;
+}
+
+std::string check_source_path(uint32_t tag) {
+  for (const auto& p : check_paths())
+    if (p.first == tag) {
+      const size_t slash = p.second.rfind('/');
+      return slash == std::string::npos ? p.second : p.second.substr(slash + 1);
+    }
+  return "unknown source";
+}
+
+}  // namespace hsa
 
 namespace {
 
@@ -41,14 +89,47 @@ struct StageMarks {
   }
 };
 
+// One line to stderr per entry-point call (its name and shapes) when
+// HSA_ATTN_LOG is set; the kernels' launch lines follow it.
+void log_call(const char* fmt, ...) {
+  if (!hsa::launch_log_enabled()) return;
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "hsa_attn: %s\n", line);
+}
+
 hsa_status_t fail(hsa_status_t s, const std::string& msg) {
   g_err = msg;
+  if (hsa::launch_log_enabled()) fprintf(stderr, "hsa_attn:   status %d: %s\n", (int)s, msg.c_str());
   return s;
 }
 
 hsa_status_t hip_fail(hipError_t e, const char* where) {
-  g_err = std::string(where) + ": " + hipGetErrorString(e);
-  return HSA_ERR_HIP;
+  return fail(HSA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+// The end of every entry point that launched work.  In the debug library
+// (device checks registered) the stream is synchronised and every kernel
+// source's check counters are read; the first failure becomes HSA_ERR_HIP
+// and the counters are cleared.  Otherwise HSA_OK.
+hsa_status_t finish(hipStream_t stream) {
+  if (hsa::check_sources().empty()) return HSA_OK;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "device checks: stream synchronise");
+  std::string report;
+  for (const auto& src : hsa::check_sources()) {
+    uint32_t c[3] = {0u, 0u, 0u};
+    if ((e = src.read(c)) != hipSuccess) return hip_fail(e, "device checks: read");
+    if (c[0] == 0u) continue;
+    if ((e = src.clear()) != hipSuccess) return hip_fail(e, "device checks: clear");
+    if (report.empty())
+      report = "device check failed at " + hsa::check_source_path(c[2]) + ":" +
+               std::to_string(c[1]) + " (" + std::to_string(c[0]) + " failures)";
+  }
+  return report.empty() ? HSA_OK : fail(HSA_ERR_HIP, report);
 }
 
 bool dtype_ok(hsa_dtype_t dt) { return dt == HSA_DTYPE_F32 || dt == HSA_DTYPE_BF16; }
@@ -285,6 +366,30 @@ int api_error(int status, const char* message) {
   return status;
 }
 
+bool launch_log_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("HSA_ATTN_LOG");
+    return v != nullptr && *v != '\0' && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void log_launch(const void* kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
+  // the kernel's symbol, demangled: "void hsa::(anonymous namespace)::name<args>(params)"
+  const char* sym = hipKernelNameRefByPtr(kernel, stream);
+  int status = -1;
+  char* dem = sym ? abi::__cxa_demangle(sym, nullptr, nullptr, &status) : nullptr;
+  std::string k = status == 0 && dem ? dem : (sym ? sym : "?");
+  free(dem);
+  if (k.compare(0, 5, "void ") == 0) k.erase(0, 5);
+  for (const char* ns : {"hsa::(anonymous namespace)::", "hsa::"})
+    if (k.compare(0, strlen(ns), ns) == 0) k.erase(0, strlen(ns));
+  const size_t paren = k.rfind('(');
+  if (paren != std::string::npos && paren > 0) k.erase(paren);
+  fprintf(stderr, "hsa_attn:   launch %s grid (%u, %u, %u) block (%u, %u, %u) lds %zu B\n",
+          k.c_str(), grid.x, grid.y, grid.z, block.x, block.y, block.z, lds);
+}
+
 }  // namespace hsa
 
 extern "C" {
@@ -306,6 +411,8 @@ hsa_status_t hsa_build_landmarks(const void* K, float* lmk, int B, int Hkv, int6
                                  int S, int64_t chunk_begin, int64_t chunk_end,
                                  hsa_dtype_t dtype, hsa_stream_t stream) {
   g_err.clear();
+  log_call("hsa_build_landmarks B=%d Hkv=%d L=%lld d=%d S=%d chunks [%lld, %lld) dtype=%d", B, Hkv,
+           (long long)L, d, S, (long long)chunk_begin, (long long)chunk_end, (int)dtype);
   if (!dtype_ok(dtype)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
   if (B < 0 || Hkv <= 0 || L < 0) return fail(HSA_ERR_INVALID_ARGUMENT, "bad B, Hkv or L");
   if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
@@ -319,7 +426,8 @@ hsa_status_t hsa_build_landmarks(const void* K, float* lmk, int B, int Hkv, int6
   if (!K || !lmk) return fail(HSA_ERR_INVALID_ARGUMENT, "K and lmk must not be NULL");
   hipError_t e = hsa::launch_landmarks(K, dt_code(dtype), lmk, (int64_t)B * Hkv, L, n, d, S,
                                        chunk_begin, chunk_end, (hipStream_t)stream);
-  return e == hipSuccess ? HSA_OK : hip_fail(e, "hsa_build_landmarks launch");
+  if (e != hipSuccess) return hip_fail(e, "hsa_build_landmarks launch");
+  return finish((hipStream_t)stream);
 }
 
 size_t hsa_prefill_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S, int topk,
@@ -381,6 +489,9 @@ hsa_status_t prefill_impl(const void* Q, const void* K, const void* V, const flo
                           int Hkv, int d, int S, int topk, int interval, hsa_dtype_t dtype,
                           void* workspace, size_t workspace_bytes, hsa_stream_t stream) {
   g_err.clear();
+  log_call("%s B=%d L=%lld Hq=%d Hkv=%d d=%d S=%d topk=%d dtype=%d",
+           interval > 1 ? "hsa_prefill_interval" : "hsa_prefill", B, (long long)L, Hq, Hkv, d, S,
+           topk, (int)dtype);
   hsa_status_t s = check_prefill(B, L, Hq, Hkv, d, S, topk, dtype);
   if (s != HSA_OK) return s;
   if (interval < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "the retrieval interval must be >= 1");
@@ -414,7 +525,7 @@ hsa_status_t prefill_impl(const void* Q, const void* K, const void* V, const flo
   pm.mark();
   if ((e = hsa::prefill_fuse(a, st)) != hipSuccess) return hip_fail(e, "fuse");
   pm.mark();
-  return HSA_OK;
+  return finish(st);
 }
 
 }  // namespace
@@ -442,6 +553,8 @@ hsa_status_t hsa_prefill_backward(const void* Q, const void* K, const void* V, c
                                   hsa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                   hsa_stream_t stream) {
   g_err.clear();
+  log_call("hsa_prefill_backward B=%d L=%lld Hq=%d Hkv=%d d=%d S=%d topk=%d dtype=%d", B,
+           (long long)L, Hq, Hkv, d, S, topk, (int)dtype);
   hsa_status_t s = check_prefill(B, L, Hq, Hkv, d, S, topk, dtype);
   if (s != HSA_OK) return s;
   if (dtype != HSA_DTYPE_BF16) return fail(HSA_ERR_UNSUPPORTED, "the backward runs bf16 only");
@@ -493,7 +606,7 @@ hsa_status_t hsa_prefill_backward(const void* Q, const void* K, const void* V, c
   pm.mark();
   if ((e = hsa::prefill_bwd_finish(ba, st)) != hipSuccess) return hip_fail(e, "backward finish");
   pm.mark();
-  return HSA_OK;
+  return finish(st);
 }
 
 size_t hsa_prefill_interval_workspace_size(int B, int64_t L, int Hq, int Hkv, int d, int S,
@@ -522,6 +635,8 @@ hsa_status_t hsa_decode(const void* q, const void* Kc, const void* Vc, const flo
                         int B, int Hq, int Hkv, int d, int S, int topk, hsa_dtype_t dtype,
                         void* workspace, size_t workspace_bytes, hsa_stream_t stream) {
   g_err.clear();
+  log_call("hsa_decode B=%d n_ctx=%lld n_max=%lld Hq=%d Hkv=%d d=%d S=%d topk=%d dtype=%d", B,
+           (long long)n_ctx, (long long)n_max, Hq, Hkv, d, S, topk, (int)dtype);
   hsa_status_t s = check_decode(B, Hq, Hkv, d, S, topk, n_ctx, n_max, dtype);
   if (s != HSA_OK) return s;
   if (B == 0) return HSA_OK;
@@ -570,7 +685,7 @@ hsa_status_t hsa_decode(const void* q, const void* Kc, const void* Vc, const flo
     if (e != hipSuccess) return hip_fail(e, "decode");
   }
   pm.mark();
-  return HSA_OK;
+  return finish(st);
 }
 
 size_t hsa_swa_decode_workspace_size(int B, int Hq, int Hkv, int d, int S, int topk,
@@ -587,6 +702,9 @@ hsa_status_t hsa_swa_decode(const void* q, const void* Kc, const void* Vc, const
                             int d, int S, int topk, hsa_dtype_t dtype, void* workspace,
                             size_t workspace_bytes, hsa_stream_t stream) {
   g_err.clear();
+  log_call("hsa_swa_decode B=%d n_ctx=%lld n_max=%lld window=%lld Hq=%d Hkv=%d d=%d S=%d topk=%d "
+           "dtype=%d", B, (long long)n_ctx, (long long)n_max, (long long)window, Hq, Hkv, d, S,
+           topk, (int)dtype);
   hsa_status_t s = check_decode(B, Hq, Hkv, d, S, topk, n_ctx, n_max, dtype);
   if (s != HSA_OK) return s;
   if (n_ctx >= n_max)
@@ -647,7 +765,7 @@ hsa_status_t hsa_swa_decode(const void* q, const void* Kc, const void* Vc, const
     if (e != hipSuccess) return hip_fail(e, "hsa_swa_decode");
   }
   pm.mark();
-  return HSA_OK;
+  return finish(st);
 }
 
 size_t dhsa_prefill_workspace_size(int B, int64_t L, int H, int d, int n_chunks,
@@ -665,8 +783,9 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
                           hsa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                           hsa_stream_t stream) {
   g_err.clear();
+  log_call("dhsa_prefill B=%d L=%lld H=%d d=%d chunks=%d budget=%lld dtype=%d", B, (long long)L, H,
+           d, n_chunks, (long long)budget, (int)dtype);
   if (!dtype_ok(dtype)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
-  if (dtype != HSA_DTYPE_BF16) return fail(HSA_ERR_UNSUPPORTED, "dhsa_prefill runs bf16 only");
   if (B < 0 || L < 1 || H <= 0) return fail(HSA_ERR_INVALID_ARGUMENT, "need B >= 0, L >= 1, H >= 1");
   if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
   if (budget < 1) return fail(HSA_ERR_INVALID_ARGUMENT, "budget N_b must be >= 1");
@@ -726,7 +845,7 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
     if (e != hipSuccess) return hip_fail(e, "dhsa");
   }
   pm.mark();
-  return HSA_OK;
+  return finish(st);
 }
 
 size_t dhsa_chunk_keys_workspace_size(int n_chunks) {
@@ -739,6 +858,8 @@ hsa_status_t dhsa_build_chunk_keys(const void* K, float* khat, const int32_t* of
                                    int64_t n_max, int d, int n_cap, hsa_dtype_t dtype,
                                    void* workspace, size_t workspace_bytes, hsa_stream_t stream) {
   g_err.clear();
+  log_call("dhsa_build_chunk_keys B=%d H=%d n_max=%lld d=%d chunks [%d, %d) dtype=%d", B, H,
+           (long long)n_max, d, chunk_begin, chunk_end, (int)dtype);
   if (!dtype_ok(dtype)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
   if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
   if (B < 0 || H <= 0 || n_max < 0 || n_chunks < 0 || n_cap < n_chunks)
@@ -763,7 +884,7 @@ hsa_status_t dhsa_build_chunk_keys(const void* K, float* khat, const int32_t* of
   if (e != hipSuccess) return hip_fail(e, "offsets upload");
   e = hsa::launch_dhsa_chunk_keys(K, khat, offs, dt_code(dtype), (int64_t)B * H, n_max, d, n_cap,
                                   chunk_begin, chunk_end, st);
-  return e == hipSuccess ? HSA_OK : hip_fail(e, "dhsa_build_chunk_keys launch");
+  return e == hipSuccess ? finish(st) : hip_fail(e, "dhsa_build_chunk_keys launch");
 }
 
 size_t dhsa_decode_workspace_size(int B, int H, int d, int n_chunks, int64_t budget,
@@ -781,6 +902,8 @@ hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* V
                          int H, int d, hsa_dtype_t dtype, void* workspace,
                          size_t workspace_bytes, hsa_stream_t stream) {
   g_err.clear();
+  log_call("dhsa_decode B=%d H=%d m=%d n_max=%lld d=%d chunks=%d budget=%lld dtype=%d", B, H, m,
+           (long long)n_max, d, n_chunks, (long long)budget, (int)dtype);
   if (!dtype_ok(dtype)) return fail(HSA_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
   if (d != 64 && d != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim must be 64 or 128");
   if (B < 0 || H <= 0) return fail(HSA_ERR_INVALID_ARGUMENT, "need B >= 0 and H >= 1");
@@ -841,7 +964,7 @@ hsa_status_t dhsa_decode(const void* q_cur, int m, const void* Kc, const void* V
     if (e != hipSuccess) return hip_fail(e, "dhsa_decode");
   }
   pm.mark();
-  return HSA_OK;
+  return finish(st);
 }
 
 }  // extern "C"
@@ -866,6 +989,8 @@ hsa_status_t swa_prefill(const void* Q, const void* K, const void* V, void* O, i
                          int Hq, int Hkv, int d, int64_t window, hsa_dtype_t dtype,
                          hsa_stream_t stream) {
   g_err.clear();
+  log_call("swa_prefill B=%d L=%lld Hq=%d Hkv=%d d=%d window=%lld dtype=%d", B, (long long)L, Hq,
+           Hkv, d, (long long)window, (int)dtype);
   hsa_status_t s = check_swa(B, Hq, Hkv, d, window, dtype);
   if (s != HSA_OK) return s;
   if (L < 0) return fail(HSA_ERR_INVALID_ARGUMENT, "need L >= 0");
@@ -893,7 +1018,7 @@ hsa_status_t swa_prefill(const void* Q, const void* K, const void* V, void* O, i
   hipError_t e = hsa::launch_swa_prefill(a, st);
   if (e != hipSuccess) return hip_fail(e, "swa_prefill");
   pm.mark();
-  return HSA_OK;
+  return finish(st);
 }
 
 hsa_status_t hsa_swa_prefill(const void* Q, const void* K, const void* V, const float* lmk,
@@ -902,6 +1027,8 @@ hsa_status_t hsa_swa_prefill(const void* Q, const void* K, const void* V, const 
                              int topk, hsa_dtype_t dtype, void* workspace,
                              size_t workspace_bytes, hsa_stream_t stream) {
   g_err.clear();
+  log_call("hsa_swa_prefill B=%d L=%lld Hq=%d Hkv=%d d=%d S=%d topk=%d window=%lld dtype=%d", B,
+           (long long)L, Hq, Hkv, d, S, topk, (long long)window, (int)dtype);
   hsa_status_t s = check_prefill(B, L, Hq, Hkv, d, S, topk, dtype);
   if (s != HSA_OK) return s;
   if ((s = check_swa(B, Hq, Hkv, d, window, dtype)) != HSA_OK) return s;
@@ -958,13 +1085,15 @@ hsa_status_t hsa_swa_prefill(const void* Q, const void* K, const void* V, const 
   pm.mark();
   if ((e = hsa::prefill_fuse(a, st)) != hipSuccess) return hip_fail(e, "fuse");
   pm.mark();
-  return HSA_OK;
+  return finish(st);
 }
 
 hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t pos,
                         int64_t n_max, int64_t window, void* o, int B, int Hq, int Hkv, int d,
                         hsa_dtype_t dtype, hsa_stream_t stream) {
   g_err.clear();
+  log_call("swa_decode B=%d pos=%lld n_max=%lld Hq=%d Hkv=%d d=%d window=%lld dtype=%d", B,
+           (long long)pos, (long long)n_max, Hq, Hkv, d, (long long)window, (int)dtype);
   hsa_status_t s = check_swa(B, Hq, Hkv, d, window, dtype);
   if (s != HSA_OK) return s;
   if (pos < 0 || pos >= n_max)
@@ -993,7 +1122,20 @@ hsa_status_t swa_decode(const void* q, const void* Kc, const void* Vc, int64_t p
   hipError_t e = hsa::launch_swa_decode(a, st);
   if (e != hipSuccess) return hip_fail(e, "swa_decode");
   pm.mark();
-  return HSA_OK;
+  return finish(st);
+}
+
+int hsa_device_checks_enabled(void) { return hsa::check_sources().empty() ? 0 : 1; }
+
+hsa_status_t hsa_device_checks_selftest(int fail_check, hsa_stream_t stream) {
+  g_err.clear();
+  log_call("hsa_device_checks_selftest fail=%d", fail_check);
+  if (hsa::check_sources().empty())
+    return ::fail(HSA_ERR_UNSUPPORTED, "device checks are compiled into the debug library only");
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hsa::launch_check_selftest(fail_check, st);
+  if (e != hipSuccess) return hip_fail(e, "hsa_device_checks_selftest launch");
+  return finish(st);
 }
 
 hsa_status_t hsa_profile_enable(int enable) {

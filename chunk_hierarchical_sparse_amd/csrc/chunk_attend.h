@@ -13,6 +13,8 @@
 
 namespace hsa {
 
+HSA_DCHECK_SOURCE()
+
 constexpr int kChunkThreads = 256;
 
 // LDS of one block of the chunk attention.
@@ -103,6 +105,8 @@ __device__ __forceinline__ void attend_chunk_body(const PrefillArgs& a, float sc
     int ei, hh;
     split_row(tile * 32 + i32, ei, hh);
     const int64_t t = row_ok(tile) ? (int64_t)(entry >> kSlotBits) : 0;
+    // a listed token sees the chunk whole: (c + 1) S <= t < L
+    HSA_DCHECK(!row_ok(tile) || (t >= (int64_t)(c + 1) * a.S && t < a.L));
     const uint16_t* qrow = Q + qbase + (int64_t)hh * qplane + t * D + 8 * hf;
 #pragma unroll
     for (int s2 = 0; s2 < D / 16; ++s2) q[s2] = *(const u32x4*)(qrow + 16 * s2);

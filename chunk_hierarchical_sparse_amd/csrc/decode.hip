@@ -25,6 +25,8 @@
 #include "kernels.h"
 
 namespace hsa {
+
+HSA_DCHECK_SOURCE()
 namespace {
 
 constexpr int kThreads = 256;
@@ -315,6 +317,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float sc
   if (k == 0)
     for (int e = tid; e < a.topk; e += kThreads) a.sel[bg * a.topk + e] = ml.order[e];
   const int c = k < got ? ml.order[k] : -1;
+  HSA_DCHECK(c < a.n_avail);
   if (c < 0 || c >= a.n_avail) return;
   // this lane's landmark columns (for s_h)
   const float* lc = a.lmk + (bg * a.lmk_chunks + c) * D;
@@ -478,6 +481,7 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
   if (win) {
     row0 = a.swa_lo + (int64_t)(r - K) * kWave;
     nk = (int)min((int64_t)kWave, a.swa_hi - row0);
+    HSA_DCHECK(row0 >= 0 && nk >= 1 && row0 + nk <= a.n_max);
   } else {
     if (a.n_avail > 0) {
       const int got = merge_sorted(a, bg, st.m);
@@ -490,6 +494,7 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
     __syncthreads();
     c = s_c;
     if (c < 0) return;  // uniform: rank past the selected chunks
+    HSA_DCHECK(c < a.n_avail);
     row0 = (int64_t)c * a.S;
     nk = a.S;
   }
@@ -687,19 +692,19 @@ hipError_t stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   if (stage == 0) {
     if (a.n_avail > 0)
-      scan_kernel<D, DT><<<dim3((unsigned)(BG * a.n_slices)), dim3(kThreads),
-                           (size_t)a.slice * sizeof(uint64_t), stream>>>(a);
+      launch<scan_kernel<D, DT>>(dim3((unsigned)(BG * a.n_slices)), dim3(kThreads),
+                                 (size_t)a.slice * sizeof(uint64_t), stream, a);
   } else if (stage == 1) {
     // one block per (b, group, rank)
     const size_t q_lds = (size_t)G * D * (DT == kF32 ? 4 : 2) + (size_t)G * kWave * sizeof(float);
     if (a.S <= kWave)
-      attend_rank_kernel<D, DT><<<dim3((unsigned)(BG * (a.topk + a.swa_pieces))), dim3(kThreads),
-                                  q_lds, stream>>>(a, scale);
+      launch<attend_rank_kernel<D, DT>>(dim3((unsigned)(BG * (a.topk + a.swa_pieces))),
+                                        dim3(kThreads), q_lds, stream, a, scale);
     else
-      attend_kernel<D, DT><<<dim3((unsigned)(BG * a.topk)), dim3(kThreads),
-                             (size_t)G * D * sizeof(float), stream>>>(a, scale);
+      launch<attend_kernel<D, DT>>(dim3((unsigned)(BG * a.topk)), dim3(kThreads),
+                                   (size_t)G * D * sizeof(float), stream, a, scale);
   } else {
-    fuse_kernel<D, DT><<<dim3((unsigned)BG), dim3(kThreads), 0, stream>>>(a);
+    launch<fuse_kernel<D, DT>>(dim3((unsigned)BG), dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -17,7 +17,8 @@
 //  4. attend: per (b, h, query chunk, 128-row tile): each lane's row finds
 //             its cut (number of whole chunks, tokens of the boundary chunk)
 //             by binary search, then the block walks the ranked chunks with
-//             the MFMA attention core and per-row key limits.
+//             the MFMA attention core (bf16) or fp32 VALU dot products
+//             (fp32), with per-row key limits.
 //  5. mask  : optional debug bitmask of the kept keys.
 #include <math.h>
 
@@ -26,6 +27,8 @@
 #include "kernels.h"
 
 namespace hsa {
+
+HSA_DCHECK_SOURCE()
 namespace {
 
 constexpr int kThreads = 256;
@@ -194,6 +197,7 @@ __device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int
   Cut c;
   c.pw = lo;
   c.rem = (int)(B - (cum[lo] - (lo > dp ? tail : 0)));
+  HSA_DCHECK(dp >= 0 && dp <= l && c.pw <= l + 1 && c.rem >= 0);
   return c;
 }
 
@@ -239,6 +243,7 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   KVRegsWide<D> rg;
   if (p_end >= 0) {
     k = order[0];
+    HSA_DCHECK(k >= 0 && k <= l);
     bk = a.offs[k];
     lk = a.offs[k + 1] - bk;
     fetch_kv_wide<D>(rg, Kb + (int64_t)bk * D, Vb + (int64_t)bk * D, min(kWideBlock, lk));
@@ -254,6 +259,7 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
       nkb = 0;
       if (np <= p_end) {
         nkc = order[np];
+        HSA_DCHECK(nkc >= 0 && nkc <= l);
         nbk = a.offs[nkc];
         nlk = a.offs[nkc + 1] - nbk;
       }
@@ -285,6 +291,106 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
                        pack_bf16x2(st.o[bb][4 * q4 + 2] * inv, st.o[bb][4 * q4 + 3] * inv)};
       *(u32x2*)(orow + dd) = v;
     }
+}
+
+// fp32 inputs: the same walk over the ranked chunks, on the VALU in fp32.
+// Two lanes per query row, 128 rows per block (the bf16 kernel's tiles):
+// lane half hf holds the float4 pieces 2u + hf of the row's query and
+// output, so the two lanes of a row read 32 consecutive bytes of a key or
+// value row and every row of the wave reads the same ones (LDS broadcasts).
+// Keys and values are staged 32 rows at a time; rows past the chunk's end
+// load its last row and are masked by the row's key count.
+constexpr int kF32Keys = 32;
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) attend_f32_kernel(DhsaArgs a, float scale_log2) {
+  constexpr int P4 = D / 8;  // float4 pieces per lane
+  __shared__ f32x4 ks[kF32Keys][D / 4];
+  __shared__ f32x4 vs[kF32Keys][D / 4];
+  __shared__ int pmax;
+  const int64_t BH = (int64_t)a.B * a.H;
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t rest = blockIdx.x / BH;
+  const int l = a.nc - 1 - (int)(rest / a.tiles_per_chunk);
+  const int tile = (int)(rest % a.tiles_per_chunk);
+  const int bl = a.offs[l], bl1 = a.offs[l + 1];
+  const int row0 = bl + tile * kRowsPerTile;
+  if (row0 >= bl1) return;
+  const int hf = threadIdx.x & 1;
+  const int i = row0 + (threadIdx.x >> 1);
+  const bool valid = i < bl1;
+  Cut cut = {0, 0};
+  if (valid) cut = row_cut(a, bh, l, i);
+  const int last = valid ? (cut.rem > 0 ? cut.pw : cut.pw - 1) : -1;
+  if (threadIdx.x == 0) pmax = -1;
+  __syncthreads();
+  atomicMax(&pmax, last);
+  __syncthreads();
+  const int p_end = pmax;
+  const float* Kb = (const float*)a.K + bh * a.L * D;
+  const float* Vb = (const float*)a.V + bh * a.L * D;
+  const float* qrow = (const float*)a.Q + (bh * a.L + min(i, (int)a.L - 1)) * D;
+  f32x4 q[P4], o[P4];
+#pragma unroll
+  for (int u = 0; u < P4; ++u) {
+    q[u] = *(const f32x4*)(qrow + 8 * u + 4 * hf);
+    o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m = -INFINITY, lsum = 0.f;
+  const int32_t* order = a.order + (bh * a.nc + l) * a.nc;
+  for (int p = 0; p <= p_end; ++p) {
+    const int k = order[p];
+    HSA_DCHECK(k >= 0 && k <= l);
+    const int bk = a.offs[k], lk = a.offs[k + 1] - bk;
+    const int len_eff = k == l ? i - bl + 1 : lk;
+    const int hi = !valid ? 0 : (p < cut.pw ? len_eff : (p == cut.pw ? cut.rem : 0));
+    for (int kb = 0; kb < lk; kb += kF32Keys) {
+      const int nk = min(kF32Keys, lk - kb);
+      __syncthreads();
+      for (int x = threadIdx.x; x < kF32Keys * D / 4; x += kThreads) {
+        const int r = x / (D / 4), c4 = x % (D / 4);
+        const int64_t row = bk + kb + min(r, nk - 1);
+        ks[r][c4] = *(const f32x4*)(Kb + row * D + 4 * c4);
+        vs[r][c4] = *(const f32x4*)(Vb + row * D + 4 * c4);
+      }
+      __syncthreads();
+      const int nv = max(0, min(hi - kb, nk));
+      float s[kF32Keys];
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kF32Keys; ++j) {
+        float part = 0.f;
+#pragma unroll
+        for (int u = 0; u < P4; ++u) {
+          const f32x4 kv = ks[j][2 * u + hf];
+          part += q[u][0] * kv[0] + q[u][1] * kv[1] + q[u][2] * kv[2] + q[u][3] * kv[3];
+        }
+        part += __shfl_xor(part, 1, kWave);  // both lanes of the row: the full dot product
+        s[j] = j < nv ? part * scale_log2 : -INFINITY;
+        bmax = fmaxf(bmax, s[j]);
+      }
+      if (nv > 0) {
+        const float mn = fmaxf(m, bmax);
+        const float al = exp2f(m - mn);  // 0 while m is -inf
+        lsum *= al;
+#pragma unroll
+        for (int u = 0; u < P4; ++u) o[u] *= al;
+#pragma unroll
+        for (int j = 0; j < kF32Keys; ++j) {
+          const float pj = exp2f(s[j] - mn);  // 0 for masked keys
+          lsum += pj;
+#pragma unroll
+          for (int u = 0; u < P4; ++u) o[u] += pj * vs[j][2 * u + hf];
+        }
+        m = mn;
+      }
+    }
+  }
+  if (!valid) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  float* orow = (float*)a.O + (bh * a.L + i) * D;
+#pragma unroll
+  for (int u = 0; u < P4; ++u) *(f32x4*)(orow + 8 * u + 4 * hf) = o[u] * inv;
 }
 
 // Debug bitmask: one thread per (b, h, row i, 32-key word).
@@ -330,31 +436,38 @@ hipError_t dhsa_stage(const DhsaArgs& a, int stage, hipStream_t stream) {
       const int VEC = a.dtype == kF32 ? 4 : 8;
       const size_t lds = 2 * (size_t)(kThreads / (a.d / VEC)) * a.d * sizeof(float);
       if (a.dtype == kF32)
-        pool_kernel<kF32><<<dim3((unsigned)rows), dim3(kThreads), lds, stream>>>(a);
+        launch<pool_kernel<kF32>>(dim3((unsigned)rows), dim3(kThreads), lds, stream, a);
       else
-        pool_kernel<kBF16><<<dim3((unsigned)rows), dim3(kThreads), lds, stream>>>(a);
+        launch<pool_kernel<kBF16>>(dim3((unsigned)rows), dim3(kThreads), lds, stream, a);
       break;
     }
     case 1:
       if (a.d == 64)
-        sc_kernel<64><<<dim3((unsigned)rows), dim3(kThreads), 0, stream>>>(a);
+        launch<sc_kernel<64>>(dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
       else
-        sc_kernel<128><<<dim3((unsigned)rows), dim3(kThreads), 0, stream>>>(a);
+        launch<sc_kernel<128>>(dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
       break;
     case 2: {
       int P = 1;
       while (P < a.nc) P <<= 1;
-      rank_kernel<<<dim3((unsigned)rows), dim3(kThreads), (size_t)P * sizeof(uint64_t),
-                    stream>>>(a, P);
+      launch<rank_kernel>(dim3((unsigned)rows), dim3(kThreads), (size_t)P * sizeof(uint64_t),
+                          stream, a, P);
       break;
     }
     case 3: {
       const float sl2 = 1.4426950408889634f / sqrtf((float)a.d);
       const int64_t blocks = rows * a.tiles_per_chunk;
-      if (a.d == 64)
-        attend_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2);
-      else
-        attend_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2);
+      const dim3 grid((unsigned)blocks), block(kThreads);
+      if (a.dtype == kF32) {
+        if (a.d == 64)
+          launch<attend_f32_kernel<64>>(grid, block, 0, stream, a, sl2);
+        else
+          launch<attend_f32_kernel<128>>(grid, block, 0, stream, a, sl2);
+      } else if (a.d == 64) {
+        launch<attend_kernel<64>>(grid, block, 0, stream, a, sl2);
+      } else {
+        launch<attend_kernel<128>>(grid, block, 0, stream, a, sl2);
+      }
       break;
     }
     default: {
@@ -362,7 +475,7 @@ hipError_t dhsa_stage(const DhsaArgs& a, int stage, hipStream_t stream) {
       const int64_t total = BH * a.L * ((a.L + 31) / 32);
       int64_t nb = (total + 255) / 256;
       if (nb > 65536) nb = 65536;
-      mask_kernel<<<dim3((unsigned)nb), dim3(256), 0, stream>>>(a);
+      launch<mask_kernel>(dim3((unsigned)nb), dim3(256), 0, stream, a);
       break;
     }
   }

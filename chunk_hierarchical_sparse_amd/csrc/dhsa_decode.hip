@@ -23,6 +23,8 @@
 #include "kernels.h"
 
 namespace hsa {
+
+HSA_DCHECK_SOURCE()
 namespace {
 
 constexpr int kThreads = 256;
@@ -293,6 +295,7 @@ __global__ void __launch_bounds__(kThreads) score_kernel(DhsaDecodeArgs a) {
   }
   int32_t pieces_all;
   int32_t q = block_exclusive_scan(pieces, part, &pieces_all);
+  HSA_DCHECK(pieces_all <= a.max_pieces);
   if (tid == 0) a.n_plan[bh] = pieces_all;
   int32_t* plan = a.plan + bh * a.max_pieces * 2;
   for (int p = p0; p < min(p0 + per, nc); ++p) {
@@ -320,6 +323,8 @@ __global__ void __launch_bounds__(kWave) attend_kernel(DhsaDecodeArgs a, float s
   if (q >= a.n_plan[bh]) return;
   const int start = a.plan[(bh * a.max_pieces + q) * 2];
   const int nk = a.plan[(bh * a.max_pieces + q) * 2 + 1];
+  // a piece holds 1..64 keys, all at or before the new query's position
+  HSA_DCHECK(start >= 0 && nk >= 1 && nk <= kPiece && start + nk <= a.pos + 1);
   const int lane = threadIdx.x;
   constexpr int CPL = D / 64;
   constexpr int VE = DT == kF32 ? 4 : 8;
@@ -460,15 +465,16 @@ hipError_t decode_dt(const DhsaDecodeArgs& a, int stage, hipStream_t stream) {
   const int64_t BH = (int64_t)a.B * a.H;
   switch (stage) {
     case 0:
-      score_kernel<D, DT><<<dim3((unsigned)BH), dim3(kThreads), dhsa_score_lds(a.P), stream>>>(a);
+      launch<score_kernel<D, DT>>(dim3((unsigned)BH), dim3(kThreads), dhsa_score_lds(a.P), stream,
+                                  a);
       break;
     case 1:
-      attend_kernel<D, DT><<<dim3((unsigned)(BH * a.max_pieces)), dim3(kWave), 0, stream>>>(
-          a, 1.0f / sqrtf((float)D));
+      launch<attend_kernel<D, DT>>(dim3((unsigned)(BH * a.max_pieces)), dim3(kWave), 0, stream, a,
+                                   1.0f / sqrtf((float)D));
       break;
     default:
-      combine_kernel<D, DT><<<dim3((unsigned)BH), dim3(kThreads),
-                              (size_t)a.max_pieces * sizeof(float), stream>>>(a);
+      launch<combine_kernel<D, DT>>(dim3((unsigned)BH), dim3(kThreads),
+                                    (size_t)a.max_pieces * sizeof(float), stream, a);
       break;
   }
   return hipGetLastError();
@@ -496,18 +502,18 @@ hipError_t launch_dhsa_chunk_keys(const void* K, float* khat, const int32_t* off
   const dim3 grid((unsigned)(BH * nchunks)), block(kThreads);
   if (d == 64) {
     if (dtype == kF32)
-      chunk_keys_kernel<64, kF32><<<grid, block, 0, stream>>>(K, khat, offs, n_max, n_cap,
-                                                              chunk_begin, nchunks);
+      launch<chunk_keys_kernel<64, kF32>>(grid, block, 0, stream, K, khat, offs, n_max, n_cap,
+                                          chunk_begin, nchunks);
     else
-      chunk_keys_kernel<64, kBF16><<<grid, block, 0, stream>>>(K, khat, offs, n_max, n_cap,
-                                                               chunk_begin, nchunks);
+      launch<chunk_keys_kernel<64, kBF16>>(grid, block, 0, stream, K, khat, offs, n_max, n_cap,
+                                           chunk_begin, nchunks);
   } else {
     if (dtype == kF32)
-      chunk_keys_kernel<128, kF32><<<grid, block, 0, stream>>>(K, khat, offs, n_max, n_cap,
-                                                               chunk_begin, nchunks);
+      launch<chunk_keys_kernel<128, kF32>>(grid, block, 0, stream, K, khat, offs, n_max, n_cap,
+                                           chunk_begin, nchunks);
     else
-      chunk_keys_kernel<128, kBF16><<<grid, block, 0, stream>>>(K, khat, offs, n_max, n_cap,
-                                                                chunk_begin, nchunks);
+      launch<chunk_keys_kernel<128, kBF16>>(grid, block, 0, stream, K, khat, offs, n_max, n_cap,
+                                            chunk_begin, nchunks);
   }
   return hipGetLastError();
 }

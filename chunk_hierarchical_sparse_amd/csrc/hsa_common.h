@@ -21,6 +21,59 @@ typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Every kernel of the library is launched through launch<Kernel>(grid,
+// block, dynamic LDS bytes, stream, kernel arguments...), which prints the
+// launch when HSA_ATTN_LOG is set (launch_log_enabled, kernels.h).
+// HSA_DCHECK(cond): in the debug library a failed condition is counted, and
+// the source line and a tag of the source file of the first failure are
+// kept in this translation unit's own counters; the kernel carries on (no
+// trap).  Every file with checks names itself once with HSA_DCHECK_SOURCE()
+// so the tag maps back to its path.  The release library compiles both away.
+constexpr uint32_t source_tag(const char* s, uint32_t h = 2166136261u) {  // FNV-1a
+  return *s ? source_tag(s + 1, (h ^ (uint32_t)(unsigned char)*s) * 16777619u) : h;
+}
+#define HSA_DCHECK_CAT2(a, b) a##b
+#define HSA_DCHECK_CAT(a, b) HSA_DCHECK_CAT2(a, b)
+#if HSA_DEVICE_CHECKS
+namespace {
+__device__ uint32_t g_checks[3];  // failures, line of the first, its source tag
+hipError_t read_checks(uint32_t counters[3]) {
+  return hipMemcpyFromSymbol(counters, HIP_SYMBOL(g_checks), sizeof(g_checks));
+}
+hipError_t clear_checks() {
+  const uint32_t zero[3] = {0u, 0u, 0u};
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_checks), zero, sizeof(zero));
+}
+const bool g_checks_registered = register_device_checks(read_checks, clear_checks);
+}  // namespace
+#define HSA_DCHECK(cond)                                            \
+  do {                                                              \
+    if (!(cond)) {                                                  \
+      constexpr uint32_t tag_ = ::hsa::source_tag(__FILE__);        \
+      if (atomicAdd(&::hsa::g_checks[0], 1u) == 0u) {               \
+        ::hsa::g_checks[1] = __LINE__;                              \
+        ::hsa::g_checks[2] = tag_;                                  \
+      }                                                             \
+    }                                                               \
+  } while (0)
+#define HSA_DCHECK_SOURCE()                                                       \
+  namespace {                                                                     \
+  const bool HSA_DCHECK_CAT(g_source_, __LINE__) =                                \
+      ::hsa::register_check_source(::hsa::source_tag(__FILE__), __FILE__);        \
+  }
+#else
+#define HSA_DCHECK(cond) \
+  do {                   \
+  } while (0)
+#define HSA_DCHECK_SOURCE()
+#endif
+
+template <auto Kern, typename... Args>
+inline void launch(dim3 grid, dim3 block, size_t lds, hipStream_t stream, const Args&... args) {
+  if (launch_log_enabled()) log_launch((const void*)Kern, grid, block, lds, stream);
+  Kern<<<grid, block, lds, stream>>>(args...);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }

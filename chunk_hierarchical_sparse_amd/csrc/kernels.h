@@ -14,7 +14,27 @@ namespace hsa {
 enum : int { kF32 = 0, kBF16 = 1 };
 
 // ---- shared ----------------------------------------------------------------
+// HSA_ATTN_LOG set to a non-zero value in the environment: every entry point
+// prints its shapes and every kernel launch its instantiated name, grid,
+// block and dynamic LDS bytes to stderr (api.cpp).
+bool launch_log_enabled();
+void log_launch(const void* kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream);
+
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream);
+
+// Device checks of the debug library (built with HSA_DEVICE_CHECKS=1, loaded
+// when HSA_ATTN_DEBUG=1): each translation unit registers readers of its own
+// check counters at load time, and each source file with checks its tag and
+// path (hsa_common.h); after an entry point's launches the library
+// synchronises the stream and reports the first failed check (api.cpp).  In
+// the release library nothing registers.
+typedef hipError_t (*CheckRead)(uint32_t counters[3]);  // failures, line, source tag
+typedef hipError_t (*CheckClear)();
+bool register_device_checks(CheckRead read, CheckClear clear);
+bool register_check_source(uint32_t tag, const char* path);
+// A one-block kernel whose single check fails when `fail` is non-zero
+// (landmarks.hip); the debug library's self-test.
+hipError_t launch_check_selftest(int fail, hipStream_t stream);
 
 // Records `message` as the calling thread's last error (hsa_last_error_message)
 // and returns `status` (an hsa_status_t value).

@@ -10,6 +10,8 @@
 #include "kernels.h"
 
 namespace hsa {
+
+HSA_DCHECK_SOURCE()
 namespace {
 
 constexpr int kThreads = 256;
@@ -33,6 +35,7 @@ __global__ void __launch_bounds__(kThreads)
   for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 
   const int64_t row0 = bh * slab_tokens + c * (int64_t)S;
+  HSA_DCHECK(c < lmk_chunks && (c + 1) * S <= slab_tokens);
 #pragma unroll 4
   for (int j = rs; j < S; j += row_sets) {
     const int64_t off = (row0 + j) * d + cg * VEC;
@@ -71,11 +74,11 @@ hipError_t launch_landmarks(const void* K, int dtype, float* lmk, int64_t BH, in
   const int VEC = dtype == kF32 ? 4 : 8;
   const size_t lds = (size_t)(kThreads / (d / VEC)) * d * sizeof(float);
   if (dtype == kF32)
-    landmark_kernel<kF32><<<dim3((unsigned)blocks), dim3(kThreads), lds, stream>>>(
-        K, lmk, slab_tokens, lmk_chunks, d, S, c0, nchunks);
+    launch<landmark_kernel<kF32>>(dim3((unsigned)blocks), dim3(kThreads), lds, stream, K, lmk,
+                                  slab_tokens, lmk_chunks, d, S, c0, nchunks);
   else
-    landmark_kernel<kBF16><<<dim3((unsigned)blocks), dim3(kThreads), lds, stream>>>(
-        K, lmk, slab_tokens, lmk_chunks, d, S, c0, nchunks);
+    launch<landmark_kernel<kBF16>>(dim3((unsigned)blocks), dim3(kThreads), lds, stream, K, lmk,
+                                   slab_tokens, lmk_chunks, d, S, c0, nchunks);
   return hipGetLastError();
 }
 
@@ -85,13 +88,24 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t value) {
        i += (int64_t)gridDim.x * blockDim.x)
     p[i] = value;
 }
+
+// One thread checks that `fail` is zero: the debug library's self-test of
+// the device-check path (no memory is touched either way).
+__global__ void check_selftest_kernel(int fail) {
+  if (threadIdx.x == 0) HSA_DCHECK(fail == 0);
+}
 }  // namespace
+
+hipError_t launch_check_selftest(int fail, hipStream_t stream) {
+  launch<check_selftest_kernel>(dim3(1), dim3(64), 0, stream, fail);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  fill_i32_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p, n, value);
+  launch<fill_i32_kernel>(dim3((unsigned)blocks), dim3(256), 0, stream, p, n, value);
   return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@
 #include "prefill_common.h"
 
 namespace hsa {
+
+HSA_DCHECK_SOURCE()
 namespace {
 
 constexpr int kThreads = 256;
@@ -450,6 +452,7 @@ __global__ void __launch_bounds__(256) count_kernel(PrefillArgs a, int64_t block
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (c[u] < 0) continue;
+      HSA_DCHECK(c[u] < a.n);
       if (use_lds)
         atomicAdd(&hist[c[u]], 1);
       else
@@ -533,6 +536,7 @@ __global__ void __launch_bounds__(256) scatter_ordered_kernel(PrefillArgs a,
       const uint32_t below = (1u << (tl & 31)) - 1u;
       rank[u] = tl < 32 ? __popc(lo & below) : __popc(lo) + __popc(hi & below);
       const int32_t p = run[c[u]] + rank[u];
+      HSA_DCHECK(p >= offs[c[u]] && p < offs[c[u] + 1]);
       const int64_t i = e0 + e;
       list[p] = (int32_t)(((i / K) << kSlotBits) | (i % K));
       epos[i] = p;
@@ -572,6 +576,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
       const int32_t c = idx[sel_of(a, i)];
       if (c >= 0) {
         const int32_t p = offs[c] + atomicAdd(&cursor[c], 1);
+        HSA_DCHECK(p < offs[c + 1]);
         list[p] = (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
         epos[i] = p;
       }
@@ -602,6 +607,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(PrefillArgs a, int64_t blo
       if (c[u] < 0) continue;
       const int64_t i = i0 + 256 * u;
       const int32_t p = atomicAdd(&pos[c[u]], 1);
+      HSA_DCHECK(p >= offs[c[u]] && p < offs[c[u] + 1]);
       list[p] = (int32_t)(((i / a.topk) << kSlotBits) | (i % a.topk));
       epos[i] = p;
     }
@@ -753,7 +759,10 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(PrefillArgs a) {
   for (int k = 0; k < KM; ++k) ep[k] = epos[min(k, a.topk - 1)];  // in bounds; unused past m
   int64_t pr[KM];
 #pragma unroll
-  for (int k = 0; k < KM; ++k) pr[k] = k < m ? partial_row(a, bg, ep[k], hh) : 0;
+  for (int k = 0; k < KM; ++k) {
+    HSA_DCHECK(k >= m || (ep[k] >= 0 && (int64_t)ep[k] < a.L * a.topk));
+    pr[k] = k < m ? partial_row(a, bg, ep[k], hh) : 0;
+  }
   u32x4 x[KM];
   float s[KM];
 #pragma unroll
@@ -819,10 +828,11 @@ hipError_t launch_select_dt(const PrefillArgs& a, hipStream_t stream) {
   const int64_t nqt = (a.nq + 63) / 64;
   const int64_t blocks = (int64_t)a.B * a.Hkv * nqt;
   if (a.dtype == kF32)
-    select_valu_kernel<D, KM, kF32><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, nqt);
+    launch<select_valu_kernel<D, KM, kF32>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
+                                            nqt);
   else
-    select_valu_kernel<D, KM, kBF16><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a,
-                                                                                           nqt);
+    launch<select_valu_kernel<D, KM, kBF16>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
+                                             nqt);
   return hipGetLastError();
 }
 
@@ -830,7 +840,7 @@ template <int D, int KM>
 hipError_t launch_select_mfma(const PrefillArgs& a, hipStream_t stream) {
   const int64_t nqt = (a.nq + 127) / 128;
   const int64_t blocks = (int64_t)a.B * a.Hkv * nqt;
-  select_mfma_kernel<D, KM><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, nqt);
+  launch<select_mfma_kernel<D, KM>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, nqt);
   return hipGetLastError();
 }
 
@@ -868,14 +878,15 @@ hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream) {
   const int use_lds = a.n <= kInvertLdsBins;
   const bool ordered = a.ordered && a.n <= kInvertDetBins;
   const size_t lds1 = use_lds ? (size_t)a.n * sizeof(int32_t) : 0;
-  count_kernel<<<dim3((unsigned)(BG * bpb)), dim3(256), lds1, stream>>>(a, bpb, use_lds);
+  launch<count_kernel>(dim3((unsigned)(BG * bpb)), dim3(256), lds1, stream, a, bpb, use_lds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  scan_kernel<<<dim3((unsigned)BG), dim3(1024), 0, stream>>>(a);
+  launch<scan_kernel>(dim3((unsigned)BG), dim3(1024), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ordered)
-    scatter_ordered_kernel<<<dim3((unsigned)(BG * bpb)), dim3(256), 3 * lds1, stream>>>(a, bpb);
+    launch<scatter_ordered_kernel>(dim3((unsigned)(BG * bpb)), dim3(256), 3 * lds1, stream, a, bpb);
   else
-    scatter_kernel<<<dim3((unsigned)(BG * bpb)), dim3(256), 2 * lds1, stream>>>(a, bpb, use_lds);
+    launch<scatter_kernel>(dim3((unsigned)(BG * bpb)), dim3(256), 2 * lds1, stream, a, bpb,
+                           use_lds);
   return hipGetLastError();
 }
 
@@ -886,33 +897,33 @@ hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream) {
   const float score_scale = scale;
   if (a.dtype == kF32) {
     if (a.d == 64)
-      attend_f32_kernel<64><<<dim3((unsigned)blocks), dim3(64), 0, stream>>>(a, scale,
-                                                                             score_scale);
+      launch<attend_f32_kernel<64>>(dim3((unsigned)blocks), dim3(64), 0, stream, a, scale,
+                                    score_scale);
     else
-      attend_f32_kernel<128><<<dim3((unsigned)blocks), dim3(64), 0, stream>>>(a, scale,
-                                                                              score_scale);
+      launch<attend_f32_kernel<128>>(dim3((unsigned)blocks), dim3(64), 0, stream, a, scale,
+                                     score_scale);
   } else if (a.S <= kKeyBlock) {
     const float sl2 = scale * 1.4426950408889634f;
     const dim3 grid((unsigned)blocks), block(kThreads);
     if (a.d == 64) {
       if (a.S == kKeyBlock)
-        attend_chunk_bf16_kernel<64, true><<<grid, block, 0, stream>>>(a, sl2, score_scale);
+        launch<attend_chunk_bf16_kernel<64, true>>(grid, block, 0, stream, a, sl2, score_scale);
       else
-        attend_chunk_bf16_kernel<64, false><<<grid, block, 0, stream>>>(a, sl2, score_scale);
+        launch<attend_chunk_bf16_kernel<64, false>>(grid, block, 0, stream, a, sl2, score_scale);
     } else {
       if (a.S == kKeyBlock)
-        attend_chunk_bf16_kernel<128, true><<<grid, block, 0, stream>>>(a, sl2, score_scale);
+        launch<attend_chunk_bf16_kernel<128, true>>(grid, block, 0, stream, a, sl2, score_scale);
       else
-        attend_chunk_bf16_kernel<128, false><<<grid, block, 0, stream>>>(a, sl2, score_scale);
+        launch<attend_chunk_bf16_kernel<128, false>>(grid, block, 0, stream, a, sl2, score_scale);
     }
   } else {
     const float sl2 = scale * 1.4426950408889634f;
     if (a.d == 64)
-      attend_bf16_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2,
-                                                                                    score_scale);
+      launch<attend_bf16_kernel<64>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, sl2,
+                                     score_scale);
     else
-      attend_bf16_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(
-          a, sl2, score_scale);
+      launch<attend_bf16_kernel<128>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, sl2,
+                                      score_scale);
   }
   return hipGetLastError();
 }
@@ -920,11 +931,11 @@ hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream) {
 template <int D, int DT>
 hipError_t launch_fuse_dt(const PrefillArgs& a, int64_t blocks, hipStream_t stream) {
   if (a.topk <= 8)
-    fuse_kernel<D, DT, 8><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
+    launch<fuse_kernel<D, DT, 8>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else if (a.topk <= 16)
-    fuse_kernel<D, DT, 16><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
+    launch<fuse_kernel<D, DT, 16>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   else
-    fuse_kernel<D, DT, 32><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a);
+    launch<fuse_kernel<D, DT, 32>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

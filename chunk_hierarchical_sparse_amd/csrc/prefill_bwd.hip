@@ -34,6 +34,8 @@
 #include "prefill_common.h"
 
 namespace hsa {
+
+HSA_DCHECK_SOURCE()
 namespace {
 
 constexpr int kThreads = 256;
@@ -108,6 +110,7 @@ __device__ __forceinline__ void load_row_pair_nb(const PrefillBwdArgs& ba, int64
                                                  int64_t qplane, int32_t entry, int hh, int hf,
                                                  u32x4 (&q)[D / 16], u32x4 (&o)[D / 16]) {
   const int64_t tok = entry >= 0 ? (int64_t)(entry >> kSlotBits) : 0;
+  HSA_DCHECK(tok < ba.p.L);
   const int64_t off = qbase + (int64_t)hh * qplane + tok * D + 8 * hf;
   const uint16_t* qr = (const uint16_t*)ba.p.Q + off;
   const uint16_t* orow = (const uint16_t*)ba.dO + off;
@@ -125,6 +128,7 @@ __device__ __forceinline__ void load_row_pair(const PrefillBwdArgs& ba, int64_t 
                                               int64_t qplane, int32_t entry, int hh, int hf,
                                               u32x4 (&q)[D / 16], u32x4 (&o)[D / 16]) {
   if (entry >= 0) {
+    HSA_DCHECK((int64_t)(entry >> kSlotBits) < ba.p.L);
     const int64_t off = qbase + (int64_t)hh * qplane + (int64_t)(entry >> kSlotBits) * D + 8 * hf;
     const uint16_t* qr = (const uint16_t*)ba.p.Q + off;
     const uint16_t* orow = (const uint16_t*)ba.dO + off;
@@ -174,6 +178,8 @@ __global__ void __launch_bounds__(kThreads) bwd_weights_kernel(PrefillBwdArgs ba
     const int kk = min(k, a.topk - 1);
     ep[k] = epos[kk];
     ck[k] = sel[kk];
+    HSA_DCHECK(k >= m || (ck[k] >= 0 && ck[k] < a.n && ep[k] >= 0 &&
+                          (int64_t)ep[k] < a.L * a.topk));
   }
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
@@ -638,6 +644,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(PrefillBwdArgs ba, flo
     const int kk = min(k, a.topk - 1);
     ep[k] = epos[kk];
     ck[k] = sel[kk];
+    HSA_DCHECK(k >= m || (ck[k] >= 0 && ck[k] < a.n && ep[k] >= 0 &&
+                          (int64_t)ep[k] < a.L * a.topk));
   }
   u32x4 x[KM];
   float dsk[KM];
@@ -679,11 +687,11 @@ hipError_t finish_d(const PrefillBwdArgs& ba, hipStream_t stream) {
   const unsigned nb = (unsigned)((rows + rpb - 1) / rpb);
   const float sc = 1.0f / sqrtf((float)D);
   if (a.topk <= 8)
-    bwd_dq_kernel<D, 8><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+    launch<bwd_dq_kernel<D, 8>>(dim3(nb), dim3(kThreads), 0, stream, ba, sc);
   else if (a.topk <= 16)
-    bwd_dq_kernel<D, 16><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+    launch<bwd_dq_kernel<D, 16>>(dim3(nb), dim3(kThreads), 0, stream, ba, sc);
   else
-    bwd_dq_kernel<D, 32><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+    launch<bwd_dq_kernel<D, 32>>(dim3(nb), dim3(kThreads), 0, stream, ba, sc);
   return hipGetLastError();
 }
 
@@ -699,18 +707,18 @@ hipError_t prefill_bwd_weights(const PrefillBwdArgs& ba, hipStream_t stream) {
   const float sc = 1.0f / sqrtf((float)a.d);
   if (a.d == 64) {
     if (a.topk <= 8)
-      bwd_weights_kernel<64, 8><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+      launch<bwd_weights_kernel<64, 8>>(dim3(nb), dim3(kThreads), 0, stream, ba, sc);
     else if (a.topk <= 16)
-      bwd_weights_kernel<64, 16><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+      launch<bwd_weights_kernel<64, 16>>(dim3(nb), dim3(kThreads), 0, stream, ba, sc);
     else
-      bwd_weights_kernel<64, 32><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+      launch<bwd_weights_kernel<64, 32>>(dim3(nb), dim3(kThreads), 0, stream, ba, sc);
   } else {
     if (a.topk <= 8)
-      bwd_weights_kernel<128, 8><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+      launch<bwd_weights_kernel<128, 8>>(dim3(nb), dim3(kThreads), 0, stream, ba, sc);
     else if (a.topk <= 16)
-      bwd_weights_kernel<128, 16><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+      launch<bwd_weights_kernel<128, 16>>(dim3(nb), dim3(kThreads), 0, stream, ba, sc);
     else
-      bwd_weights_kernel<128, 32><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba, sc);
+      launch<bwd_weights_kernel<128, 32>>(dim3(nb), dim3(kThreads), 0, stream, ba, sc);
   }
   return hipGetLastError();
 }
@@ -722,9 +730,9 @@ hipError_t prefill_bwd_score(const PrefillBwdArgs& ba, hipStream_t stream) {
   const float sc = 1.0f / sqrtf((float)a.d);
   const float sl2 = sc * 1.4426950408889634f;
   if (a.d == 64)
-    bwd_score_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(ba, sl2, sc);
+    launch<bwd_score_kernel<64>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, ba, sl2, sc);
   else
-    bwd_score_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(ba, sl2, sc);
+    launch<bwd_score_kernel<128>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, ba, sl2, sc);
   return hipGetLastError();
 }
 
@@ -734,11 +742,11 @@ hipError_t prefill_bwd_rows(const PrefillBwdArgs& ba, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.L;
   const unsigned nb = (unsigned)((rows + kThreads - 1) / kThreads);
   if (a.topk <= 8)
-    bwd_rows_kernel<8><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba);
+    launch<bwd_rows_kernel<8>>(dim3(nb), dim3(kThreads), 0, stream, ba);
   else if (a.topk <= 16)
-    bwd_rows_kernel<16><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba);
+    launch<bwd_rows_kernel<16>>(dim3(nb), dim3(kThreads), 0, stream, ba);
   else
-    bwd_rows_kernel<32><<<dim3(nb), dim3(kThreads), 0, stream>>>(ba);
+    launch<bwd_rows_kernel<32>>(dim3(nb), dim3(kThreads), 0, stream, ba);
   return hipGetLastError();
 }
 
@@ -755,9 +763,9 @@ hipError_t prefill_bwd_kv(const PrefillBwdArgs& ba, hipStream_t stream) {
   const float sl2 = sc * 1.4426950408889634f;
   const float rs = 1.0f / sqrtf((float)a.S);
   if (a.d == 64)
-    bwd_kv_kernel<64><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(ba, sl2, sc, rs);
+    launch<bwd_kv_kernel<64>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, ba, sl2, sc, rs);
   else
-    bwd_kv_kernel<128><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(ba, sl2, sc, rs);
+    launch<bwd_kv_kernel<128>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, ba, sl2, sc, rs);
   return hipGetLastError();
 }
 

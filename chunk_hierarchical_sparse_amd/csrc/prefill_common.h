@@ -9,6 +9,8 @@
 
 namespace hsa {
 
+HSA_DCHECK_SOURCE()
+
 // Partial outputs and their retrieval scores share one row index, in list
 // order: row (e * G + head of the group) for entry e of the (b, group)'s
 // chunk lists.  A tile's rows are consecutive entries of one list, so the
@@ -32,9 +34,11 @@ __device__ __forceinline__ bool locate_tile(const PrefillArgs& a, int64_t blk, i
   const int32_t* toff = a.tile_off + bg * (a.n + 1);
   if (tile >= toff[a.n]) return false;
   c = a.tile_chunk[bg * a.tiles_ub + tile];
+  HSA_DCHECK(c >= 0 && c < a.n);
   const int32_t* offs = a.offs + bg * (a.n + 1);
   e0 = offs[c] + (int)(tile - toff[c]) * a.entries_per_tile;
   e1 = min(e0 + a.entries_per_tile, offs[c + 1]);
+  HSA_DCHECK(e0 >= offs[c] && e0 < e1 && (int64_t)e1 <= a.L * a.topk);
   return true;
 }
 

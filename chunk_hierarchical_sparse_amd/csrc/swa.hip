@@ -25,6 +25,8 @@
 #include "swa_core.h"
 
 namespace hsa {
+
+HSA_DCHECK_SOURCE()
 namespace {
 
 constexpr int kThreads = 256;
@@ -118,6 +120,7 @@ __global__ void __launch_bounds__(kDecWaves * kWave) decode_kernel(SwaArgs a, fl
   for (int64_t pc = w; pc < np; pc += kDecWaves) {
     const int64_t start = k0 + (int64_t)pc * kPiece;
     const int nk = (int)min((int64_t)kPiece, a.n_ctx - start);
+    HSA_DCHECK(start >= 0 && nk >= 1 && start + nk <= a.L);
     // keys past nk re-read the piece's last key (in bounds, weight zero)
     const int64_t row = start + min(lane, nk - 1);
     u32x4 kx[D / VE];
@@ -222,8 +225,8 @@ hipError_t prefill_d(const SwaArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   if (a.dtype == kF32) {
     const int64_t rows = (int64_t)a.B * a.Hq * a.L;
-    prefill_f32_kernel<D><<<dim3((unsigned)((rows + 63) / 64)), dim3(64), 0, stream>>>(
-        a, 1.0f / sqrtf((float)D));
+    launch<prefill_f32_kernel<D>>(dim3((unsigned)((rows + 63) / 64)), dim3(64), 0, stream, a,
+                                  1.0f / sqrtf((float)D));
     return hipGetLastError();
   }
   const int GT = heads_per_block(G);
@@ -232,11 +235,14 @@ hipError_t prefill_d(const SwaArgs& a, hipStream_t stream) {
   const int64_t blocks = (units + kXcds - 1) / kXcds * kXcds;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   if (GT == 4)
-    prefill_bf16_kernel<D, 4><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2, units);
+    launch<prefill_bf16_kernel<D, 4>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, sl2,
+                                      units);
   else if (GT == 2)
-    prefill_bf16_kernel<D, 2><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2, units);
+    launch<prefill_bf16_kernel<D, 2>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, sl2,
+                                      units);
   else
-    prefill_bf16_kernel<D, 1><<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(a, sl2, units);
+    launch<prefill_bf16_kernel<D, 1>>(dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, sl2,
+                                      units);
   return hipGetLastError();
 }
 
@@ -248,11 +254,11 @@ hipError_t decode_d(const SwaArgs& a, hipStream_t stream) {
   const float scale = 1.0f / sqrtf((float)D);
   const dim3 th(kDecWaves * kWave);
   if (GT == 4)
-    decode_kernel<D, DT, 4><<<dim3(blocks), th, 0, stream>>>(a, scale);
+    launch<decode_kernel<D, DT, 4>>(dim3(blocks), th, 0, stream, a, scale);
   else if (GT == 2)
-    decode_kernel<D, DT, 2><<<dim3(blocks), th, 0, stream>>>(a, scale);
+    launch<decode_kernel<D, DT, 2>>(dim3(blocks), th, 0, stream, a, scale);
   else
-    decode_kernel<D, DT, 1><<<dim3(blocks), th, 0, stream>>>(a, scale);
+    launch<decode_kernel<D, DT, 1>>(dim3(blocks), th, 0, stream, a, scale);
   return hipGetLastError();
 }
 

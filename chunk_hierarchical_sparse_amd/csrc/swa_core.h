@@ -17,6 +17,8 @@
 
 namespace hsa {
 
+HSA_DCHECK_SOURCE()
+
 constexpr int kSwaXcds = 8;
 
 template <int D, int GT>
@@ -51,6 +53,7 @@ __device__ __forceinline__ void swa_prefill_body(const SwaArgs& a, float scale_l
                     valid);
   const int t_end = min(Li, tb + MQ);
   const int k_lo = max(0, tb - W + 1);
+  HSA_DCHECK(tb >= 0 && tb < Li && k_lo <= tb && t_end <= Li);
   KVRegsWide<D> rg;
   fetch_kv_wide<D>(rg, Kb + (int64_t)k_lo * D, Vb + (int64_t)k_lo * D,
                    min(kWideBlock, t_end - k_lo));

@@ -63,14 +63,14 @@ hipError_t launch_d(const PrefillArgs& pa, const SwaArgs& sa, hipStream_t stream
   const float sl2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)(n_hsa8 + n_swa8)), block(kChunkThreads);
   if (GT == 4)
-    upper_attend_kernel<D, S64, 4><<<grid, block, 0, stream>>>(pa, sa, sl2, scale, n_hsa8,
-                                                               n_swa_units, n_swa8);
+    launch<upper_attend_kernel<D, S64, 4>>(grid, block, 0, stream, pa, sa, sl2, scale, n_hsa8,
+                                           n_swa_units, n_swa8);
   else if (GT == 2)
-    upper_attend_kernel<D, S64, 2><<<grid, block, 0, stream>>>(pa, sa, sl2, scale, n_hsa8,
-                                                               n_swa_units, n_swa8);
+    launch<upper_attend_kernel<D, S64, 2>>(grid, block, 0, stream, pa, sa, sl2, scale, n_hsa8,
+                                           n_swa_units, n_swa8);
   else
-    upper_attend_kernel<D, S64, 1><<<grid, block, 0, stream>>>(pa, sa, sl2, scale, n_hsa8,
-                                                               n_swa_units, n_swa8);
+    launch<upper_attend_kernel<D, S64, 1>>(grid, block, 0, stream, pa, sa, sl2, scale, n_hsa8,
+                                           n_swa_units, n_swa8);
   return hipGetLastError();
 }
 

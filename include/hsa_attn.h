@@ -207,7 +207,8 @@ hsa_status_t hsa_decode_noalloc(const void* q, const void* Kc, const void* Vc, c
 /*
  * DHSA prefill ([DHSA] "What carries the argument", Eq. 4, tiling rule,
  * Algorithm 1 top-N_b preceding keys).
- *   Q, K, V  [B,H,L,d] dtype (bf16 only in this build).
+ *   Q, K, V  [B,H,L,d] dtype (F32 or BF16; fp32 runs on the VALU in fp32,
+ *            bf16 on the bf16 MFMA with fp32 accumulation).
  *   offsets  HOST int32 [n_chunks+1], 0 = b_0 < b_1 < ... < b_n = L: chunk l
  *            holds tokens b_l .. b_{l+1}-1; the same boundaries for every
  *            batch entry and head.
@@ -380,6 +381,31 @@ hsa_status_t hsa_swa_decode(const void* q, const void* Kc, const void* Vc, const
  */
 hsa_status_t hsa_profile_enable(int enable);
 int hsa_profile_read(double* stage_ms, int max_stages, int* n_stages);
+
+/*
+ * Debugging aids (not part of the method).
+ *
+ * HSA_ATTN_LOG set to a non-zero value in the environment (read once per
+ * process): every entry point prints a line with its name and shapes to
+ * stderr, every kernel launch a line with the kernel's name and template
+ * arguments, grid, block and dynamic LDS bytes, and every rejected call its
+ * status and message.
+ *
+ * The debug library (libhsa_attn_debug.so, built beside the release one with
+ * device checks compiled in; the Python binding loads it when HSA_ATTN_DEBUG
+ * is 1) checks the kernels' gather indices against the buffers they address:
+ * a failed check is counted and the kernel carries on.  Each entry point of
+ * that library then synchronises its stream and returns HSA_ERR_HIP with the
+ * source file and line of the first failed check (the counters are cleared),
+ * so it is for testing, not for capture into a graph.
+ *
+ * hsa_device_checks_enabled returns 1 in the debug library, 0 otherwise.
+ * hsa_device_checks_selftest launches a one-thread kernel whose single check
+ * fails when fail_check is non-zero (it touches no memory); the debug
+ * library then returns HSA_ERR_HIP, the release library HSA_ERR_UNSUPPORTED.
+ */
+int hsa_device_checks_enabled(void);
+hsa_status_t hsa_device_checks_selftest(int fail_check, hsa_stream_t stream);
 
 #ifdef __cplusplus
 }

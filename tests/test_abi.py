@@ -140,7 +140,8 @@ def test_dhsa_validation():
     assert dhsa([1, 10, 30]) == INV      # does not start at 0
     assert dhsa([0, 10, 30], L=31) == INV  # does not end at L
     assert dhsa([0, 10, 30], budget=0) == INV
-    assert dhsa([0, 10, 30], dt=F32) == UNS
+    assert dhsa([0, 10, 30], dt=F32) == WS  # fp32 accepted: only the workspace is missing
+    assert dhsa([0, 10, 30], dt=7) == UNS
     assert dhsa([0, 10, 30], d=80) == UNS
     assert dhsa([0, 10, 30], Q=None) == INV
     assert dhsa([0, 10, 30]) == WS
@@ -293,3 +294,64 @@ def test_hsa_swa_decode_validation():
     assert call() == WS and "workspace needs" in msg()
     assert lib().hsa_swa_decode_workspace_size(1, 4, 2, 128, 64, 8, 1000, 512) > \
         lib().hsa_decode_workspace_size(1, 4, 2, 128, 64, 8, 1000)
+
+
+LOG_SCRIPT = r"""
+import chunk_hierarchical_sparse_amd as hsa
+lib = hsa.load_library()
+st = lib.hsa_prefill(1, 1, 1, None, 1, None, None, 1, 256, 4, 2, 128, 0, 8, hsa.DTYPE_BF16,
+                     None, 0, None)
+assert st == hsa.HSA_ERR_INVALID_ARGUMENT, st
+"""
+
+
+@pytest.mark.parametrize("value,shown", [("1", True), ("0", False), ("", False)])
+def test_log_lines_name_the_call_and_its_status(value, shown):
+    # HSA_ATTN_LOG is read once per process, so each setting runs in a child
+    import subprocess
+    import sys
+    env = dict(os.environ, HSA_ATTN_LOG=value, PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", LOG_SCRIPT], env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("hsa_attn:")]
+    if not shown:
+        assert lines == []
+        return
+    assert lines[0] == "hsa_attn: hsa_prefill B=1 L=256 Hq=4 Hkv=2 d=128 S=0 topk=8 dtype=1"
+    assert lines[1].startswith("hsa_attn:   status 1: ") and "chunk size" in lines[1]
+
+
+def test_release_library_has_no_device_checks():
+    assert lib().hsa_device_checks_enabled() == 0
+    assert lib().hsa_device_checks_selftest(1, None) == UNS and "debug library" in msg()
+
+
+DEBUG_SCRIPT = r"""
+import re
+import chunk_hierarchical_sparse_amd as hsa
+path = hsa.lib_path()
+assert path.endswith("libhsa_attn_debug.so"), path
+lib = hsa.load_library()
+assert lib.hsa_device_checks_enabled() == 1
+import ctypes
+raw = ctypes.CDLL(path)
+text = open(HEADER).read()
+names = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(\w+)\(", text, re.M))
+missing = [n for n in names if not hasattr(raw, n)]
+assert not missing, missing
+st = lib.hsa_prefill(1, 1, 1, None, 1, None, None, 1, 256, 4, 2, 128, 0, 8, hsa.DTYPE_BF16,
+                     None, 0, None)
+assert st == hsa.HSA_ERR_INVALID_ARGUMENT, st
+print("ok")
+"""
+
+
+def test_debug_library_loads_with_device_checks():
+    # HSA_ATTN_DEBUG=1 selects the device-checked build of the same sources
+    import subprocess
+    import sys
+    env = dict(os.environ, HSA_ATTN_DEBUG="1", PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", f"HEADER = {HEADER!r}\n" + DEBUG_SCRIPT], env=env,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stderr[-3000:]

@@ -1,6 +1,6 @@
 """DHSA prefill on the GPU against the CPU oracle: the 16K-token workload
-(sampled rows, plus the budget property on every row), shape sweeps and the
-reductions (budget covering everything, unit chunks)."""
+(every row, plus the budget property on every row), shape sweeps and the
+reductions (budget covering everything, unit chunks), in bf16 and fp32."""
 import numpy as np
 import pytest
 import torch
@@ -13,9 +13,10 @@ from gpu_util import MARGIN, check_exempt, check_out, dev, host, qkv, say, unpac
 pytestmark = pytest.mark.gpu
 
 
-def run_case(B, H, L, d, offs, budget, seed, rows=None, check_order=True, block=2048):
-    say(f"dhsa case B={B} H={H} L={L} d={d} chunks={len(offs) - 1} budget={budget} seed={seed}")
-    Q, K, V = qkv(B, H, H, L, d, "bf16", seed)
+def run_case(B, H, L, d, offs, budget, seed, rows=None, check_order=True, block=2048, dt="bf16"):
+    say(f"dhsa case B={B} H={H} L={L} d={d} chunks={len(offs) - 1} budget={budget} seed={seed} "
+        f"{dt}")
+    Q, K, V = qkv(B, H, H, L, d, dt, seed)
     out, mask, order = hsa.dhsa_prefill(dev(Q), dev(K), dev(V), offs, budget, return_mask=True,
                                         return_order=True)
     torch.cuda.synchronize()
@@ -39,7 +40,7 @@ def run_case(B, H, L, d, offs, budget, seed, rows=None, check_order=True, block=
         assert not bad.any(), \
             f"kept sets differ above the margin at {np.argwhere(bad)[0].tolist()} (block {k0})"
         same = (bits == ref["kept"]).all(-1)
-        err = max(err, check_out(out[:, :, r][same], ref["out"][same], "bf16", "dhsa output"))
+        err = max(err, check_out(out[:, :, r][same], ref["out"][same], dt, "dhsa output"))
         n_strict += int(strict.sum())
         n_rows += strict.size
     exempt = check_exempt(np.arange(n_rows) < n_strict, "dhsa kept sets")
@@ -81,3 +82,22 @@ def test_dhsa_sweep(case):
     B, H, L, d, lo, hi, budget = case
     offs = synth.chunk_offsets(L, lo, hi, seed=90 + SWEEP.index(case))
     run_case(B, H, L, d, offs, budget, seed=90 + SWEEP.index(case))
+
+
+F32_SWEEP = [
+    # B, H, L, d, lo, hi, budget
+    (1, 2, 700, 128, 16, 128, 128),
+    (2, 2, 1000, 64, 5, 40, 200),
+    (1, 1, 300, 128, 1, 1, 37),       # unit chunks
+    (1, 2, 400, 64, 16, 64, 4096),    # dense causal
+    (1, 1, 600, 128, 100, 300, 150),  # chunks longer than a 128-row tile
+    (1, 2, 2048, 128, 16, 128, 512),
+]
+
+
+@pytest.mark.parametrize("case", F32_SWEEP, ids=[str(i) for i in range(len(F32_SWEEP))])
+def test_dhsa_f32_sweep(case):
+    # fp32 inputs run the fp32 attention (relative error <= 1e-5 of max |O|)
+    B, H, L, d, lo, hi, budget = case
+    offs = synth.chunk_offsets(L, lo, hi, seed=120 + F32_SWEEP.index(case))
+    run_case(B, H, L, d, offs, budget, seed=120 + F32_SWEEP.index(case), dt="f32")
