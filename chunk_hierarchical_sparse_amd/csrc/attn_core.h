@@ -110,6 +110,10 @@ __device__ __forceinline__ void wave_attn_init(WaveAttn<D>& st, const uint16_t* 
     for (int r = 0; r < 16; ++r) st.o[b][r] = 0.f;
   st.m = -INFINITY;
   st.l = 0.f;
+  // wait for the query rows here: left outstanding into a key loop, they
+  // make the compiler's wait before the loop's first MFMA cover every load
+  // issued since, including the next key block's prefetch
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 __device__ __forceinline__ bf16x8 cvt_bf16x8(const f32x16& p, int base) {
@@ -158,7 +162,7 @@ __device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>
     s1[r] = x1;
     mx = fmaxf(mx, fmaxf(x0, x1));
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  mx = half_pair_max(mx);
   const float m_new = fmaxf(st.m, mx);
   const float m_use = m_new == -INFINITY ? 0.f : m_new;
   const float alpha = fast_exp2(st.m - m_use);
@@ -169,7 +173,7 @@ __device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>
     s1[r] = fast_exp2(s1[r] - m_use);
     ps += s0[r] + s1[r];
   }
-  ps += __shfl_xor(ps, 32, kWave);
+  ps = half_pair_sum(ps);
   st.l = st.l * alpha + ps;
   st.m = m_new;
   bf16x8 pb4[4];
@@ -381,7 +385,7 @@ __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * scale_log2;
+    mx = half_pair_max(mx) * scale_log2;
     const float m_new = fmaxf(st.m, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     float ps = 0.f;
@@ -394,7 +398,7 @@ __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide
         ps += sc[t][r];
       }
     }
-    ps += __shfl_xor(ps, 32, kWave);
+    ps = half_pair_sum(ps);
     if (__ballot(m_new > st.m) != 0) {
       const float alpha = fast_exp2(st.m - m_use);
       st.l *= alpha;

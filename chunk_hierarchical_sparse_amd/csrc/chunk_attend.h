@@ -148,7 +148,7 @@ __device__ __forceinline__ void attend_chunk_body(const PrefillArgs& a, float sc
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = half_pair_max(mx);
     const float mxs = mx * scale_log2;
     float ps = 0.f;
 #pragma unroll
@@ -157,7 +157,7 @@ __device__ __forceinline__ void attend_chunk_body(const PrefillArgs& a, float sc
       s1[r] = fast_exp2(__builtin_fmaf(s1[r], scale_log2, -mxs));
       ps += s0[r] + s1[r];
     }
-    ps += __shfl_xor(ps, 32, kWave);
+    ps = half_pair_sum(ps);
     const float inv = 1.f / ps;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -210,8 +210,8 @@ __device__ __forceinline__ void attend_chunk_body(const PrefillArgs& a, float sc
         const uint32_t d0 = pack_bf16x2(o[bb][4 * q_odd], o[bb][4 * q_odd + 1]);
         const uint32_t d1 = pack_bf16x2(o[bb][4 * q_odd + 2], o[bb][4 * q_odd + 3]);
         // half 0 keeps the even group and sends the odd one; half 1 the reverse
-        const uint32_t got0 = __shfl_xor(hf ? e0 : d0, 32, kWave);
-        const uint32_t got1 = __shfl_xor(hf ? e1 : d1, 32, kWave);
+        const uint32_t got0 = half_pair_exchange(d0, e0, hf != 0);
+        const uint32_t got1 = half_pair_exchange(d1, e1, hf != 0);
         outv[bb][pr] = hf ? u32x4{got0, got1, d0, d1} : u32x4{e0, e1, got0, got1};
       }
     // rows of a tile are consecutive: (entry e_begin + r / G, head r % G),

@@ -21,6 +21,35 @@ typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// The values of lanes l % 32 and 32 + l % 32 of x, in every lane l: one
+// v_permlane32_swap of x with itself (no LDS round trip, no lane index).
+__device__ __forceinline__ f32x2 lane_halves(float x) {
+  const auto r =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// x[l] + x[l ^ 32] and max(x[l], x[l ^ 32]), in every lane (both lanes of a
+// pair get the same bits: the sum is taken in one order for both).
+__device__ __forceinline__ float half_pair_sum(float x) {
+  const f32x2 h = lane_halves(x);
+  return h[0] + h[1];
+}
+__device__ __forceinline__ float half_pair_max(float x) {
+  const f32x2 h = lane_halves(x);
+  return fmaxf(h[0], h[1]);
+}
+
+// The partner lane's (l ^ 32) value where lanes 0..31 offer lo_send and
+// lanes 32..63 offer hi_send: lanes 0..31 receive hi_send of lane l + 32,
+// lanes 32..63 receive lo_send of lane l - 32.
+__device__ __forceinline__ uint32_t half_pair_exchange(uint32_t lo_send, uint32_t hi_send,
+                                                       bool upper) {
+  const auto a = __builtin_amdgcn_permlane32_swap(hi_send, hi_send, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(lo_send, lo_send, false, false);
+  return upper ? b[0] : a[1];
+}
+
 // Every kernel of the library is launched through launch<Kernel>(grid,
 // block, dynamic LDS bytes, stream, kernel arguments...), which prints the
 // launch when HSA_ATTN_LOG is set (launch_log_enabled, kernels.h).

@@ -298,7 +298,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
       if (key + 32 >= a.S) s1[rr] = -INFINITY;
       mx = fmaxf(mx, fmaxf(s0[rr], s1[rr]));
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = half_pair_max(mx);
     const float mxs = mx * sl2;
     float ps = 0.f, pd = 0.f;
 #pragma unroll
@@ -308,8 +308,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
       ps += s0[rr] + s1[rr];
       pd += s0[rr] * p0[rr] + s1[rr] * p1[rr];
     }
-    ps += __shfl_xor(ps, 32, kWave);
-    pd += __shfl_xor(pd, 32, kWave);
+    ps = half_pair_sum(ps);
+    pd = half_pair_sum(pd);
     const float dw = pd / ps;
     // dS^T = w P^T (dP^T - dw), P = exp2(...) / ps; the / sqrt(d) of dQ too
     const float f = wr * sc / ps;
@@ -361,8 +361,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_score_kernel(PrefillBwdArgs b
         const uint32_t e1 = pack_bf16x2(dq[bb][8 * pr + 2], dq[bb][8 * pr + 3]);
         const uint32_t d0 = pack_bf16x2(dq[bb][8 * pr + 4], dq[bb][8 * pr + 5]);
         const uint32_t d1 = pack_bf16x2(dq[bb][8 * pr + 6], dq[bb][8 * pr + 7]);
-        const uint32_t got0 = __shfl_xor(hf ? e0 : d0, 32, kWave);
-        const uint32_t got1 = __shfl_xor(hf ? e1 : d1, 32, kWave);
+        const uint32_t got0 = half_pair_exchange(d0, e0, hf != 0);
+        const uint32_t got1 = half_pair_exchange(d1, e1, hf != 0);
         outv[bb][pr] = hf ? u32x4{got0, got1, d0, d1} : u32x4{e0, e1, got0, got1};
       }
     uint16_t* stg = sm.ostage[w];
