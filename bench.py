@@ -149,17 +149,32 @@ def to_dev(arr, torch):
 
 
 class Flush:
-    """Writes a 1 GiB scratch buffer on the current stream: run before every
-    timed call, outside its events, so that no call finds data the previous
-    one left in the L2 or the 256 MB Infinity Cache."""
+    """Cache flush run before every timed call, outside its events, so that no
+    call finds data the previous one left in the L2 or the 256 MB Infinity
+    Cache.  It writes a 1 GiB scratch buffer; in the default "write-read"
+    mode it then reads the buffer back.  A write alone leaves the last
+    ~288 MB it wrote dirty in the caches, and the timed call then pays for
+    writing them back to HBM as its own reads evict them (a probe of the
+    sliding-window decode's reads: 31-34 us after a write, 15-19 us after a
+    write followed by a read).  The read-back evicts them (written back
+    outside the events) and leaves clean lines of the scratch buffer, so the
+    timed call starts from cold, clean caches.  "write" keeps the write only."""
 
-    def __init__(self, torch, gib=1.0):
+    def __init__(self, torch, gib=1.0, mode="write-read"):
         self.buf = torch.empty(int(gib * (1 << 30)), dtype=torch.uint8, device="cuda")
+        self.words = self.buf.view(torch.int64)
+        self.mode = mode
         self.k = 0
 
     def __call__(self):
         self.k ^= 1
         self.buf.fill_(self.k)
+        if self.mode == "write-read":
+            self.words.max()  # reads every byte back; the result is not used
+
+    def describe(self):
+        return ("a 1 GiB cache-flush write, then a read of it" if self.mode == "write-read"
+                else "a 1 GiB cache-flush write")
 
 
 def _median(xs):
@@ -926,6 +941,9 @@ def main():
                          "decode16m, dhsa, dhsa_decode, swa, swa_decode, upper_prefill, "
                          "upper_decode, or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mode", choices=["write-read", "write"], default="write-read",
+                    help="cache flush before each timed call: a 1 GiB write, then a read of it "
+                         "(default), or the write alone")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="after the workloads, copy GIB GiB device-to-device twice (a plain "
@@ -961,7 +979,7 @@ def main():
     import chunk_hierarchical_sparse_amd as hsa
 
     torch.cuda.set_device(0)
-    args.flush = Flush(torch)
+    args.flush = Flush(torch, mode=args.flush_mode)
     args.copy_rate = measure_copy_rate(torch, args.flush)
     res, inputs = bench_prefill(torch, hsa, args)
     line = {"metric": METRIC, "value": res["value"], "unit": "queries/s", "n_gpus": 1,
@@ -972,7 +990,7 @@ def main():
             "traffic_floor": res["traffic_floor"],
             "ms_per_step_mean": res["ms_per_step_mean"],
             "timing": "median of K steps, each between its own HIP events on the library's "
-                      "stream after a 1 GiB cache-flush write outside the events"}
+                      "stream after " + args.flush.describe() + ", outside the events"}
     also = []
     extras = [e for e in args.extras.split(",") if e and e != "none"]
     for e in extras:
