@@ -50,9 +50,9 @@ __device__ __forceinline__ void clear_invert_counters(const PrefillArgs& a) {
 // Keep a descending top-KM list in registers.  Candidates of one lane
 // arrive in increasing index order, so a strict '>' places a later
 // equal-score candidate after the earlier one (lower index first).  The
-// list is sorted, so slot j becomes max(min(s, ls[j-1]), ls[j]) and its
-// index follows the same choice; both are written as min/max and bit
-// masks so the compiler emits straight-line code.
+// list is sorted, so slot j becomes max(min(s, ls[j-1]), ls[j]), which for
+// ls[j-1] >= ls[j] is the median of the three (one v_med3_f32), and its
+// index follows the same choice through bit masks: straight-line code.
 template <int KM>
 __device__ __forceinline__ void topk_insert_ordered(float (&ls)[KM], int (&li)[KM], float s,
                                                     int c) {
@@ -61,7 +61,7 @@ __device__ __forceinline__ void topk_insert_ordered(float (&ls)[KM], int (&li)[K
   for (int j = 0; j < KM; ++j) m[j] = -(int)(s > ls[j]);  // all ones where s beats slot j
 #pragma unroll
   for (int j = KM - 1; j > 0; --j) {
-    ls[j] = fmaxf(fminf(s, ls[j - 1]), ls[j]);
+    ls[j] = __builtin_amdgcn_fmed3f(s, ls[j - 1], ls[j]);
     const int t = (c & m[j]) | (li[j] & ~m[j]);
     li[j] = (li[j - 1] & m[j - 1]) | (t & ~m[j - 1]);
   }
@@ -220,6 +220,7 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
   const int64_t t = tq * a.interval;
   const bool tvalid = tq < a.nq;
   const int64_t navail = tvalid ? min(t / a.S, a.n) : 0;
+  const int navail_i = (int)navail;  // n < 2^26: 32-bit compares in the top-K upkeep
   const int64_t tlast_b = min(qt * QPB + QPB - 1, a.nq - 1) * a.interval;
   const int64_t bavail = min(tlast_b / a.S, a.n);
   const int64_t tlast_w = min(qt * QPB + w * 32 + 31, a.nq - 1) * a.interval;
@@ -331,7 +332,7 @@ __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a,
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int c = (int)c0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      topk_insert_ordered<KM>(ls, li, c < navail ? acc[r] : -INFINITY, c);
+      topk_insert_ordered<KM>(ls, li, c < navail_i ? acc[r] : -INFINITY, c);
     }
   }
   // merge the two halves of each query (lane l and l ^ 32)
