@@ -297,7 +297,7 @@ int swa_decode_pieces(int64_t n_ctx, int64_t window) {
 struct DhsaLayout {
   int32_t* offs;
   float *qh, *kh, *sc;
-  int32_t *order, *cumlen, *diag_pos;
+  int32_t *order, *cumlen, *diag_pos, *ranked;
   size_t bytes;
 };
 
@@ -312,6 +312,7 @@ DhsaLayout dhsa_layout(void* ws, int B, int H, int d, int nc) {
   p.order = cv.take<int32_t>((size_t)(BH * nc * nc));
   p.cumlen = cv.take<int32_t>((size_t)(BH * nc * (nc + 1)));
   p.diag_pos = cv.take<int32_t>((size_t)(BH * nc));
+  p.ranked = cv.take<int32_t>((size_t)(BH * nc * nc * 2));
   p.bytes = cv.off + kAlign;
   return p;
 }
@@ -827,6 +828,7 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
   a.order = chunk_order ? chunk_order : lay.order;
   a.cumlen = lay.cumlen;
   a.diag_pos = lay.diag_pos;
+  a.ranked = lay.ranked;
   a.mask_bits = mask_bits;
   a.B = B;
   a.H = H;

@@ -135,10 +135,13 @@ __global__ void __launch_bounds__(kThreads) rank_kernel(DhsaArgs a, int P) {
     }
   }
   int32_t* order = a.order + (bh * a.nc + l) * a.nc;
+  int32_t* ranked = a.ranked + (bh * a.nc + l) * a.nc * 2;
   for (int p = threadIdx.x; p < a.nc; p += kThreads) {
     const int32_t k = p < n ? (int32_t)key_index(keys[p]) : -1;
     order[p] = k;
     if (k == l) a.diag_pos[bh * a.nc + l] = p;
+    if (k >= 0) *(u32x2*)(ranked + 2 * p) = u32x2{(uint32_t)a.offs[k],
+                                                (uint32_t)(a.offs[k + 1] - a.offs[k])};
   }
   // cumlen[p] = total length of the chunks ranked before p, p = 0..n
   int32_t* cum = a.cumlen + (bh * a.nc + l) * (a.nc + 1);
@@ -177,12 +180,11 @@ struct Cut {
   int rem;
 };
 
-__device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int i) {
-  const int bl = a.offs[l], ll = a.offs[l + 1] - bl;
-  const int B = (int)min(a.budget, (int64_t)i + 1);
+// cum: the (b, h, l) row of prefix lengths in rank order (global or LDS).
+__device__ __forceinline__ Cut row_cut_in(const int32_t* cum, int bl, int ll, int64_t budget,
+                                          int dp, int l, int i) {
+  const int B = (int)min(budget, (int64_t)i + 1);
   const int tail = ll - (i - bl + 1);  // tokens of chunk l after i
-  const int dp = a.diag_pos[bh * a.nc + l];
-  const int32_t* cum = a.cumlen + (bh * a.nc + l) * (a.nc + 1);
   // E(p) = cum[p] - (p > dp ? tail : 0) is non-decreasing; find the largest
   // p in [0, l+1] with E(p) <= B.
   int lo = 0, hi = l + 1;
@@ -199,6 +201,12 @@ __device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int
   c.rem = (int)(B - (cum[lo] - (lo > dp ? tail : 0)));
   HSA_DCHECK(dp >= 0 && dp <= l && c.pw <= l + 1 && c.rem >= 0);
   return c;
+}
+
+__device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int i) {
+  const int bl = a.offs[l], ll = a.offs[l + 1] - bl;
+  return row_cut_in(a.cumlen + (bh * a.nc + l) * (a.nc + 1), bl, ll, a.budget,
+                    a.diag_pos[bh * a.nc + l], l, i);
 }
 
 template <int D>
@@ -221,8 +229,16 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   const int wr = (w + (int)(blockIdx.x & 3)) & 3;
   const int i = row0 + wr * 32 + (lane & 31);  // L < 2^31 is checked on the host
   const bool valid = i < bl1;
+  // Each row's cut searches the (b, h, l) row of prefix lengths: staged in
+  // LDS first (the key buffer is free until the first block is stored), so
+  // the binary search is not a chain of dependent global loads.
+  int32_t* cum_s = reinterpret_cast<int32_t*>(&sm);
+  const int32_t* cum_g = a.cumlen + (bh * a.nc + l) * (a.nc + 1);
+  for (int x = threadIdx.x; x <= l + 1; x += kThreads) cum_s[x] = cum_g[x];
+  const int dp = a.diag_pos[bh * a.nc + l];
+  __syncthreads();
   Cut cut = {0, 0};
-  if (valid) cut = row_cut(a, bh, l, i);
+  if (valid) cut = row_cut_in(cum_s, bl, bl1 - bl, a.budget, dp, l, i);
   const int last = valid ? (cut.rem > 0 ? cut.pw : cut.pw - 1) : -1;
   if (threadIdx.x == 0) pmax = -1;
   __syncthreads();
@@ -235,46 +251,53 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   WaveAttn<D> st;
   wave_attn_init<D>(st, Qb + (int64_t)min(i, (int)a.L - 1) * D, valid);
   const bool wave_any = __ballot(valid) != 0;
-  const int32_t* order = a.order + (bh * a.nc + l) * a.nc;
-  // Key blocks in rank order: chunk order[p], keys [kb, kb + 128).  Each
-  // step stores the block fetched during the previous step, starts the
+  // (first key, length) of the chunk at each rank.  The chunk after the
+  // current one is looked up a step ahead, with a buffer load (vector
+  // memory, so no wait of the LDS work covers it), and the next block's
+  // fetch never waits for a lookup.
+  const __amdgpu_buffer_rsrc_t rkr =
+      buffer_range(a.ranked + (bh * a.nc + l) * a.nc * 2, (l + 1) * 8);
+  auto rank_entry = [&](int r) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rkr, r * 8, 0, 0));
+  };
+  // Key blocks in rank order: the chunk at rank p, keys [kb, kb + 128).
+  // Each step stores the block fetched during the previous step, starts the
   // fetch of the next one, then computes.
-  int p = 0, kb = 0, k = 0, bk = 0, lk = 0;
+  int p = 0, kb = 0, bk = 0, lk = 0;
+  u32x2 up = {0u, 0u};  // the chunk at rank p + 1
   KVRegsWide<D> rg;
   if (p_end >= 0) {
-    k = order[0];
-    HSA_DCHECK(k >= 0 && k <= l);
-    bk = a.offs[k];
-    lk = a.offs[k + 1] - bk;
+    const u32x2 e0 = rank_entry(0);
+    bk = __builtin_amdgcn_readfirstlane((int)e0[0]);
+    lk = __builtin_amdgcn_readfirstlane((int)e0[1]);
+    HSA_DCHECK(bk >= 0 && lk >= 1 && bk + lk <= bl1);
     fetch_kv_wide<D>(rg, Kb + (int64_t)bk * D, Vb + (int64_t)bk * D, min(kWideBlock, lk));
+    if (p_end >= 1) up = rank_entry(1);
   }
   while (p <= p_end) {
     const int nk = min(kWideBlock, lk - kb);
     __syncthreads();
     store_kv_wide<D>(sm, rg, nk);
     __syncthreads();
-    int np = p, nkb = kb + kWideBlock, nkc = k, nbk = bk, nlk = lk;
+    int np = p, nkb = kb + kWideBlock, nbk = bk, nlk = lk;
     if (nkb >= lk) {
       np = p + 1;
       nkb = 0;
-      if (np <= p_end) {
-        nkc = order[np];
-        HSA_DCHECK(nkc >= 0 && nkc <= l);
-        nbk = a.offs[nkc];
-        nlk = a.offs[nkc + 1] - nbk;
-      }
+      nbk = __builtin_amdgcn_readfirstlane((int)up[0]);
+      nlk = __builtin_amdgcn_readfirstlane((int)up[1]);
+      HSA_DCHECK(np > p_end || (nbk >= 0 && nlk >= 1 && nbk + nlk <= bl1));
     }
     if (np <= p_end)
       fetch_kv_wide<D>(rg, Kb + (int64_t)(nbk + nkb) * D, Vb + (int64_t)(nbk + nkb) * D,
                        min(kWideBlock, nlk - nkb));
+    if (np != p && np + 1 <= p_end) up = rank_entry(np + 1);
     __builtin_amdgcn_sched_barrier(0);
-    const int len_eff = k == l ? i - bl + 1 : lk;
+    const int len_eff = bk == bl ? i - bl + 1 : lk;  // the query's own chunk starts at bl
     const int hi = !valid ? 0 : (p < cut.pw ? len_eff : (p == cut.pw ? cut.rem : 0));
     const int nv = max(0, min(hi - kb, nk));
     if (wave_any && __ballot(nv > 0) != 0) wave_attn_wide<D, kDhsaSub>(st, sm, nk, nv, scale_log2);
     p = np;
     kb = nkb;
-    k = nkc;
     bk = nbk;
     lk = nlk;
   }

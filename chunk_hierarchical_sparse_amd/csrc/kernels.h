@@ -142,6 +142,7 @@ struct DhsaArgs {
   int32_t* order;         // [B,H,nc,nc]
   int32_t* cumlen;        // [B,H,nc,nc+1]
   int32_t* diag_pos;      // [B,H,nc]
+  int32_t* ranked;        // [B,H,nc,nc,2]: (first key, length) of the chunk at each rank
   uint32_t* mask_bits;    // [B,H,L,ceil(L/32)] or null
   int B, H, d, dtype, nc, tiles_per_chunk;
   int64_t L, budget;
