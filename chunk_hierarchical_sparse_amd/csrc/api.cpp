@@ -296,7 +296,7 @@ int swa_decode_pieces(int64_t n_ctx, int64_t window) {
 
 struct DhsaLayout {
   int32_t* offs;
-  float *qh, *kh, *sc;
+  float *qh, *kh;
   int32_t *order, *cumlen, *diag_pos, *ranked;
   size_t bytes;
 };
@@ -308,7 +308,6 @@ DhsaLayout dhsa_layout(void* ws, int B, int H, int d, int nc) {
   p.offs = cv.take<int32_t>((size_t)nc + 1);
   p.qh = cv.take<float>((size_t)(BH * nc * d));
   p.kh = cv.take<float>((size_t)(BH * nc * d));
-  p.sc = cv.take<float>((size_t)(BH * nc * nc));
   p.order = cv.take<int32_t>((size_t)(BH * nc * nc));
   p.cumlen = cv.take<int32_t>((size_t)(BH * nc * (nc + 1)));
   p.diag_pos = cv.take<int32_t>((size_t)(BH * nc));
@@ -824,7 +823,6 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
   a.offs = lay.offs;
   a.qh = lay.qh;
   a.kh = lay.kh;
-  a.sc = lay.sc;
   a.order = chunk_order ? chunk_order : lay.order;
   a.cumlen = lay.cumlen;
   a.diag_pos = lay.diag_pos;

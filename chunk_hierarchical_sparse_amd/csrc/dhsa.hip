@@ -11,15 +11,16 @@
 // its tokens j <= i.
 //
 //  1. pool  : q_hat, k_hat per (b, h, chunk), fp32.
-//  2. sc    : S_c[l,k] = q_hat_l . k_hat_k for k <= l.
-//  3. rank  : per (b, h, l) bitonic sort of 64-bit keys (S_c, then lower k)
-//             -> order[p], prefix lengths in rank order, and the rank of l.
-//  4. attend: per (b, h, query chunk, 128-row tile): each lane's row finds
+//  2. rank  : per (b, h, l): S_c[l,k] = q_hat_l . k_hat_k for k <= l, as
+//             64-bit keys (S_c, then lower k) in LDS, bitonic-sorted
+//             -> order[p], prefix lengths in rank order, the rank of l and
+//             each rank's (first key, length).
+//  3. attend: per (b, h, query chunk, 128-row tile): each lane's row finds
 //             its cut (number of whole chunks, tokens of the boundary chunk)
 //             by binary search, then the block walks the ranked chunks with
 //             the MFMA attention core (bf16) or fp32 VALU dot products
 //             (fp32), with per-row key limits.
-//  5. mask  : optional debug bitmask of the kept keys.
+//  4. mask  : optional debug bitmask of the kept keys.
 #include <math.h>
 
 #include "attn_core.h"
@@ -52,13 +53,30 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(DhsaArgs a) {
   float aq[VEC], ak[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) aq[v] = ak[v] = 0.f;
-  for (int j = b0 + rs; j < b1; j += row_sets) {
-    const int64_t off = (bh * a.L + j) * d + cg * VEC;
+  // four rows per round, all loads issued before any is added (rows past
+  // the chunk read its last row and are dropped); the sum still takes the
+  // thread's rows in order
+  constexpr int U = 4;
+  for (int j0 = b0 + rs; j0 < b1; j0 += U * row_sets) {
+    float xq[U][VEC], xk[U][VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      aq[v] += load_elem<DT>(a.Q, off + v);
-      ak[v] += load_elem<DT>(a.K, off + v);
+    for (int u = 0; u < U; ++u) {
+      const int64_t off = (bh * a.L + min(j0 + u * row_sets, b1 - 1)) * d + cg * VEC;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        xq[u][v] = load_elem<DT>(a.Q, off + v);
+        xk[u][v] = load_elem<DT>(a.K, off + v);
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j0 + u * row_sets < b1) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          aq[v] += xq[u][v];
+          ak[v] += xk[u][v];
+        }
+      }
   }
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
@@ -76,46 +94,43 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(DhsaArgs a) {
   }
 }
 
-// S_c row l: lanes split d into float4 pieces, reduce with shuffles.
+// Per (b, h, l): the S_c row l (k <= l), straight into LDS as 64-bit sort
+// keys (score, then lower k), then ranked.  Lanes split d into float4
+// pieces and reduce with shuffles.
 template <int D>
-__global__ void __launch_bounds__(kThreads) sc_kernel(DhsaArgs a) {
-  const int64_t bh = blockIdx.x / a.nc;
-  const int l = blockIdx.x % a.nc;
-  constexpr int LPR = D / 4, RPW = kWave / LPR;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int li = lane % LPR, sub = lane / LPR;
-  const f32x4 q4 = *(const f32x4*)(a.qh + (bh * a.nc + l) * D + 4 * li);
-  // U steps of keys per round, every load issued unconditionally (keys past
-  // l read key l and are not stored): loads under a per-lane guard would
-  // each be waited for before the next
-  constexpr int U = 4;
-  for (int k0 = 0; k0 <= l; k0 += U * 4 * RPW) {
-    f32x4 x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = min(k0 + u * 4 * RPW + w * RPW + sub, l);
-      x[u] = *(const f32x4*)(a.kh + (bh * a.nc + k) * D + 4 * li);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = k0 + u * 4 * RPW + w * RPW + sub;
-      float p = q4[0] * x[u][0] + q4[1] * x[u][1] + q4[2] * x[u][2] + q4[3] * x[u][3];
-#pragma unroll
-      for (int o = LPR / 2; o > 0; o >>= 1) p += __shfl_xor(p, o, kWave);
-      if (li == 0 && k <= l) a.sc[(bh * a.nc + l) * a.nc + k] = p;
-    }
-  }
-}
-
 __global__ void __launch_bounds__(kThreads) rank_kernel(DhsaArgs a, int P) {
   extern __shared__ uint64_t keys[];  // [P]
   __shared__ int32_t part[kThreads];
   const int64_t bh = blockIdx.x / a.nc;
   const int l = blockIdx.x % a.nc;
   const int n = l + 1;
-  const float* sc = a.sc + (bh * a.nc + l) * a.nc;
-  for (int i = threadIdx.x; i < P; i += kThreads)
-    keys[i] = i < n ? select_key(sc[i], (uint32_t)i) : 0ull;
+  {
+    constexpr int LPR = D / 4, RPW = kWave / LPR;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int li = lane % LPR, sub = lane / LPR;
+    for (int i = n + threadIdx.x; i < P; i += kThreads) keys[i] = 0ull;
+    const f32x4 q4 = *(const f32x4*)(a.qh + (bh * a.nc + l) * D + 4 * li);
+    // U steps of keys per round, every load issued unconditionally (keys
+    // past l read key l and are not stored): loads under a per-lane guard
+    // would each be waited for before the next
+    constexpr int U = 4;
+    for (int k0 = 0; k0 <= l; k0 += U * 4 * RPW) {
+      f32x4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = min(k0 + u * 4 * RPW + w * RPW + sub, l);
+        x[u] = *(const f32x4*)(a.kh + (bh * a.nc + k) * D + 4 * li);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + u * 4 * RPW + w * RPW + sub;
+        float p = q4[0] * x[u][0] + q4[1] * x[u][1] + q4[2] * x[u][2] + q4[3] * x[u][3];
+#pragma unroll
+        for (int o = LPR / 2; o > 0; o >>= 1) p += __shfl_xor(p, o, kWave);
+        if (li == 0 && k <= l) keys[k] = select_key(p, (uint32_t)k);
+      }
+    }
+  }
   __syncthreads();
   // bitonic sort, descending
   for (int k = 2; k <= P; k <<= 1) {
@@ -464,20 +479,18 @@ hipError_t dhsa_stage(const DhsaArgs& a, int stage, hipStream_t stream) {
         launch<pool_kernel<kBF16>>(dim3((unsigned)rows), dim3(kThreads), lds, stream, a);
       break;
     }
-    case 1:
-      if (a.d == 64)
-        launch<sc_kernel<64>>(dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
-      else
-        launch<sc_kernel<128>>(dim3((unsigned)rows), dim3(kThreads), 0, stream, a);
-      break;
-    case 2: {
+    case 1: {
       int P = 1;
       while (P < a.nc) P <<= 1;
-      launch<rank_kernel>(dim3((unsigned)rows), dim3(kThreads), (size_t)P * sizeof(uint64_t),
-                          stream, a, P);
+      if (a.d == 64)
+        launch<rank_kernel<64>>(dim3((unsigned)rows), dim3(kThreads),
+                                (size_t)P * sizeof(uint64_t), stream, a, P);
+      else
+        launch<rank_kernel<128>>(dim3((unsigned)rows), dim3(kThreads),
+                                 (size_t)P * sizeof(uint64_t), stream, a, P);
       break;
     }
-    case 3: {
+    case 2: {
       const float sl2 = 1.4426950408889634f / sqrtf((float)a.d);
       const int64_t blocks = rows * a.tiles_per_chunk;
       const dim3 grid((unsigned)blocks), block(kThreads);

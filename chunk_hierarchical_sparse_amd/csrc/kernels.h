@@ -138,7 +138,6 @@ struct DhsaArgs {
   const int32_t* offs;    // device [nc+1]
   float* qh;              // [B,H,nc,d]
   float* kh;              // [B,H,nc,d]
-  float* sc;              // [B,H,nc,nc]
   int32_t* order;         // [B,H,nc,nc]
   int32_t* cumlen;        // [B,H,nc,nc+1]
   int32_t* diag_pos;      // [B,H,nc]
@@ -147,8 +146,9 @@ struct DhsaArgs {
   int B, H, d, dtype, nc, tiles_per_chunk;
   int64_t L, budget;
 };
-// stages: 0 pool, 1 sc, 2 rank, 3 attend, 4 mask (only with mask_bits)
-constexpr int kDhsaStages = 5;
+// stages: 0 pool, 1 rank (S_c rows and their ranking), 2 attend, 3 mask
+// (only with mask_bits)
+constexpr int kDhsaStages = 4;
 hipError_t dhsa_stage(const DhsaArgs& a, int stage, hipStream_t stream);
 int dhsa_max_chunks();
 

@@ -367,7 +367,8 @@ hsa_status_t hsa_swa_decode(const void* q, const void* Kc, const void* Vc, const
  *   hsa_decode  : 0 scan (landmark stream, per-slice top-K), 1 attend (merge
  *                 of the slices' candidates, one block per selected chunk),
  *                 2 fuse (softmax over the retrieval scores, weighted sum)
- *   dhsa_prefill: 0 pool, 1 S_c, 2 rank, 3 attend, 4 mask
+ *   dhsa_prefill: 0 pool, 1 rank (S_c rows and their ranking), 2 attend,
+ *                 3 mask
  *   dhsa_decode : 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
  *   swa_prefill, swa_decode: 0 attend
  *   hsa_prefill_backward: 0 landmarks, 1 select, 2 invert, 3 weights (fusion
