@@ -21,8 +21,9 @@ constexpr int kChunkThreads = 256;
 template <int D>
 struct ChunkSmem {
   KVSmem<D> kv;
-  // the landmark's three bf16 parts, then a zero row that lanes 3..31 read
-  __attribute__((aligned(16))) uint16_t lsplit[4][D];
+  // the landmark's three bf16 parts, then a zero row that lanes 3..31 read;
+  // rows padded by 16 bytes, so the four rows' reads fall on different banks
+  __attribute__((aligned(16))) uint16_t lsplit[4][D + 8];
   // each wave's tile of partial rows, rows padded by 16 bytes (conflict-free)
   __attribute__((aligned(16))) uint16_t ostage[kChunkThreads / kWave][32 * (D + 8)];
 };

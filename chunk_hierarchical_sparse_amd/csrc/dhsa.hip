@@ -42,7 +42,7 @@ constexpr int kMaxSort = 4096;  // 32 KiB of 64-bit sort keys in LDS
 template <int DT>
 __global__ void __launch_bounds__(kThreads) pool_kernel(DhsaArgs a) {
   constexpr int VEC = DT == kF32 ? 4 : 8;
-  extern __shared__ float red[];  // [2][row_sets][d]
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [2][row_sets][d]
   const int d = a.d;
   const int64_t bh = blockIdx.x / a.nc;
   const int l = blockIdx.x % a.nc;
@@ -78,10 +78,13 @@ __global__ void __launch_bounds__(kThreads) pool_kernel(DhsaArgs a) {
         }
       }
   }
+  // 16-byte stores: a lane's VEC sums are contiguous (scalar stores at a
+  // VEC-float stride put VEC lanes on one bank)
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) {
-    red[rs * d + cg * VEC + v] = aq[v];
-    red[(row_sets + rs) * d + cg * VEC + v] = ak[v];
+  for (int v = 0; v < VEC; v += 4) {
+    *(f32x4*)&red[rs * d + cg * VEC + v] = f32x4{aq[v], aq[v + 1], aq[v + 2], aq[v + 3]};
+    *(f32x4*)&red[(row_sets + rs) * d + cg * VEC + v] =
+        f32x4{ak[v], ak[v + 1], ak[v + 2], ak[v + 3]};
   }
   __syncthreads();
   const float rsq = __fsqrt_rn((float)(b1 - b0));
