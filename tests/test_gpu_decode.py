@@ -49,6 +49,11 @@ CASES = [
     (2, 16, 1, 3000, 2900, 128, 64, 8, "f32"),
     (1, 32, 2, 2048, 2047, 128, 32, 16, "bf16"),
     (2, 6, 2, 1500, 1400, 64, 64, 8, "bf16"),
+    # batches of 16 to 20 (b, group) pairs, fp32, d = 64, S = 16 and S = 128
+    (3, 12, 6, 2048, 2000, 64, 64, 8, "bf16"),
+    (4, 8, 4, 3000, 2950, 128, 64, 8, "f32"),
+    (5, 16, 4, 1024, 1000, 128, 16, 4, "bf16"),
+    (4, 4, 4, 4096, 4000, 128, 128, 4, "bf16"),
 ]
 
 
