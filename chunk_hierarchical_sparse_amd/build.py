@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "landmarks.hip", "prefill.hip", "decode.hip", "dhsa.hip", "dhsa_decode.hip",
            "swa.hip", "prefill_bwd.hip", "decode_noalloc.hip",
-           "upper.hip"]
+           "upper.hip", "prefill_qmajor.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,

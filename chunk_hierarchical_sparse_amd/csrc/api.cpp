@@ -518,6 +518,20 @@ hsa_status_t prefill_impl(const void* Q, const void* K, const void* V, const flo
   }
   pm.mark();
   if ((e = hsa::prefill_select(a, st)) != hipSuccess) return hip_fail(e, "select");
+  // the split landmarks of the query-major path use the partials' buffer
+  const size_t partial_bytes = (size_t)((int64_t)B * Hq * L * topk * d * elem_bytes(dtype));
+  if (hsa::prefill_query_major(a) &&
+      hsa::prefill_query_major_scratch((int64_t)B * Hkv, n, d) <= partial_bytes) {
+    // one selection row per wave, fused in registers: no invert, no partial
+    // outputs, no fusion pass (their stage marks stay, with nothing between)
+    pm.mark();
+    pm.mark();
+    if ((e = hsa::prefill_attend_query_major(a, lay.partial, st)) != hipSuccess)
+      return hip_fail(e, "attend");
+    pm.mark();
+    pm.mark();
+    return finish(st);
+  }
   pm.mark();
   if ((e = hsa::prefill_invert(a, st)) != hipSuccess) return hip_fail(e, "invert");
   pm.mark();

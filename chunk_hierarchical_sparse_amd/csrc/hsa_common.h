@@ -231,6 +231,21 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x = hi + lo + lo2 exactly for finite fp32 x: three bf16 parts, each the
+// round-to-nearest-even of what the previous ones leave.  Products of a
+// bf16 value with each part are exact in fp32, so three bf16 MFMA products
+// summed smallest first give an fp32-accurate dot product.
+__device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& lo, uint16_t& lo2) {
+  const __bf16 h = static_cast<__bf16>(x);  // round to nearest even
+  const float r1 = x - static_cast<float>(h);
+  const __bf16 l = static_cast<__bf16>(r1);
+  const float r2 = r1 - static_cast<float>(l);
+  const __bf16 m = static_cast<__bf16>(r2);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+  lo2 = __builtin_bit_cast(uint16_t, m);
+}
+
 // Block barrier ordering LDS accesses only: unlike __syncthreads(), global
 // loads issued before it (prefetches) stay in flight across it.
 __device__ __forceinline__ void block_sync_lds() {

@@ -94,6 +94,13 @@ hipError_t prefill_invert(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_attend(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_fuse(const PrefillArgs& a, hipStream_t stream);
 int prefill_entries_per_tile(int dtype, int G, int S);
+// Retrieval every R tokens with R * G == 32 (bf16, topk <= 8, S <= 64):
+// the query-major path (prefill_qmajor.hip) replaces the invert, the
+// chunk-major attention and the fusion.  `scratch` holds the landmarks split
+// into three bf16 parts, prefill_query_major_scratch bytes.
+bool prefill_query_major(const PrefillArgs& a);
+size_t prefill_query_major_scratch(int64_t BHkv, int64_t n, int d);
+hipError_t prefill_attend_query_major(const PrefillArgs& a, void* scratch, hipStream_t stream);
 
 // ---- HSA decode (decode.hip) -----------------------------------------------
 struct DecodeArgs {

@@ -189,16 +189,6 @@ __global__ void __launch_bounds__(kThreads) select_valu_kernel(PrefillArgs a, in
 // is as accurate as an fp32 dot product.  S^T = LMK U^T puts one query per
 // lane (lanes l and l^32 hold disjoint halves of each chunk tile), so each
 // lane keeps its own sorted top-KM list; the two halves merge at the end.
-__device__ __forceinline__ void split3_bf16(float x, uint16_t& hi, uint16_t& lo, uint16_t& lo2) {
-  const __bf16 h = static_cast<__bf16>(x);  // round to nearest even
-  const float r1 = x - static_cast<float>(h);
-  const __bf16 l = static_cast<__bf16>(r1);
-  const float r2 = r1 - static_cast<float>(l);
-  const __bf16 m = static_cast<__bf16>(r2);
-  hi = __builtin_bit_cast(uint16_t, h);
-  lo = __builtin_bit_cast(uint16_t, l);
-  lo2 = __builtin_bit_cast(uint16_t, m);
-}
 
 template <int D, int KM>
 __global__ void __launch_bounds__(kThreads, 2) select_mfma_kernel(PrefillArgs a, int64_t nqt) {

@@ -46,6 +46,16 @@ SWEEP = [
     (1, 2, 2, 300, 64, 1, 8, 5, "f32"),      # S = 1: token-level chunks
     (1, 12, 4, 1000, 128, 100, 3, 7, "bf16"),  # S > 64, G = 3
     (1, 4, 2, 520, 128, 64, 8, 600, "bf16"),  # one block spans the sequence
+    # R * G = 32 in bf16 with K <= 8 and S <= 64 runs query-major (one wave
+    # per block of R tokens, fused in registers): G = 2, 8 and 1, d = 64,
+    # S = 32 (one key sub-tile), 16 and 48 (a partial second sub-tile), a
+    # partial last block (1000 and 900 tokens), K = 4 and 6; K = 12 with
+    # R * G = 32 takes the chunk-major path
+    (2, 8, 4, 1000, 64, 32, 4, 16, "bf16"),
+    (1, 32, 4, 900, 128, 16, 8, 4, "bf16"),
+    (1, 16, 16, 700, 128, 64, 6, 32, "bf16"),
+    (1, 8, 2, 1500, 128, 48, 8, 8, "bf16"),
+    (1, 8, 2, 800, 128, 32, 12, 8, "bf16"),
 ]
 
 
