@@ -16,10 +16,12 @@
 //     (split3_bf16, exact), are the rows of one MFMA tile against Q^T, so
 //     s_k is fp32-accurate; w_k = softmax_k(s_k) before any chunk is read;
 //  2. per chunk k: S^T = K Q^T with K read straight into the MFMA operand
-//     registers, the chunk's own softmax (max m, sum l), P scaled by
-//     w_k / l and rounded to bf16, O^T += V^T P^T with V staged in the
-//     wave's own LDS buffer as [key / 4][d][4 keys].  The sum over chunks
-//     is then the fused output itself.
+//     registers (the next chunk's keys load while this one is finished),
+//     the chunk's own softmax (max m, sum l), P scaled by w_k / l and
+//     rounded to bf16, O^T += V^T P^T with V loaded into the wave's own LDS
+//     buffer by buffer-to-LDS loads (row-major, swizzled) and its operand
+//     taken by transposed LDS reads.  The sum over chunks is then the fused
+//     output itself.
 // The waves of a block are independent (no block barriers): two blocks of
 // four waves share a CU, and the waves' loads overlap one another's work.
 #include <math.h>
@@ -52,6 +54,17 @@ __global__ void __launch_bounds__(256) split_landmarks_kernel(const float* __res
   o[2 * d] = lo2;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16): in each 16-lane group,
+// lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+// i / 4 + 4 j, as its value j (j = 0..3).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Value of landmark-tile row j (0..31) from the accumulator registers of both
 // lane halves: row 8 (r / 4) + 4 h + r % 4 sits in register r of half h.
 template <int J>
@@ -65,9 +78,9 @@ template <int D>
 __global__ void __launch_bounds__(64 * kWaves, 2) qmajor_kernel(PrefillArgs a,
                                                                 const uint16_t* __restrict__ lsplit,
                                                                 float sl2) {
-  constexpr int CG = D / 4;             // 4-column groups of a value row
-  constexpr int NU = 16 * CG / 64;      // (key quad, column group) units per lane
-  __shared__ __attribute__((aligned(16))) uint16_t vsm[kWaves][16 * D * 4];
+  __shared__ __attribute__((aligned(16))) uint16_t vsm[kWaves][64 * D];  // one chunk's values
+  // each lane's fusion weights, [slot][lane] per wave
+  __shared__ float wsm[kWaves][kMaxSlots][64];
   const int lane = threadIdx.x & 63;
   // the wave index is uniform in a wave: in a scalar register, so are the
   // task, its (b, group) and every buffer base derived from them
@@ -145,6 +158,9 @@ __global__ void __launch_bounds__(64 * kWaves, 2) qmajor_kernel(PrefillArgs a,
 #pragma unroll
     for (int k = 0; k < kMaxSlots; ++k) wk[k] *= iz;
   }
+  // kept in LDS for the chunk loop and the end (registers are short there)
+#pragma unroll
+  for (int k = 0; k < kMaxSlots; ++k) wsm[w][k][lane] = wk[k];
 
   // --- 2. the chunks --------------------------------------------------------
   const uint16_t* Kb = (const uint16_t*)a.K + bg * a.L * D;
@@ -171,19 +187,58 @@ __global__ void __launch_bounds__(64 * kWaves, 2) qmajor_kernel(PrefillArgs a,
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, koff + 32 * s, 0, 0));
     }
   };
+  // Values: each chunk's rows go straight to the wave's LDS buffer by
+  // buffer-to-LDS loads (no registers, no byte permutation), row-major with
+  // the 16-byte units of row r XOR-swizzled by sw(r), so that the transposed
+  // reads of the value operand (four rows x 32 bytes per 16 lanes) spread
+  // over the banks.  Load i writes LDS bytes [1 KB i, 1 KB (i + 1)): lane p
+  // lands at 16 p, i.e. row RPI i + p / NUNIT, unit p % NUNIT, and fetches
+  // that unit's logical source (unit ^ sw(row)).
+  constexpr int NUNIT = D / 8;          // 16-byte units of a row
+  constexpr int RPI = 1024 / (2 * D);   // rows per 1 KB load
+  constexpr int NLD = 64 / RPI;         // loads per 64-row chunk
+  constexpr int SWM = NUNIT >= 16 ? 3 : 1;  // row bits that select the swizzle
+  const int prow = lane / NUNIT;        // this lane's row within each load
+  // RPI is a multiple of 4, so row & SWM = prow & SWM for every load
+  const int vsrc = (prow * D + (((lane % NUNIT) ^ (4 * (prow & SWM))) * 8)) * 2;
+  auto fetch_v = [&](int c) {
+    const char* vc = (const char*)(Vb + (int64_t)c * S * D);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int ib = i * 1024;
+      const __amdgpu_buffer_rsrc_t rs = buffer_range(vc + ib, max(cbytes - ib, 0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(vs + i * 512), 16, vsrc, 0, 0, 0);
+    }
+  };
+  // transposed-read addresses of the value operand (see the loop): lane
+  // (16-lane group g, index ti) reads row key0 + ti / 4, logical columns
+  // 32 b + 16 (g % 2) + 4 (ti % 4), whose unit 4 b + 2 (g % 2) + (ti % 4) / 2
+  // sits at that ^ 4 (row & SWM); key0 is a multiple of 4, so the swizzle is
+  // the lane's own: one offset per column block b
+  const int tg = (lane >> 4) & 1, ti = lane & 15, vr = ti >> 2, vc4 = ti & 3;
+  int voffb[D / 32];
+#pragma unroll
+  for (int bb = 0; bb < D / 32; ++bb)
+    voffb[bb] = (4 * h + vr) * D +
+                ((4 * bb + 2 * tg + (vc4 >> 1)) ^ (4 * (vr & SWM))) * 8 + 4 * (vc4 & 1);
   int cnext = 0;
   if (m > 0) {
     cnext = __builtin_amdgcn_readfirstlane(selp[0]);
+    HSA_DCHECK(cnext >= 0 && cnext < a.n);
+    fetch_k(cnext);
   }
 #pragma nounroll
   for (int k = 0; k < m; ++k) {
     const int c = cnext;
-    HSA_DCHECK(c >= 0 && c < a.n);
-    fetch_k(c);
-    // this slot's weight (k is wave-uniform: a chain of selects)
-    float wcur = wk[0];
-#pragma unroll
-    for (int j = 1; j < kMaxSlots; ++j) wcur = k == j ? wk[j] : wcur;
+    const float wcur = wsm[w][k][lane];  // this slot's weight
+    if (k + 1 < m) cnext = __builtin_amdgcn_readfirstlane(selp[k + 1]);
+    HSA_DCHECK(k + 1 >= m || (cnext >= 0 && cnext < a.n));
+    __builtin_amdgcn_sched_barrier(0);
+    // this chunk's values (the last step's reads of the buffer have all
+    // returned: their products were taken before the loop came round)
+    fetch_v(c);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s0 = {}, s1 = {};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
@@ -193,26 +248,9 @@ __global__ void __launch_bounds__(64 * kWaves, 2) qmajor_kernel(PrefillArgs a,
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kop[1][s]),
                                                      st.qf[s], s1, 0, 0, 0);
     }
-    // the value loads reuse the key operands' registers: not before the products
     __builtin_amdgcn_sched_barrier(0);
-    // the chunk's values: NU (key quad, column group) units per lane, four
-    // 8-byte key rows each (rows past the chunk read as zero).  Unit
-    // lane + 64 i is key quad (lane + 64 i) / CG: i moves it by 64 / CG
-    // quads, so each i takes its own buffer base and the same lane offset.
-    u32x2 vx[NU][4];
-    {
-      const char* vc = (const char*)(Vb + (int64_t)c * S * D);
-      const int voff = ((4 * (lane / CG)) * D + 4 * (lane % CG)) * 2;
-#pragma unroll
-      for (int i = 0; i < NU; ++i) {
-        const int ib = i * (64 / CG) * 4 * D * 2;  // bytes to this i's first key row
-        const __amdgpu_buffer_rsrc_t rs = buffer_range(vc + ib, max(cbytes - ib, 0));
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          vx[i][kk] = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff + kk * D * 2, 0, 0));
-      }
-    }
+    // the next chunk's keys load while this one is finished
+    if (k + 1 < m) fetch_k(cnext);
     __builtin_amdgcn_sched_barrier(0);
     // the chunk's own softmax (log2 domain), then P scaled by w_k / l
     float mx = -INFINITY;
@@ -245,33 +283,16 @@ __global__ void __launch_bounds__(64 * kWaves, 2) qmajor_kernel(PrefillArgs a,
     pb4[1] = cvt_bf16x8(s0, 8);
     pb4[2] = cvt_bf16x8(s1, 0);
     pb4[3] = cvt_bf16x8(s1, 8);
-    // stage V: the previous chunk's reads of this buffer were issued before
-    // these writes (LDS instructions of a wave run in order)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      const int u = lane + 64 * i, kq = u / CG, cq = u % CG;
-      const u32x2(&rr)[4] = vx[i];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int wd = x >> 1;
-        uint32_t lo, hi;
-        if ((x & 1) == 0) {
-          lo = (rr[0][wd] & 0xffffu) | (rr[1][wd] << 16);
-          hi = (rr[2][wd] & 0xffffu) | (rr[3][wd] << 16);
-        } else {
-          lo = (rr[0][wd] >> 16) | (rr[1][wd] & 0xffff0000u);
-          hi = (rr[2][wd] >> 16) | (rr[3][wd] & 0xffff0000u);
-        }
-        *(u32x2*)(&vs[(kq * D + 4 * cq + x) * 4]) = u32x2{lo, hi};
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     __builtin_amdgcn_sched_barrier(0);
-    // the next slot's chunk (its keys load at the top of the next step: kept
-    // in flight across this step's value sums they would not fit the
-    // registers)
-    if (k + 1 < m) cnext = __builtin_amdgcn_readfirstlane(selp[k + 1]);
+    // the values have landed once every load older than the key prefetch
+    // has: at most the prefetch's 2 D / 16 loads may still be in flight
+    // (vmcnt, with expcnt and lgkmcnt left at their maxima)
+    if (k + 1 < m) {
+      constexpr int N = 2 * (D / 16);
+      __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -279,14 +300,12 @@ __global__ void __launch_bounds__(64 * kWaves, 2) qmajor_kernel(PrefillArgs a,
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const bf16x8 pb = pb4[2 * kt + s2];
-        const int g0 = 8 * kt + 4 * s2 + h;  // key quad of k-slots 0..3
-        const int g1 = g0 + 2;               // key quad of k-slots 4..7
+        const int key0 = 32 * kt + 16 * s2;  // + 4 h (in voffb); + 8 for slots 4..7
 #pragma unroll
         for (int bb = 0; bb < D / 32; ++bb) {
-          const int dd = 32 * bb + i32;
-          const u32x2 v0 = *(const u32x2*)(&vs[(g0 * D + dd) * 4]);
-          const u32x2 v1 = *(const u32x2*)(&vs[(g1 * D + dd) * 4]);
-          const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
+          const u32x2 lo = lds_read_tr16(vs + voffb[bb] + key0 * D);
+          const u32x2 hi = lds_read_tr16(vs + voffb[bb] + (key0 + 8) * D);
+          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
           st.o[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
                                                              st.o[bb], 0, 0, 0);
         }
@@ -311,7 +330,7 @@ __global__ void __launch_bounds__(64 * kWaves, 2) qmajor_kernel(PrefillArgs a,
     float* wr = a.sel_w + qrow * a.topk;
 #pragma unroll
     for (int k = 0; k < kMaxSlots; ++k)
-      if (k < a.topk) wr[k] = wk[k];
+      if (k < a.topk) wr[k] = wsm[w][k][lane];
     for (int k = kMaxSlots; k < a.topk; ++k) wr[k] = 0.f;
   }
 }
