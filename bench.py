@@ -40,7 +40,8 @@ PREFILL_SRC = ["prefill.hip", "chunk_attend.h", "prefill_common.h", "attn_core.h
                "kernels.h"]
 DOMINANT = {
     "hsa_prefill": ("attend_chunk_bf16_kernel<128, true>", "PrefillArgs", PREFILL_SRC),
-    "hsa_prefill_r8": ("attend_chunk_bf16_kernel<128, true>", "PrefillArgs", PREFILL_SRC),
+    "hsa_prefill_r8": ("qmajor_kernel<128>", "PrefillArgs",
+                       ["prefill_qmajor.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
     "hsa_decode": ("scan_kernel<128, 1>", "DecodeArgs",
                    ["decode.hip", "hsa_common.h", "kernels.h"]),
     "hsa_decode_16m": ("scan_kernel<128, 1>", "DecodeArgs",
@@ -330,7 +331,9 @@ def bench_prefill(torch, hsa, args):
 
 def bench_prefill_interval(torch, hsa, args, inputs, R=8):
     """The 32K prefill workload with retrieval every R tokens (one selection
-    per block of R tokens, per-token attention and fusion)."""
+    per block of R tokens, per-token attention and fusion).  With R * G = 32
+    the library runs it query-major: the invert and fusion stages are empty
+    and the attend stage holds the fused attention."""
     Q, K, V, S, topk = inputs
     B, Hq, L, d = Q.shape
     Hkv = K.shape[1]
@@ -356,7 +359,9 @@ def bench_prefill_interval(torch, hsa, args, inputs, R=8):
         config={"workload": f"hsa_prefill_r{R}", "B": B, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d,
                 "S": S, "topk": topk, "retrieval_interval": R,
                 "inputs": "0.5*N(0,1) bf16, seed 2"},
-        roofline={"bound": "mfma", "kernel": "attend (chunk attention, bf16 MFMA)",
+        roofline={"bound": "mfma",
+                  "kernel": "attend (query-major chunk attention with the fusion, bf16 MFMA; "
+                            "the stage includes the landmark split)",
                   "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                   "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic_for("hsa_prefill_r8"),
                   "algorithmic_gflop_per_launch": attn_flop / 1e9, "avg_launch_ms": attn_ms,
