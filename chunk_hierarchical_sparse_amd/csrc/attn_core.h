@@ -208,47 +208,53 @@ __device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>
 }
 
 // ---------------------------------------------------------------------
-// Variable-length key blocks of up to 128 keys (DHSA: one chunk per block).
+// Variable-length key blocks of up to 128 keys (DHSA: one chunk per block;
+// the sliding-window attention: 128-key blocks of the window).
 //
-// V layout of these blocks: 16-byte units of 8 keys per value column, one
-// unit per A operand of O^T = V^T P^T.  Lane half h of k-step s' of 32-key
-// sub-tile u takes keys 32u + 16s' + 4h + 0..3 and the same + 8, so unit
-// "oct" o = 4u + 2s' + h holds keys 16(o/2) + 4(o%2) + {0..3, 8..11}, and
-// the operand is one 16-byte LDS read (two 8-byte reads would have to be
-// re-paired in registers).  Columns are swizzled by vcol_wide.
+// V layout of these blocks: row-major, the 16-byte units of value row r at
+// unit ^ wide_vswz(r), and the A operand of O^T = V^T P^T (lane = column,
+// eight keys) taken by two transposed reads (ds_read_b64_tr_b16), so that
+// staging is a plain 16-byte copy of each row piece.
 
 constexpr int kWideBlock = 128;
 
 template <int D>
 struct KVSmemWide {
   uint16_t k[kWideBlock * (D + 8)];
-  uint16_t v[(kWideBlock / 8) * D * 8];  // [oct][column (swizzled)][8 keys]
+  uint16_t v[kWideBlock * D];  // row-major, 16-byte units swizzled by wide_vswz
 };
 
-// Unit position of value column dd in an oct row: bits 0..1 are XORed with
-// bits 3..4.  A staging store has lane c writing columns 4c..4c+3, so every
-// 8 lanes of a 16-byte store land on distinct banks; a read of 32
-// consecutive columns is 8-unit runs permuted in place (also conflict-free),
-// and since only bits below 5 enter, column 32b + i keeps the lane's
-// offset for every b.
-__device__ __forceinline__ int vcol_wide(int dd) { return dd ^ ((dd >> 3) & 3); }
+// XOR applied to the 16-byte unit index of value row r.  A transposed read
+// takes 32 bytes from each of four consecutive rows (a multiple of four on)
+// per 16 lanes; with the four rows' units moved by 0, 4, 8, 12 (two values
+// for the 8-unit rows of d = 64) the read touches every bank once.
+template <int D>
+__device__ __forceinline__ constexpr int wide_vswz(int r) {
+  return D >= 128 ? 4 * (r & 3) : 4 * (r & 1);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16): in each 16-lane group,
+// lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+// i / 4 + 4 j, as its value j (j = 0..3).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 // One thread's share of a 128-key block held in registers between its
 // global load and its LDS store, so the next block's loads can be in flight
-// while the current block is computed.  256 threads; K as 16-byte row
-// pieces, V as 8-byte pieces (four columns) of the eight keys of an oct.
+// while the current block is computed.  256 threads; K and V as 16-byte row
+// pieces (thread t: piece t % KPR of rows t / KPR + i * (256 / KPR)).
 template <int D>
 struct KVRegsWide {
-  static constexpr int KPR = D / 8;  // 16-byte pieces per key row
-  static constexpr int VPR = D / 4;  // 8-byte pieces per value row
+  static constexpr int KPR = D / 8;  // 16-byte pieces per row
   static constexpr int NK = kWideBlock * KPR / 256;
-  static constexpr int NO = (kWideBlock / 8) * VPR / 256;  // octs per thread
   u32x4 k[NK];
-  u32x2 v[NO][8];
+  u32x4 v[NK];
 };
-
-// In-oct key of slot kk (0..7): the oct's first quad, then the quad 8 keys on.
-__device__ __forceinline__ constexpr int oct_key(int kk) { return (kk & 3) + 8 * (kk >> 2); }
 
 // Raw buffer resource over [base, base + bytes): buffer loads at offsets
 // past the range return zero instead of touching memory.  Word 3 holds the
@@ -259,70 +265,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void* base,
 
 // Loads of rows [0, nk) (nk <= 128) of a key/value block into registers;
 // rows past nk read as zero (buffer range check, no branches).  Called by
-// all 256 threads of the block: thread tid takes K piece tid % KPR of rows
-// tid / KPR + i * (256 / KPR), and V piece tid % VPR of the keys of octs
-// tid / VPR + i * (256 / VPR).  The whole byte offset of every load goes
-// in the per-lane offset operand with a zero scalar offset: the range check
-// of a raw buffer load covers the lane offset (and the instruction's
-// immediate) but not the scalar offset, so a row step passed there would
-// read past nk, past the end of the tensor for its last chunk.
+// all 256 threads of the block.  The range check of a raw buffer load
+// covers the lane offset (and the instruction's immediate) but not the
+// scalar offset, so the whole offset is in the lane operand: load i reads
+// rows i * (256 / KPR) further on by moving its buffer's base there (scalar
+// registers) and shrinking its range to match.
 template <int D>
 __device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* __restrict__ Kg,
                                               const uint16_t* __restrict__ Vg, int nk) {
   using R = KVRegsWide<D>;
   const int tid = threadIdx.x;
-  const __amdgpu_buffer_rsrc_t kr = buffer_range(Kg, nk * D * 2);
-  const __amdgpu_buffer_rsrc_t vr = buffer_range(Vg, nk * D * 2);
-  const int koff = ((tid / R::KPR) * D + (tid % R::KPR) * 8) * 2;  // bytes
+  const int bytes = nk * D * 2;
+  const char* kg = (const char*)Kg;
+  const char* vg = (const char*)Vg;
+  const int off = ((tid / R::KPR) * D + (tid % R::KPR) * 8) * 2;  // bytes
 #pragma unroll
-  for (int i = 0; i < R::NK; ++i)
-    r.k[i] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + i * (256 / R::KPR) * D * 2, 0, 0));
-  // oct o starts at key 16 (o / 2) + 4 (o % 2); octs o0 + i (256 / VPR)
-  // (an even step) start 8 i (256 / VPR) keys further on
-  const int o0 = tid / R::VPR;
-  const int voff = ((16 * (o0 >> 1) + 4 * (o0 & 1)) * D + (tid % R::VPR) * 4) * 2;
-#pragma unroll
-  for (int i = 0; i < R::NO; ++i)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      r.v[i][kk] = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                     vr, voff + (i * (256 / R::VPR) * 8 + oct_key(kk)) * D * 2, 0, 0));
+  for (int i = 0; i < R::NK; ++i) {
+    constexpr int step = (256 / R::KPR) * D * 2;
+    const int left = max(bytes - i * step, 0);
+    r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           buffer_range(kg + i * step, left), off, 0, 0));
+    r.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           buffer_range(vg + i * step, left), off, 0, 0));
+  }
 }
 
 // LDS store of a fetched block: rows up to the next multiple of 32 above nk
-// (zeros past nk) are written, rows beyond that are never read.  V goes to
-// the [oct][column][8 keys] layout, one 16-byte unit per column.
+// (zeros past nk) are written, rows beyond that are never read.  A thread's
+// rows are all one residue mod 4 (256 / KPR is a multiple of 4), so its V
+// pieces share one swizzle.
 template <int D>
 __device__ __forceinline__ void store_kv_wide(KVSmemWide<D>& sm, const KVRegsWide<D>& r,
                                               int nk) {
   using R = KVRegsWide<D>;
   const int tid = threadIdx.x;
   const int rows = (nk + 31) & ~31;
-  const int krow = tid / R::KPR;
-  uint16_t* ks = &sm.k[krow * (D + 8) + (tid % R::KPR) * 8];
+  const int krow = tid / R::KPR, c = tid % R::KPR;
+  uint16_t* ks = &sm.k[krow * (D + 8) + c * 8];
+  uint16_t* vs = &sm.v[krow * D + ((c ^ wide_vswz<D>(krow)) * 8)];
 #pragma unroll
   for (int i = 0; i < R::NK; ++i)
-    if (krow + i * (256 / R::KPR) < rows) *(u32x4*)(ks + i * (256 / R::KPR) * (D + 8)) = r.k[i];
-  const int o0 = tid / R::VPR, cq = tid % R::VPR;
-#pragma unroll
-  for (int i = 0; i < R::NO; ++i) {
-    const int o = o0 + i * (256 / R::VPR);
-    if (16 * (o >> 1) >= rows) continue;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      // column 4 cq + x: keys (slot order) as bf16 pairs
-      const int w = x >> 1;
-      uint32_t p[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t a = r.v[i][2 * j][w], b = r.v[i][2 * j + 1][w];
-        p[j] = (x & 1) == 0 ? (a & 0xffffu) | (b << 16) : (a >> 16) | (b & 0xffff0000u);
-      }
-      *(u32x4*)(&sm.v[(o * D + vcol_wide(4 * cq + x)) * 8]) = u32x4{p[0], p[1], p[2], p[3]};
+    if (krow + i * (256 / R::KPR) < rows) {
+      *(u32x4*)(ks + i * (256 / R::KPR) * (D + 8)) = r.k[i];
+      *(u32x4*)(vs + i * (256 / R::KPR) * D) = r.v[i];
     }
-  }
 }
 
 // One staged block of nkeys (<= 128, block-uniform) keys: this lane's query
@@ -410,17 +396,29 @@ __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide
     st.l += ps;
     st.m = m_new;
     __builtin_amdgcn_sched_barrier(0);
-    const int vc = vcol_wide(i32);  // = vcol_wide(32 b + i32) - 32 b for every b
+    // value operand of k-step (t, s2), column block b: lane (16-lane group
+    // g, index i) reads row key0 + i / 4 at logical columns 32 b + 16 (g % 2)
+    // + 4 (i % 4); key0 = 32 (t0 + t) + 16 s2 + 4 h (+ 8 for the operand's
+    // upper half) is a multiple of 4, so the row's swizzle is the lane's own
+    // The unit of column block b is (4 b + u0) ^ sw = 4 (b ^ (sw / 4)) + u0
+    // (sw a multiple of 4, u0 < 4), so the element offset of block b is the
+    // lane's offset for block 0 XOR 32 b: one XOR per block and read pair,
+    // and a single address register.
+    const int tg = (lane >> 4) & 1, ti = lane & 15, vr = ti >> 2, vc4 = ti & 3;
+    const int va = (4 * h + vr) * D + 4 * (vc4 & 1) + ((2 * tg + (vc4 >> 1)) ^ wide_vswz<D>(vr)) * 8;
 #pragma unroll
     for (int t = 0; t < SUB; ++t) {
       if (t >= nsub) break;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const bf16x8 pb = cvt_bf16x8(sc[t], 8 * s2);
-        const int o = 4 * (t0 + t) + 2 * s2 + h;
+        const uint16_t* vk = &sm.v[(32 * (t0 + t) + 16 * s2) * D];
 #pragma unroll
         for (int b = 0; b < D / 32; ++b) {
-          const bf16x8 av = *(const bf16x8*)(&sm.v[(o * D + 32 * b + vc) * 8]);
+          const int vo = va ^ (32 * b);
+          const u32x2 lo = lds_read_tr16(vk + vo);
+          const u32x2 hi = lds_read_tr16(vk + 8 * D + vo);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
           st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, st.o[b], 0, 0, 0);
         }
       }

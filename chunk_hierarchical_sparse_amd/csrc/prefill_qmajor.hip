@@ -54,17 +54,6 @@ __global__ void __launch_bounds__(256) split_landmarks_kernel(const float* __res
   o[2 * d] = lo2;
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Transposed 8-byte LDS read (ds_read_b64_tr_b16): in each 16-lane group,
-// lane i receives element i % 4 of the 8-byte pieces addressed by lanes
-// i / 4 + 4 j, as its value j (j = 0..3).
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
-
 // Value of landmark-tile row j (0..31) from the accumulator registers of both
 // lane halves: row 8 (r / 4) + 4 h + r % 4 sits in register r of half h.
 template <int J>
