@@ -850,7 +850,8 @@ hsa_status_t dhsa_prefill(const void* Q, const void* K, const void* V, const int
   a.tiles_per_chunk = (max_len + 127) / 128;
   a.L = L;
   a.budget = budget;
-  if ((int64_t)B * H * n_chunks * a.tiles_per_chunk >= ((int64_t)1 << 31))
+  // the bf16 attention launches up to four blocks per 128-row tile
+  if ((int64_t)B * H * n_chunks * a.tiles_per_chunk * 4 >= ((int64_t)1 << 31))
     return fail(HSA_ERR_UNSUPPORTED, "too many attention tiles for one launch");
   StageMarks pm(st);
   for (int stage = 0; stage < hsa::kDhsaStages; ++stage) {

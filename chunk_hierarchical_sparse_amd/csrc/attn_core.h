@@ -218,10 +218,10 @@ __device__ __forceinline__ void wave_attn_block(WaveAttn<D>& st, const KVSmem<D>
 
 constexpr int kWideBlock = 128;
 
-template <int D>
+template <int D, int KB = kWideBlock>
 struct KVSmemWide {
-  uint16_t k[kWideBlock * (D + 8)];
-  uint16_t v[kWideBlock * D];  // row-major, 16-byte units swizzled by wide_vswz
+  uint16_t k[KB * (D + 8)];
+  uint16_t v[KB * D];  // row-major, 16-byte units swizzled by wide_vswz
 };
 
 // XOR applied to the 16-byte unit index of value row r.  A transposed read
@@ -244,14 +244,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// One thread's share of a 128-key block held in registers between its
-// global load and its LDS store, so the next block's loads can be in flight
-// while the current block is computed.  256 threads; K and V as 16-byte row
-// pieces (thread t: piece t % KPR of rows t / KPR + i * (256 / KPR)).
-template <int D>
+// One thread's share of a KB-key block held in registers between its global
+// load and its LDS store, so the next block's loads can be in flight while
+// the current block is computed.  NT = 2 KB threads (256 for 128 keys); K
+// and V as 16-byte row pieces (thread t: piece t % KPR of rows t / KPR +
+// i * (NT / KPR)).
+template <int D, int KB = kWideBlock>
 struct KVRegsWide {
+  static constexpr int NT = 2 * KB;
   static constexpr int KPR = D / 8;  // 16-byte pieces per row
-  static constexpr int NK = kWideBlock * KPR / 256;
+  static constexpr int NK = KB * KPR / NT;
   u32x4 k[NK];
   u32x4 v[NK];
 };
@@ -263,17 +265,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
-// Loads of rows [0, nk) (nk <= 128) of a key/value block into registers;
+// Loads of rows [0, nk) (nk <= KB) of a key/value block into registers;
 // rows past nk read as zero (buffer range check, no branches).  Called by
-// all 256 threads of the block.  The range check of a raw buffer load
+// all NT threads of the block.  The range check of a raw buffer load
 // covers the lane offset (and the instruction's immediate) but not the
 // scalar offset, so the whole offset is in the lane operand: load i reads
-// rows i * (256 / KPR) further on by moving its buffer's base there (scalar
+// rows i * (NT / KPR) further on by moving its buffer's base there (scalar
 // registers) and shrinking its range to match.
-template <int D>
-__device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* __restrict__ Kg,
+template <int D, int KB = kWideBlock>
+__device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D, KB>& r,
+                                              const uint16_t* __restrict__ Kg,
                                               const uint16_t* __restrict__ Vg, int nk) {
-  using R = KVRegsWide<D>;
+  using R = KVRegsWide<D, KB>;
   const int tid = threadIdx.x;
   const int bytes = nk * D * 2;
   const char* kg = (const char*)Kg;
@@ -281,7 +284,7 @@ __device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* 
   const int off = ((tid / R::KPR) * D + (tid % R::KPR) * 8) * 2;  // bytes
 #pragma unroll
   for (int i = 0; i < R::NK; ++i) {
-    constexpr int step = (256 / R::KPR) * D * 2;
+    constexpr int step = (R::NT / R::KPR) * D * 2;
     const int left = max(bytes - i * step, 0);
     r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            buffer_range(kg + i * step, left), off, 0, 0));
@@ -292,12 +295,13 @@ __device__ __forceinline__ void fetch_kv_wide(KVRegsWide<D>& r, const uint16_t* 
 
 // LDS store of a fetched block: rows up to the next multiple of 32 above nk
 // (zeros past nk) are written, rows beyond that are never read.  A thread's
-// rows are all one residue mod 4 (256 / KPR is a multiple of 4), so its V
+// rows are all one residue mod 4 (NT / KPR is a multiple of 4), so its V
 // pieces share one swizzle.
-template <int D>
-__device__ __forceinline__ void store_kv_wide(KVSmemWide<D>& sm, const KVRegsWide<D>& r,
+template <int D, int KB = kWideBlock>
+__device__ __forceinline__ void store_kv_wide(KVSmemWide<D, KB>& sm, const KVRegsWide<D, KB>& r,
                                               int nk) {
-  using R = KVRegsWide<D>;
+  using R = KVRegsWide<D, KB>;
+  constexpr int RS = R::NT / R::KPR;  // rows between a thread's pieces
   const int tid = threadIdx.x;
   const int rows = (nk + 31) & ~31;
   const int krow = tid / R::KPR, c = tid % R::KPR;
@@ -305,9 +309,9 @@ __device__ __forceinline__ void store_kv_wide(KVSmemWide<D>& sm, const KVRegsWid
   uint16_t* vs = &sm.v[krow * D + ((c ^ wide_vswz<D>(krow)) * 8)];
 #pragma unroll
   for (int i = 0; i < R::NK; ++i)
-    if (krow + i * (256 / R::KPR) < rows) {
-      *(u32x4*)(ks + i * (256 / R::KPR) * (D + 8)) = r.k[i];
-      *(u32x4*)(vs + i * (256 / R::KPR) * D) = r.v[i];
+    if (krow + i * RS < rows) {
+      *(u32x4*)(ks + i * RS * (D + 8)) = r.k[i];
+      *(u32x4*)(vs + i * RS * D) = r.v[i];
     }
 }
 
@@ -318,8 +322,8 @@ __device__ __forceinline__ void store_kv_wide(KVSmemWide<D>& sm, const KVRegsWid
 // for the whole block; SUB = 2: two, with half the score registers), each
 // with one online-softmax update; the accumulator is rescaled only when
 // some lane's running maximum grew.
-template <int D, int SUB, bool BAND = false>
-__device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide<D>& sm,
+template <int D, int SUB, bool BAND = false, int KB = kWideBlock>
+__device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide<D, KB>& sm,
                                                int nkeys, int nvalid, float scale_log2,
                                                int nlo = 0) {
   const int lane = threadIdx.x & 63;

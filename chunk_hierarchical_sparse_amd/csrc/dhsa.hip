@@ -33,9 +33,13 @@ HSA_DCHECK_SOURCE()
 namespace {
 
 constexpr int kThreads = 256;
-// 32-key sub-tiles per online-softmax update in the attention (see
-// wave_attn_wide): four, one update per key block of up to 128 keys.
-constexpr int kDhsaSub = 4;
+// Waves per block of the bf16 attention: each wave owns 32 rows of the
+// block's query chunk, and the block walks the ranked key chunks in blocks
+// of KB = 32 * kDhsaWaves keys (one online-softmax update each).
+constexpr int kDhsaWaves = 4;
+// Rows per tile of the host's tile count (tiles_per_chunk): the fp32
+// attention's block; the bf16 attention splits each into
+// kRowsPerTile / (32 * kDhsaWaves) blocks.
 constexpr int kRowsPerTile = 128;
 constexpr int kMaxSort = 4096;  // 32 KiB of 64-bit sort keys in LDS
 
@@ -227,24 +231,26 @@ __device__ __forceinline__ Cut row_cut(const DhsaArgs& a, int64_t bh, int l, int
                     a.diag_pos[bh * a.nc + l], l, i);
 }
 
-template <int D>
-__global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float scale_log2) {
-  __shared__ KVSmemWide<D> sm;
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW, 2) attend_kernel(DhsaArgs a, float scale_log2) {
+  constexpr int KB = 32 * NW, NT = 64 * NW, ROWS = 32 * NW;
+  __shared__ KVSmemWide<D, KB> sm;
   __shared__ int pmax;
   // late query chunks attend the most keys: dispatch them first, with all
   // (b, h) of one chunk next to each other
   const int64_t BH = (int64_t)a.B * a.H;
   const int64_t bh = blockIdx.x % BH;
   const int64_t rest = blockIdx.x / BH;
-  const int l = a.nc - 1 - (int)(rest / a.tiles_per_chunk);
-  const int tile = (int)(rest % a.tiles_per_chunk);
+  const int tpc = a.tiles_per_chunk * (kRowsPerTile / ROWS);
+  const int l = a.nc - 1 - (int)(rest / tpc);
+  const int tile = (int)(rest % tpc);
   const int bl = a.offs[l], bl1 = a.offs[l + 1];
-  const int row0 = bl + tile * kRowsPerTile;
+  const int row0 = bl + tile * ROWS;
   if (row0 >= bl1) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   // the tile's 32-row groups go to the waves rotated by block, so the groups
   // past a short chunk's end (idle waves) fall on different SIMDs
-  const int wr = (w + (int)(blockIdx.x & 3)) & 3;
+  const int wr = (w + (int)(blockIdx.x % NW)) % NW;
   const int i = row0 + wr * 32 + (lane & 31);  // L < 2^31 is checked on the host
   const bool valid = i < bl1;
   // Each row's cut searches the (b, h, l) row of prefix lengths: staged in
@@ -252,7 +258,8 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   // the binary search is not a chain of dependent global loads.
   int32_t* cum_s = reinterpret_cast<int32_t*>(&sm);
   const int32_t* cum_g = a.cumlen + (bh * a.nc + l) * (a.nc + 1);
-  for (int x = threadIdx.x; x <= l + 1; x += kThreads) cum_s[x] = cum_g[x];
+  static_assert(sizeof(sm) >= (kMaxSort + 2) * sizeof(int32_t), "prefix-length row in LDS");
+  for (int x = threadIdx.x; x <= l + 1; x += NT) cum_s[x] = cum_g[x];
   const int dp = a.diag_pos[bh * a.nc + l];
   __syncthreads();
   Cut cut = {0, 0};
@@ -283,21 +290,21 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
   // fetch of the next one, then computes.
   int p = 0, kb = 0, bk = 0, lk = 0;
   u32x2 up = {0u, 0u};  // the chunk at rank p + 1
-  KVRegsWide<D> rg;
+  KVRegsWide<D, KB> rg;
   if (p_end >= 0) {
     const u32x2 e0 = rank_entry(0);
     bk = __builtin_amdgcn_readfirstlane((int)e0[0]);
     lk = __builtin_amdgcn_readfirstlane((int)e0[1]);
     HSA_DCHECK(bk >= 0 && lk >= 1 && bk + lk <= bl1);
-    fetch_kv_wide<D>(rg, Kb + (int64_t)bk * D, Vb + (int64_t)bk * D, min(kWideBlock, lk));
+    fetch_kv_wide<D, KB>(rg, Kb + (int64_t)bk * D, Vb + (int64_t)bk * D, min(KB, lk));
     if (p_end >= 1) up = rank_entry(1);
   }
   while (p <= p_end) {
-    const int nk = min(kWideBlock, lk - kb);
+    const int nk = min(KB, lk - kb);
     __syncthreads();
-    store_kv_wide<D>(sm, rg, nk);
+    store_kv_wide<D, KB>(sm, rg, nk);
     __syncthreads();
-    int np = p, nkb = kb + kWideBlock, nbk = bk, nlk = lk;
+    int np = p, nkb = kb + KB, nbk = bk, nlk = lk;
     if (nkb >= lk) {
       np = p + 1;
       nkb = 0;
@@ -306,14 +313,15 @@ __global__ void __launch_bounds__(kThreads, 2) attend_kernel(DhsaArgs a, float s
       HSA_DCHECK(np > p_end || (nbk >= 0 && nlk >= 1 && nbk + nlk <= bl1));
     }
     if (np <= p_end)
-      fetch_kv_wide<D>(rg, Kb + (int64_t)(nbk + nkb) * D, Vb + (int64_t)(nbk + nkb) * D,
-                       min(kWideBlock, nlk - nkb));
+      fetch_kv_wide<D, KB>(rg, Kb + (int64_t)(nbk + nkb) * D, Vb + (int64_t)(nbk + nkb) * D,
+                           min(KB, nlk - nkb));
     if (np != p && np + 1 <= p_end) up = rank_entry(np + 1);
     __builtin_amdgcn_sched_barrier(0);
     const int len_eff = bk == bl ? i - bl + 1 : lk;  // the query's own chunk starts at bl
     const int hi = !valid ? 0 : (p < cut.pw ? len_eff : (p == cut.pw ? cut.rem : 0));
     const int nv = max(0, min(hi - kb, nk));
-    if (wave_any && __ballot(nv > 0) != 0) wave_attn_wide<D, kDhsaSub>(st, sm, nk, nv, scale_log2);
+    if (wave_any && __ballot(nv > 0) != 0)
+      wave_attn_wide<D, NW, false, KB>(st, sm, nk, nv, scale_log2);
     p = np;
     kb = nkb;
     bk = nbk;
@@ -496,16 +504,19 @@ hipError_t dhsa_stage(const DhsaArgs& a, int stage, hipStream_t stream) {
     case 2: {
       const float sl2 = 1.4426950408889634f / sqrtf((float)a.d);
       const int64_t blocks = rows * a.tiles_per_chunk;
-      const dim3 grid((unsigned)blocks), block(kThreads);
       if (a.dtype == kF32) {
+        const dim3 grid((unsigned)blocks), block(kThreads);
         if (a.d == 64)
           launch<attend_f32_kernel<64>>(grid, block, 0, stream, a, sl2);
         else
           launch<attend_f32_kernel<128>>(grid, block, 0, stream, a, sl2);
-      } else if (a.d == 64) {
-        launch<attend_kernel<64>>(grid, block, 0, stream, a, sl2);
       } else {
-        launch<attend_kernel<128>>(grid, block, 0, stream, a, sl2);
+        constexpr int NW = kDhsaWaves;
+        const dim3 grid((unsigned)(blocks * (kRowsPerTile / (32 * NW)))), block(64 * NW);
+        if (a.d == 64)
+          launch<attend_kernel<64, NW>>(grid, block, 0, stream, a, sl2);
+        else
+          launch<attend_kernel<128, NW>>(grid, block, 0, stream, a, sl2);
       }
       break;
     }
