@@ -46,7 +46,7 @@ DOMINANT = {
                    ["decode.hip", "hsa_common.h", "kernels.h"]),
     "hsa_decode_16m": ("scan_kernel<128, 1>", "DecodeArgs",
                        ["decode.hip", "hsa_common.h", "kernels.h"]),
-    "dhsa_prefill": ("attend_kernel<128>", "DhsaArgs",
+    "dhsa_prefill": ("attend_kernel<128, 4>", "DhsaArgs",
                      ["dhsa.hip", "attn_core.h", "hsa_common.h", "kernels.h"]),
     "dhsa_decode": ("attend_kernel<128, 1>", "DhsaDecodeArgs",
                     ["dhsa_decode.hip", "hsa_common.h", "kernels.h"]),
