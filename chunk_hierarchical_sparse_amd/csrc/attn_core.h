@@ -361,10 +361,22 @@ __device__ __forceinline__ void wave_attn_wide(WaveAttn<D>& st, const KVSmemWide
     for (int t = 0; t < SUB; ++t) {
       if (t >= nsub) break;
       if (__ballot(nv < 32 * (t + 1) || (BAND && nl > 32 * t)) != 0) {
+        if (BAND) {
+          // key = 32 t + 4 h + c_r with c_r = 8 (r / 4) + r % 4 a constant:
+          // compare c_r against the lane's bounds moved by 32 t + 4 h
+          // (measured faster for the band, slower without it)
+          const int hi = nv - 32 * t - 4 * h, lo = nl - 32 * t - 4 * h;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= nv || (BAND && key < nl)) sc[t][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int cr = 8 * (r >> 2) + (r & 3);
+            if (cr >= hi || cr < lo) sc[t][r] = -INFINITY;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key >= nv) sc[t][r] = -INFINITY;
+          }
         }
       }
     }

@@ -243,11 +243,13 @@ __global__ void __launch_bounds__(64 * kWaves, 2) qmajor_kernel(PrefillArgs a,
     __builtin_amdgcn_sched_barrier(0);
     // the chunk's own softmax (log2 domain), then P scaled by w_k / l
     float mx = -INFINITY;
+    // key = 4 h + c_q (+ 32) with c_q = 8 (q / 4) + q % 4 a constant
+    const int kr = S - 4 * h;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int key = 8 * (q >> 2) + 4 * h + (q & 3);
-      const float x0 = key < S ? s0[q] * sl2 : -INFINITY;
-      const float x1 = key + 32 < S ? s1[q] * sl2 : -INFINITY;
+      const int cq = 8 * (q >> 2) + (q & 3);
+      const float x0 = cq < kr ? s0[q] * sl2 : -INFINITY;
+      const float x1 = cq + 32 < kr ? s1[q] * sl2 : -INFINITY;
       s0[q] = x0;
       s1[q] = x1;
       mx = fmaxf(mx, fmaxf(x0, x1));
