@@ -331,7 +331,8 @@ __global__ void __launch_bounds__(64 * kWaves, 2) qmajor_kernel(PrefillArgs a,
 bool prefill_query_major(const PrefillArgs& a) {
   return a.dtype == kBF16 && a.interval > 1 && a.Hkv > 0 &&
          a.interval * (a.Hq / a.Hkv) == 32 && a.topk <= kMaxSlots && a.S <= 64 &&
-         (a.d == 64 || a.d == 128);
+         (a.d == 64 || a.d == 128) &&
+         (int64_t)a.B * a.Hkv * a.nq < ((int64_t)1 << 31) * kWaves;  // one launch
 }
 
 size_t prefill_query_major_scratch(int64_t BHkv, int64_t n, int d) {

@@ -56,6 +56,7 @@ SWEEP = [
     (1, 16, 16, 700, 128, 64, 6, 32, "bf16"),
     (1, 8, 2, 1500, 128, 48, 8, 8, "bf16"),
     (1, 8, 2, 800, 128, 32, 12, 8, "bf16"),
+    (1, 8, 2, 600, 128, 1, 8, 8, "bf16"),     # query-major with S = 1 (token chunks)
 ]
 
 
