@@ -265,6 +265,7 @@ struct DecodeLayout {
   float* part_s;
   float* sw_o;
   float* sw_lse;
+  uint32_t* sync;
   int n_slices, slice;
   size_t bytes;
 };
@@ -282,6 +283,8 @@ DecodeLayout decode_layout(void* ws, int B, int Hq, int Hkv, int d, int S, int t
   p.part_s = cv.take<float>((size_t)B * Hq * topk);
   p.sw_o = swa_pieces ? cv.take<float>((size_t)B * Hq * swa_pieces * d) : nullptr;
   p.sw_lse = swa_pieces ? cv.take<float>((size_t)B * Hq * swa_pieces) : nullptr;
+  // per (b, group), the attention blocks done (the fusion's counter)
+  p.sync = cv.take<uint32_t>((size_t)B * Hkv);
   p.bytes = cv.off + kAlign;
   return p;
 }
@@ -691,8 +694,21 @@ hsa_status_t hsa_decode(const void* q, const void* Kc, const void* Vc, const flo
   a.swa_lo = a.swa_hi = 0;
   a.o_swa = nullptr;
   a.sw_o = a.sw_lse = nullptr;
+  a.sync = lay.sync;
   const hipStream_t st = (hipStream_t)stream;
   StageMarks pm(st);
+  if (hsa::decode_fused_ok(a)) {
+    // scan, then attention with the fusion folded in (the fusion's stage
+    // mark stays, with nothing between)
+    for (int stage = 0; stage < hsa::kDecodeFusedStages; ++stage) {
+      pm.mark();
+      hipError_t e = hsa::decode_fused_stage(a, stage, st);
+      if (e != hipSuccess) return hip_fail(e, "decode");
+    }
+    pm.mark();
+    pm.mark();
+    return finish(st);
+  }
   for (int stage = 0; stage < hsa::kDecodeStages; ++stage) {
     pm.mark();
     hipError_t e = hsa::decode_stage(a, stage, st);
@@ -770,6 +786,7 @@ hsa_status_t hsa_swa_decode(const void* q, const void* Kc, const void* Vc, const
   a.swa_lo = a.swa_hi - (window < n_ctx + 1 ? window : n_ctx + 1);
   a.o_swa = o_swa;
   a.sw_o = lay.sw_o;
+  a.sync = nullptr;  // the window pieces keep the three-launch path
   a.sw_lse = lay.sw_lse;
   const hipStream_t st = (hipStream_t)stream;
   StageMarks pm(st);

@@ -14,10 +14,14 @@
 //              group); the sliding-window attention of the upper layers can
 //              ride in the same launch as extra blocks, one per 64-key piece
 //              of the window.
-//  3. fuse   : one block per (b, group): per head, a softmax over the
-//              selected chunks' s_h weights the chunk outputs; the window's
-//              pieces are merged by their log-sum-exp.
+//  3. fuse   : per (b, group) and head, a softmax over the selected
+//              chunks' s_h weights the chunk outputs; the window's pieces
+//              are merged by their log-sum-exp.  Without window pieces (and
+//              S <= 64) it runs in the attend launch itself: the last of the
+//              group's K blocks to finish does it (attend_fuse_kernel).
 #include <math.h>
+
+#include <algorithm>
 
 #include <type_traits>
 
@@ -32,6 +36,25 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxCand = 8192;  // candidates per (b, group) the merge reads
 constexpr int kMaxSlice = 4096;
+
+// Data that other blocks of the same launch read goes through agent-scope
+// (device-coherent) loads and stores: they reach every XCD without a
+// release fence's write-back of the L2.  A writer waits for its stores to
+// complete before it bumps the counter that announces them.
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// this wave's stores have completed
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Bitonic sort of one 64-bit key per lane across the wave, descending
 // (lane 0 ends with the largest).
@@ -139,13 +162,11 @@ __device__ uint64_t block_topk_sorted(Get get, int M, int K, uint64_t* lists) {
   return run;
 }
 
+// Slice sl of (b, group) bg: its candidate list and extremes.  LDS: u [D]
+// floats, keys [slice], lists [4 * 32].  Called by all threads.
 template <int D, int DT>
-__global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
-  __shared__ float u[D];
-  extern __shared__ uint64_t keys[];  // [slice]
-  __shared__ uint64_t lists[4 * 32];
-  const int64_t bg = blockIdx.x / a.n_slices;
-  const int sl = blockIdx.x % a.n_slices;
+__device__ __forceinline__ void scan_body(const DecodeArgs& a, int64_t bg, int sl, float* u,
+                                          uint64_t* keys, uint64_t* lists) {
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int G = a.Hq / a.Hkv;
   const int64_t c_begin = (int64_t)sl * a.slice;
@@ -212,12 +233,23 @@ __global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
   if (w == 0) {
     const int got = min(M, a.topk);
     uint64_t* out = a.cand + (bg * a.n_slices + sl) * a.topk;
-    if (lane < a.topk) out[lane] = lane < got ? top : 0ull;
+    if (lane < a.topk) st_agent(&out[lane], lane < got ? top : 0ull);
     const uint64_t mn = __shfl(top, max(got - 1, 0), kWave);
     if (lane == 0)
       *(u64x2*)(a.cand_mm + (bg * a.n_slices + sl) * 2) =
           u64x2{got > 0 ? top : 0ull, got == a.topk ? mn : 0ull};
   }
+}
+
+// a.sync (when set): the attention's per-group counters, cleared by block 0.
+template <int D, int DT>
+__global__ void __launch_bounds__(kThreads) scan_kernel(DecodeArgs a) {
+  __shared__ float u[D];
+  extern __shared__ uint64_t keys[];  // [slice]
+  __shared__ uint64_t lists[4 * 32];
+  if (a.sync && blockIdx.x == 0)
+    for (int64_t i = threadIdx.x; i < (int64_t)a.B * a.Hkv; i += kThreads) a.sync[i] = 0u;
+  scan_body<D, DT>(a, blockIdx.x / a.n_slices, blockIdx.x % a.n_slices, u, keys, lists);
 }
 
 // LDS of the candidate merge.
@@ -424,80 +456,28 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(DecodeArgs a, float sc
   }
 }
 
-// Chunks of at most 64 keys: one block per (b, group, unit r).  Units r < K
-// are the selected chunks: every such block runs the merge and takes the
-// chunk of rank r.  Units r >= K (sliding-window attention in the same
-// launch) are 64-key pieces of the window [swa_lo, swa_hi): they need no
-// merge and start at once.  A block loads its keys and values into
-// registers with coalesced 16-byte loads (each wave instruction reads 1 KB
-// of consecutive bytes: the gather is bandwidth-bound and cold in cache, so
-// the loads must be whole lines), and a chunk block its landmark row.  The
-// keys go to LDS first (16-byte pieces XOR-swizzled by row, so lane = key
-// reads spread over the banks): wave w takes heads w, w + 4, ...: lane =
-// key for the logits and a softmax over the block's keys, whose weights go
-// to LDS, and for a chunk the head's retrieval score s_h = q . lambda /
-// sqrt(d), for a window piece the log-sum-exp of its logits.  Then the
-// values replace the keys in the same LDS buffer and lane = output columns
-// for the weighted value sum.  One 16 KB buffer (bf16, d = 128) keeps the
-// block at about 19 KB of LDS, so 8 blocks fit on a CU and every block of a
-// batch-32 decode is resident at once.  The normalised outputs go to the
-// partial buffers; fuse_kernel combines them.
+// One unit of the attend stage once its keys are known: keys [row0, row0 +
+// nk) of (b, group) bg, either chunk c of rank r or window piece r - K (win).
+// qx: this thread's first two 16-byte pieces of the group's queries, already
+// loaded.  LDS: kv [64 key rows], lam [D] floats, qs [G * D] elements, ps
+// [G * 64] floats.  Called by all threads.
 template <int D, int DT>
-__global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, float scale) {
-  constexpr int EB = DT == kF32 ? 4 : 2;  // bytes per element
-  constexpr int ROWB = D * EB;            // bytes per key row
-  constexpr int PPR = ROWB / 16;          // 16-byte pieces per row
-  constexpr int NL = kWave * PPR / kThreads;  // 16-byte loads per thread per tensor
-  constexpr int CPL = D / 64;             // output columns per lane
+__device__ __forceinline__ void attend_body(const DecodeArgs& a, int64_t bg, int r, bool win,
+                                            int64_t row0, int nk, int c, const u32x4 (&qx)[2],
+                                            unsigned char* kv, float* lam, uint32_t* qs,
+                                            float* ps, float scale) {
+  constexpr int EB = DT == kF32 ? 4 : 2;
+  constexpr int ROWB = D * EB;
+  constexpr int PPR = ROWB / 16;
+  constexpr int NL = kWave * PPR / kThreads;
+  constexpr int CPL = D / 64;
   typedef typename std::conditional<DT == kF32, float, uint16_t>::type T;
-  union Stage {
-    MergeLds m;
-    unsigned char kv[kWave * ROWB];  // keys (swizzled pieces), then values
-  };
-  __shared__ __attribute__((aligned(16))) Stage st;
-  __shared__ __attribute__((aligned(16))) float lam[D];
-  __shared__ int32_t s_c;
-  // [G][D] queries as loaded (bf16 or fp32), then [G][64] key weights
-  extern __shared__ __attribute__((aligned(16))) float dyn[];
   const int G = a.Hq / a.Hkv;
   const int K = a.topk;
-  uint32_t* qs = (uint32_t*)dyn;
-  float* ps = dyn + G * D * EB / 4;
-  const int units = K + a.swa_pieces;
-  const int64_t bg = blockIdx.x / units;
-  const int r = blockIdx.x % units;
-  const bool win = r >= K;  // block-uniform
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t qrow0 = (int64_t)((bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G);
-  // the group's queries load during the merge (G * D elements, 16 bytes at a time)
   const int nq = G * D * EB / 16;
   const u32x4* qg = (const u32x4*)((const char*)a.q + qrow0 * ROWB);
-  u32x4 qx[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) qx[i] = qg[min(tid + i * kThreads, nq - 1)];
-  int64_t row0;  // the block's first key row in the (b, group) cache
-  int nk;        // its keys (1..64)
-  int c = -1;    // chunk blocks: the chunk
-  if (win) {
-    row0 = a.swa_lo + (int64_t)(r - K) * kWave;
-    nk = (int)min((int64_t)kWave, a.swa_hi - row0);
-    HSA_DCHECK(row0 >= 0 && nk >= 1 && row0 + nk <= a.n_max);
-  } else {
-    if (a.n_avail > 0) {
-      const int got = merge_sorted(a, bg, st.m);
-      if (tid == 0) s_c = r < got ? st.m.order[r] : -1;
-      if (r == 0 && tid < K) a.sel[bg * K + tid] = st.m.order[tid];
-    } else {
-      if (tid == 0) s_c = -1;
-      if (r == 0 && tid < K) a.sel[bg * K + tid] = -1;
-    }
-    __syncthreads();
-    c = s_c;
-    if (c < 0) return;  // uniform: rank past the selected chunks
-    HSA_DCHECK(c < a.n_avail);
-    row0 = (int64_t)c * a.S;
-    nk = a.S;
-  }
   const int64_t base = (bg * a.n_max + row0) * ROWB;
   const char* Kg = (const char*)a.Kc + base;
   const char* Vg = (const char*)a.Vc + base;
@@ -521,7 +501,7 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int e = tid + i * kThreads, row = e / PPR, pc = e % PPR;
-    *(u32x4*)(&st.kv[row * ROWB + ((pc ^ (row % PPR)) * 16)]) = kx[i];
+    *(u32x4*)(&kv[row * ROWB + ((pc ^ (row % PPR)) * 16)]) = kx[i];
   }
   if (tid < D / 4) *(f32x4*)(&lam[4 * tid]) = lx;
   __syncthreads();
@@ -529,7 +509,7 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
   for (int h = w; h < G; h += kThreads / kWave) {
     // logit of key `lane`
     float acc = 0.f;
-    const unsigned char* kr = &st.kv[lane * ROWB];
+    const unsigned char* kr = &kv[lane * ROWB];
     const uint32_t* qh = qs + h * D * EB / 4;
 #pragma unroll 4
     for (int pc = 0; pc < PPR; ++pc) {
@@ -565,7 +545,7 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
         sl += qv * lam[col];
       }
       sl = wave_sum_f32(sl);
-      if (lane == 0) a.part_s[(qrow0 + h) * K + r] = sl * scale;
+      if (lane == 0) st_agent((uint32_t*)&a.part_s[(qrow0 + h) * K + r], __float_as_uint(sl * scale));
     }
   }
   __syncthreads();
@@ -573,7 +553,7 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int e = tid + i * kThreads, row = e / PPR, pc = e % PPR;
-    *(u32x4*)(&st.kv[row * ROWB + pc * 16]) = vx[i];
+    *(u32x4*)(&kv[row * ROWB + pc * 16]) = vx[i];
   }
   __syncthreads();
   for (int h = w; h < G; h += kThreads / kWave) {
@@ -586,7 +566,7 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
       const f32x4 p4 = *(const f32x4*)(&ph[j]);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const T* vr = (const T*)&st.kv[(j + jj) * ROWB] + CPL * lane;
+        const T* vr = (const T*)&kv[(j + jj) * ROWB] + CPL * lane;
         if (DT == kF32) {
 #pragma unroll
           for (int x = 0; x < CPL; ++x) o[x] += p4[jj] * ((const float*)vr)[x];
@@ -602,27 +582,99 @@ __global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, 
     float* po = (win ? a.sw_o + ((qrow0 + h) * a.swa_pieces + (r - K)) * D
                      : a.part_o + ((qrow0 + h) * K + r) * D) + CPL * lane;
     if (CPL == 2)
-      *(f32x2*)po = f32x2{o[0], o[CPL - 1]};
+      st_agent((uint64_t*)po, __builtin_bit_cast(uint64_t, f32x2{o[0], o[CPL - 1]}));
     else
-      po[0] = o[0];
+      st_agent((uint32_t*)po, __float_as_uint(o[0]));
   }
+}
+
+// Chunks of at most 64 keys: one block per (b, group, unit r).  Units r < K
+// are the selected chunks: every such block runs the merge and takes the
+// chunk of rank r.  Units r >= K (sliding-window attention in the same
+// launch) are 64-key pieces of the window [swa_lo, swa_hi): they need no
+// merge and start at once.  A block loads its keys and values into
+// registers with coalesced 16-byte loads (each wave instruction reads 1 KB
+// of consecutive bytes: the gather is bandwidth-bound and cold in cache, so
+// the loads must be whole lines), and a chunk block its landmark row.  The
+// keys go to LDS first (16-byte pieces XOR-swizzled by row, so lane = key
+// reads spread over the banks): wave w takes heads w, w + 4, ...: lane =
+// key for the logits and a softmax over the block's keys, whose weights go
+// to LDS, and for a chunk the head's retrieval score s_h = q . lambda /
+// sqrt(d), for a window piece the log-sum-exp of its logits.  Then the
+// values replace the keys in the same LDS buffer and lane = output columns
+// for the weighted value sum.  One 16 KB buffer (bf16, d = 128) keeps the
+// block at about 19 KB of LDS, so 8 blocks fit on a CU and every block of a
+// batch-32 decode is resident at once.  The normalised outputs go to the
+// partial buffers; fuse_kernel combines them.
+template <int D, int DT>
+__global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, float scale) {
+  constexpr int EB = DT == kF32 ? 4 : 2;  // bytes per element
+  constexpr int ROWB = D * EB;            // bytes per key row
+  union Stage {
+    MergeLds m;
+    unsigned char kv[kWave * ROWB];  // keys (swizzled pieces), then values
+  };
+  __shared__ __attribute__((aligned(16))) Stage st;
+  __shared__ __attribute__((aligned(16))) float lam[D];
+  __shared__ int32_t s_c;
+  // [G][D] queries as loaded (bf16 or fp32), then [G][64] key weights
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  const int G = a.Hq / a.Hkv;
+  const int K = a.topk;
+  uint32_t* qs = (uint32_t*)dyn;
+  float* ps = dyn + G * D * EB / 4;
+  const int units = K + a.swa_pieces;
+  const int64_t bg = blockIdx.x / units;
+  const int r = blockIdx.x % units;
+  const bool win = r >= K;  // block-uniform
+  const int tid = threadIdx.x;
+  const int64_t qrow0 = (int64_t)((bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G);
+  // the group's queries load during the merge (G * D elements, 16 bytes at a time)
+  const int nq = G * D * EB / 16;
+  const u32x4* qg = (const u32x4*)((const char*)a.q + qrow0 * ROWB);
+  u32x4 qx[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) qx[i] = qg[min(tid + i * kThreads, nq - 1)];
+  int64_t row0;  // the block's first key row in the (b, group) cache
+  int nk;        // its keys (1..64)
+  int c = -1;    // chunk blocks: the chunk
+  if (win) {
+    row0 = a.swa_lo + (int64_t)(r - K) * kWave;
+    nk = (int)min((int64_t)kWave, a.swa_hi - row0);
+    HSA_DCHECK(row0 >= 0 && nk >= 1 && row0 + nk <= a.n_max);
+  } else {
+    if (a.n_avail > 0) {
+      const int got = merge_sorted(a, bg, st.m);
+      if (tid == 0) s_c = r < got ? st.m.order[r] : -1;
+      if (r == 0 && tid < K) a.sel[bg * K + tid] = st.m.order[tid];
+    } else {
+      if (tid == 0) s_c = -1;
+      if (r == 0 && tid < K) a.sel[bg * K + tid] = -1;
+    }
+    __syncthreads();
+    c = s_c;
+    if (c < 0) return;  // uniform: rank past the selected chunks
+    HSA_DCHECK(c < a.n_avail);
+    row0 = (int64_t)c * a.S;
+    nk = a.S;
+  }
+  attend_body<D, DT>(a, bg, r, win, row0, nk, c, qx, st.kv, lam, qs, ps, scale);
 }
 
 // Per (b, group): per head, a softmax over the selected chunks' s_h (one
 // wave per head, lane = rank) and the weighted sum of the normalised chunk
 // outputs (16 bytes of columns per thread, all ranks' loads in flight); no
 // selected chunk gives zeros.
+// LDS: wts [32 * 64] floats, s_got.  Called by all threads.
 template <int D, int DT>
-__global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
-  __shared__ float wts[32 * kWave];  // [head of the group][rank or window piece]
-  __shared__ int s_got;
-  const int64_t bg = blockIdx.x;
+__device__ __forceinline__ void fuse_body(const DecodeArgs& a, int64_t bg, float* wts,
+                                          int& s_got) {
   const int G = a.Hq / a.Hkv;
   const int K = a.topk;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t qrow0 = (int64_t)((bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G);
   if (w == 0) {
-    const int32_t sv = lane < K ? a.sel[bg * K + lane] : -1;
+    const int32_t sv = lane < K ? (int32_t)ld_agent((const uint32_t*)&a.sel[bg * K + lane]) : -1;
     const uint64_t live = __ballot(sv >= 0);
     if (lane == 0) s_got = __popcll(live);
   }
@@ -630,7 +682,9 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
   const int got = s_got;
   for (int h = w; h < G; h += kThreads / kWave) {
     const int64_t row = qrow0 + h;
-    const float sc = lane < got ? a.part_s[row * K + lane] : -INFINITY;
+    const float sc =
+        lane < got ? __uint_as_float(ld_agent((const uint32_t*)&a.part_s[row * K + lane]))
+                   : -INFINITY;
     const float mx = wave_max_f32(sc);
     const float e = lane < got ? expf(sc - mx) : 0.f;
     const float wk = e / wave_sum_f32(e);
@@ -647,7 +701,10 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int kk = 0; kk < got; ++kk) {
-      const f32x4 v = *(const f32x4*)(po + (int64_t)kk * D);
+      const uint64_t* pv = (const uint64_t*)(po + (int64_t)kk * D);
+      const f32x2 v0 = __builtin_bit_cast(f32x2, ld_agent(pv));
+      const f32x2 v1 = __builtin_bit_cast(f32x2, ld_agent(pv + 1));
+      const f32x4 v = {v0[0], v0[1], v1[0], v1[1]};
       const float wk = wts[h * K + kk];
 #pragma unroll
       for (int x = 0; x < 4; ++x) acc[x] += wk * v[x];
@@ -683,6 +740,91 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) store_elem<DT>(a.o_swa, row * D + 4 * x4 + x, acc[x]);
   }
+}
+
+template <int D, int DT>
+__global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
+  __shared__ float wts[32 * kWave];  // [head of the group][rank or window piece]
+  __shared__ int s_got;
+  fuse_body<D, DT>(a, blockIdx.x, wts, s_got);
+}
+
+// ---- the decode with the fusion folded into the attention -------------------
+//
+// Two launches: the scan (as above; its first block also clears the
+// per-group counters of the second launch), then one block per (b, group,
+// rank) that merges the slices' candidates, attends to the chunk of its rank
+// and counts itself done: the last block of the group to finish fuses the
+// group's chunk outputs.  No block waits for another.
+
+// Grid (b, group, rank).  a.sync [B*Hkv]: blocks of the group done.  LDS
+// (dynamic): the merge's MergeLds, then 64 key rows, lam [D] floats, qs
+// [G * D] elements, ps [G * 64] floats; the fusion's wts [32 * 64] floats.
+template <int D, int DT>
+__global__ void __launch_bounds__(kThreads, DT == kF32 ? 4 : 8)
+    attend_fuse_kernel(DecodeArgs a, float scale) {
+  constexpr int EB = DT == kF32 ? 4 : 2;
+  constexpr int ROWB = D * EB;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int32_t s_c;
+  __shared__ int s_last;
+  __shared__ int s_got;
+  const int tid = threadIdx.x;
+  const int K = a.topk, G = a.Hq / a.Hkv;
+  const int64_t bg = blockIdx.x / K;
+  const int r = blockIdx.x % K;
+  unsigned char* kv = smem;
+  float* lam = (float*)(smem + kWave * ROWB);
+  uint32_t* qs = (uint32_t*)(smem + kWave * ROWB + D * 4);
+  float* ps = (float*)(smem + kWave * ROWB + D * 4 + G * D * EB);
+  const int64_t qrow0 = (int64_t)((bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G);
+  // the group's queries load during the merge
+  const int nq = G * D * EB / 16;
+  const u32x4* qg = (const u32x4*)((const char*)a.q + qrow0 * ROWB);
+  u32x4 qx[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) qx[i] = qg[min(tid + i * kThreads, nq - 1)];
+  {
+    MergeLds& ml = *(MergeLds*)smem;
+    const int got = merge_sorted(a, bg, ml);
+    if (tid == 0) s_c = r < got ? ml.order[r] : -1;
+    // the selection goes out from rank 0 (the fusion reads it)
+    if (r == 0 && tid < K) st_agent((uint32_t*)&a.sel[bg * K + tid], (uint32_t)ml.order[tid]);
+    __syncthreads();
+  }
+  const int c = s_c;
+  HSA_DCHECK(c < a.n_avail);
+  if (c >= 0 && c < a.n_avail)
+    attend_body<D, DT>(a, bg, r, false, (int64_t)c * a.S, a.S, c, qx, kv, lam, qs, ps, scale);
+  // the last block of bg fuses
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.sync[bg], 1u) == (uint32_t)(K - 1);
+  __syncthreads();
+  if (!s_last) return;
+  fuse_body<D, DT>(a, bg, (float*)smem, s_got);
+}
+
+template <int D, int DT>
+size_t attend_fuse_lds(const DecodeArgs& a) {
+  constexpr size_t EB = DT == kF32 ? 4 : 2;
+  const size_t G = (size_t)(a.Hq / a.Hkv);
+  return std::max<size_t>({kWave * D * EB + D * 4 + G * D * EB + G * kWave * 4,
+                           32 * kWave * 4, sizeof(MergeLds)});
+}
+
+template <int D, int DT>
+hipError_t fused_stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
+  const int64_t BG = (int64_t)a.B * a.Hkv;
+  if (stage == 0) {
+    launch<scan_kernel<D, DT>>(dim3((unsigned)(BG * a.n_slices)), dim3(kThreads),
+                               (size_t)a.slice * sizeof(uint64_t), stream, a);
+  } else {
+    const float scale = 1.0f / sqrtf((float)D);
+    launch<attend_fuse_kernel<D, DT>>(dim3((unsigned)(BG * a.topk)), dim3(kThreads),
+                                      attend_fuse_lds<D, DT>(a), stream, a, scale);
+  }
+  return hipGetLastError();
 }
 
 template <int D, int DT>
@@ -731,6 +873,23 @@ void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* sl
 }
 
 int64_t decode_max_chunks(int topk) { return (int64_t)kMaxSlice * (kMaxCand / topk); }
+
+bool decode_fused_ok(const DecodeArgs& a) {
+  if (a.S > kWave || a.n_avail <= 0 || a.swa_pieces != 0 || !a.sync) return false;
+  const size_t lds = a.d == 64 ? (a.dtype == kF32 ? attend_fuse_lds<64, kF32>(a)
+                                                  : attend_fuse_lds<64, kBF16>(a))
+                               : (a.dtype == kF32 ? attend_fuse_lds<128, kF32>(a)
+                                                  : attend_fuse_lds<128, kBF16>(a));
+  return lds <= 64 * 1024;
+}
+
+hipError_t decode_fused_stage(const DecodeArgs& a, int stage, hipStream_t stream) {
+  if (a.d == 64)
+    return a.dtype == kF32 ? fused_stage_dt<64, kF32>(a, stage, stream)
+                           : fused_stage_dt<64, kBF16>(a, stage, stream);
+  return a.dtype == kF32 ? fused_stage_dt<128, kF32>(a, stage, stream)
+                         : fused_stage_dt<128, kBF16>(a, stage, stream);
+}
 
 hipError_t decode_stage(const DecodeArgs& a, int stage, hipStream_t stream) {
   if (a.d == 64)

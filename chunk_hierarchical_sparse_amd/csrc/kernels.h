@@ -125,8 +125,18 @@ struct DecodeArgs {
   void* o_swa;         // [B,Hq,d]
   float* sw_o;         // [B,Hq,swa_pieces,d]: each piece's normalised output
   float* sw_lse;       // [B,Hq,swa_pieces]: natural log-sum-exp of its logits
+  // the decode with the fusion folded into the attention (decode_fused_*):
+  // per (b, group), the attention blocks done (cleared by the scan)
+  uint32_t* sync;      // [B*Hkv] or null
 };
 void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* slice);
+// Whether the folded decode takes these arguments (chunks of at most 64
+// keys, some chunk available, no window pieces, a.sync set).
+bool decode_fused_ok(const DecodeArgs& a);
+// stages: 0 scan (also clears a.sync); 1 merge + attention, the last block
+// of each (b, group) fusing its chunk outputs
+constexpr int kDecodeFusedStages = 2;
+hipError_t decode_fused_stage(const DecodeArgs& a, int stage, hipStream_t stream);
 // stages: 0 scan (landmark stream + per-slice top-K), 1 attend (merge of the
 // slices' candidates, then one block per selected chunk; with swa_pieces
 // also one block per window piece), 2 fuse (softmax over the chunks'
