@@ -46,6 +46,6 @@ def test_log_prints_entry_points_and_launches():
                         r"lds (\d+) B$")
     names = [m.group(1) for m in map(launch.match, lines) if m]
     for want in ["select_mfma_kernel<128, 8>", "attend_chunk_bf16_kernel<128, true>",
-                 "scan_kernel<128, 1>", "attend_rank_kernel<128, 1>"]:
+                 "scan_kernel<128, 1>", "attend_fuse_kernel<128, 1>"]:
         assert want in names, (want, names)
     assert any(n.startswith("fuse_kernel<128, 1") for n in names), names
