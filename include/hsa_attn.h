@@ -366,7 +366,9 @@ hsa_status_t hsa_swa_decode(const void* q, const void* Kc, const void* Vc, const
  *   hsa_prefill : 0 landmarks, 1 select, 2 invert, 3 attend, 4 fuse
  *   hsa_decode  : 0 scan (landmark stream, per-slice top-K), 1 attend (merge
  *                 of the slices' candidates, one block per selected chunk),
- *                 2 fuse (softmax over the retrieval scores, weighted sum)
+ *                 2 fuse (softmax over the retrieval scores, weighted sum;
+ *                 for chunks of at most 64 keys it runs inside the attend
+ *                 launch, and this stage is empty)
  *   dhsa_prefill: 0 pool, 1 rank (S_c rows and their ranking), 2 attend,
  *                 3 mask
  *   dhsa_decode : 0 score (pooling, S_c, rank, cut), 1 attend, 2 combine
