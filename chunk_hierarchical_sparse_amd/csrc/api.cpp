@@ -786,7 +786,7 @@ hsa_status_t hsa_swa_decode(const void* q, const void* Kc, const void* Vc, const
   a.swa_lo = a.swa_hi - (window < n_ctx + 1 ? window : n_ctx + 1);
   a.o_swa = o_swa;
   a.sw_o = lay.sw_o;
-  a.sync = nullptr;  // the window pieces keep the three-launch path
+  a.sync = nullptr;  // the fusion and the window's merge run as their own launch
   a.sw_lse = lay.sw_lse;
   const hipStream_t st = (hipStream_t)stream;
   StageMarks pm(st);

@@ -16,9 +16,9 @@
 //              of the window.
 //  3. fuse   : per (b, group) and head, a softmax over the selected
 //              chunks' s_h weights the chunk outputs; the window's pieces
-//              are merged by their log-sum-exp.  Without window pieces (and
-//              S <= 64) it runs in the attend launch itself: the last of the
-//              group's K blocks to finish does it (attend_fuse_kernel).
+//              are merged by their log-sum-exp.  For chunks of at most 64
+//              keys it runs in the attend launch itself: the last of the
+//              group's blocks to finish does it (attend_fuse_kernel).
 #include <math.h>
 
 #include <algorithm>
@@ -533,7 +533,9 @@ __device__ __forceinline__ void attend_body(const DecodeArgs& a, int64_t bg, int
     const float z = wave_sum_f32(pe);
     ps[h * kWave + lane] = pe / z;
     if (win) {
-      if (lane == 0) a.sw_lse[(qrow0 + h) * a.swa_pieces + (r - K)] = mx + logf(z);
+      if (lane == 0)
+        st_agent((uint32_t*)&a.sw_lse[(qrow0 + h) * a.swa_pieces + (r - K)],
+                 __float_as_uint(mx + logf(z)));
     } else {
       // s_h: this lane's landmark columns
       float sl = 0.f;
@@ -586,79 +588,6 @@ __device__ __forceinline__ void attend_body(const DecodeArgs& a, int64_t bg, int
     else
       st_agent((uint32_t*)po, __float_as_uint(o[0]));
   }
-}
-
-// Chunks of at most 64 keys: one block per (b, group, unit r).  Units r < K
-// are the selected chunks: every such block runs the merge and takes the
-// chunk of rank r.  Units r >= K (sliding-window attention in the same
-// launch) are 64-key pieces of the window [swa_lo, swa_hi): they need no
-// merge and start at once.  A block loads its keys and values into
-// registers with coalesced 16-byte loads (each wave instruction reads 1 KB
-// of consecutive bytes: the gather is bandwidth-bound and cold in cache, so
-// the loads must be whole lines), and a chunk block its landmark row.  The
-// keys go to LDS first (16-byte pieces XOR-swizzled by row, so lane = key
-// reads spread over the banks): wave w takes heads w, w + 4, ...: lane =
-// key for the logits and a softmax over the block's keys, whose weights go
-// to LDS, and for a chunk the head's retrieval score s_h = q . lambda /
-// sqrt(d), for a window piece the log-sum-exp of its logits.  Then the
-// values replace the keys in the same LDS buffer and lane = output columns
-// for the weighted value sum.  One 16 KB buffer (bf16, d = 128) keeps the
-// block at about 19 KB of LDS, so 8 blocks fit on a CU and every block of a
-// batch-32 decode is resident at once.  The normalised outputs go to the
-// partial buffers; fuse_kernel combines them.
-template <int D, int DT>
-__global__ void __launch_bounds__(kThreads, 8) attend_rank_kernel(DecodeArgs a, float scale) {
-  constexpr int EB = DT == kF32 ? 4 : 2;  // bytes per element
-  constexpr int ROWB = D * EB;            // bytes per key row
-  union Stage {
-    MergeLds m;
-    unsigned char kv[kWave * ROWB];  // keys (swizzled pieces), then values
-  };
-  __shared__ __attribute__((aligned(16))) Stage st;
-  __shared__ __attribute__((aligned(16))) float lam[D];
-  __shared__ int32_t s_c;
-  // [G][D] queries as loaded (bf16 or fp32), then [G][64] key weights
-  extern __shared__ __attribute__((aligned(16))) float dyn[];
-  const int G = a.Hq / a.Hkv;
-  const int K = a.topk;
-  uint32_t* qs = (uint32_t*)dyn;
-  float* ps = dyn + G * D * EB / 4;
-  const int units = K + a.swa_pieces;
-  const int64_t bg = blockIdx.x / units;
-  const int r = blockIdx.x % units;
-  const bool win = r >= K;  // block-uniform
-  const int tid = threadIdx.x;
-  const int64_t qrow0 = (int64_t)((bg / a.Hkv) * a.Hq + (bg % a.Hkv) * G);
-  // the group's queries load during the merge (G * D elements, 16 bytes at a time)
-  const int nq = G * D * EB / 16;
-  const u32x4* qg = (const u32x4*)((const char*)a.q + qrow0 * ROWB);
-  u32x4 qx[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) qx[i] = qg[min(tid + i * kThreads, nq - 1)];
-  int64_t row0;  // the block's first key row in the (b, group) cache
-  int nk;        // its keys (1..64)
-  int c = -1;    // chunk blocks: the chunk
-  if (win) {
-    row0 = a.swa_lo + (int64_t)(r - K) * kWave;
-    nk = (int)min((int64_t)kWave, a.swa_hi - row0);
-    HSA_DCHECK(row0 >= 0 && nk >= 1 && row0 + nk <= a.n_max);
-  } else {
-    if (a.n_avail > 0) {
-      const int got = merge_sorted(a, bg, st.m);
-      if (tid == 0) s_c = r < got ? st.m.order[r] : -1;
-      if (r == 0 && tid < K) a.sel[bg * K + tid] = st.m.order[tid];
-    } else {
-      if (tid == 0) s_c = -1;
-      if (r == 0 && tid < K) a.sel[bg * K + tid] = -1;
-    }
-    __syncthreads();
-    c = s_c;
-    if (c < 0) return;  // uniform: rank past the selected chunks
-    HSA_DCHECK(c < a.n_avail);
-    row0 = (int64_t)c * a.S;
-    nk = a.S;
-  }
-  attend_body<D, DT>(a, bg, r, win, row0, nk, c, qx, st.kv, lam, qs, ps, scale);
 }
 
 // Per (b, group): per head, a softmax over the selected chunks' s_h (one
@@ -718,7 +647,9 @@ __device__ __forceinline__ void fuse_body(const DecodeArgs& a, int64_t bg, float
   __syncthreads();
   for (int h = w; h < G; h += kThreads / kWave) {
     const int64_t row = qrow0 + h;
-    const float ls = lane < P ? a.sw_lse[row * P + lane] : -INFINITY;
+    const float ls =
+        lane < P ? __uint_as_float(ld_agent((const uint32_t*)&a.sw_lse[row * P + lane]))
+                 : -INFINITY;
     const float mx = wave_max_f32(ls);
     const float e = lane < P ? expf(ls - mx) : 0.f;
     const float wk = e / wave_sum_f32(e);
@@ -732,7 +663,10 @@ __device__ __forceinline__ void fuse_body(const DecodeArgs& a, int64_t bg, float
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int pp = 0; pp < P; ++pp) {
-      const f32x4 v = *(const f32x4*)(po + (int64_t)pp * D);
+      const uint64_t* pv = (const uint64_t*)(po + (int64_t)pp * D);
+      const f32x2 v0 = __builtin_bit_cast(f32x2, ld_agent(pv));
+      const f32x2 v1 = __builtin_bit_cast(f32x2, ld_agent(pv + 1));
+      const f32x4 v = {v0[0], v0[1], v1[0], v1[1]};
       const float wk = wts[h * kWave + pp];
 #pragma unroll
       for (int x = 0; x < 4; ++x) acc[x] += wk * v[x];
@@ -749,15 +683,32 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
   fuse_body<D, DT>(a, blockIdx.x, wts, s_got);
 }
 
-// ---- the decode with the fusion folded into the attention -------------------
+// ---- the attention of chunks of at most 64 keys ------------------------------
 //
-// Two launches: the scan (as above; its first block also clears the
-// per-group counters of the second launch), then one block per (b, group,
-// rank) that merges the slices' candidates, attends to the chunk of its rank
-// and counts itself done: the last block of the group to finish fuses the
-// group's chunk outputs.  No block waits for another.
+// With a.sync set (hsa_decode), two launches: the scan (as above; its first
+// block also clears the per-group counters of the second launch), then one
+// block per (b, group, unit r), the fusion folded in; with a.sync null
+// (hsa_swa_decode, whose window merge would lengthen the folded tail) the
+// fusion is the third launch.  Blocks per (b, group, unit r).  Units r < K are the selected chunks: every
+// such block runs the merge and takes the chunk of rank r.  Units r >= K
+// (sliding-window attention in the same launch) are 64-key pieces of the
+// window [swa_lo, swa_hi): they need no merge and start at once.  A block
+// loads its keys and values into registers with coalesced 16-byte loads
+// (each wave instruction reads 1 KB of consecutive bytes: the gather is
+// bandwidth-bound and cold in cache, so the loads must be whole lines), and
+// a chunk block its landmark row.  The keys go to LDS first (16-byte pieces
+// XOR-swizzled by row, so lane = key reads spread over the banks): wave w
+// takes heads w, w + 4, ...: lane = key for the logits and a softmax over
+// the block's keys, whose weights go to LDS, and for a chunk the head's
+// retrieval score s_h = q . lambda / sqrt(d), for a window piece the
+// log-sum-exp of its logits.  Then the values replace the keys in the same
+// LDS buffer and lane = output columns for the weighted value sum.  One
+// 16 KB buffer (bf16, d = 128) keeps the block at about 19 KB of LDS, so 8
+// blocks fit on a CU and every block of a batch-32 decode is resident at
+// once.  With a.sync set each block counts itself done, and the last block
+// of the group to finish runs the fusion.  No block waits for another.
 
-// Grid (b, group, rank).  a.sync [B*Hkv]: blocks of the group done.  LDS
+// Grid (b, group, unit).  a.sync [B*Hkv]: blocks of the group done.  LDS
 // (dynamic): the merge's MergeLds, then 64 key rows, lam [D] floats, qs
 // [G * D] elements, ps [G * 64] floats; the fusion's wts [32 * 64] floats.
 template <int D, int DT>
@@ -771,8 +722,10 @@ __global__ void __launch_bounds__(kThreads, DT == kF32 ? 4 : 8)
   __shared__ int s_got;
   const int tid = threadIdx.x;
   const int K = a.topk, G = a.Hq / a.Hkv;
-  const int64_t bg = blockIdx.x / K;
-  const int r = blockIdx.x % K;
+  const int units = K + a.swa_pieces;
+  const int64_t bg = blockIdx.x / units;
+  const int r = blockIdx.x % units;
+  const bool win = r >= K;  // block-uniform
   unsigned char* kv = smem;
   float* lam = (float*)(smem + kWave * ROWB);
   uint32_t* qs = (uint32_t*)(smem + kWave * ROWB + D * 4);
@@ -784,22 +737,37 @@ __global__ void __launch_bounds__(kThreads, DT == kF32 ? 4 : 8)
   u32x4 qx[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) qx[i] = qg[min(tid + i * kThreads, nq - 1)];
-  {
-    MergeLds& ml = *(MergeLds*)smem;
-    const int got = merge_sorted(a, bg, ml);
-    if (tid == 0) s_c = r < got ? ml.order[r] : -1;
-    // the selection goes out from rank 0 (the fusion reads it)
-    if (r == 0 && tid < K) st_agent((uint32_t*)&a.sel[bg * K + tid], (uint32_t)ml.order[tid]);
+  int64_t row0 = 0;  // the block's first key row in the (b, group) cache
+  int nk = 0;        // its keys (1..64)
+  int c = -1;        // chunk blocks: the chunk
+  if (win) {
+    row0 = a.swa_lo + (int64_t)(r - K) * kWave;
+    nk = (int)min((int64_t)kWave, a.swa_hi - row0);
+    HSA_DCHECK(row0 >= 0 && nk >= 1 && row0 + nk <= a.n_max);
+  } else {
+    if (a.n_avail > 0) {
+      MergeLds& ml = *(MergeLds*)smem;
+      const int got = merge_sorted(a, bg, ml);
+      if (tid == 0) s_c = r < got ? ml.order[r] : -1;
+      // the selection goes out from rank 0 (the fusion reads it)
+      if (r == 0 && tid < K) st_agent((uint32_t*)&a.sel[bg * K + tid], (uint32_t)ml.order[tid]);
+    } else {
+      if (tid == 0) s_c = -1;
+      if (r == 0 && tid < K) st_agent((uint32_t*)&a.sel[bg * K + tid], 0xffffffffu);
+    }
     __syncthreads();
+    c = s_c;
+    HSA_DCHECK(c < a.n_avail);
+    row0 = (int64_t)c * a.S;
+    nk = a.S;
   }
-  const int c = s_c;
-  HSA_DCHECK(c < a.n_avail);
-  if (c >= 0 && c < a.n_avail)
-    attend_body<D, DT>(a, bg, r, false, (int64_t)c * a.S, a.S, c, qx, kv, lam, qs, ps, scale);
+  if (win || (c >= 0 && c < a.n_avail))
+    attend_body<D, DT>(a, bg, r, win, row0, nk, c, qx, kv, lam, qs, ps, scale);
+  if (!a.sync) return;  // the fusion runs as its own launch
   // the last block of bg fuses
   wait_stores();
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.sync[bg], 1u) == (uint32_t)(K - 1);
+  if (tid == 0) s_last = atomicAdd(&a.sync[bg], 1u) == (uint32_t)(units - 1);
   __syncthreads();
   if (!s_last) return;
   fuse_body<D, DT>(a, bg, (float*)smem, s_got);
@@ -821,8 +789,9 @@ hipError_t fused_stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
                                (size_t)a.slice * sizeof(uint64_t), stream, a);
   } else {
     const float scale = 1.0f / sqrtf((float)D);
-    launch<attend_fuse_kernel<D, DT>>(dim3((unsigned)(BG * a.topk)), dim3(kThreads),
-                                      attend_fuse_lds<D, DT>(a), stream, a, scale);
+    launch<attend_fuse_kernel<D, DT>>(dim3((unsigned)(BG * (a.topk + a.swa_pieces))),
+                                      dim3(kThreads), attend_fuse_lds<D, DT>(a), stream, a,
+                                      scale);
   }
   return hipGetLastError();
 }
@@ -837,11 +806,12 @@ hipError_t stage_dt(const DecodeArgs& a, int stage, hipStream_t stream) {
       launch<scan_kernel<D, DT>>(dim3((unsigned)(BG * a.n_slices)), dim3(kThreads),
                                  (size_t)a.slice * sizeof(uint64_t), stream, a);
   } else if (stage == 1) {
-    // one block per (b, group, rank)
-    const size_t q_lds = (size_t)G * D * (DT == kF32 ? 4 : 2) + (size_t)G * kWave * sizeof(float);
+    // one block per (b, group, unit); a.sync is null here, so
+    // attend_fuse_kernel leaves the fusion to stage 2
     if (a.S <= kWave)
-      launch<attend_rank_kernel<D, DT>>(dim3((unsigned)(BG * (a.topk + a.swa_pieces))),
-                                        dim3(kThreads), q_lds, stream, a, scale);
+      launch<attend_fuse_kernel<D, DT>>(dim3((unsigned)(BG * (a.topk + a.swa_pieces))),
+                                        dim3(kThreads), attend_fuse_lds<D, DT>(a), stream, a,
+                                        scale);
     else
       launch<attend_kernel<D, DT>>(dim3((unsigned)(BG * a.topk)), dim3(kThreads),
                                    (size_t)G * D * sizeof(float), stream, a, scale);
@@ -875,7 +845,9 @@ void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* sl
 int64_t decode_max_chunks(int topk) { return (int64_t)kMaxSlice * (kMaxCand / topk); }
 
 bool decode_fused_ok(const DecodeArgs& a) {
-  if (a.S > kWave || a.n_avail <= 0 || a.swa_pieces != 0 || !a.sync) return false;
+  // with no chunk available the scan still runs (on empty slices): it
+  // clears the counters
+  if (a.S > kWave || !a.sync) return false;
   const size_t lds = a.d == 64 ? (a.dtype == kF32 ? attend_fuse_lds<64, kF32>(a)
                                                   : attend_fuse_lds<64, kBF16>(a))
                                : (a.dtype == kF32 ? attend_fuse_lds<128, kF32>(a)

@@ -131,7 +131,7 @@ struct DecodeArgs {
 };
 void decode_plan(int64_t n_avail, int topk, int64_t BHkv, int* n_slices, int* slice);
 // Whether the folded decode takes these arguments (chunks of at most 64
-// keys, some chunk available, no window pieces, a.sync set).
+// keys, some chunk available, a.sync set).
 bool decode_fused_ok(const DecodeArgs& a);
 // stages: 0 scan (also clears a.sync); 1 merge + attention, the last block
 // of each (b, group) fusing its chunk outputs
