@@ -689,7 +689,7 @@ __global__ void __launch_bounds__(kThreads) fuse_kernel(DecodeArgs a) {
 // block also clears the per-group counters of the second launch), then one
 // block per (b, group, unit r), the fusion folded in; with a.sync null
 // (hsa_swa_decode, whose window merge would lengthen the folded tail) the
-// fusion is the third launch.  Blocks per (b, group, unit r).  Units r < K are the selected chunks: every
+// fusion is the third launch.  Units r < K are the selected chunks: every
 // such block runs the merge and takes the chunk of rank r.  Units r >= K
 // (sliding-window attention in the same launch) are 64-key pieces of the
 // window [swa_lo, swa_hi): they need no merge and start at once.  A block
