@@ -85,7 +85,7 @@ constexpr int kSlotBits = 5;  // topk <= 32
 // backward, whose dK and dV sum over a chunk's list) and up to
 // kInvertDetBins chunks, the lists are in token order instead, so those
 // sums run in a fixed order.
-constexpr int kInvertTokens = 1024;
+constexpr int kInvertTokens = 512;
 constexpr int kInvertDetBins = 4096;
 // prefill_select also clears counts and cursor; prefill_invert relies on
 // that, so it runs right after prefill_select on the same stream.
